@@ -1,0 +1,132 @@
+"""Oracle: the paged INT2 history layout (four 2-bit codes per byte).
+
+Source: the QbitAI article on OSCAR, serving-path section: history is stored as INT2,
+four 2-bit values packed into one byte, in a paged KV cache (the abstracts add that the
+kernels keep paged KV-cache layouts and prefix caching). The byte layout inside a page
+is not given anywhere; the one below is this library's, and the oracle packs into the
+same layout so bytes compare directly.
+
+A physical page holds 64 tokens of every KV head. Head h of page p starts at byte
+(p * n_kv_heads + h) * 4608 and holds:
+  [   0, 2048)  K codes, token-major: slot t owns the 32 bytes at 32*t.  Dims are grouped
+                in 16s, one little-endian 32-bit word per group (word w = dims 16w..16w+15);
+                dim 16w + 4m + j sits in byte j of that word at bits 2m..2m+1.
+  [2048, 4096)  V codes, dim-major: dim d owns the 16 bytes at 2048 + 16*d.  Slots are
+                grouped in 16s (word u = slots 16u..16u+15); slot 16u + 4m + j sits in
+                byte j of that word at bits 2m..2m+1.
+  [4096, 4352)  K scale and zero point of slot t: fp16 s at 4096 + 4t, fp16 z at +2.
+  [4352, 4608)  V scale and zero point of slot t, same form at 4352 + 4t.
+History index j of a request lives in logical page j // 64, slot j % 64; the request's
+block table maps logical pages to physical pages.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+PAGE_TOKENS = 64
+HEAD_DIM = 128
+HEAD_BLOCK = 4608
+K_CODES, V_CODES, K_META, V_META = 0, 2048, 4096, 4352
+
+
+def k_code_position(slot: int, dim: int):
+    """(byte offset within the head block, bit shift) of K code (slot, dim)."""
+    w, r = divmod(dim, 16)
+    m, j = divmod(r, 4)
+    return K_CODES + 32 * slot + 4 * w + j, 2 * m
+
+
+def v_code_position(slot: int, dim: int):
+    """(byte offset within the head block, bit shift) of V code (slot, dim)."""
+    u, r = divmod(slot, 16)
+    m, j = divmod(r, 4)
+    return V_CODES + 16 * dim + 4 * u + j, 2 * m
+
+
+def _position_tables():
+    kb = np.zeros((PAGE_TOKENS, HEAD_DIM), np.int64)
+    ks = np.zeros_like(kb)
+    vb = np.zeros_like(kb)
+    vs = np.zeros_like(kb)
+    for t in range(PAGE_TOKENS):
+        for d in range(HEAD_DIM):
+            kb[t, d], ks[t, d] = k_code_position(t, d)
+            vb[t, d], vs[t, d] = v_code_position(t, d)
+    return kb, ks, vb, vs
+
+
+_KB, _KS, _VB, _VS = _position_tables()
+
+
+def new_pool(n_pages: int, n_kv_heads: int) -> np.ndarray:
+    return np.zeros((n_pages, n_kv_heads, HEAD_BLOCK), dtype=np.uint8)
+
+
+def _put_code(block: np.ndarray, byte: np.ndarray, shift: np.ndarray, code: np.ndarray):
+    # codes sharing a byte have different shifts: update one shift at a time
+    for sh in np.unique(shift):
+        sel = shift == sh
+        cur = block[byte[sel]].astype(np.int64)
+        cur &= ~(3 << int(sh))
+        cur |= (code[sel].astype(np.int64) & 3) << int(sh)
+        block[byte[sel]] = cur.astype(np.uint8)
+
+
+def _put_meta(block: np.ndarray, offset: int, s16, z16):
+    block[offset:offset + 2] = np.frombuffer(np.float16(s16).tobytes(), np.uint8)
+    block[offset + 2:offset + 4] = np.frombuffer(np.float16(z16).tobytes(), np.uint8)
+
+
+def write_token(pool: np.ndarray, page: int, slot: int, head: int,
+                k_codes, k_s16, k_z16, v_codes, v_s16, v_z16):
+    """Store one token's K and V codes and metadata for one head."""
+    blk = pool[page, head]
+    _put_code(blk, _KB[slot], _KS[slot], np.asarray(k_codes))
+    _put_code(blk, _VB[slot], _VS[slot], np.asarray(v_codes))
+    _put_meta(blk, K_META + 4 * slot, k_s16, k_z16)
+    _put_meta(blk, V_META + 4 * slot, v_s16, v_z16)
+
+
+def read_token(pool: np.ndarray, page: int, slot: int, head: int):
+    """(k_codes[128], k_s16, k_z16, v_codes[128], v_s16, v_z16) of one token and head."""
+    blk = pool[page, head].astype(np.int64)
+    kc = (blk[_KB[slot]] >> _KS[slot]) & 3
+    vc = (blk[_VB[slot]] >> _VS[slot]) & 3
+    meta = pool[page, head]
+    ks, kz = np.frombuffer(meta[K_META + 4 * slot:K_META + 4 * slot + 4].tobytes(), np.float16)
+    vs, vz = np.frombuffer(meta[V_META + 4 * slot:V_META + 4 * slot + 4].tobytes(), np.float16)
+    return kc.astype(np.uint8), ks, kz, vc.astype(np.uint8), vs, vz
+
+
+def write_history(pool: np.ndarray, table_row: np.ndarray, head: int, start: int,
+                  k_codes, k_s16, k_z16, v_codes, v_s16, v_z16):
+    """Store history entries start, start+1, ... of one request and head."""
+    for i in range(len(k_s16)):
+        j = start + i
+        write_token(pool, int(table_row[j // PAGE_TOKENS]), j % PAGE_TOKENS, head,
+                    k_codes[i], k_s16[i], k_z16[i], v_codes[i], v_s16[i], v_z16[i])
+
+
+def read_history(pool: np.ndarray, table_row: np.ndarray, head: int, n_hist: int):
+    """All n_hist history entries of one request and head, in history order:
+    (k_codes [n,128], k_s16 [n], k_z16 [n], v_codes [n,128], v_s16 [n], v_z16 [n])."""
+    kc = np.zeros((n_hist, HEAD_DIM), np.uint8)
+    vc = np.zeros((n_hist, HEAD_DIM), np.uint8)
+    ks = np.zeros(n_hist, np.float16)
+    kz = np.zeros_like(ks)
+    vs = np.zeros_like(ks)
+    vz = np.zeros_like(ks)
+    for j in range(n_hist):
+        kc[j], ks[j], kz[j], vc[j], vs[j], vz[j] = read_token(
+            pool, int(table_row[j // PAGE_TOKENS]), j % PAGE_TOKENS, head)
+    return kc, ks, kz, vc, vs, vz
+
+
+def history_bytes_per_token_head() -> int:
+    """Bytes one history token costs per KV head: K and V codes plus fp16 (s, z) each."""
+    return 2 * (HEAD_DIM * 2 // 8) + 2 * 4
+
+
+def bf16_bytes_per_token_head() -> int:
+    return 2 * HEAD_DIM * 2
