@@ -1,0 +1,280 @@
+"""Benchmark: one OSCAR decode step (demote the oldest recent token of each request into
+INT2 history, INT2 history pass, BF16 sink/recent pass, merge) on one MI355X.
+
+Workload (default): a Qwen3-8B-shaped attention layer, batch 1, 32,768 tokens of context
+(64 BF16 sink / 32,448 INT2 history / 256 BF16 recent), 32 query heads over 8 KV heads,
+head_dim 128, 64-token pages, seeded synthetic N(0,1) data with per-head outlier channels.
+Steps cycle over `--layers` distinct layer instances (separate device buffers) so every
+step reads its KV pool from HBM, not from the 256 MB last-level cache, as a real model's
+per-layer decode does.
+
+Prints one JSON line. `value` is the whole step's algorithmic HBM bytes divided by its
+time (GB/s); `roofline` reports the dominant kernel (the INT2 history pass) against the
+8 TB/s HBM peak, timed with events on its own stream inside the timed region;
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "INT2 decode attention µs/step + achieved HBM GB/s (% of peak) at 32K–128K ctx"
+HBM_PEAK_GBS = 8000.0
+HIST_BYTES = 72          # per history token per KV head: 2 x 32 B codes + 2 x (fp16 s, fp16 z)
+WIN_BYTES = 512          # per BF16 window token per KV head (K + V)
+ROT_BYTES = 128 * 128 * 2
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2, help="workload config (2: 32K, 3: 100K, 4: B=64, 5: 128K B=4)")
+    p.add_argument("--layers", type=int, default=0, help="layer instances to cycle (0: enough for 512 MB)")
+    p.add_argument("--splits", type=int, default=0, help="INT2 splits (0: library default)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 disables)")
+    return p.parse_args()
+
+
+def step_bytes(w):
+    """Algorithmic bytes of one step: what the method must move, nothing of our workspace."""
+    hist = int(sum(w.hist_lens)) * w.n_kv_heads * HIST_BYTES
+    win = int(sum(w.win_lens)) * w.n_kv_heads * WIN_BYTES
+    rot = 2 * w.n_kv_heads * ROT_BYTES
+    qo = w.batch * w.n_q_heads * 128 * (2 + 4)
+    demote = w.batch * w.n_kv_heads * (2 * 256 + HIST_BYTES)
+    int2 = hist + w.n_kv_heads * ROT_BYTES + w.batch * w.n_q_heads * 256
+    return hist + win + rot + qo + demote, int2
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def oracle_rotations(w, kv):
+    """R_K, R_V of one KV head built by the oracle itself (bf16 values in fp64)."""
+    import synth
+    from oracle import rotation as orot
+
+    if w.calib == "gram":
+        r = orot.round_bf16(orot.rotation_from_covariance(orot.gram_covariance(synth.gram_matrix_source(w, kv))))
+        return r, r
+    q, k, v = synth.calibration_set(w, kv)
+    return (orot.round_bf16(orot.rotation_from_covariance(orot.key_covariance(q))),
+            orot.round_bf16(orot.rotation_from_covariance(orot.value_covariance(q, k, v, w.sm_scale))))
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle, as it stands, on a bounded sample: demote one token of KV head 0 and
+    decode that head's query heads over the full context, repeated until the budget is
+    spent. Reported in the benchmark's unit (algorithmic GB/s)."""
+    import synth
+    from oracle import attention as oatt
+    from oracle import quant as oquant
+
+    kv = 0
+    b = 0
+    r_k, r_v = oracle_rotations(w, kv)
+    rk, rv = {kv: r_k}, {kv: r_v}
+    hk, hv = synth.history_rows(w, b, kv)
+    kc, ks, kz, _ = oquant.quantize_rows(hk.astype(np.float64), rk[kv], w.clip_ratio)
+    vc, vs, vz, _ = oquant.quantize_rows(hv.astype(np.float64), rv[kv], w.clip_ratio)
+    hist = (kc, ks, kz, vc, vs, vz)
+    wk, wv = synth.window_rows(w, b, kv)
+    wk, wv = wk.astype(np.float64), wv.astype(np.float64)
+    q = synth.query(w, b).astype(np.float64)
+    step_k, step_v = hk[-1:].astype(np.float64), hv[-1:].astype(np.float64)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oquant.quantize_rows(step_k, rk[kv], w.clip_ratio)
+        oquant.quantize_rows(step_v, rv[kv], w.clip_ratio)
+        for h in range(kv * w.gq, (kv + 1) * w.gq):
+            oatt.decode_head(q[h], rk[kv], rv[kv], wk, wv, hist, w.sm_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_rep_bytes = (w.hist_len(b) * HIST_BYTES + w.win_len(b) * WIN_BYTES + 2 * ROT_BYTES
+                     + w.gq * 128 * 6 + 2 * 256 + HIST_BYTES)
+    return {
+        "value": round(per_rep_bytes * reps / el / 1e9, 6),
+        "unit": "GB/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"request 0, KV head 0 of {w.n_kv_heads} ({w.gq} query heads) over the full "
+                  f"{w.ctx_lens[0]}-token context: demote one token + decode, {reps} repetitions in {el:.1f} s "
+                  f"(oracle pool built beforehand, untimed)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (the pool shards by KV head "
+              "or request with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from bit_kv_cache_oscar_amd import (oscar_decode_bf16, oscar_decode_int2, oscar_default_splits, oscar_demote,
+                                        oscar_merge)
+    from bit_kv_cache_oscar_amd.layer import LayerCache
+    from bit_kv_cache_oscar_amd.rotation import layer_rotations_from_calibration, layer_rotations_from_gram
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.config)
+    table, n_phys = synth.block_table(w)
+    total_bytes, int2_bytes = step_bytes(w)
+    layers = args.layers or max(2, -(-512 * 2 ** 20 // max(total_bytes, 1)))
+
+    # rotations: the library's host builder from the synthetic calibration data
+    if w.calib == "gram":
+        rk_bits, rv_bits = layer_rotations_from_gram([synth.gram_matrix_source(w, kv) for kv in range(w.n_kv_heads)])
+    else:
+        rk_bits, rv_bits = layer_rotations_from_calibration(
+            [synth.calibration_set(w, kv) for kv in range(w.n_kv_heads)], w.sm_scale)
+
+    base = LayerCache(w.n_q_heads, w.n_kv_heads, w.batch, table.shape[1], n_phys, device=dev)
+    clip = np.full(w.n_kv_heads, w.clip_ratio, np.float32)
+    base.set_rotations(rk_bits, rv_bits, clip, clip)
+    base.set_block_table(table)
+    base.set_hist_len(w.hist_lens)
+    base.set_win_len(w.win_lens)
+    # fill: every history token but the last goes in by bulk demotion; the last one is the
+    # token each timed step demotes from the recent window
+    step_k = torch.zeros((w.batch, w.n_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+    step_v = torch.zeros_like(step_k)
+    step_page = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    step_slot = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    for b in range(w.batch):
+        n = w.hist_len(b)
+        start = min(n, w.shared_pages * 64) if (w.shared_pages and b > 0) else 0
+        ks, vs = [], []
+        for kv in range(w.n_kv_heads):
+            k, v = synth.kv_rows(w, b, kv, 64 + start, 64 + n)
+            ks.append(k)
+            vs.append(v)
+            wk, wv = synth.window_rows(w, b, kv)
+            base.set_window(b, kv, wk, wv)
+        kk = torch.from_numpy(np.stack(ks, 1)).to(dev).to(torch.bfloat16)
+        vv = torch.from_numpy(np.stack(vs, 1)).to(dev).to(torch.bfloat16)
+        j = np.arange(start, n)
+        pg = torch.from_numpy(table[b, j // 64].astype(np.int32)).to(dev)
+        sl = torch.from_numpy((j % 64).astype(np.int32)).to(dev)
+        if n - start > 1:
+            base.demote(kk[:-1], vv[:-1], pg[:-1], sl[:-1])
+        step_k[b], step_v[b] = kk[-1], vv[-1]
+        step_page[b], step_slot[b] = pg[-1], sl[-1]
+    q = torch.from_numpy(np.stack([synth.query(w, b) for b in range(w.batch)])).to(dev).to(torch.bfloat16)
+    splits = args.splits or oscar_default_splits(base.desc, w.batch, int(w.hist_lens.max()))
+    base.set_splits(splits)
+    insts = [base]
+    for _ in range(layers - 1):
+        c = LayerCache(w.n_q_heads, w.n_kv_heads, w.batch, table.shape[1], n_phys, device=dev)
+        for name in ("pool", "block_table", "hist_len", "k_win", "v_win", "win_len", "rot_k", "rot_v", "clip_k",
+                     "clip_v"):
+            getattr(c, name).copy_(getattr(base, name))
+        c.set_splits(splits)
+        insts.append(c)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(c, ev=None):
+        oscar_demote(c.desc, step_k, step_v, step_page, step_slot, c.rot_k, c.rot_v, c.clip_k, c.clip_v, c.pool,
+                     stream)
+        if ev is not None:
+            ev[0].record(stream)
+        oscar_decode_int2(c.desc, q, c.rot_k, c.pool, c.block_table, c.hist_len, w.sm_scale, c.n_splits,
+                          c.partials, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        oscar_decode_bf16(c.desc, q, c.k_win, c.v_win, c.win_len, w.sm_scale, c.win_partials, stream)
+        oscar_merge(c.desc, c.partials, c.n_splits, c.win_partials, c.rot_v, c.out, stream)
+
+    for i in range(args.warmup):
+        step(insts[i % layers])
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(insts[i % layers], evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    int2_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    out = {
+        "metric": METRIC,
+        "value": round(total_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_step": round(ms * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "context_tokens": list(sorted(set(w.ctx_lens)))[:4],
+            "hist_tokens": int(w.hist_lens.max()),
+            "q_heads": w.n_q_heads,
+            "kv_heads": w.n_kv_heads,
+            "head_dim": 128,
+            "page_tokens": 64,
+            "int2_splits": splits,
+            "layer_instances": layers,
+            "step": "demote 1 token/request + INT2 pass + BF16 pass + merge",
+        },
+        "step_bytes": total_bytes,
+        "pct_of_hbm_peak": round(100 * total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+        "context_tokens_per_s": round(sum(w.ctx_lens) / (ms * 1e-3), 1),
+        "roofline": {
+            "kernel": "decode_int2_kernel",
+            "bound": "hbm",
+            "achieved": round(int2_bytes / (int2_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(int2_bytes / (int2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "us_per_launch": round(int2_ms * 1e3, 3),
+            "bytes_per_launch": int2_bytes,
+        },
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

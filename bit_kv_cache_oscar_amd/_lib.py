@@ -1,0 +1,241 @@
+"""ctypes binding of liboscar_kv.so. Each function has the C entry point's name, checks
+that the tensors match the descriptor (the C ABI cannot see tensor shapes), passes raw
+device pointers and the current HIP stream, and raises OscarError on a non-zero status.
+There is no fallback: if the library is missing, every call fails loudly."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_float, c_int32, c_size_t, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboscar_kv.so")
+
+OSCAR_OK = 0
+OSCAR_ERR_INVALID_ARG = 1
+OSCAR_ERR_UNSUPPORTED = 2
+OSCAR_ERR_WORKSPACE = 3
+OSCAR_ERR_HIP = 4
+
+HEAD_DIM = 128
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", c_int32),
+        ("group_size", c_int32),
+        ("page_tokens", c_int32),
+        ("n_q_heads", c_int32),
+        ("n_kv_heads", c_int32),
+        ("sink_tokens", c_int32),
+        ("recent_tokens", c_int32),
+    ]
+
+
+def layer_desc(n_q_heads: int, n_kv_heads: int) -> LayerDesc:
+    return LayerDesc(128, 128, 64, n_q_heads, n_kv_heads, 64, 256)
+
+
+class OscarError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"liboscar_kv status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_SIGNATURES = {
+    "oscar_version": (c_int32, []),
+    "oscar_status_string": (ctypes.c_char_p, [c_int32]),
+    "oscar_last_error": (ctypes.c_char_p, []),
+    "oscar_check_desc": (c_int32, [POINTER(LayerDesc)]),
+    "oscar_page_bytes": (c_size_t, [POINTER(LayerDesc)]),
+    "oscar_window_tokens": (c_int32, [POINTER(LayerDesc)]),
+    "oscar_window_splits": (c_int32, [POINTER(LayerDesc)]),
+    "oscar_partials_bytes": (c_size_t, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_default_splits": (c_int32, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_demote": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "oscar_decode_int2": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                    c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+    "oscar_decode_bf16": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                    c_float, c_void_p, c_size_t, c_void_p]),
+    "oscar_merge": (c_int32, [POINTER(LayerDesc), c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                              c_int32, c_void_p]),
+}
+
+
+def lib():
+    """The loaded library (loaded once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m bit_kv_cache_oscar_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != OSCAR_OK:
+        raise OscarError(status, lib().oscar_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return c_void_p(t)
+    return c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if isinstance(stream, int):
+        return c_void_p(stream)
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return c_void_p(s.cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _device16(t, name):
+    import torch
+
+    _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(t.dtype in (torch.bfloat16, torch.int16, torch.uint16, torch.float16), f"{name} must hold 16-bit values")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _device_i32(t, name, numel=None):
+    import torch
+
+    _need(t.is_cuda and t.dtype == torch.int32 and t.is_contiguous(), f"{name} must be a contiguous int32 device tensor")
+    if numel is not None:
+        _need(t.numel() >= numel, f"{name} holds {t.numel()} < {numel} entries")
+
+
+# ---------------------------------------------------------------------------------- helpers
+
+
+def oscar_version() -> int:
+    return lib().oscar_version()
+
+
+def oscar_status_string(status: int) -> str:
+    return lib().oscar_status_string(status).decode()
+
+
+def oscar_last_error() -> str:
+    return lib().oscar_last_error().decode()
+
+
+def oscar_check_desc(desc: LayerDesc) -> int:
+    return lib().oscar_check_desc(byref(desc))
+
+
+def oscar_page_bytes(desc: LayerDesc) -> int:
+    return lib().oscar_page_bytes(byref(desc))
+
+
+def oscar_window_tokens(desc: LayerDesc) -> int:
+    return lib().oscar_window_tokens(byref(desc))
+
+
+def oscar_window_splits(desc: LayerDesc) -> int:
+    return lib().oscar_window_splits(byref(desc))
+
+
+def oscar_partials_bytes(desc: LayerDesc, batch: int, n_splits: int) -> int:
+    return lib().oscar_partials_bytes(byref(desc), batch, n_splits)
+
+
+def oscar_default_splits(desc: LayerDesc, batch: int, max_hist_len: int) -> int:
+    return lib().oscar_default_splits(byref(desc), batch, max_hist_len)
+
+
+# ------------------------------------------------------------------------------ entry points
+
+
+def oscar_demote(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v, pool,
+                 stream=None):
+    """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16) into (dst_page[i], dst_slot[i])."""
+    n = int(k_src.shape[0]) if k_src.dim() else 0
+    hkv = desc.n_kv_heads
+    _device16(k_src, "k_src")
+    _device16(v_src, "v_src")
+    _need(k_src.numel() == n * hkv * HEAD_DIM and v_src.numel() == n * hkv * HEAD_DIM,
+          "k_src/v_src must be [n, n_kv_heads, 128]")
+    _device_i32(dst_page, "dst_page", n)
+    _device_i32(dst_slot, "dst_slot", n)
+    for t, name in ((rot_k, "rot_k"), (rot_v, "rot_v")):
+        _device16(t, name)
+        _need(t.numel() == hkv * HEAD_DIM * HEAD_DIM, f"{name} must be [n_kv_heads, 128, 128]")
+    for t, name in ((clip_k, "clip_k"), (clip_v, "clip_v")):
+        _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
+              f"{name} must be float32 [n_kv_heads] on the device")
+    _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
+    _check(lib().oscar_demote(byref(desc), _ptr(k_src), _ptr(v_src), n, _ptr(dst_page), _ptr(dst_slot),
+                              _ptr(rot_k), _ptr(rot_v), _ptr(clip_k), _ptr(clip_v), _ptr(pool),
+                              _stream(stream)))
+
+
+def oscar_decode_int2(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm_scale: float, n_splits: int,
+                      partials, stream=None):
+    """INT2 history pass; q [B, Hq, 128] bf16, block_table [B, max_pages] int32,
+    hist_len [B] int32; partials from oscar_partials_bytes(desc, B, n_splits)."""
+    batch = int(q.shape[0])
+    _device16(q, "q")
+    _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
+    _device16(rot_k, "rot_k")
+    _need(rot_k.numel() == desc.n_kv_heads * HEAD_DIM * HEAD_DIM, "rot_k must be [n_kv_heads, 128, 128]")
+    _need(block_table.dim() == 2 and block_table.shape[0] == batch, "block_table must be [batch, max_pages]")
+    _device_i32(block_table, "block_table")
+    _device_i32(hist_len, "hist_len", batch)
+    _need(pool.is_cuda, "pool must be on the device")
+    _need(partials.is_cuda and partials.is_contiguous(), "partials must be a contiguous device tensor")
+    nbytes = partials.numel() * partials.element_size()
+    _check(lib().oscar_decode_int2(byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool), _ptr(block_table),
+                                   int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale),
+                                   int(n_splits), _ptr(partials), nbytes, _stream(stream)))
+
+
+def oscar_decode_bf16(desc: LayerDesc, q, k_win, v_win, win_len, sm_scale: float, win_partials, stream=None):
+    """BF16 window pass; k_win/v_win [B, Hkv, 320, 128] bf16, win_len [B] int32."""
+    batch = int(q.shape[0])
+    _device16(q, "q")
+    _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
+    w = desc.sink_tokens + desc.recent_tokens
+    for t, name in ((k_win, "k_win"), (v_win, "v_win")):
+        _device16(t, name)
+        _need(t.numel() == batch * desc.n_kv_heads * w * HEAD_DIM, f"{name} must be [batch, n_kv_heads, {w}, 128]")
+    _device_i32(win_len, "win_len", batch)
+    _need(win_partials.is_cuda and win_partials.is_contiguous(), "win_partials must be a contiguous device tensor")
+    nbytes = win_partials.numel() * win_partials.element_size()
+    _check(lib().oscar_decode_bf16(byref(desc), _ptr(q), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch,
+                                   float(sm_scale), _ptr(win_partials), nbytes, _stream(stream)))
+
+
+def oscar_merge(desc: LayerDesc, partials, n_splits: int, win_partials, rot_v, out, stream=None):
+    """Join both segments into out [B, Hq, 128] float32."""
+    import torch
+
+    batch = int(out.shape[0])
+    _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous(), "out must be contiguous float32")
+    _need(out.numel() == batch * desc.n_q_heads * HEAD_DIM, "out must be [batch, n_q_heads, 128]")
+    _device16(rot_v, "rot_v")
+    _need(rot_v.numel() == desc.n_kv_heads * HEAD_DIM * HEAD_DIM, "rot_v must be [n_kv_heads, 128, 128]")
+    need = oscar_partials_bytes(desc, batch, n_splits)
+    _need(partials.numel() * partials.element_size() >= need, "partials smaller than oscar_partials_bytes")
+    wneed = oscar_partials_bytes(desc, batch, oscar_window_splits(desc))
+    _need(win_partials.numel() * win_partials.element_size() >= wneed, "win_partials too small")
+    _check(lib().oscar_merge(byref(desc), _ptr(partials), int(n_splits), _ptr(win_partials), _ptr(rot_v),
+                             _ptr(out), batch, _stream(stream)))

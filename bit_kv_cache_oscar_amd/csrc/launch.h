@@ -1,0 +1,45 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oscar {
+
+struct LayerShape {
+  int n_q;       // query heads
+  int n_kv;      // KV heads
+  int gq;        // query heads per KV head
+  int window;    // BF16 window slots per request and KV head
+};
+
+// Offsets (in floats) of the m, l and acc arrays of a partial-result workspace.
+struct PartialsView {
+  float* m;
+  float* l;
+  float* acc;
+};
+
+size_t partials_bytes(int batch, int n_q, int n_splits);
+PartialsView partials_view(void* base, int batch, int n_q, int n_splits);
+
+hipError_t launch_demote_rows(const LayerShape& L, const void* k_src, const void* v_src, int n,
+                              const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k,
+                              const void* rot_v, const float* clip_k, const float* clip_v, void* pool,
+                              hipStream_t stream);
+
+hipError_t launch_decode_int2(const LayerShape& L, const void* q, const void* rot_k, const void* pool,
+                              const int32_t* block_table, int max_pages, const int32_t* hist_len,
+                              int batch, float sm_scale, int n_splits, const PartialsView& out,
+                              hipStream_t stream);
+
+hipError_t launch_decode_bf16(const LayerShape& L, const void* q, const void* k_win, const void* v_win,
+                              const int32_t* win_len, int batch, float sm_scale, int n_win_splits,
+                              const PartialsView& out, hipStream_t stream);
+
+hipError_t launch_merge(const LayerShape& L, const PartialsView& hist, int n_splits,
+                        const PartialsView& win, int n_win_splits, const void* rot_v, float* out,
+                        int batch, hipStream_t stream);
+
+}  // namespace oscar

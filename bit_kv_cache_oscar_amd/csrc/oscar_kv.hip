@@ -1,0 +1,214 @@
+// C-ABI entry points of liboscar_kv: host-side validation, workspace views and launches.
+// No allocation, no synchronisation, no state beyond a per-thread error message.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "launch.h"
+#include "oscar_kv.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_last_error[0] = '\0';
+  return OSCAR_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(OSCAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t check_desc_impl(const oscar_layer_desc* d) {
+  if (!d) return fail(OSCAR_ERR_INVALID_ARG, "desc is null");
+  if (d->head_dim != 128) return fail(OSCAR_ERR_UNSUPPORTED, "head_dim %d != 128", d->head_dim);
+  if (d->group_size != 128) return fail(OSCAR_ERR_UNSUPPORTED, "group_size %d != 128", d->group_size);
+  if (d->page_tokens != 64) return fail(OSCAR_ERR_UNSUPPORTED, "page_tokens %d != 64", d->page_tokens);
+  if (d->sink_tokens != 64) return fail(OSCAR_ERR_UNSUPPORTED, "sink_tokens %d != 64", d->sink_tokens);
+  if (d->recent_tokens != 256) return fail(OSCAR_ERR_UNSUPPORTED, "recent_tokens %d != 256", d->recent_tokens);
+  if (d->n_q_heads <= 0 || d->n_kv_heads <= 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "head counts must be positive (%d, %d)", d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "n_q_heads %d not a multiple of n_kv_heads %d", d->n_q_heads, d->n_kv_heads);
+  const int gq = d->n_q_heads / d->n_kv_heads;
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+    return fail(OSCAR_ERR_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8,16}", gq);
+  if (d->n_kv_heads > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "n_kv_heads %d too large", d->n_kv_heads);
+  return OSCAR_OK;
+}
+
+oscar::LayerShape shape_of(const oscar_layer_desc* d) {
+  oscar::LayerShape s;
+  s.n_q = d->n_q_heads;
+  s.n_kv = d->n_kv_heads;
+  s.gq = d->n_q_heads / d->n_kv_heads;
+  s.window = d->sink_tokens + d->recent_tokens;
+  return s;
+}
+
+int window_splits_of(const oscar_layer_desc* d) { return (d->sink_tokens + d->recent_tokens + 63) / 64; }
+
+}  // namespace
+
+namespace oscar {
+
+size_t partials_bytes(int batch, int n_q, int n_splits) {
+  const size_t n = static_cast<size_t>(batch) * n_q * n_splits;
+  const size_t acc_off = (8 * n + 255) / 256 * 256;
+  return acc_off + n * 128 * sizeof(float);
+}
+
+PartialsView partials_view(void* base, int batch, int n_q, int n_splits) {
+  const size_t n = static_cast<size_t>(batch) * n_q * n_splits;
+  const size_t acc_off = (8 * n + 255) / 256 * 256;
+  char* p = static_cast<char*>(base);
+  PartialsView v;
+  v.m = reinterpret_cast<float*>(p);
+  v.l = reinterpret_cast<float*>(p + 4 * n);
+  v.acc = reinterpret_cast<float*>(p + acc_off);
+  return v;
+}
+
+}  // namespace oscar
+
+extern "C" {
+
+int32_t oscar_version(void) { return 100; }
+
+const char* oscar_status_string(int32_t status) {
+  switch (status) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_ERR_INVALID_ARG: return "invalid argument";
+    case OSCAR_ERR_UNSUPPORTED: return "unsupported shape";
+    case OSCAR_ERR_WORKSPACE: return "workspace too small";
+    case OSCAR_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* oscar_last_error(void) { return g_last_error; }
+
+int32_t oscar_check_desc(const oscar_layer_desc* desc) {
+  const int32_t st = check_desc_impl(desc);
+  return st == OSCAR_OK ? ok() : st;
+}
+
+size_t oscar_page_bytes(const oscar_layer_desc* desc) {
+  if (check_desc_impl(desc) != OSCAR_OK) return 0;
+  return static_cast<size_t>(desc->n_kv_heads) * 4608;
+}
+
+int32_t oscar_window_tokens(const oscar_layer_desc* desc) {
+  if (check_desc_impl(desc) != OSCAR_OK) return 0;
+  return desc->sink_tokens + desc->recent_tokens;
+}
+
+int32_t oscar_window_splits(const oscar_layer_desc* desc) {
+  if (check_desc_impl(desc) != OSCAR_OK) return 0;
+  return window_splits_of(desc);
+}
+
+size_t oscar_partials_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
+  return oscar::partials_bytes(batch, desc->n_q_heads, n_splits);
+}
+
+int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0) return 1;
+  const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
+  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads;
+  long long s = (2048 + groups - 1) / groups;  // about 8 workgroups per compute unit
+  const long long by_pages = (pages + 7) / 8;  // at least 8 pages (two per wave) per split
+  if (s > by_pages) s = by_pages;
+  if (s < 1) s = 1;
+  if (s > 65535) s = 65535;
+  return static_cast<int32_t>(s);
+}
+
+int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                     const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                     const float* clip_k, const float* clip_v, void* pool, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (n < 0) return fail(OSCAR_ERR_INVALID_ARG, "n %d < 0", n);
+  if (n == 0) return ok();
+  if (!k_src || !v_src || !dst_page || !dst_slot || !rot_k || !rot_v || !clip_k || !clip_v || !pool)
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (static_cast<long long>(n) * desc->n_kv_heads > 0x7FFFFFFFLL)
+    return fail(OSCAR_ERR_UNSUPPORTED, "n * n_kv_heads exceeds the grid limit");
+  const oscar::LayerShape L = shape_of(desc);
+  return hip_status(oscar::launch_demote_rows(L, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v,
+                                              pool, static_cast<hipStream_t>(stream)),
+                    "demote launch");
+}
+
+int32_t oscar_decode_int2(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* pool,
+                          const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, int32_t batch,
+                          float sm_scale, int32_t n_splits, void* partials, size_t partials_bytes, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (n_splits <= 0 || n_splits > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d out of [1, 65535]", n_splits);
+  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (!q || !rot_k || !pool || !block_table || !hist_len || !partials)
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const size_t need = oscar::partials_bytes(batch, desc->n_q_heads, n_splits);
+  if (partials_bytes < need)
+    return fail(OSCAR_ERR_WORKSPACE, "partials workspace %zu < %zu bytes", partials_bytes, need);
+  const oscar::LayerShape L = shape_of(desc);
+  const oscar::PartialsView v = oscar::partials_view(partials, batch, desc->n_q_heads, n_splits);
+  return hip_status(oscar::launch_decode_int2(L, q, rot_k, pool, block_table, max_pages, hist_len, batch, sm_scale,
+                                              n_splits, v, static_cast<hipStream_t>(stream)),
+                    "decode_int2 launch");
+}
+
+int32_t oscar_decode_bf16(const oscar_layer_desc* desc, const void* q, const void* k_win, const void* v_win,
+                          const int32_t* win_len, int32_t batch, float sm_scale, void* win_partials,
+                          size_t win_partials_bytes, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (!q || !k_win || !v_win || !win_len || !win_partials) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const int ws = window_splits_of(desc);
+  const size_t need = oscar::partials_bytes(batch, desc->n_q_heads, ws);
+  if (win_partials_bytes < need)
+    return fail(OSCAR_ERR_WORKSPACE, "window partials workspace %zu < %zu bytes", win_partials_bytes, need);
+  const oscar::LayerShape L = shape_of(desc);
+  const oscar::PartialsView v = oscar::partials_view(win_partials, batch, desc->n_q_heads, ws);
+  return hip_status(oscar::launch_decode_bf16(L, q, k_win, v_win, win_len, batch, sm_scale, ws, v,
+                                              static_cast<hipStream_t>(stream)),
+                    "decode_bf16 launch");
+}
+
+int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t n_splits, const void* win_partials,
+                    const void* rot_v, float* out, int32_t batch, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (n_splits <= 0 || n_splits > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d out of [1, 65535]", n_splits);
+  if (!partials || !win_partials || !rot_v || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  const oscar::LayerShape L = shape_of(desc);
+  const int ws = window_splits_of(desc);
+  // the const casts only build read views; merge never writes a workspace
+  const oscar::PartialsView h = oscar::partials_view(const_cast<void*>(partials), batch, desc->n_q_heads, n_splits);
+  const oscar::PartialsView w = oscar::partials_view(const_cast<void*>(win_partials), batch, desc->n_q_heads, ws);
+  return hip_status(oscar::launch_merge(L, h, n_splits, w, ws, rot_v, out, batch, static_cast<hipStream_t>(stream)),
+                    "merge launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+/*
+ * liboscar_kv: the OSCAR INT2 KV-cache hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method (OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache
+ * Quantization) keeps a three-segment token pool per request and KV head: a BF16 sink of
+ * 64 tokens, an INT2 history, and a BF16 recent window of 256 tokens (QbitAI article on
+ * OSCAR, serving-path section). Tokens leaving the recent window are rotated by a fixed
+ * per-layer, per-KV-head orthogonal R = U * Hadamard * bit-reversal (same article, section
+ * on aiming the rotation at attention), clipped, quantised to 2 bits with a per-group
+ * scale and zero point and packed four codes per byte. Decode processes the INT2 history
+ * and the BF16 sink/recent separately and joins them with an online-softmax merge.
+ *
+ * Conventions for every entry point:
+ *   - Plain C ABI. All tensor pointers are DEVICE pointers unless marked host. The caller
+ *     owns every buffer; the library allocates nothing and keeps no state.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and returns
+ *     without synchronising. Calls on different streams may run concurrently when they
+ *     write disjoint memory.
+ *   - Arguments are validated on the host before any HIP call; a failed check returns a
+ *     status and enqueues nothing. Device-resident values (page ids, lengths, slots) are
+ *     trusted: out-of-range values are undefined behaviour.
+ *   - bf16 and fp16 tensors are passed as raw 16-bit storage (`const void*`).
+ *   - Vectors are rows; rotating is y = x R (R row-major [128][128]); un-rotating is y R^T.
+ *   - Each failing call also records a message, readable with oscar_last_error() on the
+ *     same host thread.
+ *
+ * Fixed shapes: head_dim = group_size = 128, page_tokens = 64, sink_tokens = 64,
+ * recent_tokens = 256; n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}; query head h uses KV
+ * head h / (n_q_heads / n_kv_heads).
+ *
+ * INT2 pool layout (4608 bytes per page per KV head, head h of physical page p at byte
+ * (p * n_kv_heads + h) * 4608):
+ *   [   0, 2048)  K codes, token-major: slot t at 32 t; 32-bit word w holds dims 16w..16w+15,
+ *                 dim 16w + 4m + j in byte j, bits 2m..2m+1.
+ *   [2048, 4096)  V codes, dim-major: dim d at 2048 + 16 d; word u holds slots 16u..16u+15,
+ *                 slot 16u + 4m + j in byte j, bits 2m..2m+1.
+ *   [4096, 4352)  K fp16 scale s and zero point z of slot t at 4096 + 4 t (s first).
+ *   [4352, 4608)  V fp16 scale and zero point of slot t at 4352 + 4 t.
+ * A code q stands for q * s + z in the rotated basis. History entry j of a request lives in
+ * slot j % 64 of physical page block_table[b * max_pages + j / 64].
+ *
+ * Partial-result workspace (online-softmax state of one segment split): for B requests,
+ * Hq query heads and S splits, a buffer of oscar_partials_bytes(desc, B, S) bytes holding
+ *   float m[B][Hq][S]     running maximum of the scores, in log2 units (score * log2 e)
+ *   float l[B][Hq][S]     sum of 2^(score*log2e - m)
+ *   float acc[B][Hq][S][128]  sum of 2^(score*log2e - m) * value
+ * with m at byte 0, l at byte 4*B*Hq*S and acc at the next multiple of 256 bytes. An
+ * empty split holds m = -inf, l = 0, acc = 0. INT2 partials hold acc in the rotated basis.
+ */
+#ifndef OSCAR_KV_H
+#define OSCAR_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum oscar_status {
+  OSCAR_OK = 0,
+  OSCAR_ERR_INVALID_ARG = 1, /* null pointer, bad count or inconsistent shape */
+  OSCAR_ERR_UNSUPPORTED = 2, /* a shape outside the fixed set above */
+  OSCAR_ERR_WORKSPACE = 3,   /* workspace smaller than the size helper reports */
+  OSCAR_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} oscar_status;
+
+typedef struct oscar_layer_desc {
+  int32_t head_dim;      /* must be 128 */
+  int32_t group_size;    /* quantisation group, must be 128 (one group per vector) */
+  int32_t page_tokens;   /* must be 64 */
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t sink_tokens;   /* must be 64 */
+  int32_t recent_tokens; /* must be 256 */
+} oscar_layer_desc;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t oscar_version(void);
+
+/* Static text for a status code. */
+const char* oscar_status_string(int32_t status);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* oscar_last_error(void);
+
+/* Checks a descriptor; OSCAR_OK if every entry point accepts it. */
+int32_t oscar_check_desc(const oscar_layer_desc* desc);
+
+/* Bytes of one physical page (all KV heads): n_kv_heads * 4608. 0 for a bad desc. */
+size_t oscar_page_bytes(const oscar_layer_desc* desc);
+
+/* BF16 window slots per request and KV head: sink_tokens + recent_tokens. */
+int32_t oscar_window_tokens(const oscar_layer_desc* desc);
+
+/* Splits oscar_decode_bf16 produces per (request, query head): window_tokens / 64, rounded up. */
+int32_t oscar_window_splits(const oscar_layer_desc* desc);
+
+/* Bytes of a partial-result workspace for `batch` requests and `n_splits` splits. */
+size_t oscar_partials_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits);
+
+/* A split count that fills the GPU for this batch and longest history (>= 1). */
+int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len);
+
+/*
+ * oscar_demote: move tokens from the BF16 recent window into INT2 history.
+ * (QbitAI article on OSCAR, serving-path section: the oldest recent token is rotated,
+ * clipped, quantised and packed, then stored in the INT2 history; abstracts: the
+ * rotations and clipping thresholds are fixed per layer and derived offline.)
+ *
+ * For each token i < n and KV head h, and separately for K and V with their own R and c:
+ *   y = x R, with x the bf16 row; the group extremes are taken on the exact products
+ *   hi = c * max(y), lo = c * min(y)                         (fp64)
+ *   s = fp16((hi - lo) / 3), z = fp16(lo)                    (round to nearest even)
+ *   q_j = clamp(round_half_even((y_j - z) / s), 0, 3); all codes 0 when s == 0
+ * and stores the codes, s and z at (dst_page[i], dst_slot[i]) of head h in the pool,
+ * leaving every other slot's bits untouched.
+ *
+ *   k_src, v_src   bf16 [n][n_kv_heads][128], the rows to demote (unrotated)
+ *   dst_page       int32 [n], physical page of token i
+ *   dst_slot       int32 [n], slot 0..63 of token i
+ *   rot_k, rot_v   bf16 [n_kv_heads][128][128], per-head rotations
+ *   clip_k, clip_v float32 [n_kv_heads], clip ratios c in (0, 1]
+ *   pool           the INT2 pool (layout above), written in place
+ * Two tokens of one call must not share a (page, slot). n == 0 is a no-op.
+ */
+int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void* v_src,
+                     int32_t n, const int32_t* dst_page, const int32_t* dst_slot,
+                     const void* rot_k, const void* rot_v, const float* clip_k,
+                     const float* clip_v, void* pool, void* stream);
+
+/*
+ * oscar_decode_int2: the INT2 history pass of decode attention.
+ * (QbitAI article on OSCAR, serving-path section: the INT2 kernel unpacks, dequantises
+ * with the scale and zero point and accumulates in floating point; the history is paged.)
+ *
+ * For request b and query head h (KV head kv): q_rot = q R_K[kv]; each history entry j
+ * scores sm_scale * q_rot . (q_j * s_j + z_j); the history of b is cut into n_splits
+ * contiguous page ranges and one online-softmax partial (m, l, acc in the rotated V basis)
+ * is written per (b, h, split).
+ *
+ *   q            bf16 [batch][n_q_heads][128], the raw (unrotated) queries
+ *   rot_k        bf16 [n_kv_heads][128][128]
+ *   pool         INT2 pool
+ *   block_table  int32 [batch][max_pages]
+ *   hist_len     int32 [batch], history entries per request (0 allowed)
+ *   sm_scale     softmax scale applied to q . k (e.g. 1/sqrt(128) as a float)
+ *   partials     workspace of at least oscar_partials_bytes(desc, batch, n_splits) bytes
+ */
+int32_t oscar_decode_int2(const oscar_layer_desc* desc, const void* q, const void* rot_k,
+                          const void* pool, const int32_t* block_table, int32_t max_pages,
+                          const int32_t* hist_len, int32_t batch, float sm_scale,
+                          int32_t n_splits, void* partials, size_t partials_bytes, void* stream);
+
+/*
+ * oscar_decode_bf16: the BF16 sink/recent pass of decode attention.
+ * (QbitAI article on OSCAR, serving-path section: a BF16 kernel handles sink and recent.)
+ *
+ * Window slots [0, win_len[b]) of each request hold raw bf16 K/V rows (the sink, then
+ * the recent tokens; order does not matter to attention). Writes oscar_window_splits(desc)
+ * partials per (b, h), split c covering slots [64 c, 64 c + 64).
+ *
+ *   k_win, v_win  bf16 [batch][n_kv_heads][window_tokens][128]
+ *   win_len       int32 [batch], 0..window_tokens
+ *   win_partials  workspace of at least oscar_partials_bytes(desc, batch, window_splits)
+ */
+int32_t oscar_decode_bf16(const oscar_layer_desc* desc, const void* q, const void* k_win,
+                          const void* v_win, const int32_t* win_len, int32_t batch,
+                          float sm_scale, void* win_partials, size_t win_partials_bytes,
+                          void* stream);
+
+/*
+ * oscar_merge: join the INT2 and BF16 segments.
+ * (QbitAI article on OSCAR, serving-path section: the two parts are combined by an
+ * online-softmax merge.)
+ *
+ * Reduces the n_splits INT2 partials of (b, h), un-rotates their value sum by R_V^T,
+ * reduces the window partials, and writes
+ *   out = (a acc_int2 R_V^T + w acc_win) / (a l_int2 + w l_win),
+ * a = 2^(m_int2 - M), w = 2^(m_win - M), M = max of the two; 0 if both segments are empty.
+ *
+ *   partials      from oscar_decode_int2 with the same n_splits
+ *   win_partials  from oscar_decode_bf16
+ *   rot_v         bf16 [n_kv_heads][128][128]
+ *   out           float32 [batch][n_q_heads][128]
+ */
+int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t n_splits,
+                    const void* win_partials, const void* rot_v, float* out, int32_t batch,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_KV_H */

@@ -130,3 +130,52 @@ def history_bytes_per_token_head() -> int:
 
 def bf16_bytes_per_token_head() -> int:
     return 2 * HEAD_DIM * 2
+
+
+def pack_page(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16) -> np.ndarray:
+    """One head's 4608-byte block for a page of up to 64 tokens (missing slots zero).
+    Codes [n,128] uint8, scales/zeros [n] float16."""
+    n = len(k_s16)
+    assert n <= PAGE_TOKENS
+    blk = np.zeros(HEAD_BLOCK, dtype=np.uint8)
+    kc = np.zeros((PAGE_TOKENS, HEAD_DIM), np.int64)
+    vc = np.zeros((PAGE_TOKENS, HEAD_DIM), np.int64)
+    kc[:n] = k_codes
+    vc[:n] = v_codes
+    for table_b, table_s, codes in ((_KB, _KS, kc), (_VB, _VS, vc)):
+        for sh in (0, 2, 4, 6):
+            sel = table_s == sh      # within one shift every byte appears once
+            blk[table_b[sel]] |= (codes[sel] << sh).astype(np.uint8)
+    meta = np.zeros((2, PAGE_TOKENS, 2), np.float16)
+    meta[0, :n, 0], meta[0, :n, 1] = k_s16, k_z16
+    meta[1, :n, 0], meta[1, :n, 1] = v_s16, v_z16
+    blk[K_META:V_META] = meta[0].reshape(-1).view(np.uint8)
+    blk[V_META:HEAD_BLOCK] = meta[1].reshape(-1).view(np.uint8)
+    return blk
+
+
+def unpack_page(blk: np.ndarray):
+    """(k_codes [64,128], k_s16 [64], k_z16 [64], v_codes, v_s16, v_z16) of one block."""
+    b = np.asarray(blk, dtype=np.uint8).astype(np.int64)
+    kc = ((b[_KB] >> _KS) & 3).astype(np.uint8)
+    vc = ((b[_VB] >> _VS) & 3).astype(np.uint8)
+    km = np.asarray(blk[K_META:V_META], np.uint8).view(np.float16).reshape(PAGE_TOKENS, 2)
+    vm = np.asarray(blk[V_META:HEAD_BLOCK], np.uint8).view(np.float16).reshape(PAGE_TOKENS, 2)
+    return kc, km[:, 0].copy(), km[:, 1].copy(), vc, vm[:, 0].copy(), vm[:, 1].copy()
+
+
+def pack_history(pool: np.ndarray, table_row: np.ndarray, head: int, hist):
+    """Write a whole history (entries 0..n-1, page by page) of one request and head."""
+    kc, ks, kz, vc, vs, vz = hist
+    n = len(ks)
+    for p in range(-(-n // PAGE_TOKENS)):
+        a, z = p * PAGE_TOKENS, min(n, (p + 1) * PAGE_TOKENS)
+        pool[int(table_row[p]), head] = pack_page(kc[a:z], ks[a:z], kz[a:z], vc[a:z], vs[a:z], vz[a:z])
+
+
+def unpack_history(pool: np.ndarray, table_row: np.ndarray, head: int, n_hist: int):
+    """Inverse of pack_history for the first n_hist entries."""
+    parts = [unpack_page(pool[int(table_row[p]), head]) for p in range(-(-n_hist // PAGE_TOKENS))]
+    if not parts:
+        return read_history(pool, table_row, head, 0)
+    return tuple(np.concatenate([pt[i] for pt in parts])[:n_hist] for i in range(6))

@@ -38,6 +38,12 @@ N_LEVELS = 4
 BOUNDARIES = np.array([0.5, 1.5, 2.5])
 
 
+def boundary_distance(t: np.ndarray) -> np.ndarray:
+    """Distance from t to the nearest rounding boundary between levels (0.5, 1.5, 2.5)."""
+    nearest = np.rint(np.clip(t, 0.5, 2.5) - 0.5) + 0.5
+    return np.abs(t - nearest)
+
+
 def fp32(x: float) -> float:
     """The float32 nearest to x, as a Python float (exact)."""
     return float(np.float32(x))
@@ -61,6 +67,15 @@ def exact_dot(x_row: np.ndarray, r_col: np.ndarray) -> float:
     return math.fsum((x_row * r_col).tolist())
 
 
+def exact_dots(x: np.ndarray, rt: np.ndarray, ii: np.ndarray, jj: np.ndarray) -> np.ndarray:
+    """Correctly rounded x[i] . rt[j] for every pair (ii[k], jj[k]) via math.fsum."""
+    out = np.empty(len(ii))
+    for a in range(0, len(ii), 1 << 15):
+        prods = x[ii[a:a + (1 << 15)]] * rt[jj[a:a + (1 << 15)]]   # exact: bf16 x bf16
+        out[a:a + len(prods)] = list(map(math.fsum, prods.tolist()))
+    return out
+
+
 def exact_rotation(x: np.ndarray, r: np.ndarray) -> np.ndarray:
     """Every y_ij by math.fsum (slow; for small inputs and cross-checks)."""
     out = np.empty((x.shape[0], r.shape[1]))
@@ -81,15 +96,19 @@ def quantize_rows(x: np.ndarray, r: np.ndarray, clip: float):
     r = np.asarray(r, dtype=np.float64)
     c = fp32(clip)
     n = x.shape[0]
+    rt = np.ascontiguousarray(r.T)
     y, bound = rotate_with_bound(x, r)
 
-    ymax = np.empty(n)
-    ymin = np.empty(n)
-    for i in range(n):
-        top = np.nonzero(y[i] + bound[i] >= np.max(y[i] - bound[i]))[0]
-        bot = np.nonzero(y[i] - bound[i] <= np.min(y[i] + bound[i]))[0]
-        ymax[i] = max(exact_dot(x[i], r[:, j]) for j in top)
-        ymin[i] = min(exact_dot(x[i], r[:, j]) for j in bot)
+    # extremes: every entry whose bound interval reaches the largest (smallest) lower
+    # (upper) bound may be the extreme; take the exact maximum (minimum) over those
+    ymax = np.full(n, -np.inf)
+    ymin = np.full(n, np.inf)
+    top = y + bound >= (y - bound).max(axis=1, keepdims=True)
+    bot = y - bound <= (y + bound).min(axis=1, keepdims=True)
+    ii, jj = np.nonzero(top)
+    np.maximum.at(ymax, ii, exact_dots(x, rt, ii, jj))
+    ii, jj = np.nonzero(bot)
+    np.minimum.at(ymin, ii, exact_dots(x, rt, ii, jj))
 
     hi = c * ymax
     lo = c * ymin
@@ -104,14 +123,14 @@ def quantize_rows(x: np.ndarray, r: np.ndarray, clip: float):
     safe_s = np.where(zero_scale, 1.0, s64)
 
     t = (y - z64) / safe_s
-    near = np.abs(t[..., None] - BOUNDARIES).min(axis=-1) <= bound / safe_s * 4.0 + 1e-12
+    near = boundary_distance(t) <= bound / safe_s * 4.0 + 1e-12
     near &= ~zero_scale
-    for i, j in zip(*np.nonzero(near)):
-        t[i, j] = (exact_dot(x[i], r[:, j]) - z64[i, 0]) / safe_s[i, 0]
+    ii, jj = np.nonzero(near)
+    t[ii, jj] = (exact_dots(x, rt, ii, jj) - z64[ii, 0]) / safe_s[ii, 0]
 
     codes = np.clip(np.rint(t), 0, N_LEVELS - 1)
     codes = np.where(zero_scale, 0, codes).astype(np.uint8)
-    margin = np.abs(t[..., None] - BOUNDARIES).min(axis=-1)
+    margin = boundary_distance(t)
     margin = np.where(zero_scale, np.inf, margin)
     return codes, s16, z16, margin
 

@@ -172,6 +172,24 @@ def _normal(g: np.random.Generator, n: int) -> np.ndarray:
 # per-request data
 
 
+ROW_CHUNK = 4096  # positions per independent random stream
+
+
+def _rows(stream: int, w: Workload, who: int, kv: int, start: int, stop: int) -> np.ndarray:
+    """N(0,1) float32 rows for absolute positions [start, stop) of stream `who`. Each block
+    of ROW_CHUNK positions has its own generator, so any sub-range is cheap and identical
+    however it is requested."""
+    out = np.empty((stop - start, HEAD_DIM), np.float32)
+    c = start // ROW_CHUNK
+    while c * ROW_CHUNK < stop:
+        lo, hi = c * ROW_CHUNK, (c + 1) * ROW_CHUNK
+        blk = _normal(rng(w.seed, w.cfg, stream, who, kv, c), ROW_CHUNK)
+        a, z = max(lo, start), min(hi, stop)
+        out[a - start:z - start] = blk[a - lo:z - lo]
+        c += 1
+    return out
+
+
 def kv_rows(w: Workload, b: int, kv: int, start: int = 0, stop: Optional[int] = None):
     """bf16-valued float32 K and V rows [stop-start, 128] for positions [start, stop) of
     request b, KV head kv. Positions below the shared prefix come from a stream common to
@@ -182,19 +200,12 @@ def kv_rows(w: Workload, b: int, kv: int, start: int = 0, stop: Optional[int] = 
     kq_ch, kf, _, v_ch, vf = outliers(w, kv)
     sp = w.shared_prefix if w.batch > 1 else 0
     parts_k, parts_v = [], []
-    for lo, hi, who in ((0, min(sp, L), SHARED), (min(sp, L), L, b)):
-        if hi <= lo:
-            continue
+    for lo, hi, who in ((0, sp, SHARED), (sp, L, b)):
         a, z = max(lo, start), min(hi, stop)
         if z <= a:
             continue
-        gk = rng(w.seed, w.cfg, _S_K, who, kv)
-        gv = rng(w.seed, w.cfg, _S_V, who, kv)
-        # draw the whole segment so that any sub-range is reproducible
-        k = _normal(gk, hi - lo)[a - lo:z - lo]
-        v = _normal(gv, hi - lo)[a - lo:z - lo]
-        parts_k.append(_scaled(k, kq_ch, kf))
-        parts_v.append(_scaled(v, v_ch, vf))
+        parts_k.append(_scaled(_rows(_S_K, w, who, kv, a, z), kq_ch, kf))
+        parts_v.append(_scaled(_rows(_S_V, w, who, kv, a, z), v_ch, vf))
     if not parts_k:
         e = np.zeros((0, HEAD_DIM), np.float32)
         return e, e.copy()
@@ -216,9 +227,9 @@ def window_rows(w: Workload, b: int, kv: int):
     """K and V [win_len, 128] of the BF16 window of request b: the sink then the recent
     tokens, in position order."""
     L = w.ctx_lens[b]
-    k, v = kv_rows(w, b, kv)
-    idx = np.r_[0:min(L, SINK_TOKENS), max(SINK_TOKENS, L - RECENT_TOKENS):L]
-    return k[idx], v[idx]
+    k0, v0 = kv_rows(w, b, kv, 0, min(L, SINK_TOKENS))
+    k1, v1 = kv_rows(w, b, kv, max(min(L, SINK_TOKENS), L - RECENT_TOKENS), L)
+    return np.concatenate([k0, k1]), np.concatenate([v0, v1])
 
 
 def history_rows(w: Workload, b: int, kv: int):

@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and rejects
+bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_kv_cache_oscar_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "oscar_kv.h")
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("liboscar_kv.so is not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(L._SIGNATURES) == set(names)
+
+
+def test_helpers(lib):
+    d = L.layer_desc(32, 8)
+    assert L.oscar_version() >= 100
+    assert L.oscar_check_desc(d) == L.OSCAR_OK
+    assert L.oscar_page_bytes(d) == 8 * 4608
+    assert L.oscar_window_tokens(d) == 320
+    assert L.oscar_window_splits(d) == 5
+    n = 2 * 32 * 7
+    acc_off = -(-8 * n // 256) * 256
+    assert L.oscar_partials_bytes(d, 2, 7) == acc_off + n * 512
+    s = L.oscar_default_splits(d, 1, 32448)
+    assert 1 <= s <= 507
+    assert L.oscar_default_splits(d, 1, 0) == 1
+    assert L.oscar_status_string(L.OSCAR_ERR_WORKSPACE) == "workspace too small"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, L.OSCAR_ERR_UNSUPPORTED),
+    ("group_size", 64, L.OSCAR_ERR_UNSUPPORTED),
+    ("page_tokens", 16, L.OSCAR_ERR_UNSUPPORTED),
+    ("sink_tokens", 4, L.OSCAR_ERR_UNSUPPORTED),
+    ("recent_tokens", 128, L.OSCAR_ERR_UNSUPPORTED),
+    ("n_q_heads", 30, L.OSCAR_ERR_INVALID_ARG),
+    ("n_q_heads", 8 * 32, L.OSCAR_ERR_UNSUPPORTED),
+    ("n_kv_heads", 0, L.OSCAR_ERR_INVALID_ARG),
+])
+def test_bad_descriptors(lib, field, value, status):
+    d = L.layer_desc(32, 8)
+    setattr(d, field, value)
+    assert L.oscar_check_desc(d) == status
+    assert L.oscar_page_bytes(d) == 0
+    assert L.oscar_last_error()
+    st = lib.oscar_decode_int2(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, 1 << 30, None)
+    assert st == status
+
+
+def test_null_desc(lib):
+    assert lib.oscar_check_desc(None) == L.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_merge(None, FAKE, 1, FAKE, FAKE, FAKE, 1, None) == L.OSCAR_ERR_INVALID_ARG
+
+
+def test_decode_int2_argument_checks(lib):
+    d = ctypes.byref(L.layer_desc(32, 8))
+    call = lib.oscar_decode_int2
+    big = 1 << 40
+    assert call(d, None, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert call(d, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 0.08, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert call(d, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 0, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert call(d, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 0.08, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert call(d, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, -1.0, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert call(d, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, float("nan"), 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    need = L.oscar_partials_bytes(L.layer_desc(32, 8), 1, 4)
+    assert call(d, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, need - 1, None) == L.OSCAR_ERR_WORKSPACE
+    assert "workspace" in L.oscar_last_error()
+
+
+def test_decode_bf16_and_merge_argument_checks(lib):
+    desc = L.layer_desc(32, 8)
+    d = ctypes.byref(desc)
+    need = L.oscar_partials_bytes(desc, 2, 5)
+    assert lib.oscar_decode_bf16(d, FAKE, FAKE, FAKE, FAKE, 2, 0.08, FAKE, need - 4, None) == L.OSCAR_ERR_WORKSPACE
+    assert lib.oscar_decode_bf16(d, FAKE, None, FAKE, FAKE, 2, 0.08, FAKE, need, None) == L.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_decode_bf16(d, FAKE, FAKE, FAKE, FAKE, -3, 0.08, FAKE, need, None) == L.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_merge(d, FAKE, 0, FAKE, FAKE, FAKE, 2, None) == L.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_merge(d, FAKE, 3, FAKE, None, FAKE, 2, None) == L.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_merge(d, FAKE, 3, FAKE, FAKE, FAKE, 0, None) == L.OSCAR_ERR_INVALID_ARG
+
+
+def test_demote_argument_checks(lib):
+    d = ctypes.byref(L.layer_desc(32, 8))
+    f = lib.oscar_demote
+    assert f(d, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_OK  # no-op
+    assert f(d, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert f(d, FAKE, FAKE, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert f(d, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert f(d, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == L.OSCAR_ERR_INVALID_ARG
+
+
+def test_python_binding_validates_shapes_before_the_library():
+    torch = pytest.importorskip("torch")
+    d = L.layer_desc(32, 8)
+    cpu = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        L.oscar_demote(d, cpu, cpu, cpu, cpu, cpu, cpu, cpu, cpu, cpu)

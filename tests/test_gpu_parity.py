@@ -1,0 +1,381 @@
+"""GPU parity: every entry point against the oracle on seeded inputs (MI355X only).
+
+Decode is checked on pools the oracle built (so demotion tolerances cannot leak into
+decode parity), entry point by entry point and end to end; demotion is checked byte
+by byte; the full-size workloads run the whole GPU path (demote every history token,
+then decode) in the launch configuration the benchmark uses and are compared on
+sampled KV heads."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_harness import (assert_close, bits_to_f64, clips, compare_history, oracle_decode, oracle_history,
+                         oracle_pool, rotations, windows)
+from oracle import attention as oatt
+from oracle import pages as opages
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import bit_kv_cache_oscar_amd as ok
+    ok.lib()  # fails loudly if the library is not built
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def bf16(x) -> "torch.Tensor":
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+
+def make_cache(w, rk_bits, rv_bits, table, n_phys, with_windows=True):
+    from bit_kv_cache_oscar_amd.layer import LayerCache
+
+    c = LayerCache(w.n_q_heads, w.n_kv_heads, w.batch, table.shape[1], n_phys)
+    ck, cv = clips(w)
+    c.set_rotations(rk_bits, rv_bits, ck, cv)
+    c.set_block_table(table)
+    c.set_hist_len(w.hist_lens)
+    if with_windows:
+        for b in range(w.batch):
+            for kv in range(w.n_kv_heads):
+                k, v = synth.window_rows(w, b, kv)
+                c.set_window(b, kv, k, v)
+        c.set_win_len(w.win_lens)
+    return c
+
+
+def queries(w):
+    return bf16(np.stack([synth.query(w, b) for b in range(w.batch)]))
+
+
+def custom(name, hq, hkv, ctx, cfg=2, **kw):
+    base = synth.workload(cfg)
+    return synth.Workload(cfg, name, len(ctx), hq, hkv, tuple(ctx), max(ctx),
+                          outlier_fixed=base.outlier_fixed, **kw)
+
+
+DECODE_CASES = {
+    "c1": lambda: synth.workload(1),
+    "c2-4k": lambda: synth.workload(2).with_ctx([4000]),
+    "c3-6k-permuted": lambda: synth.workload(3).with_ctx([6000]),
+    "c4-shared-ragged": lambda: synth.workload(4).with_ctx([4596, 5096, 3000, 4096 + 128 + 320 + 3], capacity=6000),
+    "c5-gq8": lambda: synth.workload(5).with_ctx([3000, 2600]),
+    "gq16": lambda: custom("gq16", 32, 2, [2500, 900]),
+    "gq2": lambda: custom("gq2", 16, 8, [1500]),
+    "edges": lambda: custom("edges", 8, 2, [100, 320, 321, 64 * 3 + 320, 1, 0 + 64 * 1 + 320 + 63]),
+}
+
+
+@pytest.mark.parametrize("case", list(DECODE_CASES))
+def test_decode_on_oracle_pages(case):
+    w = DECODE_CASES[case]()
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    assert np.array_equal(bits_to_f64(rk_bits), rk) and np.array_equal(bits_to_f64(rv_bits), rv)
+    pool, table, hists = oracle_pool(w, rk, rv)
+    refs = [oracle_decode(w, b, rk, rv, hists[b]) for b in range(w.batch)]
+    from bit_kv_cache_oscar_amd import oscar_default_splits
+
+    c = make_cache(w, rk_bits, rv_bits, table, pool.shape[0])
+    c.pool.copy_(torch.from_numpy(pool.reshape(-1)))
+    q = queries(w)
+    max_pages = int(np.max(-(-w.hist_lens // 64))) if w.batch else 0
+    for s in sorted({oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())), 1, 3, max_pages + 5}):
+        say(case, "decode", "B", w.batch, "Hq", w.n_q_heads, "Hkv", w.n_kv_heads, "ctx", w.ctx_lens, "splits", s)
+        c.set_splits(s)
+        out = c.decode(q, w.sm_scale)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for b in range(w.batch):
+            assert_close(got[b], refs[b], f"{case} b{b} splits {s}")
+
+
+def _split_bounds(nh, s_total):
+    n_pages = -(-nh // 64)
+    pps = -(-n_pages // s_total) if s_total else 0
+    out = []
+    for s in range(s_total):
+        a = min(nh, s * pps * 64)
+        z = min(nh, (s + 1) * pps * 64)
+        out.append((a, max(a, z)))
+    return out
+
+
+def _partials(buf, batch, hq, splits):
+    raw = buf.cpu().numpy().view(np.float32)
+    n = batch * hq * splits
+    acc_off = -(-8 * n // 256) * 256 // 4
+    m = raw[:n].reshape(batch, hq, splits)
+    l = raw[n:2 * n].reshape(batch, hq, splits)
+    acc = raw[acc_off:acc_off + n * 128].reshape(batch, hq, splits, 128)
+    return m, l, acc
+
+
+def _check_partial(gm, gl, gacc, ref, what):
+    m, l, acc = ref
+    if l == 0.0:
+        assert gm == -np.inf and gl == 0.0 and not np.any(gacc), what
+        return
+    assert abs(gm / LOG2E - m) <= 1e-5 * max(1.0, abs(m)), what
+    assert abs(gl - l) <= 1e-4 * l, what
+    assert_close(gacc / gl, acc / l, what)
+
+
+def test_int2_partials_match_oracle():
+    from bit_kv_cache_oscar_amd import oscar_decode_int2, oscar_partials_bytes
+
+    w = synth.workload(2).with_ctx([4000, 2000])
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    pool, table, hists = oracle_pool(w, rk, rv)
+    c = make_cache(w, rk_bits, rv_bits, table, pool.shape[0], with_windows=False)
+    c.pool.copy_(torch.from_numpy(pool.reshape(-1)))
+    S = 7
+    buf = torch.zeros(oscar_partials_bytes(c.desc, w.batch, S), dtype=torch.uint8, device="cuda")
+    q = queries(w)
+    say("int2 partials", w.ctx_lens, "splits", S)
+    oscar_decode_int2(c.desc, q, c.rot_k, c.pool, c.block_table, c.hist_len, w.sm_scale, S, buf)
+    torch.cuda.synchronize()
+    gm, gl, gacc = _partials(buf, w.batch, w.n_q_heads, S)
+    for b in range(w.batch):
+        qb = synth.query(w, b).astype(np.float64)
+        bounds = _split_bounds(w.hist_len(b), S)
+        for h in range(0, w.n_q_heads, 5):
+            kv = h // w.gq
+            refs = oatt.history_partials(qb[h], rk[kv], hists[b][kv], w.sm_scale, bounds)
+            for s, ref in enumerate(refs):
+                _check_partial(gm[b, h, s], gl[b, h, s], gacc[b, h, s], ref, f"b{b} h{h} s{s}")
+
+
+def test_bf16_partials_match_oracle():
+    from bit_kv_cache_oscar_amd import oscar_decode_bf16, oscar_partials_bytes, oscar_window_splits
+
+    w = custom("win", 32, 8, [5000, 70, 320, 1])
+    (rk_bits, rv_bits), _ = rotations(w)
+    table, n_phys = synth.block_table(w)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys)
+    ws = oscar_window_splits(c.desc)
+    buf = torch.zeros(oscar_partials_bytes(c.desc, w.batch, ws), dtype=torch.uint8, device="cuda")
+    q = queries(w)
+    say("bf16 partials", w.ctx_lens)
+    oscar_decode_bf16(c.desc, q, c.k_win, c.v_win, c.win_len, w.sm_scale, buf)
+    torch.cuda.synchronize()
+    gm, gl, gacc = _partials(buf, w.batch, w.n_q_heads, ws)
+    for b in range(w.batch):
+        qb = synth.query(w, b).astype(np.float64)
+        wk, wv = windows(w, b)
+        bounds = [(min(64 * i, w.win_len(b)), min(64 * i + 64, w.win_len(b))) for i in range(ws)]
+        for h in range(0, w.n_q_heads, 3):
+            kv = h // w.gq
+            refs = oatt.window_partials(qb[h], wk[kv], wv[kv], w.sm_scale, bounds)
+            for s, ref in enumerate(refs):
+                _check_partial(gm[b, h, s], gl[b, h, s], gacc[b, h, s], ref, f"b{b} h{h} c{s}")
+
+
+def test_merge_of_oracle_partials():
+    from bit_kv_cache_oscar_amd import oscar_merge, oscar_partials_bytes, oscar_window_splits, layer_desc
+
+    g = np.random.default_rng(11)
+    B, HQ, HKV, S = 3, 8, 2, 5
+    desc = layer_desc(HQ, HKV)
+    ws = oscar_window_splits(desc)
+    w = custom("merge", HQ, HKV, [2000] * B)
+    (_, rv_bits), (_, rv) = rotations(w)
+
+    def fill(splits, empty_rate):
+        n = B * HQ * splits
+        m = g.normal(0, 20, n)
+        l = g.uniform(0.5, 50, n)
+        acc = g.normal(0, 3, (n, 128)) * l[:, None]
+        empty = g.random(n) < empty_rate
+        m[empty], l[empty], acc[empty] = -np.inf, 0.0, 0.0
+        return m, l, acc
+
+    hm, hl, hacc = fill(S, 0.3)
+    wm, wl, wacc = fill(ws, 0.3)
+    # one (b, h) with everything empty: output 0
+    for arr in (hm,):
+        arr[:S] = -np.inf
+    hl[:S], hacc[:S] = 0.0, 0.0
+    wm[:ws], wl[:ws], wacc[:ws] = -np.inf, 0.0, 0.0
+
+    def pack(m, l, acc, splits):
+        n = B * HQ * splits
+        buf = np.zeros(oscar_partials_bytes(desc, B, splits), np.uint8)
+        f = buf.view(np.float32)
+        f[:n] = (m * LOG2E).astype(np.float32)
+        f[n:2 * n] = l
+        off = -(-8 * n // 256) * 256 // 4
+        f[off:off + n * 128] = acc.reshape(-1)
+        return torch.from_numpy(buf).cuda()
+
+    out = torch.zeros((B, HQ, 128), dtype=torch.float32, device="cuda")
+    rvt = bf16(bits_to_f64(rv_bits).astype(np.float32))
+    say("merge", B, HQ, HKV, S)
+    oscar_merge(desc, pack(hm, hl, hacc, S), S, pack(wm, wl, wacc, ws), rvt, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        for h in range(HQ):
+            i = (b * HQ + h)
+            hp = [(hm[i * S + s], hl[i * S + s], hacc[i * S + s]) for s in range(S)]
+            wp = [(wm[i * ws + s], wl[i * ws + s], wacc[i * ws + s]) for s in range(ws)]
+            # the GPU sees m rounded to float32 in log2 units; use the same m on the oracle side
+            hp = [(float(np.float32(m * LOG2E)) / LOG2E, l, a) for m, l, a in hp]
+            wp = [(float(np.float32(m * LOG2E)) / LOG2E, l, a) for m, l, a in wp]
+            ref = oatt.merge_segments(hp, wp, rv[h // (HQ // HKV)])
+            assert_close(got[b, h], ref, f"merge b{b} h{h}")
+    assert not np.any(got[0, 0])
+
+
+# ------------------------------------------------------------------------------ demotion
+
+
+def _demote_all(c, w, b, pages_np, slots_np, rows_k, rows_v, chunk=1 << 16):
+    pages_t = torch.from_numpy(pages_np.astype(np.int32)).cuda()
+    slots_t = torch.from_numpy(slots_np.astype(np.int32)).cuda()
+    for a in range(0, len(pages_np), chunk):
+        z = min(len(pages_np), a + chunk)
+        c.demote(bf16(rows_k[a:z]), bf16(rows_v[a:z]), pages_t[a:z], slots_t[a:z])
+
+
+def _gpu_head_history(c, w, table_row, kv, n):
+    pool = c.pool.cpu().numpy().reshape(-1, w.n_kv_heads, opages.HEAD_BLOCK)
+    return opages.unpack_history(pool, table_row, kv, n)
+
+
+def test_demote_config1_bitexact():
+    w = synth.workload(1)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table, n_phys = synth.block_table(w)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys, with_windows=False)
+    n = w.hist_len(0)
+    hk, hv = synth.history_rows(w, 0, 0)
+    j = np.arange(n)
+    say("demote c1", n)
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, hk[:, None, :], hv[:, None, :])
+    torch.cuda.synchronize()
+    ref, km, vm = oracle_history(w, 0, 0, rk, rv)
+    flips = compare_history(_gpu_head_history(c, w, table[0], 0, n), ref, km, vm, "c1")
+    assert flips == 0
+
+
+def test_demote_random_order_on_stale_pages_and_overwrite():
+    w = custom("stale", 8, 4, [64 * 3 + 320], cfg=2)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    n_phys = 5
+    table = np.array([[4, 1, 3]], np.int32)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys, with_windows=False)
+    g = np.random.default_rng(5)
+    stale = g.integers(0, 256, n_phys * w.n_kv_heads * opages.HEAD_BLOCK, dtype=np.uint8)
+    c.pool.copy_(torch.from_numpy(stale))
+    n = 192
+    rows_k = np.stack([synth.history_rows(w, 0, kv)[0] for kv in range(w.n_kv_heads)], 1)
+    rows_v = np.stack([synth.history_rows(w, 0, kv)[1] for kv in range(w.n_kv_heads)], 1)
+    order = g.permutation(n)
+    say("demote stale pages, random order", n)
+    for half in (order[:n // 2], order[n // 2:]):
+        _demote_all(c, w, 0, table[0, half // 64], half % 64, rows_k[half], rows_v[half])
+    # overwrite 40 slots with other rows
+    redo = g.choice(n, 40, replace=False)
+    other_k = rows_k[::-1].copy()
+    other_v = rows_v[::-1].copy()
+    _demote_all(c, w, 0, table[0, redo // 64], redo % 64, other_k[redo], other_v[redo])
+    torch.cuda.synchronize()
+    final_k, final_v = rows_k.copy(), rows_v.copy()
+    final_k[redo], final_v[redo] = other_k[redo], other_v[redo]
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
+    from oracle import quant as oquant
+    for kv in range(w.n_kv_heads):
+        kc, ks, kz, km = oquant.quantize_rows(final_k[:, kv].astype(np.float64), rk[kv], w.clip_ratio)
+        vc, vs, vz, vm = oquant.quantize_rows(final_v[:, kv].astype(np.float64), rv[kv], w.clip_ratio)
+        got = opages.unpack_history(pool, table[0], kv, n)
+        assert compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"head {kv}") == 0
+    # untouched physical pages keep their bytes
+    stale3 = stale.reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
+    assert np.array_equal(pool[0], stale3[0]) and np.array_equal(pool[2], stale3[2])
+
+
+def test_demote_degenerate_rows():
+    w = custom("degenerate", 4, 2, [64 + 320], cfg=2)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table = np.array([[0]], np.int32)
+    c = make_cache(w, rk_bits, rv_bits, table, 1, with_windows=False)
+    g = np.random.default_rng(6)
+    rows = g.standard_normal((64, 2, 128)).astype(np.float32)
+    rows[0] = 0.0
+    rows[1] = 1.5
+    rows[2, :, 7] = 3000.0
+    rows[3] *= 1e-6
+    rows = synth.to_bf16_values(rows)
+    j = np.arange(64)
+    say("demote degenerate rows")
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, rows, rows[::-1].copy())
+    torch.cuda.synchronize()
+    pool = c.pool.cpu().numpy().reshape(1, 2, opages.HEAD_BLOCK)
+    from oracle import quant as oquant
+    for kv in range(2):
+        kc, ks, kz, km = oquant.quantize_rows(rows[:, kv].astype(np.float64), rk[kv], w.clip_ratio)
+        vc, vs, vz, vm = oquant.quantize_rows(rows[::-1][:, kv].astype(np.float64), rv[kv], w.clip_ratio)
+        got = opages.unpack_history(pool, table[0], kv, 64)
+        assert compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"head {kv}") == 0
+        assert ks[0] == 0 and got[1][0] == 0
+
+
+# ------------------------------------------------------------------- full-size workloads
+
+FULL_SAMPLES = {2: [(0, 0), (0, 7)], 3: [(0, 3)], 4: [(0, 0), (63, 5)], 5: [(1, 2), (3, 7)]}
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_end_to_end_sampled(cfg):
+    """The whole GPU path at the workload's real size: every history token demoted on the
+    GPU, then decoded with the default split count; sampled KV heads compared with the
+    oracle (pool bytes and the outputs of their query heads)."""
+    from bit_kv_cache_oscar_amd import oscar_default_splits
+
+    w = synth.workload(cfg)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table, n_phys = synth.block_table(w)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys)
+    say("full size", w.name, "pages", n_phys)
+    shared_done = False
+    for b in range(w.batch):
+        n = w.hist_len(b)
+        start = 0
+        if w.shared_pages and b > 0:
+            start = min(n, w.shared_pages * 64)   # the shared prefix is demoted once
+        ks, vs = [], []
+        for kv in range(w.n_kv_heads):
+            k, v = synth.kv_rows(w, b, kv, 64 + start, 64 + n)
+            ks.append(k)
+            vs.append(v)
+        j = np.arange(start, n)
+        _demote_all(c, w, b, table[b, j // 64], j % 64, np.stack(ks, 1), np.stack(vs, 1))
+        shared_done = True
+    assert shared_done
+    s = oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max()))
+    c.set_splits(s)
+    out = c.decode(queries(w), w.sm_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
+    for b, kv in FULL_SAMPLES[cfg]:
+        say("full size sample", w.name, "b", b, "kv", kv, "splits", s)
+        ref_hist, km, vm = oracle_history(w, b, kv, rk, rv)
+        gpu_hist = opages.unpack_history(pool, table[b], kv, w.hist_len(b))
+        compare_history(gpu_hist, ref_hist, km, vm, f"{w.name} b{b} kv{kv}")
+        hists = {kv: ref_hist}
+        heads = range(kv * w.gq, (kv + 1) * w.gq)
+        ref = oracle_decode(w, b, rk, rv, hists, heads=heads)
+        for h in heads:
+            assert_close(got[b, h], ref[h], f"{w.name} b{b} h{h}")

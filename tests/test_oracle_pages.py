@@ -118,3 +118,37 @@ def test_history_round_trip_through_block_table():
     assert np.array_equal(back[1], np.array(cols[1]))
     # entries 64..127 went to physical page 0, 128.. to page 5; pages 1, 3 untouched
     assert not pool[1].any() and not pool[3].any()
+
+
+def test_whole_page_packer_matches_token_writer():
+    g = np.random.default_rng(3)
+    toks = [_random_token(g) for _ in range(64)]
+    cols = list(zip(*toks))
+    hist = (np.stack(cols[0]), np.array(cols[1]), np.array(cols[2]),
+            np.stack(cols[3]), np.array(cols[4]), np.array(cols[5]))
+    for n in (64, 37, 1):
+        pool = pages.new_pool(1, 1)
+        for t in range(n):
+            pages.write_token(pool, 0, t, 0, *[x[t] for x in hist])
+        blk = pages.pack_page(*[x[:n] for x in hist])
+        assert np.array_equal(blk, pool[0, 0])
+        back = pages.unpack_page(blk)
+        for a, b in zip(back, hist):
+            assert np.array_equal(np.asarray(a)[:n], np.asarray(b)[:n])
+
+
+def test_history_pack_unpack_through_table():
+    g = np.random.default_rng(4)
+    n = 200
+    toks = [_random_token(g) for _ in range(n)]
+    cols = list(zip(*toks))
+    hist = (np.stack(cols[0]), np.array(cols[1]), np.array(cols[2]),
+            np.stack(cols[3]), np.array(cols[4]), np.array(cols[5]))
+    table = np.array([3, 1, 6, 0])
+    pool = pages.new_pool(7, 2)
+    pages.pack_history(pool, table, 1, hist)
+    slow = pages.read_history(pool, table, 1, n)
+    fast = pages.unpack_history(pool, table, 1, n)
+    for a, b, c in zip(slow, fast, hist):
+        assert np.array_equal(a, b) and np.array_equal(a, c)
+    assert not pool[:, 0].any()

@@ -125,3 +125,9 @@ def test_fp16_conversion_is_single_rounding():
 def test_overflowing_range_is_rejected():
     with pytest.raises(ValueError):
         quant.quantize_rows(_row([1e6, -1e6]), EYE, 1.0)
+
+
+def test_boundary_distance_matches_brute_force():
+    t = np.random.default_rng(9).uniform(-2, 6, 5000)
+    brute = np.abs(t[:, None] - quant.BOUNDARIES[None, :]).min(1)
+    assert np.array_equal(quant.boundary_distance(t), brute)

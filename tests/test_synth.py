@@ -72,3 +72,14 @@ def test_permuted_pages_are_a_bijection():
     assert sorted(row.tolist()) == list(range(41)) and n_phys == 41
     assert not np.array_equal(row, np.arange(41))
     assert np.all(table[0, 41:] == -1)
+
+
+def test_window_rows_for_short_contexts():
+    w = synth.workload(2).with_ctx([1, 40, 64, 100, 320, 321, 700])
+    for b, L in enumerate(w.ctx_lens):
+        k, v = synth.window_rows(w, b, 0)
+        full_k, _ = synth.kv_rows(w, b, 0)
+        assert len(k) == w.win_len(b) == min(L, 320)
+        idx = list(range(min(L, 64))) + list(range(max(min(L, 64), L - 256), L))
+        assert np.array_equal(k, full_k[idx])
+        assert w.hist_len(b) == max(0, L - 320)
