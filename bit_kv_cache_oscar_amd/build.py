@@ -25,6 +25,8 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 instructions stay off: plain fp32 VALU code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no copies between register files in the loops
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]

@@ -15,6 +15,13 @@ constexpr int kKMeta = 4096;
 constexpr int kVMeta = 4352;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Byte offsets inside a head's page block of the word holding K slot t, dims 16w..16w+15
+// and of the word holding V dim d, slots 16u..16u+15.
+__host__ __device__ constexpr int k_word_offset(int t, int w) {
+  return kKCodes + 32 * (16 * (w >> 1) + (t >> 2)) + 8 * (t & 3) + 4 * (w & 1);
+}
+__host__ __device__ constexpr int v_word_offset(int d, int u) { return kVCodes + 32 * (16 * u + (d & 15)) + 4 * (d >> 4); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -85,6 +92,65 @@ __device__ __forceinline__ T wave_min(T v) {
   return v;
 }
 
+// DPP row operations (16-lane rows): quad xor 1, quad xor 2, half-row mirror, row mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// max / sum over each 16-lane row; every lane of the row receives the result
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+__device__ __forceinline__ double lane_value_f64(double v, int src) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), src);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), src);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// fp64 sum over the whole wave without LDS traffic: row butterflies, then the four rows
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<kDppQuadXor1>(v);
+  v += dpp_f64<kDppQuadXor2>(v);
+  v += dpp_f64<kDppHalfMirror>(v);
+  v += dpp_f64<kDppMirror>(v);
+  return (lane_value_f64(v, 0) + lane_value_f64(v, 16)) + (lane_value_f64(v, 32) + lane_value_f64(v, 48));
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = row16_max(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
 // Value of lane `src` (wave-uniform) of v, broadcast to every lane.
 __device__ __forceinline__ float lane_value(float v, int src) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
@@ -92,5 +158,19 @@ __device__ __forceinline__ float lane_value(float v, int src) {
 
 // 2^x with 2^(-inf) = 0.
 __device__ __forceinline__ float exp2_safe(float x) { return exp2f(x); }
+
+}  // namespace oscar
+
+namespace oscar {
+
+// Copies one 128x128 bf16 matrix (32 KiB, 16-byte aligned) from global memory into LDS
+// with 16-byte loads spread over `nthreads` threads. The caller synchronises.
+__device__ __forceinline__ void stage_rotation(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src,
+                                               int tid, int nthreads) {
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+#pragma unroll 4
+  for (int i = tid; i < kHeadDim * kHeadDim / 8; i += nthreads) d[i] = s[i];
+}
 
 }  // namespace oscar

@@ -19,6 +19,8 @@ struct PartialsView {
   float* m;
   float* l;
   float* acc;
+  char* qlimb;    // INT2 pass only: fixed-point limbs of the rotated query [B][Hq][4][128]
+  double* qscal;  // INT2 pass only: per (request, head) score scale and scaled sum(q_rot)
 };
 
 size_t partials_bytes(int batch, int n_q, int n_splits);

@@ -6,8 +6,8 @@
 // R_V^T before joining the BF16 part; un-rotating after the reduction is exact because
 // the un-rotation is linear.
 //
-// Grid (kv_head, request), 256 threads: R_V of the head is staged once in LDS and serves
-// every query head of the group.
+// Grid (query head, request), 256 threads: R_V of the head's KV head is staged in LDS,
+// the split reductions keep many loads in flight, then one row of R_V per output dim.
 
 #include "device_common.h"
 #include "launch.h"
@@ -17,6 +17,40 @@ namespace {
 
 constexpr int kRowPad = 130;  // bf16 elements per LDS row: odd dword stride, no bank conflicts
 
+// Online-softmax reduction of `ns` partials of one (request, head) held at m[o..o+ns),
+// l[o..), acc[(o..)*128 + d]: 128 dims x 2 split-halves per pass over 256 threads.
+// Returns (max, sum) to every thread and leaves the reduced acc in out_s[128].
+__device__ __forceinline__ void reduce_splits(const float* __restrict__ pm, const float* __restrict__ pl,
+                                              const float* __restrict__ pa, size_t o, int ns, float* red_s,
+                                              float* part_s, float* out_s, float& big_out, float& l_out) {
+  const int tid = threadIdx.x;
+  float big = -INFINITY;
+  for (int s = tid; s < ns; s += 256) big = fmaxf(big, pm[o + s]);
+  big = wave_max(big);
+  if ((tid & 63) == 0) red_s[tid >> 6] = big;
+  __syncthreads();
+  big = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+  __syncthreads();
+  float l = 0.f;
+  if (big != -INFINITY)
+    for (int s = tid; s < ns; s += 256) l = fmaf(exp2f(pm[o + s] - big), pl[o + s], l);
+  l = wave_sum(l);
+  if ((tid & 63) == 0) red_s[tid >> 6] = l;
+  const int d = tid & 127;
+  const int half = tid >> 7;
+  float a = 0.f;
+  if (big != -INFINITY) {
+#pragma unroll 16
+    for (int s = half; s < ns; s += 2) a = fmaf(exp2f(pm[o + s] - big), pa[(o + s) * kHeadDim + d], a);
+  }
+  part_s[tid] = a;
+  __syncthreads();
+  l_out = red_s[0] + red_s[1] + red_s[2] + red_s[3];
+  big_out = big;
+  if (tid < 128) out_s[tid] = part_s[tid] + part_s[tid + 128];
+  __syncthreads();
+}
+
 template <int GQ>
 __global__ __launch_bounds__(256) void merge_kernel(
     const float* __restrict__ hm, const float* __restrict__ hl, const float* __restrict__ hacc, int n_splits,
@@ -25,62 +59,50 @@ __global__ __launch_bounds__(256) void merge_kernel(
   __shared__ uint16_t r_s[kHeadDim * kRowPad];
   __shared__ float accr_s[kHeadDim];
   __shared__ float accw_s[kHeadDim];
-  __shared__ float scal_s[4];
+  __shared__ float part_s[256];
+  __shared__ float red_s[4];
 
-  const int kv = blockIdx.x;
+  const int h = blockIdx.x;
+  const int kv = h / GQ;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const uint16_t* rot = rot_v + static_cast<size_t>(kv) * kHeadDim * kHeadDim;
-  for (int i = tid; i < kHeadDim * kHeadDim; i += 256) r_s[(i >> 7) * kRowPad + (i & 127)] = rot[i];
-
-  for (int g = 0; g < GQ; ++g) {
-    const int h = kv * GQ + g;
-    const int d = tid & 127;
-    const bool hist_side = tid < 128;
-    const int ns = hist_side ? n_splits : n_wsplits;
-    const size_t o = (static_cast<size_t>(b) * n_q + h) * ns;
-    const float* pm = hist_side ? hm : wm;
-    const float* pl = hist_side ? hl : wl;
-    const float* pa = hist_side ? hacc : wacc;
-    float big = -INFINITY;
-    for (int s = 0; s < ns; ++s) big = fmaxf(big, pm[o + s]);
-    float l = 0.f, a = 0.f;
-    if (big != -INFINITY) {
-      for (int s = 0; s < ns; ++s) {
-        const float w = exp2f(pm[o + s] - big);
-        l = fmaf(w, pl[o + s], l);
-        a = fmaf(w, pa[(o + s) * kHeadDim + d], a);
-      }
+  {
+    // R_V into LDS rows padded to an odd dword stride (conflict-free row reads below)
+    const uint4* src = reinterpret_cast<const uint4*>(rot_v + static_cast<size_t>(kv) * kHeadDim * kHeadDim);
+#pragma unroll
+    for (int i = tid; i < kHeadDim * kHeadDim / 8; i += 256) {
+      const uint4 v = src[i];
+      uint32_t* dst = reinterpret_cast<uint32_t*>(r_s + (i >> 4) * kRowPad + (i & 15) * 8);
+      dst[0] = v.x;
+      dst[1] = v.y;
+      dst[2] = v.z;
+      dst[3] = v.w;
     }
-    (hist_side ? accr_s : accw_s)[d] = a;
-    if (d == 0) {
-      scal_s[hist_side ? 0 : 2] = big;
-      scal_s[hist_side ? 1 : 3] = l;
-    }
-    __syncthreads();
-    if (tid < 128) {
-      float oh = 0.f;
-      const uint16_t* row = r_s + tid * kRowPad;
+  }
+  const size_t row = static_cast<size_t>(b) * n_q + h;
+  float mh, lh, mw, lw;
+  reduce_splits(hm, hl, hacc, row * n_splits, n_splits, red_s, part_s, accr_s, mh, lh);
+  reduce_splits(wm, wl, wacc, row * n_wsplits, n_wsplits, red_s, part_s, accw_s, mw, lw);
+  if (tid < 128) {
+    float oh = 0.f;
+    const uint16_t* r = r_s + tid * kRowPad;
 #pragma unroll 8
-      for (int j = 0; j < kHeadDim; ++j) oh = fmaf(accr_s[j], bf16_to_f32(row[j]), oh);
-      const float mh = scal_s[0], lh = scal_s[1], mw = scal_s[2], lw = scal_s[3];
-      const float big2 = fmaxf(mh, mw);
-      float res = 0.f;
-      if (big2 != -INFINITY) {
-        const float al = exp2f(mh - big2);
-        const float be = exp2f(mw - big2);
-        res = fmaf(al, oh, be * accw_s[tid]) / fmaf(al, lh, be * lw);
-      }
-      out[(static_cast<size_t>(b) * n_q + h) * kHeadDim + tid] = res;
+    for (int j = 0; j < kHeadDim; ++j) oh = fmaf(accr_s[j], bf16_to_f32(r[j]), oh);
+    const float big = fmaxf(mh, mw);
+    float res = 0.f;
+    if (big != -INFINITY) {
+      const float al = exp2f(mh - big);
+      const float be = exp2f(mw - big);
+      res = fmaf(al, oh, be * accw_s[tid]) / fmaf(al, lh, be * lw);
     }
-    __syncthreads();
+    out[row * kHeadDim + tid] = res;
   }
 }
 
 template <int GQ>
 hipError_t launch(const LayerShape& L, const PartialsView& hist, int n_splits, const PartialsView& win,
                   int n_wsplits, const void* rot_v, float* out, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel<GQ>, dim3(L.n_kv, batch), dim3(256), 0, stream, hist.m, hist.l, hist.acc,
+  hipLaunchKernelGGL(merge_kernel<GQ>, dim3(L.n_q, batch), dim3(256), 0, stream, hist.m, hist.l, hist.acc,
                      n_splits, win.m, win.l, win.acc, n_wsplits, static_cast<const uint16_t*>(rot_v), out, L.n_q);
   return hipGetLastError();
 }

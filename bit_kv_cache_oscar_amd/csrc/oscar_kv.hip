@@ -62,20 +62,33 @@ int window_splits_of(const oscar_layer_desc* d) { return (d->sink_tokens + d->re
 
 namespace oscar {
 
+namespace {
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+// [m | l | pad | acc | query limbs | query scalars]
 size_t partials_bytes(int batch, int n_q, int n_splits) {
   const size_t n = static_cast<size_t>(batch) * n_q * n_splits;
-  const size_t acc_off = (8 * n + 255) / 256 * 256;
-  return acc_off + n * 128 * sizeof(float);
+  const size_t heads = static_cast<size_t>(batch) * n_q;
+  const size_t acc_off = align256(8 * n);
+  const size_t ql_off = align256(acc_off + n * 128 * sizeof(float));
+  const size_t qs_off = align256(ql_off + heads * 512);
+  return qs_off + heads * 16;
 }
 
 PartialsView partials_view(void* base, int batch, int n_q, int n_splits) {
   const size_t n = static_cast<size_t>(batch) * n_q * n_splits;
-  const size_t acc_off = (8 * n + 255) / 256 * 256;
+  const size_t heads = static_cast<size_t>(batch) * n_q;
+  const size_t acc_off = align256(8 * n);
+  const size_t ql_off = align256(acc_off + n * 128 * sizeof(float));
+  const size_t qs_off = align256(ql_off + heads * 512);
   char* p = static_cast<char*>(base);
   PartialsView v;
   v.m = reinterpret_cast<float*>(p);
   v.l = reinterpret_cast<float*>(p + 4 * n);
   v.acc = reinterpret_cast<float*>(p + acc_off);
+  v.qlimb = p + ql_off;
+  v.qscal = reinterpret_cast<double*>(p + qs_off);
   return v;
 }
 
@@ -144,8 +157,8 @@ int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void
   if (n == 0) return ok();
   if (!k_src || !v_src || !dst_page || !dst_slot || !rot_k || !rot_v || !clip_k || !clip_v || !pool)
     return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
-  if (static_cast<long long>(n) * desc->n_kv_heads > 0x7FFFFFFFLL)
-    return fail(OSCAR_ERR_UNSUPPORTED, "n * n_kv_heads exceeds the grid limit");
+  if (2LL * n * desc->n_kv_heads > 0x7FFFFFFFLL)
+    return fail(OSCAR_ERR_UNSUPPORTED, "2 * n * n_kv_heads exceeds the grid limit");
   const oscar::LayerShape L = shape_of(desc);
   return hip_status(oscar::launch_demote_rows(L, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v,
                                               pool, static_cast<hipStream_t>(stream)),

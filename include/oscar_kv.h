@@ -29,13 +29,16 @@
  * head h / (n_q_heads / n_kv_heads).
  *
  * INT2 pool layout (4608 bytes per page per KV head, head h of physical page p at byte
- * (p * n_kv_heads + h) * 4608):
- *   [   0, 2048)  K codes, token-major: slot t at 32 t; 32-bit word w holds dims 16w..16w+15,
- *                 dim 16w + 4m + j in byte j, bits 2m..2m+1.
- *   [2048, 4096)  V codes, dim-major: dim d at 2048 + 16 d; word u holds slots 16u..16u+15,
- *                 slot 16u + 4m + j in byte j, bits 2m..2m+1.
+ * (p * n_kv_heads + h) * 4608). Codes are packed 16 to a little-endian 32-bit word, the code
+ * with index 4m + j of the word's 16 in byte j at bits 2m..2m+1.
+ *   [   0, 2048)  K codes: the word of slot t, dims 16w..16w+15, at byte
+ *                 32 (16 (w / 2) + t / 4) + 8 (t % 4) + 4 (w % 2).
+ *   [2048, 4096)  V codes: the word of dim d, slots 16u..16u+15, at byte
+ *                 2048 + 32 (16 u + d % 16) + 4 (d / 16).
  *   [4096, 4352)  K fp16 scale s and zero point z of slot t at 4096 + 4 t (s first).
  *   [4352, 4608)  V fp16 scale and zero point of slot t at 4352 + 4 t.
+ * (The word order lets lane l = 16 G + n of the decode pass read its K and V words as two
+ * contiguous 32-byte chunks at 32 l and 2048 + 32 l.)
  * A code q stands for q * s + z in the rotated basis. History entry j of a request lives in
  * slot j % 64 of physical page block_table[b * max_pages + j / 64].
  *
@@ -46,6 +49,9 @@
  *   float acc[B][Hq][S][128]  sum of 2^(score*log2e - m) * value
  * with m at byte 0, l at byte 4*B*Hq*S and acc at the next multiple of 256 bytes. An
  * empty split holds m = -inf, l = 0, acc = 0. INT2 partials hold acc in the rotated basis.
+ * After acc (from the next multiple of 256 bytes) the INT2 pass keeps its per-(request,
+ * query head) rotated-query data: 512 bytes of fixed-point limbs per head, then, from the
+ * next multiple of 256 bytes, two doubles per head. oscar_merge does not read that tail.
  */
 #ifndef OSCAR_KV_H
 #define OSCAR_KV_H

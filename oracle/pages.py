@@ -8,12 +8,13 @@ same layout so bytes compare directly.
 
 A physical page holds 64 tokens of every KV head. Head h of page p starts at byte
 (p * n_kv_heads + h) * 4608 and holds:
-  [   0, 2048)  K codes, token-major: slot t owns the 32 bytes at 32*t.  Dims are grouped
-                in 16s, one little-endian 32-bit word per group (word w = dims 16w..16w+15);
-                dim 16w + 4m + j sits in byte j of that word at bits 2m..2m+1.
-  [2048, 4096)  V codes, dim-major: dim d owns the 16 bytes at 2048 + 16*d.  Slots are
-                grouped in 16s (word u = slots 16u..16u+15); slot 16u + 4m + j sits in
-                byte j of that word at bits 2m..2m+1.
+  [   0, 2048)  K codes. The 16 codes of slot t, dims 16w..16w+15, form one little-endian
+                32-bit word; dim 16w + 4m + j sits in byte j of it at bits 2m..2m+1. The word
+                of (slot t, w) is at byte 32 (16 (w // 2) + t // 4) + 8 (t % 4) + 4 (w % 2):
+                the 32 bytes at 32 l hold, for l = 16 G + n, slots 4n..4n+3 and words 2G, 2G+1.
+  [2048, 4096)  V codes. The 16 codes of dim d, slots 16u..16u+15, form one word; slot
+                16u + 4m + j sits in byte j at bits 2m..2m+1. The word of (dim d, u) is at
+                byte 2048 + 32 (16 u + d % 16) + 4 (d // 16).
   [4096, 4352)  K scale and zero point of slot t: fp16 s at 4096 + 4t, fp16 z at +2.
   [4352, 4608)  V scale and zero point of slot t, same form at 4352 + 4t.
 History index j of a request lives in logical page j // 64, slot j % 64; the request's
@@ -30,18 +31,28 @@ HEAD_BLOCK = 4608
 K_CODES, V_CODES, K_META, V_META = 0, 2048, 4096, 4352
 
 
+def k_word_offset(slot: int, w: int) -> int:
+    """Byte offset of the word holding dims 16w..16w+15 of K slot `slot`."""
+    return K_CODES + 32 * (16 * (w // 2) + slot // 4) + 8 * (slot % 4) + 4 * (w % 2)
+
+
+def v_word_offset(dim: int, u: int) -> int:
+    """Byte offset of the word holding slots 16u..16u+15 of V dim `dim`."""
+    return V_CODES + 32 * (16 * u + dim % 16) + 4 * (dim // 16)
+
+
 def k_code_position(slot: int, dim: int):
     """(byte offset within the head block, bit shift) of K code (slot, dim)."""
     w, r = divmod(dim, 16)
     m, j = divmod(r, 4)
-    return K_CODES + 32 * slot + 4 * w + j, 2 * m
+    return k_word_offset(slot, w) + j, 2 * m
 
 
 def v_code_position(slot: int, dim: int):
     """(byte offset within the head block, bit shift) of V code (slot, dim)."""
     u, r = divmod(slot, 16)
     m, j = divmod(r, 4)
-    return V_CODES + 16 * dim + 4 * u + j, 2 * m
+    return v_word_offset(dim, u) + j, 2 * m
 
 
 def _position_tables():

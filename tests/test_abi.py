@@ -41,9 +41,12 @@ def test_helpers(lib):
     assert L.oscar_page_bytes(d) == 8 * 4608
     assert L.oscar_window_tokens(d) == 320
     assert L.oscar_window_splits(d) == 5
-    n = 2 * 32 * 7
-    acc_off = -(-8 * n // 256) * 256
-    assert L.oscar_partials_bytes(d, 2, 7) == acc_off + n * 512
+    n, heads = 2 * 32 * 7, 2 * 32
+    a256 = lambda x: -(-x // 256) * 256
+    acc_off = a256(8 * n)
+    ql_off = a256(acc_off + n * 512)
+    qs_off = a256(ql_off + heads * 512)
+    assert L.oscar_partials_bytes(d, 2, 7) == qs_off + heads * 16
     s = L.oscar_default_splits(d, 1, 32448)
     assert 1 <= s <= 507
     assert L.oscar_default_splits(d, 1, 0) == 1

@@ -11,14 +11,16 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "format_figures.json"
 
 
 def test_code_positions_by_hand():
-    # K: dim 5 -> word 0, r 5 -> m 1, j 1 -> byte 1, bits 2..3
+    # K: slot 0, dim 5 -> word w 0 (pair 0, odd 0) at 0, r 5 -> m 1, j 1 -> byte 1, bits 2..3
     assert pages.k_code_position(0, 5) == (1, 2)
-    # K: slot 2, dim 127 -> word 7, r 15 -> m 3, j 3 -> byte 64 + 28 + 3, bits 6..7
-    assert pages.k_code_position(2, 127) == (95, 6)
-    # V: slot 17, dim 3 -> dim row 2048 + 48, word 1, r 1 -> m 0, j 1 -> byte +4+1, bits 0..1
-    assert pages.v_code_position(17, 3) == (2048 + 48 + 5, 0)
-    # V: slot 63, dim 127 -> word 3, r 15 -> m 3, j 3
-    assert pages.v_code_position(63, 127) == (2048 + 16 * 127 + 12 + 3, 6)
+    # K: slot 2, dim 127 -> w 7: 32 (16*3 + 0) + 8*2 + 4*1 = 1556; r 15 -> m 3, j 3
+    assert pages.k_code_position(2, 127) == (1556 + 3, 6)
+    # K: slot 13, dim 20 -> w 1: 32 (0 + 3) + 8*1 + 4 = 108; r 4 -> m 1, j 0
+    assert pages.k_code_position(13, 20) == (108, 2)
+    # V: slot 17, dim 3 -> u 1: 2048 + 32 (16 + 3) + 0 = 2656; r 1 -> m 0, j 1
+    assert pages.v_code_position(17, 3) == (2656 + 1, 0)
+    # V: slot 63, dim 127 -> u 3: 2048 + 32 (48 + 15) + 4*7 = 4092; r 15 -> m 3, j 3
+    assert pages.v_code_position(63, 127) == (4092 + 3, 6)
 
 
 def test_every_code_has_its_own_two_bits():
@@ -64,19 +66,33 @@ def test_word_unpack_gives_four_consecutive_codes():
     vc = g.integers(0, 4, (64, 128)).astype(np.uint8)
     for t in range(64):
         pages.write_token(pool, 0, t, 0, kc[t], 1.0, 0.0, vc[t], 1.0, 0.0)
-    words = pool[0, 0, :4096].view("<u4")
+    blk = pool[0, 0]
     for t in (0, 9, 63):
         for w in range(8):
-            word = int(words[8 * t + w])
+            o = pages.k_word_offset(t, w)
+            word = int(blk[o:o + 4].view("<u4")[0])
             for m in range(4):
                 b = ((word >> (2 * m)) & 0x03030303).to_bytes(4, "little")
                 assert list(b) == list(kc[t, 16 * w + 4 * m:16 * w + 4 * m + 4])
     for d in (0, 77, 127):
         for u in range(4):
-            word = int(words[512 + 4 * d + u])
+            o = pages.v_word_offset(d, u)
+            word = int(blk[o:o + 4].view("<u4")[0])
             for m in range(4):
                 b = ((word >> (2 * m)) & 0x03030303).to_bytes(4, "little")
                 assert list(b) == list(vc[16 * u + 4 * m:16 * u + 4 * m + 4, d])
+
+
+def test_lane_chunks_are_contiguous():
+    # the decode pass reads, for lane l = 16 G + n, one 32-byte chunk of K words (slots
+    # 4n..4n+3, words 2G and 2G+1) and one of V words (dims 16 dt + n for dt 0..7, word G)
+    for G in range(4):
+        for n in range(16):
+            l = 16 * G + n
+            k = [pages.k_word_offset(4 * n + nt, 2 * G + h) for nt in range(4) for h in range(2)]
+            assert k == list(range(32 * l, 32 * l + 32, 4))
+            v = [pages.v_word_offset(16 * dt + n, G) for dt in range(8)]
+            assert v == list(range(2048 + 32 * l, 2048 + 32 * l + 32, 4))
 
 
 def test_history_bytes_and_ratio_to_bf16():
