@@ -32,6 +32,9 @@ HBM_PEAK_GBS = 8000.0
 HIST_BYTES = 72          # per history token per KV head: 2 x 32 B codes + 2 x (fp16 s, fp16 z)
 WIN_BYTES = 512          # per BF16 window token per KV head (K + V)
 ROT_BYTES = 128 * 128 * 2
+COPY_BYTES = 256 * 2 ** 20  # the plain copy whose counter readings calibrate FETCH_SIZE / WRITE_SIZE
+CSRC = os.path.join(ROOT, "bit_kv_cache_oscar_amd", "csrc")
+INT2_SOURCES = ("decode_int2.hip", "device_common.h", "launch.h")
 
 
 def parse():
@@ -55,6 +58,39 @@ def step_bytes(w):
     demote = w.batch * w.n_kv_heads * (2 * 256 + HIST_BYTES)
     int2 = hist + w.n_kv_heads * ROT_BYTES + w.batch * w.n_q_heads * 256
     return hist + win + rot + qo + demote, int2
+
+
+def int2_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in INT2_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the INT2 kernel from the committed counter summary of this
+    workload, or None when there is none or the kernel source changed since it was taken.
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same counter
+    reads for a plain copy of COPY_BYTES bytes in the same run."""
+    path = os.path.join(ROOT, "profiles", f"decode_int2_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        if kv.get("kernel_source_sha256") != int2_source_hash():
+            return None
+        f = float(kv["fetch_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_fetch_kib"])
+        wr = float(kv["write_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_write_kib"])
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+    return int(round(f + wr))
 
 
 def blas_threads():
@@ -198,6 +234,14 @@ def main():
         insts.append(c)
     torch.cuda.synchronize()
 
+    # one plain copy of known size (untimed): its FETCH_SIZE / WRITE_SIZE readings calibrate
+    # the counters of the kernels in the same profiled run
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
     stream = torch.cuda.current_stream()
 
     def int2(c):
@@ -268,7 +312,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(int2_bytes / (int2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "us_per_launch": round(int2_ms * 1e3, 3),
             "bytes_per_launch": int2_bytes,
         },
