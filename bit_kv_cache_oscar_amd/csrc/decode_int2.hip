@@ -5,27 +5,31 @@
 // in floating point; its result is joined with the BF16 sink/recent pass by an
 // online-softmax merge.
 //
-// The dequantisation is folded so that both contractions run on raw codes:
-//   score_t = s_t (q_rot . c_t) + z_t sum(q_rot)
-//   acc     = sum_t (p_t s_t) c_t + sum_t p_t z_t
-// Both contractions are small integer GEMMs on v_mfma_i32_16x16x64_i8:
-//   K side: [query heads x 4 limbs] x [128 dims] x [16 tokens]: q_rot (fp64) is held as a
-//           29-bit fixed-point integer split into four signed 8-bit limbs, so q_rot . c is
-//           exact and the score is folded in fp64;
-//   V side: [query heads x 4 limbs] x [64 tokens] x [16 dims]: p_t s_t of the page is held
-//           as a 28-bit fixed-point integer relative to the page maximum, in four unsigned
-//           7-bit limbs.
-// A 16-row M tile holds 4 heads x 4 limbs; GQ <= 4 uses one tile (unused rows zero).
+// Both contractions run on the raw codes, with the dequantisation folded out:
+//   score_t = s_t (q_rot . (c_t - 2)) + (z_t + 2 s_t) sum(q_rot)
+//   acc     = sum_t (p_t s^V_t) c^V_t + sum_t p_t z^V_t
+// K side, per page: [4 heads x 4 rows] x [128 dims] x [64 tokens] on
+//   v_mfma_i32_16x16x64_i8. q_rot is a 22-bit fixed-point integer Q (|Q| <= 2^21) in three
+//   signed 8-bit limbs (rows 0..2 of a head; row 3 is zero). Each limb row's accumulator
+//   starts at -2 sum_d limb_d, so the MFMA yields sum_d limb_d (c_d - 2) and the three rows
+//   combine exactly in int32 into Q . (c - 2) (|.| <= 2^29). Centring the codes at 2 keeps
+//   the two terms of the fold small, so the fold runs in fp32.
+// V side, per page: [4 heads x 4 rows] x [64 tokens] x [16 dims] per dim tile. The
+//   weight P_t = p_t s^V_t 2^E is a 24-bit integer (E wave-uniform, chosen from the largest
+//   V scale seen so that P < 2^24); its three bytes, each XORed with 0x80 into signed
+//   range, are rows 0..2 of the head, so the MFMA yields sum_t (byte_l - 128) c_t. Row 3
+//   is constant 1 and yields sum_t c_t, which restores the 128 (1 + 2^8 + 2^16) offset.
+//   The int32 accumulators run across pages and are folded into fp32 sums only when a
+//   head's reference maximum or the fixed-point exponent must change.
 //
-// Grid (split, kv_head x head group, request), 4 waves per workgroup, at most 8 query
-// heads per workgroup (16 query heads per KV head run as two groups of 8); wave w walks pages
-// split_begin + w, + 4, ... of its split, loading the next page while it processes the
-// current one. In a page, MFMA column n of K tile nt is slot 4n + nt, so each lane's four
-// scores belong to four consecutive slots and the P limbs reach the V operand layout (16
-// consecutive slots per lane group) through one LDS dword write and one 16-byte read per
-// tile. Reductions over the 16 lanes of a lane group use DPP row operations. Wave
-// partials are merged through LDS and one (m, l, acc) partial per (request, query head,
-// split) is written.
+// Grid (split, KV head x head group, request), 4 waves per workgroup, at most 8 query
+// heads per workgroup (16 query heads per KV head run as two groups of 8). Wave w walks
+// pages split_begin + w, + 4, ... of its split with two page buffers in flight. In a page,
+// MFMA column n of K tile nt is slot 4n + nt, so lane (G, n) holds head G's scores of
+// slots 4n..4n+3; byte permutes turn its four P values into one dword per limb, and a
+// wave-private LDS block carries them into the A layout of the V MFMA (slots 16G..16G+15
+// per lane). Wave partials are merged through LDS and one (m, l, acc) partial per
+// (request, query head, split) is written.
 
 #include "device_common.h"
 #include "launch.h"
@@ -34,11 +38,12 @@ namespace oscar {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kPRow = 80;  // bytes of one P-limb row in LDS: 64 slots + 16 bytes of bank spread
 typedef char i8x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i8x16 unpack16(uint32_t w) {
-  // bytes of word m hold the codes at bits 2m..2m+1 of the packed word's four bytes
+  // register m holds the codes at bits 2m..2m+1 of the packed word's four bytes
   uint4 u;
   u.x = w & 0x03030303u;
   u.y = (w >> 2) & 0x03030303u;
@@ -51,41 +56,16 @@ __device__ __forceinline__ i32x4 mfma16(i8x16 a, i8x16 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// 2^e with e in [-1022, 1023]
-__device__ __forceinline__ double pow2(int e) { return __longlong_as_double(static_cast<long long>(e + 1023) << 52); }
+// 2^e as a double, e in [-1022, 1023]
+__device__ __forceinline__ double pow2d(int e) { return __longlong_as_double(static_cast<long long>(e + 1023) << 52); }
 
-// Fixed-point exponent: |x| <= amax < 2^k  ->  x * 2^(29 - k) has magnitude < 2^29.
-__device__ __forceinline__ int fixed_shift(double amax) {
-  if (!(amax > 0.0)) return 0;
-  int k;
-  frexp(amax, &k);  // amax = f * 2^k, 0.5 <= f < 1
-  return 29 - k;
-}
-
-// Four signed 8-bit limbs of v (|v| < 2^29), least significant first, packed in a word.
-__device__ __forceinline__ uint32_t limbs4(int v) {
-  const int l0 = static_cast<signed char>(v & 0xFF);
-  v = (v - l0) >> 8;
-  const int l1 = static_cast<signed char>(v & 0xFF);
-  v = (v - l1) >> 8;
-  const int l2 = static_cast<signed char>(v & 0xFF);
-  const int l3 = (v - l2) >> 8;
-  return (static_cast<uint32_t>(l0) & 0xFF) | ((static_cast<uint32_t>(l1) & 0xFF) << 8) |
-         ((static_cast<uint32_t>(l2) & 0xFF) << 16) | ((static_cast<uint32_t>(l3) & 0xFF) << 24);
-}
-
-__device__ __forceinline__ double combine_d(const i32x4& c) {
-  // sum_j 2^(8j) c_j, exact: each (hi, lo) pair fits 32 bits, the total fits fp64
-  const int lo = c[0] + c[1] * 256;
-  const int hi = c[2] + c[3] * 256;
-  return fma(static_cast<double>(hi), 65536.0, static_cast<double>(lo));
-}
-
-// sum_j 2^(7j) c_j for the V side's 7-bit limbs (fp32 result)
-__device__ __forceinline__ float combine7_f(const i32x4& c) {
-  const int lo = c[0] + c[1] * 128;
-  const int hi = c[2] + c[3] * 128;
-  return fmaf(static_cast<float>(hi), 16384.f, static_cast<float>(lo));
+// sum_t P_t c_t of one accumulator fragment: rows 0..2 are the XORed bytes of P, row 3 the
+// plain code sum; exact in fp64 (the value stays below 2^53 for any run of pages)
+__device__ __forceinline__ double v_combo(const i32x4& c) {
+  double r = static_cast<double>(c[3]) * 8421504.0;  // 128 (1 + 2^8 + 2^16)
+  r = fma(static_cast<double>(c[2]), 65536.0, r);
+  r = fma(static_cast<double>(c[1]), 256.0, r);
+  return r + static_cast<double>(c[0]);
 }
 
 struct PageRegs {
@@ -108,53 +88,30 @@ struct PageRegs {
 };
 
 // Lane l = 16 G + n reads its page data as six 16-byte loads (the page layout keeps each
-// lane's K and V words contiguous).
-__device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* __restrict__ blk, int lane, int n) {
-  const uint4* kp = reinterpret_cast<const uint4*>(blk + kKCodes + 32 * lane);
-  const uint4* vp = reinterpret_cast<const uint4*>(blk + kVCodes + 32 * lane);
-  r.k[0] = kp[0];
-  r.k[1] = kp[1];
-  r.km = *reinterpret_cast<const uint4*>(blk + kKMeta + 16 * n);
-  r.vm = *reinterpret_cast<const uint4*>(blk + kVMeta + 16 * n);
-  r.v[0] = vp[0];
-  r.v[1] = vp[1];
+// lane's K and V words contiguous). `blk` is wave-uniform.
+__device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* __restrict__ blk, uint32_t lane32,
+                                          uint32_t n16) {
+  r.k[0] = *reinterpret_cast<const uint4*>(blk + kKCodes + lane32);
+  r.k[1] = *reinterpret_cast<const uint4*>(blk + kKCodes + lane32 + 16);
+  r.km = *reinterpret_cast<const uint4*>(blk + kKMeta + n16);
+  r.vm = *reinterpret_cast<const uint4*>(blk + kVMeta + n16);
+  r.v[0] = *reinterpret_cast<const uint4*>(blk + kVCodes + lane32);
+  r.v[1] = *reinterpret_cast<const uint4*>(blk + kVCodes + lane32 + 16);
 }
 
-// Per-(wave, tile) state of the online softmax. V sums stay in int32 MFMA accumulators
-// (fixed point relative to the reference maximum m and scale 2^-E) until the reference or
-// the scale must change; then they are flushed into float sums.
-template <int MT>
-struct SoftmaxState {
-  float m[MT];         // reference maximum (log2 units), -inf before the first token
-  float l[MT];         // sum of 2^(s - m) over this lane's tokens
-  float z[MT];         // sum of 2^(s - m) * z_v over this lane's tokens
-  float vcap[MT];      // largest V scale the current fixed-point exponent can hold
-  float down[MT];      // 2^-E of the current fixed point
-  float up[MT];        // 2^E
-  float accf[MT][8];   // flushed V sums, relative to m
-  i32x4 acci[MT][8];   // pending V sums, 7-bit limbs, relative to m and 2^-E
-};
-
-template <int MT>
-__device__ __forceinline__ void flush_tile(SoftmaxState<MT>& st, int mt) {
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    st.accf[mt][dt] = fmaf(combine7_f(st.acci[mt][dt]), st.down[mt], st.accf[mt][dt]);
-    st.acci[mt][dt] = i32x4{0, 0, 0, 0};
-  }
-}
-
-// The rotated query of one (request, query head), once per call: q_rot = q R_K in fp64
-// (bf16 products are exact), its fixed-point limbs (|q_rot| * 2^sh < 2^29, four signed
-// 8-bit limbs) and two doubles: the score scale 2^-sh * sm_scale * log2(e) and the scaled
-// sum(q_rot). Thread t: wave rh sums rows 64 rh .. +63 at columns 2 lane, 2 lane + 1.
+// The rotated query of one (request, query head): q_rot = q R_K in fp64 (bf16 products
+// are exact), as Q = rint(q_rot 2^sh) with max|q_rot| 2^sh < 2^21, in three signed 8-bit
+// limbs (limb row 3 zero); the K accumulator starts -2 sum_d limb_l(Q_d); the score scale
+// 2^-sh sm_scale log2(e) and sm_scale log2(e) sum_d q_rot_d.
+// Thread t: wave rh sums rows 64 rh .. +63 at columns 2 lane, 2 lane + 1.
 __global__ __launch_bounds__(128) void qprep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ rot_k,
                                                     int n_q, int gq, double scale_log2, char* __restrict__ qlimb,
-                                                    double* __restrict__ qscal) {
+                                                    QueryScal* __restrict__ qscal) {
   __shared__ double qd_s[kHeadDim];
   __shared__ double part_s[2][kHeadDim];
   __shared__ float amax_s[2];
   __shared__ double sum_s[2];
+  __shared__ int lsum_s[2][3];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int kv = h / gq;
@@ -188,30 +145,74 @@ __global__ __launch_bounds__(128) void qprep_kernel(const uint16_t* __restrict__
     sum_s[rh] = sm;
   }
   __syncthreads();
-  // amax rounded to float can only move up to the next power of two: the shift stays safe
-  const int sh = fixed_shift(static_cast<double>(fmaxf(amax_s[0], amax_s[1])));
-  const uint32_t w = limbs4(static_cast<int>(rint(x * pow2(sh))));
+  // amax rounded to float can only move up to the next power of two: the bound holds
+  const float amax = fmaxf(amax_s[0], amax_s[1]);
+  int k = 0;
+  if (amax > 0.f) frexpf(amax, &k);  // amax < 2^k
+  const int sh = 21 - k;
+  const int Q = static_cast<int>(rint(x * pow2d(sh)));
+  const int l0 = static_cast<signed char>(Q & 0xFF);
+  const int r1 = (Q - l0) >> 8;
+  const int l1 = static_cast<signed char>(r1 & 0xFF);
+  const int l2 = (r1 - l1) >> 8;  // |l2| <= 33
   char* dst = qlimb + head * 512;
+  dst[t] = static_cast<char>(l0);
+  dst[kHeadDim + t] = static_cast<char>(l1);
+  dst[2 * kHeadDim + t] = static_cast<char>(l2);
+  dst[3 * kHeadDim + t] = 0;
+  // exact integer limb sums over the 128 dims
+  int s0 = l0, s1 = l1, s2 = l2;
 #pragma unroll
-  for (int l = 0; l < 4; ++l) dst[l * kHeadDim + t] = static_cast<char>((w >> (8 * l)) & 0xFF);
+  for (int o = 32; o >= 1; o >>= 1) {
+    s0 += __shfl_xor(s0, o, 64);
+    s1 += __shfl_xor(s1, o, 64);
+    s2 += __shfl_xor(s2, o, 64);
+  }
+  if (lane == 0) {
+    lsum_s[rh][0] = s0;
+    lsum_s[rh][1] = s1;
+    lsum_s[rh][2] = s2;
+  }
+  __syncthreads();
   if (t == 0) {
-    qscal[2 * head] = pow2(-sh) * scale_log2;
-    qscal[2 * head + 1] = (sum_s[0] + sum_s[1]) * scale_log2;
+    QueryScal o;
+    o.kinit[0] = -2 * (lsum_s[0][0] + lsum_s[1][0]);
+    o.kinit[1] = -2 * (lsum_s[0][1] + lsum_s[1][1]);
+    o.kinit[2] = -2 * (lsum_s[0][2] + lsum_s[1][2]);
+    o.kinit[3] = 0;
+    o.qsc = static_cast<float>(pow2d(-sh) * scale_log2);
+    o.sig = static_cast<float>((sum_s[0] + sum_s[1]) * scale_log2);
+    o.pad[0] = o.pad[1] = 0.f;
+    qscal[head] = o;
   }
 }
+
+// Per-wave online-softmax state of one M tile (4 heads; this lane: head 4 mt + G).
+// "Pending" sums are in units of 2^E relative to the reference maximum m (the V sums in
+// the int32 MFMA accumulators); "flushed" sums are true values relative to m.
+template <int MT>
+struct WaveState {
+  float m[MT];        // reference maximum, log2 units; -inf before the first page
+  float bias[MT];     // E - m (0 before the first page); -inf for padding heads
+  float lq[MT];       // pending sum of p 2^E over this lane's slots
+  float zq[MT];       // pending sum of p 2^E z^V
+  float lf[MT];       // flushed l
+  float zf[MT];       // flushed sum p z^V
+  float accf[MT][8];  // flushed sum p s^V c^V of dims 16 dt + n
+  i32x4 acci[MT][8];  // pending fragments (rows: 3 XORed limbs + code sum)
+};
 
 // GQ is the number of query heads one workgroup serves (at most 8); a KV head whose group
 // is larger is served by n_groups = (query heads per KV head) / GQ workgroups along y.
 template <int GQ>
 __global__ __launch_bounds__(256) void decode_int2_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ rot_k, const uint8_t* __restrict__ pool,
-    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ hist_len, int n_q,
-    int n_kv, int n_groups, int n_splits, const char* __restrict__ qlimb, const double* __restrict__ qscal,
-    float* __restrict__ out_m, float* __restrict__ out_l, float* __restrict__ out_acc) {
+    const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table, int max_pages,
+    const int32_t* __restrict__ hist_len, int n_q, int n_kv, int n_groups, int n_splits,
+    const char* __restrict__ qlimb, const QueryScal* __restrict__ qscal, float* __restrict__ out_m,
+    float* __restrict__ out_l, float* __restrict__ out_acc) {
   constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
-  constexpr int NH = 4 * MT;        // heads including padding rows
+  constexpr int kPBytes = kWaves * MT * 16 * kPRow;
   constexpr int kWaccBytes = kWaves * GQ * kHeadDim * 4;
-  constexpr int kPBytes = kWaves * NH * 4 * kPageTokens;
   constexpr int kScratch = kWaccBytes > kPBytes ? kWaccBytes : kPBytes;
 
   // page loop: P limbs of each wave; epilogue: wave partials
@@ -238,136 +239,200 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
   const int32_t* table = block_table + static_cast<size_t>(b) * max_pages;
   const uint8_t* head_base = pool + static_cast<size_t>(kv) * kHeadBlock;
   const size_t page_stride = static_cast<size_t>(n_kv) * kHeadBlock;
+  const uint32_t lane32 = 32u * lane;
+  const uint32_t n16 = 16u * n;
 
-  // the first page's loads go out together with the rotated query's
+  // block ids of this wave's pages: lane i holds page p_begin + wave + 4 i (first 64)
+  const int p0 = p_begin + wave;
+  const int n_mine = p0 < p_end ? (p_end - p0 + kWaves - 1) / kWaves : 0;
+  int blk_lane = (lane < n_mine) ? table[p0 + kWaves * lane] : 0;
+
   PageRegs buf[2];
-  int p = p_begin + wave;
-  if (p < p_end) load_page(buf[0], head_base + table[p] * page_stride, lane, n);
+  if (n_mine > 0) {
+    const int blk = __builtin_amdgcn_readfirstlane(blk_lane);
+    load_page(buf[0], head_base + static_cast<size_t>(blk) * page_stride, lane32, n16);
+  }
 
   // K-side A operands: row n of tile mt is (head 4mt + n/4, limb n%4); lane group G owns
   // dims 32G + 16ks .. +15 of K step ks. Rows of heads beyond GQ are zero.
   const size_t head0 = static_cast<size_t>(b) * n_q + h0;
   i8x16 aK[MT][2];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int g = 4 * mt + (n >> 2);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const i8x16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-      aK[mt][ks] = g < GQ ? *reinterpret_cast<const i8x16*>(qlimb + (head0 + g) * 512 + (n & 3) * kHeadDim +
-                                                            32 * G + 16 * ks)
-                          : zero16;
-    }
-  }
-  double qsc[MT], sgm[MT];
+  i32x4 kinit[MT];
+  float qsc[MT], sig[MT];
   bool head_ok[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
+    const int ga = 4 * mt + (n >> 2);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const i8x16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+      aK[mt][ks] = ga < GQ ? *reinterpret_cast<const i8x16*>(qlimb + (head0 + ga) * 512 + (n & 3) * kHeadDim +
+                                                             32 * G + 16 * ks)
+                           : zero16;
+    }
     const int g = 4 * mt + G;
     head_ok[mt] = g < GQ;
-    qsc[mt] = head_ok[mt] ? qscal[2 * (head0 + g)] : 0.0;
-    sgm[mt] = head_ok[mt] ? qscal[2 * (head0 + g) + 1] : 0.0;
+    if (head_ok[mt]) {
+      const QueryScal s = qscal[head0 + g];
+      kinit[mt] = i32x4{s.kinit[0], s.kinit[1], s.kinit[2], s.kinit[3]};
+      qsc[mt] = s.qsc;
+      sig[mt] = s.sig;
+    } else {
+      kinit[mt] = i32x4{0, 0, 0, 0};
+      qsc[mt] = sig[mt] = 0.f;
+    }
   }
 
-  SoftmaxState<MT> st;
+  WaveState<MT> st;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     st.m[mt] = -INFINITY;
-    st.l[mt] = st.z[mt] = 0.f;
-    st.vcap[mt] = -1.f;
-    st.down[mt] = st.up[mt] = 0.f;
+    st.bias[mt] = head_ok[mt] ? 0.f : -INFINITY;
+    st.lq[mt] = st.zq[mt] = st.lf[mt] = st.zf[mt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       st.accf[mt][dt] = 0.f;
       st.acci[mt][dt] = i32x4{0, 0, 0, 0};
     }
   }
-  char (*pl)[kPageTokens] = reinterpret_cast<char (*)[kPageTokens]>(scratch_s + wave * NH * 4 * kPageTokens);
+  int E = 0;            // fixed-point exponent of the pending sums (wave-uniform)
+  float vcap = -1.f;    // V scales below vcap fit the current E
+  bool fresh = true;    // no page processed yet
+
+  // wave-private P-limb rows: row mt*16 + 4 g + l; rows with l == 3 hold constant ones
+  unsigned char* pl = scratch_s + wave * (MT * 16 * kPRow);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    *reinterpret_cast<uint32_t*>(pl + (mt * 16 + 4 * G + 3) * kPRow + 4 * n) = 0x01010101u;
+
+  // fold the pending sums into the flushed ones and move to a new frame (m_new, E_new)
+  auto flush = [&](const float* m_new, int e_new) {
+    const double down = pow2d(-E);
+    const float downf = static_cast<float>(down);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float alpha = (st.m[mt] == -INFINITY || !head_ok[mt]) ? 0.f : exp2f(st.m[mt] - m_new[mt]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        st.accf[mt][dt] = (st.accf[mt][dt] + static_cast<float>(v_combo(st.acci[mt][dt]) * down)) * alpha;
+        st.acci[mt][dt] = i32x4{0, 0, 0, 0};
+      }
+      st.lf[mt] = fmaf(st.lq[mt], downf, st.lf[mt]) * alpha;
+      st.zf[mt] = fmaf(st.zq[mt], downf, st.zf[mt]) * alpha;
+      st.lq[mt] = st.zq[mt] = 0.f;
+      st.m[mt] = m_new[mt];
+      st.bias[mt] = head_ok[mt] ? static_cast<float>(e_new) - m_new[mt] : -INFINITY;
+    }
+    E = e_new;
+  };
 
   auto process = [&](const PageRegs& cur, int ntok) {
-    // K side: exact integer q_rot . c per (head, slot); all MFMAs first
-    i32x4 ck[MT][4];
+    // K side: rows (head, limb) x 16 slots per tile, accumulators start at the centring term
+    i32x4 d[MT][4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const i8x16 b0 = unpack16(cur.kword(nt, 0));
       const i8x16 b1 = unpack16(cur.kword(nt, 1));
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const i32x4 zero = {0, 0, 0, 0};
-        ck[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, zero));
-      }
+      for (int mt = 0; mt < MT; ++mt) d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, kinit[mt]));
     }
-    // the page's largest V scale (shared by all heads)
-    float sv[4], zv[4];
+    // slot metadata of this lane's slots 4n..4n+3
+    float sk[4], u[4], sv[4], zv[4];
+    bool valid[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      sv[nt] = f16_to_f32(cur.vmeta(nt));
-      zv[nt] = f16_to_f32(cur.vmeta(nt) >> 16);
+      const uint32_t km = cur.kmeta(nt);
+      const uint32_t vm = cur.vmeta(nt);
+      sk[nt] = f16_to_f32(km);
+      u[nt] = fmaf(2.f, sk[nt], f16_to_f32(km >> 16));  // z + 2 s
+      sv[nt] = f16_to_f32(vm);
+      zv[nt] = f16_to_f32(vm >> 16);
+      valid[nt] = true;
     }
-    const float vmax = row16_max(__builtin_fmaxf(__builtin_fmaxf(sv[0], sv[1]), __builtin_fmaxf(sv[2], sv[3])));
-
+    if (ntok < kPageTokens) {
+      // slots past the history end may hold stale bits: no weight, no scale
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        valid[nt] = 4 * n + nt < ntok;
+        sk[nt] = valid[nt] ? sk[nt] : 0.f;
+        u[nt] = valid[nt] ? u[nt] : 0.f;
+        sv[nt] = valid[nt] ? sv[nt] : 0.f;
+        zv[nt] = valid[nt] ? zv[nt] : 0.f;
+      }
+    }
+    // scores relative to the frame: x = score_log2 - m + E
+    float x[MT][4];
+    float xm[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      // scores in log2 units, folded in fp64
-      double sc[4];
-      float smax = -INFINITY;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const bool valid = head_ok[mt] && (4 * n + nt < ntok);
-        const double sk = static_cast<double>(f16_to_f32(cur.kmeta(nt)));
-        const double zk = static_cast<double>(f16_to_f32(cur.kmeta(nt) >> 16));
-        sc[nt] = valid ? fma(sk, combine_d(ck[mt][nt]) * qsc[mt], zk * sgm[mt]) : -INFINITY;
-        smax = __builtin_fmaxf(smax, static_cast<float>(sc[nt]));
+        const i32x4 c = d[mt][nt];
+        const int D = c[0] + (c[1] << 8) + (c[2] << 16);  // Q . (c - 2), exact
+        const float t = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sig[mt], st.bias[mt]));
+        x[mt][nt] = valid[nt] ? t : -INFINITY;
       }
-      smax = row16_max(smax);
-      const float m_new = __builtin_fmaxf(st.m[mt], smax);
-      if (m_new > st.m[mt] || vmax > st.vcap[mt]) {
-        // new reference or scale: fold the pending integer sums into the float sums, rescale
-        flush_tile(st, mt);
-        if (m_new > st.m[mt]) {
-          const float alpha = exp2f(st.m[mt] - m_new);
-          st.l[mt] *= alpha;
-          st.z[mt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) st.accf[mt][dt] *= alpha;
-          st.m[mt] = m_new;
-        }
-        if (vmax > st.vcap[mt]) {
-          // P = p s_v <= s_v < 2^k with one bit of headroom: P 2^(27 - k) < 2^27 fits four 7-bit limbs
-          int k = 0;
-          frexpf(vmax, &k);
-          const int e = 27 - k;
-          st.up[mt] = __int_as_float((e + 127) << 23);
-          st.down[mt] = __int_as_float((127 - e) << 23);
-          st.vcap[mt] = __int_as_float((k + 127) << 23);  // 2^k: room for V scales up to 2x vmax
-        }
-      }
-      uint32_t pi[4];
-      float psum = 0.f, zsum = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const float pt = (m_new == -INFINITY) ? 0.f : exp2f(static_cast<float>(sc[nt] - static_cast<double>(m_new)));
-        psum += pt;
-        zsum = fmaf(pt, zv[nt], zsum);
-        pi[nt] = static_cast<uint32_t>(rintf(pt * sv[nt] * st.up[mt]));
-      }
-      st.l[mt] += psum;
-      st.z[mt] += zsum;
-      // limb l of slots 4n..4n+3 -> one dword of row (head, limb)
-#pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        const uint32_t word = __builtin_amdgcn_ubfe(pi[0], 7 * l, 7) | (__builtin_amdgcn_ubfe(pi[1], 7 * l, 7) << 8) |
-                              (__builtin_amdgcn_ubfe(pi[2], 7 * l, 7) << 16) |
-                              (__builtin_amdgcn_ubfe(pi[3], 7 * l, 7) << 24);
-        *reinterpret_cast<uint32_t*>(&pl[(4 * mt + G) * 4 + l][4 * n]) = word;
-      }
+      xm[mt] = fmaxf(fmaxf(x[mt][0], x[mt][1]), fmaxf(x[mt][2], x[mt][3]));
     }
-    // the wave's own LDS writes must land before its lanes read each other's
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const float svm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bool need = svm > vcap;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) need = need || (xm[mt] > static_cast<float>(E));
+    if (fresh || __any(need)) {
+      // new reference maxima per head, new exponent for the wave's V scales
+      float m_new[MT], shift[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float r = row16_max(xm[mt]) - st.bias[mt];
+        m_new[mt] = head_ok[mt] ? fmaxf(st.m[mt], r) : -INFINITY;
+      }
+      int e_new = E;
+      const float vmax = wave_max_f32(svm);
+      if (vmax > vcap) {
+        int k = 0;
+        frexpf(vmax, &k);  // vmax < 2^k
+        e_new = 23 - k;    // P = p s 2^E < 2^23 while p <= 1 and s < 2^k
+        vcap = __builtin_ldexpf(1.f, k);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        shift[mt] = head_ok[mt] ? (static_cast<float>(e_new) - m_new[mt]) - st.bias[mt] : 0.f;
+      flush(m_new, e_new);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) x[mt][nt] = head_ok[mt] ? x[mt][nt] + shift[mt] : -INFINITY;
+      fresh = false;
+    }
+    // probabilities (units of 2^E), pending sums, P limbs
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      uint32_t P[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float pe = __builtin_amdgcn_exp2f(x[mt][nt]);
+        st.lq[mt] += pe;
+        st.zq[mt] = fmaf(pe, zv[nt], st.zq[mt]);
+        P[nt] = static_cast<uint32_t>(fmaf(pe, sv[nt], 0.5f));
+      }
+      // bytes l of the four P values into one dword per limb, XORed into signed range
+      const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
+      const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+      const uint32_t u01 = __builtin_amdgcn_perm(P[1], P[0], 0x0C0C0602u);
+      const uint32_t u23 = __builtin_amdgcn_perm(P[3], P[2], 0x0C0C0602u);
+      const uint32_t L0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
+      const uint32_t L1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
+      const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u) ^ 0x80808080u;
+      unsigned char* row = pl + (mt * 16 + 4 * G) * kPRow + 4 * n;
+      *reinterpret_cast<uint32_t*>(row) = L0;
+      *reinterpret_cast<uint32_t*>(row + kPRow) = L1;
+      *reinterpret_cast<uint32_t*>(row + 2 * kPRow) = L2;
+    }
+    // the wave's LDS operations run in order: the reads below see the writes above
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     i8x16 aP[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      aP[mt] = *reinterpret_cast<const i8x16*>(&pl[(4 * mt + (n >> 2)) * 4 + (n & 3)][16 * G]);
+    for (int mt = 0; mt < MT; ++mt) aP[mt] = *reinterpret_cast<const i8x16*>(pl + (mt * 16 + n) * kPRow + 16 * G);
     // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -375,29 +440,47 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) st.acci[mt][dt] = mfma16(aP[mt], bv, st.acci[mt][dt]);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
   // two page buffers in turn: the wave's next page loads while the current one is processed
-  for (; p < p_end; p += 2 * kWaves) {
-    const int p1 = p + kWaves;
-    if (p1 < p_end) load_page(buf[1], head_base + table[p1] * page_stride, lane, n);
-    process(buf[0], min(kPageTokens, nh - p * kPageTokens));
-    if (p1 >= p_end) break;
-    const int p2 = p1 + kWaves;
-    if (p2 < p_end) load_page(buf[0], head_base + table[p2] * page_stride, lane, n);
-    process(buf[1], min(kPageTokens, nh - p1 * kPageTokens));
+  for (int i0 = 0; i0 < n_mine; i0 += 64) {
+    if (i0 > 0) blk_lane = (i0 + lane < n_mine) ? table[p0 + kWaves * (i0 + lane)] : 0;
+    const int cnt = min(64, n_mine - i0);
+    for (int i = 0; i < cnt; i += 2) {
+      const int gi = i0 + i;
+      if (i + 1 < cnt) {
+        const int blk = __builtin_amdgcn_readlane(blk_lane, i + 1);
+        load_page(buf[1], head_base + static_cast<size_t>(blk) * page_stride, lane32, n16);
+      }
+      process(buf[0], min(kPageTokens, nh - (p0 + kWaves * gi) * kPageTokens));
+      if (i + 1 >= cnt) break;
+      if (i + 2 < cnt) {
+        const int blk = __builtin_amdgcn_readlane(blk_lane, i + 2);
+        load_page(buf[0], head_base + static_cast<size_t>(blk) * page_stride, lane32, n16);
+      } else if (i0 + 64 < n_mine) {
+        const int blk = table[p0 + kWaves * (i0 + 64)];
+        load_page(buf[0], head_base + static_cast<size_t>(__builtin_amdgcn_readfirstlane(blk)) * page_stride, lane32,
+                  n16);
+      }
+      process(buf[1], min(kPageTokens, nh - (p0 + kWaves * (gi + 1)) * kPageTokens));
+    }
   }
 
   // ---- wave partials: lane (G, n) holds head 4mt + G, dims 16dt + n (the buffer is the
   // one the P limbs used, so every wave must be done with its pages first)
+  if (!fresh) {
+    float m_keep[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) m_keep[mt] = st.m[mt];
+    flush(m_keep, E);
+  }
   __syncthreads();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    flush_tile(st, mt);
     const int g = 4 * mt + G;
-    const float l = row16_sum(st.l[mt]);
-    const float zs = row16_sum(st.z[mt]);
+    const float l = row16_sum(st.lf[mt]);
+    const float zs = row16_sum(st.zf[mt]);
     if (g < GQ) {
       if (n == 0) {
         wm_s[wave][g] = st.m[mt];
@@ -411,22 +494,22 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
 
   for (int idx = tid; idx < GQ * kHeadDim; idx += 256) {
     const int g = idx >> 7;
-    const int d = idx & 127;
+    const int dd = idx & 127;
     float big = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) big = __builtin_fmaxf(big, wm_s[w][g]);
+    for (int w = 0; w < kWaves; ++w) big = fmaxf(big, wm_s[w][g]);
     float l = 0.f, a = 0.f;
     if (big != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float s = exp2f(wm_s[w][g] - big);
+        const float s = wm_s[w][g] == -INFINITY ? 0.f : exp2f(wm_s[w][g] - big);
         l = fmaf(s, wl_s[w][g], l);
-        a = fmaf(s, wacc_s[w][g][d], a);
+        a = fmaf(s, wacc_s[w][g][dd], a);
       }
     }
     const size_t o = (static_cast<size_t>(b) * n_q + h0 + g) * n_splits + split;
-    out_acc[o * kHeadDim + d] = a;
-    if (d == 0) {
+    out_acc[o * kHeadDim + dd] = a;
+    if (dd == 0) {
       out_m[o] = big;
       out_l[o] = l;
     }
@@ -444,7 +527,6 @@ hipError_t launch(const LayerShape& L, const void* q, const void* rot_k, const v
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_int2_kernel<GQ>, dim3(n_splits, L.n_kv * n_groups, batch), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(rot_k),
                      static_cast<const uint8_t*>(pool), block_table, max_pages, hist_len, L.n_q, L.n_kv, n_groups,
                      n_splits, out.qlimb, out.qscal, out.m, out.l, out.acc);
   return hipGetLastError();

@@ -14,13 +14,24 @@ struct LayerShape {
   int window;    // BF16 window slots per request and KV head
 };
 
-// Offsets (in floats) of the m, l and acc arrays of a partial-result workspace.
+// Per (request, query head) scalars of the rotated query, written by the INT2 pass's
+// query preparation: the K-side accumulator starts of the three limb rows (and 0), the
+// score scale 2^-sh sm_scale log2(e) and sm_scale log2(e) sum(q_rot).
+struct QueryScal {
+  int32_t kinit[4];
+  float qsc;
+  float sig;
+  float pad[2];
+};
+static_assert(sizeof(QueryScal) == 32, "QueryScal is 32 bytes");
+
+// Views of the m, l and acc arrays of a partial-result workspace.
 struct PartialsView {
   float* m;
   float* l;
   float* acc;
-  char* qlimb;    // INT2 pass only: fixed-point limbs of the rotated query [B][Hq][4][128]
-  double* qscal;  // INT2 pass only: per (request, head) score scale and scaled sum(q_rot)
+  char* qlimb;        // INT2 pass only: fixed-point limbs of the rotated query [B][Hq][4][128]
+  QueryScal* qscal;   // INT2 pass only: [B][Hq]
 };
 
 size_t partials_bytes(int batch, int n_q, int n_splits);

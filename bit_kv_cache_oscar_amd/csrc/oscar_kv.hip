@@ -73,7 +73,7 @@ size_t partials_bytes(int batch, int n_q, int n_splits) {
   const size_t acc_off = align256(8 * n);
   const size_t ql_off = align256(acc_off + n * 128 * sizeof(float));
   const size_t qs_off = align256(ql_off + heads * 512);
-  return qs_off + heads * 16;
+  return qs_off + heads * sizeof(QueryScal);
 }
 
 PartialsView partials_view(void* base, int batch, int n_q, int n_splits) {
@@ -88,7 +88,7 @@ PartialsView partials_view(void* base, int batch, int n_q, int n_splits) {
   v.l = reinterpret_cast<float*>(p + 4 * n);
   v.acc = reinterpret_cast<float*>(p + acc_off);
   v.qlimb = p + ql_off;
-  v.qscal = reinterpret_cast<double*>(p + qs_off);
+  v.qscal = reinterpret_cast<QueryScal*>(p + qs_off);
   return v;
 }
 

@@ -51,7 +51,8 @@
  * empty split holds m = -inf, l = 0, acc = 0. INT2 partials hold acc in the rotated basis.
  * After acc (from the next multiple of 256 bytes) the INT2 pass keeps its per-(request,
  * query head) rotated-query data: 512 bytes of fixed-point limbs per head, then, from the
- * next multiple of 256 bytes, two doubles per head. oscar_merge does not read that tail.
+ * next multiple of 256 bytes, 32 bytes of scalars per head. oscar_merge does not read
+ * that tail.
  */
 #ifndef OSCAR_KV_H
 #define OSCAR_KV_H

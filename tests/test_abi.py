@@ -46,7 +46,7 @@ def test_helpers(lib):
     acc_off = a256(8 * n)
     ql_off = a256(acc_off + n * 512)
     qs_off = a256(ql_off + heads * 512)
-    assert L.oscar_partials_bytes(d, 2, 7) == qs_off + heads * 16
+    assert L.oscar_partials_bytes(d, 2, 7) == qs_off + heads * 32
     s = L.oscar_default_splits(d, 1, 32448)
     assert 1 <= s <= 507
     assert L.oscar_default_splits(d, 1, 0) == 1
