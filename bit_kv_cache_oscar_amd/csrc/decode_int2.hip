@@ -10,23 +10,26 @@
 //   acc     = sum_t (p_t s^V_t) c^V_t + sum_t p_t z^V_t
 // K side, per page: [4 heads x 4 rows] x [128 dims] x [64 tokens] on
 //   v_mfma_i32_16x16x64_i8. q_rot is a 22-bit fixed-point integer Q (|Q| <= 2^21) in three
-//   signed 8-bit limbs (rows 0..2 of a head; row 3 is zero). Each limb row's accumulator
-//   starts at -2 sum_d limb_d, so the MFMA yields sum_d limb_d (c_d - 2) and the three rows
-//   combine exactly in int32 into Q . (c - 2) (|.| <= 2^29). Centring the codes at 2 keeps
-//   the two terms of the fold small, so the fold runs in fp32.
+//   signed 8-bit limbs (rows 0..2 of a head; row 3 is zero), read from LDS each page. The
+//   three limb rows combine exactly in int32 into Q . c, and the per-head term -2 sum Q
+//   centres it to Q . (c - 2) (|.| <= 2^29). Centring the codes at 2 keeps the two terms of
+//   the fold small, so the fold runs in fp32.
 // V side, per page: [4 heads x 4 rows] x [64 tokens] x [16 dims] per dim tile. The
-//   weight P_t = p_t s^V_t 2^E is a 24-bit integer (E wave-uniform, chosen from the largest
-//   V scale seen so that P < 2^24); its three bytes, each XORed with 0x80 into signed
-//   range, are rows 0..2 of the head, so the MFMA yields sum_t (byte_l - 128) c_t. Row 3
-//   is constant 1 and yields sum_t c_t, which restores the 128 (1 + 2^8 + 2^16) offset.
+//   weight P'_t = round(p_t s^V_t 2^E / 2) is a 23-bit integer (E wave-uniform, chosen from
+//   the largest V scale seen so that p s 2^E < 2^24), read straight from the bits of the
+//   float p s 2^E + 2^24; its three low bytes, each in signed range after an XOR with 0x80
+//   (the exponent bit already sets it for the top one), are rows 0..2 of the head, so the
+//   MFMA yields sum_t (byte_l - 128) c_t. Row 3 is constant 1 and yields sum_t c_t, which
+//   restores the 128 (1 + 2^8 + 2^16) offset.
 //   The int32 accumulators run across pages and are folded into fp32 sums only when a
-//   head's reference maximum or the fixed-point exponent must change.
+//   head's reference maximum or the fixed-point exponent must change. A reference maximum
+//   moves only when a score exceeds it by more than kTau (log2 units), so p <= 2^kTau.
 //
 // Grid (split, KV head x head group, request), 4 waves per workgroup, at most 8 query
 // heads per workgroup (16 query heads per KV head run as two groups of 8). Wave w walks
 // pages split_begin + w, + 4, ... of its split with two page buffers in flight. In a page,
 // MFMA column n of K tile nt is slot 4n + nt, so lane (G, n) holds head G's scores of
-// slots 4n..4n+3; byte permutes turn its four P values into one dword per limb, and a
+// slots 4n..4n+3; byte permutes turn its four P' values into one dword per limb, and a
 // wave-private LDS block carries them into the A layout of the V MFMA (slots 16G..16G+15
 // per lane). Wave partials are merged through LDS and one (m, l, acc) partial per
 // (request, query head, split) is written.
@@ -38,9 +41,12 @@ namespace oscar {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kPRow = 80;  // bytes of one P-limb row in LDS: 64 slots + 16 bytes of bank spread
+constexpr int kPRow = 80;    // bytes of one P-limb row in LDS: 64 slots + 16 bytes of bank spread
+constexpr int kTau = 2;      // headroom of the softmax weights above the reference maximum (log2)
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor word 3 for gfx9-family
 typedef char i8x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ i8x16 unpack16(uint32_t w) {
   // register m holds the codes at bits 2m..2m+1 of the packed word's four bytes
@@ -58,14 +64,17 @@ __device__ __forceinline__ i32x4 mfma16(i8x16 a, i8x16 b, i32x4 c) {
 
 // 2^e as a double, e in [-1022, 1023]
 __device__ __forceinline__ double pow2d(int e) { return __longlong_as_double(static_cast<long long>(e + 1023) << 52); }
+// 2^e as a float, e in [-126, 127]
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }
 
-// sum_t P_t c_t of one accumulator fragment: rows 0..2 are the XORed bytes of P, row 3 the
-// plain code sum; exact in fp64 (the value stays below 2^53 for any run of pages)
-__device__ __forceinline__ double v_combo(const i32x4& c) {
-  double r = static_cast<double>(c[3]) * 8421504.0;  // 128 (1 + 2^8 + 2^16)
-  r = fma(static_cast<double>(c[2]), 65536.0, r);
-  r = fma(static_cast<double>(c[1]), 256.0, r);
-  return r + static_cast<double>(c[0]);
+// sum_t P'_t c_t of one accumulator fragment: rows 0..2 hold sum (byte_l - 128) c, row 3
+// sum c, so byte sums are c_l + 128 c_3 >= 0 and combine without cancellation in fp32
+__device__ __forceinline__ float v_combo(const i32x4& c) {
+  const int c3 = c[3] << 7;
+  const float b0 = static_cast<float>(c[0] + c3);
+  const float b1 = static_cast<float>(c[1] + c3);
+  const float b2 = static_cast<float>(c[2] + c3);
+  return fmaf(b2, 65536.f, fmaf(b1, 256.f, b0));
 }
 
 struct PageRegs {
@@ -87,21 +96,27 @@ struct PageRegs {
   }
 };
 
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int imm) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + imm, 0, 0));
+}
+
 // Lane l = 16 G + n reads its page data as six 16-byte loads (the page layout keeps each
-// lane's K and V words contiguous). `blk` is wave-uniform.
-__device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* __restrict__ blk, uint32_t lane32,
-                                          uint32_t n16) {
-  r.k[0] = *reinterpret_cast<const uint4*>(blk + kKCodes + lane32);
-  r.k[1] = *reinterpret_cast<const uint4*>(blk + kKCodes + lane32 + 16);
-  r.km = *reinterpret_cast<const uint4*>(blk + kKMeta + n16);
-  r.vm = *reinterpret_cast<const uint4*>(blk + kVMeta + n16);
-  r.v[0] = *reinterpret_cast<const uint4*>(blk + kVCodes + lane32);
-  r.v[1] = *reinterpret_cast<const uint4*>(blk + kVCodes + lane32 + 16);
+// lane's K and V words contiguous) through a raw buffer descriptor of the page's 4608-byte
+// head block, built in scalar registers from the wave-uniform page address.
+__device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* page, uint32_t lane32, uint32_t meta16) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page), 0, kHeadBlock, kRsrcWord3);
+  r.k[0] = load16(rs, lane32, kKCodes);
+  r.k[1] = load16(rs, lane32, kKCodes + 16);
+  r.km = load16(rs, meta16, 0);
+  r.vm = load16(rs, meta16, kVMeta - kKMeta);
+  r.v[0] = load16(rs, lane32, kVCodes);
+  r.v[1] = load16(rs, lane32, kVCodes + 16);
 }
 
 // The rotated query of one (request, query head): q_rot = q R_K in fp64 (bf16 products
 // are exact), as Q = rint(q_rot 2^sh) with max|q_rot| 2^sh < 2^21, in three signed 8-bit
-// limbs (limb row 3 zero); the K accumulator starts -2 sum_d limb_l(Q_d); the score scale
+// limbs (limb row 3 zero); the centring term -2 sum_d Q_d; the score scale
 // 2^-sh sm_scale log2(e) and sm_scale log2(e) sum_d q_rot_d.
 // Thread t: wave rh sums rows 64 rh .. +63 at columns 2 lane, 2 lane + 1.
 __global__ __launch_bounds__(128) void qprep_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ rot_k,
@@ -111,7 +126,7 @@ __global__ __launch_bounds__(128) void qprep_kernel(const uint16_t* __restrict__
   __shared__ double part_s[2][kHeadDim];
   __shared__ float amax_s[2];
   __shared__ double sum_s[2];
-  __shared__ int lsum_s[2][3];
+  __shared__ int lsum_s[2];
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int kv = h / gq;
@@ -160,47 +175,37 @@ __global__ __launch_bounds__(128) void qprep_kernel(const uint16_t* __restrict__
   dst[kHeadDim + t] = static_cast<char>(l1);
   dst[2 * kHeadDim + t] = static_cast<char>(l2);
   dst[3 * kHeadDim + t] = 0;
-  // exact integer limb sums over the 128 dims
-  int s0 = l0, s1 = l1, s2 = l2;
+  // exact integer sum of Q over the 128 dims: the centring term -2 sum Q
+  int sq = Q;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    s0 += __shfl_xor(s0, o, 64);
-    s1 += __shfl_xor(s1, o, 64);
-    s2 += __shfl_xor(s2, o, 64);
-  }
-  if (lane == 0) {
-    lsum_s[rh][0] = s0;
-    lsum_s[rh][1] = s1;
-    lsum_s[rh][2] = s2;
-  }
+  for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  if (lane == 0) lsum_s[rh] = sq;
   __syncthreads();
   if (t == 0) {
     QueryScal o;
-    o.kinit[0] = -2 * (lsum_s[0][0] + lsum_s[1][0]);
-    o.kinit[1] = -2 * (lsum_s[0][1] + lsum_s[1][1]);
-    o.kinit[2] = -2 * (lsum_s[0][2] + lsum_s[1][2]);
-    o.kinit[3] = 0;
     o.qsc = static_cast<float>(pow2d(-sh) * scale_log2);
     o.sig = static_cast<float>((sum_s[0] + sum_s[1]) * scale_log2);
-    o.pad[0] = o.pad[1] = 0.f;
+    o.kcent = -2 * (lsum_s[0] + lsum_s[1]);
+    o.pad[0] = o.pad[1] = o.pad[2] = o.pad[3] = o.pad[4] = 0;
     qscal[head] = o;
   }
 }
 
-// Per-wave online-softmax state of one M tile (4 heads; this lane: head 4 mt + G).
-// "Pending" sums are in units of 2^E relative to the reference maximum m (the V sums in
-// the int32 MFMA accumulators); "flushed" sums are true values relative to m.
+// Per-wave online-softmax state held in registers (this lane: head 4 mt + G of tile mt).
+// "Pending" sums are in units of 2^E relative to the reference maximum m (the V sums in the
+// int32 MFMA accumulators, in units of 2^(E-1)). The "flushed" sums (true values relative
+// to m: sum p s^V c^V per dim, l and sum p z^V) live in LDS, touched only when flushing.
 template <int MT>
 struct WaveState {
   float m[MT];        // reference maximum, log2 units; -inf before the first page
   float bias[MT];     // E - m (0 before the first page); -inf for padding heads
   float lq[MT];       // pending sum of p 2^E over this lane's slots
   float zq[MT];       // pending sum of p 2^E z^V
-  float lf[MT];       // flushed l
-  float zf[MT];       // flushed sum p z^V
-  float accf[MT][8];  // flushed sum p s^V c^V of dims 16 dt + n
-  i32x4 acci[MT][8];  // pending fragments (rows: 3 XORed limbs + code sum)
+  i32x4 acci[MT][8];  // pending fragments (rows: 3 XORed limbs + code sum), dims 16 dt + n
 };
+
+constexpr int kQRow = 144;   // bytes of one query-limb row in LDS: 128 dims + 16 of bank spread
+constexpr int kFlushed = 10;  // flushed values per lane and tile: 8 dim tiles, l, sum p z
 
 // GQ is the number of query heads one workgroup serves (at most 8); a KV head whose group
 // is larger is served by n_groups = (query heads per KV head) / GQ workgroups along y.
@@ -212,10 +217,14 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
     float* __restrict__ out_l, float* __restrict__ out_acc) {
   constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
   constexpr int kPBytes = kWaves * MT * 16 * kPRow;
+  constexpr int kFBytes = kWaves * MT * kFlushed * 64 * 4;
+  constexpr int kLoopBytes = kPBytes + kFBytes;
   constexpr int kWaccBytes = kWaves * GQ * kHeadDim * 4;
-  constexpr int kScratch = kWaccBytes > kPBytes ? kWaccBytes : kPBytes;
+  constexpr int kScratch = kWaccBytes > kLoopBytes ? kWaccBytes : kLoopBytes;
 
-  // page loop: P limbs of each wave; epilogue: wave partials
+  // page loop: query limbs; P' limbs and flushed sums of each wave. Epilogue: wave partials
+  // over the P' and flushed-sum space.
+  __shared__ __align__(16) unsigned char q_s[4 * MT * 4 * kQRow];
   __shared__ __align__(16) unsigned char scratch_s[kScratch];
   __shared__ float wm_s[kWaves][GQ];
   __shared__ float wl_s[kWaves][GQ];
@@ -240,105 +249,118 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
   const uint8_t* head_base = pool + static_cast<size_t>(kv) * kHeadBlock;
   const size_t page_stride = static_cast<size_t>(n_kv) * kHeadBlock;
   const uint32_t lane32 = 32u * lane;
-  const uint32_t n16 = 16u * n;
-
-  // block ids of this wave's pages: lane i holds page p_begin + wave + 4 i (first 64)
-  const int p0 = p_begin + wave;
-  const int n_mine = p0 < p_end ? (p_end - p0 + kWaves - 1) / kWaves : 0;
-  int blk_lane = (lane < n_mine) ? table[p0 + kWaves * lane] : 0;
-
-  PageRegs buf[2];
-  if (n_mine > 0) {
-    const int blk = __builtin_amdgcn_readfirstlane(blk_lane);
-    load_page(buf[0], head_base + static_cast<size_t>(blk) * page_stride, lane32, n16);
-  }
-
-  // K-side A operands: row n of tile mt is (head 4mt + n/4, limb n%4); lane group G owns
-  // dims 32G + 16ks .. +15 of K step ks. Rows of heads beyond GQ are zero.
+  const uint32_t meta16 = kKMeta + 16u * n;
   const size_t head0 = static_cast<size_t>(b) * n_q + h0;
-  i8x16 aK[MT][2];
-  i32x4 kinit[MT];
+
+  // query limbs of the workgroup's heads into LDS: row 4 g + l holds limb l of head g
+  // (rows of heads beyond GQ are zero)
+  for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 256) {
+    const int row = i >> 3;
+    const int c = i & 7;
+    const int g = row >> 2;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (g < GQ) v = *reinterpret_cast<const uint4*>(qlimb + (head0 + g) * 512 + (row & 3) * kHeadDim + 16 * c);
+    *reinterpret_cast<uint4*>(q_s + row * kQRow + 16 * c) = v;
+  }
   float qsc[MT], sig[MT];
+  int kcent[MT];
   bool head_ok[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int ga = 4 * mt + (n >> 2);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const i8x16 zero16 = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-      aK[mt][ks] = ga < GQ ? *reinterpret_cast<const i8x16*>(qlimb + (head0 + ga) * 512 + (n & 3) * kHeadDim +
-                                                             32 * G + 16 * ks)
-                           : zero16;
-    }
     const int g = 4 * mt + G;
     head_ok[mt] = g < GQ;
     if (head_ok[mt]) {
       const QueryScal s = qscal[head0 + g];
-      kinit[mt] = i32x4{s.kinit[0], s.kinit[1], s.kinit[2], s.kinit[3]};
+      kcent[mt] = s.kcent;
       qsc[mt] = s.qsc;
       sig[mt] = s.sig;
     } else {
-      kinit[mt] = i32x4{0, 0, 0, 0};
+      kcent[mt] = 0;
       qsc[mt] = sig[mt] = 0.f;
     }
   }
+  // The query operands must have arrived before the page loop: their loads then never
+  // count as outstanding inside it, and its waits let the next page keep loading.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(kcent[mt]), "v"(qsc[mt]), "v"(sig[mt]));
+
+  // block ids of this wave's pages p0, p0 + 4, ...: lane i of blk_lane holds the id of the
+  // wave's page 64 chunk + i
+  const int p0 = p_begin + wave;
+  const int n_mine = p0 < p_end ? (p_end - p0 + kWaves - 1) / kWaves : 0;
+  int chunk = 0;
+  int blk_lane = (lane < n_mine) ? table[p0 + kWaves * lane] : 0;
+  auto page_of = [&](int j) -> const uint8_t* {  // j wave-uniform, 0 <= j < n_mine
+    if ((j >> 6) != chunk) {
+      chunk = j >> 6;
+      const int i = 64 * chunk + lane;
+      blk_lane = (i < n_mine) ? table[p0 + kWaves * i] : 0;
+    }
+    return head_base + static_cast<size_t>(__builtin_amdgcn_readlane(blk_lane, j & 63)) * page_stride;
+  };
 
   WaveState<MT> st;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     st.m[mt] = -INFINITY;
     st.bias[mt] = head_ok[mt] ? 0.f : -INFINITY;
-    st.lq[mt] = st.zq[mt] = st.lf[mt] = st.zf[mt] = 0.f;
+    st.lq[mt] = st.zq[mt] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      st.accf[mt][dt] = 0.f;
-      st.acci[mt][dt] = i32x4{0, 0, 0, 0};
-    }
+    for (int dt = 0; dt < 8; ++dt) st.acci[mt][dt] = i32x4{0, 0, 0, 0};
   }
   int E = 0;            // fixed-point exponent of the pending sums (wave-uniform)
+  float thr = kTau;     // E + kTau: frame-relative scores above it move the reference
   float vcap = -1.f;    // V scales below vcap fit the current E
   bool fresh = true;    // no page processed yet
 
-  // wave-private P-limb rows: row mt*16 + 4 g + l; rows with l == 3 hold constant ones
+  // wave-private P'-limb rows: row mt*16 + 4 g + l; rows with l == 3 hold constant ones
   unsigned char* pl = scratch_s + wave * (MT * 16 * kPRow);
+  // wave-private flushed sums: [mt][k][lane], k < 8: dim tile k, 8: l, 9: sum p z
+  float* fl = reinterpret_cast<float*>(scratch_s + kPBytes) + wave * (MT * kFlushed * 64) + lane;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
     *reinterpret_cast<uint32_t*>(pl + (mt * 16 + 4 * G + 3) * kPRow + 4 * n) = 0x01010101u;
+#pragma unroll
+    for (int k = 0; k < kFlushed; ++k) fl[(mt * kFlushed + k) * 64] = 0.f;
+  }
 
-  // fold the pending sums into the flushed ones and move to a new frame (m_new, E_new)
-  auto flush = [&](const float* m_new, int e_new) {
-    const double down = pow2d(-E);
-    const float downf = static_cast<float>(down);
+  // fold tile mt's pending sums into the flushed ones, rescaled to the reference m_new
+  auto flush_tile = [&](int mt, float m_new) {
+    if (!fresh) {
+      const float alpha = st.m[mt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m[mt] - m_new);
+      const float down = pow2f(-E);
+      const float down_v = pow2f(1 - E);
+      float* f = fl + mt * kFlushed * 64;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const float alpha = (st.m[mt] == -INFINITY || !head_ok[mt]) ? 0.f : exp2f(st.m[mt] - m_new[mt]);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        st.accf[mt][dt] = (st.accf[mt][dt] + static_cast<float>(v_combo(st.acci[mt][dt]) * down)) * alpha;
-        st.acci[mt][dt] = i32x4{0, 0, 0, 0};
-      }
-      st.lf[mt] = fmaf(st.lq[mt], downf, st.lf[mt]) * alpha;
-      st.zf[mt] = fmaf(st.zq[mt], downf, st.zf[mt]) * alpha;
-      st.lq[mt] = st.zq[mt] = 0.f;
-      st.m[mt] = m_new[mt];
-      st.bias[mt] = head_ok[mt] ? static_cast<float>(e_new) - m_new[mt] : -INFINITY;
+      for (int dt = 0; dt < 8; ++dt) f[dt * 64] = fmaf(v_combo(st.acci[mt][dt]), down_v, f[dt * 64]) * alpha;
+      f[8 * 64] = fmaf(st.lq[mt], down, f[8 * 64]) * alpha;
+      f[9 * 64] = fmaf(st.zq[mt], down, f[9 * 64]) * alpha;
     }
-    E = e_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.acci[mt][dt] = i32x4{0, 0, 0, 0};
+    st.lq[mt] = st.zq[mt] = 0.f;
+    st.m[mt] = m_new;
   };
 
   auto process = [&](const PageRegs& cur, int ntok) {
-    // K side: rows (head, limb) x 16 slots per tile, accumulators start at the centring term
+    // K side: rows (head, limb) x 16 slots per tile
+    i8x16 aK[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        aK[mt][ks] = *reinterpret_cast<const i8x16*>(q_s + (16 * mt + n) * kQRow + 32 * G + 16 * ks);
     i32x4 d[MT][4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const i8x16 b0 = unpack16(cur.kword(nt, 0));
       const i8x16 b1 = unpack16(cur.kword(nt, 1));
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, kinit[mt]));
+      for (int mt = 0; mt < MT; ++mt)
+        d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, i32x4{0, 0, 0, 0}));
     }
     // slot metadata of this lane's slots 4n..4n+3
     float sk[4], u[4], sv[4], zv[4];
-    bool valid[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const uint32_t km = cur.kmeta(nt);
@@ -347,64 +369,65 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
       u[nt] = fmaf(2.f, sk[nt], f16_to_f32(km >> 16));  // z + 2 s
       sv[nt] = f16_to_f32(vm);
       zv[nt] = f16_to_f32(vm >> 16);
-      valid[nt] = true;
     }
+    // scores relative to the frame: x = score_log2 - m + E
+    float x[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const i32x4 c = d[mt][nt];
+        const int D = c[0] + (c[1] << 8) + (c[2] << 16) + kcent[mt];  // Q . (c - 2), exact
+        x[mt][nt] = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sig[mt], st.bias[mt]));
+      }
     if (ntok < kPageTokens) {
       // slots past the history end may hold stale bits: no weight, no scale
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        valid[nt] = 4 * n + nt < ntok;
-        sk[nt] = valid[nt] ? sk[nt] : 0.f;
-        u[nt] = valid[nt] ? u[nt] : 0.f;
-        sv[nt] = valid[nt] ? sv[nt] : 0.f;
-        zv[nt] = valid[nt] ? zv[nt] : 0.f;
+        const bool valid = 4 * n + nt < ntok;
+        sv[nt] = valid ? sv[nt] : 0.f;
+        zv[nt] = valid ? zv[nt] : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) x[mt][nt] = valid ? x[mt][nt] : -INFINITY;
       }
     }
-    // scores relative to the frame: x = score_log2 - m + E
-    float x[MT][4];
     float xm[MT];
+    bool over = false;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const i32x4 c = d[mt][nt];
-        const int D = c[0] + (c[1] << 8) + (c[2] << 16);  // Q . (c - 2), exact
-        const float t = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sig[mt], st.bias[mt]));
-        x[mt][nt] = valid[nt] ? t : -INFINITY;
-      }
       xm[mt] = fmaxf(fmaxf(x[mt][0], x[mt][1]), fmaxf(x[mt][2], x[mt][3]));
+      over = over || xm[mt] > thr;
     }
     const float svm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bool need = svm > vcap;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) need = need || (xm[mt] > static_cast<float>(E));
-    if (fresh || __any(need)) {
-      // new reference maxima per head, new exponent for the wave's V scales
-      float m_new[MT], shift[MT];
+    const bool vover = svm > vcap;
+    if (fresh || __any(over || vover)) {
+      // a new exponent for the wave's V scales moves every tile's frame
+      int e_new = E;
+      if (__any(vover)) {
+        int k = 0;
+        frexpf(wave_max_f32(svm), &k);  // largest V scale < 2^k
+        e_new = 24 - k - kTau;          // p s 2^E < 2^24 while p <= 2^kTau and s < 2^k
+        vcap = pow2f(k);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
+        // a head's reference moves to the page maximum when that exceeds it by kTau
         const float r = row16_max(xm[mt]) - st.bias[mt];
-        m_new[mt] = head_ok[mt] ? fmaxf(st.m[mt], r) : -INFINITY;
+        const float m_new = head_ok[mt] ? (r > st.m[mt] + kTau ? r : st.m[mt]) : -INFINITY;
+        if (fresh || e_new != E || __any(m_new != st.m[mt])) {
+          const float bias_new = head_ok[mt] ? static_cast<float>(e_new) - m_new : -INFINITY;
+          const float shift = head_ok[mt] ? bias_new - st.bias[mt] : 0.f;
+          flush_tile(mt, m_new);
+          st.bias[mt] = bias_new;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) x[mt][nt] = head_ok[mt] ? x[mt][nt] + shift : -INFINITY;
+        }
       }
-      int e_new = E;
-      const float vmax = wave_max_f32(svm);
-      if (vmax > vcap) {
-        int k = 0;
-        frexpf(vmax, &k);  // vmax < 2^k
-        e_new = 23 - k;    // P = p s 2^E < 2^23 while p <= 1 and s < 2^k
-        vcap = __builtin_ldexpf(1.f, k);
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        shift[mt] = head_ok[mt] ? (static_cast<float>(e_new) - m_new[mt]) - st.bias[mt] : 0.f;
-      flush(m_new, e_new);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) x[mt][nt] = head_ok[mt] ? x[mt][nt] + shift[mt] : -INFINITY;
+      E = e_new;
+      thr = static_cast<float>(E + kTau);
       fresh = false;
     }
-    // probabilities (units of 2^E), pending sums, P limbs
+    // probabilities (units of 2^E), pending sums, P' limbs
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       uint32_t P[4];
@@ -413,16 +436,18 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
         const float pe = __builtin_amdgcn_exp2f(x[mt][nt]);
         st.lq[mt] += pe;
         st.zq[mt] = fmaf(pe, zv[nt], st.zq[mt]);
-        P[nt] = static_cast<uint32_t>(fmaf(pe, sv[nt], 0.5f));
+        // pe sv < 2^24: the float pe sv + 2^24 holds round(pe sv / 2) in its mantissa, and its
+        // exponent's low bit is bit 23
+        P[nt] = __float_as_uint(fmaf(pe, sv[nt], 16777216.f));
       }
-      // bytes l of the four P values into one dword per limb, XORed into signed range
+      // byte l of the four P' values into one dword per limb, in signed range
       const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
       const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
       const uint32_t u01 = __builtin_amdgcn_perm(P[1], P[0], 0x0C0C0602u);
       const uint32_t u23 = __builtin_amdgcn_perm(P[3], P[2], 0x0C0C0602u);
       const uint32_t L0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
       const uint32_t L1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
-      const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u) ^ 0x80808080u;
+      const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // bit 7 set by the exponent
       unsigned char* row = pl + (mt * 16 + 4 * G) * kPRow + 4 * n;
       *reinterpret_cast<uint32_t*>(row) = L0;
       *reinterpret_cast<uint32_t*>(row + kPRow) = L1;
@@ -443,51 +468,47 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
-  // two page buffers in turn: the wave's next page loads while the current one is processed
-  for (int i0 = 0; i0 < n_mine; i0 += 64) {
-    if (i0 > 0) blk_lane = (i0 + lane < n_mine) ? table[p0 + kWaves * (i0 + lane)] : 0;
-    const int cnt = min(64, n_mine - i0);
-    for (int i = 0; i < cnt; i += 2) {
-      const int gi = i0 + i;
-      if (i + 1 < cnt) {
-        const int blk = __builtin_amdgcn_readlane(blk_lane, i + 1);
-        load_page(buf[1], head_base + static_cast<size_t>(blk) * page_stride, lane32, n16);
-      }
-      process(buf[0], min(kPageTokens, nh - (p0 + kWaves * gi) * kPageTokens));
-      if (i + 1 >= cnt) break;
-      if (i + 2 < cnt) {
-        const int blk = __builtin_amdgcn_readlane(blk_lane, i + 2);
-        load_page(buf[0], head_base + static_cast<size_t>(blk) * page_stride, lane32, n16);
-      } else if (i0 + 64 < n_mine) {
-        const int blk = table[p0 + kWaves * (i0 + 64)];
-        load_page(buf[0], head_base + static_cast<size_t>(__builtin_amdgcn_readfirstlane(blk)) * page_stride, lane32,
-                  n16);
-      }
-      process(buf[1], min(kPageTokens, nh - (p0 + kWaves * (gi + 1)) * kPageTokens));
+  // two page buffers in turn: the wave's next page loads while the current one is processed.
+  // The prefetch is unconditional (the last page asks for itself again, an L2 hit), so no
+  // path without it joins between the loads and the use of the current page.
+  auto ntok_of = [&](int j) { return min(kPageTokens, nh - (p0 + kWaves * j) * kPageTokens); };
+  __syncthreads();  // query limbs in LDS
+  if (n_mine > 0) {
+    PageRegs buf[2];
+    load_page(buf[0], page_of(0), lane32, meta16);
+    for (int i = 0;;) {
+      load_page(buf[1], page_of(min(i + 1, n_mine - 1)), lane32, meta16);
+      process(buf[0], ntok_of(i));
+      if (++i >= n_mine) break;
+      load_page(buf[0], page_of(min(i + 1, n_mine - 1)), lane32, meta16);
+      process(buf[1], ntok_of(i));
+      if (++i >= n_mine) break;
     }
   }
 
-  // ---- wave partials: lane (G, n) holds head 4mt + G, dims 16dt + n (the buffer is the
-  // one the P limbs used, so every wave must be done with its pages first)
-  if (!fresh) {
-    float m_keep[MT];
+  // ---- wave partials: lane (G, n) holds head 4mt + G, dims 16dt + n
+  float accf[MT][8], lf[MT], zf[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) m_keep[mt] = st.m[mt];
-    flush(m_keep, E);
+  for (int mt = 0; mt < MT; ++mt) {
+    if (!fresh) flush_tile(mt, st.m[mt]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) accf[mt][dt] = fl[(mt * kFlushed + dt) * 64];
+    lf[mt] = fl[(mt * kFlushed + 8) * 64];
+    zf[mt] = fl[(mt * kFlushed + 9) * 64];
   }
-  __syncthreads();
+  __syncthreads();  // every wave has read its flushed sums: the space becomes wacc_s
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int g = 4 * mt + G;
-    const float l = row16_sum(st.lf[mt]);
-    const float zs = row16_sum(st.zf[mt]);
+    const float l = row16_sum(lf[mt]);
+    const float zs = row16_sum(zf[mt]);
     if (g < GQ) {
       if (n == 0) {
         wm_s[wave][g] = st.m[mt];
         wl_s[wave][g] = l;
       }
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) wacc_s[wave][g][16 * dt + n] = st.accf[mt][dt] + zs;
+      for (int dt = 0; dt < 8; ++dt) wacc_s[wave][g][16 * dt + n] = accf[mt][dt] + zs;
     }
   }
   __syncthreads();

@@ -15,13 +15,13 @@ struct LayerShape {
 };
 
 // Per (request, query head) scalars of the rotated query, written by the INT2 pass's
-// query preparation: the K-side accumulator starts of the three limb rows (and 0), the
-// score scale 2^-sh sm_scale log2(e) and sm_scale log2(e) sum(q_rot).
+// query preparation: the score scale 2^-sh sm_scale log2(e), sm_scale log2(e) sum(q_rot)
+// and the centring term -2 sum(Q) of the fixed-point query Q.
 struct QueryScal {
-  int32_t kinit[4];
   float qsc;
   float sig;
-  float pad[2];
+  int32_t kcent;
+  int32_t pad[5];
 };
 static_assert(sizeof(QueryScal) == 32, "QueryScal is 32 bytes");
 
