@@ -1,5 +1,6 @@
 """Benchmark: one OSCAR decode step (demote the oldest recent token of each request into
-INT2 history, INT2 history pass, BF16 sink/recent pass, merge) on one MI355X.
+INT2 history, BF16 sink/recent pass, INT2 history pass, merge and un-rotation) on one
+MI355X, through oscar_decode_step (two launches: prepare, attend).
 
 Workload (default): a Qwen3-8B-shaped attention layer, batch 1, 32,768 tokens of context
 (64 BF16 sink / 32,448 INT2 history / 256 BF16 recent), 32 query heads over 8 KV heads,
@@ -9,9 +10,10 @@ step reads its KV pool from HBM, not from the 256 MB last-level cache, as a real
 per-layer decode does.
 
 Prints one JSON line. `value` is the whole step's algorithmic HBM bytes divided by its
-time (GB/s); `roofline` reports the dominant kernel (the INT2 history pass) against the
-8 TB/s HBM peak, timed with events on its own stream inside the timed region;
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+time (GB/s); `roofline` reports the dominant kernel (the attend launch: INT2 history pass
+and merge) against the 8 TB/s HBM peak, timed with events on its stream over back-to-back
+oscar_attend launches; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
+same workload.
 """
 
 from __future__ import annotations
@@ -34,7 +36,7 @@ WIN_BYTES = 512          # per BF16 window token per KV head (K + V)
 ROT_BYTES = 128 * 128 * 2
 COPY_BYTES = 256 * 2 ** 20  # the plain copy whose counter readings calibrate FETCH_SIZE / WRITE_SIZE
 CSRC = os.path.join(ROOT, "bit_kv_cache_oscar_amd", "csrc")
-INT2_SOURCES = ("decode_int2.hip", "device_common.h", "launch.h")
+ATTEND_SOURCES = ("step.hip", "int2_pass.h", "merge_pass.h", "device_common.h", "launch.h")
 
 
 def parse():
@@ -56,26 +58,27 @@ def step_bytes(w):
     rot = 2 * w.n_kv_heads * ROT_BYTES
     qo = w.batch * w.n_q_heads * 128 * (2 + 4)
     demote = w.batch * w.n_kv_heads * (2 * 256 + HIST_BYTES)
-    int2 = hist + w.n_kv_heads * ROT_BYTES + w.batch * w.n_q_heads * 256
-    return hist + win + rot + qo + demote, int2
+    # the attend launch: history pages, R_V for the un-rotation, the output
+    attend = hist + w.n_kv_heads * ROT_BYTES + w.batch * w.n_q_heads * 128 * 4
+    return hist + win + rot + qo + demote, attend
 
 
-def int2_source_hash():
+def attend_source_hash():
     import hashlib
 
     h = hashlib.sha256()
-    for f in INT2_SOURCES:
+    for f in ATTEND_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
 def measured_traffic(workload):
-    """HBM bytes per launch of the INT2 kernel from the committed counter summary of this
+    """HBM bytes per launch of the attend kernel from the committed counter summary of this
     workload, or None when there is none or the kernel source changed since it was taken.
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same counter
     reads for a plain copy of COPY_BYTES bytes in the same run."""
-    path = os.path.join(ROOT, "profiles", f"decode_int2_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -84,7 +87,7 @@ def measured_traffic(workload):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        if kv.get("kernel_source_sha256") != int2_source_hash():
+        if kv.get("kernel_source_sha256") != attend_source_hash():
             return None
         f = float(kv["fetch_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_fetch_kib"])
         wr = float(kv["write_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_write_kib"])
@@ -171,8 +174,7 @@ def main():
     import torch
 
     import synth
-    from bit_kv_cache_oscar_amd import (oscar_decode_bf16, oscar_decode_int2, oscar_default_splits, oscar_demote,
-                                        oscar_merge)
+    from bit_kv_cache_oscar_amd import oscar_attend, oscar_default_splits
     from bit_kv_cache_oscar_amd.layer import LayerCache
     from bit_kv_cache_oscar_amd.rotation import layer_rotations_from_calibration, layer_rotations_from_gram
 
@@ -180,7 +182,7 @@ def main():
     dev = torch.device("cuda:0")
     w = synth.workload(args.config)
     table, n_phys = synth.block_table(w)
-    total_bytes, int2_bytes = step_bytes(w)
+    total_bytes, attend_bytes = step_bytes(w)
     layers = args.layers or max(2, -(-512 * 2 ** 20 // max(total_bytes, 1)))
 
     # rotations: the library's host builder from the synthetic calibration data
@@ -244,16 +246,11 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def int2(c):
-        oscar_decode_int2(c.desc, q, c.rot_k, c.pool, c.block_table, c.hist_len, w.sm_scale, c.n_splits,
-                          c.partials, stream)
+    def attend(c):
+        oscar_attend(c.desc, c.rot_v, c.pool, c.block_table, c.hist_len, c.n_splits, c.workspace, c.out, stream)
 
     def step(c):
-        oscar_demote(c.desc, step_k, step_v, step_page, step_slot, c.rot_k, c.rot_v, c.clip_k, c.clip_v, c.pool,
-                     stream)
-        int2(c)
-        oscar_decode_bf16(c.desc, q, c.k_win, c.v_win, c.win_len, w.sm_scale, c.win_partials, stream)
-        oscar_merge(c.desc, c.partials, c.n_splits, c.win_partials, c.rot_v, c.out, stream)
+        c.step(step_k, step_v, step_page, step_slot, q, w.sm_scale, stream)
 
     def timed(fn, k):
         start = torch.cuda.Event(enable_timing=True)
@@ -266,13 +263,16 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / k
 
+    for c in insts:  # every instance's workspace allocated and prepared before any timing
+        step(c)
     for i in range(args.warmup):
         step(insts[i % layers])
     torch.cuda.synchronize()
-    # timed region 1: whole steps back to back; timed region 2: the dominant kernel alone,
-    # launched back to back on the same stream over the same layer instances
+    # timed region 1: whole steps back to back; timed region 2: the dominant kernel (attend)
+    # alone, launched back to back on the same stream over the same layer instances (each
+    # instance's workspace holds its prepared query and window partials from the warm-up)
     ms = timed(step, args.steps)
-    int2_ms = timed(int2, args.steps)
+    attend_ms = timed(attend, args.steps)
 
     out = {
         "metric": METRIC,
@@ -299,22 +299,22 @@ def main():
             "page_tokens": 64,
             "int2_splits": splits,
             "layer_instances": layers,
-            "step": "demote 1 token/request + INT2 pass + BF16 pass + merge",
+            "step": "oscar_decode_step: demote 1 token/request + BF16 pass + INT2 pass + merge",
         },
         "step_bytes": total_bytes,
         "pct_of_hbm_peak": round(100 * total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
         "context_tokens_per_s": round(sum(w.ctx_lens) / (ms * 1e-3), 1),
         "roofline": {
-            "kernel": "decode_int2_kernel",
+            "kernel": "main_kernel (oscar_attend: INT2 history pass + merge)",
             "bound": "hbm",
-            "achieved": round(int2_bytes / (int2_ms * 1e-3) / 1e9, 2),
+            "achieved": round(attend_bytes / (attend_ms * 1e-3) / 1e9, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(int2_bytes / (int2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "frac": round(attend_bytes / (attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.name),
-            "us_per_launch": round(int2_ms * 1e3, 3),
-            "bytes_per_launch": int2_bytes,
+            "us_per_launch": round(attend_ms * 1e3, 3),
+            "bytes_per_launch": attend_bytes,
         },
     }
     if args.cpu_seconds > 0:

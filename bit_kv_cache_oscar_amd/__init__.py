@@ -17,15 +17,20 @@ from ._lib import (  # noqa: F401
     OscarError,
     layer_desc,
     lib,
+    oscar_attend,
     oscar_check_desc,
+    oscar_decode,
     oscar_decode_bf16,
     oscar_decode_int2,
+    oscar_decode_step,
+    oscar_decode_workspace_bytes,
     oscar_default_splits,
     oscar_demote,
     oscar_last_error,
     oscar_merge,
     oscar_page_bytes,
     oscar_partials_bytes,
+    oscar_prepare,
     oscar_status_string,
     oscar_version,
     oscar_window_splits,

@@ -62,6 +62,19 @@ _SIGNATURES = {
                                     c_float, c_void_p, c_size_t, c_void_p]),
     "oscar_merge": (c_int32, [POINTER(LayerDesc), c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                               c_int32, c_void_p]),
+    "oscar_decode_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_decode_step": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
+                                    c_void_p, c_void_p]),
+    "oscar_decode": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                               c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
+                               c_void_p, c_void_p]),
+    "oscar_prepare": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
+    "oscar_attend": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
+                               c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
 }
 
 
@@ -162,6 +175,10 @@ def oscar_default_splits(desc: LayerDesc, batch: int, max_hist_len: int) -> int:
     return lib().oscar_default_splits(byref(desc), batch, max_hist_len)
 
 
+def oscar_decode_workspace_bytes(desc: LayerDesc, batch: int, n_splits: int) -> int:
+    return lib().oscar_decode_workspace_bytes(byref(desc), batch, n_splits)
+
+
 # ------------------------------------------------------------------------------ entry points
 
 
@@ -239,3 +256,121 @@ def oscar_merge(desc: LayerDesc, partials, n_splits: int, win_partials, rot_v, o
     _need(win_partials.numel() * win_partials.element_size() >= wneed, "win_partials too small")
     _check(lib().oscar_merge(byref(desc), _ptr(partials), int(n_splits), _ptr(win_partials), _ptr(rot_v),
                              _ptr(out), batch, _stream(stream)))
+
+
+def _check_decode_args(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
+                       n_splits: int, workspace, out):
+    import torch
+
+    batch = int(q.shape[0])
+    _device16(q, "q")
+    _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
+    for t, name in ((rot_k, "rot_k"), (rot_v, "rot_v")):
+        _device16(t, name)
+        _need(t.numel() == desc.n_kv_heads * HEAD_DIM * HEAD_DIM, f"{name} must be [n_kv_heads, 128, 128]")
+    _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
+    _need(block_table.dim() == 2 and block_table.shape[0] == batch, "block_table must be [batch, max_pages]")
+    _device_i32(block_table, "block_table")
+    _device_i32(hist_len, "hist_len", batch)
+    w = desc.sink_tokens + desc.recent_tokens
+    for t, name in ((k_win, "k_win"), (v_win, "v_win")):
+        _device16(t, name)
+        _need(t.numel() == batch * desc.n_kv_heads * w * HEAD_DIM, f"{name} must be [batch, n_kv_heads, {w}, 128]")
+    _device_i32(win_len, "win_len", batch)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous(), "out must be contiguous float32")
+    _need(out.numel() == batch * desc.n_q_heads * HEAD_DIM, "out must be [batch, n_q_heads, 128]")
+    return batch, workspace.numel() * workspace.element_size()
+
+
+def oscar_decode(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
+                 sm_scale: float, n_splits: int, workspace, out, stream=None):
+    """Decode attention over the three segments in two launches; workspace from
+    oscar_decode_workspace_bytes(desc, B, n_splits); out [B, Hq, 128] float32."""
+    batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
+                                       n_splits, workspace, out)
+    _check(lib().oscar_decode(byref(desc), _ptr(q), _ptr(rot_k), _ptr(rot_v), _ptr(pool), _ptr(block_table),
+                              int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win), _ptr(win_len),
+                              batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out),
+                              _stream(stream)))
+
+
+def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool,
+                      block_table, hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace, out,
+                      stream=None):
+    """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16, n may be 0) and decode, in two launches."""
+    batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
+                                       n_splits, workspace, out)
+    n = int(k_src.shape[0]) if k_src is not None and k_src.dim() else 0
+    if n:
+        hkv = desc.n_kv_heads
+        _device16(k_src, "k_src")
+        _device16(v_src, "v_src")
+        _need(k_src.numel() == n * hkv * HEAD_DIM and v_src.numel() == n * hkv * HEAD_DIM,
+              "k_src/v_src must be [n, n_kv_heads, 128]")
+        _device_i32(dst_page, "dst_page", n)
+        _device_i32(dst_slot, "dst_slot", n)
+        for t, name in ((clip_k, "clip_k"), (clip_v, "clip_v")):
+            _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
+                  f"{name} must be float32 [n_kv_heads] on the device")
+    _check(lib().oscar_decode_step(byref(desc), _ptr(k_src) if n else None, _ptr(v_src) if n else None, n,
+                                   _ptr(dst_page) if n else None, _ptr(dst_slot) if n else None,
+                                   _ptr(clip_k) if n else None, _ptr(clip_v) if n else None, _ptr(q), _ptr(rot_k),
+                                   _ptr(rot_v), _ptr(pool), _ptr(block_table), int(block_table.shape[1]),
+                                   _ptr(hist_len), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch, float(sm_scale),
+                                   int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream)))
+
+
+def oscar_attend(desc: LayerDesc, rot_v, pool, block_table, hist_len, n_splits: int, workspace, out, stream=None):
+    """The second launch of oscar_decode_step alone (INT2 pass + merge into out)."""
+    import torch
+
+    batch = int(out.shape[0])
+    _device16(rot_v, "rot_v")
+    _need(rot_v.numel() == desc.n_kv_heads * HEAD_DIM * HEAD_DIM, "rot_v must be [n_kv_heads, 128, 128]")
+    _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
+    _need(block_table.dim() == 2 and block_table.shape[0] == batch, "block_table must be [batch, max_pages]")
+    _device_i32(block_table, "block_table")
+    _device_i32(hist_len, "hist_len", batch)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous(), "out must be contiguous float32")
+    _need(out.numel() == batch * desc.n_q_heads * HEAD_DIM, "out must be [batch, n_q_heads, 128]")
+    _check(lib().oscar_attend(byref(desc), _ptr(rot_v), _ptr(pool), _ptr(block_table), int(block_table.shape[1]),
+                              _ptr(hist_len), batch, int(n_splits), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+
+
+def oscar_prepare(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win,
+                  v_win, win_len, sm_scale: float, n_splits: int, workspace, stream=None):
+    """The first launch of oscar_decode_step alone (demotion, window pass, query rotation)."""
+    batch = int(q.shape[0])
+    _device16(q, "q")
+    _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
+    for t, name in ((rot_k, "rot_k"), (rot_v, "rot_v")):
+        _device16(t, name)
+        _need(t.numel() == desc.n_kv_heads * HEAD_DIM * HEAD_DIM, f"{name} must be [n_kv_heads, 128, 128]")
+    w = desc.sink_tokens + desc.recent_tokens
+    for t, name in ((k_win, "k_win"), (v_win, "v_win")):
+        _device16(t, name)
+        _need(t.numel() == batch * desc.n_kv_heads * w * HEAD_DIM, f"{name} must be [batch, n_kv_heads, {w}, 128]")
+    _device_i32(win_len, "win_len", batch)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    n = int(k_src.shape[0]) if k_src is not None and k_src.dim() else 0
+    if n:
+        hkv = desc.n_kv_heads
+        _device16(k_src, "k_src")
+        _device16(v_src, "v_src")
+        _need(k_src.numel() == n * hkv * HEAD_DIM and v_src.numel() == n * hkv * HEAD_DIM,
+              "k_src/v_src must be [n, n_kv_heads, 128]")
+        _device_i32(dst_page, "dst_page", n)
+        _device_i32(dst_slot, "dst_slot", n)
+        for t, name in ((clip_k, "clip_k"), (clip_v, "clip_v")):
+            _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
+                  f"{name} must be float32 [n_kv_heads] on the device")
+        _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
+    _check(lib().oscar_prepare(byref(desc), _ptr(k_src) if n else None, _ptr(v_src) if n else None, n,
+                               _ptr(dst_page) if n else None, _ptr(dst_slot) if n else None,
+                               _ptr(clip_k) if n else None, _ptr(clip_v) if n else None, _ptr(q), _ptr(rot_k),
+                               _ptr(rot_v), _ptr(pool), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch,
+                               float(sm_scale), int(n_splits), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -1,0 +1,581 @@
+// INT2 history pass of decode attention on the gfx950 matrix cores: device code shared
+// by the standalone INT2 kernels and the fused decode kernels.
+//
+// Method: OSCAR; QbitAI article on OSCAR, serving-path section: the INT2 kernel unpacks
+// the 2-bit codes, dequantises with the per-group scale and zero point and accumulates
+// in floating point; its result is joined with the BF16 sink/recent pass by an
+// online-softmax merge.
+//
+// Both contractions run on the raw codes, with the dequantisation folded out:
+//   score_t = s_t (q_rot . (c_t - 2)) + (z_t + 2 s_t) sum(q_rot)
+//   acc     = sum_t (p_t s^V_t) c^V_t + sum_t p_t z^V_t
+// K side, per page: [4 heads x 4 rows] x [128 dims] x [64 tokens] on
+//   v_mfma_i32_16x16x64_i8. q_rot is a 22-bit fixed-point integer Q (|Q| <= 2^21) in three
+//   signed 8-bit limbs (rows 0..2 of a head; row 3 is zero), read from LDS each page. The
+//   three limb rows combine exactly in int32 into Q . c, and the per-head term -2 sum Q
+//   centres it to Q . (c - 2) (|.| <= 2^29). Centring the codes at 2 keeps the two terms of
+//   the fold small, so the fold runs in fp32.
+// V side, per page: [4 heads x 4 rows] x [64 tokens] x [16 dims] per dim tile. The
+//   weight P'_t = round(p_t s^V_t 2^E / 2) is a 23-bit integer (E wave-uniform, chosen from
+//   the largest V scale seen so that p s 2^E < 2^24), read straight from the bits of the
+//   float p s 2^E + 2^24; its three low bytes, each in signed range after an XOR with 0x80
+//   (the exponent bit already sets it for the top one), are rows 0..2 of the head, so the
+//   MFMA yields sum_t (byte_l - 128) c_t. Row 3 is constant 1 and yields sum_t c_t, which
+//   restores the 128 (1 + 2^8 + 2^16) offset.
+//   The int32 accumulators run across pages and are folded into fp32 sums only when a
+//   head's reference maximum or the fixed-point exponent must change. A reference maximum
+//   moves only when a score exceeds it by more than kTau (log2 units), so p <= 2^kTau.
+//
+// A workgroup serves one (history split, KV head x head group, request), 4 waves, at most 8
+// query heads (16 query heads per KV head run as two groups of 8). Wave w walks
+// pages split_begin + w, + 4, ... of its split with two page buffers in flight. In a page,
+// MFMA column n of K tile nt is slot 4n + nt, so lane (G, n) holds head G's scores of
+// slots 4n..4n+3; byte permutes turn its four P' values into one dword per limb, and a
+// wave-private LDS block carries them into the A layout of the V MFMA (slots 16G..16G+15
+// per lane). Wave partials are merged through LDS and one (m, l, acc) partial per
+// (request, query head, split) is written.
+
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace oscar {
+namespace int2 {
+
+constexpr int kWaves = 4;
+constexpr int kPRow = 80;    // bytes of one P-limb row in LDS: 64 slots + 16 bytes of bank spread
+constexpr int kTau = 2;      // headroom of the softmax weights above the reference maximum (log2)
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor word 3 for gfx9-family
+typedef char i8x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i8x16 unpack16(uint32_t w) {
+  // register m holds the codes at bits 2m..2m+1 of the packed word's four bytes
+  uint4 u;
+  u.x = w & 0x03030303u;
+  u.y = (w >> 2) & 0x03030303u;
+  u.z = (w >> 4) & 0x03030303u;
+  u.w = (w >> 6) & 0x03030303u;
+  return __builtin_bit_cast(i8x16, u);
+}
+
+__device__ __forceinline__ i32x4 mfma16(i8x16 a, i8x16 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// 2^e as a double, e in [-1022, 1023]
+__device__ __forceinline__ double pow2d(int e) { return __longlong_as_double(static_cast<long long>(e + 1023) << 52); }
+// 2^e as a float, e in [-126, 127]
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((e + 127) << 23); }
+
+// sum_t P'_t c_t of one accumulator fragment: rows 0..2 hold sum (byte_l - 128) c, row 3
+// sum c, so byte sums are c_l + 128 c_3 >= 0 and combine without cancellation in fp32
+__device__ __forceinline__ float v_combo(const i32x4& c) {
+  const int c3 = c[3] << 7;
+  const float b0 = static_cast<float>(c[0] + c3);
+  const float b1 = static_cast<float>(c[1] + c3);
+  const float b2 = static_cast<float>(c[2] + c3);
+  return fmaf(b2, 65536.f, fmaf(b1, 256.f, b0));
+}
+
+struct PageRegs {
+  uint4 k[2];  // K words: slots 4n..4n+3 (two words each: dims 32G..32G+15, 32G+16..32G+31)
+  uint4 km;    // K (scale, zero) of slots 4n..4n+3
+  uint4 vm;    // V (scale, zero) of slots 4n..4n+3
+  uint4 v[2];  // V words of dims 16dt + n, dt = 0..7, slots 16G..16G+15
+
+  __device__ __forceinline__ uint32_t kword(int nt, int h) const {
+    const uint4& c = k[nt >> 1];
+    return (nt & 1) ? (h ? c.w : c.z) : (h ? c.y : c.x);
+  }
+  __device__ __forceinline__ uint32_t kmeta(int nt) const { return nt == 0 ? km.x : nt == 1 ? km.y : nt == 2 ? km.z : km.w; }
+  __device__ __forceinline__ uint32_t vmeta(int nt) const { return nt == 0 ? vm.x : nt == 1 ? vm.y : nt == 2 ? vm.z : vm.w; }
+  __device__ __forceinline__ uint32_t vword(int dt) const {
+    const uint4& c = v[dt >> 2];
+    const int i = dt & 3;
+    return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w;
+  }
+};
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int imm) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + imm, 0, 0));
+}
+
+// Lane l = 16 G + n reads its page data as six 16-byte loads (the page layout keeps each
+// lane's K and V words contiguous) through a raw buffer descriptor of the page's 4608-byte
+// head block, built in scalar registers from the wave-uniform page address.
+// `bytes` is kHeadBlock, or 0 for a request that reads nothing (every load then returns 0
+// without touching memory).
+__device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* page, uint32_t lane32, uint32_t meta16,
+                                          int bytes = kHeadBlock) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page), 0, bytes, kRsrcWord3);
+  r.k[0] = load16(rs, lane32, kKCodes);
+  r.k[1] = load16(rs, lane32, kKCodes + 16);
+  r.km = load16(rs, meta16, 0);
+  r.vm = load16(rs, meta16, kVMeta - kKMeta);
+  r.v[0] = load16(rs, lane32, kVCodes);
+  r.v[1] = load16(rs, lane32, kVCodes + 16);
+}
+
+// The rotated query of one (request, query head) h of request b: q_rot = q R_K in fp64
+// (bf16 products are exact), as Q = rint(q_rot 2^sh) with max|q_rot| 2^sh < 2^21, in three
+// signed 8-bit limbs (limb row 3 zero); the centring term -2 sum_d Q_d; the score scale
+// 2^-sh sm_scale log2(e) and sm_scale log2(e) sum_d q_rot_d. All 256 threads of the
+// workgroup take part: wave w sums rows 32 w .. +31 at columns 2 lane, 2 lane + 1.
+constexpr int kQprepSmem = 4 * kHeadDim * 8 + kHeadDim * 8 + 64;
+
+__device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ rot_k, int n_q, int gq, double scale_log2,
+                                           char* __restrict__ qlimb, QueryScal* __restrict__ qscal, int h, int b) {
+  double(*part_s)[kHeadDim] = reinterpret_cast<double(*)[kHeadDim]>(smem);
+  double* qd_s = reinterpret_cast<double*>(smem + 4 * kHeadDim * 8);
+  float* amax_s = reinterpret_cast<float*>(smem + 5 * kHeadDim * 8);
+  double* sum_s = reinterpret_cast<double*>(smem + 5 * kHeadDim * 8 + 16);
+  int* lsum_s = reinterpret_cast<int*>(smem + 5 * kHeadDim * 8 + 32);
+  const int kv = h / gq;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const size_t head = static_cast<size_t>(b) * n_q + h;
+
+  const uint32_t* rcol = reinterpret_cast<const uint32_t*>(rot_k + static_cast<size_t>(kv) * kHeadDim * kHeadDim +
+                                                           static_cast<size_t>(32 * w) * kHeadDim) + lane;
+  uint32_t rr[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) rr[u] = rcol[u * (kHeadDim / 2)];
+  if (t < kHeadDim) qd_s[t] = static_cast<double>(bf16_to_f32(q[head * kHeadDim + t]));
+  __syncthreads();
+  double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) {
+    const double qv = qd_s[32 * w + u];
+    a0 = fma(qv, static_cast<double>(__uint_as_float(rr[u] << 16)), a0);
+    a1 = fma(qv, static_cast<double>(__uint_as_float(rr[u] & 0xFFFF0000u)), a1);
+  }
+  part_s[w][2 * lane] = a0;
+  part_s[w][2 * lane + 1] = a1;
+  __syncthreads();
+  // threads 0..127 own q_rot[t]; waves 2 and 3 only join the barriers
+  const int tt = t & (kHeadDim - 1);
+  const double x = (part_s[0][tt] + part_s[1][tt]) + (part_s[2][tt] + part_s[3][tt]);
+  const float am = wave_max_f32(static_cast<float>(fabs(x)));
+  const double sm = wave_sum_f64(x);
+  if (lane == 0 && w < 2) {
+    amax_s[w] = am;
+    sum_s[w] = sm;
+  }
+  __syncthreads();
+  // amax rounded to float can only move up to the next power of two: the bound holds
+  const float amax = fmaxf(amax_s[0], amax_s[1]);
+  int k = 0;
+  if (amax > 0.f) frexpf(amax, &k);  // amax < 2^k
+  const int sh = 21 - k;
+  const int Q = static_cast<int>(rint(x * pow2d(sh)));
+  const int l0 = static_cast<signed char>(Q & 0xFF);
+  const int r1 = (Q - l0) >> 8;
+  const int l1 = static_cast<signed char>(r1 & 0xFF);
+  const int l2 = (r1 - l1) >> 8;  // |l2| <= 33
+  if (t < kHeadDim) {
+    char* dst = qlimb + head * 512;
+    dst[t] = static_cast<char>(l0);
+    dst[kHeadDim + t] = static_cast<char>(l1);
+    dst[2 * kHeadDim + t] = static_cast<char>(l2);
+    dst[3 * kHeadDim + t] = 0;
+  }
+  // exact integer sum of Q over the 128 dims: the centring term -2 sum Q
+  int sq = Q;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+  if (lane == 0 && w < 2) lsum_s[w] = sq;
+  __syncthreads();
+  if (t == 0) {
+    QueryScal o;
+    o.qsc = static_cast<float>(pow2d(-sh) * scale_log2);
+    o.sig = static_cast<float>((sum_s[0] + sum_s[1]) * scale_log2);
+    o.kcent = -2 * (lsum_s[0] + lsum_s[1]);
+    o.pad[0] = o.pad[1] = o.pad[2] = o.pad[3] = o.pad[4] = 0;
+    qscal[head] = o;
+  }
+}
+
+// Per-wave online-softmax state held in registers (this lane: head 4 mt + G of tile mt).
+// "Pending" sums are in units of 2^E relative to the reference maximum m (the V sums in the
+// int32 MFMA accumulators, in units of 2^(E-1)). The "flushed" sums (true values relative
+// to m: sum p s^V c^V per dim, l and sum p z^V) live in LDS, touched only when flushing.
+template <int MT>
+struct WaveState {
+  float m[MT];        // reference maximum, log2 units; -inf before the first page
+  float bias[MT];     // E - m (0 before the first page); -inf for padding heads
+  float lq[MT];       // pending sum of p 2^E over this lane's slots
+  float zq[MT];       // pending sum of p 2^E z^V
+  i32x4 acci[MT][8];  // pending fragments (rows: 3 XORed limbs + code sum), dims 16 dt + n
+};
+
+constexpr int kQRow = 144;   // bytes of one query-limb row in LDS: 128 dims + 16 of bank spread
+constexpr int kFlushed = 10;  // flushed values per lane and tile: 8 dim tiles, l, sum p z
+
+// GQ is the number of query heads one workgroup serves (at most 8); a KV head whose group
+// is larger is served by n_groups = (query heads per KV head) / GQ workgroups along y.
+template <int GQ>
+constexpr int int2_smem_bytes() {
+  constexpr int MT = (GQ + 3) / 4;
+  constexpr int loop = kWaves * MT * 16 * kPRow + kWaves * MT * kFlushed * 64 * 4;
+  constexpr int wacc = kWaves * GQ * kHeadDim * 4;
+  return 4 * MT * 4 * kQRow + (wacc > loop ? wacc : loop) + 2 * kWaves * GQ * 4;
+}
+
+// Partial-result store: with kCoherent, an agent-scope store that is visible to every
+// workgroup of the launch once it has completed (for a merge inside the same launch).
+template <bool kCoherent>
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  if constexpr (kCoherent)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// One workgroup (256 threads) of the INT2 pass: history split `split` of request b for the
+// query heads gy*GQ .. gy*GQ+GQ-1 (KV head gy / n_groups). `smem` holds int2_smem_bytes<GQ>().
+template <int GQ, bool kCoherent = false>
+__device__ __forceinline__ void int2_split(
+    unsigned char* __restrict__ smem, int split, int gy, int b, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table, int max_pages,
+    const int32_t* __restrict__ hist_len, int n_q, int n_kv, int n_groups, int n_splits,
+    const char* __restrict__ qlimb, const QueryScal* __restrict__ qscal, float* __restrict__ out_m,
+    float* __restrict__ out_l, float* __restrict__ out_acc) {
+  constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
+  constexpr int kPBytes = kWaves * MT * 16 * kPRow;
+  constexpr int kFBytes = kWaves * MT * kFlushed * 64 * 4;
+  constexpr int kLoopBytes = kPBytes + kFBytes;
+  constexpr int kWaccBytes = kWaves * GQ * kHeadDim * 4;
+  constexpr int kScratch = kWaccBytes > kLoopBytes ? kWaccBytes : kLoopBytes;
+
+  // page loop: query limbs; P' limbs and flushed sums of each wave. Epilogue: wave partials
+  // over the P' and flushed-sum space.
+  unsigned char* q_s = smem;
+  unsigned char* scratch_s = smem + 4 * MT * 4 * kQRow;
+  float(*wm_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kScratch);
+  float(*wl_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kScratch + kWaves * GQ * 4);
+  float (*wacc_s)[GQ][kHeadDim] = reinterpret_cast<float (*)[GQ][kHeadDim]>(scratch_s);
+
+  const int kv = gy / n_groups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;  // MFMA column / row index
+  const int G = lane >> 4;  // lane group
+  const int h0 = gy * GQ;  // first query head of this workgroup
+
+  const int nh = hist_len[b];
+  const int n_pages = (nh + kPageTokens - 1) / kPageTokens;
+  const int pps = (n_pages + n_splits - 1) / n_splits;
+  const int p_begin = split * pps;
+  const int p_end = min(n_pages, p_begin + pps);
+  const int32_t* table = block_table + static_cast<size_t>(b) * max_pages;
+  const uint8_t* head_base = pool + static_cast<size_t>(kv) * kHeadBlock;
+  const size_t page_stride = static_cast<size_t>(n_kv) * kHeadBlock;
+  const uint32_t lane32 = 32u * lane;
+  const uint32_t meta16 = kKMeta + 16u * n;
+  const size_t head0 = static_cast<size_t>(b) * n_q + h0;
+
+  // block ids of this wave's pages p0, p0 + 4, ...: lane i of blk_lane holds the id of the
+  // wave's page 64 chunk + i
+  const int p0 = p_begin + wave;
+  const int n_mine = p0 < p_end ? (p_end - p0 + kWaves - 1) / kWaves : 0;
+  int chunk = 0;
+  int blk_lane = (lane < n_mine) ? table[p0 + kWaves * lane] : 0;
+  asm volatile("" ::"v"(blk_lane));
+  auto page_of = [&](int j) -> const uint8_t* {  // j wave-uniform, 0 <= j < n_mine
+    if ((j >> 6) != chunk) {
+      chunk = j >> 6;
+      const int i = 64 * chunk + lane;
+      blk_lane = (i < n_mine) ? table[p0 + kWaves * i] : 0;
+      // wait for the new ids here, on this rare path: the page loads in flight are then
+      // never counted as something the id reads below depend on
+      asm volatile("" ::"v"(blk_lane));
+    }
+    return head_base + static_cast<size_t>(__builtin_amdgcn_readlane(blk_lane, j & 63)) * page_stride;
+  };
+  // three page buffers: pages i + 1 and i + 2 load while page i is processed. The first two
+  // are requested before the query operands; a wave without pages issues the same loads
+  // against an empty buffer, so every path carries the same loads into the loop.
+  const int rec = n_mine > 0 ? kHeadBlock : 0;
+  PageRegs buf[3];
+  load_page(buf[0], page_of(0), lane32, meta16, rec);
+
+  // query limbs of the workgroup's heads into LDS: row 4 g + l holds limb l of head g
+  // (rows of heads beyond GQ are zero)
+  for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 256) {
+    const int row = i >> 3;
+    const int c = i & 7;
+    const int g = row >> 2;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (g < GQ) v = *reinterpret_cast<const uint4*>(qlimb + (head0 + g) * 512 + (row & 3) * kHeadDim + 16 * c);
+    *reinterpret_cast<uint4*>(q_s + row * kQRow + 16 * c) = v;
+  }
+  float qsc[MT], sig[MT];
+  int kcent[MT];
+  bool head_ok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int g = 4 * mt + G;
+    head_ok[mt] = g < GQ;
+    if (head_ok[mt]) {
+      const QueryScal s = qscal[head0 + g];
+      kcent[mt] = s.kcent;
+      qsc[mt] = s.qsc;
+      sig[mt] = s.sig;
+    } else {
+      kcent[mt] = 0;
+      qsc[mt] = sig[mt] = 0.f;
+    }
+  }
+  load_page(buf[1], page_of(n_mine > 1 ? 1 : 0), lane32, meta16, rec);
+  // The query operands must have arrived before the page loop: their loads then never
+  // count as outstanding inside it, and its waits let the next pages keep loading.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(kcent[mt]), "v"(qsc[mt]), "v"(sig[mt]));
+
+  WaveState<MT> st;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    st.m[mt] = -INFINITY;
+    st.bias[mt] = head_ok[mt] ? 0.f : -INFINITY;
+    st.lq[mt] = st.zq[mt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.acci[mt][dt] = i32x4{0, 0, 0, 0};
+  }
+  int E = 0;            // fixed-point exponent of the pending sums (wave-uniform)
+  float thr = kTau;     // E + kTau: frame-relative scores above it move the reference
+  float vcap = -1.f;    // V scales below vcap fit the current E
+  bool fresh = true;    // no page processed yet
+
+  // wave-private P'-limb rows: row mt*16 + 4 g + l; rows with l == 3 hold constant ones
+  unsigned char* pl = scratch_s + wave * (MT * 16 * kPRow);
+  // wave-private flushed sums: [mt][k][lane], k < 8: dim tile k, 8: l, 9: sum p z
+  float* fl = reinterpret_cast<float*>(scratch_s + kPBytes) + wave * (MT * kFlushed * 64) + lane;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    *reinterpret_cast<uint32_t*>(pl + (mt * 16 + 4 * G + 3) * kPRow + 4 * n) = 0x01010101u;
+#pragma unroll
+    for (int k = 0; k < kFlushed; ++k) fl[(mt * kFlushed + k) * 64] = 0.f;
+  }
+
+  // fold tile mt's pending sums into the flushed ones, rescaled to the reference m_new
+  auto flush_tile = [&](int mt, float m_new) {
+    if (!fresh) {
+      const float alpha = st.m[mt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m[mt] - m_new);
+      const float down = pow2f(-E);
+      const float down_v = pow2f(1 - E);
+      float* f = fl + mt * kFlushed * 64;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) f[dt * 64] = fmaf(v_combo(st.acci[mt][dt]), down_v, f[dt * 64]) * alpha;
+      f[8 * 64] = fmaf(st.lq[mt], down, f[8 * 64]) * alpha;
+      f[9 * 64] = fmaf(st.zq[mt], down, f[9 * 64]) * alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.acci[mt][dt] = i32x4{0, 0, 0, 0};
+    st.lq[mt] = st.zq[mt] = 0.f;
+    st.m[mt] = m_new;
+  };
+
+  auto process = [&](const PageRegs& cur, int ntok) {
+    // K side: rows (head, limb) x 16 slots per tile
+    i8x16 aK[MT][2];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        aK[mt][ks] = *reinterpret_cast<const i8x16*>(q_s + (16 * mt + n) * kQRow + 32 * G + 16 * ks);
+    i32x4 d[MT][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const i8x16 b0 = unpack16(cur.kword(nt, 0));
+      const i8x16 b1 = unpack16(cur.kword(nt, 1));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, i32x4{0, 0, 0, 0}));
+    }
+    // slot metadata of this lane's slots 4n..4n+3
+    float sk[4], u[4], sv[4], zv[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint32_t km = cur.kmeta(nt);
+      const uint32_t vm = cur.vmeta(nt);
+      sk[nt] = f16_to_f32(km);
+      u[nt] = fmaf(2.f, sk[nt], f16_to_f32(km >> 16));  // z + 2 s
+      sv[nt] = f16_to_f32(vm);
+      zv[nt] = f16_to_f32(vm >> 16);
+    }
+    // scores relative to the frame: x = score_log2 - m + E
+    float x[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const i32x4 c = d[mt][nt];
+        const int D = c[0] + (c[1] << 8) + (c[2] << 16) + kcent[mt];  // Q . (c - 2), exact
+        x[mt][nt] = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sig[mt], st.bias[mt]));
+      }
+    if (ntok < kPageTokens) {
+      // slots past the history end may hold stale bits: no weight, no scale
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const bool valid = 4 * n + nt < ntok;
+        sv[nt] = valid ? sv[nt] : 0.f;
+        zv[nt] = valid ? zv[nt] : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) x[mt][nt] = valid ? x[mt][nt] : -INFINITY;
+      }
+    }
+    float xm[MT];
+    bool over = false;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      xm[mt] = fmaxf(fmaxf(x[mt][0], x[mt][1]), fmaxf(x[mt][2], x[mt][3]));
+      over = over || xm[mt] > thr;
+    }
+    const float svm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    const bool vover = svm > vcap;
+    if (fresh || __any(over || vover)) {
+      // a new exponent for the wave's V scales moves every tile's frame
+      int e_new = E;
+      if (__any(vover)) {
+        int k = 0;
+        frexpf(wave_max_f32(svm), &k);  // largest V scale < 2^k
+        e_new = 24 - k - kTau;          // p s 2^E < 2^24 while p <= 2^kTau and s < 2^k
+        vcap = pow2f(k);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        // a head's reference moves to the page maximum when that exceeds it by kTau
+        const float r = row16_max(xm[mt]) - st.bias[mt];
+        const float m_new = head_ok[mt] ? (r > st.m[mt] + kTau ? r : st.m[mt]) : -INFINITY;
+        if (fresh || e_new != E || __any(m_new != st.m[mt])) {
+          const float bias_new = head_ok[mt] ? static_cast<float>(e_new) - m_new : -INFINITY;
+          const float shift = head_ok[mt] ? bias_new - st.bias[mt] : 0.f;
+          flush_tile(mt, m_new);
+          st.bias[mt] = bias_new;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) x[mt][nt] = head_ok[mt] ? x[mt][nt] + shift : -INFINITY;
+        }
+      }
+      E = e_new;
+      thr = static_cast<float>(E + kTau);
+      fresh = false;
+    }
+    // probabilities (units of 2^E), pending sums, P' limbs
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      uint32_t P[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const float pe = __builtin_amdgcn_exp2f(x[mt][nt]);
+        st.lq[mt] += pe;
+        st.zq[mt] = fmaf(pe, zv[nt], st.zq[mt]);
+        // pe sv < 2^24: the float pe sv + 2^24 holds round(pe sv / 2) in its mantissa, and its
+        // exponent's low bit is bit 23
+        P[nt] = __float_as_uint(fmaf(pe, sv[nt], 16777216.f));
+      }
+      // byte l of the four P' values into one dword per limb, in signed range
+      const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
+      const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+      const uint32_t u01 = __builtin_amdgcn_perm(P[1], P[0], 0x0C0C0602u);
+      const uint32_t u23 = __builtin_amdgcn_perm(P[3], P[2], 0x0C0C0602u);
+      const uint32_t L0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
+      const uint32_t L1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
+      const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // bit 7 set by the exponent
+      unsigned char* row = pl + (mt * 16 + 4 * G) * kPRow + 4 * n;
+      *reinterpret_cast<uint32_t*>(row) = L0;
+      *reinterpret_cast<uint32_t*>(row + kPRow) = L1;
+      *reinterpret_cast<uint32_t*>(row + 2 * kPRow) = L2;
+    }
+    // the wave's LDS operations run in order: the reads below see the writes above
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    i8x16 aP[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) aP[mt] = *reinterpret_cast<const i8x16*>(pl + (mt * 16 + n) * kPRow + 16 * G);
+    // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const i8x16 bv = unpack16(cur.vword(dt));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) st.acci[mt][dt] = mfma16(aP[mt], bv, st.acci[mt][dt]);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  // The prefetch is unconditional (past the last page the last page asks for itself again,
+  // an L2 hit), so no path without it joins between the loads and the use of a page.
+  auto ntok_of = [&](int j) { return min(kPageTokens, nh - (p0 + kWaves * j) * kPageTokens); };
+  auto next_of = [&](int j) { return page_of(j < n_mine ? j : n_mine - 1); };
+  __syncthreads();  // query limbs in LDS
+  if (n_mine > 0) {
+    for (int i = 0;;) {
+      load_page(buf[2], next_of(i + 2), lane32, meta16);
+      process(buf[0], ntok_of(i));
+      if (++i >= n_mine) break;
+      load_page(buf[0], next_of(i + 2), lane32, meta16);
+      process(buf[1], ntok_of(i));
+      if (++i >= n_mine) break;
+      load_page(buf[1], next_of(i + 2), lane32, meta16);
+      process(buf[2], ntok_of(i));
+      if (++i >= n_mine) break;
+    }
+  }
+
+  // ---- wave partials: lane (G, n) holds head 4mt + G, dims 16dt + n
+  float accf[MT][8], lf[MT], zf[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (!fresh) flush_tile(mt, st.m[mt]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) accf[mt][dt] = fl[(mt * kFlushed + dt) * 64];
+    lf[mt] = fl[(mt * kFlushed + 8) * 64];
+    zf[mt] = fl[(mt * kFlushed + 9) * 64];
+  }
+  __syncthreads();  // every wave has read its flushed sums: the space becomes wacc_s
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int g = 4 * mt + G;
+    const float l = row16_sum(lf[mt]);
+    const float zs = row16_sum(zf[mt]);
+    if (g < GQ) {
+      if (n == 0) {
+        wm_s[wave][g] = st.m[mt];
+        wl_s[wave][g] = l;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) wacc_s[wave][g][16 * dt + n] = accf[mt][dt] + zs;
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < GQ * kHeadDim; idx += 256) {
+    const int g = idx >> 7;
+    const int dd = idx & 127;
+    float big = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) big = fmaxf(big, wm_s[w][g]);
+    float l = 0.f, a = 0.f;
+    if (big != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float s = wm_s[w][g] == -INFINITY ? 0.f : exp2f(wm_s[w][g] - big);
+        l = fmaf(s, wl_s[w][g], l);
+        a = fmaf(s, wacc_s[w][g][dd], a);
+      }
+    }
+    const size_t o = (static_cast<size_t>(b) * n_q + h0 + g) * n_splits + split;
+    store_partial<kCoherent>(out_acc + o * kHeadDim + dd, a);
+    if (dd == 0) {
+      store_partial<kCoherent>(out_m + o, big);
+      store_partial<kCoherent>(out_l + o, l);
+    }
+  }
+}
+
+}  // namespace int2
+}  // namespace oscar

@@ -36,6 +36,7 @@ struct PartialsView {
 
 size_t partials_bytes(int batch, int n_q, int n_splits);
 PartialsView partials_view(void* base, int batch, int n_q, int n_splits);
+size_t step_workspace_bytes(int batch, int n_q, int n_kv, int n_splits, int n_wsplits);
 
 hipError_t launch_demote_rows(const LayerShape& L, const void* k_src, const void* v_src, int n,
                               const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k,
@@ -50,6 +51,40 @@ hipError_t launch_decode_int2(const LayerShape& L, const void* q, const void* ro
 hipError_t launch_decode_bf16(const LayerShape& L, const void* q, const void* k_win, const void* v_win,
                               const int32_t* win_len, int batch, float sm_scale, int n_win_splits,
                               const PartialsView& out, hipStream_t stream);
+
+// Everything the fused decode step needs (passed to its kernels by value).
+struct StepArgs {
+  // demotion (n_dem_items = 2 * tokens * n_kv; 0 for decode only)
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int n_dem_items;
+  const int32_t* dst_page;
+  const int32_t* dst_slot;
+  const float* clip_k;
+  const float* clip_v;
+  uint8_t* pool;
+  // decode
+  const uint16_t* q;
+  const uint16_t* rot_k;
+  const uint16_t* rot_v;
+  const int32_t* block_table;
+  int max_pages;
+  const int32_t* hist_len;
+  const uint16_t* k_win;
+  const uint16_t* v_win;
+  const int32_t* win_len;
+  int batch, n_q, n_kv, gq, window, n_splits, n_wsplits, n_groups;
+  double scale_log2;
+  PartialsView hist;  // INT2 partials and the query tail
+  PartialsView win;   // window partials
+  int* counters;      // [batch][n_kv] arrival counters
+  float* out;
+};
+
+// Demotion + window pass + query preparation (one launch), and the INT2 pass with the merge
+// done by the last workgroup of each (request, KV head) (one launch).
+hipError_t launch_prepare(StepArgs a, hipStream_t stream);
+hipError_t launch_attend(StepArgs a, hipStream_t stream);
 
 hipError_t launch_merge(const LayerShape& L, const PartialsView& hist, int n_splits,
                         const PartialsView& win, int n_win_splits, const void* rot_v, float* out,

@@ -76,6 +76,12 @@ size_t partials_bytes(int batch, int n_q, int n_splits) {
   return qs_off + heads * sizeof(QueryScal);
 }
 
+// [INT2 partials + query tail | window partials | arrival counters]
+size_t step_workspace_bytes(int batch, int n_q, int n_kv, int n_splits, int n_wsplits) {
+  return align256(partials_bytes(batch, n_q, n_splits)) + align256(partials_bytes(batch, n_q, n_wsplits)) +
+         align256(static_cast<size_t>(batch) * n_kv * 4);
+}
+
 PartialsView partials_view(void* base, int batch, int n_q, int n_splits) {
   const size_t n = static_cast<size_t>(batch) * n_q * n_splits;
   const size_t heads = static_cast<size_t>(batch) * n_q;
@@ -139,9 +145,10 @@ size_t oscar_partials_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t
 int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len) {
   if (check_desc_impl(desc) != OSCAR_OK || batch <= 0) return 1;
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
-  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads;
-  long long s = (2048 + groups - 1) / groups;  // about 8 workgroups per compute unit
-  const long long by_pages = (pages + 7) / 8;  // at least 8 pages (two per wave) per split
+  const int gq = desc->n_q_heads / desc->n_kv_heads;
+  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1);
+  long long s = (512 + groups / 2) / groups;   // about two workgroups per compute unit
+  const long long by_pages = (pages + 3) / 4;  // at least one page per wave
   if (s > by_pages) s = by_pages;
   if (s < 1) s = 1;
   if (s > 65535) s = 65535;
@@ -205,6 +212,128 @@ int32_t oscar_decode_bf16(const oscar_layer_desc* desc, const void* q, const voi
   return hip_status(oscar::launch_decode_bf16(L, q, k_win, v_win, win_len, batch, sm_scale, ws, v,
                                               static_cast<hipStream_t>(stream)),
                     "decode_bf16 launch");
+}
+
+size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
+  return oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits, window_splits_of(desc));
+}
+
+namespace {
+
+// Checks shared by the two halves of the decode step; fills the workspace views.
+int32_t check_step_common(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits, void* workspace,
+                          size_t workspace_bytes, oscar::StepArgs& a) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (n_splits <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d <= 0", n_splits);
+  if (n_splits > 256) return fail(OSCAR_ERR_UNSUPPORTED, "n_splits %d > 256 (the two-launch decode)", n_splits);
+  if (!workspace) return fail(OSCAR_ERR_INVALID_ARG, "null workspace");
+  const int ws = window_splits_of(desc);
+  const size_t need = oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits, ws);
+  if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const oscar::LayerShape L = shape_of(desc);
+  char* base = static_cast<char*>(workspace);
+  const size_t hist_bytes = (oscar::partials_bytes(batch, desc->n_q_heads, n_splits) + 255) / 256 * 256;
+  const size_t win_bytes = (oscar::partials_bytes(batch, desc->n_q_heads, ws) + 255) / 256 * 256;
+  a = oscar::StepArgs{};
+  a.batch = batch;
+  a.n_q = L.n_q;
+  a.n_kv = L.n_kv;
+  a.gq = L.gq;
+  a.window = L.window;
+  a.n_splits = n_splits;
+  a.n_wsplits = ws;
+  a.n_groups = 1;
+  a.hist = oscar::partials_view(base, batch, desc->n_q_heads, n_splits);
+  a.win = oscar::partials_view(base + hist_bytes, batch, desc->n_q_heads, ws);
+  a.counters = reinterpret_cast<int*>(base + hist_bytes + win_bytes);
+  return OSCAR_OK;
+}
+
+}  // namespace
+
+int32_t oscar_prepare(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                      const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
+                      const void* q, const void* rot_k, const void* rot_v, void* pool, const void* k_win,
+                      const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  oscar::StepArgs a;
+  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
+  if (st != OSCAR_OK) return st;
+  if (n < 0) return fail(OSCAR_ERR_INVALID_ARG, "n %d < 0", n);
+  if (n > 0 && (!k_src || !v_src || !dst_page || !dst_slot || !clip_k || !clip_v || !rot_v || !pool))
+    return fail(OSCAR_ERR_INVALID_ARG, "null demotion argument");
+  if (!q || !rot_k || !k_win || !v_win || !win_len) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const long long grid = 2LL * n * desc->n_kv_heads +
+                         static_cast<long long>(window_splits_of(desc)) * desc->n_kv_heads * batch +
+                         static_cast<long long>(desc->n_q_heads) * batch;
+  if (grid > 0x7FFFFFFFLL) return fail(OSCAR_ERR_UNSUPPORTED, "demotion rows exceed the grid limit");
+  a.k_src = static_cast<const uint16_t*>(k_src);
+  a.v_src = static_cast<const uint16_t*>(v_src);
+  a.n_dem_items = 2 * n * desc->n_kv_heads;
+  a.dst_page = dst_page;
+  a.dst_slot = dst_slot;
+  a.clip_k = clip_k;
+  a.clip_v = clip_v;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.q = static_cast<const uint16_t*>(q);
+  a.rot_k = static_cast<const uint16_t*>(rot_k);
+  a.rot_v = static_cast<const uint16_t*>(rot_v);
+  a.k_win = static_cast<const uint16_t*>(k_win);
+  a.v_win = static_cast<const uint16_t*>(v_win);
+  a.win_len = win_len;
+  a.scale_log2 = static_cast<double>(sm_scale) * 1.4426950408889634;
+  return hip_status(oscar::launch_prepare(a, static_cast<hipStream_t>(stream)), "prepare launch");
+}
+
+int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void* pool, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
+                     size_t workspace_bytes, float* out, void* stream) {
+  oscar::StepArgs a;
+  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
+  if (st != OSCAR_OK) return st;
+  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  a.rot_v = static_cast<const uint16_t*>(rot_v);
+  a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));  // only read by the attend launch
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.hist_len = hist_len;
+  a.out = out;
+  return hip_status(oscar::launch_attend(a, static_cast<hipStream_t>(stream)), "attend launch");
+}
+
+int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                          const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
+                          const void* q, const void* rot_k, const void* rot_v, void* pool,
+                          const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, const void* k_win,
+                          const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
+                          int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  // the attend half's arguments are checked before anything is enqueued
+  oscar::StepArgs a;
+  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
+  if (st != OSCAR_OK) return st;
+  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  st = oscar_prepare(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win, v_win,
+                     win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, stream);
+  if (st != OSCAR_OK) return st;
+  return oscar_attend(desc, rot_v, pool, block_table, max_pages, hist_len, batch, n_splits, workspace,
+                      workspace_bytes, out, stream);
+}
+
+int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* rot_v,
+                     const void* pool, const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                     const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
+                     int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  // nothing is demoted, so the pool is only read
+  return oscar_decode_step(desc, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, q, rot_k, rot_v,
+                           const_cast<void*>(pool), block_table, max_pages, hist_len, k_win, v_win, win_len, batch,
+                           sm_scale, n_splits, workspace, workspace_bytes, out, stream);
 }
 
 int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t n_splits, const void* win_partials,

@@ -1,0 +1,120 @@
+// Decode step in two launches: oscar_prepare, then oscar_attend (oscar_decode_step and
+// oscar_decode issue both).
+//
+// Method: OSCAR; QbitAI article on OSCAR, serving-path section: a decode step demotes the
+// oldest recent token into the INT2 history (rotate, clip, quantise, pack), then attends
+// over the BF16 sink/recent segment and the INT2 history separately and joins the two by
+// an online-softmax merge.
+//
+// Launch 1 (prep), one 256-thread workgroup per item, the items being independent:
+//   demotion rows (token, KV head, K or V); BF16 window splits (split, KV head, request);
+//   query preparation per (request, query head), which also zeroes the request's
+//   per-KV-head arrival counters.
+// Launch 2 (main), grid (history split, KV head x head group, request): the INT2 pass of
+// the split, then a ticket: every workgroup writes its partial with agent-scope stores,
+// waits for them to complete and adds one to its (request, KV head) counter; the workgroup that draws the last ticket merges
+// all INT2 and window partials of that KV head's query heads, un-rotates and writes the
+// output, after re-arming the counter (so the main launch may be repeated on its own). No
+// workgroup ever waits for another.
+
+#include "demote_pass.h"
+#include "int2_pass.h"
+#include "merge_pass.h"
+#include "window_pass.h"
+
+namespace oscar {
+namespace {
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int GQW>
+__global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
+  __shared__ __align__(16) unsigned char smem[cmax(cmax(demote::kSmemBytes, window::window_smem_bytes<GQW>()),
+                                                   int2::kQprepSmem)];
+  int id = blockIdx.x;
+  if (id < a.n_dem_items) {
+    demote::demote_row(smem, id, a.k_src, a.v_src, a.n_kv, a.dst_page, a.dst_slot, a.rot_k, a.rot_v, a.clip_k,
+                       a.clip_v, a.pool);
+    return;
+  }
+  id -= a.n_dem_items;
+  const int n_win = a.n_wsplits * a.n_kv * a.batch;
+  if (id < n_win) {
+    const int c = id % a.n_wsplits;
+    const int kv = (id / a.n_wsplits) % a.n_kv;
+    const int b = id / (a.n_wsplits * a.n_kv);
+    window::window_split<GQW>(smem, c, kv, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q, a.n_kv, a.window,
+                              a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+    return;
+  }
+  id -= n_win;
+  const int h = id % a.n_q;
+  const int b = id / a.n_q;
+  if (threadIdx.x == 0 && h % a.gq == 0) a.counters[b * a.n_kv + h / a.gq] = 0;
+  int2::qprep_head(smem, a.q, a.rot_k, a.n_q, a.gq, a.scale_log2, a.hist.qlimb, a.hist.qscal, h, b);
+}
+
+// GQ query heads per workgroup, GQT per KV head (GQT = GQ n_groups)
+template <int GQ, int GQT>
+__global__ __launch_bounds__(256) void main_kernel(StepArgs a) {
+  // the INT2 pass and the merge use the same LDS one after the other
+  __shared__ __align__(16) unsigned char smem[cmax(int2::int2_smem_bytes<GQ>(), merge::smem_bytes<GQT>())];
+  __shared__ int ticket_s;
+  int2::int2_split<GQ, true>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table, a.max_pages,
+                             a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits, a.hist.qlimb, a.hist.qscal, a.hist.m,
+                             a.hist.l, a.hist.acc);
+  // the partials went out as agent-scope stores: once each thread's stores have completed
+  // and the barrier has passed, the ticket below is drawn after all of them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int kv = blockIdx.y / a.n_groups;
+  const int b = blockIdx.z;
+  int* counter = a.counters + b * a.n_kv + kv;
+  if (threadIdx.x == 0) ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (ticket_s != a.n_splits * a.n_groups - 1) return;
+  // last arrival for (b, kv): every workgroup of the group has drawn its ticket, so re-arm the
+  // counter for the next launch; the group's partials are read with agent-scope loads
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge::merge_group<GQT>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, a.rot_v, a.out);
+}
+
+template <int GQT>
+hipError_t launch_prep(const StepArgs& a, hipStream_t stream) {
+  const unsigned n_prep = static_cast<unsigned>(a.n_dem_items + a.n_wsplits * a.n_kv * a.batch + a.n_q * a.batch);
+  hipLaunchKernelGGL(prep_kernel<GQT>, dim3(n_prep), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int GQ, int GQT>
+hipError_t launch_main(const StepArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((main_kernel<GQ, GQT>), dim3(a.n_splits, a.n_kv * a.n_groups, a.batch), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prepare(StepArgs a, hipStream_t stream) {
+  switch (a.gq) {
+    case 1: return launch_prep<1>(a, stream);
+    case 2: return launch_prep<2>(a, stream);
+    case 4: return launch_prep<4>(a, stream);
+    case 8: return launch_prep<8>(a, stream);
+    case 16: return launch_prep<16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attend(StepArgs a, hipStream_t stream) {
+  switch (a.gq) {
+    case 1: a.n_groups = 1; return launch_main<1, 1>(a, stream);
+    case 2: a.n_groups = 1; return launch_main<2, 2>(a, stream);
+    case 4: a.n_groups = 1; return launch_main<4, 4>(a, stream);
+    case 8: a.n_groups = 1; return launch_main<8, 8>(a, stream);
+    case 16: a.n_groups = 2; return launch_main<8, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace oscar

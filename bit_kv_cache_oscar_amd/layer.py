@@ -49,6 +49,7 @@ class LayerCache:
         self.out = torch.zeros((batch, n_q_heads, HEAD_DIM), dtype=torch.float32, device=self.device)
         self.n_splits = 1
         self._partials = None
+        self._workspace = None
         self.win_partials = torch.zeros(L.oscar_partials_bytes(self.desc, batch, L.oscar_window_splits(self.desc)),
                                         dtype=torch.uint8, device=self.device)
 
@@ -81,6 +82,14 @@ class LayerCache:
             self._partials = torch.zeros(need, dtype=torch.uint8, device=self.device)
 
     @property
+    def workspace(self) -> torch.Tensor:
+        """Workspace of the two-launch decode (no initialisation needed)."""
+        need = L.oscar_decode_workspace_bytes(self.desc, self.batch, self.n_splits)
+        if self._workspace is None or self._workspace.numel() < need:
+            self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._workspace
+
+    @property
     def partials(self) -> torch.Tensor:
         if self._partials is None:
             self.set_splits(self.n_splits)
@@ -100,4 +109,19 @@ class LayerCache:
         L.oscar_decode_bf16(self.desc, q, self.k_win, self.v_win, self.win_len, sm_scale, self.win_partials,
                             stream)
         L.oscar_merge(self.desc, self.partials, self.n_splits, self.win_partials, self.rot_v, self.out, stream)
+        return self.out
+
+    def decode_fused(self, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
+        """The same output as decode(), in two launches (oscar_decode)."""
+        L.oscar_decode(self.desc, q, self.rot_k, self.rot_v, self.pool, self.block_table, self.hist_len,
+                       self.k_win, self.v_win, self.win_len, sm_scale, self.n_splits, self.workspace, self.out,
+                       stream)
+        return self.out
+
+    def step(self, k_rows, v_rows, pages, slots, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
+        """Demote k_rows/v_rows [n, Hkv, 128] into (pages, slots), then decode q: one decode step in
+        two launches (oscar_decode_step). hist_len must already count the demoted tokens."""
+        L.oscar_decode_step(self.desc, k_rows, v_rows, pages, slots, self.clip_k, self.clip_v, q, self.rot_k,
+                            self.rot_v, self.pool, self.block_table, self.hist_len, self.k_win, self.v_win,
+                            self.win_len, sm_scale, self.n_splits, self.workspace, self.out, stream)
         return self.out

@@ -195,6 +195,73 @@ int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t 
                     const void* win_partials, const void* rot_v, float* out, int32_t batch,
                     void* stream);
 
+/* Bytes of the workspace of oscar_decode / oscar_decode_step for `batch` requests and
+ * `n_splits` history splits (0 for a bad desc). */
+size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits);
+
+/*
+ * oscar_decode_step: one decode step of one layer in two launches: demotion, then decode
+ * attention over all three segments. The same result as oscar_demote, oscar_decode_int2,
+ * oscar_decode_bf16 and oscar_merge called in that order.
+ * (QbitAI article on OSCAR, serving-path section: the oldest recent token is rotated,
+ * clipped, quantised, packed and demoted into the INT2 history; decode processes the BF16
+ * sink/recent and the INT2 history separately and joins them by an online-softmax merge.)
+ *
+ * Launch 1 runs the n demotions (as oscar_demote), the BF16 window pass and the query
+ * rotation; launch 2 runs the INT2 pass, and for each (request, KV head) the workgroup
+ * that finishes last merges that KV head's query heads and writes `out`. Arguments are
+ * those of the four calls above; in addition:
+ *   workspace  at least oscar_decode_workspace_bytes(desc, batch, n_splits) bytes of device
+ *              memory, owned by the caller; its contents need no initialisation and are
+ *              overwritten (INT2 and window partials, query data, arrival counters)
+ *   out        float32 [batch][n_q_heads][128]
+ *   n_splits   1..256 (OSCAR_ERR_UNSUPPORTED above)
+ * Demotions land before the history is read: a token demoted by this call is part of the
+ * history it attends over (hist_len must count it). n == 0 demotes nothing (then k_src,
+ * v_src, dst_page, dst_slot, clip_k and clip_v may be null). Calls that share a
+ * workspace must not overlap in time.
+ */
+int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                          const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
+                          const void* q, const void* rot_k, const void* rot_v, void* pool,
+                          const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, const void* k_win,
+                          const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
+                          int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * oscar_decode: decode attention over the three segments in two launches, without
+ * demotion (oscar_decode_step with n == 0; the pool is only read).
+ * (QbitAI article on OSCAR, serving-path section: INT2 and BF16 segments processed
+ * separately, joined by an online-softmax merge.)
+ */
+int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* rot_v,
+                     const void* pool, const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                     const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
+                     int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * oscar_prepare: the first launch of oscar_decode_step on its own: the n demotions, the
+ * BF16 window pass and the query rotation, written into the workspace (and the pool).
+ * Arguments as in oscar_decode_step. A later oscar_attend with the same desc, batch,
+ * n_splits and workspace completes the step.
+ */
+int32_t oscar_prepare(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                      const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
+                      const void* q, const void* rot_k, const void* rot_v, void* pool, const void* k_win,
+                      const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * oscar_attend: the second launch of oscar_decode_step on its own: the INT2 history pass
+ * of every split, then for each (request, KV head) the merge with the window partials
+ * that oscar_prepare left in the workspace, the R_V^T un-rotation and the output. It
+ * only reads the workspace's prepared data, so it may be repeated without a new
+ * oscar_prepare.
+ */
+int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void* pool, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
+                     size_t workspace_bytes, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

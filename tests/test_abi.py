@@ -115,6 +115,54 @@ def test_demote_argument_checks(lib):
     assert f(d, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == L.OSCAR_ERR_INVALID_ARG
 
 
+def test_decode_workspace_size():
+    d = L.layer_desc(32, 8)
+    a256 = lambda x: -(-x // 256) * 256
+    want = a256(L.oscar_partials_bytes(d, 3, 7)) + a256(L.oscar_partials_bytes(d, 3, 5)) + a256(3 * 8 * 4)
+    assert L.oscar_decode_workspace_bytes(d, 3, 7) == want
+    bad = L.layer_desc(32, 8)
+    bad.head_dim = 64
+    assert L.oscar_decode_workspace_bytes(bad, 3, 7) == 0
+
+
+def test_decode_step_argument_checks(lib):
+    desc = L.layer_desc(32, 8)
+    d = ctypes.byref(desc)
+    need = L.oscar_decode_workspace_bytes(desc, 2, 4)
+    step = lib.oscar_decode_step
+    args = [FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4,
+            FAKE, need, FAKE, None]
+
+    def call(over):
+        a = list(args)
+        for k, v in over.items():
+            a[k] = v
+        return step(d, *a)
+
+    # argument positions after desc: 0 k_src, 2 n, 9 rot_v, 12 max_pages, 17 batch, 18 sm_scale,
+    # 19 n_splits, 21 workspace_bytes, 22 out
+    assert call({21: need - 1}) == L.OSCAR_ERR_WORKSPACE
+    assert call({2: -1}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({0: None}) == L.OSCAR_ERR_INVALID_ARG        # demotion source missing with n > 0
+    assert call({17: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({19: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({12: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({18: float("nan")}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({22: None}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({9: None}) == L.OSCAR_ERR_INVALID_ARG
+    # n == 0 needs no demotion arguments; the remaining checks still apply
+    assert call({2: 0, 0: None, 1: None, 3: None, 4: None, 5: None, 6: None, 21: need - 1}) == L.OSCAR_ERR_WORKSPACE
+    att = lib.oscar_attend
+    assert att(d, FAKE, FAKE, FAKE, 4, FAKE, 2, 4, FAKE, need - 1, FAKE, None) == L.OSCAR_ERR_WORKSPACE
+    assert att(d, FAKE, FAKE, FAKE, 0, FAKE, 2, 4, FAKE, need, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert att(d, FAKE, FAKE, None, 4, FAKE, 2, 4, FAKE, need, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    prep = lib.oscar_prepare
+    assert prep(d, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4, FAKE,
+                need - 1, None) == L.OSCAR_ERR_WORKSPACE
+    assert prep(d, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4, FAKE,
+                need, None) == L.OSCAR_ERR_INVALID_ARG
+
+
 def test_python_binding_validates_shapes_before_the_library():
     torch = pytest.importorskip("torch")
     d = L.layer_desc(32, 8)

@@ -98,6 +98,12 @@ def test_decode_on_oracle_pages(case):
         got = out.cpu().numpy()
         for b in range(w.batch):
             assert_close(got[b], refs[b], f"{case} b{b} splits {s}")
+        # the two-launch path, twice in a row (its arrival counters must re-arm between calls)
+        for rep in range(2):
+            c.out.fill_(np.nan)
+            got = c.decode_fused(q, w.sm_scale).cpu().numpy()
+            for b in range(w.batch):
+                assert_close(got[b], refs[b], f"{case} b{b} splits {s} fused call {rep}")
 
 
 def _split_bounds(nh, s_total):
@@ -379,3 +385,59 @@ def test_full_size_end_to_end_sampled(cfg):
         ref = oracle_decode(w, b, rk, rv, hists, heads=heads)
         for h in heads:
             assert_close(got[b, h], ref[h], f"{w.name} b{b} h{h}")
+
+
+STEP_CASES = ["c1", "c2-4k", "c4-shared-ragged", "c5-gq8", "gq16", "edges"]
+
+
+@pytest.mark.parametrize("case", STEP_CASES)
+def test_decode_step_demotes_then_decodes(case):
+    """oscar_decode_step: every history token but the last of each request goes in through
+    oscar_demote, the last ones through the step itself, which then decodes; the pool is
+    compared byte by byte (with the exemption band) and the output with the oracle."""
+    from bit_kv_cache_oscar_amd import oscar_default_splits
+
+    w = DECODE_CASES[case]()
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table, n_phys = synth.block_table(w)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys)
+    last_k, last_v, last_p, last_s = [], [], [], []
+    for b in range(w.batch):
+        n = w.hist_len(b)
+        start = min(n, w.shared_pages * 64) if (w.shared_pages and b > 0) else 0
+        if n == 0 or n - 1 < start:
+            continue  # no history, or its last token belongs to the shared prefix demoted for request 0
+        ks, vs = [], []
+        for kv in range(w.n_kv_heads):
+            k, v = synth.kv_rows(w, b, kv, 64 + start, 64 + n)
+            ks.append(k)
+            vs.append(v)
+        ks, vs = np.stack(ks, 1), np.stack(vs, 1)
+        j = np.arange(start, n)
+        if n - 1 > start:
+            _demote_all(c, w, b, table[b, j[:-1] // 64], j[:-1] % 64, ks[:-1], vs[:-1])
+        last_k.append(ks[-1])
+        last_v.append(vs[-1])
+        last_p.append(table[b, (n - 1) // 64])
+        last_s.append((n - 1) % 64)
+    s = oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max()))
+    c.set_splits(s)
+    dev = torch.device("cuda")
+    if last_k:
+        kr, vr = bf16(np.stack(last_k)), bf16(np.stack(last_v))
+        pg = torch.tensor(last_p, dtype=torch.int32, device=dev)
+        sl = torch.tensor(last_s, dtype=torch.int32, device=dev)
+    else:
+        kr = vr = pg = sl = None
+    say(case, "step", "B", w.batch, "Hq", w.n_q_heads, "Hkv", w.n_kv_heads, "demoted in step", len(last_k), "splits", s)
+    got = c.step(kr, vr, pg, sl, queries(w), w.sm_scale).cpu().numpy()
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
+    for b in range(w.batch):
+        hists = {}
+        for kv in range(w.n_kv_heads):
+            ref_hist, km, vm = oracle_history(w, b, kv, rk, rv)
+            gpu_hist = opages.unpack_history(pool, table[b], kv, w.hist_len(b))
+            compare_history(gpu_hist, ref_hist, km, vm, f"{case} b{b} kv{kv}")
+            hists[kv] = ref_hist
+        ref = oracle_decode(w, b, rk, rv, hists)
+        assert_close(got[b], ref, f"{case} step b{b}")
