@@ -22,6 +22,14 @@ __host__ __device__ constexpr int k_word_offset(int t, int w) {
 }
 __host__ __device__ constexpr int v_word_offset(int d, int u) { return kVCodes + 32 * (16 * u + (d & 15)) + 4 * (d >> 4); }
 
+// Word 3 of a raw buffer descriptor (gfx9 family): 32-bit float data format, no swizzle.
+// A load whose offset lies past the descriptor's byte count returns 0 and touches no memory.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

@@ -46,7 +46,6 @@ namespace int2 {
 constexpr int kWaves = 4;
 constexpr int kPRow = 80;    // bytes of one P-limb row in LDS: 64 slots + 16 bytes of bank spread
 constexpr int kTau = 2;      // headroom of the softmax weights above the reference maximum (log2)
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer descriptor word 3 for gfx9-family
 typedef char i8x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -219,12 +218,13 @@ constexpr int kFlushed = 10;  // flushed values per lane and tile: 8 dim tiles, 
 
 // GQ is the number of query heads one workgroup serves (at most 8); a KV head whose group
 // is larger is served by n_groups = (query heads per KV head) / GQ workgroups along y.
-template <int GQ>
+// NW is the number of waves of the workgroup.
+template <int GQ, int NW = kWaves>
 constexpr int int2_smem_bytes() {
   constexpr int MT = (GQ + 3) / 4;
-  constexpr int loop = kWaves * MT * 16 * kPRow + kWaves * MT * kFlushed * 64 * 4;
-  constexpr int wacc = kWaves * GQ * kHeadDim * 4;
-  return 4 * MT * 4 * kQRow + (wacc > loop ? wacc : loop) + 2 * kWaves * GQ * 4;
+  constexpr int loop = NW * MT * 16 * kPRow + NW * MT * kFlushed * 64 * 4;
+  constexpr int wacc = NW * GQ * kHeadDim * 4;
+  return 4 * MT * 4 * kQRow + (wacc > loop ? wacc : loop) + 2 * NW * GQ * 4;
 }
 
 // Partial-result store: with kCoherent, an agent-scope store that is visible to every
@@ -237,19 +237,20 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
     *p = v;
 }
 
-// One workgroup (256 threads) of the INT2 pass: history split `split` of request b for the
-// query heads gy*GQ .. gy*GQ+GQ-1 (KV head gy / n_groups). `smem` holds int2_smem_bytes<GQ>().
-template <int GQ, bool kCoherent = false>
+// One workgroup (NW waves) of the INT2 pass: history split `split` of request b for the
+// query heads gy*GQ .. gy*GQ+GQ-1 (KV head gy / n_groups). `smem` holds
+// int2_smem_bytes<GQ, NW>().
+template <int GQ, bool kCoherent = false, int NW = kWaves>
 __device__ __forceinline__ void int2_split(
     unsigned char* __restrict__ smem, int split, int gy, int b, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ hist_len, int n_q, int n_kv, int n_groups, int n_splits,
     const char* __restrict__ qlimb, const QueryScal* __restrict__ qscal, float* __restrict__ out_m,
     float* __restrict__ out_l, float* __restrict__ out_acc) {
   constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
-  constexpr int kPBytes = kWaves * MT * 16 * kPRow;
-  constexpr int kFBytes = kWaves * MT * kFlushed * 64 * 4;
+  constexpr int kPBytes = NW * MT * 16 * kPRow;
+  constexpr int kFBytes = NW * MT * kFlushed * 64 * 4;
   constexpr int kLoopBytes = kPBytes + kFBytes;
-  constexpr int kWaccBytes = kWaves * GQ * kHeadDim * 4;
+  constexpr int kWaccBytes = NW * GQ * kHeadDim * 4;
   constexpr int kScratch = kWaccBytes > kLoopBytes ? kWaccBytes : kLoopBytes;
 
   // page loop: query limbs; P' limbs and flushed sums of each wave. Epilogue: wave partials
@@ -257,7 +258,7 @@ __device__ __forceinline__ void int2_split(
   unsigned char* q_s = smem;
   unsigned char* scratch_s = smem + 4 * MT * 4 * kQRow;
   float(*wm_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kScratch);
-  float(*wl_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kScratch + kWaves * GQ * 4);
+  float(*wl_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kScratch + NW * GQ * 4);
   float (*wacc_s)[GQ][kHeadDim] = reinterpret_cast<float (*)[GQ][kHeadDim]>(scratch_s);
 
   const int kv = gy / n_groups;
@@ -280,18 +281,18 @@ __device__ __forceinline__ void int2_split(
   const uint32_t meta16 = kKMeta + 16u * n;
   const size_t head0 = static_cast<size_t>(b) * n_q + h0;
 
-  // block ids of this wave's pages p0, p0 + 4, ...: lane i of blk_lane holds the id of the
+  // block ids of this wave's pages p0, p0 + NW, ...: lane i of blk_lane holds the id of the
   // wave's page 64 chunk + i
   const int p0 = p_begin + wave;
-  const int n_mine = p0 < p_end ? (p_end - p0 + kWaves - 1) / kWaves : 0;
+  const int n_mine = p0 < p_end ? (p_end - p0 + NW - 1) / NW : 0;
   int chunk = 0;
-  int blk_lane = (lane < n_mine) ? table[p0 + kWaves * lane] : 0;
+  int blk_lane = (lane < n_mine) ? table[p0 + NW * lane] : 0;
   asm volatile("" ::"v"(blk_lane));
   auto page_of = [&](int j) -> const uint8_t* {  // j wave-uniform, 0 <= j < n_mine
     if ((j >> 6) != chunk) {
       chunk = j >> 6;
       const int i = 64 * chunk + lane;
-      blk_lane = (i < n_mine) ? table[p0 + kWaves * i] : 0;
+      blk_lane = (i < n_mine) ? table[p0 + NW * i] : 0;
       // wait for the new ids here, on this rare path: the page loads in flight are then
       // never counted as something the id reads below depend on
       asm volatile("" ::"v"(blk_lane));
@@ -307,7 +308,7 @@ __device__ __forceinline__ void int2_split(
 
   // query limbs of the workgroup's heads into LDS: row 4 g + l holds limb l of head g
   // (rows of heads beyond GQ are zero)
-  for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 256) {
+  for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 64 * NW) {
     const int row = i >> 3;
     const int c = i & 7;
     const int g = row >> 2;
@@ -509,7 +510,7 @@ __device__ __forceinline__ void int2_split(
 
   // The prefetch is unconditional (past the last page the last page asks for itself again,
   // an L2 hit), so no path without it joins between the loads and the use of a page.
-  auto ntok_of = [&](int j) { return min(kPageTokens, nh - (p0 + kWaves * j) * kPageTokens); };
+  auto ntok_of = [&](int j) { return min(kPageTokens, nh - (p0 + NW * j) * kPageTokens); };
   auto next_of = [&](int j) { return page_of(j < n_mine ? j : n_mine - 1); };
   __syncthreads();  // query limbs in LDS
   if (n_mine > 0) {
@@ -553,16 +554,16 @@ __device__ __forceinline__ void int2_split(
   }
   __syncthreads();
 
-  for (int idx = tid; idx < GQ * kHeadDim; idx += 256) {
+  for (int idx = tid; idx < GQ * kHeadDim; idx += 64 * NW) {
     const int g = idx >> 7;
     const int dd = idx & 127;
     float big = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) big = fmaxf(big, wm_s[w][g]);
+    for (int w = 0; w < NW; ++w) big = fmaxf(big, wm_s[w][g]);
     float l = 0.f, a = 0.f;
     if (big != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float s = wm_s[w][g] == -INFINITY ? 0.f : exp2f(wm_s[w][g] - big);
         l = fmaf(s, wl_s[w][g], l);
         a = fmaf(s, wacc_s[w][g][dd], a);

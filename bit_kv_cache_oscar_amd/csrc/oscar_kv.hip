@@ -147,8 +147,16 @@ int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
   const int gq = desc->n_q_heads / desc->n_kv_heads;
   const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1);
-  long long s = (512 + groups / 2) / groups;   // about two workgroups per compute unit
-  const long long by_pages = (pages + 3) / 4;  // at least one page per wave
+  // small grids: one 8-wave workgroup per compute unit (at most 256 workgroups, which the
+  // fused decode runs with 8 waves); larger ones: about two 4-wave workgroups per unit
+  long long s, by_pages;
+  if (groups <= 128) {
+    s = 256 / groups;
+    by_pages = (pages + 7) / 8;  // at least one page per wave
+  } else {
+    s = (512 + groups / 2) / groups;
+    by_pages = (pages + 3) / 4;
+  }
   if (s > by_pages) s = by_pages;
   if (s < 1) s = 1;
   if (s > 65535) s = 65535;

@@ -54,21 +54,24 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
   int2::qprep_head(smem, a.q, a.rot_k, a.n_q, a.gq, a.scale_log2, a.hist.qlimb, a.hist.qscal, h, b);
 }
 
-// GQ query heads per workgroup, GQT per KV head (GQT = GQ n_groups)
-template <int GQ, int GQT>
-__global__ __launch_bounds__(256) void main_kernel(StepArgs a) {
+// GQ query heads per workgroup, GQT per KV head (GQT = GQ n_groups), NW waves
+template <int GQ, int GQT, int NW>
+__global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // the INT2 pass and the merge use the same LDS one after the other
-  __shared__ __align__(16) unsigned char smem[cmax(int2::int2_smem_bytes<GQ>(), merge::smem_bytes<GQT>())];
+  __shared__ __align__(16) unsigned char smem[cmax(int2::int2_smem_bytes<GQ, NW>(), merge::smem_bytes<GQT, NW>())];
   __shared__ int ticket_s;
-  int2::int2_split<GQ, true>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table, a.max_pages,
-                             a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits, a.hist.qlimb, a.hist.qscal, a.hist.m,
-                             a.hist.l, a.hist.acc);
+  int2::int2_split<GQ, true, NW>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table, a.max_pages,
+                                 a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits, a.hist.qlimb, a.hist.qscal,
+                                 a.hist.m, a.hist.l, a.hist.acc);
+  const int kv = blockIdx.y / a.n_groups;
+  const int b = blockIdx.z;
+  // R_V fragments of the merge, requested while the partial stores drain
+  uint4 rb[8 / NW][4];
+  merge::load_rv<NW>(a.rot_v, kv, rb);
   // the partials went out as agent-scope stores: once each thread's stores have completed
   // and the barrier has passed, the ticket below is drawn after all of them
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const int kv = blockIdx.y / a.n_groups;
-  const int b = blockIdx.z;
   int* counter = a.counters + b * a.n_kv + kv;
   if (threadIdx.x == 0) ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(256) void main_kernel(StepArgs a) {
   // last arrival for (b, kv): every workgroup of the group has drawn its ticket, so re-arm the
   // counter for the next launch; the group's partials are read with agent-scope loads
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  merge::merge_group<GQT>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, a.rot_v, a.out);
+  merge::merge_group<GQT, NW>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, rb, a.out);
 }
 
 template <int GQT>
@@ -86,10 +89,15 @@ hipError_t launch_prep(const StepArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Up to 256 workgroups (one per CU) run with 8 waves each, so few splits still give
+// every SIMD two waves; larger grids use 4 waves per workgroup.
 template <int GQ, int GQT>
 hipError_t launch_main(const StepArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((main_kernel<GQ, GQT>), dim3(a.n_splits, a.n_kv * a.n_groups, a.batch), dim3(256), 0, stream,
-                     a);
+  const dim3 grid(a.n_splits, a.n_kv * a.n_groups, a.batch);
+  if (static_cast<long long>(grid.x) * grid.y * grid.z <= 256)
+    hipLaunchKernelGGL((main_kernel<GQ, GQT, 8>), grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((main_kernel<GQ, GQT, 4>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

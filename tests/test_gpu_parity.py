@@ -74,7 +74,16 @@ DECODE_CASES = {
     "gq16": lambda: custom("gq16", 32, 2, [2500, 900]),
     "gq2": lambda: custom("gq2", 16, 8, [1500]),
     "edges": lambda: custom("edges", 8, 2, [100, 320, 321, 64 * 3 + 320, 1, 0 + 64 * 1 + 320 + 63]),
+    "gq1": lambda: custom("gq1", 4, 4, [900, 1700]),
 }
+
+
+def wide_splits(w):
+    """The smallest split count whose decode grid exceeds 256 workgroups (the fused decode
+    then runs 4 waves per workgroup instead of 8), or None past the 256-split limit."""
+    groups = w.batch * w.n_kv_heads * (w.gq // 8 if w.gq > 8 else 1)
+    s = 256 // groups + 1
+    return s if s <= 256 else None
 
 
 @pytest.mark.parametrize("case", list(DECODE_CASES))
@@ -90,7 +99,8 @@ def test_decode_on_oracle_pages(case):
     c.pool.copy_(torch.from_numpy(pool.reshape(-1)))
     q = queries(w)
     max_pages = int(np.max(-(-w.hist_lens // 64))) if w.batch else 0
-    for s in sorted({oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())), 1, 3, max_pages + 5}):
+    splits = {oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())), 1, 3, max_pages + 5, wide_splits(w)}
+    for s in sorted(x for x in splits if x is not None):
         say(case, "decode", "B", w.batch, "Hq", w.n_q_heads, "Hkv", w.n_kv_heads, "ctx", w.ctx_lens, "splits", s)
         c.set_splits(s)
         out = c.decode(q, w.sm_scale)
