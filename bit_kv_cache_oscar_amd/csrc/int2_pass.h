@@ -12,16 +12,23 @@
 // K side, per page: [4 heads x 4 rows] x [128 dims] x [64 tokens] on
 //   v_mfma_i32_16x16x64_i8. q_rot is a 22-bit fixed-point integer Q (|Q| <= 2^21) in three
 //   signed 8-bit limbs (rows 0..2 of a head; row 3 is zero), read from LDS each page. The
-//   three limb rows combine exactly in int32 into Q . c, and the per-head term -2 sum Q
-//   centres it to Q . (c - 2) (|.| <= 2^29). Centring the codes at 2 keeps the two terms of
-//   the fold small, so the fold runs in fp32.
+//   three limb rows combine exactly in int32 into Q . c; the per-head term -2 sum Q, which
+//   seeds the accumulator, centres it to Q . (c - 2) (|.| <= 2^29). Centring the codes at 2
+//   keeps the two terms of the fold small, so the fold runs in fp32. (Fewer query bits
+//   would let the codes enter with the cheaper scaled unpacking of the V side, but 22 bits
+//   are what keeps the score error well inside the output tolerance.)
 // V side, per page: [4 heads x 4 rows] x [64 tokens] x [16 dims] per dim tile. The
-//   weight P'_t = round(p_t s^V_t 2^E / 2) is a 23-bit integer (E wave-uniform, chosen from
-//   the largest V scale seen so that p s 2^E < 2^24), read straight from the bits of the
-//   float p s 2^E + 2^24; its three low bytes, each in signed range after an XOR with 0x80
-//   (the exponent bit already sets it for the top one), are rows 0..2 of the head, so the
-//   MFMA yields sum_t (byte_l - 128) c_t. Row 3 is constant 1 and yields sum_t c_t, which
-//   restores the 128 (1 + 2^8 + 2^16) offset.
+//   codes enter as int8 straight from the packed word with one mask per byte field
+//   (unpack16_scaled): field m (bits 2m..2m+1 of each byte) yields c 4^m for m < 3 and,
+//   after a shift by 2, 16 c for m = 3, so every code carries a factor (1, 4, 16, 16)[m].
+//   The weight P'_t = round(p_t s^V_t 2^E / (2 factor_t)) is an integer below 2^23 (E
+//   wave-uniform, chosen from the largest V scale seen so that p s 2^E < 2^24), read
+//   straight from the bits of the float p s 2^E / factor + 2^24; the code of slot t sits in
+//   field ((t % 16) / 4), so factor_t is constant per lane and P'_t times the scaled code is
+//   round(p s 2^E / 2) c up to rounding (P' keeps at least 19 significant bits). Its three low bytes, each in signed range after an
+//   XOR with 0x80 (the exponent bit already sets it for the top one), are rows 0..2 of the
+//   head, so the MFMA yields sum_t (byte_l - 128) c'_t with c' the scaled code. Row 3 is
+//   constant 1 and yields sum_t c'_t, which restores the 128 (1 + 2^8 + 2^16) offset.
 //   The int32 accumulators run across pages and are folded into fp32 sums only when a
 //   head's reference maximum or the fixed-point exponent must change. A reference maximum
 //   moves only when a score exceeds it by more than kTau (log2 units), so p <= 2^kTau.
@@ -50,13 +57,23 @@ typedef char i8x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// register m holds the codes at bits 2m..2m+1 of the packed word's four bytes
 __device__ __forceinline__ i8x16 unpack16(uint32_t w) {
-  // register m holds the codes at bits 2m..2m+1 of the packed word's four bytes
   uint4 u;
   u.x = w & 0x03030303u;
   u.y = (w >> 2) & 0x03030303u;
   u.z = (w >> 4) & 0x03030303u;
   u.w = (w >> 6) & 0x03030303u;
+  return __builtin_bit_cast(i8x16, u);
+}
+
+// as unpack16, with register m's codes times (1, 4, 16, 16)[m]: three masks and a shift
+__device__ __forceinline__ i8x16 unpack16_scaled(uint32_t w) {
+  uint4 u;
+  u.x = w & 0x03030303u;
+  u.y = w & 0x0C0C0C0Cu;
+  u.z = w & 0x30303030u;
+  u.w = (w >> 2) & 0x30303030u;
   return __builtin_bit_cast(i8x16, u);
 }
 
@@ -281,41 +298,17 @@ __device__ __forceinline__ void int2_split(
   const uint32_t meta16 = kKMeta + 16u * n;
   const size_t head0 = static_cast<size_t>(b) * n_q + h0;
 
-  // block ids of this wave's pages p0, p0 + NW, ...: lane i of blk_lane holds the id of the
-  // wave's page 64 chunk + i
-  const int p0 = p_begin + wave;
-  const int n_mine = p0 < p_end ? (p_end - p0 + NW - 1) / NW : 0;
-  int chunk = 0;
-  int blk_lane = (lane < n_mine) ? table[p0 + NW * lane] : 0;
-  asm volatile("" ::"v"(blk_lane));
-  auto page_of = [&](int j) -> const uint8_t* {  // j wave-uniform, 0 <= j < n_mine
-    if ((j >> 6) != chunk) {
-      chunk = j >> 6;
-      const int i = 64 * chunk + lane;
-      blk_lane = (i < n_mine) ? table[p0 + NW * i] : 0;
-      // wait for the new ids here, on this rare path: the page loads in flight are then
-      // never counted as something the id reads below depend on
-      asm volatile("" ::"v"(blk_lane));
-    }
-    return head_base + static_cast<size_t>(__builtin_amdgcn_readlane(blk_lane, j & 63)) * page_stride;
-  };
-  // three page buffers: pages i + 1 and i + 2 load while page i is processed. The first two
-  // are requested before the query operands; a wave without pages issues the same loads
-  // against an empty buffer, so every path carries the same loads into the loop.
-  const int rec = n_mine > 0 ? kHeadBlock : 0;
-  PageRegs buf[3];
-  load_page(buf[0], page_of(0), lane32, meta16, rec);
-
-  // query limbs of the workgroup's heads into LDS: row 4 g + l holds limb l of head g
-  // (rows of heads beyond GQ are zero)
-  for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 64 * NW) {
-    const int row = i >> 3;
-    const int c = i & 7;
-    const int g = row >> 2;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (g < GQ) v = *reinterpret_cast<const uint4*>(qlimb + (head0 + g) * 512 + (row & 3) * kHeadDim + 16 * c);
-    *reinterpret_cast<uint4*>(q_s + row * kQRow + 16 * c) = v;
-  }
+  // Prologue, in two memory round trips: the query operands (which do not depend on the
+  // block table) and the block ids, then the first two pages.
+  // query limbs of the workgroup's heads, bound for LDS: row 4 g + l holds limb l of head
+  // g (rows of heads beyond GQ are zero); one 16-byte chunk per thread
+  constexpr int kQChunks = 4 * MT * 4 * (kHeadDim / 16);
+  static_assert(kQChunks <= 64 * NW, "one query-limb chunk per thread");
+  const int qrow = tid >> 3;
+  const int qc = tid & 7;
+  uint4 qv = {0u, 0u, 0u, 0u};
+  if (tid < kQChunks && (qrow >> 2) < GQ)
+    qv = *reinterpret_cast<const uint4*>(qlimb + (head0 + (qrow >> 2)) * 512 + (qrow & 3) * kHeadDim + 16 * qc);
   float qsc[MT], sig[MT];
   int kcent[MT];
   bool head_ok[MT];
@@ -333,11 +326,37 @@ __device__ __forceinline__ void int2_split(
       qsc[mt] = sig[mt] = 0.f;
     }
   }
-  load_page(buf[1], page_of(n_mine > 1 ? 1 : 0), lane32, meta16, rec);
-  // The query operands must have arrived before the page loop: their loads then never
-  // count as outstanding inside it, and its waits let the next pages keep loading.
+
+  // block ids of this wave's pages p0, p0 + NW, ...: lane i of blk_lane holds the id of the
+  // wave's page 64 chunk + i
+  const int p0 = p_begin + wave;
+  const int n_mine = p0 < p_end ? (p_end - p0 + NW - 1) / NW : 0;
+  int chunk = 0;
+  int blk_lane = (lane < n_mine) ? table[p0 + NW * lane] : 0;
+  // Everything requested so far has arrived here: none of it counts as outstanding in the
+  // page loop, whose waits then let the next pages keep loading.
+  asm volatile("" ::"v"(blk_lane), "v"(qv.x), "v"(qv.y), "v"(qv.z), "v"(qv.w));
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(kcent[mt]), "v"(qsc[mt]), "v"(sig[mt]));
+  if (tid < kQChunks) *reinterpret_cast<uint4*>(q_s + qrow * kQRow + 16 * qc) = qv;
+  auto page_of = [&](int j) -> const uint8_t* {  // j wave-uniform, 0 <= j < n_mine
+    if ((j >> 6) != chunk) {
+      chunk = j >> 6;
+      const int i = 64 * chunk + lane;
+      blk_lane = (i < n_mine) ? table[p0 + NW * i] : 0;
+      // wait for the new ids here, on this rare path: the page loads in flight are then
+      // never counted as something the id reads below depend on
+      asm volatile("" ::"v"(blk_lane));
+    }
+    return head_base + static_cast<size_t>(__builtin_amdgcn_readlane(blk_lane, j & 63)) * page_stride;
+  };
+  // three page buffers: pages i + 1 and i + 2 load while page i is processed. A wave
+  // without pages issues the same loads against an empty buffer, so every path carries
+  // the same loads into the loop.
+  const int rec = n_mine > 0 ? kHeadBlock : 0;
+  PageRegs buf[3];
+  load_page(buf[0], page_of(0), lane32, meta16, rec);
+  load_page(buf[1], page_of(n_mine > 1 ? 1 : 0), lane32, meta16, rec);
 
   WaveState<MT> st;
 #pragma unroll
@@ -350,7 +369,11 @@ __device__ __forceinline__ void int2_split(
   }
   int E = 0;            // fixed-point exponent of the pending sums (wave-uniform)
   float thr = kTau;     // E + kTau: frame-relative scores above it move the reference
-  float vcap = -1.f;    // V scales below vcap fit the current E
+  // the codes of this lane's slots carry the factor (1, 4, 16, 16)[n % 4]: the V scales
+  // are taken over it (powers of two, exact)
+  const float vscale = (n & 3) == 0 ? 1.f : ((n & 3) == 1 ? 0.25f : 0.0625f);
+  const float vunscale = (n & 3) == 0 ? 1.f : ((n & 3) == 1 ? 4.f : 16.f);
+  float vcap_l = -1.f;  // V scales below vcap_l / vscale fit the current E
   bool fresh = true;    // no page processed yet
 
   // wave-private P'-limb rows: row mt*16 + 4 g + l; rows with l == 3 hold constant ones
@@ -397,7 +420,7 @@ __device__ __forceinline__ void int2_split(
       const i8x16 b1 = unpack16(cur.kword(nt, 1));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, i32x4{0, 0, 0, 0}));
+        d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, i32x4{kcent[mt], 0, 0, 0}));
     }
     // slot metadata of this lane's slots 4n..4n+3
     float sk[4], u[4], sv[4], zv[4];
@@ -407,7 +430,7 @@ __device__ __forceinline__ void int2_split(
       const uint32_t vm = cur.vmeta(nt);
       sk[nt] = f16_to_f32(km);
       u[nt] = fmaf(2.f, sk[nt], f16_to_f32(km >> 16));  // z + 2 s
-      sv[nt] = f16_to_f32(vm);
+      sv[nt] = f16_to_f32(vm) * vscale;  // V scale over the factor of this lane's codes
       zv[nt] = f16_to_f32(vm >> 16);
     }
     // scores relative to the frame: x = score_log2 - m + E
@@ -417,7 +440,9 @@ __device__ __forceinline__ void int2_split(
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const i32x4 c = d[mt][nt];
-        const int D = c[0] + (c[1] << 8) + (c[2] << 16) + kcent[mt];  // Q . (c - 2), exact
+        // Q . (c - 2), exact (the partial terms may wrap; the sum fits)
+        const int D = static_cast<int>(static_cast<uint32_t>(c[0]) + (static_cast<uint32_t>(c[1]) << 8) +
+                                       (static_cast<uint32_t>(c[2]) << 16));
         x[mt][nt] = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sig[mt], st.bias[mt]));
       }
     if (ntok < kPageTokens) {
@@ -439,15 +464,15 @@ __device__ __forceinline__ void int2_split(
       over = over || xm[mt] > thr;
     }
     const float svm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    const bool vover = svm > vcap;
+    const bool vover = svm > vcap_l;
     if (fresh || __any(over || vover)) {
       // a new exponent for the wave's V scales moves every tile's frame
       int e_new = E;
       if (__any(vover)) {
         int k = 0;
-        frexpf(wave_max_f32(svm), &k);  // largest V scale < 2^k
-        e_new = 24 - k - kTau;          // p s 2^E < 2^24 while p <= 2^kTau and s < 2^k
-        vcap = pow2f(k);
+        frexpf(wave_max_f32(svm * vunscale), &k);  // largest V scale < 2^k
+        e_new = 24 - k - kTau;                     // p s 2^E < 2^24 while p <= 2^kTau and s < 2^k
+        vcap_l = pow2f(k) * vscale;
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -501,7 +526,7 @@ __device__ __forceinline__ void int2_split(
     // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const i8x16 bv = unpack16(cur.vword(dt));
+      const i8x16 bv = unpack16_scaled(cur.vword(dt));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) st.acci[mt][dt] = mfma16(aP[mt], bv, st.acci[mt][dt]);
     }
@@ -513,18 +538,21 @@ __device__ __forceinline__ void int2_split(
   auto ntok_of = [&](int j) { return min(kPageTokens, nh - (p0 + NW * j) * kPageTokens); };
   auto next_of = [&](int j) { return page_of(j < n_mine ? j : n_mine - 1); };
   __syncthreads();  // query limbs in LDS
-  if (n_mine > 0) {
-    for (int i = 0;;) {
-      load_page(buf[2], next_of(i + 2), lane32, meta16);
-      process(buf[0], ntok_of(i));
-      if (++i >= n_mine) break;
-      load_page(buf[0], next_of(i + 2), lane32, meta16);
-      process(buf[1], ntok_of(i));
-      if (++i >= n_mine) break;
-      load_page(buf[1], next_of(i + 2), lane32, meta16);
-      process(buf[2], ntok_of(i));
-      if (++i >= n_mine) break;
-    }
+  // Whole triples of pages in a loop with one exit, then the last one or two: with a
+  // single back edge the compiler's wait for a page covers only that page, and the
+  // next one keeps loading.
+  int i = 0;
+  for (; i + 3 <= n_mine; i += 3) {
+    load_page(buf[2], next_of(i + 2), lane32, meta16);
+    process(buf[0], ntok_of(i));
+    load_page(buf[0], next_of(i + 3), lane32, meta16);
+    process(buf[1], ntok_of(i + 1));
+    load_page(buf[1], next_of(i + 4), lane32, meta16);
+    process(buf[2], ntok_of(i + 2));
+  }
+  if (i < n_mine) {
+    process(buf[0], ntok_of(i));
+    if (i + 1 < n_mine) process(buf[1], ntok_of(i + 1));
   }
 
   // ---- wave partials: lane (G, n) holds head 4mt + G, dims 16dt + n
