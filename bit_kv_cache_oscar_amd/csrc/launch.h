@@ -42,6 +42,10 @@ hipError_t launch_demote_rows(const LayerShape& L, const void* k_src, const void
                               const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k,
                               const void* rot_v, const float* clip_k, const float* clip_v, void* pool,
                               hipStream_t stream);
+hipError_t launch_demote_bulk(const LayerShape& L, const void* k_src, const void* v_src, int n,
+                              const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k,
+                              const void* rot_v, const float* clip_k, const float* clip_v, void* pool,
+                              hipStream_t stream);
 
 hipError_t launch_decode_int2(const LayerShape& L, const void* q, const void* rot_k, const void* pool,
                               const int32_t* block_table, int max_pages, const int32_t* hist_len,

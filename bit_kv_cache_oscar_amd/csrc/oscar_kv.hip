@@ -56,6 +56,8 @@ oscar::LayerShape shape_of(const oscar_layer_desc* d) {
   return s;
 }
 
+constexpr int kBulkMinRows = 64;  // oscar_demote takes the matrix-core kernel from this many tokens
+
 int window_splits_of(const oscar_layer_desc* d) { return (d->sink_tokens + d->recent_tokens + 63) / 64; }
 
 }  // namespace
@@ -175,6 +177,11 @@ int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void
   if (2LL * n * desc->n_kv_heads > 0x7FFFFFFFLL)
     return fail(OSCAR_ERR_UNSUPPORTED, "2 * n * n_kv_heads exceeds the grid limit");
   const oscar::LayerShape L = shape_of(desc);
+  // many rows: the matrix-core kernel (whole 16-token tiles); a few: one workgroup per row
+  if (n >= kBulkMinRows)
+    return hip_status(oscar::launch_demote_bulk(L, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v,
+                                                pool, static_cast<hipStream_t>(stream)),
+                      "demote launch");
   return hip_status(oscar::launch_demote_rows(L, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v,
                                               pool, static_cast<hipStream_t>(stream)),
                     "demote launch");
