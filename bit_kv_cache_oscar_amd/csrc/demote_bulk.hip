@@ -9,16 +9,19 @@
 // with R^T staged in LDS; a wave does 32 tokens per iteration as two 16-token tiles:
 //   y^T = R^T x^T on v_mfma_f32_16x16x32_bf16 (bf16 products are exact, sums in fp32), so
 //   lane (G, n) of a tile holds dims 16 mt + 4 G + e (mt < 8, e < 4) of token n.
-// The fp32 sums differ from the exact ones by at most delta = 32 2^-24 |x| max_j |R_:,j|
-// (Cauchy-Schwarz bounds sum_i |x_i R_ij|; the matrix cores' fp32 accumulation was measured
-// below 6.4 2^-24 sum |x_i R_ij| on adversarial magnitude mixes, and 32 leaves a margin).
+// The fp32 sums differ from the exact ones by at most delta = 16 2^-24 |x| max_j |R_:,j|
+// (Cauchy-Schwarz bounds sum_i |x_i R_ij| by |x| |R_:,j|; the matrix cores' fp32
+// accumulation was measured below 2.3 2^-24 |x| |R_:,j|, and below 6.4 2^-24 sum |x_i R_ij|,
+// on adversarial magnitude mixes, so 16 leaves a margin of 7).
 // Scales and zero points are then fixed exactly:
 //   - the exact extremes lie within delta of the fp32 ones; the fp64 chain of the quantiser
 //     is monotone in both, so when both ends of that interval round to the same fp16 scale
 //     and zero point, those are the values the exact extremes give;
 //   - otherwise the candidates (dims within 2 delta of an fp32 extreme) are summed again in
-//     fp64 from the exact products with compensated (two-sum) sums across the wave, and the
-//     chain runs on the exact extremes.
+//     fp64 from the exact products, four at a time (one per 16-lane group, a DPP tree), with
+//     an error bound of its own, and the same interval test runs on those sums; when even
+//     that leaves the fp16 values open, compensated (two-sum) sums across the wave give the
+//     exact extremes and the chain runs on them.
 // Codes come from the fp32 y when delta / s16 <= 9e-5, which keeps every code on the side of
 // its rounding boundary the exact value is on unless the exact value lies within 1e-4 of
 // the boundary; a token failing that test has all 128 values summed exactly instead.
@@ -33,10 +36,10 @@ namespace oscar {
 namespace {
 
 constexpr int kBWaves = 4;
-constexpr int kIters = 2;                              // 32-token iterations per wave
-constexpr int kRowsPerBlock = kBWaves * 32 * kIters;   // 256
+constexpr int kIters = 8;                              // 32-token iterations per wave
+constexpr int kRowsPerBlock = kBWaves * 32 * kIters;   // 1024
 constexpr int kRTRow = kHeadDim + 8;                   // bf16 per LDS row of R^T (16 bytes of bank spread)
-constexpr double kAccUlps = 32.0;                      // fp32 accumulation budget, units of 2^-24 sum|x R|
+constexpr double kAccUlps = 16.0;                      // fp32 accumulation budget, units of 2^-24 |x| max|R_:,j|
 constexpr double kCodeSlack = 9e-5;                    // largest tolerated error of t = (y - z16) / s16
 
 struct BulkSmem {
@@ -85,6 +88,76 @@ __device__ __forceinline__ double coop_dot(const uint16_t* xrow, const uint16_t*
   return s + c;
 }
 
+// sum_i x_i R_ij in fp64 from the exact products, by the whole wave as a plain tree (lane L
+// takes i = 2L, 2L+1): seven rounded additions, so |error| <= 7 2^-53 sum_i |x_i R_ij|
+__device__ __forceinline__ double tree_dot(const uint16_t* xrow, const uint16_t* rtrow, int lane) {
+#pragma clang fp contract(off)
+  const uint32_t xv = *reinterpret_cast<const uint32_t*>(xrow + 2 * lane);
+  const uint32_t rv = *reinterpret_cast<const uint32_t*>(rtrow + 2 * lane);
+  double s = bf16lo(xv) * bf16lo(rv) + bf16hi(xv) * bf16hi(rv);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+  return s;
+}
+
+// a 64-bit value through a DPP row operation (both halves with the same control)
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                                     static_cast<uint32_t>(lo)));
+}
+
+// y_j of one x row for the dim j of this lane's 16-lane group: lane q of the group takes
+// i = 8q .. 8q + 7, the exact products are summed in fp64 in the lane and over the group by
+// DPP (eleven rounded additions, |error| <= 11 2^-53 sum_i |x_i R_ij|); every lane of the
+// group gets the sum
+__device__ __forceinline__ double group_dot(const uint16_t* xrow, const uint16_t* rtrow, int q) {
+#pragma clang fp contract(off)
+  const uint4 xv = *reinterpret_cast<const uint4*>(xrow + 8 * q);
+  const uint4 rv = *reinterpret_cast<const uint4*>(rtrow + 8 * q);
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    s += bf16lo(xw[k]) * bf16lo(rw[k]);
+    s += bf16hi(xw[k]) * bf16hi(rw[k]);
+  }
+  s += dpp_f64<kDppQuadXor1>(s);
+  s += dpp_f64<kDppQuadXor2>(s);
+  s += dpp_f64<kDppHalfMirror>(s);
+  s += dpp_f64<kDppMirror>(s);
+  return s;
+}
+
+// the fp32 neighbours of a finite fp32 value (one unit in the last place down / up)
+__device__ __forceinline__ float f32_prev(float f) {
+  const int b = __float_as_int(f);
+  return f > 0.f ? __int_as_float(b - 1) : (f < 0.f ? __int_as_float(b + 1) : -__int_as_float(1));
+}
+__device__ __forceinline__ float f32_next(float f) {
+  const int b = __float_as_int(f);
+  return f > 0.f ? __int_as_float(b + 1) : (f < 0.f ? __int_as_float(b - 1) : __int_as_float(1));
+}
+
+// an fp32 value at or below / at or above the fp64 value x (|x| below the fp32 range)
+__device__ __forceinline__ float f32_down(double x) {
+  const float f = static_cast<float>(x);
+  return static_cast<double>(f) > x ? f32_prev(f) : f;
+}
+__device__ __forceinline__ float f32_up(double x) {
+  const float f = static_cast<float>(x);
+  return static_cast<double>(f) < x ? f32_next(f) : f;
+}
+
+// fp16 bits of an fp32 value, rounded to nearest even by the hardware conversion
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
 // exact code of value y (fp64) under (s16, z16), as the quantiser defines it
 __device__ __forceinline__ uint32_t exact_code(double y, uint16_t s16, uint16_t z16) {
 #pragma clang fp contract(off)
@@ -115,21 +188,73 @@ __device__ __attribute__((noinline)) uint64_t exact_tokens(const uint16_t* xs, c
     const uint16_t* xrow = xs + nf * kHeadDim;
     const double fdl = __shfl(delta, nf, 64);
     uint32_t cnf = n_ == nf ? cand : 0u;
+    // first fp64 sums of the candidates with an error bound of their own, four at a time;
+    // the compensated sums only when that interval still leaves the fp16 results open
+    const uint32_t cnf0 = cnf;
     double emax = -INFINITY, emin = INFINITY;
     uint64_t lanes = __ballot(cnf != 0u);
     while (lanes) {
-      const int ls = __builtin_ctzll(lanes);
-      const uint32_t cm = __builtin_amdgcn_readlane(cnf, ls);
-      const int b = __builtin_ctz(cm);
-      if (lane == ls) cnf &= cnf - 1u;
-      lanes = __ballot(cnf != 0u);
-      const int j = 16 * (b >> 2) + 4 * (ls >> 4) + (b & 3);
-      const double y = coop_dot(xrow, rt + j * kRTRow, lane);
-      emax = fmax(emax, y);
-      emin = fmin(emin, y);
+      int js[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        js[r] = -1;
+        if (lanes) {
+          const int ls = __builtin_ctzll(lanes);
+          const uint32_t cm = __builtin_amdgcn_readlane(cnf, ls);
+          const int b = __builtin_ctz(cm);
+          if (lane == ls) cnf &= cnf - 1u;
+          lanes = __ballot(cnf != 0u);
+          js[r] = 16 * (b >> 2) + 4 * (ls >> 4) + (b & 3);
+        }
+      }
+      const int g = lane >> 4;
+      const int jg = g == 0 ? js[0] : (g == 1 ? js[1] : (g == 2 ? js[2] : js[3]));
+      const double y = group_dot(xrow, rt + (jg < 0 ? 0 : jg) * kRTRow, lane & 15);
+      const uint64_t yu = static_cast<uint64_t>(__double_as_longlong(y));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (js[r] < 0) continue;
+        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(yu)), 16 * r);
+        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(yu >> 32)), 16 * r);
+        const double yr = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+        emax = fmax(emax, yr);
+        emin = fmin(emin, yr);
+      }
     }
-    uint16_t es16, ez16;
-    scale_zero(cr, emax, emin, es16, ez16);
+    uint16_t es16 = 0, ez16 = 0;
+    bool known = false;
+    if (cr > 0.0) {
+#pragma clang fp contract(off)
+      // sum |x_i R_ij| <= fdl 2^20 (fdl = 16 2^-24 times that bound), so the sums are within
+      // 11 2^-53 2^20 fdl < 2^-28 fdl; then room for rounding the chain in fp64, and the fp16
+      // decision on fp32 ends rounded outward
+      const double d64 = fdl * 0x1p-28 + 0x1p-50 * fmax(fabs(emax), fabs(emin)) + 0x1p-1000;
+      const double hA = cr * (emax - d64), hB = cr * (emax + d64);
+      const double lC = cr * (emin - d64), lD = cr * (emin + d64);
+      const double m = 0x1p-50 * (fabs(hB) + fabs(lC)) + 0x1p-1000;
+      const double sLo = (hA - lD) * (1.0 / 3.0) - m, sHi = (hB - lC) * (1.0 / 3.0) + m;
+      es16 = f32_to_f16_bits(f32_down(sLo));
+      ez16 = f32_to_f16_bits(f32_down(lC - m));
+      known = sLo >= 0.0 && es16 == f32_to_f16_bits(f32_up(sHi)) && ez16 == f32_to_f16_bits(f32_up(lD + m));
+    }
+    if (!known) {
+      cnf = cnf0;
+      emax = -INFINITY;
+      emin = INFINITY;
+      lanes = __ballot(cnf != 0u);
+      while (lanes) {
+        const int ls = __builtin_ctzll(lanes);
+        const uint32_t cm = __builtin_amdgcn_readlane(cnf, ls);
+        const int b = __builtin_ctz(cm);
+        if (lane == ls) cnf &= cnf - 1u;
+        lanes = __ballot(cnf != 0u);
+        const int j = 16 * (b >> 2) + 4 * (ls >> 4) + (b & 3);
+        const double y = coop_dot(xrow, rt + j * kRTRow, lane);
+        emax = fmax(emax, y);
+        emin = fmin(emin, y);
+      }
+      scale_zero(cr, emax, emin, es16, ez16);
+    }
     const double esv = h2d(es16);
     const bool full = !(cr > 0.0) || (esv != 0.0 && !(fdl <= kCodeSlack * esv));
     if (full) {
@@ -307,29 +432,35 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
       nx += __shfl_xor(nx, 32, 64);
       // error bound of every fp32 value of this token (the norms carry their own fp32
       // rounding, covered by the last factor)
-      const double delta =
-          kAccUlps * 0x1p-24 * sqrt(static_cast<double>(nx) * static_cast<double>(colmax2)) * (1.0 + 0x1p-10);
+      const float dl = static_cast<float>(kAccUlps * 0x1p-24) * sqrtf(nx * colmax2) * (1.f + 0x1p-10f);
 
-      // scale and zero point from the interval of the extremes
+      // scale and zero point from the interval of the extremes. The exact extremes lie in
+      // [mx - dl, mx + dl] and [mn - dl, mn + dl]; the chain below evaluates the quantiser's
+      // steps on those ends in fp32 and widens the results by more than every rounding of
+      // either evaluation (fp32 here, fp64 in the quantiser), so they bound the true scale
+      // and zero point. Rounding to fp16 is monotone: equal ends mean a determined value.
       uint16_t s16 = 0, z16 = 0;
       bool exact = true;
       {
 #pragma clang fp contract(off)
-        const double ymx = mx, ymn = mn;
-        if (cr > 0.0 && delta < INFINITY && mx != -INFINITY) {
-          const double hA = cr * (ymx - delta), hB = cr * (ymx + delta);
-          const double lC = cr * (ymn - delta), lD = cr * (ymn + delta);
-          const double sMin = (hA - lD) / 3.0, sMax = (hB - lC) / 3.0;
-          s16 = f64_to_f16_rne(sMin);
-          z16 = f64_to_f16_rne(lC);
-          exact = s16 == f64_to_f16_rne(sMax) && z16 == f64_to_f16_rne(lD);
-          const double sv = h2d(s16);
-          if (exact && sv != 0.0) exact = delta <= kCodeSlack * sv;
+        const float c32 = static_cast<float>(cr);
+        if (cr > 0.0 && dl < INFINITY && mx != -INFINITY) {
+          const float hA = c32 * (mx - dl), hB = c32 * (mx + dl);
+          const float lC = c32 * (mn - dl), lD = c32 * (mn + dl);
+          const float ms = 0x1p-21f * (fabsf(hB) + fabsf(lC)) + 0x1p-140f;
+          const float mz = 0x1p-21f * fabsf(lC) + 0x1p-140f;
+          const float sLo = (hA - lD) * (1.f / 3.f) - ms, sHi = (hB - lC) * (1.f / 3.f) + ms;
+          s16 = f32_to_f16_bits(sLo);
+          z16 = f32_to_f16_bits(lC - mz);
+          exact = sLo >= 0.f && s16 == f32_to_f16_bits(sHi) && z16 == f32_to_f16_bits(lD + mz);
+          const float sv = f16_to_f32(s16);
+          if (exact && sv != 0.f) exact = dl <= static_cast<float>(kCodeSlack) * sv;
         } else {
           exact = false;
         }
         if (!valid) exact = true;  // nothing to do for tokens past the end
       }
+      const double delta = dl;
 
       // tokens whose interval test failed: exact candidates, then the exact chain; tokens
       // whose codes cannot come from fp32 values: all 128 values exact
@@ -341,7 +472,6 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         // within 2 delta exactly), one bit per (mt, e)
         uint32_t cand = 0u;
         if (!exact) {
-          const float dl = static_cast<float>(delta);
           const float thi = mx - 3.f * dl;
           const float tlo = mn + 3.f * dl;
 #pragma unroll
