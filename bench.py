@@ -164,6 +164,58 @@ def cpu_baseline(w, budget_s):
     }
 
 
+BULK_TOKENS = 32768  # the bulk-demotion workload: 262,144 K rows and 262,144 V rows at 8 KV heads
+
+
+def bulk_demote(w, rk_bits, rv_bits, dev, stream, reps):
+    """oscar_demote of BULK_TOKENS history tokens (every KV head, K and V) into fresh pages,
+    timed with HIP events on the launch stream; rows drawn like the workload's history."""
+    import torch
+
+    import synth
+    from bit_kv_cache_oscar_amd.layer import LayerCache
+
+    n_pages = BULK_TOKENS // 64
+    c = LayerCache(w.n_q_heads, w.n_kv_heads, 1, n_pages, n_pages, device=dev)
+    clip = np.full(w.n_kv_heads, w.clip_ratio, np.float32)
+    c.set_rotations(rk_bits, rv_bits, clip, clip)
+    ks, vs = [], []
+    for kv in range(w.n_kv_heads):
+        k, v = synth.kv_rows(w, 0, kv, 64, 64 + BULK_TOKENS)
+        ks.append(k)
+        vs.append(v)
+    kk = torch.from_numpy(np.stack(ks, 1)).to(dev).to(torch.bfloat16)
+    vv = torch.from_numpy(np.stack(vs, 1)).to(dev).to(torch.bfloat16)
+    j = torch.arange(BULK_TOKENS, dtype=torch.int32, device=dev)
+    pg, sl = (j // 64).contiguous(), (j % 64).contiguous()
+    c.demote(kk, vv, pg, sl, stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        c.demote(kk, vv, pg, sl, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / reps
+    rows = 2 * BULK_TOKENS * w.n_kv_heads
+    # 256 B in and 36 B out per row, and both rotations of every KV head
+    nbytes = rows * (256 + 36) + w.n_kv_heads * 2 * ROT_BYTES
+    return {
+        "kernel": "demote_bulk_kernel (oscar_demote)",
+        "tokens": BULK_TOKENS,
+        "rows": rows,
+        "us": round(us, 3),
+        "bound": "hbm",
+        "achieved": round(nbytes / (us * 1e-6) / 1e9, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes": nbytes,
+        "mfma_tflops": round(rows * 2 * 128 * 128 / (us * 1e-6) / 1e12, 2),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -317,6 +369,9 @@ def main():
             "bytes_per_launch": attend_bytes,
         },
     }
+    if args.config == 5:
+        # the bulk-demotion row of this workload (after the decode timing: it allocates)
+        out["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5))
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
