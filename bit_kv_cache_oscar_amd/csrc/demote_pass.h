@@ -6,12 +6,17 @@
 // is rotated, clipped, quantised and packed four 2-bit codes per byte into the INT2
 // history, with a scale and zero point per group.
 //
-// One workgroup of 256 threads handles one row (token, KV head, K or V) with its rotation
-// staged in LDS; threads j and j + 128 sum the two halves of output dim j. Each half is
-// accumulated in fp64 with compensated (two-sum) chains over exact bf16 x bf16 products
-// and the halves are joined by the same two-sum, so the group extremes, and from them the
-// fp16 scale and zero point, come from the dot product's fp64 value; the scale/zero
-// arithmetic is fp64 exactly as specified.
+// One workgroup of 256 threads handles one row (token, KV head, K or V). Every global
+// read of the row (the token, the rotation, the destination and the clip ratio) is
+// issued before any arithmetic. Wave w sums the terms 32w..32w+31 of the output dims
+// 2 lane, 2 lane + 1 in fp64 (bf16 x bf16 products are exact there), with sum |p| beside
+// each sum; wave 0 joins the four quarters and bounds the error of each dim by
+// 2^-47 sum|p| (at most 36 roundings on any path of the fixed summation order). The
+// group extremes, fp16 scale and zero point, and every code are then taken at both ends
+// of these intervals: when both ends agree (all but a vanishing fraction of rows), the
+// decisions equal those made from the exact dot products. Otherwise wave 0 recomputes
+// the row's dot products with compensated (two-sum) fp64 sums and decides from those.
+// The scale/zero arithmetic is fp64 exactly as specified.
 
 #pragma once
 
@@ -21,7 +26,13 @@
 namespace oscar {
 namespace demote {
 
-constexpr int kSmemBytes = kHeadDim * kHeadDim * 2 + kHeadDim * 8 + kHeadDim * 16 + 64 + kHeadDim;
+// quarter partials of waves 1..3: [3][64 lanes][s0, s1, a0, a1]
+constexpr int kSmemBytes = 3 * 64 * 4 * 8;
+
+// Fixed-order fp64 sum of 128 exact products: 32 terms per quarter chain, three joins,
+// each sum rounded once, so |error| <= 36 (2^-53 + tiny) sum|p| < 2^-47 sum|p|; the
+// remaining 28 2^-53 sum|p| covers the rounding of the interval ends themselves.
+constexpr double kBound = 0x1p-47;
 
 __device__ __forceinline__ void two_sum_add(double& s, double& c, double p) {
   const double t = s + p;
@@ -30,6 +41,48 @@ __device__ __forceinline__ void two_sum_add(double& s, double& c, double p) {
   s = t;
 }
 
+struct ScaleZero {
+  uint16_t s16, z16;
+};
+
+// fp16 scale and zero point of a group whose extremes are ymax, ymin (clip ratio cr)
+__device__ __forceinline__ ScaleZero scale_zero(double cr, double ymax, double ymin) {
+#pragma clang fp contract(off)
+  const double hi = cr * ymax;
+  const double lo = cr * ymin;
+  return {f64_to_f16_rne((hi - lo) / 3.0), f64_to_f16_rne(lo)};
+}
+
+// 2-bit code of rotated value y: round half to even of (y - z) / s, clamped to [0, 3]
+__device__ __forceinline__ int code_of(double y, double z16d, double s16d) {
+#pragma clang fp contract(off)
+  if (s16d == 0.0) return 0;
+  const double t = rint((y - z16d) / s16d);
+  return t > 3.0 ? 3 : (t >= 0.0 ? static_cast<int>(t) : 0);
+}
+
+struct Pair {
+  double y0, y1;
+};
+
+// Compensated fp64 dot products of dims 2 lane and 2 lane + 1 over all 128 terms (the
+// rare path: rows whose interval decisions did not settle).
+__device__ __noinline__ Pair exact_pair(const uint16_t* __restrict__ src, const uint16_t* __restrict__ rot,
+                                        int lane) {
+#pragma clang fp contract(off)
+  double s0 = 0.0, c0 = 0.0, s1 = 0.0, c1 = 0.0;
+  for (int i = 0; i < kHeadDim; ++i) {
+    const double xd = bf16_to_f64(src[i]);
+    const uint32_t r = *reinterpret_cast<const uint32_t*>(rot + i * kHeadDim + 2 * lane);
+    two_sum_add(s0, c0, xd * static_cast<double>(__uint_as_float(r << 16)));
+    two_sum_add(s1, c1, xd * static_cast<double>(__uint_as_float(r & 0xFFFF0000u)));
+  }
+  return {s0 + c0, s1 + c1};
+}
+
+// Bit position of dim d's code in its K word (dim 16w + 4m + jj at bits 8jj + 2m).
+__device__ __forceinline__ int k_shift(int d) { return 8 * (d & 3) + 2 * ((d & 15) >> 2); }
+
 // `item` = 2 (token n_kv + head) + (1 for V, 0 for K)
 __device__ __forceinline__ void demote_row(unsigned char* __restrict__ smem, int item,
                                            const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
@@ -37,104 +90,120 @@ __device__ __forceinline__ void demote_row(unsigned char* __restrict__ smem, int
                                            const int32_t* __restrict__ dst_slot, const uint16_t* __restrict__ rot_k,
                                            const uint16_t* __restrict__ rot_v, const float* __restrict__ clip_k,
                                            const float* __restrict__ clip_v, uint8_t* __restrict__ pool) {
-  // every product and sum below is rounded on its own, as the quantiser specifies
 #pragma clang fp contract(off)
-  uint16_t* r_s = reinterpret_cast<uint16_t*>(smem);
-  double* xs = reinterpret_cast<double*>(smem + kHeadDim * kHeadDim * 2);
-  double* half_s = xs + kHeadDim;                 // (s, c) of the upper halves
-  double* red_s = half_s + 2 * kHeadDim;          // wave maxima then minima
-  uint8_t* codes_s = reinterpret_cast<uint8_t*>(red_s + 8);
-
+  double(*part)[64][4] = reinterpret_cast<double(*)[64][4]>(smem);
   const int row = item >> 1;  // token * n_kv + head
   const int is_v = item & 1;
   const int tok = row / n_kv;
   const int head = row - tok * n_kv;
-  const int tid = threadIdx.x;
-  const int j = tid & (kHeadDim - 1);
-  const int half = tid >> 7;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const uint16_t* src = (is_v ? v_src : k_src) + static_cast<size_t>(row) * kHeadDim;
-  stage_rotation(r_s, (is_v ? rot_v : rot_k) + static_cast<size_t>(head) * kHeadDim * kHeadDim, tid, 256);
-  if (tid < kHeadDim) xs[tid] = bf16_to_f64(src[tid]);
-  __syncthreads();
+  const uint16_t* rot = (is_v ? rot_v : rot_k) + static_cast<size_t>(head) * kHeadDim * kHeadDim;
 
-  // two independent compensated chains per half (for latency), joined by the same two-sum
-  double s[2] = {0.0, 0.0}, c[2] = {0.0, 0.0};
-  const int i0 = 64 * half;
-#pragma unroll 8
-  for (int i = i0; i < i0 + 64; i += 2)
+  // ---- every read of the row, issued before any arithmetic
+  uint32_t xw[16], rw[32];
+  const uint32_t* xp = reinterpret_cast<const uint32_t*>(src + 32 * wave);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) two_sum_add(s[u], c[u], xs[i + u] * bf16_to_f64(r_s[(i + u) * kHeadDim + j]));
-  double st = s[0], ct = c[0] + c[1];
-  two_sum_add(st, ct, s[1]);
-  if (half) {
-    half_s[2 * j] = st;
-    half_s[2 * j + 1] = ct;
-  }
-  __syncthreads();
-  double y = 0.0;
-  if (!half) {
-    ct += half_s[2 * j + 1];
-    two_sum_add(st, ct, half_s[2 * j]);
-    y = st + ct;
-  }
-  // extremes over the 128 dims (waves 0 and 1)
-  const double wmax = wave_max(y);
-  const double wmin = wave_min(y);
-  if ((tid & 63) == 0 && wave < 2) {
-    red_s[wave] = wmax;
-    red_s[4 + wave] = wmin;
-  }
-  __syncthreads();
-  const double ymax = fmax(red_s[0], red_s[1]);
-  const double ymin = fmin(red_s[4], red_s[5]);
-
-  const double cr = static_cast<double>(is_v ? clip_v[head] : clip_k[head]);
-  const double hi = cr * ymax;
-  const double lo = cr * ymin;
-  const double sc = (hi - lo) / 3.0;
-  const uint16_t s16 = f64_to_f16_rne(sc);
-  const uint16_t z16 = f64_to_f16_rne(lo);
-  const double s16d = f16_bits_to_f64(s16);
-  const double z16d = f16_bits_to_f64(z16);
-  int code = 0;
-  if (s16d != 0.0) {
-    const double t = rint((y - z16d) / s16d);
-    code = t < 0.0 ? 0 : (t > 3.0 ? 3 : static_cast<int>(t));
+  for (int k = 0; k < 16; ++k) xw[k] = xp[k];
+  const uint32_t* rp = reinterpret_cast<const uint32_t*>(rot + 32 * wave * kHeadDim + 2 * lane);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) rw[i] = rp[i * (kHeadDim / 2)];
+  int page = 0, slot = 0;
+  float crf = 0.f;
+  if (wave == 0) {
+    page = dst_page[tok];
+    slot = dst_slot[tok];
+    crf = is_v ? clip_v[head] : clip_k[head];
   }
 
-  const int page = dst_page[tok];
-  const int slot = dst_slot[tok];
+  // ---- this quarter's 32 terms of dims 2 lane, 2 lane + 1, and sum |p|
+  double s0 = 0.0, s1 = 0.0, a0 = 0.0, a1 = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t xb = (i & 1) ? (xw[i >> 1] & 0xFFFF0000u) : (xw[i >> 1] << 16);
+    const double xd = static_cast<double>(__uint_as_float(xb));
+    const double r0 = static_cast<double>(__uint_as_float(rw[i] << 16));
+    const double r1 = static_cast<double>(__uint_as_float(rw[i] & 0xFFFF0000u));
+    s0 = fma(xd, r0, s0);
+    s1 = fma(xd, r1, s1);
+    a0 = fma(fabs(xd), fabs(r0), a0);
+    a1 = fma(fabs(xd), fabs(r1), a1);
+  }
+  if (wave > 0) {
+    double* pp = part[wave - 1][lane];
+    pp[0] = s0;
+    pp[1] = s1;
+    pp[2] = a0;
+    pp[3] = a1;
+  }
+  __syncthreads();
+  if (wave > 0) return;  // uniform per wave; no barrier follows
+
+  // ---- wave 0: join the quarters, decide on the error intervals
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    const double* pp = part[w][lane];
+    s0 = s0 + pp[0];
+    s1 = s1 + pp[1];
+    a0 = a0 + pp[2];
+    a1 = a1 + pp[3];
+  }
+  double y0 = s0, y1 = s1;
+  double d0 = kBound * a0, d1 = kBound * a1;
+  const double cr = static_cast<double>(crf);
+  ScaleZero sz;
+  int c0, c1;
+  for (int pass = 0;; ++pass) {
+    const double ymax = wave_max_f64(fmax(y0, y1));
+    const double ymin = wave_min_f64(fmin(y0, y1));
+    const double dm = wave_max_f64(fmax(d0, d1));
+    // the scale is monotone in each extreme, so its range over the intervals is spanned
+    // by these two corners; the zero point by the two ends of ymin's interval
+    sz = scale_zero(cr, ymax - dm, ymin + dm);
+    const ScaleZero sz2 = scale_zero(cr, ymax + dm, ymin - dm);
+    const double s16d = f16_bits_to_f64(sz.s16);
+    const double z16d = f16_bits_to_f64(sz.z16);
+    c0 = code_of(y0 - d0, z16d, s16d);
+    c1 = code_of(y1 - d1, z16d, s16d);
+    // wave-uniform: both ends of every interval give the same decision (dm finite also
+    // rules out overflow and NaN in the products)
+    const bool row_ok = (sz.s16 == sz2.s16) && (sz.z16 == sz2.z16) && dm <= 1e300;
+    const bool lane_ok = (c0 == code_of(y0 + d0, z16d, s16d)) && (c1 == code_of(y1 + d1, z16d, s16d));
+    if (pass == 1 || (row_ok && __all(lane_ok))) break;
+    const Pair e = exact_pair(src, rot, lane);
+    y0 = e.y0;
+    y1 = e.y1;
+    d0 = d1 = 0.0;
+  }
+
+  // ---- stores: scale/zero, then the codes
   uint8_t* blk = pool + (static_cast<size_t>(page) * n_kv + head) * kHeadBlock;
-  if (tid == 0) {
+  if (lane == 0) {
     uint32_t* meta = reinterpret_cast<uint32_t*>(blk + (is_v ? kVMeta : kKMeta) + 4 * slot);
-    *meta = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
+    *meta = static_cast<uint32_t>(sz.s16) | (static_cast<uint32_t>(sz.z16) << 16);
   }
+  const int dd = 2 * lane;
   if (is_v) {
     // V codes are dim-major: this dim's word for slots 16u..16u+15 is shared with other
     // tokens, so clear and set only this slot's two bits.
-    if (!half) {
-      const int r = slot & 15;
-      const int sh = 8 * (r & 3) + 2 * (r >> 2);
-      uint32_t* w = reinterpret_cast<uint32_t*>(blk + v_word_offset(j, slot >> 4));
-      atomicAnd(w, ~(3u << sh));
-      atomicOr(w, static_cast<uint32_t>(code) << sh);
-    }
-    return;  // uniform over the workgroup: is_v is per row
+    const int r = slot & 15;
+    const int sh = 8 * (r & 3) + 2 * (r >> 2);
+    uint32_t* w0 = reinterpret_cast<uint32_t*>(blk + v_word_offset(dd, slot >> 4));
+    uint32_t* w1 = reinterpret_cast<uint32_t*>(blk + v_word_offset(dd + 1, slot >> 4));
+    atomicAnd(w0, ~(3u << sh));
+    atomicAnd(w1, ~(3u << sh));
+    atomicOr(w0, static_cast<uint32_t>(c0) << sh);
+    atomicOr(w1, static_cast<uint32_t>(c1) << sh);
+    return;
   }
-  if (!half) codes_s[j] = static_cast<uint8_t>(code);
-  __syncthreads();
-  if (tid < 8) {
-    // K word w holds dims 16w..16w+15, dim 16w+4m+jj at bits 8jj+2m.
-    uint32_t word = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        word |= static_cast<uint32_t>(codes_s[16 * tid + 4 * m + jj]) << (8 * jj + 2 * m);
-    *reinterpret_cast<uint32_t*>(blk + k_word_offset(slot, tid)) = word;
-  }
+  // K word w (dims 16w..16w+15) gathers lanes 8w..8w+7; their bits are disjoint
+  uint32_t bits = (static_cast<uint32_t>(c0) << k_shift(dd)) | (static_cast<uint32_t>(c1) << k_shift(dd + 1));
+  bits |= __shfl_xor(bits, 1, 64);
+  bits |= __shfl_xor(bits, 2, 64);
+  bits |= __shfl_xor(bits, 4, 64);
+  if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(blk + k_word_offset(slot, lane >> 3)) = bits;
 }
 
 }  // namespace demote

@@ -44,35 +44,20 @@ __device__ __forceinline__ float f16_to_f32(uint32_t h) {
   return static_cast<float>(v);
 }
 
-// Nearest fp16 of a double (ties to even), in one rounding step from the fp64 value.
-// Overflow gives +-inf, NaN gives a quiet NaN, magnitudes below half the smallest
-// subnormal give +-0.
+// Nearest fp16 of a double (ties to even), as if rounded once from the fp64 value: the
+// double is first rounded to fp32 with rounding to odd (to nearest, then, when inexact,
+// stepped back toward zero if it went away from it and given an odd last bit), which keeps
+// 24 >= 11 + 2 significand bits, so the hardware's fp32 -> fp16 rounding to nearest even
+// then yields the fp64 value's nearest fp16 (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", IEEE Trans. Computers
+// 57(4), 2008). Overflow gives +-inf, magnitudes below half the smallest subnormal +-0.
 __device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
-  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
-  const uint32_t sign = static_cast<uint32_t>(u >> 48) & 0x8000u;
-  const uint64_t a = u & 0x7FFFFFFFFFFFFFFFull;
-  if (a >= 0x7FF0000000000000ull) return static_cast<uint16_t>(sign | (a > 0x7FF0000000000000ull ? 0x7E00u : 0x7C00u));
-  const int e = static_cast<int>(a >> 52);
-  if (e == 0) return static_cast<uint16_t>(sign);
-  const uint64_t m = (a & 0xFFFFFFFFFFFFFull) | 0x10000000000000ull;  // value = m * 2^(e-1075)
-  int he = e - 1008;                                                  // fp16 biased exponent
-  int shift = 42;                                                     // keep 11 bits when normal
-  if (he < 1) {
-    shift = 43 - he;  // subnormal: units of 2^-24
-    he = 0;
-  }
-  if (shift >= 54) return static_cast<uint16_t>(sign);
-  uint64_t q = m >> shift;
-  const uint64_t rem = m & ((1ull << shift) - 1);
-  const uint64_t halfway = 1ull << (shift - 1);
-  if (rem > halfway || (rem == halfway && (q & 1))) ++q;
-  if (he == 0) return static_cast<uint16_t>(sign | static_cast<uint32_t>(q));  // q == 1024 is the min normal
-  if (q == 2048) {
-    q = 1024;
-    ++he;
-  }
-  if (he >= 31) return static_cast<uint16_t>(sign | 0x7C00u);
-  return static_cast<uint16_t>(sign | (static_cast<uint32_t>(he) << 10) | static_cast<uint32_t>(q - 1024));
+  const float r = static_cast<float>(x);
+  const double back = static_cast<double>(r);
+  uint32_t bits = __float_as_uint(r);
+  if (back != x) bits = (bits - (fabs(back) > fabs(x) ? 1u : 0u)) | 1u;
+  const _Float16 h = static_cast<_Float16>(__uint_as_float(bits));
+  return __builtin_bit_cast(uint16_t, h);
 }
 
 __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
@@ -150,6 +135,29 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return (lane_value_f64(v, 0) + lane_value_f64(v, 16)) + (lane_value_f64(v, 32) + lane_value_f64(v, 48));
 }
 
+// Value of lane `src` (wave-uniform) of v, broadcast to every lane.
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+// fp64 max / min over the whole wave (row butterflies, then the four rows)
+template <int SEL>  // 0: max, 1: min
+__device__ __forceinline__ double wave_ext_f64(double v) {
+  auto op = [](double a, double b) { return SEL == 0 ? fmax(a, b) : fmin(a, b); };
+  v = op(v, dpp_f64<kDppQuadXor1>(v));
+  v = op(v, dpp_f64<kDppQuadXor2>(v));
+  v = op(v, dpp_f64<kDppHalfMirror>(v));
+  v = op(v, dpp_f64<kDppMirror>(v));
+  return op(op(lane_value_f64(v, 0), lane_value_f64(v, 16)), op(lane_value_f64(v, 32), lane_value_f64(v, 48)));
+}
+__device__ __forceinline__ double wave_max_f64(double v) { return wave_ext_f64<0>(v); }
+__device__ __forceinline__ double wave_min_f64(double v) { return wave_ext_f64<1>(v); }
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
 __device__ __forceinline__ float wave_max_f32(float v) {
   v = row16_max(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -159,10 +167,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
-// Value of lane `src` (wave-uniform) of v, broadcast to every lane.
-__device__ __forceinline__ float lane_value(float v, int src) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
-}
 
 // 2^x with 2^(-inf) = 0.
 __device__ __forceinline__ float exp2_safe(float x) { return exp2f(x); }

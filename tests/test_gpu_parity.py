@@ -347,6 +347,60 @@ def test_demote_degenerate_rows():
         assert ks[0] == 0 and got[1][0] == 0
 
 
+def test_demote_rows_kernel_random_and_exact_ties():
+    """Fewer than 64 tokens go through the per-row kernel. Random rows under the workload's
+    rotations; then rows under R = I with clip 1 whose rotated values sit exactly on code
+    boundaries (they round half to even) or whose minimum is exactly 0, where the kernel's
+    error intervals cannot settle the decision and its compensated path decides: those
+    codes must equal the oracle's exactly."""
+    w = custom("rows", 4, 2, [64 + 320], cfg=2)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table = np.array([[0]], np.int32)
+    c = make_cache(w, rk_bits, rv_bits, table, 1, with_windows=False)
+    g = np.random.default_rng(8)
+    n = 40
+    rows_k = g.standard_normal((n, 2, 128)).astype(np.float32) * 3
+    rows_v = g.standard_normal((n, 2, 128)).astype(np.float32)
+    rows_k[5, :, 3] = 40.0  # an outlier channel
+    rows_k[7] *= 1e-6       # fp16 subnormal scale and zero point
+    rows_v[9] *= 2e-8       # scale near half the smallest fp16 subnormal
+    rows_k, rows_v = synth.to_bf16_values(rows_k), synth.to_bf16_values(rows_v)
+    j = np.arange(n)
+    say("demote rows kernel, random", n)
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, rows_k, rows_v)
+    torch.cuda.synchronize()
+    pool = c.pool.cpu().numpy().reshape(1, 2, opages.HEAD_BLOCK)
+    from oracle import quant as oquant
+    for kv in range(2):
+        kc, ks, kz, km = oquant.quantize_rows(rows_k[:, kv].astype(np.float64), rk[kv], w.clip_ratio)
+        vc, vs, vz, vm = oquant.quantize_rows(rows_v[:, kv].astype(np.float64), rv[kv], w.clip_ratio)
+        got = opages.unpack_history(pool, table[0], kv, n)
+        assert compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"rows head {kv}") == 0
+
+    eye_bits = np.zeros((2, 128, 128), np.uint16)
+    eye_bits[:, np.arange(128), np.arange(128)] = 0x3F80
+    one = np.ones(2, np.float32)
+    c.set_rotations(eye_bits, eye_bits, one, one)
+    ties_a = np.resize(np.array([0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0]), 128)       # min exactly 0, s = 1
+    ties_b = np.resize(np.array([-1.0, -0.5, 0.0, 0.5, 1.0, 1.5, 2.0]), 128)     # z = -1, s = 1
+    plain = np.resize(np.array([-1.0, -0.375, 0.25, 0.625, 2.0]), 128)           # no value near a boundary
+    rows = np.stack([ties_a, ties_b, plain, ties_b[::-1].copy()])[:, None, :].repeat(2, 1).astype(np.float32)
+    m = len(rows)
+    j = np.arange(n, n + m)
+    say("demote rows kernel, exact ties", m)
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, rows, rows[::-1].copy())
+    torch.cuda.synchronize()
+    pool = c.pool.cpu().numpy().reshape(1, 2, opages.HEAD_BLOCK)
+    for kv in range(2):
+        kc, ks, kz, km = oquant.quantize_rows(rows[:, kv].astype(np.float64), np.eye(128), 1.0)
+        vc, vs, vz, vm = oquant.quantize_rows(rows[::-1][:, kv].astype(np.float64), np.eye(128), 1.0)
+        got = opages.unpack_history(pool, table[0], kv, n + m)
+        got = tuple(a[n:] for a in got)
+        compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"ties head {kv}")
+        assert np.array_equal(got[0], kc) and np.array_equal(got[3], vc), "tie codes differ"
+        assert np.any(km == 0.0), "the rows must hold exact ties"
+
+
 # ------------------------------------------------------------------- full-size workloads
 
 FULL_SAMPLES = {2: [(0, 0), (0, 7)], 3: [(0, 3)], 4: [(0, 0), (63, 5)], 5: [(1, 2), (3, 7)]}
