@@ -48,6 +48,8 @@ __device__ __forceinline__ void window_split(
   const int h0 = kv * GQ;
   const int t0 = c * kPageTokens;
   const size_t base = ((static_cast<size_t>(b) * n_kv + kv) * window + t0) * kHeadDim;
+  // the window length first: the score mask needs it as soon as K and q have arrived
+  const int ntok = max(0, min(kPageTokens, min(win_len[b], window) - t0));
 
   // ---- every read, issued up front. Slots past the window length are read too (they lie
   // in the window buffer) and masked below.
@@ -76,7 +78,6 @@ __device__ __forceinline__ void window_split(
     vv[i] = t0 + t < window ? *reinterpret_cast<const uint32_t*>(v_win + base + static_cast<size_t>(t) * kHeadDim + 2 * dp)
                             : 0u;
   }
-  const int ntok = max(0, min(kPageTokens, min(win_len[b], window) - t0));
 
   // ---- scores: C[slot][head], lane holds head r of slots 16 wave + 4g + j
   wf32x4 acc = {0.f, 0.f, 0.f, 0.f};
