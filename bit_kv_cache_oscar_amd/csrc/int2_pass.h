@@ -241,7 +241,7 @@ constexpr int int2_smem_bytes() {
   constexpr int MT = (GQ + 3) / 4;
   constexpr int loop = NW * MT * 16 * kPRow + NW * MT * kFlushed * 64 * 4;
   constexpr int wacc = NW * GQ * kHeadDim * 4;
-  return 4 * MT * 4 * kQRow + (wacc > loop ? wacc : loop) + 2 * NW * GQ * 4;
+  return 4 * MT * 4 * kQRow + loop + wacc + 2 * NW * GQ * 4;
 }
 
 // Partial-result store: with kCoherent, an agent-scope store that is visible to every
@@ -268,15 +268,14 @@ __device__ __forceinline__ void int2_split(
   constexpr int kFBytes = NW * MT * kFlushed * 64 * 4;
   constexpr int kLoopBytes = kPBytes + kFBytes;
   constexpr int kWaccBytes = NW * GQ * kHeadDim * 4;
-  constexpr int kScratch = kWaccBytes > kLoopBytes ? kWaccBytes : kLoopBytes;
 
   // page loop: query limbs; P' limbs and flushed sums of each wave. Epilogue: wave partials
-  // over the P' and flushed-sum space.
+  // in a space of their own, so a wave writes its partial as soon as its pages are done.
   unsigned char* q_s = smem;
   unsigned char* scratch_s = smem + 4 * MT * 4 * kQRow;
-  float(*wm_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kScratch);
-  float(*wl_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kScratch + NW * GQ * 4);
-  float (*wacc_s)[GQ][kHeadDim] = reinterpret_cast<float (*)[GQ][kHeadDim]>(scratch_s);
+  float (*wacc_s)[GQ][kHeadDim] = reinterpret_cast<float (*)[GQ][kHeadDim]>(scratch_s + kLoopBytes);
+  float(*wm_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kLoopBytes + kWaccBytes);
+  float(*wl_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kLoopBytes + kWaccBytes + NW * GQ * 4);
 
   const int kv = gy / n_groups;
   const int tid = threadIdx.x;
@@ -565,7 +564,6 @@ __device__ __forceinline__ void int2_split(
     lf[mt] = fl[(mt * kFlushed + 8) * 64];
     zf[mt] = fl[(mt * kFlushed + 9) * 64];
   }
-  __syncthreads();  // every wave has read its flushed sums: the space becomes wacc_s
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int g = 4 * mt + G;
