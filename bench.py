@@ -5,9 +5,10 @@ MI355X, through oscar_decode_step (two launches: prepare, attend).
 Workload (default): a Qwen3-8B-shaped attention layer, batch 1, 32,768 tokens of context
 (64 BF16 sink / 32,448 INT2 history / 256 BF16 recent), 32 query heads over 8 KV heads,
 head_dim 128, 64-token pages, seeded synthetic N(0,1) data with per-head outlier channels.
-Steps cycle over `--layers` distinct layer instances (separate device buffers) so every
-step reads its KV pool from HBM, not from the 256 MB last-level cache, as a real model's
-per-layer decode does.
+Steps cycle over `--layers` distinct layer instances (separate pools, windows and
+rotations) so every step reads its KV pool from HBM, not from the 256 MB last-level cache,
+as a real model's per-layer decode does; like a model's layers, the instances share one
+block table and one set of history and window lengths.
 
 Prints one JSON line. `value` is the whole step's algorithmic HBM bytes divided by its
 time (GB/s); `roofline` reports the dominant kernel (the attend launch: INT2 history pass
@@ -281,9 +282,10 @@ def main():
     insts = [base]
     for _ in range(layers - 1):
         c = LayerCache(w.n_q_heads, w.n_kv_heads, w.batch, table.shape[1], n_phys, device=dev)
-        for name in ("pool", "block_table", "hist_len", "k_win", "v_win", "win_len", "rot_k", "rot_v", "clip_k",
-                     "clip_v"):
+        for name in ("pool", "k_win", "v_win", "rot_k", "rot_v", "clip_k", "clip_v"):
             getattr(c, name).copy_(getattr(base, name))
+        # one request's page table and lengths serve every layer of a model
+        c.block_table, c.hist_len, c.win_len = base.block_table, base.hist_len, base.win_len
         c.set_splits(splits)
         insts.append(c)
     torch.cuda.synchronize()
