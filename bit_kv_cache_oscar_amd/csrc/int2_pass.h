@@ -491,7 +491,11 @@ __device__ __forceinline__ void int2_split(
       thr = static_cast<float>(E + kTau);
       fresh = false;
     }
-    // probabilities (units of 2^E), pending sums, P' limbs
+    // probabilities (units of 2^E), pending sums, P' limbs. A tile whose P' are all zero
+    // (every weight p s^V 2^E below one unit) adds exactly nothing to the V sums: its limb
+    // rows then hold -128 c per code and the constant row c, which cancel in v_combo, so its
+    // limbs and matrix products are skipped (wave-uniform).
+    bool vskip[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       uint32_t P[4];
@@ -504,30 +508,39 @@ __device__ __forceinline__ void int2_split(
         // exponent's low bit is bit 23
         P[nt] = __float_as_uint(fmaf(pe, sv[nt], 16777216.f));
       }
-      // byte l of the four P' values into one dword per limb, in signed range
-      const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
-      const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
-      const uint32_t u01 = __builtin_amdgcn_perm(P[1], P[0], 0x0C0C0602u);
-      const uint32_t u23 = __builtin_amdgcn_perm(P[3], P[2], 0x0C0C0602u);
-      const uint32_t L0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
-      const uint32_t L1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
-      const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // bit 7 set by the exponent
-      unsigned char* row = pl + (mt * 16 + 4 * G) * kPRow + 4 * n;
-      *reinterpret_cast<uint32_t*>(row) = L0;
-      *reinterpret_cast<uint32_t*>(row + kPRow) = L1;
-      *reinterpret_cast<uint32_t*>(row + 2 * kPRow) = L2;
+      vskip[mt] = __all((P[0] | P[1] | P[2] | P[3]) == 0x4B800000u);  // 2^24: P' = 0
+      if (!vskip[mt]) {
+        // byte l of the four P' values into one dword per limb, in signed range
+        const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
+        const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+        const uint32_t u01 = __builtin_amdgcn_perm(P[1], P[0], 0x0C0C0602u);
+        const uint32_t u23 = __builtin_amdgcn_perm(P[3], P[2], 0x0C0C0602u);
+        const uint32_t L0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
+        const uint32_t L1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
+        const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // bit 7 set by the exponent
+        unsigned char* row = pl + (mt * 16 + 4 * G) * kPRow + 4 * n;
+        *reinterpret_cast<uint32_t*>(row) = L0;
+        *reinterpret_cast<uint32_t*>(row + kPRow) = L1;
+        *reinterpret_cast<uint32_t*>(row + 2 * kPRow) = L2;
+      }
     }
-    // the wave's LDS operations run in order: the reads below see the writes above
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    i8x16 aP[MT];
+    bool vall = true;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) aP[mt] = *reinterpret_cast<const i8x16*>(pl + (mt * 16 + n) * kPRow + 16 * G);
-    // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32
+    for (int mt = 0; mt < MT; ++mt) vall = vall && vskip[mt];
+    if (!vall) {
+      // the wave's LDS operations run in order: the reads below see the writes above
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      i8x16 aP[MT];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const i8x16 bv = unpack16_scaled(cur.vword(dt));
+      for (int mt = 0; mt < MT; ++mt) aP[mt] = *reinterpret_cast<const i8x16*>(pl + (mt * 16 + n) * kPRow + 16 * G);
+      // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) st.acci[mt][dt] = mfma16(aP[mt], bv, st.acci[mt][dt]);
+      for (int dt = 0; dt < 8; ++dt) {
+        const i8x16 bv = unpack16_scaled(cur.vword(dt));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          if (MT == 1 || !vskip[mt]) st.acci[mt][dt] = mfma16(aP[mt], bv, st.acci[mt][dt]);
+      }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
