@@ -51,6 +51,7 @@ struct BulkSmem {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ double bf16lo(uint32_t w) { return static_cast<double>(__uint_as_float(w << 16)); }
 __device__ __forceinline__ double bf16hi(uint32_t w) { return static_cast<double>(__uint_as_float(w & 0xFFFF0000u)); }
@@ -418,11 +419,9 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         const uint32_t w4[4] = {bx[tt][ks].x, bx[tt][ks].y, bx[tt][ks].z, bx[tt][ks].w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float lo = __uint_as_float(w4[k] << 16);
-          const float hi = __uint_as_float(w4[k] & 0xFFFF0000u);
-          nx = fmaf(lo, lo, fmaf(hi, hi, nx));
-        }
+        for (int k = 0; k < 4; ++k)
+          nx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[k]), __builtin_bit_cast(bf16x2, w4[k]), nx,
+                                               false);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -502,9 +501,10 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         uint32_t w = 0u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float q = rintf((acc[mt][tt][e] - zf) * inv_s);
-          q = fminf(fmaxf(q, 0.f), 3.f);
-          w |= static_cast<uint32_t>(q) << (8 * e);
+          // t + 1/2 clamped to [0, 3.5], truncated: the nearest level (a tie rounds up, and a
+          // tie of the fp32 value lies inside the tolerated band around the boundary)
+          const float t = __builtin_amdgcn_fmed3f(fmaf(acc[mt][tt][e] - zf, inv_s, 0.5f), 0.f, 3.5f);
+          w |= static_cast<uint32_t>(t) << (8 * e);
         }
         if (sf == 0.f) w = 0u;
         cw[mt] = w;
@@ -542,11 +542,13 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
           const int q = lane + 64 * r;
           const int tk = q >> 3;
           const int w = q & 7;
+          // page and slot of the word's token from lane tk, which loaded them (every lane
+          // of the wave takes part in the shuffles)
+          const int pg = __shfl(page, tk, 64);
+          const int sl = __shfl(slot, tk, 64);
           if (t0 + tk < n) {
             const uint4 b = *reinterpret_cast<const uint4*>(cs + tk * kHeadDim + 16 * w);
             const uint32_t word = b.x | (b.y << 2) | (b.z << 4) | (b.w << 6);
-            const int pg = dst_page[t0 + tk];
-            const int sl = dst_slot[t0 + tk];
             uint8_t* blk = pool + (static_cast<size_t>(pg) * n_kv + head) * kHeadBlock;
             *reinterpret_cast<uint32_t*>(blk + k_word_offset(sl, w)) = word;
           }
