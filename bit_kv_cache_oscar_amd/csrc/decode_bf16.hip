@@ -12,8 +12,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(
     const int32_t* __restrict__ win_len, int n_q, int n_kv, int window, int n_wsplits, double scale_log2,
     float* __restrict__ out_m, float* __restrict__ out_l, float* __restrict__ out_acc) {
   __shared__ __align__(16) unsigned char smem[window::window_smem_bytes<GQ>()];
-  window::window_split<GQ>(smem, blockIdx.x, blockIdx.y, blockIdx.z, q, k_win, v_win, win_len, n_q, n_kv, window,
-                           n_wsplits, scale_log2, out_m, out_l, out_acc);
+  window::window_split<GQ>(smem, blockIdx.x, blockIdx.y, blockIdx.y * GQ, blockIdx.z, q, k_win, v_win, win_len, n_q,
+                           n_kv, window, n_wsplits, scale_log2, out_m, out_l, out_acc);
 }
 
 template <int GQ>

@@ -78,6 +78,7 @@ struct StepArgs {
   const uint16_t* v_win;
   const int32_t* win_len;
   int batch, n_q, n_kv, gq, window, n_splits, n_wsplits, n_groups;
+  int win_groups;  // workgroups per (window split, KV head, request), each for gq / win_groups heads
   double scale_log2;
   PartialsView hist;  // INT2 partials and the query tail
   PartialsView win;   // window partials

@@ -7,7 +7,8 @@
 // an online-softmax merge.
 //
 // Launch 1 (prep), one 256-thread workgroup per item, the items being independent:
-//   demotion rows (token, KV head, K or V); BF16 window splits (split, KV head, request);
+//   demotion rows (token, KV head, K or V); BF16 window splits (split, KV head, request,
+//   and for a small pass a group of the KV head's query heads);
 //   query preparation per (request, query head), which also zeroes the request's
 //   per-KV-head arrival counters.
 // Launch 2 (main), grid (history split, KV head x head group, request): the INT2 pass of
@@ -38,13 +39,26 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
     return;
   }
   id -= a.n_dem_items;
-  const int n_win = a.n_wsplits * a.n_kv * a.batch;
+  const int n_win = a.n_wsplits * a.n_kv * a.batch * a.win_groups;
   if (id < n_win) {
-    const int c = id % a.n_wsplits;
-    const int kv = (id / a.n_wsplits) % a.n_kv;
-    const int b = id / (a.n_wsplits * a.n_kv);
-    window::window_split<GQW>(smem, c, kv, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q, a.n_kv, a.window,
-                              a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+    const int grp = id % a.win_groups;
+    const int rest = id / a.win_groups;
+    const int c = rest % a.n_wsplits;
+    const int kv = (rest / a.n_wsplits) % a.n_kv;
+    const int b = rest / (a.n_wsplits * a.n_kv);
+    // win_groups is 1, 2 or 4 and divides GQW (the launch chose it)
+    if (a.win_groups == 1) {
+      window::window_split<GQW>(smem, c, kv, kv * GQW, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q, a.n_kv, a.window,
+                                a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+    } else if (a.win_groups == 2) {
+      if constexpr (GQW % 2 == 0)
+        window::window_split<GQW / 2>(smem, c, kv, kv * GQW + grp * (GQW / 2), b, a.q, a.k_win, a.v_win, a.win_len,
+                                      a.n_q, a.n_kv, a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+    } else {
+      if constexpr (GQW % 4 == 0)
+        window::window_split<GQW / 4>(smem, c, kv, kv * GQW + grp * (GQW / 4), b, a.q, a.k_win, a.v_win, a.win_len,
+                                      a.n_q, a.n_kv, a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+    }
     return;
   }
   id -= n_win;
@@ -82,9 +96,17 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   merge::merge_group<GQT, NW>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, rb, a.out);
 }
 
+// A small window pass (fewer than 256 workgroups) spreads each KV head's query heads over up
+// to four workgroups: each then has a fraction of the value sums and stores, and the batch-1
+// window pass, the longest item of the launch, ends sooner. The K and V rows it reads again
+// come from L2.
 template <int GQT>
-hipError_t launch_prep(const StepArgs& a, hipStream_t stream) {
-  const unsigned n_prep = static_cast<unsigned>(a.n_dem_items + a.n_wsplits * a.n_kv * a.batch + a.n_q * a.batch);
+hipError_t launch_prep(StepArgs a, hipStream_t stream) {
+  const long long base = static_cast<long long>(a.n_wsplits) * a.n_kv * a.batch;
+  a.win_groups = 1;
+  while (a.win_groups < 4 && GQT % (2 * a.win_groups) == 0 && base * 2 * a.win_groups <= 256) a.win_groups *= 2;
+  const unsigned n_prep =
+      static_cast<unsigned>(a.n_dem_items + base * a.win_groups + static_cast<long long>(a.n_q) * a.batch);
   hipLaunchKernelGGL(prep_kernel<GQT>, dim3(n_prep), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

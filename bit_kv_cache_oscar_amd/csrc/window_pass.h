@@ -31,10 +31,11 @@ constexpr int window_smem_bytes() {
 }
 
 // One workgroup (256 threads) of the BF16 window pass: slots 64 c .. 64 c + 63 of KV head kv
-// of request b for the KV head's GQ query heads (GQ <= 16). `smem` holds window_smem_bytes<GQ>().
+// of request b for its query heads h0 .. h0 + GQ - 1 (GQ <= 16; the KV head's heads, or a
+// group of them when several workgroups share a KV head). `smem` holds window_smem_bytes<GQ>().
 template <int GQ>
 __device__ __forceinline__ void window_split(
-    unsigned char* __restrict__ smem, int c, int kv, int b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_win, const uint16_t* __restrict__ v_win,
+    unsigned char* __restrict__ smem, int c, int kv, int h0, int b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_win, const uint16_t* __restrict__ v_win,
     const int32_t* __restrict__ win_len, int n_q, int n_kv, int window, int n_wsplits, double scale_log2,
     float* __restrict__ out_m, float* __restrict__ out_l, float* __restrict__ out_acc) {
   static_assert(GQ >= 1 && GQ <= 16, "one 16-column score tile holds the KV head's query heads");
@@ -45,7 +46,6 @@ __device__ __forceinline__ void window_split(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h0 = kv * GQ;
   const int t0 = c * kPageTokens;
   const size_t base = ((static_cast<size_t>(b) * n_kv + kv) * window + t0) * kHeadDim;
   // the window length first: the score mask needs it as soon as K and q have arrived
