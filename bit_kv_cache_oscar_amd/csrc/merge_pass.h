@@ -12,7 +12,7 @@
 // maximum M: weights w = 2^(m - M), L = sum w l, and
 //   out = ((sum_INT2 w acc) R_V^T + sum_window w acc) / L.
 // Heads go in passes of up to eight. The R_V fragments of the un-rotation are loaded
-// before the ticket (load_rv). Every global load of a pass is issued before any of its
+// with the partials (load_rv). Every global load of a pass is issued before any of its
 // arithmetic, so a pass whose splits fit one batch costs one memory round trip:
 //   - the (m, l) of the first 64 partials of each head of the wave, first, since the
 //     weights need only these,
@@ -117,8 +117,8 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
 }
 
 // B fragments of the un-rotation for wave `wave`'s dim tiles NTW wave + nt: column n =
-// dim 16 tile + n, rows k = 32 ks + 8 (lane / 16) .. + 7, i.e. R_V[dim][k]. Loaded by
-// every workgroup before its ticket, so the merging one has them in registers.
+// dim 16 tile + n, rows k = 32 ks + 8 (lane / 16) .. + 7, i.e. R_V[dim][k]. Loaded by the
+// merging workgroup just before the partials, so both arrive in one round trip.
 template <int NW>
 __device__ __forceinline__ void load_rv(const uint16_t* __restrict__ rot_v, int kv, uint4 (&rb)[8 / NW][4]) {
   constexpr int NTW = 8 / NW;

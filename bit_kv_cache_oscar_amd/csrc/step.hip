@@ -79,9 +79,6 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
                                  a.hist.m, a.hist.l, a.hist.acc);
   const int kv = blockIdx.y / a.n_groups;
   const int b = blockIdx.z;
-  // R_V fragments of the merge, requested while the partial stores drain
-  uint4 rb[8 / NW][4];
-  merge::load_rv<NW>(a.rot_v, kv, rb);
   // the partials went out as agent-scope stores: once each thread's stores have completed
   // and the barrier has passed, the ticket below is drawn after all of them
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -93,6 +90,10 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // last arrival for (b, kv): every workgroup of the group has drawn its ticket, so re-arm the
   // counter for the next launch; the group's partials are read with agent-scope loads
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // R_V fragments of the un-rotation: requested first, they travel with the partials' loads
+  // (one round trip), and only the merging workgroup reads R_V
+  uint4 rb[8 / NW][4];
+  merge::load_rv<NW>(a.rot_v, kv, rb);
   merge::merge_group<GQT, NW>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, rb, a.out);
 }
 
