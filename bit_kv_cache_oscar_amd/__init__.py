@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     oscar_attend,
     oscar_check_desc,
     oscar_decode,
+    oscar_decode_multi,
     oscar_decode_bf16,
     oscar_decode_int2,
     oscar_decode_step,

@@ -70,6 +70,9 @@ _SIGNATURES = {
     "oscar_decode": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
                                c_void_p, c_void_p]),
+    "oscar_decode_multi": (c_int32, [POINTER(LayerDesc), c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32,
+                                     c_void_p, c_size_t, c_void_p, c_void_p]),
     "oscar_prepare": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                 c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
@@ -259,12 +262,13 @@ def oscar_merge(desc: LayerDesc, partials, n_splits: int, win_partials, rot_v, o
 
 
 def _check_decode_args(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
-                       n_splits: int, workspace, out):
+                       n_splits: int, workspace, out, n_tok: int = 1):
     import torch
 
     batch = int(q.shape[0])
     _device16(q, "q")
-    _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
+    shape = "[batch, n_q_heads, 128]" if n_tok == 1 else "[batch, T, n_q_heads, 128]"
+    _need(q.numel() == batch * n_tok * desc.n_q_heads * HEAD_DIM, f"q must be {shape}")
     for t, name in ((rot_k, "rot_k"), (rot_v, "rot_v")):
         _device16(t, name)
         _need(t.numel() == desc.n_kv_heads * HEAD_DIM * HEAD_DIM, f"{name} must be [n_kv_heads, 128, 128]")
@@ -279,7 +283,7 @@ def _check_decode_args(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist
     _device_i32(win_len, "win_len", batch)
     _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
     _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous(), "out must be contiguous float32")
-    _need(out.numel() == batch * desc.n_q_heads * HEAD_DIM, "out must be [batch, n_q_heads, 128]")
+    _need(out.numel() == batch * n_tok * desc.n_q_heads * HEAD_DIM, f"out must be {shape}")
     return batch, workspace.numel() * workspace.element_size()
 
 
@@ -293,6 +297,21 @@ def oscar_decode(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, 
                               int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win), _ptr(win_len),
                               batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out),
                               _stream(stream)))
+
+
+def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
+                       sm_scale: float, n_splits: int, workspace, out, stream=None):
+    """Decode attention for T query tokens per request (q [B, T, Hq, 128] bf16, out the same
+    shape in float32; token t sees the window up to its own position) in two launches;
+    workspace from oscar_decode_workspace_bytes(desc, B * T, n_splits)."""
+    _need(q.dim() == 4 and q.shape[2] == desc.n_q_heads and q.shape[3] == HEAD_DIM, "q must be [batch, T, n_q_heads, 128]")
+    n_tok = int(q.shape[1])
+    batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
+                                       n_splits, workspace, out, n_tok)
+    _check(lib().oscar_decode_multi(byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v), _ptr(pool),
+                                    _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win),
+                                    _ptr(v_win), _ptr(win_len), batch, float(sm_scale), int(n_splits),
+                                    _ptr(workspace), nbytes, _ptr(out), _stream(stream)))
 
 
 def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool,

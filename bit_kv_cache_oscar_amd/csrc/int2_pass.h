@@ -145,7 +145,8 @@ constexpr int kQprepSmem = 4 * kHeadDim * 8 + kHeadDim * 8 + 64;
 
 __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ rot_k, int n_q, int gq, double scale_log2,
-                                           char* __restrict__ qlimb, QueryScal* __restrict__ qscal, int h, int b) {
+                                           char* __restrict__ qlimb, QueryScal* __restrict__ qscal, int h, int b,
+                                           int nqt = 1) {
   double(*part_s)[kHeadDim] = reinterpret_cast<double(*)[kHeadDim]>(smem);
   double* qd_s = reinterpret_cast<double*>(smem + 4 * kHeadDim * 8);
   float* amax_s = reinterpret_cast<float*>(smem + 5 * kHeadDim * 8);
@@ -162,7 +163,7 @@ __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* 
   uint32_t rr[32];
 #pragma unroll
   for (int u = 0; u < 32; ++u) rr[u] = rcol[u * (kHeadDim / 2)];
-  if (t < kHeadDim) qd_s[t] = static_cast<double>(bf16_to_f32(q[head * kHeadDim + t]));
+  if (t < kHeadDim) qd_s[t] = static_cast<double>(bf16_to_f32(q[query_row(b, h, n_q, gq, nqt) * kHeadDim + t]));
   __syncthreads();
   double a0 = 0.0, a1 = 0.0;
 #pragma unroll

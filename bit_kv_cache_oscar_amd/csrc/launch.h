@@ -14,6 +14,22 @@ struct LayerShape {
   int window;    // BF16 window slots per request and KV head
 };
 
+// Memory row of virtual query head hv of request b. With nqt query tokens per request (a
+// multi-query decode), KV head kv has nqt * gq virtual heads, (token t, head g) in
+// token-major order, while q and out hold [batch][nqt][n_q][128] with n_q = n_qv / nqt;
+// with one token the two numberings coincide.
+__host__ __device__ inline size_t query_row(int b, int hv, int n_qv, int gqv, int nqt) {
+  if (nqt == 1) return static_cast<size_t>(b) * n_qv + hv;
+  const int gq = gqv / nqt;
+  const int kv = hv / gqv;
+  const int r = hv - kv * gqv;
+  const int t = r / gq;
+  return (static_cast<size_t>(b) * nqt + t) * (n_qv / nqt) + static_cast<size_t>(kv) * gq + (r - t * gq);
+}
+
+// Query token of virtual head hv (0 for a single-token decode).
+__host__ __device__ inline int query_token(int hv, int gqv, int nqt) { return (hv % gqv) / (gqv / nqt); }
+
 // Per (request, query head) scalars of the rotated query, written by the INT2 pass's
 // query preparation: the score scale 2^-sh sm_scale log2(e), sm_scale log2(e) sum(q_rot)
 // and the centring term -2 sum(Q) of the fixed-point query Q.
@@ -79,6 +95,7 @@ struct StepArgs {
   const int32_t* win_len;
   int batch, n_q, n_kv, gq, window, n_splits, n_wsplits, n_groups;
   int win_groups;  // workgroups per (window split, KV head, request), each for gq / win_groups heads
+  int nqt;         // query tokens per request; n_q and gq count virtual heads (token, head)
   double scale_log2;
   PartialsView hist;  // INT2 partials and the query tail
   PartialsView win;   // window partials

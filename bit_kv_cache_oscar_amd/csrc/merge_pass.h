@@ -140,7 +140,7 @@ __device__ __forceinline__ void load_rv(const uint16_t* __restrict__ rot_v, int 
 template <int GQT, int NW>
 __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, int b, int kv, int n_q,
                                             const PartialsView& hist, int ns, const PartialsView& win, int nw,
-                                            const uint4 (&rb)[8 / NW][4], float* __restrict__ out) {
+                                            const uint4 (&rb)[8 / NW][4], float* __restrict__ out, int nqt = 1) {
   constexpr int HP = Shape<GQT, NW>::HP;
   constexpr int SL = Shape<GQT, NW>::SL;
   constexpr int HW = Shape<GQT, NW>::HW;
@@ -318,7 +318,9 @@ __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, in
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int g = 4 * (lane >> 4) + j;
-        if (g < HP) out[(row0 + g) * kHeadDim + d] = (c[j] + accw_s[g * SL * kRow + d]) * inv_s[g];
+        if (g < HP)
+          out[query_row(b, kv * GQT + p0 + g, n_q, GQT, nqt) * kHeadDim + d] =
+              (c[j] + accw_s[g * SL * kRow + d]) * inv_s[g];
       }
     }
     if (p0 + HP < GQT) __syncthreads();  // the next pass reuses the LDS

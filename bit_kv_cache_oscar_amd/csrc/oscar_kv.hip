@@ -236,9 +236,10 @@ size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
 
 namespace {
 
-// Checks shared by the two halves of the decode step; fills the workspace views.
+// Checks shared by the two halves of the decode step; fills the workspace views. With nqt
+// query tokens per request the heads are virtual (token, head) pairs: nqt n_q of them.
 int32_t check_step_common(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits, void* workspace,
-                          size_t workspace_bytes, oscar::StepArgs& a) {
+                          size_t workspace_bytes, oscar::StepArgs& a, int nqt = 1) {
   int32_t st = check_desc_impl(desc);
   if (st != OSCAR_OK) return st;
   if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
@@ -247,23 +248,25 @@ int32_t check_step_common(const oscar_layer_desc* desc, int32_t batch, int32_t n
   if (n_splits > 256) return fail(OSCAR_ERR_UNSUPPORTED, "n_splits %d > 256 (the two-launch decode)", n_splits);
   if (!workspace) return fail(OSCAR_ERR_INVALID_ARG, "null workspace");
   const int ws = window_splits_of(desc);
-  const size_t need = oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits, ws);
+  const int n_qv = desc->n_q_heads * nqt;
+  const size_t need = oscar::step_workspace_bytes(batch, n_qv, desc->n_kv_heads, n_splits, ws);
   if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   const oscar::LayerShape L = shape_of(desc);
   char* base = static_cast<char*>(workspace);
-  const size_t hist_bytes = (oscar::partials_bytes(batch, desc->n_q_heads, n_splits) + 255) / 256 * 256;
-  const size_t win_bytes = (oscar::partials_bytes(batch, desc->n_q_heads, ws) + 255) / 256 * 256;
+  const size_t hist_bytes = (oscar::partials_bytes(batch, n_qv, n_splits) + 255) / 256 * 256;
+  const size_t win_bytes = (oscar::partials_bytes(batch, n_qv, ws) + 255) / 256 * 256;
   a = oscar::StepArgs{};
   a.batch = batch;
-  a.n_q = L.n_q;
+  a.n_q = n_qv;
   a.n_kv = L.n_kv;
-  a.gq = L.gq;
+  a.gq = L.gq * nqt;
+  a.nqt = nqt;
   a.window = L.window;
   a.n_splits = n_splits;
   a.n_wsplits = ws;
   a.n_groups = 1;
-  a.hist = oscar::partials_view(base, batch, desc->n_q_heads, n_splits);
-  a.win = oscar::partials_view(base + hist_bytes, batch, desc->n_q_heads, ws);
+  a.hist = oscar::partials_view(base, batch, n_qv, n_splits);
+  a.win = oscar::partials_view(base + hist_bytes, batch, n_qv, ws);
   a.counters = reinterpret_cast<int*>(base + hist_bytes + win_bytes);
   return OSCAR_OK;
 }
@@ -349,6 +352,45 @@ int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* ro
   return oscar_decode_step(desc, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, q, rot_k, rot_v,
                            const_cast<void*>(pool), block_table, max_pages, hist_len, k_win, v_win, win_len, batch,
                            sm_scale, n_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
+                           const void* rot_v, const void* pool, const int32_t* block_table, int32_t max_pages,
+                           const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,
+                           int32_t batch, float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                           float* out, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (n_tokens <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_tokens %d <= 0", n_tokens);
+  const int gq = desc->n_q_heads / desc->n_kv_heads;
+  if ((n_tokens & (n_tokens - 1)) != 0 || static_cast<long long>(gq) * n_tokens > 16)
+    return fail(OSCAR_ERR_UNSUPPORTED, "n_tokens %d: a power of two with n_tokens x %d query heads per KV head <= 16",
+                n_tokens, gq);
+  if (static_cast<long long>(batch) * n_tokens > 65535)
+    return fail(OSCAR_ERR_UNSUPPORTED, "batch x n_tokens %lld > 65535", static_cast<long long>(batch) * n_tokens);
+  oscar::StepArgs a;
+  st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a, n_tokens);
+  if (st != OSCAR_OK) return st;
+  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (!q || !rot_k || !rot_v || !pool || !block_table || !hist_len || !k_win || !v_win || !win_len || !out)
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  a.q = static_cast<const uint16_t*>(q);
+  a.rot_k = static_cast<const uint16_t*>(rot_k);
+  a.rot_v = static_cast<const uint16_t*>(rot_v);
+  a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));  // only read: nothing is demoted
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.hist_len = hist_len;
+  a.k_win = static_cast<const uint16_t*>(k_win);
+  a.v_win = static_cast<const uint16_t*>(v_win);
+  a.win_len = win_len;
+  a.scale_log2 = static_cast<double>(sm_scale) * 1.4426950408889634;
+  a.out = out;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(oscar::launch_prepare(a, s), "prepare launch");
+  if (st != OSCAR_OK) return st;
+  return hip_status(oscar::launch_attend(a, s), "attend launch");
 }
 
 int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t n_splits, const void* win_partials,

@@ -49,15 +49,17 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
     // win_groups is 1, 2 or 4 and divides GQW (the launch chose it)
     if (a.win_groups == 1) {
       window::window_split<GQW>(smem, c, kv, kv * GQW, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q, a.n_kv, a.window,
-                                a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+                                a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc, GQW, a.nqt);
     } else if (a.win_groups == 2) {
       if constexpr (GQW % 2 == 0)
         window::window_split<GQW / 2>(smem, c, kv, kv * GQW + grp * (GQW / 2), b, a.q, a.k_win, a.v_win, a.win_len,
-                                      a.n_q, a.n_kv, a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+                                      a.n_q, a.n_kv, a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc,
+                                      GQW, a.nqt);
     } else {
       if constexpr (GQW % 4 == 0)
         window::window_split<GQW / 4>(smem, c, kv, kv * GQW + grp * (GQW / 4), b, a.q, a.k_win, a.v_win, a.win_len,
-                                      a.n_q, a.n_kv, a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc);
+                                      a.n_q, a.n_kv, a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc,
+                                      GQW, a.nqt);
     }
     return;
   }
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
   const int h = id % a.n_q;
   const int b = id / a.n_q;
   if (threadIdx.x == 0 && h % a.gq == 0) a.counters[b * a.n_kv + h / a.gq] = 0;
-  int2::qprep_head(smem, a.q, a.rot_k, a.n_q, a.gq, a.scale_log2, a.hist.qlimb, a.hist.qscal, h, b);
+  int2::qprep_head(smem, a.q, a.rot_k, a.n_q, a.gq, a.scale_log2, a.hist.qlimb, a.hist.qscal, h, b, a.nqt);
 }
 
 // GQ query heads per workgroup, GQT per KV head (GQT = GQ n_groups), NW waves
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // (one round trip), and only the merging workgroup reads R_V
   uint4 rb[8 / NW][4];
   merge::load_rv<NW>(a.rot_v, kv, rb);
-  merge::merge_group<GQT, NW>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, rb, a.out);
+  merge::merge_group<GQT, NW>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, rb, a.out, a.nqt);
 }
 
 // A small window pass (fewer than 256 workgroups) spreads each KV head's query heads over up

@@ -37,7 +37,7 @@ template <int GQ>
 __device__ __forceinline__ void window_split(
     unsigned char* __restrict__ smem, int c, int kv, int h0, int b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_win, const uint16_t* __restrict__ v_win,
     const int32_t* __restrict__ win_len, int n_q, int n_kv, int window, int n_wsplits, double scale_log2,
-    float* __restrict__ out_m, float* __restrict__ out_l, float* __restrict__ out_acc) {
+    float* __restrict__ out_m, float* __restrict__ out_l, float* __restrict__ out_acc, int gqv = GQ, int nqt = 1) {
   static_assert(GQ >= 1 && GQ <= 16, "one 16-column score tile holds the KV head's query heads");
   float(*mx_s)[16] = reinterpret_cast<float(*)[16]>(smem);
   float(*l_s)[16] = reinterpret_cast<float(*)[16]>(smem + 4 * 64);
@@ -49,7 +49,8 @@ __device__ __forceinline__ void window_split(
   const int t0 = c * kPageTokens;
   const size_t base = ((static_cast<size_t>(b) * n_kv + kv) * window + t0) * kHeadDim;
   // the window length first: the score mask needs it as soon as K and q have arrived
-  const int ntok = max(0, min(kPageTokens, min(win_len[b], window) - t0));
+  const int wl = min(win_len[b], window);
+  const int ntok = max(0, min(kPageTokens, wl - t0));
 
   // ---- every read, issued up front. Slots past the window length are read too (they lie
   // in the window buffer) and masked below.
@@ -58,6 +59,10 @@ __device__ __forceinline__ void window_split(
   const int r = lane & 15;
   const int g = lane >> 4;
   const int kslot = 16 * wave + r;
+  // slots of this split that head r sees: query token t of a multi-query decode sees the
+  // window up to its own position, nqt - 1 - t slots short of the window length
+  const int ntok_r =
+      r < GQ ? max(0, min(kPageTokens, wl - (nqt - 1 - query_token(h0 + r, gqv, nqt)) - t0)) : 0;
   uint4 ka[4], qb[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -66,7 +71,7 @@ __device__ __forceinline__ void window_split(
                 : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    qb[s] = r < GQ ? *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(b) * n_q + h0 + r) * kHeadDim + 32 * s + 8 * g)
+    qb[s] = r < GQ ? *reinterpret_cast<const uint4*>(q + query_row(b, h0 + r, n_q, gqv, nqt) * kHeadDim + 32 * s + 8 * g)
                    : make_uint4(0, 0, 0, 0);
   // value operands: thread (dim pair dp, slot group sg)
   const int dp = tid & 63;
@@ -90,7 +95,7 @@ __device__ __forceinline__ void window_split(
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const bool valid = 16 * wave + 4 * g + j < ntok;
+    const bool valid = 16 * wave + 4 * g + j < ntok_r;
     sc[j] = valid ? acc[j] * sl2 : -INFINITY;
     mx = fmaxf(mx, sc[j]);
   }
@@ -104,7 +109,7 @@ __device__ __forceinline__ void window_split(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int slot = 16 * wave + 4 * g + j;
-    const float pt = slot < ntok ? exp2f(sc[j] - big) : 0.f;
+    const float pt = slot < ntok_r ? exp2f(sc[j] - big) : 0.f;
     if (r < GQ) p_s[r][slot] = pt;
     ls += pt;
   }
@@ -143,7 +148,7 @@ __device__ __forceinline__ void window_split(
     const size_t o = (static_cast<size_t>(b) * n_q + h0 + h) * n_wsplits + c;
     out_acc[o * kHeadDim + d] = (acc_s[0][h][d] + acc_s[1][h][d]) + (acc_s[2][h][d] + acc_s[3][h][d]);
     if (d == 0) {
-      out_m[o] = ntok > 0 ? fmaxf(fmaxf(mx_s[0][h], mx_s[1][h]), fmaxf(mx_s[2][h], mx_s[3][h])) : -INFINITY;
+      out_m[o] = fmaxf(fmaxf(mx_s[0][h], mx_s[1][h]), fmaxf(mx_s[2][h], mx_s[3][h]));  // -inf: no slot
       out_l[o] = (l_s[0][h] + l_s[1][h]) + (l_s[2][h] + l_s[3][h]);
     }
   }

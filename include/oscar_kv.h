@@ -244,6 +244,31 @@ int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* ro
                      int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * oscar_decode_multi: decode attention for n_tokens consecutive query tokens per request
+ * over one pool, in two launches, without demotion (speculative verification or a
+ * chunked prefill reading the compressed prefix).
+ * (QbitAI article on OSCAR, serving-path section: paged KV and radix prefix cache reuse,
+ * with separate BF16 and INT2 passes joined by an online-softmax merge; several query
+ * tokens over one compressed prefix is this library's reading of that reuse.)
+ *
+ * Query token t (0 <= t < n_tokens) of request b is the token at window position
+ * win_len[b] - n_tokens + t: it attends to the whole INT2 history and to window slots
+ * [0, win_len[b] - (n_tokens - 1 - t)) (causal among the query tokens, whose K and V are
+ * the last n_tokens window slots). With n_tokens == 1 this is oscar_decode.
+ *   q          bf16 [batch][n_tokens][n_q_heads][128]
+ *   out        float32 [batch][n_tokens][n_q_heads][128]
+ *   n_tokens   a power of two with n_tokens * (n_q_heads / n_kv_heads) <= 16 (else
+ *              OSCAR_ERR_UNSUPPORTED); batch * n_tokens <= 65535
+ *   workspace  at least oscar_decode_workspace_bytes(desc, batch * n_tokens, n_splits) bytes
+ * The other arguments are those of oscar_decode.
+ */
+int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
+                           const void* rot_v, const void* pool, const int32_t* block_table, int32_t max_pages,
+                           const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,
+                           int32_t batch, float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                           float* out, void* stream);
+
+/*
  * oscar_prepare: the first launch of oscar_decode_step on its own: the n demotions, the
  * BF16 window pass and the query rotation, written into the workspace (and the pool).
  * Arguments as in oscar_decode_step. A later oscar_attend with the same desc, batch,

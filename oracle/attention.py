@@ -96,6 +96,24 @@ def decode(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float) -> np.ndarray:
     return out
 
 
+def decode_multi(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float) -> np.ndarray:
+    """Outputs [T, Hq, 128] of one request's T consecutive query tokens (q [T, Hq, 128]).
+
+    Reading (the pages name prefix-cache reuse; several query tokens over one compressed
+    prefix, as in speculative verification or chunked prefill, is this library's reading):
+    the T query tokens are the last T window tokens, so token t sits at window position
+    n_w - T + t and attends to the whole history and to window slots [0, n_w - (T - 1 - t)),
+    causal among the query tokens. T = 1 is decode()."""
+    q = np.asarray(q, np.float64)
+    n_tok, n_w = q.shape[0], np.asarray(win_k).shape[1]
+    outs = []
+    for t in range(n_tok):
+        keep = max(0, n_w - (n_tok - 1 - t))
+        outs.append(decode(q[t], rot_k, rot_v, np.asarray(win_k)[:, :keep], np.asarray(win_v)[:, :keep], hists,
+                           sm_scale))
+    return np.stack(outs)
+
+
 def history_partials(q, rot_k, hist, sm_scale: float, bounds):
     """INT2-segment partials of one query head over history ranges [a, b) (rotated
     basis, natural-log units)."""

@@ -223,6 +223,25 @@ def query(w: Workload, b: int) -> np.ndarray:
     return to_bf16_values(q)
 
 
+def query_tokens(w: Workload, b: int, n_tok: int) -> np.ndarray:
+    """bf16-valued float32 queries [n_tok, Hq, 128] of request b's last n_tok positions (a
+    multi-query step); the last one is query(w, b), the others come from their own streams
+    with the same per-head outlier channels."""
+    out = np.empty((n_tok, w.n_q_heads, HEAD_DIM), np.float32)
+    for t in range(n_tok):
+        if t == n_tok - 1:
+            out[t] = query(w, b)
+            continue
+        g = rng(w.seed, w.cfg, _S_Q, b, n_tok, t)
+        q = g.standard_normal((w.n_q_heads, HEAD_DIM), dtype=np.float32)
+        for kv in range(w.n_kv_heads):
+            kq_ch, _, qf, _, _ = outliers(w, kv)
+            for i in range(w.gq):
+                q[kv * w.gq + i, kq_ch] *= qf[i]
+        out[t] = to_bf16_values(q)
+    return out
+
+
 def window_rows(w: Workload, b: int, kv: int):
     """K and V [win_len, 128] of the BF16 window of request b: the sink then the recent
     tokens, in position order."""

@@ -169,3 +169,30 @@ def test_python_binding_validates_shapes_before_the_library():
     cpu = torch.zeros(4, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         L.oscar_demote(d, cpu, cpu, cpu, cpu, cpu, cpu, cpu, cpu, cpu)
+
+
+def test_decode_multi_argument_checks(lib):
+    desc = L.layer_desc(32, 8)  # 4 query heads per KV head: up to 4 query tokens
+    d = ctypes.byref(desc)
+    f = lib.oscar_decode_multi
+    need = L.oscar_decode_workspace_bytes(desc, 2 * 4, 4)
+    #       q, n_tokens, rot_k, rot_v, pool, table, max_pages, hist_len, k_win, v_win, win_len, batch,
+    #       sm_scale, n_splits, workspace, bytes, out, stream
+    args = [FAKE, 4, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4, FAKE, need, FAKE, None]
+
+    def call(over):
+        a = list(args)
+        for k, v in over.items():
+            a[k] = v
+        return f(d, *a)
+
+    assert call({15: need - 1}) == L.OSCAR_ERR_WORKSPACE
+    assert call({1: 3}) == L.OSCAR_ERR_UNSUPPORTED       # not a power of two
+    assert call({1: 8}) == L.OSCAR_ERR_UNSUPPORTED       # 8 x 4 virtual heads > 16
+    assert call({1: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({0: None}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({10: None}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({6: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({12: 0.0}) == L.OSCAR_ERR_INVALID_ARG
+    # one token needs the one-token workspace
+    assert call({1: 1, 15: L.oscar_decode_workspace_bytes(desc, 2, 4) - 1}) == L.OSCAR_ERR_WORKSPACE

@@ -116,6 +116,54 @@ def test_decode_on_oracle_pages(case):
                 assert_close(got[b], refs[b], f"{case} b{b} splits {s} fused call {rep}")
 
 
+MULTI_CASES = {
+    "c2-4k-T2": ("c2-4k", 2),
+    "c2-4k-T4": ("c2-4k", 4),
+    "gq2-T8": ("gq2", 8),
+    "edges-T2": ("edges", 2),
+    "c5-gq8-T2": ("c5-gq8", 2),
+}
+
+
+@pytest.mark.parametrize("name", list(MULTI_CASES))
+def test_decode_multi_on_oracle_pages(name):
+    """T query tokens per request over one pool: token t sees the whole history and the window
+    up to its own position. The virtual (token, head) rows fill the fused kernels' head tiles
+    (T x query heads per KV head up to 16, two head groups at 16)."""
+    from bit_kv_cache_oscar_amd import oscar_decode_multi, oscar_decode_workspace_bytes, oscar_default_splits
+
+    case, n_tok = MULTI_CASES[name]
+    w = DECODE_CASES[case]()
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    pool, table, hists = oracle_pool(w, rk, rv)
+    c = make_cache(w, rk_bits, rv_bits, table, pool.shape[0])
+    c.pool.copy_(torch.from_numpy(pool.reshape(-1)))
+    qn = np.stack([synth.query_tokens(w, b, n_tok) for b in range(w.batch)])
+    q = bf16(qn)
+    refs = []
+    for b in range(w.batch):
+        wk, wv = windows(w, b)
+        refs.append(oatt.decode_multi(qn[b].astype(np.float64), rk, rv, wk, wv, hists[b], w.sm_scale))
+    splits = {oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())), 3}
+    for s in sorted(splits):
+        ws = torch.zeros(oscar_decode_workspace_bytes(c.desc, w.batch * n_tok, s), dtype=torch.uint8, device="cuda")
+        out = torch.empty((w.batch, n_tok, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
+        for rep in range(2):  # twice: the arrival counters must re-arm
+            say(name, "multi-query decode", "B", w.batch, "T", n_tok, "Hq", w.n_q_heads, "splits", s, "call", rep)
+            out.fill_(np.nan)
+            oscar_decode_multi(c.desc, q, c.rot_k, c.rot_v, c.pool, c.block_table, c.hist_len, c.k_win, c.v_win,
+                               c.win_len, w.sm_scale, s, ws, out)
+            got = out.cpu().numpy()
+            for b in range(w.batch):
+                for t in range(n_tok):
+                    assert_close(got[b, t], refs[b][t], f"{name} b{b} t{t} splits {s} call {rep}")
+    # the last token of each request is a one-token decode of the same pool
+    c.set_splits(max(splits))
+    single = c.decode_fused(q[:, -1].contiguous(), w.sm_scale).cpu().numpy()
+    for b in range(w.batch):
+        assert_close(single[b], refs[b][-1], f"{name} b{b} one-token decode")
+
+
 def _split_bounds(nh, s_total):
     n_pages = -(-nh // 64)
     pps = -(-n_pages // s_total) if s_total else 0

@@ -135,3 +135,41 @@ def test_gqa_heads_use_their_own_kv_head():
         kv = h // 2
         ref = brute_force(q[h].tolist(), win_k[kv].tolist(), win_v[kv].tolist(), 0.5)
         assert np.abs(out[h] - ref).max() <= 1e-12
+
+
+def test_multi_query_tokens_see_the_window_up_to_their_own_position():
+    # brute force with an explicit causal cut of the window: token t of T sees window slots
+    # [0, n_w - (T - 1 - t)) and the whole (un-rotated, dequantised) history
+    _, r, win_k, win_v, hist = _tiny_case(seed=5, n_hist=7, n_win=6)
+    g = np.random.default_rng(6)
+    n_tok = 4
+    q = g.standard_normal((n_tok, 2, 128))
+    rk = np.stack([r])
+    out = att.decode_multi(q, rk, rk, win_k, win_v, [hist], 0.3)
+    assert out.shape == (n_tok, 2, 128)
+    khat = quant.dequantize(hist[0], hist[1], hist[2]) @ r.T
+    vhat = quant.dequantize(hist[3], hist[4], hist[5]) @ r.T
+    for t in range(n_tok):
+        keep = 6 - (n_tok - 1 - t)
+        keys = np.concatenate([win_k[0][:keep], khat]).tolist()
+        vals = np.concatenate([win_v[0][:keep], vhat]).tolist()
+        for h in range(2):
+            ref = brute_force(q[t, h].tolist(), keys, vals, 0.3)
+            assert np.abs(out[t, h] - ref).max() <= 1e-10
+
+
+def test_multi_query_special_cases():
+    q1, r, win_k, win_v, hist = _tiny_case(seed=7, n_hist=5, n_win=2)
+    rk = np.stack([r])
+    # one token is the single-query decode
+    assert np.array_equal(att.decode_multi(q1[None], rk, rk, win_k, win_v, [hist], 0.3)[0],
+                          att.decode(q1, rk, rk, win_k, win_v, [hist], 0.3))
+    g = np.random.default_rng(8)
+    q = g.standard_normal((4, 2, 128))
+    out = att.decode_multi(q, rk, rk, win_k, win_v, [hist], 0.3)
+    # the last token sees the whole window
+    assert np.array_equal(out[3], att.decode(q[3], rk, rk, win_k, win_v, [hist], 0.3))
+    # with more query tokens than window slots the first ones see the history alone
+    empty = np.zeros((1, 0, 128))
+    for t in (0, 1):
+        assert np.array_equal(out[t], att.decode(q[t], rk, rk, empty, empty, [hist], 0.3))
