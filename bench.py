@@ -13,8 +13,9 @@ block table and one set of history and window lengths.
 Prints one JSON line. `value` is the whole step's algorithmic HBM bytes divided by its
 time (GB/s); `roofline` reports the dominant kernel (the attend launch: INT2 history pass
 and merge) against the 8 TB/s HBM peak, timed with events on its stream over back-to-back
-oscar_attend launches; `cpu_baseline` is the CPU oracle timed on a bounded sample of the
-same workload.
+oscar_attend launches; `multi_query` times oscar_decode_multi (T query tokens per request
+over the same pools, as in speculative verification) the same way; `cpu_baseline` is the
+CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -227,7 +228,8 @@ def main():
     import torch
 
     import synth
-    from bit_kv_cache_oscar_amd import oscar_attend, oscar_default_splits
+    from bit_kv_cache_oscar_amd import (oscar_attend, oscar_decode_multi, oscar_decode_workspace_bytes,
+                                        oscar_default_splits)
     from bit_kv_cache_oscar_amd.layer import LayerCache
     from bit_kv_cache_oscar_amd.rotation import layer_rotations_from_calibration, layer_rotations_from_gram
 
@@ -328,6 +330,41 @@ def main():
     ms = timed(step, args.steps)
     attend_ms = timed(attend, args.steps)
 
+    # timed region 3, the multi-query row: T query tokens per request over the same pools
+    # (speculative verification reading the compressed prefix), oscar_decode_multi back to
+    # back over the layer instances; T query heads' worth of rows per KV head, up to 16
+    n_tok = min(4, 16 // w.gq)
+    multi = None
+    if n_tok >= 2:
+        qm = torch.from_numpy(np.stack([synth.query_tokens(w, b, n_tok) for b in range(w.batch)])).to(dev)
+        qm = qm.to(torch.bfloat16)
+        wsm = torch.zeros(oscar_decode_workspace_bytes(base.desc, w.batch * n_tok, splits), dtype=torch.uint8,
+                          device=dev)
+        outm = torch.empty((w.batch, n_tok, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+
+        def decode_multi(c):
+            oscar_decode_multi(c.desc, qm, c.rot_k, c.rot_v, c.pool, c.block_table, c.hist_len, c.k_win, c.v_win,
+                               c.win_len, w.sm_scale, splits, wsm, outm, stream)
+
+        for i in range(max(2, args.warmup)):
+            decode_multi(insts[i % layers])
+        multi_ms = timed(decode_multi, args.steps)
+        hist = int(sum(w.hist_lens)) * w.n_kv_heads * HIST_BYTES
+        win = int(sum(w.win_lens)) * w.n_kv_heads * WIN_BYTES
+        mbytes = hist + win + 2 * w.n_kv_heads * ROT_BYTES + w.batch * n_tok * w.n_q_heads * 128 * (2 + 4)
+        multi = {
+            "entry": "oscar_decode_multi (prepare + attend, no demotion)",
+            "query_tokens": n_tok,
+            "us_per_call": round(multi_ms * 1e3, 3),
+            "bound": "hbm",
+            "achieved": round(mbytes / (multi_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(mbytes / (multi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_call": mbytes,
+            "query_tokens_per_s": round(w.batch * n_tok / (multi_ms * 1e-3), 1),
+        }
+
     out = {
         "metric": METRIC,
         "value": round(total_bytes / (ms * 1e-3) / 1e9, 2),
@@ -371,6 +408,8 @@ def main():
             "bytes_per_launch": attend_bytes,
         },
     }
+    if multi is not None:
+        out["multi_query"] = multi
     if args.config == 5:
         # the bulk-demotion row of this workload (after the decode timing: it allocates)
         out["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5))
