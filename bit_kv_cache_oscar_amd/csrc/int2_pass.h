@@ -139,80 +139,81 @@ __device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* page, uint
 // The rotated query of one (request, query head) h of request b: q_rot = q R_K in fp64
 // (bf16 products are exact), as Q = rint(q_rot 2^sh) with max|q_rot| 2^sh < 2^21, in three
 // signed 8-bit limbs (limb row 3 zero); the centring term -2 sum_d Q_d; the score scale
-// 2^-sh sm_scale log2(e) and sm_scale log2(e) sum_d q_rot_d. All 256 threads of the
-// workgroup take part: wave w sums rows 32 w .. +31 at columns 2 lane, 2 lane + 1.
-constexpr int kQprepSmem = 4 * kHeadDim * 8 + kHeadDim * 8 + 64;
+// 2^-sh sm_scale log2(e) and sm_scale log2(e) sum_d q_rot_d. Every read (the query row, the
+// rotation's column pairs) is issued first; wave w sums rows 32 w .. +31 at columns
+// 2 lane, 2 lane + 1, waves 1..3 hand their sums to wave 0 through LDS (one barrier), and
+// wave 0 does the rest alone.
+constexpr int kQprepSmem = 3 * 64 * 2 * 8;
 
 __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ rot_k, int n_q, int gq, double scale_log2,
                                            char* __restrict__ qlimb, QueryScal* __restrict__ qscal, int h, int b,
                                            int nqt = 1) {
-  double(*part_s)[kHeadDim] = reinterpret_cast<double(*)[kHeadDim]>(smem);
-  double* qd_s = reinterpret_cast<double*>(smem + 4 * kHeadDim * 8);
-  float* amax_s = reinterpret_cast<float*>(smem + 5 * kHeadDim * 8);
-  double* sum_s = reinterpret_cast<double*>(smem + 5 * kHeadDim * 8 + 16);
-  int* lsum_s = reinterpret_cast<int*>(smem + 5 * kHeadDim * 8 + 32);
+  double(*part_s)[64][2] = reinterpret_cast<double(*)[64][2]>(smem);
   const int kv = h / gq;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const size_t head = static_cast<size_t>(b) * n_q + h;
 
+  // ---- reads: this wave's 32 query values (the same for every lane) and rotation rows
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + query_row(b, h, n_q, gq, nqt) * kHeadDim + 32 * w);
+  uint32_t qq[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) qq[u] = qw[u];
   const uint32_t* rcol = reinterpret_cast<const uint32_t*>(rot_k + static_cast<size_t>(kv) * kHeadDim * kHeadDim +
                                                            static_cast<size_t>(32 * w) * kHeadDim) + lane;
   uint32_t rr[32];
 #pragma unroll
   for (int u = 0; u < 32; ++u) rr[u] = rcol[u * (kHeadDim / 2)];
-  if (t < kHeadDim) qd_s[t] = static_cast<double>(bf16_to_f32(q[query_row(b, h, n_q, gq, nqt) * kHeadDim + t]));
-  __syncthreads();
   double a0 = 0.0, a1 = 0.0;
 #pragma unroll
   for (int u = 0; u < 32; ++u) {
-    const double qv = qd_s[32 * w + u];
+    const double qv = static_cast<double>(__uint_as_float((u & 1) ? (qq[u >> 1] & 0xFFFF0000u) : (qq[u >> 1] << 16)));
     a0 = fma(qv, static_cast<double>(__uint_as_float(rr[u] << 16)), a0);
     a1 = fma(qv, static_cast<double>(__uint_as_float(rr[u] & 0xFFFF0000u)), a1);
   }
-  part_s[w][2 * lane] = a0;
-  part_s[w][2 * lane + 1] = a1;
-  __syncthreads();
-  // threads 0..127 own q_rot[t]; waves 2 and 3 only join the barriers
-  const int tt = t & (kHeadDim - 1);
-  const double x = (part_s[0][tt] + part_s[1][tt]) + (part_s[2][tt] + part_s[3][tt]);
-  const float am = wave_max_f32(static_cast<float>(fabs(x)));
-  const double sm = wave_sum_f64(x);
-  if (lane == 0 && w < 2) {
-    amax_s[w] = am;
-    sum_s[w] = sm;
+  if (w > 0) {
+    part_s[w - 1][lane][0] = a0;
+    part_s[w - 1][lane][1] = a1;
   }
   __syncthreads();
+  if (w > 0) return;  // uniform per wave; no barrier follows
+
+  // ---- wave 0: q_rot at dims 2 lane, 2 lane + 1
+  const double x0 = ((a0 + part_s[0][lane][0]) + part_s[1][lane][0]) + part_s[2][lane][0];
+  const double x1 = ((a1 + part_s[0][lane][1]) + part_s[1][lane][1]) + part_s[2][lane][1];
   // amax rounded to float can only move up to the next power of two: the bound holds
-  const float amax = fmaxf(amax_s[0], amax_s[1]);
+  const float amax = wave_max_f32(static_cast<float>(fmax(fabs(x0), fabs(x1))));
+  const double sm = wave_sum_f64(x0 + x1);
   int k = 0;
   if (amax > 0.f) frexpf(amax, &k);  // amax < 2^k
   const int sh = 21 - k;
-  const int Q = static_cast<int>(rint(x * pow2d(sh)));
-  const int l0 = static_cast<signed char>(Q & 0xFF);
-  const int r1 = (Q - l0) >> 8;
-  const int l1 = static_cast<signed char>(r1 & 0xFF);
-  const int l2 = (r1 - l1) >> 8;  // |l2| <= 33
-  if (t < kHeadDim) {
-    char* dst = qlimb + head * 512;
-    dst[t] = static_cast<char>(l0);
-    dst[kHeadDim + t] = static_cast<char>(l1);
-    dst[2 * kHeadDim + t] = static_cast<char>(l2);
-    dst[3 * kHeadDim + t] = 0;
-  }
+  const int Q0 = static_cast<int>(rint(x0 * pow2d(sh)));
+  const int Q1 = static_cast<int>(rint(x1 * pow2d(sh)));
+  // signed 8-bit limbs: Q = l0 + 2^8 l1 + 2^16 l2, |l2| <= 33
+  auto limbs = [](int Q, int& l0, int& l1, int& l2) {
+    l0 = static_cast<signed char>(Q & 0xFF);
+    const int r1 = (Q - l0) >> 8;
+    l1 = static_cast<signed char>(r1 & 0xFF);
+    l2 = (r1 - l1) >> 8;
+  };
+  int a[3], c[3];
+  limbs(Q0, a[0], a[1], a[2]);
+  limbs(Q1, c[0], c[1], c[2]);
+  uint16_t* dst = reinterpret_cast<uint16_t*>(qlimb + head * 512) + lane;
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    dst[r * (kHeadDim / 2)] = static_cast<uint16_t>((a[r] & 0xFF) | ((c[r] & 0xFF) << 8));
+  dst[3 * (kHeadDim / 2)] = 0;
   // exact integer sum of Q over the 128 dims: the centring term -2 sum Q
-  int sq = Q;
+  int sq = Q0 + Q1;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
-  if (lane == 0 && w < 2) lsum_s[w] = sq;
-  __syncthreads();
-  if (t == 0) {
+  if (lane == 0) {
     QueryScal o;
     o.qsc = static_cast<float>(pow2d(-sh) * scale_log2);
-    o.sig = static_cast<float>((sum_s[0] + sum_s[1]) * scale_log2);
-    o.kcent = -2 * (lsum_s[0] + lsum_s[1]);
+    o.sig = static_cast<float>(sm * scale_log2);
+    o.kcent = -2 * sq;
     o.pad[0] = o.pad[1] = o.pad[2] = o.pad[3] = o.pad[4] = 0;
     qscal[head] = o;
   }
