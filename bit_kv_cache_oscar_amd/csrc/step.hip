@@ -41,8 +41,12 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
   id -= a.n_dem_items;
   const int n_win = a.n_wsplits * a.n_kv * a.batch * a.win_groups;
   if (id < n_win) {
-    const int grp = id % a.win_groups;
-    const int rest = id / a.win_groups;
+    // the head group varies slowest: the groups of one split are n_win / win_groups apart,
+    // a multiple of 8 for the workloads that split (5 splits x 8 KV heads), so they run on
+    // one XCD and the K and V rows the first reads come from that XCD's L2 for the others
+    const int base = n_win / a.win_groups;
+    const int grp = id / base;
+    const int rest = id - grp * base;
     const int c = rest % a.n_wsplits;
     const int kv = (rest / a.n_wsplits) % a.n_kv;
     const int b = rest / (a.n_wsplits * a.n_kv);
