@@ -89,18 +89,6 @@ __device__ __forceinline__ double coop_dot(const uint16_t* xrow, const uint16_t*
   return s + c;
 }
 
-// sum_i x_i R_ij in fp64 from the exact products, by the whole wave as a plain tree (lane L
-// takes i = 2L, 2L+1): seven rounded additions, so |error| <= 7 2^-53 sum_i |x_i R_ij|
-__device__ __forceinline__ double tree_dot(const uint16_t* xrow, const uint16_t* rtrow, int lane) {
-#pragma clang fp contract(off)
-  const uint32_t xv = *reinterpret_cast<const uint32_t*>(xrow + 2 * lane);
-  const uint32_t rv = *reinterpret_cast<const uint32_t*>(rtrow + 2 * lane);
-  double s = bf16lo(xv) * bf16lo(rv) + bf16hi(xv) * bf16hi(rv);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
-  return s;
-}
-
 // a 64-bit value through a DPP row operation (both halves with the same control)
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {

@@ -153,11 +153,6 @@ __device__ __forceinline__ double wave_ext_f64(double v) {
 __device__ __forceinline__ double wave_max_f64(double v) { return wave_ext_f64<0>(v); }
 __device__ __forceinline__ double wave_min_f64(double v) { return wave_ext_f64<1>(v); }
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-  v = row16_sum(v);
-  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
-}
-
 __device__ __forceinline__ float wave_max_f32(float v) {
   v = row16_max(v);
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
@@ -165,24 +160,6 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
   return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-
-
-// 2^x with 2^(-inf) = 0.
-__device__ __forceinline__ float exp2_safe(float x) { return exp2f(x); }
-
-}  // namespace oscar
-
-namespace oscar {
-
-// Copies one 128x128 bf16 matrix (32 KiB, 16-byte aligned) from global memory into LDS
-// with 16-byte loads spread over `nthreads` threads. The caller synchronises.
-__device__ __forceinline__ void stage_rotation(uint16_t* __restrict__ dst, const uint16_t* __restrict__ src,
-                                               int tid, int nthreads) {
-  const uint4* s = reinterpret_cast<const uint4*>(src);
-  uint4* d = reinterpret_cast<uint4*>(dst);
-#pragma unroll 4
-  for (int i = tid; i < kHeadDim * kHeadDim / 8; i += nthreads) d[i] = s[i];
 }
 
 }  // namespace oscar
