@@ -56,6 +56,20 @@ oscar::LayerShape shape_of(const oscar_layer_desc* d) {
   return s;
 }
 
+// The INT2 pass keeps each wave's pending value sums in int32 between the (data-driven)
+// moves of its reference maximum; a page adds at most 255 x 48 x 64 to one of them, so a
+// wave may walk at most 2048 pages, and with four waves per workgroup a split at most
+// 8192 (a request's pages are bounded by its block-table row).
+constexpr long long kMaxSplitPages = 8192;
+
+int32_t check_pages(int32_t max_pages, int32_t n_splits) {
+  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (n_splits > 0 && (static_cast<long long>(max_pages) + n_splits - 1) / n_splits > kMaxSplitPages)
+    return fail(OSCAR_ERR_UNSUPPORTED, "max_pages %d over %d splits: more than %lld pages per split", max_pages,
+                n_splits, kMaxSplitPages);
+  return OSCAR_OK;
+}
+
 constexpr int kBulkMinRows = 64;  // oscar_demote takes the matrix-core kernel from this many tokens
 
 int window_splits_of(const oscar_layer_desc* d) { return (d->sink_tokens + d->recent_tokens + 63) / 64; }
@@ -160,6 +174,9 @@ int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_
     by_pages = (pages + 3) / 4;
   }
   if (s > by_pages) s = by_pages;
+  // no split may hold more pages than the INT2 pass accepts
+  const long long need = (pages + kMaxSplitPages - 1) / kMaxSplitPages;
+  if (s < need) s = need;
   if (s < 1) s = 1;
   if (s > 65535) s = 65535;
   return static_cast<int32_t>(s);
@@ -195,7 +212,7 @@ int32_t oscar_decode_int2(const oscar_layer_desc* desc, const void* q, const voi
   if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
   if (n_splits <= 0 || n_splits > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d out of [1, 65535]", n_splits);
-  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (int32_t e = check_pages(max_pages, n_splits)) return e;
   if (!q || !rot_k || !pool || !block_table || !hist_len || !partials)
     return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
@@ -314,7 +331,7 @@ int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void
   oscar::StepArgs a;
   int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
   if (st != OSCAR_OK) return st;
-  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (int32_t e = check_pages(max_pages, n_splits)) return e;
   if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
   a.rot_v = static_cast<const uint16_t*>(rot_v);
   a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));  // only read by the attend launch
@@ -335,7 +352,7 @@ int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const
   oscar::StepArgs a;
   int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
   if (st != OSCAR_OK) return st;
-  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (int32_t e = check_pages(max_pages, n_splits)) return e;
   if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
   st = oscar_prepare(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win, v_win,
                      win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, stream);
@@ -371,7 +388,7 @@ int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t 
   oscar::StepArgs a;
   st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a, n_tokens);
   if (st != OSCAR_OK) return st;
-  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (int32_t e = check_pages(max_pages, n_splits)) return e;
   if (!q || !rot_k || !rot_v || !pool || !block_table || !hist_len || !k_win || !v_win || !win_len || !out)
     return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");

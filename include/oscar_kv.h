@@ -154,8 +154,12 @@ int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void
  *   rot_k        bf16 [n_kv_heads][128][128]
  *   pool         INT2 pool
  *   block_table  int32 [batch][max_pages]
- *   hist_len     int32 [batch], history entries per request (0 allowed)
+ *   hist_len     int32 [batch], history entries per request (0 allowed, at most
+ *                64 max_pages)
  *   sm_scale     softmax scale applied to q . k (e.g. 1/sqrt(128) as a float)
+ *   n_splits     1..65535, with at most 8192 pages per split: ceil(max_pages / n_splits)
+ *                <= 8192, else OSCAR_ERR_UNSUPPORTED (the pass keeps int32 value sums
+ *                per wave; oscar_default_splits respects the bound)
  *   partials     workspace of at least oscar_partials_bytes(desc, batch, n_splits) bytes
  */
 int32_t oscar_decode_int2(const oscar_layer_desc* desc, const void* q, const void* rot_k,
@@ -219,7 +223,8 @@ size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
  *              memory, owned by the caller; its contents need no initialisation and are
  *              overwritten (INT2 and window partials, query data, arrival counters)
  *   out        float32 [batch][n_q_heads][128]
- *   n_splits   1..256 (OSCAR_ERR_UNSUPPORTED above)
+ *   n_splits   1..256 (OSCAR_ERR_UNSUPPORTED above), and ceil(max_pages / n_splits) <= 8192
+ *              as for oscar_decode_int2
  * Demotions land before the history is read: a token demoted by this call is part of the
  * history it attends over (hist_len must count it). n == 0 demotes nothing (then k_src,
  * v_src, dst_page, dst_slot, clip_k and clip_v may be null). Calls that share a

@@ -91,6 +91,18 @@ def test_decode_int2_argument_checks(lib):
     need = L.oscar_partials_bytes(L.layer_desc(32, 8), 1, 4)
     assert call(d, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, need - 1, None) == L.OSCAR_ERR_WORKSPACE
     assert "workspace" in L.oscar_last_error()
+    # at most 8192 pages per split: the pass's int32 value sums are bounded for that many
+    assert call(d, FAKE, FAKE, FAKE, FAKE, 8193, FAKE, 1, 0.08, 1, FAKE, big, None) == L.OSCAR_ERR_UNSUPPORTED
+    assert "pages per split" in L.oscar_last_error()
+
+
+def test_default_splits_respect_the_pages_per_split_bound():
+    d = L.layer_desc(32, 8)
+    for batch in (1, 4, 64):
+        for tokens in (2 ** 20, 2 ** 26, 2 ** 31 - 1):
+            s = L.oscar_default_splits(d, batch, tokens)
+            pages = -(-tokens // 64)
+            assert 1 <= s <= 65535 and -(-pages // s) <= 8192, (batch, tokens, s)
 
 
 def test_decode_bf16_and_merge_argument_checks(lib):
@@ -147,6 +159,7 @@ def test_decode_step_argument_checks(lib):
     assert call({17: 0}) == L.OSCAR_ERR_INVALID_ARG
     assert call({19: 0}) == L.OSCAR_ERR_INVALID_ARG
     assert call({12: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({12: 4 * 8192 + 1}) == L.OSCAR_ERR_UNSUPPORTED   # more than 8192 pages per split
     assert call({18: float("nan")}) == L.OSCAR_ERR_INVALID_ARG
     assert call({22: None}) == L.OSCAR_ERR_INVALID_ARG
     assert call({9: None}) == L.OSCAR_ERR_INVALID_ARG
