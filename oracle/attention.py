@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import codebook as _codebook
 from .quant import dequantize
 
 
@@ -62,18 +63,21 @@ def finalize(part) -> np.ndarray:
     return acc / l if l > 0.0 else np.zeros_like(acc)
 
 
-def head_inputs(hist):
+def head_inputs(hist, codebook=None):
     """Dequantised (khat, vhat) of one head's history tuple
-    (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16)."""
+    (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16); with codebook = (K levels, V levels)
+    in sixteenths, through those levels instead of the uniform ones."""
     kc, ks, kz, vc, vs, vz = hist
+    if codebook is not None:
+        return _codebook.dequantize(kc, ks, kz, codebook[0]), _codebook.dequantize(vc, vs, vz, codebook[1])
     return dequantize(kc, ks, kz), dequantize(vc, vs, vz)
 
 
-def decode_head(q, rot_k, rot_v, win_k, win_v, hist, sm_scale: float) -> np.ndarray:
+def decode_head(q, rot_k, rot_v, win_k, win_v, hist, sm_scale: float, codebook=None) -> np.ndarray:
     """Output of one query head: one softmax over window and history tokens together."""
     q = np.asarray(q, np.float64)
     q_rot = q @ rot_k
-    khat, vhat = head_inputs(hist)
+    khat, vhat = head_inputs(hist, codebook)
     s = np.concatenate([sm_scale * (np.asarray(win_k, np.float64) @ q), sm_scale * (khat @ q_rot)])
     if s.size == 0:
         return np.zeros(q.shape[0])
@@ -83,16 +87,18 @@ def decode_head(q, rot_k, rot_v, win_k, win_v, hist, sm_scale: float) -> np.ndar
     return out / p.sum()
 
 
-def decode(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float) -> np.ndarray:
+def decode(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float, codebooks=None) -> np.ndarray:
     """Outputs [Hq, 128] of one request.
     q [Hq,128]; rot_k, rot_v [Hkv,128,128]; win_k, win_v [Hkv, n_w, 128];
-    hists[kv] = history tuple of KV head kv."""
+    hists[kv] = history tuple of KV head kv; codebooks[kv] = (K levels, V levels) in
+    sixteenths for the codebook variant (None: the uniform levels)."""
     hq, hkv = q.shape[0], rot_k.shape[0]
     gq = hq // hkv
     out = np.zeros((hq, q.shape[1]))
     for h in range(hq):
         kv = h // gq
-        out[h] = decode_head(q[h], rot_k[kv], rot_v[kv], win_k[kv], win_v[kv], hists[kv], sm_scale)
+        out[h] = decode_head(q[h], rot_k[kv], rot_v[kv], win_k[kv], win_v[kv], hists[kv], sm_scale,
+                             None if codebooks is None else codebooks[kv])
     return out
 
 
