@@ -18,20 +18,25 @@ from ._lib import (  # noqa: F401
     layer_desc,
     lib,
     oscar_attend,
+    oscar_attend_codebook,
     oscar_check_desc,
     oscar_decode,
+    oscar_decode_codebook,
     oscar_decode_multi,
     oscar_decode_bf16,
     oscar_decode_int2,
     oscar_decode_step,
+    oscar_decode_step_codebook,
     oscar_decode_workspace_bytes,
     oscar_default_splits,
     oscar_demote,
+    oscar_demote_codebook,
     oscar_last_error,
     oscar_merge,
     oscar_page_bytes,
     oscar_partials_bytes,
     oscar_prepare,
+    oscar_prepare_codebook,
     oscar_status_string,
     oscar_version,
     oscar_window_splits,

@@ -78,6 +78,23 @@ _SIGNATURES = {
                                 c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     "oscar_attend": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
                                c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    # Lloyd-Max codebook variants: the entry point without the suffix with `codebook`
+    # inserted before the pool
+    "oscar_demote_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "oscar_decode_step_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                             c_float, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "oscar_decode_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                        c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "oscar_prepare_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
+                                         c_void_p]),
+    "oscar_attend_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                        c_void_p, c_int32, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
 }
 
 
@@ -139,6 +156,15 @@ def _device_i32(t, name, numel=None):
         _need(t.numel() >= numel, f"{name} holds {t.numel()} < {numel} entries")
 
 
+def _check_codebook(desc: LayerDesc, codebook):
+    """The Lloyd-Max variant's levels: uint8 [n_kv_heads, 2, 4] on the device (K, V)."""
+    import torch
+
+    _need(codebook.is_cuda and codebook.dtype == torch.uint8 and codebook.is_contiguous(),
+          "codebook must be a contiguous uint8 device tensor")
+    _need(codebook.numel() == desc.n_kv_heads * 8, "codebook must be [n_kv_heads, 2, 4]")
+
+
 # ---------------------------------------------------------------------------------- helpers
 
 
@@ -186,8 +212,9 @@ def oscar_decode_workspace_bytes(desc: LayerDesc, batch: int, n_splits: int) -> 
 
 
 def oscar_demote(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v, pool,
-                 stream=None):
-    """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16) into (dst_page[i], dst_slot[i])."""
+                 stream=None, codebook=None):
+    """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16) into (dst_page[i], dst_slot[i]).
+    With `codebook` (uint8 [Hkv, 2, 4]) this is oscar_demote_codebook."""
     n = int(k_src.shape[0]) if k_src.dim() else 0
     hkv = desc.n_kv_heads
     _device16(k_src, "k_src")
@@ -203,9 +230,21 @@ def oscar_demote(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v
         _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
               f"{name} must be float32 [n_kv_heads] on the device")
     _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
-    _check(lib().oscar_demote(byref(desc), _ptr(k_src), _ptr(v_src), n, _ptr(dst_page), _ptr(dst_slot),
-                              _ptr(rot_k), _ptr(rot_v), _ptr(clip_k), _ptr(clip_v), _ptr(pool),
-                              _stream(stream)))
+    if codebook is None:
+        _check(lib().oscar_demote(byref(desc), _ptr(k_src), _ptr(v_src), n, _ptr(dst_page), _ptr(dst_slot),
+                                  _ptr(rot_k), _ptr(rot_v), _ptr(clip_k), _ptr(clip_v), _ptr(pool),
+                                  _stream(stream)))
+    else:
+        _check_codebook(desc, codebook)
+        _check(lib().oscar_demote_codebook(byref(desc), _ptr(k_src), _ptr(v_src), n, _ptr(dst_page),
+                                           _ptr(dst_slot), _ptr(rot_k), _ptr(rot_v), _ptr(clip_k), _ptr(clip_v),
+                                           _ptr(codebook), _ptr(pool), _stream(stream)))
+
+
+def oscar_demote_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v, codebook,
+                          pool, stream=None):
+    """oscar_demote against the Lloyd-Max codebook (uint8 [Hkv, 2, 4], sixteenths of the scale)."""
+    oscar_demote(desc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v, pool, stream, codebook)
 
 
 def oscar_decode_int2(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm_scale: float, n_splits: int,
@@ -288,15 +327,26 @@ def _check_decode_args(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist
 
 
 def oscar_decode(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
-                 sm_scale: float, n_splits: int, workspace, out, stream=None):
+                 sm_scale: float, n_splits: int, workspace, out, stream=None, codebook=None):
     """Decode attention over the three segments in two launches; workspace from
-    oscar_decode_workspace_bytes(desc, B, n_splits); out [B, Hq, 128] float32."""
+    oscar_decode_workspace_bytes(desc, B, n_splits); out [B, Hq, 128] float32. With
+    `codebook` this is oscar_decode_codebook."""
     batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
                                        n_splits, workspace, out)
-    _check(lib().oscar_decode(byref(desc), _ptr(q), _ptr(rot_k), _ptr(rot_v), _ptr(pool), _ptr(block_table),
-                              int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win), _ptr(win_len),
-                              batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out),
-                              _stream(stream)))
+    rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win),
+            _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
+    if codebook is None:
+        _check(lib().oscar_decode(byref(desc), _ptr(q), _ptr(rot_k), _ptr(rot_v), *rest))
+    else:
+        _check_codebook(desc, codebook)
+        _check(lib().oscar_decode_codebook(byref(desc), _ptr(q), _ptr(rot_k), _ptr(rot_v), _ptr(codebook), *rest))
+
+
+def oscar_decode_codebook(desc: LayerDesc, q, rot_k, rot_v, codebook, pool, block_table, hist_len, k_win, v_win,
+                          win_len, sm_scale: float, n_splits: int, workspace, out, stream=None):
+    """oscar_decode over a pool written with the Lloyd-Max codebook (uint8 [Hkv, 2, 4])."""
+    oscar_decode(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len, sm_scale, n_splits,
+                 workspace, out, stream, codebook)
 
 
 def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
@@ -316,8 +366,9 @@ def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist
 
 def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool,
                       block_table, hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace, out,
-                      stream=None):
-    """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16, n may be 0) and decode, in two launches."""
+                      stream=None, codebook=None):
+    """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16, n may be 0) and decode, in two launches.
+    With `codebook` this is oscar_decode_step_codebook."""
     batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
                                        n_splits, workspace, out)
     n = int(k_src.shape[0]) if k_src is not None and k_src.dim() else 0
@@ -332,16 +383,30 @@ def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k,
         for t, name in ((clip_k, "clip_k"), (clip_v, "clip_v")):
             _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
                   f"{name} must be float32 [n_kv_heads] on the device")
-    _check(lib().oscar_decode_step(byref(desc), _ptr(k_src) if n else None, _ptr(v_src) if n else None, n,
-                                   _ptr(dst_page) if n else None, _ptr(dst_slot) if n else None,
-                                   _ptr(clip_k) if n else None, _ptr(clip_v) if n else None, _ptr(q), _ptr(rot_k),
-                                   _ptr(rot_v), _ptr(pool), _ptr(block_table), int(block_table.shape[1]),
-                                   _ptr(hist_len), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch, float(sm_scale),
-                                   int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream)))
+    head = (_ptr(k_src) if n else None, _ptr(v_src) if n else None, n, _ptr(dst_page) if n else None,
+            _ptr(dst_slot) if n else None, _ptr(clip_k) if n else None, _ptr(clip_v) if n else None, _ptr(q),
+            _ptr(rot_k), _ptr(rot_v))
+    rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win),
+            _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
+    if codebook is None:
+        _check(lib().oscar_decode_step(byref(desc), *head, *rest))
+    else:
+        _check_codebook(desc, codebook)
+        _check(lib().oscar_decode_step_codebook(byref(desc), *head, _ptr(codebook), *rest))
 
 
-def oscar_attend(desc: LayerDesc, rot_v, pool, block_table, hist_len, n_splits: int, workspace, out, stream=None):
-    """The second launch of oscar_decode_step alone (INT2 pass + merge into out)."""
+def oscar_decode_step_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v,
+                               codebook, pool, block_table, hist_len, k_win, v_win, win_len, sm_scale: float,
+                               n_splits: int, workspace, out, stream=None):
+    """oscar_decode_step with the Lloyd-Max codebook (uint8 [Hkv, 2, 4]) for demotion and decode."""
+    oscar_decode_step(desc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, block_table,
+                      hist_len, k_win, v_win, win_len, sm_scale, n_splits, workspace, out, stream, codebook)
+
+
+def oscar_attend(desc: LayerDesc, rot_v, pool, block_table, hist_len, n_splits: int, workspace, out, stream=None,
+                 codebook=None):
+    """The second launch of oscar_decode_step alone (INT2 pass + merge into out). With
+    `codebook` this is oscar_attend_codebook."""
     import torch
 
     batch = int(out.shape[0])
@@ -354,14 +419,25 @@ def oscar_attend(desc: LayerDesc, rot_v, pool, block_table, hist_len, n_splits: 
     _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
     _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous(), "out must be contiguous float32")
     _need(out.numel() == batch * desc.n_q_heads * HEAD_DIM, "out must be [batch, n_q_heads, 128]")
-    _check(lib().oscar_attend(byref(desc), _ptr(rot_v), _ptr(pool), _ptr(block_table), int(block_table.shape[1]),
-                              _ptr(hist_len), batch, int(n_splits), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+    rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), batch, int(n_splits),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
+    if codebook is None:
+        _check(lib().oscar_attend(byref(desc), _ptr(rot_v), *rest))
+    else:
+        _check_codebook(desc, codebook)
+        _check(lib().oscar_attend_codebook(byref(desc), _ptr(rot_v), _ptr(codebook), *rest))
+
+
+def oscar_attend_codebook(desc: LayerDesc, rot_v, codebook, pool, block_table, hist_len, n_splits: int, workspace,
+                          out, stream=None):
+    """oscar_attend for a workspace that oscar_prepare_codebook prepared with the same codebook."""
+    oscar_attend(desc, rot_v, pool, block_table, hist_len, n_splits, workspace, out, stream, codebook)
 
 
 def oscar_prepare(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win,
-                  v_win, win_len, sm_scale: float, n_splits: int, workspace, stream=None):
-    """The first launch of oscar_decode_step alone (demotion, window pass, query rotation)."""
+                  v_win, win_len, sm_scale: float, n_splits: int, workspace, stream=None, codebook=None):
+    """The first launch of oscar_decode_step alone (demotion, window pass, query rotation).
+    With `codebook` this is oscar_prepare_codebook."""
     batch = int(q.shape[0])
     _device16(q, "q")
     _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
@@ -387,9 +463,21 @@ def oscar_prepare(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, cli
             _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
                   f"{name} must be float32 [n_kv_heads] on the device")
         _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
-    _check(lib().oscar_prepare(byref(desc), _ptr(k_src) if n else None, _ptr(v_src) if n else None, n,
-                               _ptr(dst_page) if n else None, _ptr(dst_slot) if n else None,
-                               _ptr(clip_k) if n else None, _ptr(clip_v) if n else None, _ptr(q), _ptr(rot_k),
-                               _ptr(rot_v), _ptr(pool), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch,
-                               float(sm_scale), int(n_splits), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    head = (_ptr(k_src) if n else None, _ptr(v_src) if n else None, n, _ptr(dst_page) if n else None,
+            _ptr(dst_slot) if n else None, _ptr(clip_k) if n else None, _ptr(clip_v) if n else None, _ptr(q),
+            _ptr(rot_k), _ptr(rot_v))
+    rest = (_ptr(pool), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch, float(sm_scale), int(n_splits),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if codebook is None:
+        _check(lib().oscar_prepare(byref(desc), *head, *rest))
+    else:
+        _check_codebook(desc, codebook)
+        _check(lib().oscar_prepare_codebook(byref(desc), *head, _ptr(codebook), *rest))
+
+
+def oscar_prepare_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v,
+                           codebook, pool, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace,
+                           stream=None):
+    """oscar_prepare with the Lloyd-Max codebook (uint8 [Hkv, 2, 4]) for demotion and the query data."""
+    oscar_prepare(desc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win, v_win,
+                  win_len, sm_scale, n_splits, workspace, stream, codebook)

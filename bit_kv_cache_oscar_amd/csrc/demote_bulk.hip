@@ -25,6 +25,9 @@
 // Codes come from the fp32 y when delta / s16 <= 9e-5, which keeps every code on the side of
 // its rounding boundary the exact value is on unless the exact value lies within 1e-4 of
 // the boundary; a token failing that test has all 128 values summed exactly instead.
+// With a codebook (the Lloyd-Max variant) the scale, zero point and every interval test are
+// the same, and each code is the nearest codebook level of t instead (boundaries: the
+// midpoints between levels).
 // Packing goes through LDS: K words are a token's 16 consecutive dims, V words a dim's 16
 // consecutive slots; a tile whose 16 tokens fill slots 16u..16u+15 of one page in order
 // writes whole V words, any other tile merges its V codes into the shared words with 32-bit
@@ -147,12 +150,15 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
-// exact code of value y (fp64) under (s16, z16), as the quantiser defines it
-__device__ __forceinline__ uint32_t exact_code(double y, uint16_t s16, uint16_t z16) {
+// exact code of value y (fp64) under (s16, z16), as the quantiser defines it: uniform
+// levels for lv == 0, else the nearest level of codebook word lv
+__device__ __forceinline__ uint32_t exact_code(double y, uint16_t s16, uint16_t z16, uint32_t lv) {
 #pragma clang fp contract(off)
   const double s = h2d(s16);
   if (s == 0.0) return 0u;
-  const double t = rint((y - h2d(z16)) / s);
+  const double tq = (y - h2d(z16)) / s;
+  if (lv != 0u) return static_cast<uint32_t>(codebook_code(tq, lv));
+  const double t = rint(tq);
   return t < 0.0 ? 0u : (t > 3.0 ? 3u : static_cast<uint32_t>(t));
 }
 
@@ -165,7 +171,7 @@ __device__ __forceinline__ uint32_t exact_code(double y, uint16_t s16, uint16_t 
 // main loop.
 __device__ __attribute__((noinline)) uint64_t exact_tokens(const uint16_t* xs, const uint16_t* rt, uint32_t* fbw,
                                                           uint64_t todo, uint32_t cand, double delta, uint32_t sz,
-                                                          double cr) {
+                                                          double cr, uint32_t lv) {
   const int lane = threadIdx.x & 63;
   const int n_ = lane & 15;
   uint16_t s16 = static_cast<uint16_t>(sz & 0xFFFFu);
@@ -278,7 +284,7 @@ __device__ __attribute__((noinline)) uint64_t exact_tokens(const uint16_t* xs, c
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int j = lane + 64 * h;
-        const uint32_t q = exact_code(yv[h], es16, ez16);
+        const uint32_t q = exact_code(yv[h], es16, ez16, lv);
         // fb word (token nf, mt = j / 16) holds dim 16 mt + 4 g + e at bits 8 g + 2 e
         const int r = j & 15;
         atomicOr(&fbw[nf * 8 + (j >> 4)], q << (8 * (r >> 2) + 2 * (r & 3)));
@@ -294,11 +300,13 @@ __device__ __attribute__((noinline)) uint64_t exact_tokens(const uint16_t* xs, c
   return static_cast<uint64_t>(s16) | (static_cast<uint64_t>(z16) << 16) | (static_cast<uint64_t>(fbk) << 32);
 }
 
+// CB: the Lloyd-Max codebook variant (codebook words [n_kv][K, V])
+template <bool CB>
 __global__ __launch_bounds__(256) void demote_bulk_kernel(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, int n, int n_kv,
     const int32_t* __restrict__ dst_page, const int32_t* __restrict__ dst_slot,
     const uint16_t* __restrict__ rot_k, const uint16_t* __restrict__ rot_v, const float* __restrict__ clip_k,
-    const float* __restrict__ clip_v, uint8_t* __restrict__ pool) {
+    const float* __restrict__ clip_v, uint8_t* __restrict__ pool, const uint32_t* __restrict__ codebook) {
   __shared__ __align__(16) BulkSmem sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -310,6 +318,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
   const uint16_t* src = is_v ? v_src : k_src;
   const uint16_t* rot = (is_v ? rot_v : rot_k) + static_cast<size_t>(head) * kHeadDim * kHeadDim;
   const double cr = static_cast<double>(is_v ? clip_v[head] : clip_k[head]);
+  const uint32_t lv = CB ? codebook[2 * head + is_v] : 0u;  // codebook word (0: uniform levels)
 
   // R^T into LDS: thread (i, half) copies row i, columns 64 half .. + 63
   {
@@ -472,7 +481,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(xs + n_ * kHeadDim + 32 * ks + 8 * G) = bx[tt][ks];
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const uint64_t r = exact_tokens(xs, sm.rt, fbw, todo, cand, delta,
-                                        static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16), cr);
+                                        static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16), cr, lv);
         s16 = static_cast<uint16_t>(r & 0xFFFFu);
         z16 = static_cast<uint16_t>((r >> 16) & 0xFFFFu);
         fbk = (r >> 32) & 1u;
@@ -489,10 +498,16 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         uint32_t w = 0u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // t + 1/2 clamped to [0, 3.5], truncated: the nearest level (a tie rounds up, and a
-          // tie of the fp32 value lies inside the tolerated band around the boundary)
-          const float t = __builtin_amdgcn_fmed3f(fmaf(acc[mt][tt][e] - zf, inv_s, 0.5f), 0.f, 3.5f);
-          w |= static_cast<uint32_t>(t) << (8 * e);
+          if constexpr (CB) {
+            // the nearest codebook level (a tie of the fp32 value lies inside the tolerated
+            // band around the midpoint)
+            w |= static_cast<uint32_t>(codebook_code((acc[mt][tt][e] - zf) * inv_s, lv)) << (8 * e);
+          } else {
+            // t + 1/2 clamped to [0, 3.5], truncated: the nearest level (a tie rounds up, and
+            // a tie of the fp32 value lies inside the tolerated band around the boundary)
+            const float t = __builtin_amdgcn_fmed3f(fmaf(acc[mt][tt][e] - zf, inv_s, 0.5f), 0.f, 3.5f);
+            w |= static_cast<uint32_t>(t) << (8 * e);
+          }
         }
         if (sf == 0.f) w = 0u;
         cw[mt] = w;
@@ -582,13 +597,19 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
 hipError_t launch_demote_bulk(const LayerShape& L, const void* k_src, const void* v_src, int n,
                               const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k,
                               const void* rot_v, const float* clip_k, const float* clip_v, void* pool,
-                              hipStream_t stream) {
+                              hipStream_t stream, const uint32_t* codebook) {
   if (n <= 0) return hipSuccess;
   const unsigned blocks = static_cast<unsigned>((n + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL(demote_bulk_kernel, dim3(blocks, L.n_kv, 2), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(k_src), static_cast<const uint16_t*>(v_src), n, L.n_kv, dst_page,
-                     dst_slot, static_cast<const uint16_t*>(rot_k), static_cast<const uint16_t*>(rot_v), clip_k,
-                     clip_v, static_cast<uint8_t*>(pool));
+  if (codebook)
+    hipLaunchKernelGGL(demote_bulk_kernel<true>, dim3(blocks, L.n_kv, 2), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(k_src), static_cast<const uint16_t*>(v_src), n, L.n_kv, dst_page,
+                       dst_slot, static_cast<const uint16_t*>(rot_k), static_cast<const uint16_t*>(rot_v), clip_k,
+                       clip_v, static_cast<uint8_t*>(pool), codebook);
+  else
+    hipLaunchKernelGGL(demote_bulk_kernel<false>, dim3(blocks, L.n_kv, 2), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(k_src), static_cast<const uint16_t*>(v_src), n, L.n_kv, dst_page,
+                       dst_slot, static_cast<const uint16_t*>(rot_k), static_cast<const uint16_t*>(rot_v), clip_k,
+                       clip_v, static_cast<uint8_t*>(pool), nullptr);
   return hipGetLastError();
 }
 

@@ -16,7 +16,9 @@
 // of these intervals: when both ends agree (all but a vanishing fraction of rows), the
 // decisions equal those made from the exact dot products. Otherwise wave 0 recomputes
 // the row's dot products with compensated (two-sum) fp64 sums and decides from those.
-// The scale/zero arithmetic is fp64 exactly as specified.
+// The scale/zero arithmetic is fp64 exactly as specified. With a codebook (the Lloyd-Max
+// variant, QbitAI article on OSCAR, comparison with TurboQuant) the scale and zero point
+// are the same and each code is the nearest of the four codebook levels instead.
 
 #pragma once
 
@@ -53,12 +55,15 @@ __device__ __forceinline__ ScaleZero scale_zero(double cr, double ymax, double y
   return {f64_to_f16_rne((hi - lo) / 3.0), f64_to_f16_rne(lo)};
 }
 
-// 2-bit code of rotated value y: round half to even of (y - z) / s, clamped to [0, 3]
-__device__ __forceinline__ int code_of(double y, double z16d, double s16d) {
+// 2-bit code of rotated value y from t = (y - z) / s: round half to even, clamped to
+// [0, 3], for the uniform levels (lv == 0); the nearest level of codebook word lv otherwise
+__device__ __forceinline__ int code_of(double y, double z16d, double s16d, uint32_t lv) {
 #pragma clang fp contract(off)
   if (s16d == 0.0) return 0;
-  const double t = rint((y - z16d) / s16d);
-  return t > 3.0 ? 3 : (t >= 0.0 ? static_cast<int>(t) : 0);
+  const double t = (y - z16d) / s16d;
+  if (lv != 0u) return codebook_code(t, lv);
+  const double r = rint(t);
+  return r > 3.0 ? 3 : (r >= 0.0 ? static_cast<int>(r) : 0);
 }
 
 struct Pair {
@@ -89,7 +94,8 @@ __device__ __forceinline__ void demote_row(unsigned char* __restrict__ smem, int
                                            int n_kv, const int32_t* __restrict__ dst_page,
                                            const int32_t* __restrict__ dst_slot, const uint16_t* __restrict__ rot_k,
                                            const uint16_t* __restrict__ rot_v, const float* __restrict__ clip_k,
-                                           const float* __restrict__ clip_v, uint8_t* __restrict__ pool) {
+                                           const float* __restrict__ clip_v, uint8_t* __restrict__ pool,
+                                           const uint32_t* __restrict__ codebook = nullptr) {
 #pragma clang fp contract(off)
   double(*part)[64][4] = reinterpret_cast<double(*)[64][4]>(smem);
   const int row = item >> 1;  // token * n_kv + head
@@ -112,10 +118,12 @@ __device__ __forceinline__ void demote_row(unsigned char* __restrict__ smem, int
   for (int i = 0; i < 32; ++i) rw[i] = rp[i * (kHeadDim / 2)];
   int page = 0, slot = 0;
   float crf = 0.f;
+  uint32_t lv = 0u;  // codebook word (0: the uniform levels)
   if (wave == 0) {
     page = dst_page[tok];
     slot = dst_slot[tok];
     crf = is_v ? clip_v[head] : clip_k[head];
+    if (codebook) lv = codebook[2 * head + is_v];
   }
 
   // ---- this quarter's 32 terms of dims 2 lane, 2 lane + 1, and sum |p|
@@ -165,12 +173,12 @@ __device__ __forceinline__ void demote_row(unsigned char* __restrict__ smem, int
     const ScaleZero sz2 = scale_zero(cr, ymax + dm, ymin - dm);
     const double s16d = f16_bits_to_f64(sz.s16);
     const double z16d = f16_bits_to_f64(sz.z16);
-    c0 = code_of(y0 - d0, z16d, s16d);
-    c1 = code_of(y1 - d1, z16d, s16d);
+    c0 = code_of(y0 - d0, z16d, s16d, lv);
+    c1 = code_of(y1 - d1, z16d, s16d, lv);
     // wave-uniform: both ends of every interval give the same decision (dm finite also
     // rules out overflow and NaN in the products)
     const bool row_ok = (sz.s16 == sz2.s16) && (sz.z16 == sz2.z16) && dm <= 1e300;
-    const bool lane_ok = (c0 == code_of(y0 + d0, z16d, s16d)) && (c1 == code_of(y1 + d1, z16d, s16d));
+    const bool lane_ok = (c0 == code_of(y0 + d0, z16d, s16d, lv)) && (c1 == code_of(y1 + d1, z16d, s16d, lv));
     if (pass == 1 || (row_ok && __all(lane_ok))) break;
     const Pair e = exact_pair(src, rot, lane);
     y0 = e.y0;

@@ -30,6 +30,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
 }
 
+// Codebook word of the Lloyd-Max variant, one per (KV head, K or V): byte c holds level c
+// of the four in sixteenths of the group's scale above its zero point (increasing, within
+// [0, 48]; the uniform INT2 levels are 0, 16, 32, 48). Integer centre of the level range:
+// every level lies within 24 of it.
+__host__ __device__ inline int codebook_mid(uint32_t lv) {
+  return static_cast<int>(((lv & 0xFFu) + (lv >> 24)) >> 1);
+}
+
+// Code of t = (y - z16) / s16 under a codebook word: the nearest level, a midpoint between
+// two levels going to the even index. The midpoints are multiples of 1/32, exact in fp64
+// and fp32.
+template <typename T>
+__device__ __forceinline__ int codebook_code(T t, uint32_t lv) {
+  const T th0 = static_cast<T>(static_cast<int>((lv & 0xFFu) + ((lv >> 8) & 0xFFu))) * static_cast<T>(0.03125);
+  const T th1 = static_cast<T>(static_cast<int>(((lv >> 8) & 0xFFu) + ((lv >> 16) & 0xFFu))) * static_cast<T>(0.03125);
+  const T th2 = static_cast<T>(static_cast<int>(((lv >> 16) & 0xFFu) + (lv >> 24))) * static_cast<T>(0.03125);
+  return static_cast<int>(t > th0) + static_cast<int>(t >= th1) + static_cast<int>(t > th2);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

@@ -33,6 +33,16 @@
 //   head's reference maximum or the fixed-point exponent must change. A reference maximum
 //   moves only when a score exceeds it by more than kTau (log2 units), so p <= 2^kTau.
 //
+// Lloyd-Max codebook variant (QbitAI article on OSCAR, comparison with TurboQuant: a
+// stronger Lloyd-Max codebook in place of the uniform levels): a code c dequantises to
+// z + s k_c / 16 with four levels k_c per (KV head, K or V). The codes are unpacked as
+// above and mapped through the levels by one byte permute per four codes. K takes the
+// levels centred, k_c - mid (mid the integer centre of the levels, |k_c - mid| <= 24), so
+// the MFMA yields Q . (k - mid) with no centring seed (the query preparation keeps
+// sum |Q| < 2^26 + 64 for it), and the fold is s 2^-sh Q . (k - mid) / 16 + (z + s mid / 16)
+// sum(q_rot). V takes the levels themselves (0..48, the same bound as the scaled codes),
+// every lane with the factor 16.
+//
 // A workgroup serves one (history split, KV head x head group, request), 4 waves, at most 8
 // query heads (16 query heads per KV head run as two groups of 8). Wave w walks
 // pages split_begin + w, + 4, ... of its split with two page buffers in flight. In a page,
@@ -74,6 +84,16 @@ __device__ __forceinline__ i8x16 unpack16_scaled(uint32_t w) {
   u.y = w & 0x0C0C0C0Cu;
   u.z = w & 0x30303030u;
   u.w = (w >> 2) & 0x30303030u;
+  return __builtin_bit_cast(i8x16, u);
+}
+
+// as unpack16, each code replaced by byte `code` of the lookup word `lut`
+__device__ __forceinline__ i8x16 unpack16_lut(uint32_t w, uint32_t lut) {
+  uint4 u;
+  u.x = __builtin_amdgcn_perm(lut, lut, w & 0x03030303u);
+  u.y = __builtin_amdgcn_perm(lut, lut, (w >> 2) & 0x03030303u);
+  u.z = __builtin_amdgcn_perm(lut, lut, (w >> 4) & 0x03030303u);
+  u.w = __builtin_amdgcn_perm(lut, lut, (w >> 6) & 0x03030303u);
   return __builtin_bit_cast(i8x16, u);
 }
 
@@ -148,7 +168,7 @@ constexpr int kQprepSmem = 3 * 64 * 2 * 8;
 __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* __restrict__ q,
                                            const uint16_t* __restrict__ rot_k, int n_q, int gq, double scale_log2,
                                            char* __restrict__ qlimb, QueryScal* __restrict__ qscal, int h, int b,
-                                           int nqt = 1) {
+                                           int nqt = 1, const uint32_t* __restrict__ codebook = nullptr) {
   double(*part_s)[64][2] = reinterpret_cast<double(*)[64][2]>(smem);
   const int kv = h / gq;
   const int lane = threadIdx.x & 63;
@@ -165,6 +185,7 @@ __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* 
   uint32_t rr[32];
 #pragma unroll
   for (int u = 0; u < 32; ++u) rr[u] = rcol[u * (kHeadDim / 2)];
+  const uint32_t klv = codebook ? codebook[2 * kv] : 0u;  // K codebook word (0: uniform levels)
   double a0 = 0.0, a1 = 0.0;
 #pragma unroll
   for (int u = 0; u < 32; ++u) {
@@ -187,7 +208,16 @@ __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* 
   const double sm = wave_sum_f64(x0 + x1);
   int k = 0;
   if (amax > 0.f) frexpf(amax, &k);  // amax < 2^k
-  const int sh = 21 - k;
+  int sh = 21 - k;
+  if (klv != 0u) {
+    // codebook levels enter the K dot centred, as k - mid with |k - mid| <= 24: sum |Q| is
+    // held below 2^26 + 64 (the computed sum of |q_rot| is within 1e-14 of the true one),
+    // so Q . (k - mid) stays below 2^31
+    const double l1 = wave_sum_f64(fabs(x0) + fabs(x1));
+    int kl = 0;
+    if (l1 > 0.0) frexp(l1, &kl);  // l1 < 2^kl
+    sh = min(sh, 26 - kl);
+  }
   const int Q0 = static_cast<int>(rint(x0 * pow2d(sh)));
   const int Q1 = static_cast<int>(rint(x1 * pow2d(sh)));
   // signed 8-bit limbs: Q = l0 + 2^8 l1 + 2^16 l2, |l2| <= 33
@@ -211,9 +241,10 @@ __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* 
   for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
   if (lane == 0) {
     QueryScal o;
-    o.qsc = static_cast<float>(pow2d(-sh) * scale_log2);
+    // the codebook's dot is in sixteenths of the scale and needs no centring term
+    o.qsc = static_cast<float>(pow2d(-sh) * scale_log2 * (klv != 0u ? 0.0625 : 1.0));
     o.sig = static_cast<float>(sm * scale_log2);
-    o.kcent = -2 * sq;
+    o.kcent = klv != 0u ? 0 : -2 * sq;
     o.pad[0] = o.pad[1] = o.pad[2] = o.pad[3] = o.pad[4] = 0;
     qscal[head] = o;
   }
@@ -258,13 +289,13 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
 
 // One workgroup (NW waves) of the INT2 pass: history split `split` of request b for the
 // query heads gy*GQ .. gy*GQ+GQ-1 (KV head gy / n_groups). `smem` holds
-// int2_smem_bytes<GQ, NW>().
-template <int GQ, bool kCoherent = false, int NW = kWaves>
+// int2_smem_bytes<GQ, NW>(). With CB, `codebook` holds the codebook words [n_kv][K, V].
+template <int GQ, bool kCoherent = false, int NW = kWaves, bool CB = false>
 __device__ __forceinline__ void int2_split(
     unsigned char* __restrict__ smem, int split, int gy, int b, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ hist_len, int n_q, int n_kv, int n_groups, int n_splits,
     const char* __restrict__ qlimb, const QueryScal* __restrict__ qscal, float* __restrict__ out_m,
-    float* __restrict__ out_l, float* __restrict__ out_acc) {
+    float* __restrict__ out_l, float* __restrict__ out_acc, const uint32_t* __restrict__ codebook = nullptr) {
   constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
   constexpr int kPBytes = NW * MT * 16 * kPRow;
   constexpr int kFBytes = NW * MT * kFlushed * 64 * 4;
@@ -280,6 +311,19 @@ __device__ __forceinline__ void int2_split(
   float(*wl_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kLoopBytes + kWaccBytes + NW * GQ * 4);
 
   const int kv = gy / n_groups;
+  // codebook variant: lookup words of the centred K levels (k - mid as int8) and of the V
+  // levels, and the fold's centre mid / 16 (2 for the uniform codes, centred at 2)
+  uint32_t klut = 0u, vlut = 0u;
+  float kmid = 2.f;
+  if constexpr (CB) {
+    const uint32_t kw = codebook[2 * kv];
+    vlut = codebook[2 * kv + 1];
+    const int mid = codebook_mid(kw);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      klut |= (static_cast<uint32_t>(static_cast<int>((kw >> (8 * c)) & 0xFFu) - mid) & 0xFFu) << (8 * c);
+    kmid = static_cast<float>(mid) * 0.0625f;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -372,8 +416,9 @@ __device__ __forceinline__ void int2_split(
   float thr = kTau;     // E + kTau: frame-relative scores above it move the reference
   // the codes of this lane's slots carry the factor (1, 4, 16, 16)[n % 4]: the V scales
   // are taken over it (powers of two, exact)
-  const float vscale = (n & 3) == 0 ? 1.f : ((n & 3) == 1 ? 0.25f : 0.0625f);
-  const float vunscale = (n & 3) == 0 ? 1.f : ((n & 3) == 1 ? 4.f : 16.f);
+  // (with a codebook every lane's V levels carry the factor 16 of the sixteenths)
+  const float vscale = CB ? 0.0625f : ((n & 3) == 0 ? 1.f : ((n & 3) == 1 ? 0.25f : 0.0625f));
+  const float vunscale = CB ? 16.f : ((n & 3) == 0 ? 1.f : ((n & 3) == 1 ? 4.f : 16.f));
   float vcap_l = -1.f;  // V scales below vcap_l / vscale fit the current E
   bool fresh = true;    // no page processed yet
 
@@ -417,8 +462,14 @@ __device__ __forceinline__ void int2_split(
     i32x4 d[MT][4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const i8x16 b0 = unpack16(cur.kword(nt, 0));
-      const i8x16 b1 = unpack16(cur.kword(nt, 1));
+      i8x16 b0, b1;
+      if constexpr (CB) {
+        b0 = unpack16_lut(cur.kword(nt, 0), klut);
+        b1 = unpack16_lut(cur.kword(nt, 1), klut);
+      } else {
+        b0 = unpack16(cur.kword(nt, 0));
+        b1 = unpack16(cur.kword(nt, 1));
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, i32x4{kcent[mt], 0, 0, 0}));
@@ -430,7 +481,7 @@ __device__ __forceinline__ void int2_split(
       const uint32_t km = cur.kmeta(nt);
       const uint32_t vm = cur.vmeta(nt);
       sk[nt] = f16_to_f32(km);
-      u[nt] = fmaf(2.f, sk[nt], f16_to_f32(km >> 16));  // z + 2 s
+      u[nt] = fmaf(kmid, sk[nt], f16_to_f32(km >> 16));  // z + 2 s (codebook: z + s mid / 16)
       sv[nt] = f16_to_f32(vm) * vscale;  // V scale over the factor of this lane's codes
       zv[nt] = f16_to_f32(vm >> 16);
     }
@@ -538,7 +589,11 @@ __device__ __forceinline__ void int2_split(
       // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const i8x16 bv = unpack16_scaled(cur.vword(dt));
+        i8x16 bv;
+        if constexpr (CB)
+          bv = unpack16_lut(cur.vword(dt), vlut);
+        else
+          bv = unpack16_scaled(cur.vword(dt));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           if (MT == 1 || !vskip[mt]) st.acci[mt][dt] = mfma16(aP[mt], bv, st.acci[mt][dt]);

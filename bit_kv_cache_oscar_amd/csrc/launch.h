@@ -54,14 +54,15 @@ size_t partials_bytes(int batch, int n_q, int n_splits);
 PartialsView partials_view(void* base, int batch, int n_q, int n_splits);
 size_t step_workspace_bytes(int batch, int n_q, int n_kv, int n_splits, int n_wsplits);
 
+// `codebook`: null for the uniform levels, else the codebook words [n_kv][K, V]
 hipError_t launch_demote_rows(const LayerShape& L, const void* k_src, const void* v_src, int n,
                               const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k,
                               const void* rot_v, const float* clip_k, const float* clip_v, void* pool,
-                              hipStream_t stream);
+                              hipStream_t stream, const uint32_t* codebook = nullptr);
 hipError_t launch_demote_bulk(const LayerShape& L, const void* k_src, const void* v_src, int n,
                               const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k,
                               const void* rot_v, const float* clip_k, const float* clip_v, void* pool,
-                              hipStream_t stream);
+                              hipStream_t stream, const uint32_t* codebook = nullptr);
 
 hipError_t launch_decode_int2(const LayerShape& L, const void* q, const void* rot_k, const void* pool,
                               const int32_t* block_table, int max_pages, const int32_t* hist_len,
@@ -101,6 +102,9 @@ struct StepArgs {
   PartialsView win;   // window partials
   int* counters;      // [batch][n_kv] arrival counters
   float* out;
+  // Lloyd-Max codebook variant: words [n_kv][K, V], byte c = level c in sixteenths of the
+  // scale; null for the uniform INT2 levels
+  const uint32_t* codebook;
 };
 
 // Demotion + window pass + query preparation (one launch), and the INT2 pass with the merge

@@ -182,9 +182,20 @@ int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_
   return static_cast<int32_t>(s);
 }
 
-int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
-                     const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
-                     const float* clip_k, const float* clip_v, void* pool, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The codebook argument of the Lloyd-Max entry points: non-null and 4-byte aligned.
+int32_t check_codebook(const void* codebook) {
+  if (!codebook) return fail(OSCAR_ERR_INVALID_ARG, "null codebook");
+  if (reinterpret_cast<uintptr_t>(codebook) % 4 != 0) return fail(OSCAR_ERR_INVALID_ARG, "codebook not 4-byte aligned");
+  return OSCAR_OK;
+}
+
+int32_t demote_impl(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                    const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                    const float* clip_k, const float* clip_v, const uint32_t* codebook, void* pool, void* stream) {
   int32_t st = check_desc_impl(desc);
   if (st != OSCAR_OK) return st;
   if (n < 0) return fail(OSCAR_ERR_INVALID_ARG, "n %d < 0", n);
@@ -197,11 +208,30 @@ int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void
   // many rows: the matrix-core kernel (whole 16-token tiles); a few: one workgroup per row
   if (n >= kBulkMinRows)
     return hip_status(oscar::launch_demote_bulk(L, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v,
-                                                pool, static_cast<hipStream_t>(stream)),
+                                                pool, static_cast<hipStream_t>(stream), codebook),
                       "demote launch");
   return hip_status(oscar::launch_demote_rows(L, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v,
-                                              pool, static_cast<hipStream_t>(stream)),
+                                              pool, static_cast<hipStream_t>(stream), codebook),
                     "demote launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t oscar_demote(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                     const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                     const float* clip_k, const float* clip_v, void* pool, void* stream) {
+  return demote_impl(desc, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v, nullptr, pool, stream);
+}
+
+int32_t oscar_demote_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                              const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                              const float* clip_k, const float* clip_v, const uint8_t* codebook, void* pool,
+                              void* stream) {
+  if (int32_t e = check_codebook(codebook)) return e;
+  return demote_impl(desc, k_src, v_src, n, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v,
+                     reinterpret_cast<const uint32_t*>(codebook), pool, stream);
 }
 
 int32_t oscar_decode_int2(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* pool,
@@ -251,6 +281,8 @@ size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
   return oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits, window_splits_of(desc));
 }
 
+}  // extern "C"
+
 namespace {
 
 // Checks shared by the two halves of the decode step; fills the workspace views. With nqt
@@ -288,13 +320,11 @@ int32_t check_step_common(const oscar_layer_desc* desc, int32_t batch, int32_t n
   return OSCAR_OK;
 }
 
-}  // namespace
-
-int32_t oscar_prepare(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
-                      const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
-                      const void* q, const void* rot_k, const void* rot_v, void* pool, const void* k_win,
-                      const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+int32_t prepare_impl(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                     const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
+                     const void* q, const void* rot_k, const void* rot_v, const uint32_t* codebook, void* pool,
+                     const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
+                     int32_t n_splits, void* workspace, size_t workspace_bytes, void* stream) {
   oscar::StepArgs a;
   int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
   if (st != OSCAR_OK) return st;
@@ -322,12 +352,13 @@ int32_t oscar_prepare(const oscar_layer_desc* desc, const void* k_src, const voi
   a.v_win = static_cast<const uint16_t*>(v_win);
   a.win_len = win_len;
   a.scale_log2 = static_cast<double>(sm_scale) * 1.4426950408889634;
+  a.codebook = codebook;
   return hip_status(oscar::launch_prepare(a, static_cast<hipStream_t>(stream)), "prepare launch");
 }
 
-int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void* pool, const int32_t* block_table,
-                     int32_t max_pages, const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
-                     size_t workspace_bytes, float* out, void* stream) {
+int32_t attend_impl(const oscar_layer_desc* desc, const void* rot_v, const uint32_t* codebook, const void* pool,
+                    const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, int32_t batch,
+                    int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream) {
   oscar::StepArgs a;
   int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
   if (st != OSCAR_OK) return st;
@@ -339,7 +370,47 @@ int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void
   a.max_pages = max_pages;
   a.hist_len = hist_len;
   a.out = out;
+  a.codebook = codebook;
   return hip_status(oscar::launch_attend(a, static_cast<hipStream_t>(stream)), "attend launch");
+}
+
+int32_t step_impl(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                  const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
+                  const void* q, const void* rot_k, const void* rot_v, const uint32_t* codebook, void* pool,
+                  const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, const void* k_win,
+                  const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                  void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  // the attend half's arguments are checked before anything is enqueued
+  oscar::StepArgs a;
+  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
+  if (st != OSCAR_OK) return st;
+  if (int32_t e = check_pages(max_pages, n_splits)) return e;
+  if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  st = prepare_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, codebook, pool, k_win,
+                    v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, stream);
+  if (st != OSCAR_OK) return st;
+  return attend_impl(desc, rot_v, codebook, pool, block_table, max_pages, hist_len, batch, n_splits, workspace,
+                     workspace_bytes, out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t oscar_prepare(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                      const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
+                      const void* q, const void* rot_k, const void* rot_v, void* pool, const void* k_win,
+                      const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return prepare_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, nullptr, pool, k_win,
+                      v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, stream);
+}
+
+int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void* pool, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
+                     size_t workspace_bytes, float* out, void* stream) {
+  return attend_impl(desc, rot_v, nullptr, pool, block_table, max_pages, hist_len, batch, n_splits, workspace,
+                     workspace_bytes, out, stream);
 }
 
 int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
@@ -348,17 +419,9 @@ int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const
                           const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, const void* k_win,
                           const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
                           int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream) {
-  // the attend half's arguments are checked before anything is enqueued
-  oscar::StepArgs a;
-  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
-  if (st != OSCAR_OK) return st;
-  if (int32_t e = check_pages(max_pages, n_splits)) return e;
-  if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
-  st = oscar_prepare(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win, v_win,
-                     win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, stream);
-  if (st != OSCAR_OK) return st;
-  return oscar_attend(desc, rot_v, pool, block_table, max_pages, hist_len, batch, n_splits, workspace,
-                      workspace_bytes, out, stream);
+  return step_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, nullptr, pool,
+                   block_table, max_pages, hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, workspace,
+                   workspace_bytes, out, stream);
 }
 
 int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* rot_v,
@@ -366,9 +429,54 @@ int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* ro
                      const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
                      int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream) {
   // nothing is demoted, so the pool is only read
-  return oscar_decode_step(desc, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, q, rot_k, rot_v,
-                           const_cast<void*>(pool), block_table, max_pages, hist_len, k_win, v_win, win_len, batch,
-                           sm_scale, n_splits, workspace, workspace_bytes, out, stream);
+  return step_impl(desc, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, q, rot_k, rot_v, nullptr,
+                   const_cast<void*>(pool), block_table, max_pages, hist_len, k_win, v_win, win_len, batch, sm_scale,
+                   n_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t oscar_prepare_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                               const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                               const float* clip_v, const void* q, const void* rot_k, const void* rot_v,
+                               const uint8_t* codebook, void* pool, const void* k_win, const void* v_win,
+                               const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (int32_t e = check_codebook(codebook)) return e;
+  return prepare_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v,
+                      reinterpret_cast<const uint32_t*>(codebook), pool, k_win, v_win, win_len, batch, sm_scale,
+                      n_splits, workspace, workspace_bytes, stream);
+}
+
+int32_t oscar_attend_codebook(const oscar_layer_desc* desc, const void* rot_v, const uint8_t* codebook,
+                              const void* pool, const int32_t* block_table, int32_t max_pages,
+                              const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
+                              size_t workspace_bytes, float* out, void* stream) {
+  if (int32_t e = check_codebook(codebook)) return e;
+  return attend_impl(desc, rot_v, reinterpret_cast<const uint32_t*>(codebook), pool, block_table, max_pages, hist_len,
+                     batch, n_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t oscar_decode_step_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                                   const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                                   const float* clip_v, const void* q, const void* rot_k, const void* rot_v,
+                                   const uint8_t* codebook, void* pool, const int32_t* block_table,
+                                   int32_t max_pages, const int32_t* hist_len, const void* k_win, const void* v_win,
+                                   const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                                   void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  if (int32_t e = check_codebook(codebook)) return e;
+  return step_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v,
+                   reinterpret_cast<const uint32_t*>(codebook), pool, block_table, max_pages, hist_len, k_win, v_win,
+                   win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t oscar_decode_codebook(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* rot_v,
+                              const uint8_t* codebook, const void* pool, const int32_t* block_table,
+                              int32_t max_pages, const int32_t* hist_len, const void* k_win, const void* v_win,
+                              const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                              void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  if (int32_t e = check_codebook(codebook)) return e;
+  return step_impl(desc, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, q, rot_k, rot_v,
+                   reinterpret_cast<const uint32_t*>(codebook), const_cast<void*>(pool), block_table, max_pages,
+                   hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, out, stream);
 }
 
 int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
   int id = blockIdx.x;
   if (id < a.n_dem_items) {
     demote::demote_row(smem, id, a.k_src, a.v_src, a.n_kv, a.dst_page, a.dst_slot, a.rot_k, a.rot_v, a.clip_k,
-                       a.clip_v, a.pool);
+                       a.clip_v, a.pool, a.codebook);
     return;
   }
   id -= a.n_dem_items;
@@ -71,18 +71,20 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
   const int h = id % a.n_q;
   const int b = id / a.n_q;
   if (threadIdx.x == 0 && h % a.gq == 0) a.counters[b * a.n_kv + h / a.gq] = 0;
-  int2::qprep_head(smem, a.q, a.rot_k, a.n_q, a.gq, a.scale_log2, a.hist.qlimb, a.hist.qscal, h, b, a.nqt);
+  int2::qprep_head(smem, a.q, a.rot_k, a.n_q, a.gq, a.scale_log2, a.hist.qlimb, a.hist.qscal, h, b, a.nqt,
+                   a.codebook);
 }
 
-// GQ query heads per workgroup, GQT per KV head (GQT = GQ n_groups), NW waves
-template <int GQ, int GQT, int NW>
+// GQ query heads per workgroup, GQT per KV head (GQT = GQ n_groups), NW waves; CB: the
+// codebook variant
+template <int GQ, int GQT, int NW, bool CB>
 __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // the INT2 pass and the merge use the same LDS one after the other
   __shared__ __align__(16) unsigned char smem[cmax(int2::int2_smem_bytes<GQ, NW>(), merge::smem_bytes<GQT, NW>())];
   __shared__ int ticket_s;
-  int2::int2_split<GQ, true, NW>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table, a.max_pages,
-                                 a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits, a.hist.qlimb, a.hist.qscal,
-                                 a.hist.m, a.hist.l, a.hist.acc);
+  int2::int2_split<GQ, true, NW, CB>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table, a.max_pages,
+                                     a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits, a.hist.qlimb, a.hist.qscal,
+                                     a.hist.m, a.hist.l, a.hist.acc, a.codebook);
   const int kv = blockIdx.y / a.n_groups;
   const int b = blockIdx.z;
   // the partials went out as agent-scope stores: once each thread's stores have completed
@@ -120,14 +122,19 @@ hipError_t launch_prep(StepArgs a, hipStream_t stream) {
 
 // Up to 256 workgroups (one per CU) run with 8 waves each, so few splits still give
 // every SIMD two waves; larger grids use 4 waves per workgroup.
-template <int GQ, int GQT>
-hipError_t launch_main(const StepArgs& a, hipStream_t stream) {
+template <int GQ, int GQT, bool CB>
+hipError_t launch_main_cb(const StepArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_splits, a.n_kv * a.n_groups, a.batch);
   if (static_cast<long long>(grid.x) * grid.y * grid.z <= 256)
-    hipLaunchKernelGGL((main_kernel<GQ, GQT, 8>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((main_kernel<GQ, GQT, 8, CB>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((main_kernel<GQ, GQT, 4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((main_kernel<GQ, GQT, 4, CB>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int GQ, int GQT>
+hipError_t launch_main(const StepArgs& a, hipStream_t stream) {
+  return a.codebook ? launch_main_cb<GQ, GQT, true>(a, stream) : launch_main_cb<GQ, GQT, false>(a, stream);
 }
 
 }  // namespace

@@ -48,6 +48,7 @@ class LayerCache:
         self.clip_v = torch.ones_like(self.clip_k)
         self.out = torch.zeros((batch, n_q_heads, HEAD_DIM), dtype=torch.float32, device=self.device)
         self.n_splits = 1
+        self.codebook = None  # Lloyd-Max variant: uint8 [Hkv, 2, 4] levels (None: uniform INT2)
         self._partials = None
         self._workspace = None
         self.win_partials = torch.zeros(L.oscar_partials_bytes(self.desc, batch, L.oscar_window_splits(self.desc)),
@@ -59,6 +60,21 @@ class LayerCache:
         self.rot_v.copy_(_bf16_tensor(rot_v_bits, self.device).reshape(self.rot_v.shape))
         self.clip_k.copy_(torch.as_tensor(np.asarray(clip_k, np.float32)).reshape(-1))
         self.clip_v.copy_(torch.as_tensor(np.asarray(clip_v, np.float32)).reshape(-1))
+
+    def set_codebook(self, k_levels, v_levels):
+        """Switch the layer to the Lloyd-Max codebook variant: k_levels/v_levels [Hkv, 4] are each
+        head's four levels in sixteenths of the scale (strictly increasing, within [0, 48]).
+        A pool is written and read with one codebook; None for both restores the uniform levels."""
+        if k_levels is None and v_levels is None:
+            self.codebook = None
+            return
+        k = np.asarray(k_levels, np.int64).reshape(self.n_kv, 4)
+        v = np.asarray(v_levels, np.int64).reshape(self.n_kv, 4)
+        for lv in (k, v):
+            if np.any(lv < 0) or np.any(lv > 48) or np.any(np.diff(lv, axis=1) <= 0):
+                raise ValueError("codebook levels must be strictly increasing within [0, 48]")
+        cb = np.stack([k, v], axis=1).astype(np.uint8)
+        self.codebook = torch.from_numpy(np.ascontiguousarray(cb)).to(self.device)
 
     def set_block_table(self, table: np.ndarray):
         t = torch.from_numpy(np.where(table < 0, 0, table).astype(np.int32))
@@ -100,10 +116,12 @@ class LayerCache:
                stream=None):
         """Demote tokens k_rows/v_rows [n, Hkv, 128] bf16 into (pages[i], slots[i])."""
         L.oscar_demote(self.desc, k_rows, v_rows, pages, slots, self.rot_k, self.rot_v, self.clip_k,
-                       self.clip_v, self.pool, stream)
+                       self.clip_v, self.pool, stream, self.codebook)
 
     def decode(self, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
         """Attention output [B, Hq, 128] float32 for queries q [B, Hq, 128] bf16."""
+        if self.codebook is not None:
+            raise ValueError("the separate entry points read uniform INT2 levels; use decode_fused() or step()")
         L.oscar_decode_int2(self.desc, q, self.rot_k, self.pool, self.block_table, self.hist_len, sm_scale,
                             self.n_splits, self.partials, stream)
         L.oscar_decode_bf16(self.desc, q, self.k_win, self.v_win, self.win_len, sm_scale, self.win_partials,
@@ -115,7 +133,7 @@ class LayerCache:
         """The same output as decode(), in two launches (oscar_decode)."""
         L.oscar_decode(self.desc, q, self.rot_k, self.rot_v, self.pool, self.block_table, self.hist_len,
                        self.k_win, self.v_win, self.win_len, sm_scale, self.n_splits, self.workspace, self.out,
-                       stream)
+                       stream, self.codebook)
         return self.out
 
     def step(self, k_rows, v_rows, pages, slots, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
@@ -123,5 +141,5 @@ class LayerCache:
         two launches (oscar_decode_step). hist_len must already count the demoted tokens."""
         L.oscar_decode_step(self.desc, k_rows, v_rows, pages, slots, self.clip_k, self.clip_v, q, self.rot_k,
                             self.rot_v, self.pool, self.block_table, self.hist_len, self.k_win, self.v_win,
-                            self.win_len, sm_scale, self.n_splits, self.workspace, self.out, stream)
+                            self.win_len, sm_scale, self.n_splits, self.workspace, self.out, stream, self.codebook)
         return self.out

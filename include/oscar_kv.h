@@ -296,6 +296,62 @@ int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void
                      int32_t max_pages, const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
                      size_t workspace_bytes, float* out, void* stream);
 
+/*
+ * Lloyd-Max codebook variant (QbitAI article on OSCAR, section comparing OSCAR with
+ * TurboQuant: the code release pairs the attention-aware rotation with a Lloyd-Max
+ * codebook in place of the uniform INT2 levels; the article gives nothing beyond that
+ * name, so the format below is this library's reading).
+ *
+ *   codebook   uint8 [n_kv_heads][2][4], device memory, 4-byte aligned: entry
+ *              [h][0][c] is level c of KV head h's K codebook, [h][1][c] of its V codebook,
+ *              in sixteenths of the group's scale. Levels must be strictly increasing and
+ *              within [0, 48] (other values give undefined results, never a fault). The
+ *              uniform INT2 levels are 0, 16, 32, 48.
+ *
+ * Scale and zero point are those of the uniform scheme (same clip, s = (hi - lo) / 3,
+ * fp16 each, decided exactly as in oscar_demote). A code c stands for z + s * k_c / 16
+ * in the rotated basis, and the code of y is the nearest level to t = (y - z) / s, with
+ * the even index at a midpoint between two levels (for the uniform levels: round half to
+ * even, clamped to [0, 3]); every code is 0 when s == 0. The near-boundary exemption of
+ * oscar_demote's matrix-core path applies to the midpoints between levels. The pool layout
+ * is unchanged; a pool must be written and read with the same codebook.
+ *
+ * Each entry point below is the one named without the suffix with `codebook` added (a
+ * null or misaligned codebook returns OSCAR_ERR_INVALID_ARG); every other argument and
+ * rule is that entry point's.
+ */
+int32_t oscar_demote_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                              const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                              const float* clip_k, const float* clip_v, const uint8_t* codebook, void* pool,
+                              void* stream);
+
+int32_t oscar_decode_step_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                                   const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                                   const float* clip_v, const void* q, const void* rot_k, const void* rot_v,
+                                   const uint8_t* codebook, void* pool, const int32_t* block_table,
+                                   int32_t max_pages, const int32_t* hist_len, const void* k_win, const void* v_win,
+                                   const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                                   void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+int32_t oscar_decode_codebook(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* rot_v,
+                              const uint8_t* codebook, const void* pool, const int32_t* block_table,
+                              int32_t max_pages, const int32_t* hist_len, const void* k_win, const void* v_win,
+                              const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                              void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+int32_t oscar_prepare_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                               const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                               const float* clip_v, const void* q, const void* rot_k, const void* rot_v,
+                               const uint8_t* codebook, void* pool, const void* k_win, const void* v_win,
+                               const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* oscar_prepare_codebook must have prepared the workspace with the same codebook. */
+int32_t oscar_attend_codebook(const oscar_layer_desc* desc, const void* rot_v, const uint8_t* codebook,
+                              const void* pool, const int32_t* block_table, int32_t max_pages,
+                              const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
+                              size_t workspace_bytes, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -209,3 +209,43 @@ def test_decode_multi_argument_checks(lib):
     assert call({12: 0.0}) == L.OSCAR_ERR_INVALID_ARG
     # one token needs the one-token workspace
     assert call({1: 1, 15: L.oscar_decode_workspace_bytes(desc, 2, 4) - 1}) == L.OSCAR_ERR_WORKSPACE
+
+
+def test_codebook_entry_points_check_the_codebook_first(lib):
+    desc = L.layer_desc(32, 8)
+    d = ctypes.byref(desc)
+    need = L.oscar_decode_workspace_bytes(desc, 2, 4)
+    dem = lib.oscar_demote_codebook
+    #            k, v, n, page, slot, rot_k, rot_v, clip_k, clip_v, codebook, pool, stream
+    assert dem(d, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert dem(d, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert dem(d, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_OK  # no-op
+    assert dem(d, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == L.OSCAR_ERR_INVALID_ARG
+    step = lib.oscar_decode_step_codebook
+    # the oscar_decode_step arguments with the codebook inserted before the pool (position 10)
+    args = [FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 2,
+            0.08, 4, FAKE, need, FAKE, None]
+
+    def call(over):
+        a = list(args)
+        for k, v in over.items():
+            a[k] = v
+        return step(d, *a)
+
+    assert call({10: None}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({10: FAKE + 1}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({22: need - 1}) == L.OSCAR_ERR_WORKSPACE
+    assert call({13: 4 * 8192 + 1}) == L.OSCAR_ERR_UNSUPPORTED
+    dec = lib.oscar_decode_codebook
+    #          q, rot_k, rot_v, codebook, pool, table, max_pages, hist, k_win, v_win, win_len, batch, sm, S, ws, bytes
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4, FAKE, need, FAKE, None]
+    assert dec(d, *(base[:3] + [None] + base[4:])) == L.OSCAR_ERR_INVALID_ARG
+    assert dec(d, *(base[:15] + [need - 1] + base[16:])) == L.OSCAR_ERR_WORKSPACE
+    att = lib.oscar_attend_codebook
+    assert att(d, FAKE, None, FAKE, FAKE, 4, FAKE, 2, 4, FAKE, need, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert att(d, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 4, FAKE, need - 1, FAKE, None) == L.OSCAR_ERR_WORKSPACE
+    prep = lib.oscar_prepare_codebook
+    assert prep(d, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4,
+                FAKE, need, None) == L.OSCAR_ERR_INVALID_ARG
+    assert prep(d, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4,
+                FAKE, need - 1, None) == L.OSCAR_ERR_WORKSPACE
