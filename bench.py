@@ -14,8 +14,10 @@ Prints one JSON line. `value` is the whole step's algorithmic HBM bytes divided 
 time (GB/s); `roofline` reports the dominant kernel (the attend launch: INT2 history pass
 and merge) against the 8 TB/s HBM peak, timed with events on its stream over back-to-back
 oscar_attend launches; `multi_query` times oscar_decode_multi (T query tokens per request
-over the same pools, as in speculative verification) the same way; `cpu_baseline` is the
-CPU oracle timed on a bounded sample of the same workload.
+over the same pools, as in speculative verification) the same way; `codebook` times the
+Lloyd-Max codebook variant (the same history demoted against per-head codebooks fitted on
+the calibration set, then oscar_decode_step_codebook and oscar_attend_codebook) the same
+way; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -75,12 +77,13 @@ def attend_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the attend kernel from the committed counter summary of this
-    workload, or None when there is none or the kernel source changed since it was taken.
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same counter
-    reads for a plain copy of COPY_BYTES bytes in the same run."""
-    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.txt")
+def measured_traffic(workload, kernel="attend"):
+    """HBM bytes per launch of the attend kernel (kernel="attend_codebook": its codebook
+    variant) from the committed counter summary of this workload, or None when there is none
+    or the kernel source changed since it was taken. FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) are each scaled by what the same counter reads for a plain copy of COPY_BYTES
+    bytes in the same run."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -169,9 +172,10 @@ def cpu_baseline(w, budget_s):
 BULK_TOKENS = 32768  # the bulk-demotion workload: 262,144 K rows and 262,144 V rows at 8 KV heads
 
 
-def bulk_demote(w, rk_bits, rv_bits, dev, stream, reps):
+def bulk_demote(w, rk_bits, rv_bits, dev, stream, reps, codebook=None):
     """oscar_demote of BULK_TOKENS history tokens (every KV head, K and V) into fresh pages,
-    timed with HIP events on the launch stream; rows drawn like the workload's history."""
+    timed with HIP events on the launch stream; rows drawn like the workload's history.
+    With codebook = (K levels, V levels) [Hkv, 4], oscar_demote_codebook."""
     import torch
 
     import synth
@@ -181,6 +185,8 @@ def bulk_demote(w, rk_bits, rv_bits, dev, stream, reps):
     c = LayerCache(w.n_q_heads, w.n_kv_heads, 1, n_pages, n_pages, device=dev)
     clip = np.full(w.n_kv_heads, w.clip_ratio, np.float32)
     c.set_rotations(rk_bits, rv_bits, clip, clip)
+    if codebook is not None:
+        c.set_codebook(*codebook)
     ks, vs = [], []
     for kv in range(w.n_kv_heads):
         k, v = synth.kv_rows(w, 0, kv, 64, 64 + BULK_TOKENS)
@@ -204,7 +210,8 @@ def bulk_demote(w, rk_bits, rv_bits, dev, stream, reps):
     # 256 B in and 36 B out per row, and both rotations of every KV head
     nbytes = rows * (256 + 36) + w.n_kv_heads * 2 * ROT_BYTES
     return {
-        "kernel": "demote_bulk_kernel (oscar_demote)",
+        "kernel": "demote_bulk_kernel (oscar_demote)" if codebook is None
+                  else "demote_bulk_kernel<codebook> (oscar_demote_codebook)",
         "tokens": BULK_TOKENS,
         "rows": rows,
         "us": round(us, 3),
@@ -259,6 +266,7 @@ def main():
     step_v = torch.zeros_like(step_k)
     step_page = torch.zeros(w.batch, dtype=torch.int32, device=dev)
     step_slot = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    fill_rows = []  # per request: the rows demoted by the fill, kept on the device for the codebook row
     for b in range(w.batch):
         n = w.hist_len(b)
         start = min(n, w.shared_pages * 64) if (w.shared_pages and b > 0) else 0
@@ -276,6 +284,7 @@ def main():
         sl = torch.from_numpy((j % 64).astype(np.int32)).to(dev)
         if n - start > 1:
             base.demote(kk[:-1], vv[:-1], pg[:-1], sl[:-1])
+            fill_rows.append((kk[:-1], vv[:-1], pg[:-1], sl[:-1]))
         step_k[b], step_v[b] = kk[-1], vv[-1]
         step_page[b], step_slot[b] = pg[-1], sl[-1]
     q = torch.from_numpy(np.stack([synth.query(w, b) for b in range(w.batch)])).to(dev).to(torch.bfloat16)
@@ -365,6 +374,52 @@ def main():
             "query_tokens_per_s": round(w.batch * n_tok / (multi_ms * 1e-3), 1),
         }
 
+    # timed region 4, the Lloyd-Max codebook variant: per-head K and V codebooks fitted on the
+    # calibration set by the library's host calibration; the same history demoted against
+    # them into every instance's pool; then whole steps and the attend launch alone, as above
+    cb_row = None
+    if w.calib != "gram":
+        from bit_kv_cache_oscar_amd import oscar_attend_codebook
+        from bit_kv_cache_oscar_amd.codebook import layer_codebooks
+
+        klv, vlv = layer_codebooks([synth.calibration_set(w, kv) for kv in range(w.n_kv_heads)], rk_bits, rv_bits,
+                                   clip, clip)
+        base.set_codebook(klv, vlv)
+        for kk, vv, pg, sl in fill_rows:
+            base.demote(kk, vv, pg, sl)
+        for c in insts[1:]:
+            c.pool.copy_(base.pool)
+            c.codebook = base.codebook
+
+        def step_cb(c):
+            c.step(step_k, step_v, step_page, step_slot, q, w.sm_scale, stream)
+
+        def attend_cb(c):
+            oscar_attend_codebook(c.desc, c.rot_v, c.codebook, c.pool, c.block_table, c.hist_len, c.n_splits,
+                                  c.workspace, c.out, stream)
+
+        for c in insts:  # every workspace prepared with the codebook before the attend timing
+            step_cb(c)
+        for i in range(args.warmup):
+            step_cb(insts[i % layers])
+        cb_ms = timed(step_cb, args.steps)
+        cb_attend_ms = timed(attend_cb, args.steps)
+        cb_row = {
+            "entry": "oscar_decode_step_codebook (prepare + attend); attend alone: oscar_attend_codebook",
+            "k_levels_head0": [int(x) for x in klv[0]],
+            "v_levels_head0": [int(x) for x in vlv[0]],
+            "us_per_step": round(cb_ms * 1e3, 3),
+            "step_gbs": round(total_bytes / (cb_ms * 1e-3) / 1e9, 2),
+            "attend_us_per_launch": round(cb_attend_ms * 1e3, 3),
+            "bound": "hbm",
+            "achieved": round(attend_bytes / (cb_attend_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(attend_bytes / (cb_attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name, "attend_codebook"),
+        }
+        del fill_rows
+
     out = {
         "metric": METRIC,
         "value": round(total_bytes / (ms * 1e-3) / 1e9, 2),
@@ -410,9 +465,14 @@ def main():
     }
     if multi is not None:
         out["multi_query"] = multi
+    if cb_row is not None:
+        out["codebook"] = cb_row
     if args.config == 5:
         # the bulk-demotion row of this workload (after the decode timing: it allocates)
         out["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5))
+        if cb_row is not None:
+            cb_row["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5),
+                                                (klv, vlv))
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

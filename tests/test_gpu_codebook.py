@@ -253,3 +253,46 @@ def test_codebook_step_demotes_then_decodes(case):
             compare_history(gpu, ref, km, vm, f"{case} codebook b{b} kv{kv}")
             hists[kv] = ref
         assert_close(got[b], oracle_decode_cb(w, b, rk, rv, hists, klv, vlv), f"{case} codebook step b{b}")
+
+
+FULL_SAMPLES_CB = {2: [(0, 0), (0, 5)], 3: [(0, 6)], 5: [(2, 1), (3, 7)]}
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_codebook_full_size_end_to_end_sampled(cfg):
+    """The codebook variant at the workload's real size, as the benchmark runs it: per-head
+    codebooks fitted on the calibration set, every history token demoted on the GPU against
+    them, then oscar_decode_codebook with the default split count; sampled KV heads compared
+    with the oracle (pool bytes and their query heads' outputs)."""
+    from bit_kv_cache_oscar_amd import oscar_default_splits
+
+    w = synth.workload(cfg)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    cal = [synth.calibration_set(w, kv) for kv in range(w.n_kv_heads)]
+    klv = np.stack([ocb.fit(cal[kv][1], rk[kv], w.clip_ratio) for kv in range(w.n_kv_heads)])
+    vlv = np.stack([ocb.fit(cal[kv][2], rv[kv], w.clip_ratio) for kv in range(w.n_kv_heads)])
+    table, n_phys = synth.block_table(w)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys)
+    c.set_codebook(klv, vlv)
+    say("codebook full size", w.name, "pages", n_phys, "K levels", klv[0].tolist(), "V levels", vlv[0].tolist())
+    for b in range(w.batch):
+        n = w.hist_len(b)
+        ks = np.stack([synth.kv_rows(w, b, kv, 64, 64 + n)[0] for kv in range(w.n_kv_heads)], 1)
+        vs = np.stack([synth.kv_rows(w, b, kv, 64, 64 + n)[1] for kv in range(w.n_kv_heads)], 1)
+        j = np.arange(n)
+        _demote_all(c, w, b, table[b, j // 64], j % 64, ks, vs)
+    s = oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max()))
+    c.set_splits(s)
+    got = c.decode_fused(queries(w), w.sm_scale).cpu().numpy()
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
+    for b, kv in FULL_SAMPLES_CB[cfg]:
+        say("codebook full size sample", w.name, "b", b, "kv", kv, "splits", s)
+        hk, hv = synth.history_rows(w, b, kv)
+        ref, km, vm = oracle_history_cb(hk, hv, rk[kv], rv[kv], w.clip_ratio, klv[kv], vlv[kv])
+        gpu = opages.unpack_history(pool, table[b], kv, w.hist_len(b))
+        compare_history(gpu, ref, km, vm, f"{w.name} codebook b{b} kv{kv}")
+        q = synth.query(w, b).astype(np.float64)
+        wk, wv = windows(w, b)
+        for h in range(kv * w.gq, (kv + 1) * w.gq):
+            r = oatt.decode_head(q[h], rk[kv], rv[kv], wk[kv], wv[kv], ref, w.sm_scale, codebook=(klv[kv], vlv[kv]))
+            assert_close(got[b, h], r, f"{w.name} codebook b{b} h{h}")
