@@ -101,6 +101,18 @@ def measured_traffic(workload, kernel="attend"):
     return int(round(f + wr))
 
 
+def timed_once(fn, stream, torch):
+    """Milliseconds of one call of fn, with HIP events on `stream`."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop)
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -338,6 +350,23 @@ def main():
     # instance's workspace holds its prepared query and window partials from the warm-up)
     ms = timed(step, args.steps)
     attend_ms = timed(attend, args.steps)
+    # spread: five more timed regions of each, the same way (the reported figures stay the
+    # first region's)
+    rep_step = sorted([ms] + [timed(step, args.steps) for _ in range(5)])
+    rep_attend = sorted([attend_ms] + [timed(attend, args.steps) for _ in range(5)])
+
+    def pct(v):
+        return [round(float(np.percentile(v, p)) * 1e3, 3) for p in (10, 50, 90)]
+
+    # measured stream ceiling of this machine: the library's read probe over 1 GiB, best of five
+    from bit_kv_cache_oscar_amd import oscar_read_probe
+
+    probe = torch.ones(2 ** 28, dtype=torch.int32, device=dev)
+    probe_out = torch.zeros(4096, dtype=torch.int32, device=dev)
+    oscar_read_probe(probe, probe_out, stream)
+    ceil_ms = min(timed_once(lambda: oscar_read_probe(probe, probe_out, stream), stream, torch) for _ in range(5))
+    del probe, probe_out
+    ceiling_gbs = 2 ** 30 / (ceil_ms * 1e-3) / 1e9
 
     # timed region 3, the multi-query row: T query tokens per request over the same pools
     # (speculative verification reading the compressed prefix), oscar_decode_multi back to
@@ -461,7 +490,12 @@ def main():
             "traffic": measured_traffic(w.name),
             "us_per_launch": round(attend_ms * 1e3, 3),
             "bytes_per_launch": attend_bytes,
+            "us_per_launch_p10_p50_p90": pct(rep_attend),
+            "frac_of_measured_ceiling": round(attend_bytes / (attend_ms * 1e-3) / 1e9 / ceiling_gbs, 4),
         },
+        "us_per_step_p10_p50_p90": pct(rep_step),
+        "stream_ceiling": {"probe": "oscar_read_probe over 1 GiB (streaming 16-byte loads), best of 5",
+                           "gbs": round(ceiling_gbs, 1), "frac_of_peak": round(ceiling_gbs / HBM_PEAK_GBS, 4)},
     }
     if multi is not None:
         out["multi_query"] = multi

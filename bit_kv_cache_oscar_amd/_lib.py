@@ -78,6 +78,8 @@ _SIGNATURES = {
                                 c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     "oscar_attend": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
                                c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "oscar_read_probe_words": (c_int32, []),
+    "oscar_read_probe": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     # Lloyd-Max codebook variants: the entry point without the suffix with `codebook`
     # inserted before the pool
     "oscar_demote_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
@@ -281,6 +283,18 @@ def oscar_decode_bf16(desc: LayerDesc, q, k_win, v_win, win_len, sm_scale: float
     nbytes = win_partials.numel() * win_partials.element_size()
     _check(lib().oscar_decode_bf16(byref(desc), _ptr(q), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch,
                                    float(sm_scale), _ptr(win_partials), nbytes, _stream(stream)))
+
+
+def oscar_read_probe(buf, out, stream=None):
+    """Streaming read of the whole device tensor buf (a measurement helper); out: int32 device
+    tensor of at least oscar_read_probe_words() entries."""
+    import torch
+
+    nbytes = buf.numel() * buf.element_size()
+    _need(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous device tensor")
+    _need(out.is_cuda and out.dtype == torch.int32 and out.numel() >= lib().oscar_read_probe_words(),
+          "out must be an int32 device tensor of oscar_read_probe_words() entries")
+    _check(lib().oscar_read_probe(_ptr(buf), nbytes, _ptr(out), _stream(stream)))
 
 
 def oscar_merge(desc: LayerDesc, partials, n_splits: int, win_partials, rot_v, out, stream=None):

@@ -112,6 +112,11 @@ struct StepArgs {
 hipError_t launch_prepare(StepArgs a, hipStream_t stream);
 hipError_t launch_attend(StepArgs a, hipStream_t stream);
 
+// Read-bandwidth probe: reads bytes / 16 16-byte words of buf, writes read_probe_blocks()
+// words to out.
+int read_probe_blocks();
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
+
 hipError_t launch_merge(const LayerShape& L, const PartialsView& hist, int n_splits,
                         const PartialsView& win, int n_win_splits, const void* rot_v, float* out,
                         int batch, hipStream_t stream);

@@ -518,6 +518,15 @@ int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t 
   return hip_status(oscar::launch_attend(a, s), "attend launch");
 }
 
+int32_t oscar_read_probe_words(void) { return oscar::read_probe_blocks(); }
+
+int32_t oscar_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "buf and bytes must be multiples of 16");
+  return hip_status(oscar::launch_read_probe(buf, bytes, out, static_cast<hipStream_t>(stream)), "probe launch");
+}
+
 int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t n_splits, const void* win_partials,
                     const void* rot_v, float* out, int32_t batch, void* stream) {
   int32_t st = check_desc_impl(desc);

@@ -297,6 +297,16 @@ int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void
                      size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * oscar_read_probe: a measurement helper, not part of the method: reads `bytes` bytes of
+ * device memory at `buf` (both multiples of 16) with a streaming kernel and writes
+ * oscar_read_probe_words() uint32 words (an XOR of what was read) to `out`. Its time over a
+ * buffer much larger than the last-level cache is the box's measured read ceiling, against
+ * which the decode kernels' achieved bandwidth is also reported.
+ */
+int32_t oscar_read_probe_words(void);
+int32_t oscar_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
+/*
  * Lloyd-Max codebook variant (QbitAI article on OSCAR, section comparing OSCAR with
  * TurboQuant: the code release pairs the attention-aware rotation with a Lloyd-Max
  * codebook in place of the uniform INT2 levels; the article gives nothing beyond that
