@@ -37,6 +37,7 @@ from ._lib import (  # noqa: F401
     oscar_partials_bytes,
     oscar_prepare,
     oscar_prepare_codebook,
+    oscar_read_probe,
     oscar_status_string,
     oscar_version,
     oscar_window_splits,
