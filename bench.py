@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "INT2 decode attention µs/step + achieved HBM GB/s (% of peak) at 32K–128K ctx"
 HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CUs x 4 SIMDs x 64 lanes x 2 (FMA) x 2 (dual issue) x 2.4 GHz
 HIST_BYTES = 72          # per history token per KV head: 2 x 32 B codes + 2 x (fp16 s, fp16 z)
 WIN_BYTES = 512          # per BF16 window token per KV head (K + V)
 ROT_BYTES = 128 * 128 * 2
@@ -449,6 +450,44 @@ def main():
         }
         del fill_rows
 
+    # the calibration row: the covariances behind R_K and R_V (oscar_calib_covariances) from
+    # the workload's 512-token calibration sequence of every KV head
+    calib_row = None
+    if w.calib != "gram":
+        from bit_kv_cache_oscar_amd import oscar_calib_covariances, oscar_calib_workspace_bytes
+
+        cal = [synth.calibration_set(w, kv) for kv in range(w.n_kv_heads)]
+        n_cal = cal[0][1].shape[0]
+        qc = torch.from_numpy(np.concatenate([c[0] for c in cal], axis=1)).to(dev).to(torch.bfloat16)
+        kc = torch.from_numpy(np.stack([c[1] for c in cal], axis=1)).to(dev).to(torch.bfloat16)
+        vc = torch.from_numpy(np.stack([c[2] for c in cal], axis=1)).to(dev).to(torch.bfloat16)
+        wsc = torch.empty(oscar_calib_workspace_bytes(base.desc, n_cal), dtype=torch.uint8, device=dev)
+        sig_k = torch.empty((w.n_kv_heads, 128, 128), dtype=torch.float32, device=dev)
+        sig_v = torch.empty_like(sig_k)
+
+        def calib():
+            oscar_calib_covariances(base.desc, qc, kc, vc, w.sm_scale, wsc, sig_k, sig_v, stream)
+
+        calib()
+        reps = 20
+        cal_ms = timed_once(lambda: [calib() for _ in range(reps)], stream, torch) / reps
+        rows = n_cal * w.n_q_heads
+        gram_flops = 2 * 2 * rows * 128 * 128             # the key and value Gram sums
+        attn_flops = 2 * 2 * w.n_q_heads * (n_cal * (n_cal + 1) // 2) * 128   # S_h V, causal
+        tflops = (gram_flops + attn_flops) / (cal_ms * 1e-3) / 1e12
+        calib_row = {
+            "entry": "oscar_calib_covariances (Sigma_K = sum Q^T Q, Sigma_V = sum (S V)^T (S V))",
+            "tokens": n_cal,
+            "us": round(cal_ms * 1e3, 3),
+            "bound": "alu",
+            "gram_flops": gram_flops,
+            "attn_flops": attn_flops,
+            "achieved": round(tflops, 3),
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
+        }
+
     out = {
         "metric": METRIC,
         "value": round(total_bytes / (ms * 1e-3) / 1e9, 2),
@@ -501,6 +540,8 @@ def main():
         out["multi_query"] = multi
     if cb_row is not None:
         out["codebook"] = cb_row
+    if calib_row is not None:
+        out["calibration"] = calib_row
     if args.config == 5:
         # the bulk-demotion row of this workload (after the decode timing: it allocates)
         out["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5))

@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     lib,
     oscar_attend,
     oscar_attend_codebook,
+    oscar_calib_covariances,
+    oscar_calib_workspace_bytes,
     oscar_check_desc,
     oscar_decode,
     oscar_decode_codebook,

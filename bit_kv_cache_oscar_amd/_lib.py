@@ -78,6 +78,9 @@ _SIGNATURES = {
                                 c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     "oscar_attend": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
                                c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "oscar_calib_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32]),
+    "oscar_calib_covariances": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                          c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
     "oscar_read_probe_words": (c_int32, []),
     "oscar_read_probe": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
     # Lloyd-Max codebook variants: the entry point without the suffix with `codebook`
@@ -283,6 +286,31 @@ def oscar_decode_bf16(desc: LayerDesc, q, k_win, v_win, win_len, sm_scale: float
     nbytes = win_partials.numel() * win_partials.element_size()
     _check(lib().oscar_decode_bf16(byref(desc), _ptr(q), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch,
                                    float(sm_scale), _ptr(win_partials), nbytes, _stream(stream)))
+
+
+def oscar_calib_workspace_bytes(desc: LayerDesc, n_tokens: int) -> int:
+    return int(lib().oscar_calib_workspace_bytes(byref(desc), int(n_tokens)))
+
+
+def oscar_calib_covariances(desc: LayerDesc, q, k, v, sm_scale: float, workspace, sigma_k, sigma_v, stream=None):
+    """Calibration covariances of one sequence: q [T, Hq, 128], k and v [T, Hkv, 128] bf16;
+    sigma_k, sigma_v float32 [Hkv, 128, 128] outputs; workspace from
+    oscar_calib_workspace_bytes(desc, T)."""
+    import torch
+
+    n_tok = int(q.shape[0])
+    _device16(q, "q")
+    _need(q.numel() == n_tok * desc.n_q_heads * HEAD_DIM, "q must be [T, n_q_heads, 128]")
+    for t, name in ((k, "k"), (v, "v")):
+        _device16(t, name)
+        _need(t.numel() == n_tok * desc.n_kv_heads * HEAD_DIM, f"{name} must be [T, n_kv_heads, 128]")
+    for t, name in ((sigma_k, "sigma_k"), (sigma_v, "sigma_v")):
+        _need(t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()
+              and t.numel() == desc.n_kv_heads * HEAD_DIM * HEAD_DIM, f"{name} must be float32 [n_kv_heads, 128, 128]")
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    _check(lib().oscar_calib_covariances(byref(desc), _ptr(q), _ptr(k), _ptr(v), n_tok, float(sm_scale),
+                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _ptr(sigma_k), _ptr(sigma_v), _stream(stream)))
 
 
 def oscar_read_probe(buf, out, stream=None):

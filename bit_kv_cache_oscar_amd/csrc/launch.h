@@ -112,6 +112,12 @@ struct StepArgs {
 hipError_t launch_prepare(StepArgs a, hipStream_t stream);
 hipError_t launch_attend(StepArgs a, hipStream_t stream);
 
+// Calibration covariances: Sigma_K and Sigma_V [n_kv][128][128] fp32 of one calibration
+// sequence of T tokens (q [T][n_q][128], k and v [T][n_kv][128] bf16); o_work holds
+// T n_q 128 floats (the attention outputs).
+hipError_t launch_calib(const LayerShape& L, const void* q, const void* k, const void* v, int T, float sm_scale,
+                        float* o_work, float* sigma_k, float* sigma_v, hipStream_t stream);
+
 // Read-bandwidth probe: reads bytes / 16 16-byte words of buf, writes read_probe_blocks()
 // words to out.
 int read_probe_blocks();

@@ -518,6 +518,30 @@ int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t 
   return hip_status(oscar::launch_attend(a, s), "attend launch");
 }
 
+size_t oscar_calib_workspace_bytes(const oscar_layer_desc* desc, int32_t n_tokens) {
+  if (check_desc_impl(desc) != OSCAR_OK || n_tokens < 0) return 0;
+  return static_cast<size_t>(n_tokens) * desc->n_q_heads * 128 * sizeof(float);
+}
+
+int32_t oscar_calib_covariances(const oscar_layer_desc* desc, const void* q, const void* k, const void* v,
+                                int32_t n_tokens, float sm_scale, void* workspace, size_t workspace_bytes,
+                                float* sigma_k, float* sigma_v, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (n_tokens <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_tokens %d <= 0", n_tokens);
+  if (n_tokens > 65536) return fail(OSCAR_ERR_UNSUPPORTED, "n_tokens %d > 65536", n_tokens);
+  if (!q || !k || !v || !workspace || !sigma_k || !sigma_v) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const size_t need = oscar_calib_workspace_bytes(desc, n_tokens);
+  if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(k) % 16 ||
+      reinterpret_cast<uintptr_t>(v) % 16 || reinterpret_cast<uintptr_t>(workspace) % 16)
+    return fail(OSCAR_ERR_INVALID_ARG, "q, k, v and workspace must be 16-byte aligned");
+  return hip_status(oscar::launch_calib(shape_of(desc), q, k, v, n_tokens, sm_scale, static_cast<float*>(workspace),
+                                        sigma_k, sigma_v, static_cast<hipStream_t>(stream)),
+                    "calibration launch");
+}
+
 int32_t oscar_read_probe_words(void) { return oscar::read_probe_blocks(); }
 
 int32_t oscar_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {

@@ -297,6 +297,33 @@ int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void
                      size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * oscar_calib_covariances: the offline calibration statistics of one layer, from one
+ * calibration sequence of n_tokens tokens, on the GPU.
+ * (QbitAI article on OSCAR, section on aiming the rotation at attention: the key rotation's
+ * U comes from the eigenvectors of the query covariance Q^T Q, the value rotation's from the
+ * score-weighted value covariance V^T S^T S V, S the attention scores; both are estimated
+ * offline on calibration data.)
+ *
+ * For each KV head kv, with G = n_q_heads / n_kv_heads and the query heads h of its group:
+ *   sigma_k[kv] = sum_h sum_t q[t, h]^T q[t, h]
+ *   sigma_v[kv] = sum_h (S_h V)^T (S_h V),  S_h[t, u] = softmax over u <= t of
+ *                 sm_scale * q[t, h] . k[u, kv]  (causal), V = v[:, kv]
+ * in fp32 (products of the bf16 inputs are exact; sums in fp32; exp in fp32).
+ *   q          bf16 [n_tokens][n_q_heads][128]
+ *   k, v       bf16 [n_tokens][n_kv_heads][128]
+ *   workspace  at least oscar_calib_workspace_bytes(desc, n_tokens) bytes (the attention
+ *              outputs S_h V, fp32); q, k, v and workspace 16-byte aligned
+ *   sigma_k, sigma_v  float32 [n_kv_heads][128][128], written (exactly symmetric)
+ *   n_tokens   1..65536 (OSCAR_ERR_UNSUPPORTED above)
+ * The eigendecomposition that turns sigma into U, and R = U * H * P, is host work on
+ * 128 x 128 matrices (not done here).
+ */
+size_t oscar_calib_workspace_bytes(const oscar_layer_desc* desc, int32_t n_tokens);
+int32_t oscar_calib_covariances(const oscar_layer_desc* desc, const void* q, const void* k, const void* v,
+                                int32_t n_tokens, float sm_scale, void* workspace, size_t workspace_bytes,
+                                float* sigma_k, float* sigma_v, void* stream);
+
+/*
  * oscar_read_probe: a measurement helper, not part of the method: reads `bytes` bytes of
  * device memory at `buf` (both multiples of 16) with a streaming kernel and writes
  * oscar_read_probe_words() uint32 words (an XOR of what was read) to `out`. Its time over a

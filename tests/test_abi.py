@@ -249,3 +249,28 @@ def test_codebook_entry_points_check_the_codebook_first(lib):
                 FAKE, need, None) == L.OSCAR_ERR_INVALID_ARG
     assert prep(d, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0.08, 4,
                 FAKE, need - 1, None) == L.OSCAR_ERR_WORKSPACE
+
+
+def test_calib_argument_checks(lib):
+    desc = L.layer_desc(32, 8)
+    d = ctypes.byref(desc)
+    f = lib.oscar_calib_covariances
+    need = L.oscar_calib_workspace_bytes(desc, 512)
+    assert need == 512 * 32 * 128 * 4
+    #         q, k, v, T, sm_scale, workspace, bytes, sigma_k, sigma_v, stream
+    args = [FAKE, FAKE, FAKE, 512, 0.088, FAKE, need, FAKE, FAKE, None]
+
+    def call(over):
+        a = list(args)
+        for k, v in over.items():
+            a[k] = v
+        return f(d, *a)
+
+    assert call({6: need - 1}) == L.OSCAR_ERR_WORKSPACE
+    assert call({3: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({3: 65537}) == L.OSCAR_ERR_UNSUPPORTED
+    assert call({4: 0.0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({0: None}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({8: None}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({1: FAKE + 8}) == L.OSCAR_ERR_INVALID_ARG   # misaligned
+    assert L.oscar_calib_workspace_bytes(desc, -1) == 0
