@@ -17,7 +17,9 @@ oscar_attend launches; `multi_query` times oscar_decode_multi (T query tokens pe
 over the same pools, as in speculative verification) the same way; `codebook` times the
 Lloyd-Max codebook variant (the same history demoted against per-head codebooks fitted on
 the calibration set, then oscar_decode_step_codebook and oscar_attend_codebook) the same
-way; `cpu_baseline` is the CPU oracle timed on a bounded sample of the same workload.
+way; `calibration` times the GPU calibration covariances; `bf16_baseline` times plain BF16
+decode over the same context held uncompressed; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -488,6 +490,42 @@ def main():
             "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4),
         }
 
+    # the uncompressed baseline: plain BF16 decode attention over the same context held dense
+    # (oscar_decode_dense_bf16), on instances cycled as above; the MI355X counterpart of the
+    # pages' INT2-versus-BF16 decode comparison (context, not a target). Its cost does not
+    # depend on the values: random bf16 rows.
+    from bit_kv_cache_oscar_amd import oscar_decode_dense_bf16, oscar_dense_workspace_bytes
+
+    cap = -(-int(max(w.ctx_lens)) // 64) * 64
+    dense_bytes = 2 * w.batch * w.n_kv_heads * cap * 128 * 2
+    n_dense = max(1, min(4, -(-512 * 2 ** 20 // dense_bytes)))
+    lens_t = torch.tensor(list(w.ctx_lens), dtype=torch.int32, device=dev)
+    dense = [(torch.randn((w.batch, w.n_kv_heads, cap, 128), device=dev).to(torch.bfloat16),
+              torch.randn((w.batch, w.n_kv_heads, cap, 128), device=dev).to(torch.bfloat16)) for _ in range(n_dense)]
+    ws_d = torch.empty(oscar_dense_workspace_bytes(base.desc, w.batch, cap), dtype=torch.uint8, device=dev)
+    out_d = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+
+    def dense_call(i):
+        kd, vd = dense[i % n_dense]
+        oscar_decode_dense_bf16(base.desc, q, kd, vd, lens_t, w.sm_scale, ws_d, out_d, stream)
+
+    for i in range(max(2, args.warmup)):
+        dense_call(i)
+    dense_ms = timed_once(lambda: [dense_call(i) for i in range(args.steps)], stream, torch) / args.steps
+    dense_alg = int(sum(w.ctx_lens)) * w.n_kv_heads * WIN_BYTES + w.batch * w.n_q_heads * 128 * (2 + 4)
+    dense_row = {
+        "entry": "oscar_decode_dense_bf16 (BF16 K/V of the whole context, no compression)",
+        "us_per_call": round(dense_ms * 1e3, 3),
+        "achieved": round(dense_alg / (dense_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "frac": round(dense_alg / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "bytes_per_call": dense_alg,
+        "int2_step_speedup": round(dense_ms / ms, 3),
+        "int2_attend_speedup": round(dense_ms / attend_ms, 3),
+        "kv_bytes_ratio": round(dense_alg / max(total_bytes, 1), 3),
+    }
+    del dense, ws_d, out_d
+
     out = {
         "metric": METRIC,
         "value": round(total_bytes / (ms * 1e-3) / 1e9, 2),
@@ -542,6 +580,7 @@ def main():
         out["codebook"] = cb_row
     if calib_row is not None:
         out["calibration"] = calib_row
+    out["bf16_baseline"] = dense_row
     if args.config == 5:
         # the bulk-demotion row of this workload (after the decode timing: it allocates)
         out["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5))

@@ -24,6 +24,8 @@ from ._lib import (  # noqa: F401
     oscar_check_desc,
     oscar_decode,
     oscar_decode_codebook,
+    oscar_decode_dense_bf16,
+    oscar_dense_workspace_bytes,
     oscar_decode_multi,
     oscar_decode_bf16,
     oscar_decode_int2,

@@ -78,6 +78,9 @@ _SIGNATURES = {
                                 c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     "oscar_attend": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_int32,
                                c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "oscar_dense_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_decode_dense_bf16": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                          c_int32, c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
     "oscar_calib_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32]),
     "oscar_calib_covariances": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_int32, c_float,
                                           c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
@@ -286,6 +289,33 @@ def oscar_decode_bf16(desc: LayerDesc, q, k_win, v_win, win_len, sm_scale: float
     nbytes = win_partials.numel() * win_partials.element_size()
     _check(lib().oscar_decode_bf16(byref(desc), _ptr(q), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch,
                                    float(sm_scale), _ptr(win_partials), nbytes, _stream(stream)))
+
+
+def oscar_dense_workspace_bytes(desc: LayerDesc, batch: int, capacity: int) -> int:
+    return int(lib().oscar_dense_workspace_bytes(byref(desc), int(batch), int(capacity)))
+
+
+def oscar_decode_dense_bf16(desc: LayerDesc, q, k, v, lens, sm_scale: float, workspace, out, stream=None):
+    """Plain BF16 decode over a dense KV buffer (the uncompressed baseline): q [B, Hq, 128],
+    k and v [B, Hkv, capacity, 128] bf16, lens int32 [B]; out [B, Hq, 128] float32."""
+    import torch
+
+    batch = int(q.shape[0])
+    _device16(q, "q")
+    _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
+    _need(k.dim() == 4 and k.shape[0] == batch and k.shape[1] == desc.n_kv_heads and k.shape[3] == HEAD_DIM,
+          "k must be [batch, n_kv_heads, capacity, 128]")
+    cap = int(k.shape[2])
+    for t, name in ((k, "k"), (v, "v")):
+        _device16(t, name)
+        _need(tuple(t.shape) == tuple(k.shape), f"{name} must be [batch, n_kv_heads, capacity, 128]")
+    _device_i32(lens, "lens", batch)
+    _need(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    _need(out.is_cuda and out.dtype == torch.float32 and out.is_contiguous()
+          and out.numel() == batch * desc.n_q_heads * HEAD_DIM, "out must be float32 [batch, n_q_heads, 128]")
+    _check(lib().oscar_decode_dense_bf16(byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), cap, batch,
+                                         float(sm_scale), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
 
 
 def oscar_calib_workspace_bytes(desc: LayerDesc, n_tokens: int) -> int:

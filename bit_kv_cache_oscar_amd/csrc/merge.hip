@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const int kv = h / GQ;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  {
+  if (n_splits > 0) {  // (no INT2 partials: no rotated sum to un-rotate, R_V is not read)
     // R_V into LDS rows padded to an odd dword stride (conflict-free row reads below)
     const uint4* src = reinterpret_cast<const uint4*>(rot_v + static_cast<size_t>(kv) * kHeadDim * kHeadDim);
 #pragma unroll
@@ -86,8 +86,10 @@ __global__ __launch_bounds__(256) void merge_kernel(
   if (tid < 128) {
     float oh = 0.f;
     const uint16_t* r = r_s + tid * kRowPad;
+    if (n_splits > 0) {
 #pragma unroll 8
-    for (int j = 0; j < kHeadDim; ++j) oh = fmaf(accr_s[j], bf16_to_f32(r[j]), oh);
+      for (int j = 0; j < kHeadDim; ++j) oh = fmaf(accr_s[j], bf16_to_f32(r[j]), oh);
+    }
     const float big = fmaxf(mh, mw);
     float res = 0.f;
     if (big != -INFINITY) {

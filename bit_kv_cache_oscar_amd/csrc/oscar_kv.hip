@@ -276,6 +276,35 @@ int32_t oscar_decode_bf16(const oscar_layer_desc* desc, const void* q, const voi
                     "decode_bf16 launch");
 }
 
+size_t oscar_dense_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t capacity) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch < 0 || capacity < 0 || capacity % 64 != 0) return 0;
+  return oscar::partials_bytes(batch, desc->n_q_heads, capacity / 64);
+}
+
+int32_t oscar_decode_dense_bf16(const oscar_layer_desc* desc, const void* q, const void* k, const void* v,
+                                const int32_t* len, int32_t capacity, int32_t batch, float sm_scale, void* workspace,
+                                size_t workspace_bytes, float* out, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (capacity <= 0 || capacity % 64 != 0) return fail(OSCAR_ERR_INVALID_ARG, "capacity %d not a positive multiple of 64", capacity);
+  if (capacity / 64 > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "capacity %d > 64 * 65535", capacity);
+  if (!q || !k || !v || !len || !workspace || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const int splits = capacity / 64;
+  const size_t need = oscar::partials_bytes(batch, desc->n_q_heads, splits);
+  if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  oscar::LayerShape L = shape_of(desc);
+  L.window = capacity;  // the window pass's buffer layout, over the whole dense context
+  const oscar::PartialsView pv = oscar::partials_view(workspace, batch, desc->n_q_heads, splits);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(oscar::launch_decode_bf16(L, q, k, v, len, batch, sm_scale, splits, pv, s), "dense pass launch");
+  if (st != OSCAR_OK) return st;
+  // no INT2 partials: the merge reduces the dense splits and normalises
+  return hip_status(oscar::launch_merge(L, pv, 0, pv, splits, nullptr, out, batch, s), "dense merge launch");
+}
+
 size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
   if (check_desc_impl(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
   return oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits, window_splits_of(desc));

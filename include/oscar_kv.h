@@ -297,6 +297,24 @@ int32_t oscar_attend(const oscar_layer_desc* desc, const void* rot_v, const void
                      size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * oscar_decode_dense_bf16: plain BF16 decode attention over a dense, uncompressed KV buffer:
+ * the baseline the INT2 path is measured against (the pages compare OSCAR's decode speed with
+ * a BF16 cache at the same context: QbitAI article on OSCAR, system section). Not part of the
+ * OSCAR path; it runs the BF16 window pass's device code over the whole context in splits of
+ * 64 tokens, then the merge with no INT2 part.
+ *   q         bf16 [batch][n_q_heads][128]
+ *   k, v      bf16 [batch][n_kv_heads][capacity][128]; request b's tokens at [0, len[b])
+ *   len       int32 [batch], 0..capacity (device)
+ *   capacity  a positive multiple of 64, at most 64 * 65535
+ *   workspace at least oscar_dense_workspace_bytes(desc, batch, capacity) bytes
+ *   out       float32 [batch][n_q_heads][128] = softmax(sm_scale q k^T) v per query head
+ */
+size_t oscar_dense_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t capacity);
+int32_t oscar_decode_dense_bf16(const oscar_layer_desc* desc, const void* q, const void* k, const void* v,
+                                const int32_t* len, int32_t capacity, int32_t batch, float sm_scale, void* workspace,
+                                size_t workspace_bytes, float* out, void* stream);
+
+/*
  * oscar_calib_covariances: the offline calibration statistics of one layer, from one
  * calibration sequence of n_tokens tokens, on the GPU.
  * (QbitAI article on OSCAR, section on aiming the rotation at attention: the key rotation's

@@ -274,3 +274,28 @@ def test_calib_argument_checks(lib):
     assert call({8: None}) == L.OSCAR_ERR_INVALID_ARG
     assert call({1: FAKE + 8}) == L.OSCAR_ERR_INVALID_ARG   # misaligned
     assert L.oscar_calib_workspace_bytes(desc, -1) == 0
+
+
+def test_dense_bf16_argument_checks(lib):
+    desc = L.layer_desc(32, 8)
+    d = ctypes.byref(desc)
+    f = lib.oscar_decode_dense_bf16
+    need = L.oscar_dense_workspace_bytes(desc, 2, 4096)
+    assert need == L.oscar_partials_bytes(desc, 2, 64)
+    assert L.oscar_dense_workspace_bytes(desc, 2, 4000) == 0   # not a multiple of 64
+    #         q, k, v, len, capacity, batch, sm_scale, workspace, bytes, out, stream
+    args = [FAKE, FAKE, FAKE, FAKE, 4096, 2, 0.088, FAKE, need, FAKE, None]
+
+    def call(over):
+        a = list(args)
+        for k, v in over.items():
+            a[k] = v
+        return f(d, *a)
+
+    assert call({8: need - 1}) == L.OSCAR_ERR_WORKSPACE
+    assert call({4: 4000}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({4: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({4: 64 * 65536}) == L.OSCAR_ERR_UNSUPPORTED
+    assert call({5: 0}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({3: None}) == L.OSCAR_ERR_INVALID_ARG
+    assert call({6: -1.0}) == L.OSCAR_ERR_INVALID_ARG
