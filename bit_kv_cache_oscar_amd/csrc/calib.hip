@@ -9,9 +9,9 @@
 // Two launches per layer:
 //  1. attention outputs O_h = S_h V for every query head h, S_h the causal softmax of
 //     sm_scale q_h k^T over the calibration sequence, in fp32 on the vector ALU: a workgroup
-//     takes 16 query tokens of one head, 16 lanes per token with 8 dims each (bf16 products
-//     are exact in fp32); keys and values pass through LDS in tiles of 64 and are walked in
-//     order with an online softmax in log2 units;
+//     takes 16 query tokens of one head; keys and values pass through LDS in tiles of 64,
+//     each thread scoring four keys (bf16 products are exact in fp32), with an online softmax
+//     in log2 units whose maximum moves once per tile;
 //  2. Gram sums Sigma[kv] = sum over (token t, query head h of the group) of x^T x, with
 //     x = q[t, h] for the keys and x = O_h[t] for the values, on v_mfma_f32_16x16x4_f32: one
 //     workgroup per 16x16 output tile, its four waves summing quarters of the rows in a fixed
@@ -37,39 +37,41 @@ __device__ __forceinline__ void bf16x8_to_f32(const uint4& w, float* out) {
   }
 }
 
-// grid (ceil(T / 16), Hq), 256 threads: thread (r, c) = (tid / 16, tid % 16) holds dims
-// 8c..8c+7 of query token 16 blockIdx.x + r of head blockIdx.y. Keys and values come in
-// tiles of 64 tokens staged in LDS (one round of loads per tile, the next tile's loads
-// issued before the current tile is used).
+// grid (ceil(T / 16), Hq), 256 threads, for 16 query tokens of head blockIdx.y. Keys and
+// values pass through LDS in tiles of 64 (rows padded to 17 16-byte chunks, so the 16 rows a
+// score step reads lie in distinct banks); the next tile's loads are issued before the current
+// tile is used. Per tile, thread (token, k) = (tid / 16, tid % 16):
+//   scores of keys k, k + 16, k + 32, k + 48 (four independent 128-term fp32 dot products);
+//   the token's running maximum and sum move once per tile (16-lane reductions);
+//   its weights go to LDS, and the thread then adds the tile's weighted values of dims
+//   8k .. 8k + 7 to its running sums.
 __global__ __launch_bounds__(256) void calib_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, int T, int n_q, int n_kv,
                                                          int gq, float scale_log2, float* __restrict__ out) {
-  __shared__ uint4 kv_s[2][kKeyTile][kHeadDim / 8];  // [K, V][key][16-byte chunk]
-  const int r = threadIdx.x >> 4;
-  const int c = threadIdx.x & 15;
+  constexpr int kRow = kHeadDim / 8 + 1;  // 16-byte chunks per padded LDS row
+  __shared__ uint4 k_s[kKeyTile][kRow];
+  __shared__ uint4 v_s[kKeyTile][kRow];
+  __shared__ uint4 q_s[kTileTokens][kRow];
+  __shared__ float p_s[kTileTokens][kKeyTile];
+  const int r = threadIdx.x >> 4;  // token of the tile (score and value steps alike)
+  const int c = threadIdx.x & 15;  // key offset (scores), 16-byte chunk of dims (values)
   const int h = blockIdx.y;
   const int kv = h / gq;
   const int t = blockIdx.x * kTileTokens + r;
   const bool valid = t < T;
-  float qd[8];
-  {
-    uint4 w = {0u, 0u, 0u, 0u};
-    if (valid) w = *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(t) * n_q + h) * kHeadDim + 8 * c);
-    bf16x8_to_f32(w, qd);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qd[i] *= scale_log2;  // scores in log2 units
-  }
+  q_s[r][c] = valid ? *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(t) * n_q + h) * kHeadDim + 8 * c)
+                    : make_uint4(0u, 0u, 0u, 0u);
   // keys 0 .. u_end - 1 cover every token of the tile (causal)
   const int u_end = min(T, static_cast<int>(blockIdx.x) * kTileTokens + kTileTokens);
   const size_t row_stride = static_cast<size_t>(n_kv) * kHeadDim;
   // loader role: thread (r, c) moves chunk c of keys r + 16 i, i < 4, of K and V
   const uint16_t* kbase = k + static_cast<size_t>(kv) * kHeadDim + 8 * c;
   const uint16_t* vbase = v + static_cast<size_t>(kv) * kHeadDim + 8 * c;
-  uint4 lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3;  // the next tile's rows r, r + 16, r + 32, r + 48
+  uint4 lk0, lk1, lk2, lk3, lv0, lv1, lv2, lv3;
 #define CALIB_FETCH(U0)                                                                           \
   do {                                                                                           \
     const int ub = (U0) + r;                                                                     \
-    /* past the end: the last key again, masked in the loop */                                   \
+    /* past the end: the last key again, masked below */                                         \
     lk0 = *reinterpret_cast<const uint4*>(kbase + min(ub, u_end - 1) * row_stride);              \
     lk1 = *reinterpret_cast<const uint4*>(kbase + min(ub + 16, u_end - 1) * row_stride);         \
     lk2 = *reinterpret_cast<const uint4*>(kbase + min(ub + 32, u_end - 1) * row_stride);         \
@@ -79,64 +81,68 @@ __global__ __launch_bounds__(256) void calib_attn_kernel(const uint16_t* __restr
     lv2 = *reinterpret_cast<const uint4*>(vbase + min(ub + 32, u_end - 1) * row_stride);         \
     lv3 = *reinterpret_cast<const uint4*>(vbase + min(ub + 48, u_end - 1) * row_stride);         \
   } while (0)
+  static_assert(kKeyTile == 64 && kTileTokens == 16, "four keys per thread and tile, 16 tokens");
   float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  static_assert(kKeyTile == 64, "four rows per thread and tile");
   CALIB_FETCH(0);
   for (int u0 = 0; u0 < u_end; u0 += kKeyTile) {
-    __syncthreads();  // the previous tile is no longer read
-    kv_s[0][r][c] = lk0;
-    kv_s[0][r + 16][c] = lk1;
-    kv_s[0][r + 32][c] = lk2;
-    kv_s[0][r + 48][c] = lk3;
-    kv_s[1][r][c] = lv0;
-    kv_s[1][r + 16][c] = lv1;
-    kv_s[1][r + 32][c] = lv2;
-    kv_s[1][r + 48][c] = lv3;
+    __syncthreads();  // the previous tile (and its weights) are no longer read
+    k_s[r][c] = lk0;
+    k_s[r + 16][c] = lk1;
+    k_s[r + 32][c] = lk2;
+    k_s[r + 48][c] = lk3;
+    v_s[r][c] = lv0;
+    v_s[r + 16][c] = lv1;
+    v_s[r + 32][c] = lv2;
+    v_s[r + 48][c] = lv3;
     __syncthreads();
     if (u0 + kKeyTile < u_end) CALIB_FETCH(u0 + kKeyTile);  // uniform: in flight during this tile
+    // scores of keys c + 16 j (bf16 products exact in fp32)
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int ch = 0; ch < kHeadDim / 8; ++ch) {
+      float qf[8];
+      bf16x8_to_f32(q_s[r][ch], qf);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float kf[8];
+        bf16x8_to_f32(k_s[c + 16 * j][ch], kf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[j] = fmaf(qf[i], kf[i], sc[j]);
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = u0 + c + 16 * j;
+      // causal mask and the end of the keys; tokens past T take key 0 only (never stored)
+      const bool keep = u < u_end && (valid ? (u <= t) : (u == 0));
+      sc[j] = keep ? sc[j] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, sc[j]);
+    }
+    const float m_new = fmaxf(m, row16_max(tmax));  // finite: every token keeps key 0
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float p = __builtin_amdgcn_exp2f(sc[j] - m_new);
+      p_s[r][c + 16 * j] = p;
+      ps += p;
+    }
+    l = fmaf(l, alpha, row16_sum(ps));
+    m = m_new;
+    __syncthreads();  // the token's weights are in LDS
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
     const int n_keys = min(kKeyTile, u_end - u0);
-    // eight keys at a time: their scores are independent, and the running maximum and the
-    // rescaling of the sums move once per eight keys
-    for (int jb = 0; jb < n_keys; jb += 8) {
-      float sc[8];
+#pragma unroll 4
+    for (int j = 0; j < n_keys; ++j) {
+      float vf[8];
+      bf16x8_to_f32(v_s[j][c], vf);
+      const float p = p_s[r][j];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        float kd[8];
-        bf16x8_to_f32(kv_s[0][jb + jj][c], kd);
-        float d = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) d = fmaf(qd[i], kd[i], d);
-        sc[jj] = d;
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) sc[jj] = row16_sum(sc[jj]);
-      float bm = -INFINITY;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int u = u0 + jb + jj;
-        // causal mask and the tile's end; tokens past T take key 0 only (never stored)
-        const bool keep = (jb + jj < n_keys) && (valid ? (u <= t) : (u == 0));
-        sc[jj] = keep ? sc[jj] : -INFINITY;
-        bm = fmaxf(bm, sc[jj]);
-      }
-      const float m_new = fmaxf(m, bm);
-      if (m_new == -INFINITY) continue;  // nothing seen yet (uniform per token row)
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        float vd[8];
-        bf16x8_to_f32(kv_s[1][jb + jj][c], vd);
-        const float p = __builtin_amdgcn_exp2f(sc[jj] - m_new);
-        l += p;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, vd[i], acc[i]);
-      }
-      m = m_new;
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(p, vf[i], acc[i]);
     }
   }
 #undef CALIB_FETCH
