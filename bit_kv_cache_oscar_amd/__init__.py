@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     oscar_decode_dense_bf16,
     oscar_dense_workspace_bytes,
     oscar_decode_multi,
+    oscar_decode_multi_codebook,
     oscar_decode_bf16,
     oscar_decode_int2,
     oscar_decode_step,

@@ -97,6 +97,9 @@ _SIGNATURES = {
     "oscar_decode_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,
                                         c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "oscar_decode_multi_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
     "oscar_prepare_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
@@ -422,7 +425,7 @@ def oscar_decode_codebook(desc: LayerDesc, q, rot_k, rot_v, codebook, pool, bloc
 
 
 def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
-                       sm_scale: float, n_splits: int, workspace, out, stream=None):
+                       sm_scale: float, n_splits: int, workspace, out, stream=None, codebook=None):
     """Decode attention for T query tokens per request (q [B, T, Hq, 128] bf16, out the same
     shape in float32; token t sees the window up to its own position) in two launches;
     workspace from oscar_decode_workspace_bytes(desc, B * T, n_splits)."""
@@ -430,10 +433,21 @@ def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist
     n_tok = int(q.shape[1])
     batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
                                        n_splits, workspace, out, n_tok)
-    _check(lib().oscar_decode_multi(byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v), _ptr(pool),
-                                    _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win),
-                                    _ptr(v_win), _ptr(win_len), batch, float(sm_scale), int(n_splits),
-                                    _ptr(workspace), nbytes, _ptr(out), _stream(stream)))
+    rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win),
+            _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
+    if codebook is None:
+        _check(lib().oscar_decode_multi(byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v), *rest))
+    else:
+        _check_codebook(desc, codebook)
+        _check(lib().oscar_decode_multi_codebook(byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v),
+                                                 _ptr(codebook), *rest))
+
+
+def oscar_decode_multi_codebook(desc: LayerDesc, q, rot_k, rot_v, codebook, pool, block_table, hist_len, k_win, v_win,
+                                win_len, sm_scale: float, n_splits: int, workspace, out, stream=None):
+    """oscar_decode_multi over a pool written with the Lloyd-Max codebook (uint8 [Hkv, 2, 4])."""
+    oscar_decode_multi(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len, sm_scale, n_splits,
+                       workspace, out, stream, codebook)
 
 
 def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool,

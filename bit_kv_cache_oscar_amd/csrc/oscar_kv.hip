@@ -508,11 +508,15 @@ int32_t oscar_decode_codebook(const oscar_layer_desc* desc, const void* q, const
                    hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, out, stream);
 }
 
-int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
-                           const void* rot_v, const void* pool, const int32_t* block_table, int32_t max_pages,
-                           const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,
-                           int32_t batch, float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
-                           float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int32_t multi_impl(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
+                   const void* rot_v, const uint32_t* codebook, const void* pool, const int32_t* block_table,
+                   int32_t max_pages, const int32_t* hist_len, const void* k_win, const void* v_win,
+                   const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits, void* workspace,
+                   size_t workspace_bytes, float* out, void* stream) {
   int32_t st = check_desc_impl(desc);
   if (st != OSCAR_OK) return st;
   if (n_tokens <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_tokens %d <= 0", n_tokens);
@@ -541,10 +545,36 @@ int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t 
   a.win_len = win_len;
   a.scale_log2 = static_cast<double>(sm_scale) * 1.4426950408889634;
   a.out = out;
+  a.codebook = codebook;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(oscar::launch_prepare(a, s), "prepare launch");
   if (st != OSCAR_OK) return st;
   return hip_status(oscar::launch_attend(a, s), "attend launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
+                           const void* rot_v, const void* pool, const int32_t* block_table, int32_t max_pages,
+                           const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,
+                           int32_t batch, float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                           float* out, void* stream) {
+  return multi_impl(desc, q, n_tokens, rot_k, rot_v, nullptr, pool, block_table, max_pages, hist_len, k_win, v_win,
+                    win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t oscar_decode_multi_codebook(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
+                                    const void* rot_v, const uint8_t* codebook, const void* pool,
+                                    const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                    const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                    float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                                    float* out, void* stream) {
+  if (int32_t e = check_codebook(codebook)) return e;
+  return multi_impl(desc, q, n_tokens, rot_k, rot_v, reinterpret_cast<const uint32_t*>(codebook), pool, block_table,
+                    max_pages, hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, workspace,
+                    workspace_bytes, out, stream);
 }
 
 size_t oscar_calib_workspace_bytes(const oscar_layer_desc* desc, int32_t n_tokens) {

@@ -401,6 +401,13 @@ int32_t oscar_prepare_codebook(const oscar_layer_desc* desc, const void* k_src, 
                                const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+int32_t oscar_decode_multi_codebook(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
+                                    const void* rot_v, const uint8_t* codebook, const void* pool,
+                                    const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                    const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                    float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                                    float* out, void* stream);
+
 /* oscar_prepare_codebook must have prepared the workspace with the same codebook. */
 int32_t oscar_attend_codebook(const oscar_layer_desc* desc, const void* rot_v, const uint8_t* codebook,
                               const void* pool, const int32_t* block_table, int32_t max_pages,

@@ -102,8 +102,9 @@ def decode(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float, codebooks=None
     return out
 
 
-def decode_multi(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float) -> np.ndarray:
-    """Outputs [T, Hq, 128] of one request's T consecutive query tokens (q [T, Hq, 128]).
+def decode_multi(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float, codebooks=None) -> np.ndarray:
+    """Outputs [T, Hq, 128] of one request's T consecutive query tokens (q [T, Hq, 128]);
+    codebooks as in decode() (None: the uniform levels).
 
     Reading (the pages name prefix-cache reuse; several query tokens over one compressed
     prefix, as in speculative verification or chunked prefill, is this library's reading):
@@ -116,7 +117,7 @@ def decode_multi(q, rot_k, rot_v, win_k, win_v, hists, sm_scale: float) -> np.nd
     for t in range(n_tok):
         keep = max(0, n_w - (n_tok - 1 - t))
         outs.append(decode(q[t], rot_k, rot_v, np.asarray(win_k)[:, :keep], np.asarray(win_v)[:, :keep], hists,
-                           sm_scale))
+                           sm_scale, codebooks))
     return np.stack(outs)
 
 

@@ -296,3 +296,47 @@ def test_codebook_full_size_end_to_end_sampled(cfg):
         for h in range(kv * w.gq, (kv + 1) * w.gq):
             r = oatt.decode_head(q[h], rk[kv], rv[kv], wk[kv], wv[kv], ref, w.sm_scale, codebook=(klv[kv], vlv[kv]))
             assert_close(got[b, h], r, f"{w.name} codebook b{b} h{h}")
+
+
+@pytest.mark.parametrize("case,n_tok,book", [("c2-4k", 4, "fitted"), ("c5-gq8", 2, "skewed"), ("edges", 2, "fitted")])
+def test_codebook_multi_query_on_oracle_pages(case, n_tok, book):
+    """oscar_decode_multi_codebook: T query tokens per request over a codebook pool built by
+    the oracle, causal over the window, twice per split count."""
+    from bit_kv_cache_oscar_amd import oscar_decode_multi_codebook, oscar_decode_workspace_bytes, oscar_default_splits
+
+    w = DECODE_CASES[case]()
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    klv, vlv = fitted(w, rk, rv) if book == "fitted" and w.hist_len(0) > 0 else fixed(w, SKEWED)
+    table, n_phys = synth.block_table(w)
+    pool = opages.new_pool(n_phys, w.n_kv_heads)
+    hists = []
+    for b in range(w.batch):
+        hb = []
+        for kv in range(w.n_kv_heads):
+            hk, hv = synth.history_rows(w, b, kv)
+            hist, _, _ = oracle_history_cb(hk, hv, rk[kv], rv[kv], w.clip_ratio, klv[kv], vlv[kv])
+            opages.pack_history(pool, table[b], kv, hist)
+            hb.append(hist)
+        hists.append(hb)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys)
+    c.set_codebook(klv, vlv)
+    c.pool.copy_(torch.from_numpy(pool.reshape(-1)))
+    qn = np.stack([synth.query_tokens(w, b, n_tok) for b in range(w.batch)])
+    q = bf16(qn)
+    books = [(klv[kv], vlv[kv]) for kv in range(w.n_kv_heads)]
+    refs = []
+    for b in range(w.batch):
+        wk, wv = windows(w, b)
+        refs.append(oatt.decode_multi(qn[b].astype(np.float64), rk, rv, wk, wv, hists[b], w.sm_scale, codebooks=books))
+    for s in sorted({oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())), 3}):
+        ws = torch.zeros(oscar_decode_workspace_bytes(c.desc, w.batch * n_tok, s), dtype=torch.uint8, device="cuda")
+        out = torch.empty((w.batch, n_tok, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
+        for rep in range(2):
+            say(case, book, "codebook multi-query", "T", n_tok, "splits", s, "call", rep)
+            out.fill_(np.nan)
+            oscar_decode_multi_codebook(c.desc, q, c.rot_k, c.rot_v, c.codebook, c.pool, c.block_table, c.hist_len,
+                                        c.k_win, c.v_win, c.win_len, w.sm_scale, s, ws, out)
+            got = out.cpu().numpy()
+            for b in range(w.batch):
+                for t in range(n_tok):
+                    assert_close(got[b, t], refs[b][t], f"{case} codebook multi b{b} t{t} splits {s} call {rep}")

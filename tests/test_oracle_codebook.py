@@ -148,3 +148,29 @@ def test_decode_through_the_uniform_codebook_is_the_uniform_decode():
     # a different codebook changes the dequantised history, hence the output
     c = attention.decode(q, rot, rot, wk, wv, hists, 0.088, codebooks=[([0, 8, 30, 48], [3, 18, 33, 45])] * 2)
     assert not np.allclose(a, c)
+
+
+def test_multi_query_decode_through_codebooks():
+    """decode_multi with codebooks: the uniform levels give the uniform multi-query decode
+    exactly, and each token's output is decode() with the same codebook over its causal
+    share of the window."""
+    g = np.random.default_rng(12)
+    rot = np.stack([round_bf16(rotation_from_covariance(np.diag(g.uniform(0.5, 2, 128))))])
+    xk = round_bf16(g.standard_normal((30, 128)))
+    xv = round_bf16(g.standard_normal((30, 128)))
+    book = ([2, 20, 27, 41], [0, 5, 30, 48])
+    kc, ks, kz, _ = codebook.quantize_rows(xk, rot[0], 0.9, book[0])
+    vc, vs, vz, _ = codebook.quantize_rows(xv, rot[0], 0.9, book[1])
+    hists = [(kc, ks, kz, vc, vs, vz)]
+    q = round_bf16(g.standard_normal((3, 2, 128)))
+    wk = round_bf16(g.standard_normal((1, 9, 128)))
+    wv = round_bf16(g.standard_normal((1, 9, 128)))
+    u = (codebook.UNIFORM16, codebook.UNIFORM16)
+    assert np.array_equal(attention.decode_multi(q, rot, rot, wk, wv, hists, 0.088, codebooks=[u]),
+                          attention.decode_multi(q, rot, rot, wk, wv, hists, 0.088))
+    got = attention.decode_multi(q, rot, rot, wk, wv, hists, 0.088, codebooks=[book])
+    for t in range(3):
+        keep = 9 - (2 - t)
+        ref = attention.decode(q[t], rot, rot, wk[:, :keep], wv[:, :keep], hists, 0.088, codebooks=[book])
+        assert np.array_equal(got[t], ref)
+    assert not np.allclose(got, attention.decode_multi(q, rot, rot, wk, wv, hists, 0.088))
