@@ -577,9 +577,17 @@ int32_t oscar_decode_multi_codebook(const oscar_layer_desc* desc, const void* q,
                     workspace_bytes, out, stream);
 }
 
+}  // extern "C"
+
+namespace oscar {
+size_t calib_workspace_bytes(int T, int n_q, int n_kv);  // calib.hip
+}
+
+extern "C" {
+
 size_t oscar_calib_workspace_bytes(const oscar_layer_desc* desc, int32_t n_tokens) {
   if (check_desc_impl(desc) != OSCAR_OK || n_tokens < 0) return 0;
-  return static_cast<size_t>(n_tokens) * desc->n_q_heads * 128 * sizeof(float);
+  return oscar::calib_workspace_bytes(n_tokens, desc->n_q_heads, desc->n_kv_heads);
 }
 
 int32_t oscar_calib_covariances(const oscar_layer_desc* desc, const void* q, const void* k, const void* v,

@@ -330,7 +330,7 @@ int32_t oscar_decode_dense_bf16(const oscar_layer_desc* desc, const void* q, con
  *   q          bf16 [n_tokens][n_q_heads][128]
  *   k, v       bf16 [n_tokens][n_kv_heads][128]
  *   workspace  at least oscar_calib_workspace_bytes(desc, n_tokens) bytes (the attention
- *              outputs S_h V, fp32); q, k, v and workspace 16-byte aligned
+ *              outputs S_h V and partial Gram sums, fp32); q, k, v and workspace 16-byte aligned
  *   sigma_k, sigma_v  float32 [n_kv_heads][128][128], written (exactly symmetric)
  *   n_tokens   1..65536 (OSCAR_ERR_UNSUPPORTED above)
  * The eigendecomposition that turns sigma into U, and R = U * H * P, is host work on

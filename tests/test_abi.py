@@ -256,7 +256,7 @@ def test_calib_argument_checks(lib):
     d = ctypes.byref(desc)
     f = lib.oscar_calib_covariances
     need = L.oscar_calib_workspace_bytes(desc, 512)
-    assert need == 512 * 32 * 128 * 4
+    assert need == 512 * 32 * 128 * 4 + 32 * 8 * 128 * 128 * 4
     #         q, k, v, T, sm_scale, workspace, bytes, sigma_k, sigma_v, stream
     args = [FAKE, FAKE, FAKE, 512, 0.088, FAKE, need, FAKE, FAKE, None]
 
