@@ -18,4 +18,4 @@ Pinned by the `not gpu` tests: every function here is checked against closed for
 invariants, brute force or hand-built cases (tests/test_oracle_*.py).
 """
 
-from . import rotation, quant, codebook, clip, pages, attention  # noqa: F401
+from . import rotation, quant, codebook, clip, pages, groups, attention  # noqa: F401

@@ -26,6 +26,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import codebook as _codebook
+from . import groups as _groups
 from .quant import dequantize
 
 
@@ -66,8 +67,14 @@ def finalize(part) -> np.ndarray:
 def head_inputs(hist, codebook=None):
     """Dequantised (khat, vhat) of one head's history tuple
     (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16); with codebook = (K levels, V levels)
-    in sixteenths, through those levels instead of the uniform ones."""
+    in sixteenths, through those levels instead of the uniform ones. Scales and zero points
+    of shape [n, n_g] (n_g > 1) are per group of 128 / n_g rotated dims (groups.py)."""
     kc, ks, kz, vc, vs, vz = hist
+    if np.ndim(ks) == 2:
+        if codebook is not None:
+            raise ValueError("codebooks are defined for one group per vector")
+        g = 128 // np.shape(ks)[1]
+        return _groups.dequantize_grouped(kc, ks, kz, g), _groups.dequantize_grouped(vc, vs, vz, g)
     if codebook is not None:
         return _codebook.dequantize(kc, ks, kz, codebook[0]), _codebook.dequantize(vc, vs, vz, codebook[1])
     return dequantize(kc, ks, kz), dequantize(vc, vs, vz)
