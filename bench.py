@@ -533,6 +533,10 @@ def main():
         "bytes_per_call": dense_alg,
         "int2_step_speedup": round(dense_ms / ms, 3),
         "int2_attend_speedup": round(dense_ms / attend_ms, 3),
+        # against any BF16 decode of this context on this machine: its bytes at the measured read
+        # ceiling (a bound no BF16 kernel can beat)
+        "bf16_at_ceiling_us": round(dense_alg / (ceiling_gbs * 1e9) * 1e6, 3),
+        "int2_step_speedup_vs_ceiling": round(dense_alg / (ceiling_gbs * 1e9) / (ms * 1e-3), 3),
         "kv_bytes_ratio": round(dense_alg / max(total_bytes, 1), 3),
     }
     del dense, ws_d, out_d
