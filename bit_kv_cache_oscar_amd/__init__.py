@@ -30,11 +30,13 @@ from ._lib import (  # noqa: F401
     oscar_decode_multi_codebook,
     oscar_decode_bf16,
     oscar_decode_int2,
+    oscar_decode_int2_grouped,
     oscar_decode_step,
     oscar_decode_step_codebook,
     oscar_decode_workspace_bytes,
     oscar_default_splits,
     oscar_demote,
+    oscar_demote_grouped,
     oscar_demote_codebook,
     oscar_last_error,
     oscar_merge,

@@ -32,8 +32,8 @@ class LayerDesc(ctypes.Structure):
     ]
 
 
-def layer_desc(n_q_heads: int, n_kv_heads: int) -> LayerDesc:
-    return LayerDesc(128, 128, 64, n_q_heads, n_kv_heads, 64, 256)
+def layer_desc(n_q_heads: int, n_kv_heads: int, group_size: int = 128) -> LayerDesc:
+    return LayerDesc(128, group_size, 64, n_q_heads, n_kv_heads, 64, 256)
 
 
 class OscarError(RuntimeError):
@@ -56,6 +56,10 @@ _SIGNATURES = {
     "oscar_default_splits": (c_int32, [POINTER(LayerDesc), c_int32, c_int32]),
     "oscar_demote": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "oscar_demote_grouped": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "oscar_decode_int2_grouped": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                            c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     "oscar_decode_int2": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                     c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t, c_void_p]),
     "oscar_decode_bf16": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
@@ -225,7 +229,8 @@ def oscar_decode_workspace_bytes(desc: LayerDesc, batch: int, n_splits: int) -> 
 def oscar_demote(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v, pool,
                  stream=None, codebook=None):
     """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16) into (dst_page[i], dst_slot[i]).
-    With `codebook` (uint8 [Hkv, 2, 4]) this is oscar_demote_codebook."""
+    With `codebook` (uint8 [Hkv, 2, 4]) this is oscar_demote_codebook; with a desc of
+    group_size 64 or 32, oscar_demote_grouped."""
     n = int(k_src.shape[0]) if k_src.dim() else 0
     hkv = desc.n_kv_heads
     _device16(k_src, "k_src")
@@ -241,7 +246,12 @@ def oscar_demote(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v
         _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
               f"{name} must be float32 [n_kv_heads] on the device")
     _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
-    if codebook is None:
+    if desc.group_size != 128:
+        _need(codebook is None, "codebooks are defined for one group per vector")
+        _check(lib().oscar_demote_grouped(byref(desc), _ptr(k_src), _ptr(v_src), n, _ptr(dst_page), _ptr(dst_slot),
+                                          _ptr(rot_k), _ptr(rot_v), _ptr(clip_k), _ptr(clip_v), _ptr(pool),
+                                          _stream(stream)))
+    elif codebook is None:
         _check(lib().oscar_demote(byref(desc), _ptr(k_src), _ptr(v_src), n, _ptr(dst_page), _ptr(dst_slot),
                                   _ptr(rot_k), _ptr(rot_v), _ptr(clip_k), _ptr(clip_v), _ptr(pool),
                                   _stream(stream)))
@@ -261,7 +271,8 @@ def oscar_demote_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot
 def oscar_decode_int2(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm_scale: float, n_splits: int,
                       partials, stream=None):
     """INT2 history pass; q [B, Hq, 128] bf16, block_table [B, max_pages] int32,
-    hist_len [B] int32; partials from oscar_partials_bytes(desc, B, n_splits)."""
+    hist_len [B] int32; partials from oscar_partials_bytes(desc, B, n_splits). A desc with
+    group_size 64 or 32 reads grouped pages (oscar_decode_int2_grouped)."""
     batch = int(q.shape[0])
     _device16(q, "q")
     _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
@@ -273,7 +284,8 @@ def oscar_decode_int2(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm
     _need(pool.is_cuda, "pool must be on the device")
     _need(partials.is_cuda and partials.is_contiguous(), "partials must be a contiguous device tensor")
     nbytes = partials.numel() * partials.element_size()
-    _check(lib().oscar_decode_int2(byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool), _ptr(block_table),
+    fn = lib().oscar_decode_int2 if desc.group_size == 128 else lib().oscar_decode_int2_grouped
+    _check(fn(byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool), _ptr(block_table),
                                    int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale),
                                    int(n_splits), _ptr(partials), nbytes, _stream(stream)))
 
@@ -567,3 +579,36 @@ def oscar_prepare_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, cl
     """oscar_prepare with the Lloyd-Max codebook (uint8 [Hkv, 2, 4]) for demotion and the query data."""
     oscar_prepare(desc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win, v_win,
                   win_len, sm_scale, n_splits, workspace, stream, codebook)
+
+
+def oscar_demote_grouped(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_k, rot_v, clip_k, clip_v, pool,
+                         stream=None):
+    """oscar_demote into grouped pages (desc.group_size 128, 64 or 32); arguments as oscar_demote."""
+    n = int(k_src.shape[0]) if k_src.dim() else 0
+    _device16(k_src, "k_src")
+    _device16(v_src, "v_src")
+    _need(k_src.numel() == n * desc.n_kv_heads * HEAD_DIM and v_src.numel() == k_src.numel(),
+          "k_src/v_src must be [n, n_kv_heads, 128]")
+    _device_i32(dst_page, "dst_page", n)
+    _device_i32(dst_slot, "dst_slot", n)
+    _need(pool.is_cuda and pool.is_contiguous(), "pool must be a contiguous device tensor")
+    _check(lib().oscar_demote_grouped(byref(desc), _ptr(k_src), _ptr(v_src), n, _ptr(dst_page), _ptr(dst_slot),
+                                      _ptr(rot_k), _ptr(rot_v), _ptr(clip_k), _ptr(clip_v), _ptr(pool),
+                                      _stream(stream)))
+
+
+def oscar_decode_int2_grouped(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm_scale: float,
+                              n_splits: int, partials, stream=None):
+    """INT2 history pass over grouped pages (desc.group_size 128, 64 or 32); arguments as
+    oscar_decode_int2."""
+    batch = int(q.shape[0])
+    _device16(q, "q")
+    _need(q.numel() == batch * desc.n_q_heads * HEAD_DIM, "q must be [batch, n_q_heads, 128]")
+    _need(block_table.dim() == 2 and block_table.shape[0] == batch, "block_table must be [batch, max_pages]")
+    _device_i32(block_table, "block_table")
+    _device_i32(hist_len, "hist_len", batch)
+    _need(pool.is_cuda and partials.is_cuda and partials.is_contiguous(), "pool/partials must be device tensors")
+    _check(lib().oscar_decode_int2_grouped(byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool), _ptr(block_table),
+                                           int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale),
+                                           int(n_splits), _ptr(partials), partials.numel() * partials.element_size(),
+                                           _stream(stream)))

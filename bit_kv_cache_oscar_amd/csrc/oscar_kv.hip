@@ -47,6 +47,17 @@ int32_t check_desc_impl(const oscar_layer_desc* d) {
   return OSCAR_OK;
 }
 
+// As check_desc_impl, with groups of 64 or 32 dims allowed as well (the entry points that
+// read or write grouped pages, and those that do not depend on the group size).
+int32_t check_desc_grouped(const oscar_layer_desc* d) {
+  if (!d) return fail(OSCAR_ERR_INVALID_ARG, "desc is null");
+  if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128)
+    return fail(OSCAR_ERR_UNSUPPORTED, "group_size %d not in {32, 64, 128}", d->group_size);
+  oscar_layer_desc one = *d;
+  one.group_size = 128;
+  return check_desc_impl(&one);
+}
+
 oscar::LayerShape shape_of(const oscar_layer_desc* d) {
   oscar::LayerShape s;
   s.n_q = d->n_q_heads;
@@ -116,6 +127,17 @@ PartialsView partials_view(void* base, int batch, int n_q, int n_splits) {
 
 }  // namespace oscar
 
+namespace oscar {
+// grouped.hip: groups of 64 or 32 rotated dims (128 is the one-group format)
+size_t grouped_page_bytes(int n_kv, int group);
+hipError_t launch_demote_grouped(int n_kv, int group, const void* k_src, const void* v_src, int n,
+                                 const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                                 const float* clip_k, const float* clip_v, void* pool, hipStream_t stream);
+hipError_t launch_decode_grouped(const LayerShape& L, int group, const void* q, const void* rot_k, const void* pool,
+                                 const int32_t* block_table, int max_pages, const int32_t* hist_len, int batch,
+                                 float sm_scale, int n_splits, const PartialsView& out, hipStream_t stream);
+}  // namespace oscar
+
 extern "C" {
 
 int32_t oscar_version(void) { return 100; }
@@ -134,32 +156,32 @@ const char* oscar_status_string(int32_t status) {
 const char* oscar_last_error(void) { return g_last_error; }
 
 int32_t oscar_check_desc(const oscar_layer_desc* desc) {
-  const int32_t st = check_desc_impl(desc);
+  const int32_t st = check_desc_grouped(desc);
   return st == OSCAR_OK ? ok() : st;
 }
 
 size_t oscar_page_bytes(const oscar_layer_desc* desc) {
-  if (check_desc_impl(desc) != OSCAR_OK) return 0;
-  return static_cast<size_t>(desc->n_kv_heads) * 4608;
+  if (check_desc_grouped(desc) != OSCAR_OK) return 0;
+  return oscar::grouped_page_bytes(desc->n_kv_heads, desc->group_size);
 }
 
 int32_t oscar_window_tokens(const oscar_layer_desc* desc) {
-  if (check_desc_impl(desc) != OSCAR_OK) return 0;
+  if (check_desc_grouped(desc) != OSCAR_OK) return 0;
   return desc->sink_tokens + desc->recent_tokens;
 }
 
 int32_t oscar_window_splits(const oscar_layer_desc* desc) {
-  if (check_desc_impl(desc) != OSCAR_OK) return 0;
+  if (check_desc_grouped(desc) != OSCAR_OK) return 0;
   return window_splits_of(desc);
 }
 
 size_t oscar_partials_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
-  if (check_desc_impl(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
+  if (check_desc_grouped(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
   return oscar::partials_bytes(batch, desc->n_q_heads, n_splits);
 }
 
 int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len) {
-  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0) return 1;
+  if (check_desc_grouped(desc) != OSCAR_OK || batch <= 0) return 1;
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
   const int gq = desc->n_q_heads / desc->n_kv_heads;
   const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1);
@@ -259,7 +281,7 @@ int32_t oscar_decode_int2(const oscar_layer_desc* desc, const void* q, const voi
 int32_t oscar_decode_bf16(const oscar_layer_desc* desc, const void* q, const void* k_win, const void* v_win,
                           const int32_t* win_len, int32_t batch, float sm_scale, void* win_partials,
                           size_t win_partials_bytes, void* stream) {
-  int32_t st = check_desc_impl(desc);
+  int32_t st = check_desc_grouped(desc);
   if (st != OSCAR_OK) return st;
   if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
@@ -620,7 +642,7 @@ int32_t oscar_read_probe(const void* buf, size_t bytes, uint32_t* out, void* str
 
 int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t n_splits, const void* win_partials,
                     const void* rot_v, float* out, int32_t batch, void* stream) {
-  int32_t st = check_desc_impl(desc);
+  int32_t st = check_desc_grouped(desc);
   if (st != OSCAR_OK) return st;
   if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
@@ -634,5 +656,46 @@ int32_t oscar_merge(const oscar_layer_desc* desc, const void* partials, int32_t 
   return hip_status(oscar::launch_merge(L, h, n_splits, w, ws, rot_v, out, batch, static_cast<hipStream_t>(stream)),
                     "merge launch");
 }
+
+int32_t oscar_demote_grouped(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                             const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                             const float* clip_k, const float* clip_v, void* pool, void* stream) {
+  int32_t st = check_desc_grouped(desc);
+  if (st != OSCAR_OK) return st;
+  if (n < 0) return fail(OSCAR_ERR_INVALID_ARG, "n %d < 0", n);
+  if (n == 0) return ok();
+  if (!k_src || !v_src || !dst_page || !dst_slot || !rot_k || !rot_v || !clip_k || !clip_v || !pool)
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (2LL * n * desc->n_kv_heads > 0x7FFFFFFFLL)
+    return fail(OSCAR_ERR_UNSUPPORTED, "2 * n * n_kv_heads exceeds the grid limit");
+  return hip_status(oscar::launch_demote_grouped(desc->n_kv_heads, desc->group_size, k_src, v_src, n, dst_page,
+                                                 dst_slot, rot_k, rot_v, clip_k, clip_v, pool,
+                                                 static_cast<hipStream_t>(stream)),
+                    "grouped demote launch");
+}
+
+int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                  int32_t batch, float sm_scale, int32_t n_splits, void* partials,
+                                  size_t partials_bytes, void* stream) {
+  int32_t st = check_desc_grouped(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (n_splits <= 0 || n_splits > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d out of [1, 65535]", n_splits);
+  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (!q || !rot_k || !pool || !block_table || !hist_len || !partials)
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const size_t need = oscar::partials_bytes(batch, desc->n_q_heads, n_splits);
+  if (partials_bytes < need)
+    return fail(OSCAR_ERR_WORKSPACE, "partials workspace %zu < %zu bytes", partials_bytes, need);
+  const oscar::LayerShape L = shape_of(desc);
+  const oscar::PartialsView v = oscar::partials_view(partials, batch, desc->n_q_heads, n_splits);
+  return hip_status(oscar::launch_decode_grouped(L, desc->group_size, q, rot_k, pool, block_table, max_pages, hist_len,
+                                                 batch, sm_scale, n_splits, v, static_cast<hipStream_t>(stream)),
+                    "grouped decode launch");
+}
+
 
 }  // extern "C"

@@ -27,8 +27,9 @@ def _bf16_tensor(bits_or_values, device) -> torch.Tensor:
 
 class LayerCache:
     def __init__(self, n_q_heads: int, n_kv_heads: int, batch: int, max_pages: int, n_pages: int,
-                 device="cuda"):
-        self.desc = L.layer_desc(n_q_heads, n_kv_heads)
+                 device="cuda", group_size: int = 128):
+        # group_size 64 or 32: grouped pages, read and written by demote() and decode() only
+        self.desc = L.layer_desc(n_q_heads, n_kv_heads, group_size)
         st = L.oscar_check_desc(self.desc)
         if st != L.OSCAR_OK:
             raise L.OscarError(st, L.oscar_last_error())

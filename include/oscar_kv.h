@@ -24,9 +24,11 @@
  *   - Each failing call also records a message, readable with oscar_last_error() on the
  *     same host thread.
  *
- * Fixed shapes: head_dim = group_size = 128, page_tokens = 64, sink_tokens = 64,
+ * Fixed shapes: head_dim = 128, page_tokens = 64, sink_tokens = 64,
  * recent_tokens = 256; n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}; query head h uses KV
- * head h / (n_q_heads / n_kv_heads).
+ * head h / (n_q_heads / n_kv_heads). group_size is 128 (one scale and zero point per
+ * vector) for every entry point except the *_grouped ones, which also take 64 and 32; the
+ * size helpers, oscar_decode_bf16 and oscar_merge take any of the three.
  *
  * INT2 pool layout (4608 bytes per page per KV head, head h of physical page p at byte
  * (p * n_kv_heads + h) * 4608). Codes are packed 16 to a little-endian 32-bit word, the code
@@ -74,7 +76,7 @@ typedef enum oscar_status {
 
 typedef struct oscar_layer_desc {
   int32_t head_dim;      /* must be 128 */
-  int32_t group_size;    /* quantisation group, must be 128 (one group per vector) */
+  int32_t group_size;    /* quantisation group: 128 (one per vector), or 64 / 32 (grouped pages) */
   int32_t page_tokens;   /* must be 64 */
   int32_t n_q_heads;
   int32_t n_kv_heads;
@@ -91,10 +93,12 @@ const char* oscar_status_string(int32_t status);
 /* Message of the last failed call on this host thread ("" if none). */
 const char* oscar_last_error(void);
 
-/* Checks a descriptor; OSCAR_OK if every entry point accepts it. */
+/* Checks a descriptor; OSCAR_OK if it is valid (group_size 128, 64 or 32; entry points
+ * other than the *_grouped ones return OSCAR_ERR_UNSUPPORTED for 64 and 32). */
 int32_t oscar_check_desc(const oscar_layer_desc* desc);
 
-/* Bytes of one physical page (all KV heads): n_kv_heads * 4608. 0 for a bad desc. */
+/* Bytes of one physical page (all KV heads): n_kv_heads * (4096 + 512 * 128 / group_size),
+ * that is n_kv_heads * 4608 for one group per vector. 0 for a bad desc. */
 size_t oscar_page_bytes(const oscar_layer_desc* desc);
 
 /* BF16 window slots per request and KV head: sink_tokens + recent_tokens. */
@@ -413,6 +417,35 @@ int32_t oscar_attend_codebook(const oscar_layer_desc* desc, const void* rot_v, c
                               const void* pool, const int32_t* block_table, int32_t max_pages,
                               const int32_t* hist_len, int32_t batch, int32_t n_splits, void* workspace,
                               size_t workspace_bytes, float* out, void* stream);
+
+/* ---------------------------------------------------------------- grouped pages
+ * Quantisation groups of G = 64 or 32 rotated dims (desc->group_size; 128 gives the
+ * one-group codes and scales in the grouped page layout below). Method: OSCAR, QbitAI
+ * article, section on aiming the rotation at attention (the bit-reversal in R balances the
+ * INT2 groups; scale and zero point per group).
+ *
+ * Grouped page layout, per head block of 4096 + 512 n_g bytes (n_g = 128 / G): the K and V
+ * codes exactly as in the one-group layout (bytes 0..4095); then the K (s16, z16) pair of
+ * slot t and group g at 4096 + 4 (n_g t + g); then the V pairs, from 4096 + 256 n_g, the
+ * same way. Group g covers rotated dims [g G, g G + G). Pages written by one layout are
+ * read only by the same layout.
+ */
+
+/* oscar_demote into grouped pages: each rotated, clipped vector takes one (scale, zero
+ * point) per group, from that group's extremes. Arguments, ownership and errors as
+ * oscar_demote; pool holds pages of oscar_page_bytes(desc) bytes. */
+int32_t oscar_demote_grouped(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                             const int32_t* dst_page, const int32_t* dst_slot, const void* rot_k, const void* rot_v,
+                             const float* clip_k, const float* clip_v, void* pool, void* stream);
+
+/* INT2 history pass over grouped pages: each code dequantises with its own group's scale
+ * and zero point. Arguments as oscar_decode_int2, with partials in the same format (so
+ * oscar_decode_bf16 and oscar_merge complete the decode); there is no per-split page
+ * limit. Runs on the vector ALU in fp32. */
+int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                  int32_t batch, float sm_scale, int32_t n_splits, void* partials,
+                                  size_t partials_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -55,7 +55,8 @@ def test_helpers(lib):
 
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, L.OSCAR_ERR_UNSUPPORTED),
-    ("group_size", 64, L.OSCAR_ERR_UNSUPPORTED),
+    ("group_size", 96, L.OSCAR_ERR_UNSUPPORTED),
+    ("group_size", 16, L.OSCAR_ERR_UNSUPPORTED),
     ("page_tokens", 16, L.OSCAR_ERR_UNSUPPORTED),
     ("sink_tokens", 4, L.OSCAR_ERR_UNSUPPORTED),
     ("recent_tokens", 128, L.OSCAR_ERR_UNSUPPORTED),
@@ -71,6 +72,37 @@ def test_bad_descriptors(lib, field, value, status):
     assert L.oscar_last_error()
     st = lib.oscar_decode_int2(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, 1 << 30, None)
     assert st == status
+
+
+@pytest.mark.parametrize("group", [64, 32])
+def test_grouped_descriptors(lib, group):
+    """Groups of 64 and 32 dims: valid descriptors with larger pages; the one-group entry
+    points refuse them, the grouped ones and the group-independent passes accept them."""
+    d = L.layer_desc(32, 8, group)
+    one = L.layer_desc(32, 8)
+    assert L.oscar_check_desc(d) == L.OSCAR_OK
+    assert L.oscar_page_bytes(d) == 8 * (4096 + 512 * (128 // group))
+    assert L.oscar_partials_bytes(d, 2, 7) == L.oscar_partials_bytes(one, 2, 7)
+    assert L.oscar_window_splits(d) == 5
+    big = 1 << 40
+    r = ctypes.byref(d)
+    assert lib.oscar_decode_int2(r, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, big, None) == \
+        L.OSCAR_ERR_UNSUPPORTED
+    assert lib.oscar_demote(r, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_UNSUPPORTED
+    g = lib.oscar_decode_int2_grouped
+    assert g(r, None, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert g(r, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 0.08, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert g(r, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 0, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert g(r, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, -1.0, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    need = L.oscar_partials_bytes(d, 1, 4)
+    assert g(r, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, need - 1, None) == L.OSCAR_ERR_WORKSPACE
+    dm = lib.oscar_demote_grouped
+    assert dm(r, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_OK
+    assert dm(r, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert dm(r, FAKE, None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    bad = L.layer_desc(32, 8, 48)
+    assert dm(ctypes.byref(bad), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        L.OSCAR_ERR_UNSUPPORTED
 
 
 def test_null_desc(lib):
