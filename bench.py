@@ -417,6 +417,77 @@ def main():
             "query_tokens_per_s": round(w.batch * n_tok / (multi_ms * 1e-3), 1),
         }
 
+    # timed region 5, grouped pages (one scale and zero point per 64 or 32 rotated dims): the
+    # same history demoted into grouped pools of every instance, then the three-launch decode
+    # (oscar_decode_int2_grouped, oscar_decode_bf16, oscar_merge) and the grouped INT2 pass
+    # alone, back to back over the instances
+    from bit_kv_cache_oscar_amd import oscar_decode_int2_grouped, oscar_default_splits
+    from bit_kv_cache_oscar_amd.layer import LayerCache
+
+    grouped_rows = {}
+    for group in (64, 32):
+        ng = 128 // group
+        gins = []
+        for i in range(layers):
+            g = LayerCache(w.n_q_heads, w.n_kv_heads, w.batch, base.block_table.shape[1],
+                           base.pool.numel() // (w.n_kv_heads * 4608), device=dev, group_size=group)
+            for name in ("rot_k", "rot_v", "clip_k", "clip_v", "block_table", "hist_len", "k_win", "v_win",
+                         "win_len"):
+                getattr(g, name).copy_(getattr(base, name))
+            if i == 0:
+                for kk, vv, pg, sl in fill_rows:
+                    g.demote(kk, vv, pg, sl, stream)
+            else:
+                g.pool.copy_(gins[0].pool)
+            g.set_splits(oscar_default_splits(g.desc, w.batch, int(max(w.hist_lens))))
+            gins.append(g)
+        torch.cuda.synchronize()
+
+        def g_decode(c):
+            c.decode(q, w.sm_scale, stream)
+
+        def g_int2(c):
+            oscar_decode_int2_grouped(c.desc, q, c.rot_k, c.pool, c.block_table, c.hist_len, w.sm_scale, c.n_splits,
+                                      c.partials, stream)
+
+        saved = insts
+        insts = gins
+        # split counts: the library default and about 16, 8, 4 and 2 pages per split (this
+        # pass gains from more, smaller workgroups); the fastest is reported
+        n_pg = -(-int(max(w.hist_lens)) // 64)
+        sweep = {}
+        for sp in sorted({gins[0].n_splits} | {max(1, min(65535, -(-n_pg // k))) for k in (16, 8, 4, 2)}):
+            for c in gins:
+                c.set_splits(sp)
+            for i in range(max(2, args.warmup)):
+                g_decode(insts[i % layers])
+            sweep[sp] = timed(g_int2, args.steps)
+        best = min(sweep, key=sweep.get)
+        for c in gins:
+            c.set_splits(best)
+        g_decode(insts[0])
+        g_ms = timed(g_decode, args.steps)
+        g_int2_ms = timed(g_int2, args.steps)
+        insts = saved
+        g_bytes = int(sum(w.hist_lens)) * w.n_kv_heads * (64 + 8 * ng) + w.n_kv_heads * ROT_BYTES + \
+            w.batch * w.n_q_heads * 128 * 2
+        grouped_rows[f"group_{group}"] = {
+            "entry": "oscar_decode_int2_grouped + oscar_decode_bf16 + oscar_merge; pass alone: "
+                     "oscar_decode_int2_grouped",
+            "history_bytes_per_token_head": 64 + 8 * ng,
+            "splits": gins[0].n_splits,
+            "int2_pass_us_by_splits": {str(k): round(v * 1e3, 3) for k, v in sorted(sweep.items())},
+            "us_per_decode": round(g_ms * 1e3, 3),
+            "int2_pass_us_per_launch": round(g_int2_ms * 1e3, 3),
+            "bound": "hbm",
+            "achieved": round(g_bytes / (g_int2_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(g_bytes / (g_int2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
+        del gins
+        torch.cuda.empty_cache()
+
     # timed region 4, the Lloyd-Max codebook variant: per-head K and V codebooks fitted on the
     # calibration set by the library's host calibration; the same history demoted against
     # them into every instance's pool; then whole steps and the attend launch alone, as above
@@ -595,6 +666,7 @@ def main():
         out["multi_query"] = multi
     if cb_row is not None:
         out["codebook"] = cb_row
+    out["grouped"] = grouped_rows
     if calib_row is not None:
         out["calibration"] = calib_row
     out["bf16_baseline"] = dense_row

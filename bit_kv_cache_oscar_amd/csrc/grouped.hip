@@ -20,7 +20,8 @@
 // core pass is not generalised): grid (split, KV head, request), 256 threads; per page, thread
 // (token, quarter of the dims) scores its token against every query head of the KV head, the
 // weights take an online softmax in log2 units, and thread (dim, half of the slots) adds the
-// dequantised values; the next page's code and metadata words load during the current page.
+// dequantised values; the code and metadata words of the next two pages load during the
+// current page.
 
 #include "demote_pass.h"
 
@@ -190,6 +191,8 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
   constexpr int G = kHeadDim / NG;
   constexpr int kHB = grouped_block_bytes<NG>();
   __shared__ float qr_s[GQ][kHeadDim];
+  __shared__ __align__(16) uint16_t rot_s[64][kHeadDim + 8];  // half of R_K's rows, padded
+  __shared__ __align__(16) uint16_t q_s[GQ][kHeadDim];
   __shared__ float sp_s[GQ][4];     // sum of q_rot over each quarter of the dims
   __shared__ float w_s[GQ][64];     // scores, then weights, of the page's slots
   __shared__ uint32_t meta_s[2][64 * NG];
@@ -200,16 +203,43 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
   const int b = blockIdx.z;
   const int h0 = kv * GQ;
 
-  // ---- q_rot = q R_K of the KV head's query heads (fp32 sums of exact bf16 products)
-  for (int idx = t; idx < GQ * kHeadDim; idx += 256) {
-    const int h = idx / kHeadDim;
-    const int d = idx % kHeadDim;
-    const uint16_t* qh = q + (static_cast<size_t>(b) * n_q + h0 + h) * kHeadDim;
-    const uint16_t* rc = rot_k + static_cast<size_t>(kv) * kHeadDim * kHeadDim + d;
-    float acc = 0.f;
+  // ---- q_rot = q R_K of the KV head's query heads (fp32 sums of exact bf16 products, in
+  // order of the rows of R_K): the queries and R_K, in two halves of 64 rows, pass through
+  // LDS in 16-byte loads that are all in flight at once
+  for (int idx = t; idx < GQ * kHeadDim / 8; idx += 256) {
+    const int h = idx >> 4;
+    const int ch = idx & 15;
+    *reinterpret_cast<uint4*>(&q_s[h][8 * ch]) =
+        *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(b) * n_q + h0 + h) * kHeadDim + 8 * ch);
+  }
+  constexpr int kOut = (GQ * kHeadDim + 255) / 256;  // q_rot entries per thread
+  float qacc[kOut];
+#pragma unroll
+  for (int o = 0; o < kOut; ++o) qacc[o] = 0.f;
+  for (int hf = 0; hf < 2; ++hf) {
+    __syncthreads();  // the previous half is no longer read
+    for (int idx = t; idx < 64 * kHeadDim / 8; idx += 256) {
+      const int row = idx >> 4;
+      const int ch = idx & 15;
+      *reinterpret_cast<uint4*>(&rot_s[row][8 * ch]) = *reinterpret_cast<const uint4*>(
+          rot_k + (static_cast<size_t>(kv) * kHeadDim + 64 * hf + row) * kHeadDim + 8 * ch);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < kOut; ++o) {
+      const int idx = t + 256 * o;
+      if (idx < GQ * kHeadDim) {
+        const int h = idx / kHeadDim;
+        const int d = idx % kHeadDim;
 #pragma unroll 16
-    for (int i = 0; i < kHeadDim; ++i) acc = fmaf(bf16_to_f32(qh[i]), bf16_to_f32(rc[i * kHeadDim]), acc);
-    qr_s[h][d] = acc;
+        for (int i = 0; i < 64; ++i) qacc[o] = fmaf(bf16_to_f32(q_s[h][64 * hf + i]), bf16_to_f32(rot_s[i][d]), qacc[o]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 0; o < kOut; ++o) {
+    const int idx = t + 256 * o;
+    if (idx < GQ * kHeadDim) qr_s[idx / kHeadDim][idx % kHeadDim] = qacc[o];
   }
   if (t < GQ) {
     m_s[t] = -INFINITY;
@@ -244,8 +274,13 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
 #pragma unroll
   for (int h = 0; h < GQ; ++h) acc[h] = 0.f;
 
-  GPage cur = {0u, 0u, 0u, 0u, 0u, 0u};
+  // pages two ahead in flight, and the block-table entry of the page after them, so that no
+  // page waits on a table load followed by a data load
+  GPage cur = {0u, 0u, 0u, 0u, 0u, 0u}, nxt = cur;
+  int id_ahead = 0;
   if (p_begin < p_end) cur = grouped_load<NG>(head_base + static_cast<size_t>(table[p_begin]) * page_stride, tok, part, d, half);
+  if (p_begin + 1 < p_end) nxt = grouped_load<NG>(head_base + static_cast<size_t>(table[p_begin + 1]) * page_stride, tok, part, d, half);
+  if (p_begin + 2 < p_end) id_ahead = table[p_begin + 2];
   for (int p = p_begin; p < p_end; ++p) {
     const int ntok = min(kPageTokens, nh - p * kPageTokens);
     __syncthreads();  // the previous page's metadata and weights are no longer read
@@ -254,7 +289,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
       meta_s[1][t] = cur.vm;
     }
     const GPage now = cur;
-    if (p + 1 < p_end) cur = grouped_load<NG>(head_base + static_cast<size_t>(table[p + 1]) * page_stride, tok, part, d, half);
+    cur = nxt;
+    if (p + 2 < p_end) nxt = grouped_load<NG>(head_base + static_cast<size_t>(id_ahead) * page_stride, tok, part, d, half);
+    if (p + 3 < p_end) id_ahead = table[p + 3];
     __syncthreads();  // metadata of the page in LDS
     // ---- scores: token tok against every head, dims of quarter `part`
     {

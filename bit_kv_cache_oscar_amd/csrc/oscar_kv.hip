@@ -687,6 +687,8 @@ int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, c
   if (!q || !rot_k || !pool || !block_table || !hist_len || !partials)
     return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(rot_k) % 16 != 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "q and rot_k must be 16-byte aligned");
   const size_t need = oscar::partials_bytes(batch, desc->n_q_heads, n_splits);
   if (partials_bytes < need)
     return fail(OSCAR_ERR_WORKSPACE, "partials workspace %zu < %zu bytes", partials_bytes, need);

@@ -441,7 +441,8 @@ int32_t oscar_demote_grouped(const oscar_layer_desc* desc, const void* k_src, co
 /* INT2 history pass over grouped pages: each code dequantises with its own group's scale
  * and zero point. Arguments as oscar_decode_int2, with partials in the same format (so
  * oscar_decode_bf16 and oscar_merge complete the decode); there is no per-split page
- * limit. Runs on the vector ALU in fp32. */
+ * limit; q and rot_k must be 16-byte aligned (else OSCAR_ERR_INVALID_ARG). Runs on the
+ * vector ALU in fp32; about four pages per split suit it. */
 int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* pool,
                                   const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
                                   int32_t batch, float sm_scale, int32_t n_splits, void* partials,

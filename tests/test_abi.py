@@ -96,6 +96,9 @@ def test_grouped_descriptors(lib, group):
     assert g(r, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, -1.0, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
     need = L.oscar_partials_bytes(d, 1, 4)
     assert g(r, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, need - 1, None) == L.OSCAR_ERR_WORKSPACE
+    assert g(r, FAKE + 8, FAKE, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert g(r, FAKE, FAKE + 2, FAKE, FAKE, 4, FAKE, 1, 0.08, 4, FAKE, big, None) == L.OSCAR_ERR_INVALID_ARG
+    assert "aligned" in L.oscar_last_error()
     dm = lib.oscar_demote_grouped
     assert dm(r, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_OK
     assert dm(r, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
