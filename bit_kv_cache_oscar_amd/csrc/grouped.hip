@@ -18,10 +18,11 @@
 // taken per group (a group's dims are held by 64 / n_g consecutive lanes of wave 0).
 // INT2 pass: a plain dequantise-and-FMA pass on the vector ALU (the one-group path's matrix-
 // core pass is not generalised): grid (split, KV head, request), 256 threads; per page, thread
-// (token, quarter of the dims) scores its token against every query head of the KV head, the
-// weights take an online softmax in log2 units, and thread (dim, half of the slots) adds the
-// dequantised values; the code and metadata words of the next two pages load during the
-// current page.
+// (token, quarter of the dims) scores its token against every query head of the KV head; the
+// weights take an online softmax in log2 units and are multiplied by each slot's V scale of
+// every group (the zero points summed once per page); thread (dim, half of the slots) adds
+// weight-times-scale times code. The code and metadata words of the next two pages load
+// during the current page.
 
 #include "demote_pass.h"
 
@@ -194,7 +195,9 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
   __shared__ __align__(16) uint16_t rot_s[64][kHeadDim + 8];  // half of R_K's rows, padded
   __shared__ __align__(16) uint16_t q_s[GQ][kHeadDim];
   __shared__ float sp_s[GQ][4];     // sum of q_rot over each quarter of the dims
-  __shared__ float w_s[GQ][64];     // scores, then weights, of the page's slots
+  __shared__ float w_s[GQ][64];     // scores of the page's slots
+  __shared__ float ws_s[GQ][NG][64];  // weight * V scale of (head, group, slot)
+  __shared__ float zs_s[GQ][NG];      // sum over the page of weight * V zero point
   __shared__ uint32_t meta_s[2][64 * NG];
   __shared__ float m_s[GQ], l_s[GQ], al_s[GQ];
   const int t = threadIdx.x;
@@ -327,8 +330,21 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
       const float m_new = fmaxf(m_old, mx);  // finite: a page holds at least one token
       const float p0 = __builtin_amdgcn_exp2f(x0 - m_new);
       const float p1 = __builtin_amdgcn_exp2f(x1 - m_new);
-      w_s[h][2 * j] = p0;
-      w_s[h][2 * j + 1] = p1;
+      // the dequantisation folded into the weights: per group g, weight * scale of each slot,
+      // and the page's sum of weight * zero point (slots past the history end take 0: their
+      // metadata may hold anything)
+      const bool ok0 = 2 * j < ntok, ok1 = 2 * j + 1 < ntok;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const uint32_t m0 = meta_s[1][NG * (2 * j) + g];
+        const uint32_t m1 = meta_s[1][NG * (2 * j + 1) + g];
+        ws_s[h][g][2 * j] = ok0 ? p0 * f16_to_f32(m0) : 0.f;
+        ws_s[h][g][2 * j + 1] = ok1 ? p1 * f16_to_f32(m1) : 0.f;
+        float zz = (ok0 ? p0 * f16_to_f32(m0 >> 16) : 0.f) + (ok1 ? p1 * f16_to_f32(m1 >> 16) : 0.f);
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) zz += __shfl_xor(zz, o, 64);
+        if (j == 0) zs_s[h][g] = zz;
+      }
       float ps = p0 + p1;
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) ps += __shfl_xor(ps, o, 64);
@@ -340,19 +356,21 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
       }
     }
     __syncthreads();
-    // ---- values: dim d, slots 32 half .. + 31, dequantised with each slot's group scale
+    // ---- values: dim d, slots 32 half .. + 31: sum of (weight * scale) * code over the
+    // slots, plus (once, in half 0) the page's sum of weight * zero point of d's group
     {
 #pragma unroll
       for (int h = 0; h < GQ; ++h) acc[h] *= al_s[h];
-#pragma unroll 4
+#pragma unroll 8
       for (int i = 0; i < 32; ++i) {
         const int slot = 32 * half + i;
-        const uint32_t vm = meta_s[1][NG * slot + gv];
         const float code = code_at(i < 16 ? now.v0 : now.v1, i & 15);
-        // slots past the history end have weight 0 (their words may hold anything)
-        const float vhat = slot < ntok ? fmaf(code, f16_to_f32(vm), f16_to_f32(vm >> 16)) : 0.f;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) acc[h] = fmaf(w_s[h][slot], vhat, acc[h]);
+        for (int h = 0; h < GQ; ++h) acc[h] = fmaf(ws_s[h][gv][slot], code, acc[h]);
+      }
+      if (half == 0) {
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) acc[h] += zs_s[h][gv];
       }
     }
   }
