@@ -216,3 +216,41 @@ def test_one_group_grouped_entries_match_the_one_group_path():
     for b in range(w.batch):
         assert_close(got[b], ref[b], f"one-group grouped decode vs one-group decode b{b}")
     assert ctypes.sizeof(L.LayerDesc) == 28
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_grouped_full_size_sampled(group):
+    """The grouped path at the 32K workload's real size (32768-token context, 32 query heads,
+    8 KV heads): every history token demoted on the GPU, then decoded at about four pages
+    per split (the split count the benchmark settles on); sampled KV heads compared with
+    the oracle (pool contents and the outputs of their query heads)."""
+    from test_gpu_parity import _demote_all
+
+    w = synth.workload(2)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table, n_phys = synth.block_table(w)
+    c = grouped_cache(w, rk_bits, rv_bits, table, n_phys, group)
+    for b in range(w.batch):
+        n = w.hist_len(b)
+        ks, vs = [], []
+        for kv in range(w.n_kv_heads):
+            k, v = synth.kv_rows(w, b, kv, 64, 64 + n)
+            ks.append(k)
+            vs.append(v)
+        j = np.arange(n)
+        say("grouped full size", w.name, "group", group, "b", b, "tokens", n)
+        _demote_all(c, w, b, table[b, j // 64], j % 64, np.stack(ks, 1), np.stack(vs, 1))
+    s = -(-(-(-int(w.hist_lens.max()) // 64)) // 4)
+    c.set_splits(s)
+    got = c.decode(queries(w), w.sm_scale).cpu().numpy()
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, ogroups.head_block_bytes(group))
+    for b, kv in ((0, 0), (0, 5)):
+        say("grouped full size sample", w.name, "group", group, "b", b, "kv", kv, "splits", s)
+        ref_hist, km, vm = oracle_history_grouped(w, b, kv, rk, rv, group)
+        gpu_hist = unpack_grouped(pool, table[b], kv, w.hist_len(b), group)
+        compare_history(gpu_hist, ref_hist, km, vm, f"{w.name} g{group} b{b} kv{kv}")
+        q = synth.query(w, b).astype(np.float64)
+        wk, wv = windows(w, b)
+        for h in range(kv * w.gq, (kv + 1) * w.gq):
+            ref = oatt.decode_head(q[h], rk[kv], rv[kv], wk[kv], wv[kv], ref_hist, w.sm_scale)
+            assert_close(got[b, h], ref, f"{w.name} g{group} b{b} h{h}")
