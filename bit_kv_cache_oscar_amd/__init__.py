@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     oscar_decode_bf16,
     oscar_decode_int2,
     oscar_decode_int2_grouped,
+    oscar_decode_step_grouped,
     oscar_decode_step,
     oscar_decode_step_codebook,
     oscar_decode_workspace_bytes,

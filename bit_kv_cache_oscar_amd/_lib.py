@@ -71,6 +71,10 @@ _SIGNATURES = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
                                     c_void_p, c_void_p]),
+    "oscar_decode_step_grouped": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32,
+                                            c_void_p, c_size_t, c_void_p, c_void_p]),
     "oscar_decode": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
                                c_void_p, c_void_p]),
@@ -466,7 +470,8 @@ def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k,
                       block_table, hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace, out,
                       stream=None, codebook=None):
     """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16, n may be 0) and decode, in two launches.
-    With `codebook` this is oscar_decode_step_codebook."""
+    With `codebook` this is oscar_decode_step_codebook; with a desc of group_size 64 or 32,
+    oscar_decode_step_grouped (four launches)."""
     batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
                                        n_splits, workspace, out)
     n = int(k_src.shape[0]) if k_src is not None and k_src.dim() else 0
@@ -486,7 +491,10 @@ def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k,
             _ptr(rot_k), _ptr(rot_v))
     rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win),
             _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
-    if codebook is None:
+    if desc.group_size != 128:
+        _need(codebook is None, "codebooks are defined for one group per vector")
+        _check(lib().oscar_decode_step_grouped(byref(desc), *head, *rest))
+    elif codebook is None:
         _check(lib().oscar_decode_step(byref(desc), *head, *rest))
     else:
         _check_codebook(desc, codebook)
@@ -612,3 +620,12 @@ def oscar_decode_int2_grouped(desc: LayerDesc, q, rot_k, pool, block_table, hist
                                            int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale),
                                            int(n_splits), _ptr(partials), partials.numel() * partials.element_size(),
                                            _stream(stream)))
+
+
+def oscar_decode_step_grouped(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool,
+                              block_table, hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace,
+                              out, stream=None):
+    """oscar_decode_step over grouped pages (desc.group_size 64 or 32)."""
+    _need(desc.group_size in (64, 32), "oscar_decode_step_grouped takes a desc of group_size 64 or 32")
+    oscar_decode_step(desc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, block_table,
+                      hist_len, k_win, v_win, win_len, sm_scale, n_splits, workspace, out, stream)

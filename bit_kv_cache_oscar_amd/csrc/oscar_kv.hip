@@ -138,6 +138,15 @@ hipError_t launch_decode_grouped(const LayerShape& L, int group, const void* q, 
                                  float sm_scale, int n_splits, const PartialsView& out, hipStream_t stream);
 }  // namespace oscar
 
+namespace {
+// Workspace of oscar_decode_step_grouped: the INT2 partials, then (from the next multiple of
+// 256 bytes) the window partials.
+size_t grouped_step_workspace(const oscar_layer_desc* d, int batch, int n_splits) {
+  const size_t a = oscar::partials_bytes(batch, d->n_q_heads, n_splits);
+  return (a + 255) / 256 * 256 + oscar::partials_bytes(batch, d->n_q_heads, window_splits_of(d));
+}
+}  // namespace
+
 extern "C" {
 
 int32_t oscar_version(void) { return 100; }
@@ -328,7 +337,8 @@ int32_t oscar_decode_dense_bf16(const oscar_layer_desc* desc, const void* q, con
 }
 
 size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
-  if (check_desc_impl(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
+  if (check_desc_grouped(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
+  if (desc->group_size != 128) return grouped_step_workspace(desc, batch, n_splits);
   return oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits, window_splits_of(desc));
 }
 
@@ -699,5 +709,52 @@ int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, c
                     "grouped decode launch");
 }
 
+
+int32_t oscar_decode_step_grouped(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                                  const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                                  const float* clip_v, const void* q, const void* rot_k, const void* rot_v, void* pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                  const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                  float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes, float* out,
+                                  void* stream) {
+  int32_t st = check_desc_grouped(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (n_splits <= 0 || n_splits > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d out of [1, 65535]", n_splits);
+  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
+  if (n < 0) return fail(OSCAR_ERR_INVALID_ARG, "n %d < 0", n);
+  if (n > 0 && (!k_src || !v_src || !dst_page || !dst_slot || !clip_k || !clip_v))
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!q || !rot_k || !rot_v || !pool || !block_table || !hist_len || !k_win || !v_win || !win_len || !workspace || !out)
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (2LL * n * desc->n_kv_heads > 0x7FFFFFFFLL)
+    return fail(OSCAR_ERR_UNSUPPORTED, "2 * n * n_kv_heads exceeds the grid limit");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(rot_k) % 16 != 0)
+    return fail(OSCAR_ERR_INVALID_ARG, "q and rot_k must be 16-byte aligned");
+  const size_t need = grouped_step_workspace(desc, batch, n_splits);
+  if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const oscar::LayerShape L = shape_of(desc);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ws = window_splits_of(desc);
+  char* base = static_cast<char*>(workspace);
+  const size_t win_off = (oscar::partials_bytes(batch, desc->n_q_heads, n_splits) + 255) / 256 * 256;
+  const oscar::PartialsView h = oscar::partials_view(base, batch, desc->n_q_heads, n_splits);
+  const oscar::PartialsView w = oscar::partials_view(base + win_off, batch, desc->n_q_heads, ws);
+  if (n > 0) {
+    st = hip_status(oscar::launch_demote_grouped(desc->n_kv_heads, desc->group_size, k_src, v_src, n, dst_page,
+                                                 dst_slot, rot_k, rot_v, clip_k, clip_v, pool, s),
+                    "grouped demote launch");
+    if (st != OSCAR_OK) return st;
+  }
+  st = hip_status(oscar::launch_decode_bf16(L, q, k_win, v_win, win_len, batch, sm_scale, ws, w, s), "window pass launch");
+  if (st != OSCAR_OK) return st;
+  st = hip_status(oscar::launch_decode_grouped(L, desc->group_size, q, rot_k, pool, block_table, max_pages, hist_len,
+                                               batch, sm_scale, n_splits, h, s),
+                  "grouped decode launch");
+  if (st != OSCAR_OK) return st;
+  return hip_status(oscar::launch_merge(L, h, n_splits, w, ws, rot_v, out, batch, s), "merge launch");
+}
 
 }  // extern "C"

@@ -448,6 +448,21 @@ int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, c
                                   int32_t batch, float sm_scale, int32_t n_splits, void* partials,
                                   size_t partials_bytes, void* stream);
 
+/* One decode step over grouped pages: oscar_demote_grouped of the n tokens, then
+ * oscar_decode_bf16, oscar_decode_int2_grouped and oscar_merge, in four launches on `stream`
+ * (the same result as those calls in that order). Arguments as oscar_decode_step, with
+ * n_splits in 1..65535 and no per-split page limit; workspace of at least
+ * oscar_decode_workspace_bytes(desc, batch, n_splits) bytes (for a grouped desc: the INT2
+ * partials, then from the next multiple of 256 bytes the window partials), owned by the
+ * caller, no initialisation needed. q and rot_k 16-byte aligned. */
+int32_t oscar_decode_step_grouped(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                                  const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                                  const float* clip_v, const void* q, const void* rot_k, const void* rot_v, void* pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                  const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                  float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes, float* out,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -103,6 +103,16 @@ def test_grouped_descriptors(lib, group):
     assert dm(r, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_OK
     assert dm(r, FAKE, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
     assert dm(r, FAKE, None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    st = lib.oscar_decode_step_grouped
+    args = [FAKE, FAKE, 0, None, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1, 0.08,
+            4, FAKE]
+    wneed = L.oscar_decode_workspace_bytes(d, 1, 4)
+    a256 = -(-L.oscar_partials_bytes(d, 1, 4) // 256) * 256
+    assert wneed == a256 + L.oscar_partials_bytes(d, 1, L.oscar_window_splits(d))
+    assert st(r, *args, wneed - 1, FAKE, None) == L.OSCAR_ERR_WORKSPACE
+    assert st(r, FAKE, FAKE, 2, None, FAKE, FAKE, FAKE, *args[7:], wneed, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert st(r, *args[:7], None, *args[8:], wneed, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
+    assert lib.oscar_decode_step(r, *args, big, FAKE, None) == L.OSCAR_ERR_UNSUPPORTED
     bad = L.layer_desc(32, 8, 48)
     assert dm(ctypes.byref(bad), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
         L.OSCAR_ERR_UNSUPPORTED

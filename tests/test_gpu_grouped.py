@@ -254,3 +254,48 @@ def test_grouped_full_size_sampled(group):
         for h in range(kv * w.gq, (kv + 1) * w.gq):
             ref = oatt.decode_head(q[h], rk[kv], rv[kv], wk[kv], wv[kv], ref_hist, w.sm_scale)
             assert_close(got[b, h], ref, f"{w.name} g{group} b{b} h{h}")
+
+
+@pytest.mark.parametrize("case,group", [("c2-4k", 32), ("c5-gq8", 64), ("gq16", 32)])
+def test_grouped_step_demotes_then_decodes(case, group):
+    """oscar_decode_step_grouped: every history token but the last of each request goes in
+    through oscar_demote_grouped, the last ones through the step; the pool (every token of
+    every KV head) and the output against the oracle, twice in a row."""
+    w = DECODE_CASES[case]()
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table, n_phys = synth.block_table(w)
+    c = grouped_cache(w, rk_bits, rv_bits, table, n_phys, group)
+    last_k, last_v, last_p, last_s = [], [], [], []
+    hists = [[None] * w.n_kv_heads for _ in range(w.batch)]
+    for b in range(w.batch):
+        rows = [synth.history_rows(w, b, kv) for kv in range(w.n_kv_heads)]
+        n = len(rows[0][0])
+        assert n >= 2
+        hk = np.stack([r[0] for r in rows], 1)
+        hv = np.stack([r[1] for r in rows], 1)
+        j = np.arange(n - 1)
+        c.demote(bf16(hk[:-1]), bf16(hv[:-1]), torch.from_numpy(table[b, j // 64].astype(np.int32)).cuda(),
+                 torch.from_numpy((j % 64).astype(np.int32)).cuda())
+        last_k.append(hk[-1])
+        last_v.append(hv[-1])
+        last_p.append(table[b, (n - 1) // 64])
+        last_s.append((n - 1) % 64)
+        for kv in range(w.n_kv_heads):
+            hists[b][kv], _, _ = oracle_history_grouped(w, b, kv, rk, rv, group)
+    refs = decode_refs(w, rk, rv, hists)
+    pages = torch.tensor(np.array(last_p, np.int32)).cuda()
+    slots = torch.tensor(np.array(last_s, np.int32)).cuda()
+    c.set_splits(5)
+    q = queries(w)
+    for rep in range(2):
+        say(case, "grouped step", "group", group, "B", w.batch, "call", rep)
+        c.out.fill_(np.nan)
+        got = c.step(bf16(np.stack(last_k)), bf16(np.stack(last_v)), pages, slots, q, w.sm_scale).cpu().numpy()
+        for b in range(w.batch):
+            assert_close(got[b], refs[b], f"{case} g{group} step b{b} call {rep}")
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, ogroups.head_block_bytes(group))
+    for b in range(w.batch):
+        for kv in range(w.n_kv_heads):
+            ref, km, vm = oracle_history_grouped(w, b, kv, rk, rv, group)
+            got_h = unpack_grouped(pool, table[b], kv, w.hist_len(b), group)
+            compare_history(got_h, ref, km, vm, f"{case} g{group} step pool b{b} kv{kv}")
