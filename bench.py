@@ -468,6 +468,12 @@ def main():
         g_decode(insts[0])
         g_ms = timed(g_decode, args.steps)
         g_int2_ms = timed(g_int2, args.steps)
+
+        def g_step(c):
+            c.step(step_k, step_v, step_page, step_slot, q, w.sm_scale, stream)
+
+        g_step(insts[0])
+        g_step_ms = timed(g_step, args.steps)
         insts = saved
         g_bytes = int(sum(w.hist_lens)) * w.n_kv_heads * (64 + 8 * ng) + w.n_kv_heads * ROT_BYTES + \
             w.batch * w.n_q_heads * 128 * 2
@@ -478,6 +484,8 @@ def main():
             "splits": gins[0].n_splits,
             "int2_pass_us_by_splits": {str(k): round(v * 1e3, 3) for k, v in sorted(sweep.items())},
             "us_per_decode": round(g_ms * 1e3, 3),
+            "us_per_step": round(g_step_ms * 1e3, 3),
+            "step_entry": "oscar_decode_step_grouped (demote one token per request, window pass, grouped pass, merge)",
             "int2_pass_us_per_launch": round(g_int2_ms * 1e3, 3),
             "bound": "hbm",
             "achieved": round(g_bytes / (g_int2_ms * 1e-3) / 1e9, 2),
