@@ -17,7 +17,8 @@
 // intervals, compensated sums when they do not settle; the extremes, scale and zero point are
 // taken per group (a group's dims are held by 64 / n_g consecutive lanes of wave 0).
 // INT2 pass: a plain dequantise-and-FMA pass on the vector ALU (the one-group path's matrix-
-// core pass is not generalised): grid (split, KV head, request), 256 threads; per page, thread
+// core pass is not generalised) after the query rotation on bf16 MFMA: grid (split, KV head,
+// request), 256 threads; per page, thread
 // (token, quarter of the dims) scores its token against every query head of the KV head; the
 // weights take an online softmax in log2 units and are multiplied by each slot's V scale of
 // every group (the zero points summed once per page); thread (dim, half of the slots) adds
@@ -28,6 +29,9 @@
 
 namespace oscar {
 namespace {
+
+typedef float gf32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 
 template <int NG>
 constexpr int grouped_block_bytes() {
@@ -206,43 +210,55 @@ __global__ __launch_bounds__(256) void decode_grouped_kernel(
   const int b = blockIdx.z;
   const int h0 = kv * GQ;
 
-  // ---- q_rot = q R_K of the KV head's query heads (fp32 sums of exact bf16 products, in
-  // order of the rows of R_K): the queries and R_K, in two halves of 64 rows, pass through
-  // LDS in 16-byte loads that are all in flight at once
+  // ---- q_rot = q R_K of the KV head's query heads: the queries and R_K, in two halves of 64
+  // rows, pass through LDS in 16-byte loads that are all in flight at once
   for (int idx = t; idx < GQ * kHeadDim / 8; idx += 256) {
     const int h = idx >> 4;
     const int ch = idx & 15;
     *reinterpret_cast<uint4*>(&q_s[h][8 * ch]) =
         *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(b) * n_q + h0 + h) * kHeadDim + 8 * ch);
   }
-  constexpr int kOut = (GQ * kHeadDim + 255) / 256;  // q_rot entries per thread
-  float qacc[kOut];
+  // q_rot on the matrix cores (v_mfma_f32_16x16x32_bf16; bf16 products are exact, sums fp32):
+  // A = the query rows (head n of lane (g, n), zero past GQ), B = R_K columns; wave w owns
+  // dims 32 w .. 32 w + 31 (two 16-dim tiles); lane (g, n) ends with heads 4 g + i of dim n
+  {
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int g = lane >> 4;
+    const int n = lane & 15;
+    gf32x4 qc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int hf = 0; hf < 2; ++hf) {
+      __syncthreads();  // the previous half is no longer read
+      for (int idx = t; idx < 64 * kHeadDim / 8; idx += 256) {
+        const int row = idx >> 4;
+        const int ch = idx & 15;
+        *reinterpret_cast<uint4*>(&rot_s[row][8 * ch]) = *reinterpret_cast<const uint4*>(
+            rot_k + (static_cast<size_t>(kv) * kHeadDim + 64 * hf + row) * kHeadDim + 8 * ch);
+      }
+      __syncthreads();
 #pragma unroll
-  for (int o = 0; o < kOut; ++o) qacc[o] = 0.f;
-  for (int hf = 0; hf < 2; ++hf) {
-    __syncthreads();  // the previous half is no longer read
-    for (int idx = t; idx < 64 * kHeadDim / 8; idx += 256) {
-      const int row = idx >> 4;
-      const int ch = idx & 15;
-      *reinterpret_cast<uint4*>(&rot_s[row][8 * ch]) = *reinterpret_cast<const uint4*>(
-          rot_k + (static_cast<size_t>(kv) * kHeadDim + 64 * hf + row) * kHeadDim + 8 * ch);
-    }
-    __syncthreads();
+      for (int st = 0; st < 2; ++st) {
+        const int r0 = 32 * st + 8 * g;  // first R_K row (within the half) of this lane's k range
+        const uint4 av = n < GQ ? *reinterpret_cast<const uint4*>(&q_s[n < GQ ? n : 0][64 * hf + r0])
+                                : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int o = 0; o < kOut; ++o) {
-      const int idx = t + 256 * o;
-      if (idx < GQ * kHeadDim) {
-        const int h = idx / kHeadDim;
-        const int d = idx % kHeadDim;
-#pragma unroll 16
-        for (int i = 0; i < 64; ++i) qacc[o] = fmaf(bf16_to_f32(q_s[h][64 * hf + i]), bf16_to_f32(rot_s[i][d]), qacc[o]);
+        for (int j = 0; j < 2; ++j) {
+          const int col = 32 * wave + 16 * j + n;
+          uint32_t bw[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            bw[k] = static_cast<uint32_t>(rot_s[r0 + 2 * k][col]) | (static_cast<uint32_t>(rot_s[r0 + 2 * k + 1][col]) << 16);
+          const uint4 bv = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+          qc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gbf16x8, av),
+                                                         __builtin_bit_cast(gbf16x8, bv), qc[j], 0, 0, 0);
+        }
       }
     }
-  }
 #pragma unroll
-  for (int o = 0; o < kOut; ++o) {
-    const int idx = t + 256 * o;
-    if (idx < GQ * kHeadDim) qr_s[idx / kHeadDim][idx % kHeadDim] = qacc[o];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i < GQ) qr_s[4 * g + i][32 * wave + 16 * j + n] = qc[j][i];
   }
   if (t < GQ) {
     m_s[t] = -INFINITY;
