@@ -255,7 +255,10 @@ def test_codebook_step_demotes_then_decodes(case):
         assert_close(got[b], oracle_decode_cb(w, b, rk, rv, hists, klv, vlv), f"{case} codebook step b{b}")
 
 
-FULL_SAMPLES_CB = {2: [(0, 0), (0, 5)], 3: [(0, 6)], 5: [(2, 1), (3, 7)]}
+# every KV head of the 32K workload; four pairs of the 100K and 128K workloads, the last
+# request and the last KV head among them
+FULL_SAMPLES_CB = {2: [(0, kv) for kv in range(8)], 3: [(0, 0), (0, 3), (0, 6), (0, 7)],
+                   5: [(0, 0), (1, 4), (2, 1), (3, 7)]}
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 5])

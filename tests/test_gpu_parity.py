@@ -451,52 +451,84 @@ def test_demote_rows_kernel_random_and_exact_ties():
 
 # ------------------------------------------------------------------- full-size workloads
 
-FULL_SAMPLES = {2: [(0, 0), (0, 7)], 3: [(0, 3)], 4: [(0, 0), (63, 5)], 5: [(1, 2), (3, 7)]}
+# (request, KV head) pairs compared at full size: every KV head of the batch-1 workloads;
+# at batch 64 and at 128K, ten and eight pairs spread over requests and heads, the last
+# request and the last KV head among them
+FULL_PAIRS = {
+    2: [(0, kv) for kv in range(8)],
+    3: [(0, kv) for kv in range(8)],
+    4: [(0, 0), (7, 3), (15, 6), (22, 1), (31, 4), (40, 2), (48, 7), (56, 5), (63, 0), (63, 7)],
+    5: [(0, 0), (0, 7), (1, 2), (1, 5), (2, 1), (2, 6), (3, 3), (3, 7)],
+}
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_end_to_end_sampled(cfg):
-    """The whole GPU path at the workload's real size: every history token demoted on the
-    GPU, then decoded with the default split count; sampled KV heads compared with the
-    oracle (pool bytes and the outputs of their query heads)."""
-    from bit_kv_cache_oscar_amd import oscar_default_splits
+def test_full_size_benchmarked_path(cfg):
+    """The whole GPU path at the workload's real size, in the launch configuration the
+    benchmark times: every history token but the last demoted through oscar_demote (the
+    bulk kernel), then oscar_decode_step at the library's default split count, which
+    demotes the last token of each request and decodes in two launches (prepare; attend =
+    INT2 pass with the in-launch ticket merge). Then the attend launch alone, twice, on the
+    workspace the step prepared (what the benchmark's roofline row times), oscar_decode
+    (the two launches without demotion) and the four separate entry points. Pool bytes and
+    the outputs of every query head of the listed (request, KV head) pairs are compared
+    with the oracle; every path must meet the decode tolerance."""
+    from bit_kv_cache_oscar_amd import oscar_attend, oscar_default_splits
 
     w = synth.workload(cfg)
     (rk_bits, rv_bits), (rk, rv) = rotations(w)
     table, n_phys = synth.block_table(w)
     c = make_cache(w, rk_bits, rv_bits, table, n_phys)
     say("full size", w.name, "pages", n_phys)
-    shared_done = False
+    last_k, last_v, last_p, last_s = [], [], [], []
     for b in range(w.batch):
         n = w.hist_len(b)
-        start = 0
-        if w.shared_pages and b > 0:
-            start = min(n, w.shared_pages * 64)   # the shared prefix is demoted once
+        start = min(n, w.shared_pages * 64) if (w.shared_pages and b > 0) else 0
+        assert n - 1 > start
         ks, vs = [], []
         for kv in range(w.n_kv_heads):
             k, v = synth.kv_rows(w, b, kv, 64 + start, 64 + n)
             ks.append(k)
             vs.append(v)
+        ks, vs = np.stack(ks, 1), np.stack(vs, 1)
         j = np.arange(start, n)
-        _demote_all(c, w, b, table[b, j // 64], j % 64, np.stack(ks, 1), np.stack(vs, 1))
-        shared_done = True
-    assert shared_done
+        _demote_all(c, w, b, table[b, j[:-1] // 64], j[:-1] % 64, ks[:-1], vs[:-1])
+        last_k.append(ks[-1])
+        last_v.append(vs[-1])
+        last_p.append(table[b, (n - 1) // 64])
+        last_s.append((n - 1) % 64)
+        del ks, vs
     s = oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max()))
     c.set_splits(s)
-    out = c.decode(queries(w), w.sm_scale)
+    q = queries(w)
+    dev = torch.device("cuda")
+    pg = torch.tensor(np.array(last_p, np.int32), device=dev)
+    sl = torch.tensor(np.array(last_s, np.int32), device=dev)
+    say("full size step", w.name, "splits", s, "grid", s * w.n_kv_heads * max(1, w.gq // 8) * w.batch)
+    outs = {"step": c.step(bf16(np.stack(last_k)), bf16(np.stack(last_v)), pg, sl, q, w.sm_scale).cpu().numpy()}
+    for rep in range(2):
+        say("full size attend alone", w.name, "call", rep)
+        c.out.fill_(np.nan)
+        oscar_attend(c.desc, c.rot_v, c.pool, c.block_table, c.hist_len, s, c.workspace, c.out)
+        outs[f"attend {rep}"] = c.out.cpu().numpy()
+    c.out.fill_(np.nan)
+    say("full size two-launch decode", w.name)
+    outs["decode_fused"] = c.decode_fused(q, w.sm_scale).cpu().numpy()
+    c.out.fill_(np.nan)
+    say("full size four entry points", w.name)
+    outs["decode"] = c.decode(q, w.sm_scale).cpu().numpy()
     torch.cuda.synchronize()
-    got = out.cpu().numpy()
     pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
-    for b, kv in FULL_SAMPLES[cfg]:
-        say("full size sample", w.name, "b", b, "kv", kv, "splits", s)
+    for b, kv in FULL_PAIRS[cfg]:
+        say("full size compare", w.name, "b", b, "kv", kv)
         ref_hist, km, vm = oracle_history(w, b, kv, rk, rv)
         gpu_hist = opages.unpack_history(pool, table[b], kv, w.hist_len(b))
         compare_history(gpu_hist, ref_hist, km, vm, f"{w.name} b{b} kv{kv}")
-        hists = {kv: ref_hist}
         heads = range(kv * w.gq, (kv + 1) * w.gq)
-        ref = oracle_decode(w, b, rk, rv, hists, heads=heads)
-        for h in heads:
-            assert_close(got[b, h], ref[h], f"{w.name} b{b} h{h}")
+        ref = oracle_decode(w, b, rk, rv, {kv: ref_hist}, heads=heads)
+        for name, got in outs.items():
+            for h in heads:
+                assert_close(got[b, h], ref[h], f"{w.name} {name} b{b} h{h}")
 
 
 STEP_CASES = ["c1", "c2-4k", "c4-shared-ragged", "c5-gq8", "gq16", "edges"]
@@ -553,3 +585,84 @@ def test_decode_step_demotes_then_decodes(case):
             hists[kv] = ref_hist
         ref = oracle_decode(w, b, rk, rv, hists)
         assert_close(got[b], ref, f"{case} step b{b}")
+
+
+def plain_rotations(kind, n_kv):
+    """(bits [n_kv, 128, 128] from the library's host builder, fp64 values from the oracle)
+    for R = H P (Hadamard and bit reversal, no eigenbasis: the eigenbasis of a diagonal
+    covariance with descending entries is the identity) or R = I (no rotation)."""
+    from bit_kv_cache_oscar_amd import rotation as prot
+    from oracle import rotation as orot
+
+    if kind == "identity":
+        bits = np.zeros((128, 128), np.uint16)
+        bits[np.arange(128), np.arange(128)] = 0x3F80
+        vals = np.eye(128)
+    else:
+        sigma = np.diag(np.arange(128, 0, -1).astype(np.float64))
+        bits = prot.bf16_bits_from_f64(prot.rotation_fp64(sigma))
+        vals = orot.round_bf16(orot.rotation_from_covariance(sigma))
+        hp = orot.sylvester_hadamard(128) @ orot.bit_reversal_matrix(128)
+        assert np.array_equal(vals, orot.round_bf16(hp))
+    assert np.array_equal(bits_to_f64(bits), vals)
+    return np.repeat(bits[None], n_kv, 0), np.repeat(vals[None], n_kv, 0)
+
+
+@pytest.mark.parametrize("case", ["c2-4k", "c5-gq8", "c4-shared-ragged"])
+@pytest.mark.parametrize("kind", ["hadamard"])
+def test_plain_rotations_demote_and_decode(kind, case):
+    """R = H P (Hadamard and bit reversal without the eigenbasis, the QuaRot-style baseline
+    the pages compare with) and R = I (naive INT2): the whole history demoted on the GPU (the
+    last token of each request through oscar_decode_step), then decoded through the step,
+    the attend launch alone, oscar_decode and the four separate entry points; the pool and
+    every output against the oracle."""
+    from bit_kv_cache_oscar_amd import oscar_attend, oscar_default_splits
+
+    w = DECODE_CASES[case]()
+    rk_bits, rk = plain_rotations(kind, w.n_kv_heads)
+    table, n_phys = synth.block_table(w)
+    c = make_cache(w, rk_bits, rk_bits, table, n_phys)
+    last_k, last_v, last_p, last_s = [], [], [], []
+    hists = [[None] * w.n_kv_heads for _ in range(w.batch)]
+    for b in range(w.batch):
+        n = w.hist_len(b)
+        start = min(n, w.shared_pages * 64) if (w.shared_pages and b > 0) else 0
+        ks, vs = [], []
+        for kv in range(w.n_kv_heads):
+            k, v = synth.kv_rows(w, b, kv, 64 + start, 64 + n)
+            ks.append(k)
+            vs.append(v)
+            hists[b][kv], _, _ = oracle_history(w, b, kv, rk, rk)
+        ks, vs = np.stack(ks, 1), np.stack(vs, 1)
+        j = np.arange(start, n)
+        if n - 1 > start:
+            _demote_all(c, w, b, table[b, j[:-1] // 64], j[:-1] % 64, ks[:-1], vs[:-1])
+        if n - 1 >= start:
+            last_k.append(ks[-1])
+            last_v.append(vs[-1])
+            last_p.append(table[b, (n - 1) // 64])
+            last_s.append((n - 1) % 64)
+    s = oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max()))
+    c.set_splits(s)
+    q = queries(w)
+    dev = torch.device("cuda")
+    pg = torch.tensor(np.array(last_p, np.int32), device=dev)
+    sl = torch.tensor(np.array(last_s, np.int32), device=dev)
+    say(case, kind, "step", "B", w.batch, "splits", s)
+    outs = {"step": c.step(bf16(np.stack(last_k)), bf16(np.stack(last_v)), pg, sl, q, w.sm_scale).cpu().numpy()}
+    c.out.fill_(np.nan)
+    oscar_attend(c.desc, c.rot_v, c.pool, c.block_table, c.hist_len, s, c.workspace, c.out)
+    outs["attend"] = c.out.cpu().numpy()
+    c.out.fill_(np.nan)
+    outs["decode_fused"] = c.decode_fused(q, w.sm_scale).cpu().numpy()
+    c.out.fill_(np.nan)
+    outs["decode"] = c.decode(q, w.sm_scale).cpu().numpy()
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
+    for b in range(w.batch):
+        for kv in range(w.n_kv_heads):
+            ref_hist, km, vm = oracle_history(w, b, kv, rk, rk)
+            gpu_hist = opages.unpack_history(pool, table[b], kv, w.hist_len(b))
+            compare_history(gpu_hist, ref_hist, km, vm, f"{case} {kind} b{b} kv{kv}")
+        ref = oracle_decode(w, b, rk, rk, hists[b])
+        for name, got in outs.items():
+            assert_close(got[b], ref, f"{case} {kind} {name} b{b}")
