@@ -71,6 +71,11 @@ _SIGNATURES = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
                                     c_void_p, c_void_p]),
+    "oscar_decode_step_noalloc_max_bytes": (c_size_t, []),
+    "oscar_decode_step_noalloc": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                            c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                            c_int32, c_void_p, c_void_p]),
     "oscar_decode_step_grouped": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                             c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32,
@@ -499,6 +504,35 @@ def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k,
     else:
         _check_codebook(desc, codebook)
         _check(lib().oscar_decode_step_codebook(byref(desc), *head, _ptr(codebook), *rest))
+
+
+def oscar_decode_step_noalloc_max_bytes() -> int:
+    return int(lib().oscar_decode_step_noalloc_max_bytes())
+
+
+def oscar_decode_step_noalloc(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v,
+                              pool, block_table, hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int,
+                              out, stream=None):
+    """oscar_decode_step with the library's static device workspace instead of a caller's
+    (for callers that cannot allocate); uniform INT2 levels, one group per vector."""
+    _need(desc.group_size == 128, "the no-allocation step reads one-group pages")
+    batch = int(q.shape[0])
+    _need(out.is_cuda and out.dtype.is_floating_point and out.element_size() == 4
+          and out.numel() == batch * desc.n_q_heads * HEAD_DIM, "out must be float32 [batch, n_q_heads, 128]")
+    n = int(k_src.shape[0]) if k_src is not None and k_src.dim() else 0
+    if n:
+        hkv = desc.n_kv_heads
+        _device16(k_src, "k_src")
+        _device16(v_src, "v_src")
+        _need(k_src.numel() == n * hkv * HEAD_DIM and v_src.numel() == n * hkv * HEAD_DIM,
+              "k_src/v_src must be [n, n_kv_heads, 128]")
+        _device_i32(dst_page, "dst_page", n)
+        _device_i32(dst_slot, "dst_slot", n)
+    _check(lib().oscar_decode_step_noalloc(
+        byref(desc), _ptr(k_src) if n else None, _ptr(v_src) if n else None, n, _ptr(dst_page) if n else None,
+        _ptr(dst_slot) if n else None, _ptr(clip_k) if n else None, _ptr(clip_v) if n else None, _ptr(q),
+        _ptr(rot_k), _ptr(rot_v), _ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len),
+        _ptr(k_win), _ptr(v_win), _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(out), _stream(stream)))
 
 
 def oscar_decode_step_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v,

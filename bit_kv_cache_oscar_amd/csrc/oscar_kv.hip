@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "launch.h"
 #include "oscar_kv.h"
 
@@ -538,6 +540,74 @@ int32_t oscar_decode_codebook(const oscar_layer_desc* desc, const void* q, const
   return step_impl(desc, nullptr, nullptr, 0, nullptr, nullptr, nullptr, nullptr, q, rot_k, rot_v,
                    reinterpret_cast<const uint32_t*>(codebook), const_cast<void*>(pool), block_table, max_pages,
                    hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, out, stream);
+}
+
+}  // extern "C"
+
+// ---- the decode step without a caller workspace ----------------------------------------
+//
+// For callers that cannot allocate device memory (code under HIP graph capture, serving
+// loops that forbid hipMalloc): the step's workspace (INT2 and window partials, query
+// data, arrival counters) is this file-scope device array instead. Every GPU the library
+// runs on holds its own copy until the process ends. Its address on the current device is
+// taken once, with hipGetSymbolAddress, and kept per device: in host code the array's name
+// is not a device address.
+namespace {
+
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(16) << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the current device (looked up on the first call there).
+int32_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(OSCAR_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(OSCAR_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return OSCAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t oscar_decode_step_noalloc_max_bytes(void) { return kStaticScratchBytes; }
+
+int32_t oscar_decode_step_noalloc(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                                  const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                                  const float* clip_v, const void* q, const void* rot_k, const void* rot_v, void* pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                  const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                  float sm_scale, int32_t n_splits, float* out, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (n_splits <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d <= 0", n_splits);
+  if (batch > 65535 || n_splits > 256)
+    return fail(OSCAR_ERR_UNSUPPORTED, "batch %d or n_splits %d out of range", batch, n_splits);
+  const size_t need = oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits,
+                                                  window_splits_of(desc));
+  if (need > kStaticScratchBytes)
+    return fail(OSCAR_ERR_WORKSPACE, "step needs %zu bytes of workspace; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != OSCAR_OK) return st;
+  return step_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, nullptr, pool,
+                   block_table, max_pages, hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, ws,
+                   kStaticScratchBytes, out, stream);
 }
 
 }  // extern "C"

@@ -242,6 +242,28 @@ int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const
                           int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * oscar_decode_step_noalloc: oscar_decode_step without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving loops that
+ * forbid hipMalloc). The same kernels and the same result as oscar_decode_step; its
+ * workspace is a static device array of oscar_decode_step_noalloc_max_bytes() bytes
+ * (16 MiB) that the library holds on every GPU it runs on until the process ends.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library call.
+ *   Errors: OSCAR_ERR_WORKSPACE when oscar_decode_workspace_bytes(desc, batch, n_splits)
+ *   exceeds the array (nothing is enqueued); otherwise those of oscar_decode_step.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time on one GPU
+ * (on different streams, or from different threads) race and must not be issued. The
+ * array keeps the last call's contents; the step's first launch clears the arrival
+ * counters it needs at zero. `stream` must belong to the current device.
+ */
+size_t oscar_decode_step_noalloc_max_bytes(void);
+int32_t oscar_decode_step_noalloc(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
+                                  const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
+                                  const float* clip_v, const void* q, const void* rot_k, const void* rot_v, void* pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                  const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                  float sm_scale, int32_t n_splits, float* out, void* stream);
+
+/*
  * oscar_decode: decode attention over the three segments in two launches, without
  * demotion (oscar_decode_step with n == 0; the pool is only read).
  * (QbitAI article on OSCAR, serving-path section: INT2 and BF16 segments processed
