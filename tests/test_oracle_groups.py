@@ -7,6 +7,9 @@ import numpy as np
 import pytest
 
 from oracle import attention, groups, pages, quant
+from oracle import groups as ogroups
+
+import synth
 from oracle.rotation import round_bf16, rotation_from_covariance
 
 EYE = np.eye(128)
@@ -113,3 +116,70 @@ def test_attention_over_a_lossless_grouped_history():
     got = attention.decode_head(q, EYE, EYE, wk, wv, (kc, ks, kz, vc, vs, vz), 0.1)
     want = attention.softmax_attention(q, np.vstack([y[0], wk]), np.vstack([y[1], wv]), 0.1)
     assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# What the bit reversal buys (QbitAI article on OSCAR, section on aiming the rotation at
+# attention: the bit-reversal permutation makes the INT2 groups more even, so that no group
+# is dominated by a few outlier channels; the accuracy section compares with a
+# Hadamard-only rotation and with plain INT2). Measured on the oracle with the workloads'
+# outlier rows, for R = U H P against U H (no bit reversal), H P (no eigenbasis) and I.
+
+def _variants(w, kv):
+    from oracle import rotation as orot
+
+    q, k, v = synth.calibration_set(w, kv)
+    h = orot.sylvester_hadamard(128)
+    p = orot.bit_reversal_matrix(128)
+    out = {}
+    for name, sigma in (("K", orot.key_covariance(q)), ("V", orot.value_covariance(q, k, v, w.sm_scale))):
+        _, u = orot.eigenbasis(sigma)
+        out[name] = {"UHP": orot.round_bf16(u @ h @ p), "UH": orot.round_bf16(u @ h),
+                     "HP": orot.round_bf16(h @ p), "I": np.eye(128)}
+    return out
+
+
+def _errors(x, r, clip, group, q=None):
+    """(relative squared reconstruction error in the rotated basis, relative squared error of
+    the attention logits q . k when q is given) of rows x under rotation r and group size."""
+    from oracle import quant as oquant
+
+    if group == 128:
+        c, s, z, _ = oquant.quantize_rows(x, r, clip)
+        yh = oquant.dequantize(c, s, z)
+    else:
+        c, s, z, _ = ogroups.quantize_rows_grouped(x, r, clip, group)
+        yh = ogroups.dequantize_grouped(c, s, z, group)
+    y = x @ r
+    rec = float(np.sum((yh - y) ** 2) / np.sum(y ** 2))
+    if q is None:
+        return rec, None
+    qr = q @ r
+    ref = q @ x.T
+    logit = float(np.sum((qr @ yh.T - ref) ** 2) / np.sum(ref ** 2))
+    return rec, logit
+
+
+@pytest.mark.parametrize("cfg,kv", [(2, 0), (5, 3)])
+def test_bit_reversal_balances_the_groups(cfg, kv):
+    """At one group per vector the bit reversal only reorders the group (U H P and U H give
+    the same error); at groups of 64 and 32 rotated dims it lowers the reconstruction error
+    and the key side's attention-logit error well below U H's; the eigenbasis matters too
+    (U H P beats H P at every group size), and plain INT2 (R = I) is far worse."""
+    w = synth.workload(cfg)
+    rots = _variants(w, kv)
+    hk, hv = synth.kv_rows(w, 0, kv, 64, 64 + 384)
+    q = synth.query(w, 0).astype(np.float64)[kv * w.gq:(kv + 1) * w.gq]
+    for name, x in (("K", hk.astype(np.float64)), ("V", hv.astype(np.float64))):
+        for group in (128, 64, 32):
+            err = {rn: _errors(x, r, w.clip_ratio, group, q if name == "K" else None)
+                   for rn, r in rots[name].items()}
+            rec = {k: v[0] for k, v in err.items()}
+            what = f"cfg {cfg} kv {kv} {name} G {group}: {rec}"
+            if group == 128:
+                assert rec["UHP"] == pytest.approx(rec["UH"], rel=1e-9), what
+            else:
+                assert rec["UHP"] < (0.8 if group == 64 else 0.4) * rec["UH"], what
+                if name == "K":
+                    assert err["UHP"][1] < (0.8 if group == 64 else 0.4) * err["UH"][1], what
+            assert rec["UHP"] < 0.95 * rec["HP"] and rec["UHP"] < 0.5 * rec["I"], what
