@@ -5,26 +5,46 @@
 // history, with a scale and zero point per group. The quantiser is the one demote_pass.h
 // implements per row; this kernel reaches the same scales and codes for many rows at once.
 //
-// A workgroup (4 waves) takes up to 256 consecutive rows (tokens) of one (KV head, K or V)
-// with R^T staged in LDS; a wave does 32 tokens per iteration as two 16-token tiles:
-//   y^T = R^T x^T on v_mfma_f32_16x16x32_bf16 (bf16 products are exact, sums in fp32), so
-//   lane (G, n) of a tile holds dims 16 mt + 4 G + e (mt < 8, e < 4) of token n.
-// The fp32 sums differ from the exact ones by at most delta = 16 2^-24 |x| max_j |R_:,j|
-// (Cauchy-Schwarz bounds sum_i |x_i R_ij| by |x| |R_:,j|; the matrix cores' fp32
-// accumulation was measured below 2.3 2^-24 |x| |R_:,j|, and below 6.4 2^-24 sum |x_i R_ij|,
-// on adversarial magnitude mixes, so 16 leaves a margin of 7).
-// Scales and zero points are then fixed exactly:
-//   - the exact extremes lie within delta of the fp32 ones; the fp64 chain of the quantiser
-//     is monotone in both, so when both ends of that interval round to the same fp16 scale
-//     and zero point, those are the values the exact extremes give;
-//   - otherwise the candidates (dims within 2 delta of an fp32 extreme) are summed again in
-//     fp64 from the exact products, four at a time (one per 16-lane group, a DPP tree), with
-//     an error bound of its own, and the same interval test runs on those sums; when even
-//     that leaves the fp16 values open, compensated (two-sum) sums across the wave give the
-//     exact extremes and the chain runs on them.
-// Codes come from the fp32 y when delta / s16 <= 9e-5, which keeps every code on the side of
-// its rounding boundary the exact value is on unless the exact value lies within 1e-4 of
-// the boundary; a token failing that test has all 128 values summed exactly instead.
+// A workgroup (4 waves) takes up to 1024 consecutive rows (tokens) of one (KV head, K or V)
+// with R^T staged in LDS; a wave does 32 tokens per iteration as two 16-token tiles, the
+// two tiles' extremes, interval tests and exact sums taken together (their dependency
+// chains interleave, and one exact pass serves both):
+//   y^T = R^T x^T as four 32-deep chunks on v_mfma_f32_16x16x32_bf16, each from a zero
+//   accumulator, joined on the vector ALU as ((c0 + c1) + c2) + c3; lane (G, n) of a tile
+//   holds dims 16 mt + 4 G + e (mt < 8, e < 4) of token n.
+//
+// Error of the fp32 values. A chunk is 32 exact products (a bf16 x bf16 product fits fp32)
+// joined by at most 32 fp32 additions in whatever order and grouping the matrix core uses.
+// Assuming only that each such addition lands within one fp32 ulp of its exact result (true
+// of rounding to nearest, of truncation and of any faithful rounding) and that subnormal
+// inputs and results may be flushed to zero, the classical bound for summation in any
+// order (Higham, Accuracy and Stability of Numerical Algorithms, 2nd ed., section 4.2, with
+// unit 2^-23 per addition) bounds a chunk's error by gamma_32 sum |p| over its products,
+// gamma_32 < 32 2^-23 (1 + 2^-17); the three joins round to nearest (unit 2^-24), adding at
+// most 3 2^-24 (1 + 2^-15) sum |p|. With sum_i |x_i R_ij| <= |x| max_j |R_:,j|
+// (Cauchy-Schwarz),
+//   delta = 68 2^-24 (|x| max_j |R_:,j| (1 + 2^-10) + 2^-60) + 2^-116
+// bounds the error of every value of the token (the norms are fp32 sums of exact squares,
+// covered by the factor 1 + 2^-10; 2^-60 covers squares flushed to zero, 2^-116 the at most
+// 259 flushed products and partial sums of 2^-126 each). The matrix cores' own summation
+// order is thus never relied on, only this per-addition bound.
+//
+// Scales and zero points (bit for bit the quantiser's):
+//   - the exact extremes lie within delta of the fp32 ones and the quantiser's fp64 chain is
+//     monotone in both: when both ends of those intervals round to the same fp16 scale and
+//     zero point (evaluated in fp32 with outward margins), those are the values;
+//   - otherwise the candidates (values within 3 delta of an fp32 extreme) are summed again
+//     in fp64 from the exact products, 16 lanes per sum, four sums at a time, for every
+//     undecided token of the tile together (|error| <= 11 2^-53 sum |p| < 2^-31 delta), and the
+//     same test runs in fp64;
+//   - when even that interval holds an fp16 rounding boundary, compensated (two-sum) sums
+//     over the wave give the extremes and the chain runs on them.
+// Codes: from the fp32 values, except a value whose t = (y - z16) / s16 lies within the
+// error bound of t of a rounding boundary (exact ties included): it is summed again in
+// fp64 and decided on that interval, and by a compensated sum when the interval still
+// holds the boundary, so ties round to even as the quantiser says. A token whose bound on
+// t exceeds 2^-7 (its range tiny next to its norm) has all 128 values summed with
+// compensation instead.
 // With a codebook (the Lloyd-Max variant) the scale, zero point and every interval test are
 // the same, and each code is the nearest codebook level of t instead (boundaries: the
 // midpoints between levels).
@@ -42,14 +62,14 @@ constexpr int kBWaves = 4;
 constexpr int kIters = 8;                              // 32-token iterations per wave
 constexpr int kRowsPerBlock = kBWaves * 32 * kIters;   // 1024
 constexpr int kRTRow = kHeadDim + 8;                   // bf16 per LDS row of R^T (16 bytes of bank spread)
-constexpr double kAccUlps = 16.0;                      // fp32 accumulation budget, units of 2^-24 |x| max|R_:,j|
-constexpr double kCodeSlack = 9e-5;                    // largest tolerated error of t = (y - z16) / s16
+constexpr float kGamma = 68.f * 0x1p-24f;              // chunk bound plus the three joins, per sum |p|
+constexpr float kFullT = 0x1p-7f;                      // bound on t above which a token is summed exactly
 
 struct BulkSmem {
-  uint16_t rt[kHeadDim * kRTRow];   // R^T: row j holds column j of R
-  uint32_t stage[kBWaves][1024];    // per wave, one tile: x rows (bf16 [16][128]) or codes (bytes)
-  uint32_t fb[kBWaves][16][8];      // per wave, one tile: exact 2-bit codes of tokens summed exactly
-  float colmax2;                    // max_j |R_:,j|^2
+  uint16_t rt[kHeadDim * kRTRow];             // R^T: row j holds column j of R
+  uint16_t xs[kBWaves][2][16 * kHeadDim];     // per wave, the x rows of the iteration's two tiles (bf16 [16][128])
+  unsigned char cs[kBWaves][16 * kHeadDim];   // per wave, the codes of the current tile
+  float colmax2[kBWaves];                     // per wave's share, max_j |R_:,j|^2
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -74,7 +94,8 @@ __device__ __forceinline__ void scale_zero(double cr, double ymax, double ymin, 
 }
 
 // sum_i x_i R_ij in fp64 from the exact products, by the whole wave: lane L takes i = 2L, 2L+1
-// and the 64 (sum, compensation) pairs are joined by two-sum steps; every lane gets the result
+// and the 64 (sum, compensation) pairs are joined by two-sum steps; every lane gets the
+// result (within 2^-52 of it plus 2^-100 sum |p| of the exact sum)
 __device__ __forceinline__ double coop_dot(const uint16_t* xrow, const uint16_t* rtrow, int lane) {
 #pragma clang fp contract(off)
   const uint32_t xv = *reinterpret_cast<const uint32_t*>(xrow + 2 * lane);
@@ -112,17 +133,31 @@ __device__ __forceinline__ double group_dot(const uint16_t* xrow, const uint16_t
   const uint4 rv = *reinterpret_cast<const uint4*>(rtrow + 8 * q);
   const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
   const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+  // fma: each product is exact in fp64, so the fused step rounds exactly as a sum does
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    s += bf16lo(xw[k]) * bf16lo(rw[k]);
-    s += bf16hi(xw[k]) * bf16hi(rw[k]);
+    s = fma(bf16lo(xw[k]), bf16lo(rw[k]), s);
+    s = fma(bf16hi(xw[k]), bf16hi(rw[k]), s);
   }
   s += dpp_f64<kDppQuadXor1>(s);
   s += dpp_f64<kDppQuadXor2>(s);
   s += dpp_f64<kDppHalfMirror>(s);
   s += dpp_f64<kDppMirror>(s);
   return s;
+}
+
+__device__ __forceinline__ double lane_f64(double v, int src) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), src);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), src);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int src) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), src);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), src);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // the fp32 neighbours of a finite fp32 value (one unit in the last place down / up)
@@ -150,154 +185,206 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
+__device__ __forceinline__ bool f16_finite(uint16_t h) { return (h & 0x7C00u) != 0x7C00u; }
+
 // exact code of value y (fp64) under (s16, z16), as the quantiser defines it: uniform
-// levels for lv == 0, else the nearest level of codebook word lv
+// levels for lv == 0, else the nearest level of codebook word lv; every code is 0 when the
+// scale is 0 or the scale or zero point overflowed fp16
 __device__ __forceinline__ uint32_t exact_code(double y, uint16_t s16, uint16_t z16, uint32_t lv) {
 #pragma clang fp contract(off)
   const double s = h2d(s16);
-  if (s == 0.0) return 0u;
+  if (s == 0.0 || !f16_finite(s16) || !f16_finite(z16)) return 0u;
   const double tq = (y - h2d(z16)) / s;
   if (lv != 0u) return static_cast<uint32_t>(codebook_code(tq, lv));
   const double t = rint(tq);
   return t < 0.0 ? 0u : (t > 3.0 ? 3u : static_cast<uint32_t>(t));
 }
 
-// Exact scale and zero point for the tokens of a tile listed in `todo` (bit n: token n of
-// the tile), whose x rows are in xs (bf16 [16][128]); where fp32 values cannot give a
-// token's codes, its exact codes go to fbw (2 bits per dim, 8 words per token). Per lane:
-// cand = candidate bits (mt, e) of this lane's token, delta its error bound, sz its packed
-// (s16, z16) so far. Returns the lane's (s16 | z16 << 16), with bit 32 set when its token's
-// codes are in fbw. Out of line: the path is rare, and its registers stay out of the kernel's
-// main loop.
-__device__ __attribute__((noinline)) uint64_t exact_tokens(const uint16_t* xs, const uint16_t* rt, uint32_t* fbw,
-                                                          uint64_t todo, uint32_t cand, double delta, uint32_t sz,
-                                                          double cr, uint32_t lv) {
+// distance from t to the nearest decision boundary of the code: the level midpoints of
+// codebook word lv, or 0.5, 1.5, 2.5 for the uniform levels
+template <typename T>
+__device__ __forceinline__ T boundary_gap(T t, uint32_t lv) {
+  if (lv != 0u) {
+    const T th0 = static_cast<T>(static_cast<int>((lv & 0xFFu) + ((lv >> 8) & 0xFFu))) * static_cast<T>(0.03125);
+    const T th1 = static_cast<T>(static_cast<int>(((lv >> 8) & 0xFFu) + ((lv >> 16) & 0xFFu))) * static_cast<T>(0.03125);
+    const T th2 = static_cast<T>(static_cast<int>(((lv >> 16) & 0xFFu) + (lv >> 24))) * static_cast<T>(0.03125);
+    return fmin(fmin(fabs(t - th0), fabs(t - th1)), fabs(t - th2));
+  }
+  const T b = fmin(fmax(floor(t) + static_cast<T>(0.5), static_cast<T>(0.5)), static_cast<T>(2.5));
+  return fabs(t - b);
+}
+
+// Byte offset of token n, dim j in a tile's code stage: K codes token-major, V dim-major.
+__device__ __forceinline__ int code_pos(bool is_v, int n, int j) { return is_v ? j * 16 + n : n * kHeadDim + j; }
+
+// Dim of candidate bit b (= 4 mt + e) of a lane in lane group G.
+__device__ __forceinline__ int dim_of(int b, int G) { return 16 * (b >> 2) + 4 * G + (b & 3); }
+
+// Extremes of the undecided tokens of an iteration's two tiles from their candidates:
+// bits 32 tt + 4 mt + e of cmax / cmin are this lane's candidates in tile tt (its token n,
+// its lane group's dims); xs2 holds the x rows of both tiles (tile tt, token n at row
+// 16 tt + n). Up to four candidates per pass, one per 16-lane group, fp64 sums
+// (group_dot). Returns, in every lane of a token, the max of the token's cmax values and the
+// min of its cmin values per tile. Out of line: its registers stay out of the kernel's main
+// loop.
+struct Extremes {
+  double emax[2], emin[2];
+};
+__device__ __attribute__((noinline)) Extremes candidate_extremes(const uint16_t* xs2, const uint16_t* rt,
+                                                                 uint64_t cmax, uint64_t cmin) {
   const int lane = threadIdx.x & 63;
-  const int n_ = lane & 15;
-  uint16_t s16 = static_cast<uint16_t>(sz & 0xFFFFu);
-  uint16_t z16 = static_cast<uint16_t>(sz >> 16);
-  bool fbk = false;
-  while (todo) {
-    const int nf = __builtin_ctzll(todo);  // wave-uniform token of the tile
-    todo &= todo - 1;
-    const uint16_t* xrow = xs + nf * kHeadDim;
-    const double fdl = __shfl(delta, nf, 64);
-    uint32_t cnf = n_ == nf ? cand : 0u;
-    // first fp64 sums of the candidates with an error bound of their own, four at a time;
-    // the compensated sums only when that interval still leaves the fp16 results open
-    const uint32_t cnf0 = cnf;
-    double emax = -INFINITY, emin = INFINITY;
-    uint64_t lanes = __ballot(cnf != 0u);
-    while (lanes) {
-      int js[4];
+  Extremes e = {{-INFINITY, -INFINITY}, {INFINITY, INFINITY}};
+  uint64_t cand = cmax | cmin;
+  uint64_t lanes = __ballot(cand != 0ull);
+  while (lanes) {
+    int js[4], rows[4], owner[4], kind[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        js[r] = -1;
-        if (lanes) {
-          const int ls = __builtin_ctzll(lanes);
-          const uint32_t cm = __builtin_amdgcn_readlane(cnf, ls);
-          const int b = __builtin_ctz(cm);
-          if (lane == ls) cnf &= cnf - 1u;
-          lanes = __ballot(cnf != 0u);
-          js[r] = 16 * (b >> 2) + 4 * (ls >> 4) + (b & 3);
-        }
-      }
-      const int g = lane >> 4;
-      const int jg = g == 0 ? js[0] : (g == 1 ? js[1] : (g == 2 ? js[2] : js[3]));
-      const double y = group_dot(xrow, rt + (jg < 0 ? 0 : jg) * kRTRow, lane & 15);
-      const uint64_t yu = static_cast<uint64_t>(__double_as_longlong(y));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (js[r] < 0) continue;
-        const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(yu)), 16 * r);
-        const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(yu >> 32)), 16 * r);
-        const double yr = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
-        emax = fmax(emax, yr);
-        emin = fmin(emin, yr);
-      }
-    }
-    uint16_t es16 = 0, ez16 = 0;
-    bool known = false;
-    if (cr > 0.0) {
-#pragma clang fp contract(off)
-      // sum |x_i R_ij| <= fdl 2^20 (fdl = 16 2^-24 times that bound), so the sums are within
-      // 11 2^-53 2^20 fdl < 2^-28 fdl; then room for rounding the chain in fp64, and the fp16
-      // decision on fp32 ends rounded outward
-      const double d64 = fdl * 0x1p-28 + 0x1p-50 * fmax(fabs(emax), fabs(emin)) + 0x1p-1000;
-      const double hA = cr * (emax - d64), hB = cr * (emax + d64);
-      const double lC = cr * (emin - d64), lD = cr * (emin + d64);
-      const double m = 0x1p-50 * (fabs(hB) + fabs(lC)) + 0x1p-1000;
-      const double sLo = (hA - lD) * (1.0 / 3.0) - m, sHi = (hB - lC) * (1.0 / 3.0) + m;
-      es16 = f32_to_f16_bits(f32_down(sLo));
-      ez16 = f32_to_f16_bits(f32_down(lC - m));
-      known = sLo >= 0.0 && es16 == f32_to_f16_bits(f32_up(sHi)) && ez16 == f32_to_f16_bits(f32_up(lD + m));
-    }
-    if (!known) {
-      cnf = cnf0;
-      emax = -INFINITY;
-      emin = INFINITY;
-      lanes = __ballot(cnf != 0u);
-      while (lanes) {
+    for (int r = 0; r < 4; ++r) {
+      owner[r] = -1;
+      js[r] = 0;
+      rows[r] = 0;
+      kind[r] = 0;
+      if (lanes) {
         const int ls = __builtin_ctzll(lanes);
-        const uint32_t cm = __builtin_amdgcn_readlane(cnf, ls);
-        const int b = __builtin_ctz(cm);
-        if (lane == ls) cnf &= cnf - 1u;
-        lanes = __ballot(cnf != 0u);
-        const int j = 16 * (b >> 2) + 4 * (ls >> 4) + (b & 3);
-        const double y = coop_dot(xrow, rt + j * kRTRow, lane);
-        emax = fmax(emax, y);
-        emin = fmin(emin, y);
+        const uint64_t cm = lane_u64(cand, ls);
+        const int b = __builtin_ctzll(cm);
+        const uint64_t xm = lane_u64(cmax, ls);
+        const uint64_t nm = lane_u64(cmin, ls);
+        kind[r] = static_cast<int>((xm >> b) & 1ull) | (static_cast<int>((nm >> b) & 1ull) << 1) | ((b >> 5) << 2);
+        if (lane == ls) cand &= cand - 1ull;
+        lanes = __ballot(cand != 0ull);
+        owner[r] = ls;
+        rows[r] = 16 * (b >> 5) + (ls & 15);
+        js[r] = dim_of(b & 31, ls >> 4);
       }
-      scale_zero(cr, emax, emin, es16, ez16);
     }
-    const double esv = h2d(es16);
-    const bool full = !(cr > 0.0) || (esv != 0.0 && !(fdl <= kCodeSlack * esv));
-    if (full) {
-      // every value of token nf exact: lane L takes dims L and L + 64
-      if (lane < 8) fbw[nf * 8 + lane] = 0u;
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      double ymx2 = -INFINITY, ymn2 = INFINITY;
-      double yv[2];
+    const int g = lane >> 4;
+    const int jg = g == 0 ? js[0] : (g == 1 ? js[1] : (g == 2 ? js[2] : js[3]));
+    const int rg = g == 0 ? rows[0] : (g == 1 ? rows[1] : (g == 2 ? rows[2] : rows[3]));
+    const double y = group_dot(xs2 + rg * kHeadDim, rt + jg * kRTRow, lane & 15);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = lane + 64 * h;
-        const uint16_t* rr = rt + j * kRTRow;
-        double s = 0.0, c = 0.0;
-        for (int i = 0; i < kHeadDim; i += 8) {
-          const uint4 xv = *reinterpret_cast<const uint4*>(xrow + i);
-          const uint4 rv = *reinterpret_cast<const uint4*>(rr + i);
-          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-          const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            demote::two_sum_add(s, c, bf16lo(xw[k]) * bf16lo(rw[k]));
-            demote::two_sum_add(s, c, bf16hi(xw[k]) * bf16hi(rw[k]));
-          }
+    for (int r = 0; r < 4; ++r) {
+      if (owner[r] < 0) continue;
+      const double yr = lane_f64(y, 16 * r);
+      if ((lane & 15) == (owner[r] & 15)) {
+        const int tt = kind[r] >> 2;
+        if (kind[r] & 1) {
+          if (tt) e.emax[1] = fmax(e.emax[1], yr);
+          else e.emax[0] = fmax(e.emax[0], yr);
         }
-        yv[h] = s + c;
-        ymx2 = fmax(ymx2, yv[h]);
-        ymn2 = fmin(ymn2, yv[h]);
+        if (kind[r] & 2) {
+          if (tt) e.emin[1] = fmin(e.emin[1], yr);
+          else e.emin[0] = fmin(e.emin[0], yr);
+        }
       }
-      ymx2 = wave_max(ymx2);
-      ymn2 = wave_min(ymn2);
-      scale_zero(cr, ymx2, ymn2, es16, ez16);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int j = lane + 64 * h;
-        const uint32_t q = exact_code(yv[h], es16, ez16, lv);
-        // fb word (token nf, mt = j / 16) holds dim 16 mt + 4 g + e at bits 8 g + 2 e
-        const int r = j & 15;
-        atomicOr(&fbw[nf * 8 + (j >> 4)], q << (8 * (r >> 2) + 2 * (r & 3)));
-      }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    }
-    if (n_ == nf) {
-      s16 = es16;
-      z16 = ez16;
-      fbk = full;
     }
   }
-  return static_cast<uint64_t>(s16) | (static_cast<uint64_t>(z16) << 16) | (static_cast<uint64_t>(fbk) << 32);
+  return e;
+}
+
+// Codes of the flagged values of a tile (flags: this lane's bits (mt, e)), decided from
+// fp64 sums on an interval, and from compensated sums where that interval holds the
+// boundary; written into the tile's code stage. sz: this lane's packed (s16, z16); dl: its
+// token's error bound.
+__device__ __attribute__((noinline)) void fix_codes(const uint16_t* xs, const uint16_t* rt, unsigned char* cs,
+                                                    uint32_t flags, uint32_t sz, float dl, bool is_v, uint32_t lv) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  uint64_t lanes = __ballot(flags != 0u);
+  while (lanes) {
+    int js[4], ns[4], owner[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      owner[r] = -1;
+      js[r] = 0;
+      ns[r] = 0;
+      if (lanes) {
+        const int ls = __builtin_ctzll(lanes);
+        const uint32_t fm = __builtin_amdgcn_readlane(flags, ls);
+        const int b = __builtin_ctz(fm);
+        if (lane == ls) flags &= flags - 1u;
+        lanes = __ballot(flags != 0u);
+        owner[r] = ls;
+        ns[r] = ls & 15;
+        js[r] = dim_of(b, ls >> 4);
+      }
+    }
+    const int g = lane >> 4;
+    const int jg = g == 0 ? js[0] : (g == 1 ? js[1] : (g == 2 ? js[2] : js[3]));
+    const int ng = g == 0 ? ns[0] : (g == 1 ? ns[1] : (g == 2 ? ns[2] : ns[3]));
+    const double y = group_dot(xs + ng * kHeadDim, rt + jg * kRTRow, lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (owner[r] < 0) continue;
+      // wave-uniform from here: the value, its token's scale, zero point and bound
+      const double yr = lane_f64(y, 16 * r);
+      const uint32_t szr = __builtin_amdgcn_readlane(sz, owner[r]);
+      const float dlr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dl), owner[r]));
+      const uint16_t s16 = static_cast<uint16_t>(szr & 0xFFFFu);
+      const uint16_t z16 = static_cast<uint16_t>(szr >> 16);
+      const double s = h2d(s16);
+      const double t = (yr - h2d(z16)) / s;
+      // the fp64 sum is within 11 2^-53 sum|p| < 2^-31 dl of the exact value; two more
+      // roundings for t
+      const double bnd = static_cast<double>(dlr) * 0x1p-31 / s + 0x1p-50 * (fabs(t) + 1.0);
+      uint32_t q;
+      if (boundary_gap(t, lv) > bnd) {
+        // the exact t lies on the same side of every boundary as this one
+        if (lv == 0u) {
+          const double r = rint(t);
+          q = r < 0.0 ? 0u : (r > 3.0 ? 3u : static_cast<uint32_t>(r));
+        } else {
+          q = static_cast<uint32_t>(codebook_code(t, lv));
+        }
+      } else {
+        const double ye = coop_dot(xs + ns[r] * kHeadDim, rt + js[r] * kRTRow, lane);
+        q = exact_code(ye, s16, z16, lv);
+      }
+      if (lane == 0) cs[code_pos(is_v, ns[r], js[r])] = static_cast<unsigned char>(q);
+    }
+  }
+}
+
+// Every value of the tile's token nf summed with compensation (lane L: dims L and L + 64);
+// its extremes give the scale and zero point and each value its code, written into the
+// code stage. Returns the packed (s16, z16) (wave-uniform).
+__device__ __attribute__((noinline)) uint32_t full_token(const uint16_t* xs, const uint16_t* rt, unsigned char* cs,
+                                                         int nf, double cr, bool is_v, uint32_t lv) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const uint16_t* xrow = xs + nf * kHeadDim;
+  double yv[2];
+  double ymx = -INFINITY, ymn = INFINITY;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    const uint16_t* rr = rt + j * kRTRow;
+    double s = 0.0, c = 0.0;
+    for (int i = 0; i < kHeadDim; i += 8) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xrow + i);
+      const uint4 rv = *reinterpret_cast<const uint4*>(rr + i);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        demote::two_sum_add(s, c, bf16lo(xw[k]) * bf16lo(rw[k]));
+        demote::two_sum_add(s, c, bf16hi(xw[k]) * bf16hi(rw[k]));
+      }
+    }
+    yv[h] = s + c;
+    ymx = fmax(ymx, yv[h]);
+    ymn = fmin(ymn, yv[h]);
+  }
+  ymx = wave_max(ymx);
+  ymn = wave_min(ymn);
+  uint16_t s16, z16;
+  scale_zero(cr, ymx, ymn, s16, z16);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane + 64 * h;
+    cs[code_pos(is_v, nf, j)] = static_cast<unsigned char>(exact_code(yv[h], s16, z16, lv));
+  }
+  return static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
 }
 
 // CB: the Lloyd-Max codebook variant (codebook words [n_kv][K, V])
@@ -319,6 +406,28 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
   const uint16_t* rot = (is_v ? rot_v : rot_k) + static_cast<size_t>(head) * kHeadDim * kHeadDim;
   const double cr = static_cast<double>(is_v ? clip_v[head] : clip_k[head]);
   const uint32_t lv = CB ? codebook[2 * head + is_v] : 0u;  // codebook word (0: uniform levels)
+  const size_t head_stride = static_cast<size_t>(n_kv) * kHeadDim;  // elements between tokens
+  const int meta_off = is_v ? kVMeta : kKMeta;
+
+  // x fragments (B operand) of one iteration: lane (G, n) holds token tb + 16 tt + n,
+  // elements 32 ks + 8 G .. + 7 (tokens past the end read the last row; nothing of theirs is
+  // stored), with the tokens' destination page and slot
+  uint4 bx[2][4];
+  int pg[2], sl[2];
+  auto load_iter = [&](int it) {
+    const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * 32;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = min(tb + 16 * tt + n_, n - 1);
+      const uint16_t* xr = src + static_cast<size_t>(t) * head_stride + static_cast<size_t>(head) * kHeadDim;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bx[tt][ks] = *reinterpret_cast<const uint4*>(xr + 32 * ks + 8 * G);
+      pg[tt] = dst_page[t];
+      sl[tt] = dst_slot[t];
+    }
+  };
+  const int tb0 = blockIdx.x * kRowsPerBlock + wave * 32;
+  if (tb0 < n) load_iter(0);  // in flight while R^T is staged
 
   // R^T into LDS: thread (i, half) copies row i, columns 64 half .. + 63
   {
@@ -354,189 +463,301 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
       }
     }
     a = wave_max(a);
-    if (lane == 0) sm.fb[wave][0][0] = __float_as_uint(a);
+    if (lane == 0) sm.colmax2[wave] = a;
   }
   __syncthreads();
-  const float colmax2 = fmaxf(__uint_as_float(sm.fb[0][0][0]), __uint_as_float(sm.fb[1][0][0]));
-  __syncthreads();  // fb is reused below
+  // the fp32 sums of 128 exact squares: within 2^-16 relative, covered by the factor below
+  const float colmax2 = fmaxf(sm.colmax2[0], sm.colmax2[1]);
 
-  uint16_t* xs = reinterpret_cast<uint16_t*>(sm.stage[wave]);        // x rows of a tile [16][128]
-  unsigned char* cs = reinterpret_cast<unsigned char*>(sm.stage[wave]);  // codes of a tile
-  uint32_t* fbw = &sm.fb[wave][0][0];
-  const size_t head_stride = static_cast<size_t>(n_kv) * kHeadDim;  // elements between tokens
-  const int meta_off = is_v ? kVMeta : kKMeta;
+  unsigned char* cs = sm.cs[wave];
 
   for (int it = 0; it < kIters; ++it) {
     const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * 32;  // first token of the iteration
     if (tb >= n) break;  // wave-uniform
-    // x fragments (B operand): lane (G, n) holds token tb + 16 tt + n, elements 32 ks + 8 G .. + 7
-    // (tokens past the end read the last row; nothing of theirs is stored)
-    uint4 bx[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t = min(tb + 16 * tt + n_, n - 1);
-      const uint16_t* xr = src + static_cast<size_t>(t) * head_stride + static_cast<size_t>(head) * kHeadDim;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bx[tt][ks] = *reinterpret_cast<const uint4*>(xr + 32 * ks + 8 * G);
-    }
-    // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n
+    if (it > 0) load_iter(it);  // (iteration 0's rows were requested before R^T was staged)
+    // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n; four chunks from zero,
+    // joined in a fixed order with rounding to nearest
     f32x4 acc[8][2];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      acc[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 ch[4][2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 a = *reinterpret_cast<const uint4*>(sm.rt + (16 * mt + n_) * kRTRow + 32 * ks + 8 * G);
         const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[0][ks]), acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[1][ks]), acc[mt][1], 0, 0, 0);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        ch[ks][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[0][ks]), z, 0, 0, 0);
+        ch[ks][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[1][ks]), z, 0, 0, 0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma clang fp contract(off)
+        acc[mt][tt] = ((ch[0][tt] + ch[1][tt]) + ch[2][tt]) + ch[3][tt];
       }
     }
-
+    // this iteration's rows into LDS (for the exact paths) and their squared norms
+    float nxs[2];
+    int cpg[2], csl[2];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int t0 = tb + 16 * tt;  // first token of the tile
-      if (t0 >= n) break;           // wave-uniform
-      const int tok = t0 + n_;
-      const bool valid = tok < n;
-      const int page = dst_page[valid ? tok : t0];
-      const int slot = dst_slot[valid ? tok : t0];
-
-      // per-token extremes and |x|^2 (lane-local, then over the 4 lane groups)
-      float mx = -INFINITY, mn = INFINITY, nx = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mx = fmaxf(mx, acc[mt][tt][e]);
-          mn = fminf(mn, acc[mt][tt][e]);
-        }
+      float nx = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        *reinterpret_cast<uint4*>(sm.xs[wave][tt] + n_ * kHeadDim + 32 * ks + 8 * G) = bx[tt][ks];
         const uint32_t w4[4] = {bx[tt][ks].x, bx[tt][ks].y, bx[tt][ks].z, bx[tt][ks].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           nx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[k]), __builtin_bit_cast(bf16x2, w4[k]), nx,
                                                false);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mn = fminf(mn, __shfl_xor(mn, 16, 64));
-      mn = fminf(mn, __shfl_xor(mn, 32, 64));
-      nx += __shfl_xor(nx, 16, 64);
-      nx += __shfl_xor(nx, 32, 64);
-      // error bound of every fp32 value of this token (the norms carry their own fp32
-      // rounding, covered by the last factor)
-      const float dl = static_cast<float>(kAccUlps * 0x1p-24) * sqrtf(nx * colmax2) * (1.f + 0x1p-10f);
+      nxs[tt] = nx;
+      cpg[tt] = pg[tt];
+      csl[tt] = sl[tt];
+    }
 
-      // scale and zero point from the interval of the extremes. The exact extremes lie in
-      // [mx - dl, mx + dl] and [mn - dl, mn + dl]; the chain below evaluates the quantiser's
-      // steps on those ends in fp32 and widens the results by more than every rounding of
-      // either evaluation (fp32 here, fp64 in the quantiser), so they bound the true scale
-      // and zero point. Rounding to fp16 is monotone: equal ends mean a determined value.
-      uint16_t s16 = 0, z16 = 0;
-      bool exact = true;
-      {
+
+    // ---- both tiles at once: extremes, norms, error bounds and the fp32 interval test of
+    // the scale and zero point
+    float mx[2], mn[2], dl[2];
+    bool valid[2], known[2], full[2];
+    uint16_t s16[2], z16[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      valid[tt] = tb + 16 * tt + n_ < n;
+      float a = -INFINITY, b = INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a = fmaxf(a, acc[mt][tt][e]);
+          b = fminf(b, acc[mt][tt][e]);
+        }
+      mx[tt] = a;
+      mn[tt] = b;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      mx[tt] = fmaxf(mx[tt], __shfl_xor(mx[tt], 16, 64));
+      mn[tt] = fminf(mn[tt], __shfl_xor(mn[tt], 16, 64));
+      nxs[tt] += __shfl_xor(nxs[tt], 16, 64);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      mx[tt] = fmaxf(mx[tt], __shfl_xor(mx[tt], 32, 64));
+      mn[tt] = fminf(mn[tt], __shfl_xor(mn[tt], 32, 64));
+      nxs[tt] += __shfl_xor(nxs[tt], 32, 64);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma clang fp contract(off)
-        const float c32 = static_cast<float>(cr);
-        if (cr > 0.0 && dl < INFINITY && mx != -INFINITY) {
-          const float hA = c32 * (mx - dl), hB = c32 * (mx + dl);
-          const float lC = c32 * (mn - dl), lD = c32 * (mn + dl);
-          const float ms = 0x1p-21f * (fabsf(hB) + fabsf(lC)) + 0x1p-140f;
-          const float mz = 0x1p-21f * fabsf(lC) + 0x1p-140f;
-          const float sLo = (hA - lD) * (1.f / 3.f) - ms, sHi = (hB - lC) * (1.f / 3.f) + ms;
-          s16 = f32_to_f16_bits(sLo);
-          z16 = f32_to_f16_bits(lC - mz);
-          exact = sLo >= 0.f && s16 == f32_to_f16_bits(sHi) && z16 == f32_to_f16_bits(lD + mz);
-          const float sv = f16_to_f32(s16);
-          if (exact && sv != 0.f) exact = dl <= static_cast<float>(kCodeSlack) * sv;
-        } else {
-          exact = false;
-        }
-        if (!valid) exact = true;  // nothing to do for tokens past the end
+      // the bound of every fp32 value of this token
+      dl[tt] = kGamma * (sqrtf(nxs[tt] * colmax2) * (1.f + 0x1p-10f) + 0x1p-60f) + 0x1p-116f;
+      // The exact extremes lie in [mx - dl, mx + dl] and [mn - dl, mn + dl]; the chain below
+      // evaluates the quantiser's steps on those ends in fp32 and widens the results by more
+      // than every rounding of either evaluation (fp32 here, fp64 in the quantiser), so they
+      // bound the true scale and zero point. Rounding to fp16 is monotone: equal ends mean a
+      // determined value.
+      const float d = dl[tt];
+      const float c32 = static_cast<float>(cr);
+      s16[tt] = z16[tt] = 0;
+      known[tt] = false;
+      full[tt] = false;
+      if (cr > 0.0 && d < INFINITY && mx[tt] != -INFINITY) {
+        const float hA = c32 * (mx[tt] - d), hB = c32 * (mx[tt] + d);
+        const float lC = c32 * (mn[tt] - d), lD = c32 * (mn[tt] + d);
+        const float ms = 0x1p-21f * (fabsf(hB) + fabsf(lC)) + 0x1p-140f;
+        const float mz = 0x1p-21f * fabsf(lC) + 0x1p-140f;
+        const float sLo = (hA - lD) * (1.f / 3.f) - ms, sHi = (hB - lC) * (1.f / 3.f) + ms;
+        s16[tt] = f32_to_f16_bits(sLo);
+        z16[tt] = f32_to_f16_bits(lC - mz);
+        known[tt] = sLo >= 0.f && s16[tt] == f32_to_f16_bits(sHi) && z16[tt] == f32_to_f16_bits(lD + mz);
+      } else {
+        full[tt] = true;  // a clip ratio of 0 or less, or a non-finite row: every value exact
       }
-      const double delta = dl;
-
-      // tokens whose interval test failed: exact candidates, then the exact chain; tokens
-      // whose codes cannot come from fp32 values: all 128 values exact
-      bool fbk = false;  // this lane's token takes its codes from fb
-      uint64_t todo = __ballot(!exact && G == 0);
-      if (todo) {
-        // candidate dims of this lane's token: fp32 values within 3 delta of an fp32 extreme
-        // (fp32 rounding of the thresholds is below delta / 16, so this holds every value
-        // within 2 delta exactly), one bit per (mt, e)
-        uint32_t cand = 0u;
-        if (!exact) {
-          const float thi = mx - 3.f * dl;
-          const float tlo = mn + 3.f * dl;
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (acc[mt][tt][e] >= thi || acc[mt][tt][e] <= tlo) cand |= 1u << (4 * mt + e);
-        }
-        // the tile's x rows into LDS (bf16 [16][128])
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<uint4*>(xs + n_ * kHeadDim + 32 * ks + 8 * G) = bx[tt][ks];
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const uint64_t r = exact_tokens(xs, sm.rt, fbw, todo, cand, delta,
-                                        static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16), cr, lv);
-        s16 = static_cast<uint16_t>(r & 0xFFFFu);
-        z16 = static_cast<uint16_t>((r >> 16) & 0xFFFFu);
-        fbk = (r >> 32) & 1u;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (!valid[tt]) {  // nothing to do for tokens past the end
+        known[tt] = true;
+        full[tt] = false;
       }
+    }
 
-      // codes of this lane's 32 values into the stage (the x rows are no longer needed)
-      const float sf = f16_to_f32(s16);
-      const float zf = f16_to_f32(z16);
-      const float inv_s = sf != 0.f ? 1.f / sf : 0.f;
-      uint32_t cw[8];  // dims 16 mt + 4 G + e at byte e
+    // ---- the undecided tokens of both tiles: their candidates' fp64 sums, then the same
+    // test in fp64; compensated sums when even that leaves the fp16 values open
+    const bool und0 = !known[0] && !full[0];
+    const bool und1 = !known[1] && !full[1];
+    if (__any(und0 || und1)) {
+      uint64_t cmax = 0ull, cmin = 0ull;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const bool und = tt ? und1 : und0;
+        // candidates: values within 3 dl of an fp32 extreme (the thresholds' own rounding is
+        // below dl / 256, so this holds every value within 2 dl of the exact extreme)
+        const float thi = und ? mx[tt] - 3.f * dl[tt] : INFINITY;
+        const float tlo = und ? mn[tt] + 3.f * dl[tt] : -INFINITY;
+        uint32_t a = 0u, b = 0u;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a |= acc[mt][tt][e] >= thi ? (1u << (4 * mt + e)) : 0u;
+            b |= acc[mt][tt][e] <= tlo ? (1u << (4 * mt + e)) : 0u;
+          }
+        // a token with more than two candidates on one side in one lane (a range comparable
+        // to its bound) takes the full path instead
+        const uint64_t many = __ballot(und && (__builtin_popcount(a) > 2 || __builtin_popcount(b) > 2));
+        const uint32_t toks = static_cast<uint32_t>((many | (many >> 16) | (many >> 32) | (many >> 48)) & 0xFFFFull);
+        if ((toks >> n_) & 1u) {
+          full[tt] = true;
+          a = b = 0u;
+        }
+        cmax |= static_cast<uint64_t>(a) << (32 * tt);
+        cmin |= static_cast<uint64_t>(b) << (32 * tt);
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      const Extremes ce = candidate_extremes(sm.xs[wave][0], sm.rt, cmax, cmin);
+      bool settled[2] = {true, true};
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+#pragma clang fp contract(off)
+        if (!known[tt] && !full[tt]) {
+          // the sums are within 11 2^-53 sum|p| < 2^-31 dl of the exact extremes; then room
+          // for rounding the chain in fp64, and the fp16 decision on fp32 ends rounded outward
+          const double emax = ce.emax[tt], emin = ce.emin[tt];
+          const double d64 =
+              static_cast<double>(dl[tt]) * 0x1p-31 + 0x1p-50 * fmax(fabs(emax), fabs(emin)) + 0x1p-1000;
+          const double hA = cr * (emax - d64), hB = cr * (emax + d64);
+          const double lC = cr * (emin - d64), lD = cr * (emin + d64);
+          const double m = 0x1p-50 * (fabs(hB) + fabs(lC)) + 0x1p-1000;
+          const double sLo = (hA - lD) * (1.0 / 3.0) - m, sHi = (hB - lC) * (1.0 / 3.0) + m;
+          s16[tt] = f32_to_f16_bits(f32_down(sLo));
+          z16[tt] = f32_to_f16_bits(f32_down(lC - m));
+          settled[tt] = sLo >= 0.0 && s16[tt] == f32_to_f16_bits(f32_up(sHi)) &&
+                        z16[tt] == f32_to_f16_bits(f32_up(lD + m));
+        }
+      }
+      // the vanishing remainder: compensated sums of the candidates, token by token
+      uint64_t rest = __ballot(!settled[0] && G == 0) | (__ballot(!settled[1] && G == 0) << 16);
+      while (rest) {
+        const int m = __builtin_ctzll(rest);  // token 16 tt + n of the iteration
+        rest &= rest - 1;
+        const int tt = m >> 4;
+        const int nf = m & 15;
+        double ex = -INFINITY, en = INFINITY;
+        for (int g = 0; g < 4; ++g) {
+          const int ls = 16 * g + nf;
+          const uint32_t cxm = static_cast<uint32_t>(lane_u64(cmax, ls) >> (32 * tt));
+          const uint32_t cnm = static_cast<uint32_t>(lane_u64(cmin, ls) >> (32 * tt));
+          uint32_t cm = cxm | cnm;
+          while (cm) {
+            const int b = __builtin_ctz(cm);
+            cm &= cm - 1u;
+            const double y = coop_dot(sm.xs[wave][tt] + nf * kHeadDim, sm.rt + dim_of(b, g) * kRTRow, lane);
+            if ((cxm >> b) & 1u) ex = fmax(ex, y);
+            if ((cnm >> b) & 1u) en = fmin(en, y);
+          }
+        }
+        uint16_t a16, b16;
+        scale_zero(cr, ex, en, a16, b16);
+        if (n_ == nf) {
+          if (tt) {
+            s16[1] = a16;
+            z16[1] = b16;
+          } else {
+            s16[0] = a16;
+            z16[0] = b16;
+          }
+        }
+      }
+    }
+
+    // ---- per tile: codes, the exact decisions near boundaries, packing and stores
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t0 = tb + 16 * tt;  // first token of the tile
+      if (t0 >= n) break;           // wave-uniform
+      const uint16_t* xs = sm.xs[wave][tt];
+      const int page = cpg[tt];
+      const int slot = csl[tt];
+
+      // codes of this lane's 32 values: v = (y - z16) / s16 + 1/2 as one fused step
+      // (|v - (t + 1/2)| <= dt + (8 + 4.1 |z16 / s16|) 2^-24 near a boundary), the code
+      // floor(v) on [0, 3.5]; values with v within bt of an integer may lie on the other
+      // side of it than the exact value and take the exact path (the integers 0 and 4 are no
+      // boundaries: flagging them only costs an exact sum)
+      const float sf = f16_to_f32(s16[tt]);
+      const float zf = f16_to_f32(z16[tt]);
+      const bool usable = sf != 0.f && f16_finite(s16[tt]) && f16_finite(z16[tt]);
+      const float inv_s = usable ? 1.f / sf : 0.f;
+      const float zs = zf * inv_s;
+      const float cb = CB ? -zs : 0.5f - zs;
+      const float dt = dl[tt] * inv_s * (1.f + 0x1p-20f);
+      bool fullt = full[tt] || (valid[tt] && usable && dt > kFullT);
+      const float bt = (valid[tt] && usable && !fullt) ? dt + (1.f + 0.6f * fabsf(zs)) * 0x1p-21f : -1.f;
+      float gmax = 0.f;  // largest closeness to a boundary of this lane's values
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         uint32_t w = 0u;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          const float v = fmaf(acc[mt][tt][e], inv_s, cb);
+          uint32_t q;
           if constexpr (CB) {
-            // the nearest codebook level (a tie of the fp32 value lies inside the tolerated
-            // band around the midpoint)
-            w |= static_cast<uint32_t>(codebook_code((acc[mt][tt][e] - zf) * inv_s, lv)) << (8 * e);
+            q = static_cast<uint32_t>(codebook_code(v, lv));
+            gmax = fmaxf(gmax, 1.f - boundary_gap(v, lv));
           } else {
-            // t + 1/2 clamped to [0, 3.5], truncated: the nearest level (a tie rounds up, and
-            // a tie of the fp32 value lies inside the tolerated band around the boundary)
-            const float t = __builtin_amdgcn_fmed3f(fmaf(acc[mt][tt][e] - zf, inv_s, 0.5f), 0.f, 3.5f);
-            w |= static_cast<uint32_t>(t) << (8 * e);
+            q = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(v, 0.f, 3.5f));
+            gmax = fmaxf(gmax, fabsf(__builtin_amdgcn_fractf(v) - 0.5f));
           }
+          w |= q << (8 * e);
         }
-        if (sf == 0.f) w = 0u;
-        cw[mt] = w;
-      }
-      if (fbk) {
+        if (!usable) w = 0u;
+        if (!is_v) {
+          *reinterpret_cast<uint32_t*>(cs + n_ * kHeadDim + 16 * mt + 4 * G) = w;
+        } else {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const uint32_t f = (fbw[n_ * 8 + mt] >> (8 * G)) & 0xFFu;
-          cw[mt] = (f & 3u) | (((f >> 2) & 3u) << 8) | (((f >> 4) & 3u) << 16) | ((f >> 6) << 24);
+          for (int e = 0; e < 4; ++e) cs[(16 * mt + 4 * G + e) * 16 + n_] = static_cast<unsigned char>(w >> (8 * e));
         }
       }
+      // uniform levels: |fract(v) - 1/2| >= 1/2 - bt means v within bt of an integer; the
+      // codebook's 1 - gap >= 1 - bt means t within bt of a level midpoint
+      const bool flagged = CB ? (gmax >= 1.f - bt) : (gmax >= 0.5f - bt);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (!is_v) {
-        // K: bytes [token][dim]
+      uint32_t sz = static_cast<uint32_t>(s16[tt]) | (static_cast<uint32_t>(z16[tt]) << 16);
+      if (__any(flagged && bt >= 0.f)) {
+        // which of this lane's values: the same v again
+        uint32_t flags = 0u;
+        if (flagged && bt >= 0.f) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<uint32_t*>(cs + n_ * kHeadDim + 16 * mt + 4 * G) = cw[mt];
-      } else {
-        // V: bytes [dim][token]
+          for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) cs[(16 * mt + 4 * G + e) * 16 + n_] = static_cast<unsigned char>(cw[mt] >> (8 * e));
+            for (int e = 0; e < 4; ++e) {
+              const float v = fmaf(acc[mt][tt][e], inv_s, cb);
+              bool near;
+              if constexpr (CB) {
+                near = boundary_gap(v, lv) <= bt;
+              } else {
+                const float f = __builtin_amdgcn_fractf(v);
+                near = fminf(f, 1.f - f) <= bt;
+              }
+              if (near) flags |= 1u << (4 * mt + e);
+            }
+        }
+        fix_codes(xs, sm.rt, cs, flags, sz, dl[tt], is_v, lv);
+      }
+      uint64_t fulls = __ballot(fullt && G == 0);
+      while (fulls) {
+        const int nf = __builtin_ctzll(fulls);
+        fulls &= fulls - 1;
+        const uint32_t r = full_token(xs, sm.rt, cs, nf, cr, is_v, lv);
+        if (n_ == nf) sz = r;
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
       // scale and zero point of the token
-      if (valid && G == 0) {
+      if (valid[tt] && G == 0) {
         uint8_t* blk = pool + (static_cast<size_t>(page) * n_kv + head) * kHeadBlock;
-        *reinterpret_cast<uint32_t*>(blk + meta_off + 4 * slot) = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
+        *reinterpret_cast<uint32_t*>(blk + meta_off + 4 * slot) = sz;
       }
       if (!is_v) {
         // K words: word q = lane + 64 r is (token q / 8 of the tile, dims 16 (q % 8) ..)
@@ -547,20 +768,20 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
           const int w = q & 7;
           // page and slot of the word's token from lane tk, which loaded them (every lane
           // of the wave takes part in the shuffles)
-          const int pg = __shfl(page, tk, 64);
-          const int sl = __shfl(slot, tk, 64);
+          const int pgw = __shfl(page, tk, 64);
+          const int slw = __shfl(slot, tk, 64);
           if (t0 + tk < n) {
             const uint4 b = *reinterpret_cast<const uint4*>(cs + tk * kHeadDim + 16 * w);
             const uint32_t word = b.x | (b.y << 2) | (b.z << 4) | (b.w << 6);
-            uint8_t* blk = pool + (static_cast<size_t>(pg) * n_kv + head) * kHeadBlock;
-            *reinterpret_cast<uint32_t*>(blk + k_word_offset(sl, w)) = word;
+            uint8_t* blk = pool + (static_cast<size_t>(pgw) * n_kv + head) * kHeadBlock;
+            *reinterpret_cast<uint32_t*>(blk + k_word_offset(slw, w)) = word;
           }
         }
       } else {
         // V: whole words when the tile fills slots 16u..16u+15 of one page in order
         const int page0 = __shfl(page, 0, 64);
         const int slot0 = __shfl(slot, 0, 64);
-        const bool mine_ok = valid && page == page0 && slot == (slot0 & ~15) + n_;
+        const bool mine_ok = valid[tt] && page == page0 && slot == (slot0 & ~15) + n_;
         const bool aligned = (slot0 & 15) == 0 && __ballot(G == 0 && mine_ok) == 0xFFFFull;
         if (aligned) {
           uint8_t* blk = pool + (static_cast<size_t>(page0) * n_kv + head) * kHeadBlock;
@@ -571,7 +792,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
             const uint32_t word = b.x | (b.y << 2) | (b.z << 4) | (b.w << 6);
             *reinterpret_cast<uint32_t*>(blk + v_word_offset(d, slot0 >> 4)) = word;
           }
-        } else if (valid) {
+        } else if (valid[tt]) {
           // this lane's 32 codes into their shared words, two bits each
           uint8_t* blk = pool + (static_cast<size_t>(page) * n_kv + head) * kHeadBlock;
           const int rs = slot & 15;
@@ -583,7 +804,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
               const int d = 16 * mt + 4 * G + e;
               uint32_t* w = reinterpret_cast<uint32_t*>(blk + v_word_offset(d, slot >> 4));
               atomicAnd(w, ~(3u << sh));
-              atomicOr(w, ((cw[mt] >> (8 * e)) & 3u) << sh);
+              atomicOr(w, static_cast<uint32_t>(cs[d * 16 + n_] & 3u) << sh);
             }
         }
       }

@@ -56,10 +56,13 @@ __device__ __forceinline__ ScaleZero scale_zero(double cr, double ymax, double y
 }
 
 // 2-bit code of rotated value y from t = (y - z) / s: round half to even, clamped to
-// [0, 3], for the uniform levels (lv == 0); the nearest level of codebook word lv otherwise
+// [0, 3], for the uniform levels (lv == 0); the nearest level of codebook word lv otherwise;
+// 0 when the scale is 0 or the scale or zero point is infinite
 __device__ __forceinline__ int code_of(double y, double z16d, double s16d, uint32_t lv) {
 #pragma clang fp contract(off)
-  if (s16d == 0.0) return 0;
+  // a scale of 0, or a scale or zero point that overflowed fp16: every code is 0 (no NaN is
+  // ever formed)
+  if (s16d == 0.0 || !(fabs(s16d) < INFINITY) || !(fabs(z16d) < INFINITY)) return 0;
   const double t = (y - z16d) / s16d;
   if (lv != 0u) return codebook_code(t, lv);
   const double r = rint(t);

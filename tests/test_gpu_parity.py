@@ -609,7 +609,7 @@ def plain_rotations(kind, n_kv):
 
 
 @pytest.mark.parametrize("case", ["c2-4k", "c5-gq8", "c4-shared-ragged"])
-@pytest.mark.parametrize("kind", ["hadamard"])
+@pytest.mark.parametrize("kind", ["hadamard", "identity"])
 def test_plain_rotations_demote_and_decode(kind, case):
     """R = H P (Hadamard and bit reversal without the eigenbasis, the QuaRot-style baseline
     the pages compare with) and R = I (naive INT2): the whole history demoted on the GPU (the
@@ -666,3 +666,90 @@ def test_plain_rotations_demote_and_decode(kind, case):
         ref = oracle_decode(w, b, rk, rk, hists[b])
         for name, got in outs.items():
             assert_close(got[b], ref, f"{case} {kind} {name} b{b}")
+
+
+def _adversarial_rows(rk, g, n_each):
+    """bf16 rows [4 n_each, 128] for one KV head's rotation rk (fp64 bf16 values):
+    cancellation (x = y_t R^T rounded to bf16, with y_t two entries of +-1000 and the rest
+    near 0.01, so most rotated values are sums of terms near 100 that cancel to a few units);
+    mixed magnitudes (entries of 3000 and 0.001 in random dims); single spikes (x = c R_:,j,
+    one large rotated value and the rest cancellation residue); and plain outlier rows."""
+    rows = []
+    for _ in range(n_each):
+        yt = g.standard_normal(128) * 0.01
+        yt[g.choice(128, 2, replace=False)] = g.choice([-1000.0, 1000.0], 2)
+        rows.append(yt @ rk.T)
+    for _ in range(n_each):
+        x = g.standard_normal(128) * 1e-3
+        big = g.choice(128, 64, replace=False)
+        x[big] = g.standard_normal(64) * 3000.0
+        rows.append(x)
+    for _ in range(n_each):
+        rows.append(g.uniform(5.0, 500.0) * g.choice([-1.0, 1.0]) * rk[:, g.integers(128)])
+    for _ in range(n_each):
+        x = g.standard_normal(128)
+        x[g.choice(128, 4, replace=False)] *= 20.0
+        rows.append(x)
+    return synth.to_bf16_values(np.array(rows, np.float32))
+
+
+def test_bulk_demotion_adversarial_rows_exact():
+    """The matrix-core demotion kernel on rows built to stress its error bound: large
+    cancellation (sum |x_i R_ij| hundreds of times |y_j|), mixed magnitudes (3000 next to
+    0.001) and single spikes, with plain outlier rows beside them; every scale, zero point
+    and code equal to the oracle's, with no code in the tolerated band allowed to differ."""
+    w = custom("adversarial", 4, 2, [64 * 8 + 320], cfg=2)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table = np.array([list(range(8))], np.int32)
+    c = make_cache(w, rk_bits, rv_bits, table, 8, with_windows=False)
+    g = np.random.default_rng(31)
+    n = 4 * 128
+    rows_k = np.stack([_adversarial_rows(rk[kv], g, 128) for kv in range(2)], 1)
+    rows_v = np.stack([_adversarial_rows(rv[kv], g, 128) for kv in range(2)], 1)
+    perm = g.permutation(n)  # mixed within tiles
+    rows_k, rows_v = rows_k[perm], rows_v[perm]
+    j = np.arange(n)
+    say("bulk demotion, adversarial rows", n)
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, rows_k, rows_v)
+    torch.cuda.synchronize()
+    pool = c.pool.cpu().numpy().reshape(8, 2, opages.HEAD_BLOCK)
+    from oracle import quant as oquant
+    for kv in range(2):
+        kc, ks, kz, km = oquant.quantize_rows(rows_k[:, kv].astype(np.float64), rk[kv], w.clip_ratio)
+        vc, vs, vz, vm = oquant.quantize_rows(rows_v[:, kv].astype(np.float64), rv[kv], w.clip_ratio)
+        got = opages.unpack_history(pool, table[0], kv, n)
+        assert compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"adversarial head {kv}") == 0
+
+
+@pytest.mark.parametrize("n", [40, 128])
+def test_demotion_fp16_overflow_contract(n):
+    """A row whose clipped range exceeds fp16 is outside the quantiser's domain (the oracle
+    rejects it); both demotion kernels (per row below 64 tokens, matrix cores from 64) store
+    the fp16 rounding of its scale and zero point (infinite) and codes 0, and leave the
+    other rows of the call exact."""
+    w = custom("overflow", 4, 2, [64 * 2 + 320], cfg=2)
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table = np.array([[0, 1]], np.int32)
+    c = make_cache(w, rk_bits, rv_bits, table, 2, with_windows=False)
+    g = np.random.default_rng(5)
+    rows = synth.to_bf16_values(g.standard_normal((n, 2, 128)).astype(np.float32))
+    rows[3] = synth.to_bf16_values(np.full((2, 128), 1.0e5, np.float32) * g.choice([-1.0, 1.0], (2, 128)))
+    j = np.arange(n)
+    say("demotion overflow contract", n)
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, rows, rows[::-1].copy())
+    torch.cuda.synchronize()
+    pool = c.pool.cpu().numpy().reshape(2, 2, opages.HEAD_BLOCK)
+    from oracle import quant as oquant
+    keep = np.arange(n) != 3
+    keep_v = np.arange(n) != n - 1 - 3
+    for kv in range(2):
+        got = opages.unpack_history(pool, table[0], kv, n)
+        kcg, ksg, kzg, vcg, vsg, vzg = got
+        with pytest.raises(ValueError):
+            oquant.quantize_rows(rows[3:4, kv].astype(np.float64), rk[kv], w.clip_ratio)
+        assert np.isinf(np.float64(ksg[3])) and np.isinf(np.float64(kzg[3])) and not np.any(kcg[3])
+        assert np.isinf(np.float64(vsg[n - 4])) and not np.any(vcg[n - 4])
+        kc, ks, kz, km = oquant.quantize_rows(rows[keep, kv].astype(np.float64), rk[kv], w.clip_ratio)
+        vc, vs, vz, vm = oquant.quantize_rows(rows[::-1][keep_v, kv].astype(np.float64), rv[kv], w.clip_ratio)
+        mine = (kcg[keep], ksg[keep], kzg[keep], vcg[keep_v], vsg[keep_v], vzg[keep_v])
+        assert compare_history(mine, (kc, ks, kz, vc, vs, vz), km, vm, f"overflow call head {kv}") == 0
