@@ -71,6 +71,16 @@ _SIGNATURES = {
                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                     c_void_p, c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
                                     c_void_p, c_void_p]),
+    "oscar_decode_step_append_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_decode_step_append_splits": (c_int32, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_decode_step_append": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
+                                           c_void_p, c_void_p]),
+    "oscar_decode_step_append_codebook": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                    c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                                    c_int32, c_void_p, c_size_t, c_void_p, c_void_p]),
     "oscar_decode_step_noalloc_max_bytes": (c_size_t, []),
     "oscar_decode_step_noalloc": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -504,6 +514,48 @@ def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k,
     else:
         _check_codebook(desc, codebook)
         _check(lib().oscar_decode_step_codebook(byref(desc), *head, _ptr(codebook), *rest))
+
+
+def oscar_decode_step_append_workspace_bytes(desc: LayerDesc, batch: int, n_splits: int) -> int:
+    return int(lib().oscar_decode_step_append_workspace_bytes(byref(desc), int(batch), int(n_splits)))
+
+
+def oscar_decode_step_append_splits(desc: LayerDesc, batch: int, max_hist_len: int) -> int:
+    return int(lib().oscar_decode_step_append_splits(byref(desc), int(batch), int(max_hist_len)))
+
+
+def oscar_decode_step_append(desc: LayerDesc, k_src, v_src, clip_k, clip_v, q, rot_k, rot_v, pool, block_table,
+                             hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace, out,
+                             stream=None, codebook=None):
+    """One decode step in one launch: token b of k_src/v_src [batch, n_kv_heads, 128] bf16
+    (None: nothing) becomes history token hist_len[b] - 1 of request b, then decode. The
+    workspace's arrival counters must be zero before the first call (zero-fill it once)."""
+    _need(desc.group_size == 128, "the one-launch step reads one-group pages")
+    batch = int(q.shape[0])
+    _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len, n_splits,
+                       workspace, out)
+    need = oscar_decode_step_append_workspace_bytes(desc, batch, n_splits)
+    nbytes = workspace.numel() * workspace.element_size()
+    _need(nbytes >= need, f"workspace holds {nbytes} bytes, needs {need}")
+    app = k_src is not None
+    if app:
+        hkv = desc.n_kv_heads
+        _device16(k_src, "k_src")
+        _device16(v_src, "v_src")
+        _need(k_src.numel() == batch * hkv * HEAD_DIM and v_src.numel() == batch * hkv * HEAD_DIM,
+              "k_src/v_src must be [batch, n_kv_heads, 128]")
+        for t, name in ((clip_k, "clip_k"), (clip_v, "clip_v")):
+            _need(t.is_cuda and t.numel() == hkv and t.dtype.is_floating_point and t.element_size() == 4,
+                  f"{name} must be float32 [n_kv_heads] on the device")
+    head = (_ptr(k_src) if app else None, _ptr(v_src) if app else None, _ptr(clip_k) if app else None,
+            _ptr(clip_v) if app else None, _ptr(q), _ptr(rot_k), _ptr(rot_v))
+    rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win),
+            _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
+    if codebook is None:
+        _check(lib().oscar_decode_step_append(byref(desc), *head, *rest))
+    else:
+        _check_codebook(desc, codebook)
+        _check(lib().oscar_decode_step_append_codebook(byref(desc), *head, _ptr(codebook), *rest))
 
 
 def oscar_decode_step_noalloc_max_bytes() -> int:

@@ -287,6 +287,18 @@ __device__ __forceinline__ void store_partial(float* p, float v) {
     *p = v;
 }
 
+// Options of the one-launch decode step: the query is prepared inside the workgroup (from q
+// and R_K) instead of read from an earlier launch's workspace; the last `n_excl` history
+// tokens of each request are left out (the step's appended token, which its own workgroup
+// attends); partials are written with `pstride` split columns per head.
+struct InlineQuery {
+  const uint16_t* q = nullptr;      // bf16 [B][Hq][128]; null: query data from qlimb / qscal
+  const uint16_t* rot_k = nullptr;  // bf16 [Hkv][128][128]
+  double scale_log2 = 0.0;
+  int n_excl = 0;
+  int pstride = 0;                  // 0: n_splits
+};
+
 // One workgroup (NW waves) of the INT2 pass: history split `split` of request b for the
 // query heads gy*GQ .. gy*GQ+GQ-1 (KV head gy / n_groups). `smem` holds
 // int2_smem_bytes<GQ, NW>(). With CB, `codebook` holds the codebook words [n_kv][K, V].
@@ -295,7 +307,8 @@ __device__ __forceinline__ void int2_split(
     unsigned char* __restrict__ smem, int split, int gy, int b, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ hist_len, int n_q, int n_kv, int n_groups, int n_splits,
     const char* __restrict__ qlimb, const QueryScal* __restrict__ qscal, float* __restrict__ out_m,
-    float* __restrict__ out_l, float* __restrict__ out_acc, const uint32_t* __restrict__ codebook = nullptr) {
+    float* __restrict__ out_l, float* __restrict__ out_acc, const uint32_t* __restrict__ codebook = nullptr,
+    const InlineQuery& iq = InlineQuery()) {
   constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
   constexpr int kPBytes = NW * MT * 16 * kPRow;
   constexpr int kFBytes = NW * MT * kFlushed * 64 * 4;
@@ -331,7 +344,8 @@ __device__ __forceinline__ void int2_split(
   const int G = lane >> 4;  // lane group
   const int h0 = gy * GQ;  // first query head of this workgroup
 
-  const int nh = hist_len[b];
+  const int nh = max(0, hist_len[b] - iq.n_excl);
+  const int pstride = iq.pstride > 0 ? iq.pstride : n_splits;
   const int n_pages = (nh + kPageTokens - 1) / kPageTokens;
   const int pps = (n_pages + n_splits - 1) / n_splits;
   const int p_begin = split * pps;
@@ -351,8 +365,9 @@ __device__ __forceinline__ void int2_split(
   static_assert(kQChunks <= 64 * NW, "one query-limb chunk per thread");
   const int qrow = tid >> 3;
   const int qc = tid & 7;
+  const bool inline_q = iq.q != nullptr;  // uniform
   uint4 qv = {0u, 0u, 0u, 0u};
-  if (tid < kQChunks && (qrow >> 2) < GQ)
+  if (!inline_q && tid < kQChunks && (qrow >> 2) < GQ)
     qv = *reinterpret_cast<const uint4*>(qlimb + (head0 + (qrow >> 2)) * 512 + (qrow & 3) * kHeadDim + 16 * qc);
   float qsc[MT], sig[MT];
   int kcent[MT];
@@ -361,15 +376,33 @@ __device__ __forceinline__ void int2_split(
   for (int mt = 0; mt < MT; ++mt) {
     const int g = 4 * mt + G;
     head_ok[mt] = g < GQ;
-    if (head_ok[mt]) {
+    kcent[mt] = 0;
+    qsc[mt] = sig[mt] = 0.f;
+    if (head_ok[mt] && !inline_q) {
       const QueryScal s = qscal[head0 + g];
       kcent[mt] = s.kcent;
       qsc[mt] = s.qsc;
       sig[mt] = s.sig;
-    } else {
-      kcent[mt] = 0;
-      qsc[mt] = sig[mt] = 0.f;
     }
+  }
+  // inline query preparation: wave w holds rows RW w .. RW w + RW - 1 of R_K at this lane's
+  // columns 2 lane, 2 lane + 1 (requested here, with the block ids below)
+  constexpr int RW = kHeadDim / NW;
+  uint32_t rk[RW];
+  // the wave's query values (dims RW w .. + RW - 1 of each head), 16 bytes per lane for
+  // lanes < GQ RW / 8, bound for wave-private LDS: requested before the block ids and the
+  // pages, so that waiting for them never waits for a page
+  constexpr int kQLanes = GQ * RW / 8;
+  static_assert(kQLanes <= 64, "one 16-byte query chunk per lane");
+  uint4 qchunk = {0u, 0u, 0u, 0u};
+  if (inline_q) {
+    const uint32_t* rp = reinterpret_cast<const uint32_t*>(iq.rot_k + static_cast<size_t>(kv) * kHeadDim * kHeadDim +
+                                                           static_cast<size_t>(RW * wave) * kHeadDim) + lane;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) rk[r] = rp[r * (kHeadDim / 2)];
+    if (lane < kQLanes)
+      qchunk = *reinterpret_cast<const uint4*>(iq.q + (head0 + lane / (RW / 8)) * kHeadDim + RW * wave +
+                                               8 * (lane % (RW / 8)));
   }
 
   // block ids of this wave's pages p0, p0 + NW, ...: lane i of blk_lane holds the id of the
@@ -381,9 +414,10 @@ __device__ __forceinline__ void int2_split(
   // Everything requested so far has arrived here: none of it counts as outstanding in the
   // page loop, whose waits then let the next pages keep loading.
   asm volatile("" ::"v"(blk_lane), "v"(qv.x), "v"(qv.y), "v"(qv.z), "v"(qv.w));
+  asm volatile("" ::"v"(qchunk.x), "v"(qchunk.y), "v"(qchunk.z), "v"(qchunk.w));
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(kcent[mt]), "v"(qsc[mt]), "v"(sig[mt]));
-  if (tid < kQChunks) *reinterpret_cast<uint4*>(q_s + qrow * kQRow + 16 * qc) = qv;
+  if (!inline_q && tid < kQChunks) *reinterpret_cast<uint4*>(q_s + qrow * kQRow + 16 * qc) = qv;
   auto page_of = [&](int j) -> const uint8_t* {  // j wave-uniform, 0 <= j < n_mine
     if ((j >> 6) != chunk) {
       chunk = j >> 6;
@@ -402,6 +436,108 @@ __device__ __forceinline__ void int2_split(
   PageRegs buf[3];
   load_page(buf[0], page_of(0), lane32, meta16, rec);
   load_page(buf[1], page_of(n_mine > 1 ? 1 : 0), lane32, meta16, rec);
+  if (inline_q) {
+    // while the first pages load: q_rot = q R_K for the workgroup's heads in fp64 (bf16
+    // products are exact), each wave over its RW rows, joined through LDS; then per head
+    // (one wave each) the 22-bit fixed point, its limbs into the LDS rows of the page loop,
+    // and the head's scalars, as the separate query preparation computes them
+    // the join uses the page loop's LDS; the heads' scalars the epilogue's (wm_s, wl_s),
+    // which the page loop's set-up below does not touch
+    static_assert(NW * GQ * 64 * 16 <= kLoopBytes + kWaccBytes, "the query join fits the loop's LDS");
+    static_assert(GQ * static_cast<int>(sizeof(QueryScal)) <= 2 * NW * GQ * 4, "the heads' scalars fit");
+    static_assert(NW * GQ * 64 * 16 + NW * GQ * RW * 2 <= kLoopBytes + kWaccBytes, "the staged query fits too");
+    double(*qpart)[GQ][64][2] = reinterpret_cast<double(*)[GQ][64][2]>(scratch_s);
+    // wave-private staging of the wave's query values: [GQ][RW] bf16 (the wave's own LDS
+    // accesses run in order, so no barrier is needed before reading them back)
+    uint32_t* qst = reinterpret_cast<uint32_t*>(scratch_s + NW * GQ * 64 * 16) + wave * (GQ * RW / 2);
+    if (lane < kQLanes) *reinterpret_cast<uint4*>(qst + 4 * lane) = qchunk;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+      for (int r = 0; r < RW; r += 2) {
+        const uint32_t qq = qst[g * (RW / 2) + r / 2];  // wave-uniform
+        const double q0 = static_cast<double>(__uint_as_float(qq << 16));
+        const double q1 = static_cast<double>(__uint_as_float(qq & 0xFFFF0000u));
+        a0 = fma(q0, static_cast<double>(__uint_as_float(rk[r] << 16)), a0);
+        a1 = fma(q0, static_cast<double>(__uint_as_float(rk[r] & 0xFFFF0000u)), a1);
+        a0 = fma(q1, static_cast<double>(__uint_as_float(rk[r + 1] << 16)), a0);
+        a1 = fma(q1, static_cast<double>(__uint_as_float(rk[r + 1] & 0xFFFF0000u)), a1);
+      }
+      qpart[wave][g][lane][0] = a0;
+      qpart[wave][g][lane][1] = a1;
+    }
+    // padding rows (heads past GQ, and every head's zero row 3) of the limb block
+    for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 64 * NW) {
+      const int row = i >> 3;
+      if ((row >> 2) >= GQ || (row & 3) == 3) *reinterpret_cast<uint4*>(q_s + row * kQRow + 16 * (i & 7)) = uint4{0, 0, 0, 0};
+    }
+    __syncthreads();
+    uint32_t klv = 0u;
+    if constexpr (CB) klv = codebook[2 * kv];
+    QueryScal* qs_s = reinterpret_cast<QueryScal*>(wm_s);
+    for (int g = wave; g < GQ; g += NW) {
+      double x0 = 0.0, x1 = 0.0;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        x0 += qpart[w2][g][lane][0];
+        x1 += qpart[w2][g][lane][1];
+      }
+      const float amax = wave_max_f32(static_cast<float>(fmax(fabs(x0), fabs(x1))));
+      const double sm = wave_sum_f64(x0 + x1);
+      int k = 0;
+      if (amax > 0.f) frexpf(amax, &k);  // amax < 2^k
+      int sh = 21 - k;
+      if (klv != 0u) {
+        const double l1 = wave_sum_f64(fabs(x0) + fabs(x1));
+        int kl = 0;
+        if (l1 > 0.0) frexp(l1, &kl);
+        sh = min(sh, 26 - kl);
+      }
+      const int Q0 = static_cast<int>(rint(x0 * pow2d(sh)));
+      const int Q1 = static_cast<int>(rint(x1 * pow2d(sh)));
+      auto limbs = [](int Q, int& l0, int& l1, int& l2) {
+        l0 = static_cast<signed char>(Q & 0xFF);
+        const int r1 = (Q - l0) >> 8;
+        l1 = static_cast<signed char>(r1 & 0xFF);
+        l2 = (r1 - l1) >> 8;
+      };
+      int la[3], lc[3];
+      limbs(Q0, la[0], la[1], la[2]);
+      limbs(Q1, lc[0], lc[1], lc[2]);
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+        *reinterpret_cast<uint16_t*>(q_s + (4 * g + r) * kQRow + 2 * lane) =
+            static_cast<uint16_t>((la[r] & 0xFF) | ((lc[r] & 0xFF) << 8));
+      // exact integer sum of Q over the 128 dims (|Q| < 2^21): row butterflies, then the rows
+      int sq = Q0 + Q1;
+      sq += __builtin_amdgcn_update_dpp(0, sq, kDppQuadXor1, 0xF, 0xF, false);
+      sq += __builtin_amdgcn_update_dpp(0, sq, kDppQuadXor2, 0xF, 0xF, false);
+      sq += __builtin_amdgcn_update_dpp(0, sq, kDppHalfMirror, 0xF, 0xF, false);
+      sq += __builtin_amdgcn_update_dpp(0, sq, kDppMirror, 0xF, 0xF, false);
+      sq = (__builtin_amdgcn_readlane(sq, 0) + __builtin_amdgcn_readlane(sq, 16)) +
+           (__builtin_amdgcn_readlane(sq, 32) + __builtin_amdgcn_readlane(sq, 48));
+      if (lane == 0) {
+        QueryScal o;
+        o.qsc = static_cast<float>(pow2d(-sh) * iq.scale_log2 * (klv != 0u ? 0.0625 : 1.0));
+        o.sig = static_cast<float>(sm * iq.scale_log2);
+        o.kcent = klv != 0u ? 0 : -2 * sq;
+        qs_s[g] = o;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int g = 4 * mt + G;
+      if (head_ok[mt]) {
+        const QueryScal o = qs_s[g];
+        kcent[mt] = o.kcent;
+        qsc[mt] = o.qsc;
+        sig[mt] = o.sig;
+      }
+    }
+  }
 
   WaveState<MT> st;
 #pragma unroll
@@ -665,7 +801,7 @@ __device__ __forceinline__ void int2_split(
         a = fmaf(s, wacc_s[w][g][dd], a);
       }
     }
-    const size_t o = (static_cast<size_t>(b) * n_q + h0 + g) * n_splits + split;
+    const size_t o = (static_cast<size_t>(b) * n_q + h0 + g) * pstride + split;
     store_partial<kCoherent>(out_acc + o * kHeadDim + dd, a);
     if (dd == 0) {
       store_partial<kCoherent>(out_m + o, big);

@@ -105,12 +105,26 @@ struct StepArgs {
   // Lloyd-Max codebook variant: words [n_kv][K, V], byte c = level c in sixteenths of the
   // scale; null for the uniform INT2 levels
   const uint32_t* codebook;
+  // one-launch step: 1 when token b of k_src / v_src is appended to request b's history
+  // (history token hist_len[b] - 1), 0 for no demotion
+  int append;
 };
 
 // Demotion + window pass + query preparation (one launch), and the INT2 pass with the merge
 // done by the last workgroup of each (request, KV head) (one launch).
 hipError_t launch_prepare(StepArgs a, hipStream_t stream);
 hipError_t launch_attend(StepArgs a, hipStream_t stream);
+
+// The decode step in one launch: window items, appended-token items (each request's
+// appended token demoted, its term written as INT2 partial column n_splits), then INT2
+// splits with the query prepared inline; the last arrival per (request, KV head) merges. `hist` views n_splits + append columns; the counters must be zero at the start
+// and are left at zero.
+hipError_t launch_step_append(StepArgs a, hipStream_t stream);
+// waves per workgroup of launch_step_append's grid
+int step_append_waves(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits);
+// whether the one-launch grid runs in a single dispatch round of 8-wave workgroups (else the
+// step is better run as prepare + attend)
+bool step_append_one_launch(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits);
 
 // Calibration covariances: Sigma_K and Sigma_V [n_kv][128][128] fp32 of one calibration
 // sequence of T tokens (q [T][n_q][128], k and v [T][n_kv][128] bf16); o_work holds

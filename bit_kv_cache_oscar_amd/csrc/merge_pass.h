@@ -135,9 +135,10 @@ __device__ __forceinline__ void load_rv(const uint16_t* __restrict__ rot_v, int 
 
 // Merge of the GQT query heads of KV head kv of request b: `ns` INT2 partials per head
 // (rotated V basis, written by this launch with agent-scope stores) and `nw` window
-// partials per head (written by an earlier launch) into out[b][h][128]. 64 NW threads;
-// 1 <= ns <= kMaxSplits, nw <= kMaxWin; rb from load_rv<NW>.
-template <int GQT, int NW>
+// partials per head into out[b][h][128]. 64 NW threads; 1 <= ns <= kMaxSplits,
+// nw <= kMaxWin; rb from load_rv<NW>. kWinAgent: the window partials were written by this
+// launch with agent-scope stores (else by an earlier launch) and are read at agent scope.
+template <int GQT, int NW, bool kWinAgent = false>
 __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, int b, int kv, int n_q,
                                             const PartialsView& hist, int ns, const PartialsView& win, int nw,
                                             const uint4 (&rb)[8 / NW][4], float* __restrict__ out, int nqt = 1) {
@@ -180,8 +181,8 @@ __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, in
       const int g = gbase + j;
       const uint32_t ho = lane < ns ? static_cast<uint32_t>((g * ns + lane) * 4) : kNoLoad;
       const uint32_t wo = lane >= ns && lane < np ? static_cast<uint32_t>((g * nw + lane - ns) * 4) : kNoLoad;
-      m0[j] = load4_agent(rs_m, ho) + load4(rs_wm, wo);
-      l0[j] = load4_agent(rs_l, ho) + load4(rs_wl, wo);
+      m0[j] = load4_agent(rs_m, ho) + (kWinAgent ? load4_agent(rs_wm, wo) : load4(rs_wm, wo));
+      l0[j] = load4_agent(rs_l, ho) + (kWinAgent ? load4_agent(rs_wl, wo) : load4(rs_wl, wo));
     }
     const uint32_t vbase = static_cast<uint32_t>((g2 * ns * kHeadDim + 4 * quad) * 4);
     // first batch of INT2 value sums: splits slice kBatch + k
@@ -196,7 +197,8 @@ __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, in
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
       const int cw = slice + c * SL;
-      vw[c] = load16(rs_wacc, cw < nw ? static_cast<uint32_t>((((g2 * nw + cw) * kHeadDim) + 4 * quad) * 4) : kNoLoad);
+      const uint32_t off = cw < nw ? static_cast<uint32_t>((((g2 * nw + cw) * kHeadDim) + 4 * quad) * 4) : kNoLoad;
+      vw[c] = kWinAgent ? load16_agent(rs_wacc, off) : load16(rs_wacc, off);
     }
 
     // weights of the wave's heads: common maximum, w = 2^(m - M), 1 / L
@@ -213,8 +215,9 @@ __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, in
           const int s = c0 + lane;
           const uint32_t ho = s < ns ? static_cast<uint32_t>((g * ns + s) * 4) : kNoLoad;
           const uint32_t wo = s >= ns && s < np ? static_cast<uint32_t>((g * nw + s - ns) * 4) : kNoLoad;
-          const float m = s < np ? load4_agent(rs_m, ho) + load4(rs_wm, wo) : -INFINITY;
-          const float l = load4_agent(rs_l, ho) + load4(rs_wl, wo);
+          const float m =
+              s < np ? load4_agent(rs_m, ho) + (kWinAgent ? load4_agent(rs_wm, wo) : load4(rs_wm, wo)) : -INFINITY;
+          const float l = load4_agent(rs_l, ho) + (kWinAgent ? load4_agent(rs_wl, wo) : load4(rs_wl, wo));
           if (s < np) {
             wm[s] = m;
             wl[s] = l;

@@ -544,6 +544,146 @@ int32_t oscar_decode_codebook(const oscar_layer_desc* desc, const void* q, const
 
 }  // extern "C"
 
+// ---- the decode step in one launch, each request appending one token --------------------
+namespace {
+
+int32_t step_append_impl(const oscar_layer_desc* desc, const void* k_src, const void* v_src, const float* clip_k,
+                         const float* clip_v, const void* q, const void* rot_k, const void* rot_v,
+                         const uint32_t* codebook, void* pool, const int32_t* block_table, int32_t max_pages,
+                         const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,
+                         int32_t batch, float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                         float* out, void* stream) {
+  int32_t st = check_desc_impl(desc);
+  if (st != OSCAR_OK) return st;
+  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
+  if (n_splits <= 0) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d <= 0", n_splits);
+  if (n_splits > 255) return fail(OSCAR_ERR_UNSUPPORTED, "n_splits %d > 255 (the one-launch step)", n_splits);
+  if (int32_t e = check_pages(max_pages, n_splits)) return e;
+  const bool append = k_src != nullptr;
+  if (append && (!v_src || !clip_k || !clip_v)) return fail(OSCAR_ERR_INVALID_ARG, "null demotion argument");
+  if (!append && v_src) return fail(OSCAR_ERR_INVALID_ARG, "v_src without k_src");
+  if (!q || !rot_k || !rot_v || !pool || !block_table || !hist_len || !k_win || !v_win || !win_len || !out)
+    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
+  if (!workspace) return fail(OSCAR_ERR_INVALID_ARG, "null workspace");
+  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  const int ws = window_splits_of(desc);
+  const int pstride = n_splits + (append ? 1 : 0);
+  const size_t need = oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits + 1, ws);
+  if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const int gq = desc->n_q_heads / desc->n_kv_heads;
+  const long long items = static_cast<long long>(ws + 1) * desc->n_kv_heads * batch +
+                          static_cast<long long>(n_splits) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1) * batch;
+  if (items > 0x7FFFFFFFLL) return fail(OSCAR_ERR_UNSUPPORTED, "grid of %lld workgroups too large", items);
+  const oscar::LayerShape L = shape_of(desc);
+  char* base = static_cast<char*>(workspace);
+  const size_t hist_bytes = (oscar::partials_bytes(batch, L.n_q, n_splits + 1) + 255) / 256 * 256;
+  const size_t win_bytes = (oscar::partials_bytes(batch, L.n_q, ws) + 255) / 256 * 256;
+  oscar::StepArgs a{};
+  a.batch = batch;
+  a.n_q = L.n_q;
+  a.n_kv = L.n_kv;
+  a.gq = L.gq;
+  a.nqt = 1;
+  a.window = L.window;
+  a.n_splits = n_splits;
+  a.n_wsplits = ws;
+  a.n_groups = 1;
+  a.hist = oscar::partials_view(base, batch, L.n_q, pstride);
+  a.win = oscar::partials_view(base + hist_bytes, batch, L.n_q, ws);
+  a.counters = reinterpret_cast<int*>(base + hist_bytes + win_bytes);
+  a.k_src = static_cast<const uint16_t*>(k_src);
+  a.v_src = static_cast<const uint16_t*>(v_src);
+  a.append = append ? 1 : 0;
+  a.clip_k = clip_k;
+  a.clip_v = clip_v;
+  a.pool = static_cast<uint8_t*>(pool);
+  a.q = static_cast<const uint16_t*>(q);
+  a.rot_k = static_cast<const uint16_t*>(rot_k);
+  a.rot_v = static_cast<const uint16_t*>(rot_v);
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.hist_len = hist_len;
+  a.k_win = static_cast<const uint16_t*>(k_win);
+  a.v_win = static_cast<const uint16_t*>(v_win);
+  a.win_len = win_len;
+  a.scale_log2 = static_cast<double>(sm_scale) * 1.4426950408889634;
+  a.out = out;
+  a.codebook = codebook;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (oscar::step_append_one_launch(batch, L.n_kv, gq > 8 ? gq / 8 : 1, n_splits, ws))
+    return hip_status(oscar::launch_step_append(a, hs), "one-launch step");
+  // a larger grid: prepare (the appended tokens demoted to the slots hist_len - 1 gives,
+  // the window pass, the query preparation), then attend over the whole history
+  a.hist = oscar::partials_view(base, batch, L.n_q, n_splits);
+  a.n_dem_items = append ? 2 * batch * L.n_kv : 0;
+  st = hip_status(oscar::launch_prepare(a, hs), "prepare launch");
+  if (st != OSCAR_OK) return st;
+  return hip_status(oscar::launch_attend(a, hs), "attend launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t oscar_decode_step_append_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
+  return oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits + 1, window_splits_of(desc));
+}
+
+int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0) return 1;
+  const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
+  const int gq = desc->n_q_heads / desc->n_kv_heads;
+  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1);
+  // window items and appended-token items
+  const long long n_win = static_cast<long long>(window_splits_of(desc) + 1) * batch * desc->n_kv_heads;
+  // one 8-wave workgroup per compute unit for window items and splits together while that
+  // keeps at least half the units on the history; otherwise two 4-wave workgroups per unit;
+  // past that (large batches) the two-launch default
+  // one launch when its window and appended-token items and at least half the compute
+  // units' worth of history splits fit one 8-wave workgroup per unit; otherwise the step
+  // runs as prepare + attend, with the two-launch default
+  long long s = (256 - n_win) / groups;
+  const long long by_pages = (pages + 7) / 8;
+  if (s < 1 || s * groups < 128) {
+    const int d = oscar_default_splits(desc, batch, max_hist_len);
+    return d > 255 ? 255 : d;
+  }
+  if (s > by_pages) s = by_pages;
+  const long long need = (pages + kMaxSplitPages - 1) / kMaxSplitPages;
+  if (s < need) s = need;
+  if (s < 1) s = 1;
+  if (s > 255) s = 255;
+  return static_cast<int32_t>(s);
+}
+
+int32_t oscar_decode_step_append(const oscar_layer_desc* desc, const void* k_src, const void* v_src,
+                                 const float* clip_k, const float* clip_v, const void* q, const void* rot_k,
+                                 const void* rot_v, void* pool, const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,
+                                 int32_t batch, float sm_scale, int32_t n_splits, void* workspace,
+                                 size_t workspace_bytes, float* out, void* stream) {
+  return step_append_impl(desc, k_src, v_src, clip_k, clip_v, q, rot_k, rot_v, nullptr, pool, block_table, max_pages,
+                          hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, out,
+                          stream);
+}
+
+int32_t oscar_decode_step_append_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src,
+                                          const float* clip_k, const float* clip_v, const void* q, const void* rot_k,
+                                          const void* rot_v, const uint8_t* codebook, void* pool,
+                                          const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                          const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                          float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                                          float* out, void* stream) {
+  if (int32_t e = check_codebook(codebook)) return e;
+  return step_append_impl(desc, k_src, v_src, clip_k, clip_v, q, rot_k, rot_v,
+                          reinterpret_cast<const uint32_t*>(codebook), pool, block_table, max_pages, hist_len, k_win,
+                          v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, out, stream);
+}
+
+}  // extern "C"
+
 // ---- the decode step without a caller workspace ----------------------------------------
 //
 // For callers that cannot allocate device memory (code under HIP graph capture, serving

@@ -34,8 +34,8 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
                                                    int2::kQprepSmem)];
   int id = blockIdx.x;
   if (id < a.n_dem_items) {
-    demote::demote_row(smem, id, a.k_src, a.v_src, a.n_kv, a.dst_page, a.dst_slot, a.rot_k, a.rot_v, a.clip_k,
-                       a.clip_v, a.pool, a.codebook);
+    demote::demote_row(smem, id, a.k_src, a.v_src, a.n_kv, a.append ? nullptr : a.dst_page, a.dst_slot, a.rot_k,
+                       a.rot_v, a.clip_k, a.clip_v, a.pool, a.codebook, a.block_table, a.max_pages, a.hist_len);
     return;
   }
   id -= a.n_dem_items;
@@ -137,6 +137,93 @@ hipError_t launch_main(const StepArgs& a, hipStream_t stream) {
   return a.codebook ? launch_main_cb<GQ, GQT, true>(a, stream) : launch_main_cb<GQ, GQT, false>(a, stream);
 }
 
+// The one-launch step. Items 0 .. n_win - 1 are window splits (split c, KV head, request);
+// when appending, the next B n_kv items each demote the appended token of one (request, KV
+// head) and write its own attention term; the rest are INT2 splits (split, KV head x head
+// group, request) with the query prepared inline and the appended token left out. Every
+// item starts at once, writes its partials with agent-scope stores and draws a ticket; the
+// last of a (request, KV head) merges.
+template <int GQ, int GQT, int NW, bool CB>
+__global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
+  constexpr int kSmem = cmax(cmax(int2::int2_smem_bytes<GQ, NW>(), merge::smem_bytes<GQT, NW>()),
+                             cmax(window::window_smem_bytes<GQT>(), demote::append_smem_bytes<GQT>()));
+  __shared__ __align__(16) unsigned char smem[kSmem];
+  __shared__ int ticket_s;
+  const int n_win = a.n_wsplits * a.n_kv * a.batch;
+  const int pstride = a.n_splits + a.append;
+  int id = blockIdx.x;
+  int kv, b;
+  const int n_app = a.append ? a.n_kv * a.batch : 0;
+  if (id < n_win) {
+    const int c = id % a.n_wsplits;
+    kv = (id / a.n_wsplits) % a.n_kv;
+    b = id / (a.n_wsplits * a.n_kv);
+    window::window_split<GQT, NW, true>(smem, c, kv, kv * GQT, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q, a.n_kv,
+                                        a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc, GQT, 1);
+  } else if (id < n_win + n_app) {
+    id -= n_win;
+    kv = id % a.n_kv;
+    b = id / a.n_kv;
+    demote::append_token<NW, GQT>(smem, b, kv, a, a.n_splits, pstride);
+  } else {
+    id -= n_win + n_app;
+    const int split = id % a.n_splits;
+    const int gy = (id / a.n_splits) % (a.n_kv * a.n_groups);
+    b = id / (a.n_splits * a.n_kv * a.n_groups);
+    kv = gy / a.n_groups;
+    int2::InlineQuery iq;
+    iq.q = a.q;
+    iq.rot_k = a.rot_k;
+    iq.scale_log2 = a.scale_log2;
+    iq.n_excl = a.append;
+    iq.pstride = pstride;
+    int2::int2_split<GQ, true, NW, CB>(smem, split, gy, b, a.pool, a.block_table, a.max_pages, a.hist_len, a.n_q,
+                                       a.n_kv, a.n_groups, a.n_splits, nullptr, nullptr, a.hist.m, a.hist.l,
+                                       a.hist.acc, a.codebook, iq);
+  }
+  // the partials went out as agent-scope stores: once each thread's stores have completed
+  // and the barrier has passed, the ticket below is drawn after all of them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* counter = a.counters + b * a.n_kv + kv;
+  if (threadIdx.x == 0) ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (ticket_s != a.n_splits * a.n_groups + a.n_wsplits + a.append - 1) return;
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint4 rb[8 / NW][4];
+  merge::load_rv<NW>(a.rot_v, kv, rb);
+  merge::merge_group<GQT, NW, true>(smem, b, kv, a.n_q, a.hist, pstride, a.win, a.n_wsplits, rb, a.out, 1);
+}
+
+constexpr int kStepSlots8 = 256;  // 8-wave workgroups resident at once (one per compute unit)
+
+int append_waves(long long items) { return items <= kStepSlots8 ? 8 : 4; }
+
+}  // namespace
+
+bool step_append_one_launch(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits) {
+  return static_cast<long long>(n_wsplits + 1) * n_kv * batch + static_cast<long long>(n_splits) * n_kv * n_groups * batch <=
+         kStepSlots8;
+}
+
+namespace {
+
+template <int GQ, int GQT, bool CB>
+hipError_t launch_append_cb(const StepArgs& a, hipStream_t stream) {
+  const long long items = static_cast<long long>(a.n_wsplits + a.append) * a.n_kv * a.batch +
+                          static_cast<long long>(a.n_splits) * a.n_kv * a.n_groups * a.batch;
+  if (append_waves(items) == 8)
+    hipLaunchKernelGGL((append_kernel<GQ, GQT, 8, CB>), dim3(static_cast<unsigned>(items)), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((append_kernel<GQ, GQT, 4, CB>), dim3(static_cast<unsigned>(items)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int GQ, int GQT>
+hipError_t launch_append(const StepArgs& a, hipStream_t stream) {
+  return a.codebook ? launch_append_cb<GQ, GQT, true>(a, stream) : launch_append_cb<GQ, GQT, false>(a, stream);
+}
+
 }  // namespace
 
 hipError_t launch_prepare(StepArgs a, hipStream_t stream) {
@@ -157,6 +244,26 @@ hipError_t launch_attend(StepArgs a, hipStream_t stream) {
     case 4: a.n_groups = 1; return launch_main<4, 4>(a, stream);
     case 8: a.n_groups = 1; return launch_main<8, 8>(a, stream);
     case 16: a.n_groups = 2; return launch_main<8, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace oscar
+
+namespace oscar {
+
+int step_append_waves(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits) {
+  return append_waves(static_cast<long long>(n_wsplits + 1) * n_kv * batch +
+                      static_cast<long long>(n_splits) * n_kv * n_groups * batch);
+}
+
+hipError_t launch_step_append(StepArgs a, hipStream_t stream) {
+  switch (a.gq) {
+    case 1: a.n_groups = 1; return launch_append<1, 1>(a, stream);
+    case 2: a.n_groups = 1; return launch_append<2, 2>(a, stream);
+    case 4: a.n_groups = 1; return launch_append<4, 4>(a, stream);
+    case 8: a.n_groups = 1; return launch_append<8, 8>(a, stream);
+    case 16: a.n_groups = 2; return launch_append<8, 16>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

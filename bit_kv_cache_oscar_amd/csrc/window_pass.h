@@ -30,10 +30,13 @@ constexpr int window_smem_bytes() {
   return 4 * (2 * 4 * 16 + GQ * kPageTokens + 4 * GQ * kHeadDim);
 }
 
-// One workgroup (256 threads) of the BF16 window pass: slots 64 c .. 64 c + 63 of KV head kv
-// of request b for its query heads h0 .. h0 + GQ - 1 (GQ <= 16; the KV head's heads, or a
-// group of them when several workgroups share a KV head). `smem` holds window_smem_bytes<GQ>().
-template <int GQ>
+// One workgroup of the BF16 window pass: slots 64 c .. 64 c + 63 of KV head kv of request b
+// for its query heads h0 .. h0 + GQ - 1 (GQ <= 16; the KV head's heads, or a group of them
+// when several workgroups share a KV head). `smem` holds window_smem_bytes<GQ>(). The pass
+// uses four waves; a workgroup of NWB waves (4 or 8) lets the others pass its barriers
+// idle. kCoherent: the partial goes out with agent-scope stores (for a merge inside the
+// same launch).
+template <int GQ, int NWB = 4, bool kCoherent = false>
 __device__ __forceinline__ void window_split(
     unsigned char* __restrict__ smem, int c, int kv, int h0, int b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_win, const uint16_t* __restrict__ v_win,
     const int32_t* __restrict__ win_len, int n_q, int n_kv, int window, int n_wsplits, double scale_log2,
@@ -43,9 +46,11 @@ __device__ __forceinline__ void window_split(
   float(*l_s)[16] = reinterpret_cast<float(*)[16]>(smem + 4 * 64);
   float(*p_s)[kPageTokens] = reinterpret_cast<float(*)[kPageTokens]>(smem + 4 * 128);
   float(*acc_s)[GQ][kHeadDim] = reinterpret_cast<float(*)[GQ][kHeadDim]>(smem + 4 * 128 + 4 * GQ * kPageTokens);
+  static_assert(NWB == 4 || NWB == 8, "4 or 8 waves");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool act = NWB == 4 || wave < 4;  // wave-uniform: the waves that do the pass
   const int t0 = c * kPageTokens;
   const size_t base = ((static_cast<size_t>(b) * n_kv + kv) * window + t0) * kHeadDim;
   // the window length first: the score mask needs it as soon as K and q have arrived
@@ -66,12 +71,12 @@ __device__ __forceinline__ void window_split(
   uint4 ka[4], qb[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    ka[s] = t0 + kslot < window
+    ka[s] = act && t0 + kslot < window
                 ? *reinterpret_cast<const uint4*>(k_win + base + static_cast<size_t>(kslot) * kHeadDim + 32 * s + 8 * g)
                 : make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    qb[s] = r < GQ ? *reinterpret_cast<const uint4*>(q + query_row(b, h0 + r, n_q, gqv, nqt) * kHeadDim + 32 * s + 8 * g)
+    qb[s] = act && r < GQ ? *reinterpret_cast<const uint4*>(q + query_row(b, h0 + r, n_q, gqv, nqt) * kHeadDim + 32 * s + 8 * g)
                    : make_uint4(0, 0, 0, 0);
   // value operands: thread (dim pair dp, slot group sg)
   const int dp = tid & 63;
@@ -80,7 +85,7 @@ __device__ __forceinline__ void window_split(
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int t = 16 * sg + i;
-    vv[i] = t0 + t < window ? *reinterpret_cast<const uint32_t*>(v_win + base + static_cast<size_t>(t) * kHeadDim + 2 * dp)
+    vv[i] = act && t0 + t < window ? *reinterpret_cast<const uint32_t*>(v_win + base + static_cast<size_t>(t) * kHeadDim + 2 * dp)
                             : 0u;
   }
 
@@ -101,7 +106,7 @@ __device__ __forceinline__ void window_split(
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  if (g == 0) mx_s[wave][r] = mx;
+  if (act && g == 0) mx_s[wave][r] = mx;
   __syncthreads();
   // per head: reference point = the largest score, weights, their sum
   const float big = fmaxf(fmaxf(mx_s[0][r], mx_s[1][r]), fmaxf(mx_s[2][r], mx_s[3][r]));
@@ -110,12 +115,12 @@ __device__ __forceinline__ void window_split(
   for (int j = 0; j < 4; ++j) {
     const int slot = 16 * wave + 4 * g + j;
     const float pt = slot < ntok_r ? exp2f(sc[j] - big) : 0.f;
-    if (r < GQ) p_s[r][slot] = pt;
+    if (act && r < GQ) p_s[r][slot] = pt;
     ls += pt;
   }
   ls += __shfl_xor(ls, 16, 64);
   ls += __shfl_xor(ls, 32, 64);
-  if (g == 0) l_s[wave][r] = ls;
+  if (act && g == 0) l_s[wave][r] = ls;
   __syncthreads();
 
   // ---- value sum: slots past ntok have weight 0 but their V words may hold anything
@@ -136,20 +141,28 @@ __device__ __forceinline__ void window_split(
       a1[h] = fmaf(pt, v1, a1[h]);
     }
   }
+  if (act) {
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    acc_s[sg][h][2 * dp] = a0[h];
-    acc_s[sg][h][2 * dp + 1] = a1[h];
+    for (int h = 0; h < GQ; ++h) {
+      acc_s[sg][h][2 * dp] = a0[h];
+      acc_s[sg][h][2 * dp + 1] = a1[h];
+    }
   }
   __syncthreads();
-  for (int idx = tid; idx < GQ * kHeadDim; idx += 256) {
+  for (int idx = tid; idx < GQ * kHeadDim; idx += 64 * NWB) {
     const int h = idx >> 7;
     const int d = idx & 127;
     const size_t o = (static_cast<size_t>(b) * n_q + h0 + h) * n_wsplits + c;
-    out_acc[o * kHeadDim + d] = (acc_s[0][h][d] + acc_s[1][h][d]) + (acc_s[2][h][d] + acc_s[3][h][d]);
+    auto put = [](float* p, float v) {
+      if constexpr (kCoherent)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        *p = v;
+    };
+    put(out_acc + o * kHeadDim + d, (acc_s[0][h][d] + acc_s[1][h][d]) + (acc_s[2][h][d] + acc_s[3][h][d]));
     if (d == 0) {
-      out_m[o] = fmaxf(fmaxf(mx_s[0][h], mx_s[1][h]), fmaxf(mx_s[2][h], mx_s[3][h]));  // -inf: no slot
-      out_l[o] = (l_s[0][h] + l_s[1][h]) + (l_s[2][h] + l_s[3][h]);
+      put(out_m + o, fmaxf(fmaxf(mx_s[0][h], mx_s[1][h]), fmaxf(mx_s[2][h], mx_s[3][h])));  // -inf: no slot
+      put(out_l + o, (l_s[0][h] + l_s[1][h]) + (l_s[2][h] + l_s[3][h]));
     }
   }
 }

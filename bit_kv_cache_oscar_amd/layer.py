@@ -52,6 +52,7 @@ class LayerCache:
         self.codebook = None  # Lloyd-Max variant: uint8 [Hkv, 2, 4] levels (None: uniform INT2)
         self._partials = None
         self._workspace = None
+        self._append_ws = None
         self.win_partials = torch.zeros(L.oscar_partials_bytes(self.desc, batch, L.oscar_window_splits(self.desc)),
                                         dtype=torch.uint8, device=self.device)
 
@@ -107,6 +108,15 @@ class LayerCache:
         return self._workspace
 
     @property
+    def append_workspace(self) -> torch.Tensor:
+        """Workspace of the one-launch step, zero-filled when allocated (its arrival counters
+        must start at zero; every call leaves them there)."""
+        need = L.oscar_decode_step_append_workspace_bytes(self.desc, self.batch, self.n_splits)
+        if self._append_ws is None or self._append_ws.numel() < need:
+            self._append_ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+        return self._append_ws
+
+    @property
     def partials(self) -> torch.Tensor:
         if self._partials is None:
             self.set_splits(self.n_splits)
@@ -143,4 +153,12 @@ class LayerCache:
         L.oscar_decode_step(self.desc, k_rows, v_rows, pages, slots, self.clip_k, self.clip_v, q, self.rot_k,
                             self.rot_v, self.pool, self.block_table, self.hist_len, self.k_win, self.v_win,
                             self.win_len, sm_scale, self.n_splits, self.workspace, self.out, stream, self.codebook)
+        return self.out
+
+    def step_append(self, k_rows, v_rows, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
+        """One decode step in one launch (oscar_decode_step_append): k_rows/v_rows [B, Hkv, 128]
+        (or None) become history token hist_len[b] - 1 of each request b, then decode q."""
+        L.oscar_decode_step_append(self.desc, k_rows, v_rows, self.clip_k, self.clip_v, q, self.rot_k, self.rot_v,
+                                   self.pool, self.block_table, self.hist_len, self.k_win, self.v_win, self.win_len,
+                                   sm_scale, self.n_splits, self.append_workspace, self.out, stream, self.codebook)
         return self.out

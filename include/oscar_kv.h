@@ -242,6 +242,59 @@ int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const
                           int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * oscar_decode_step_append: one decode step of one layer in a single launch, for the
+ * serving loop's usual demotion: each request b appends one token, its oldest recent token,
+ * to the end of its INT2 history, then decodes.
+ * (QbitAI article on OSCAR, serving-path section: the oldest recent token is rotated,
+ * clipped, quantised, packed and demoted into the INT2 history; decode processes the BF16
+ * sink/recent and the INT2 history separately and joins them by an online-softmax merge.)
+ *
+ * Token b of k_src / v_src (bf16 [batch][n_kv_heads][128]) becomes history token
+ * hist_len[b] - 1 of request b, in the page and slot the block table gives it (hist_len
+ * counts it), demoted exactly as oscar_demote demotes it; the output is then that of
+ * oscar_decode over the updated pool. That page must be one no other request of the call
+ * reads (as in paged serving, where a request appends into its own last page, never into
+ * a shared prefix page). k_src == NULL (with v_src, clip_k, clip_v NULL or
+ * ignored) demotes nothing and decodes the pool as it is. A request with hist_len 0 while
+ * appending is skipped (nothing is demoted for it).
+ * One launch: window workgroups, and INT2 workgroups that rotate the query themselves; the
+ * window workgroup of each (request, KV head)'s first split also demotes the appended token
+ * and contributes that token's attention term; the workgroup that finishes last per
+ * (request, KV head) merges. No workgroup waits for another. While the appended token's V
+ * codes are written, INT2 workgroups may read the 32-bit words that hold them; that slot has
+ * weight zero in their pass, so whichever value such a read returns, the result is the same.
+ * Arguments are those of oscar_decode_step, plus:
+ *   n_splits   1..255, and ceil(max_pages / n_splits) <= 8192; oscar_decode_step_append_splits
+ *              gives the count for which the launch's workgroups fit the chip at once
+ *   workspace  at least oscar_decode_step_append_workspace_bytes(desc, batch, n_splits)
+ *              bytes of device memory, owned by the caller, whose arrival counters must be
+ *              zero before the first call: zero-fill it once after allocating it; every
+ *              call leaves them at zero (oscar_decode_step and oscar_decode leave them at
+ *              zero too, so a workspace can serve both). Calls that share a workspace must
+ *              not overlap in time.
+ * Errors: OSCAR_ERR_INVALID_ARG (null pointers, batch or n_splits <= 0, bad sm_scale),
+ * OSCAR_ERR_UNSUPPORTED (sizes past the limits above), OSCAR_ERR_WORKSPACE (too small),
+ * OSCAR_ERR_HIP (launch failure).
+ */
+size_t oscar_decode_step_append_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits);
+int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len);
+int32_t oscar_decode_step_append(const oscar_layer_desc* desc, const void* k_src, const void* v_src,
+                                 const float* clip_k, const float* clip_v, const void* q, const void* rot_k,
+                                 const void* rot_v, void* pool, const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,
+                                 int32_t batch, float sm_scale, int32_t n_splits, void* workspace,
+                                 size_t workspace_bytes, float* out, void* stream);
+/* oscar_decode_step_append with the Lloyd-Max codebook (as oscar_demote_codebook and
+ * oscar_decode_codebook). */
+int32_t oscar_decode_step_append_codebook(const oscar_layer_desc* desc, const void* k_src, const void* v_src,
+                                          const float* clip_k, const float* clip_v, const void* q, const void* rot_k,
+                                          const void* rot_v, const uint8_t* codebook, void* pool,
+                                          const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
+                                          const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
+                                          float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                                          float* out, void* stream);
+
+/*
  * oscar_decode_step_noalloc: oscar_decode_step without a workspace argument, for callers
  * that cannot allocate device memory (code under HIP graph capture, serving loops that
  * forbid hipMalloc). The same kernels and the same result as oscar_decode_step; its

@@ -517,6 +517,19 @@ def test_full_size_benchmarked_path(cfg):
     c.out.fill_(np.nan)
     say("full size four entry points", w.name)
     outs["decode"] = c.decode(q, w.sm_scale).cpu().numpy()
+    # the one-launch step at its own split count (what the benchmark's step times): the
+    # same last tokens appended again (the same bytes), twice, then once without appending
+    from bit_kv_cache_oscar_amd import oscar_decode_step_append_splits
+
+    sa = oscar_decode_step_append_splits(c.desc, w.batch, int(w.hist_lens.max()))
+    c.set_splits(sa)
+    for rep in range(2):
+        say("full size one-launch step", w.name, "splits", sa, "call", rep)
+        c.out.fill_(np.nan)
+        outs[f"one-launch {rep}"] = c.step_append(bf16(np.stack(last_k)), bf16(np.stack(last_v)), q,
+                                                 w.sm_scale).cpu().numpy()
+    c.out.fill_(np.nan)
+    outs["one-launch decode"] = c.step_append(None, None, q, w.sm_scale).cpu().numpy()
     torch.cuda.synchronize()
     pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
     for b, kv in FULL_PAIRS[cfg]:
@@ -753,3 +766,82 @@ def test_demotion_fp16_overflow_contract(n):
         vc, vs, vz, vm = oquant.quantize_rows(rows[::-1][keep_v, kv].astype(np.float64), rv[kv], w.clip_ratio)
         mine = (kcg[keep], ksg[keep], kzg[keep], vcg[keep_v], vsg[keep_v], vzg[keep_v])
         assert compare_history(mine, (kc, ks, kz, vc, vs, vz), km, vm, f"overflow call head {kv}") == 0
+
+
+APPEND_CASES = {
+    "c1": lambda: synth.workload(1),
+    "c2-4k": lambda: synth.workload(2).with_ctx([4000]),
+    "c3-6k-permuted": lambda: synth.workload(3).with_ctx([6000]),
+    # every request's last history token past the shared prefix: appended tokens land in
+    # pages of their own request
+    "c4-shared-ragged": lambda: synth.workload(4).with_ctx([4596, 5096, 4500, 4096 + 128 + 320 + 3], capacity=6000),
+    "c5-gq8": lambda: synth.workload(5).with_ctx([3000, 2600]),
+    "gq16": lambda: custom("gq16", 32, 2, [2500, 900]),
+    "gq2": lambda: custom("gq2", 16, 8, [1500]),
+    "gq1": lambda: custom("gq1", 4, 4, [900, 1700]),
+    "edges": lambda: custom("edges", 8, 2, [321, 64 * 3 + 320 + 1, 64 + 320, 64 * 5 + 320 + 63]),
+}
+
+
+def _fill_but_last(c, w, table):
+    """Every history token but each request's last through oscar_demote; returns the last
+    tokens' rows [B, Hkv, 128] (float32 bf16 values)."""
+    last_k, last_v = [], []
+    for b in range(w.batch):
+        n = w.hist_len(b)
+        start = min(n, w.shared_pages * 64) if (w.shared_pages and b > 0) else 0
+        assert n - 1 >= start, "the appended token must lie in a page of its own request"
+        ks, vs = [], []
+        for kv in range(w.n_kv_heads):
+            k, v = synth.kv_rows(w, b, kv, 64 + start, 64 + n)
+            ks.append(k)
+            vs.append(v)
+        ks, vs = np.stack(ks, 1), np.stack(vs, 1)
+        j = np.arange(start, n)
+        if n - 1 > start:
+            _demote_all(c, w, b, table[b, j[:-1] // 64], j[:-1] % 64, ks[:-1], vs[:-1])
+        last_k.append(ks[-1])
+        last_v.append(vs[-1])
+    return np.stack(last_k), np.stack(last_v)
+
+
+@pytest.mark.parametrize("case", list(APPEND_CASES))
+def test_decode_step_append_one_launch(case):
+    """oscar_decode_step_append: every history token but each request's last through
+    oscar_demote, the last one appended by the one-launch step, which then decodes; the pool
+    (every token) and the output against the oracle, at the one-launch default split count
+    and at 3 splits; then the same launch without appending (the pool as it is), twice in a
+    row (the arrival counters must re-arm)."""
+    from bit_kv_cache_oscar_amd import oscar_decode_step_append_splits
+
+    w = APPEND_CASES[case]()
+    (rk_bits, rv_bits), (rk, rv) = rotations(w)
+    table, n_phys = synth.block_table(w)
+    c = make_cache(w, rk_bits, rv_bits, table, n_phys)
+    lk, lv = _fill_but_last(c, w, table)
+    refs = []
+    for b in range(w.batch):
+        hists = {}
+        for kv in range(w.n_kv_heads):
+            hists[kv], _, _ = oracle_history(w, b, kv, rk, rv)
+        refs.append(oracle_decode(w, b, rk, rv, hists))
+    q = queries(w)
+    s = oscar_decode_step_append_splits(c.desc, w.batch, int(w.hist_lens.max()))
+    for splits in sorted({s, 3}):
+        c.set_splits(splits)
+        say(case, "one-launch step", "B", w.batch, "Hq", w.n_q_heads, "Hkv", w.n_kv_heads, "splits", splits)
+        c.out.fill_(np.nan)
+        got = c.step_append(bf16(lk), bf16(lv), q, w.sm_scale).cpu().numpy()
+        for b in range(w.batch):
+            assert_close(got[b], refs[b], f"{case} one-launch step b{b} splits {splits}")
+        pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
+        for b in range(w.batch):
+            for kv in range(w.n_kv_heads):
+                ref_hist, km, vm = oracle_history(w, b, kv, rk, rv)
+                gpu_hist = opages.unpack_history(pool, table[b], kv, w.hist_len(b))
+                compare_history(gpu_hist, ref_hist, km, vm, f"{case} one-launch pool b{b} kv{kv}")
+        for rep in range(2):
+            c.out.fill_(np.nan)
+            got = c.step_append(None, None, q, w.sm_scale).cpu().numpy()
+            for b in range(w.batch):
+                assert_close(got[b], refs[b], f"{case} one-launch decode b{b} splits {splits} call {rep}")
