@@ -23,6 +23,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "merge_pass.h"
 #include "launch.h"
 
 namespace oscar {
@@ -252,9 +253,10 @@ __device__ __forceinline__ void demote_row(unsigned char* __restrict__ smem, int
 
 // LDS of append_token: per row group, the quarter sums of waves 1..3 ([3][64][4] doubles),
 // and the K group's quarter sums of q R_K for each query head ([3][GQT][64][2] doubles)
+// and the packed bf16 high / low parts of the dequantised V row for its un-rotation
 template <int GQT>
 constexpr int append_smem_bytes() {
-  return 2 * 3 * 64 * 4 * 8 + 3 * GQT * 64 * 2 * 8;
+  return 2 * 3 * 64 * 4 * 8 + 3 * GQT * 64 * 2 * 8 + 2 * merge::kARow * 4;
 }
 
 // Level of code c in the dequantisation: c for the uniform levels, level c of the codebook
@@ -272,14 +274,17 @@ __device__ __forceinline__ double level_of(int c, uint32_t lv) {
 // products are exact); V on waves 4..7, or after K on a 4-wave workgroup. It is the work of
 // a workgroup of its own, from the start of the launch. Every wave of the workgroup calls
 // this (it holds barriers); the partial goes out with agent-scope stores.
-// A request with an empty history gets an empty partial.
-template <int NW, int GQT>
+// A request with an empty history gets an empty partial. With kUnrot the partial's value
+// is un-rotated (times R_V^T) before it is written, as the INT2 splits' then are.
+template <int NW, int GQT, bool kUnrot = false>
 __device__ __forceinline__ void append_token(unsigned char* __restrict__ smem, int b, int kv, const StepArgs& a,
                                              int col, int pstride) {
 #pragma clang fp contract(off)
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   double(*rpart)[3][64][4] = reinterpret_cast<double(*)[3][64][4]>(smem);
   double(*qpart)[GQT][64][2] = reinterpret_cast<double(*)[GQT][64][2]>(smem + 2 * 3 * 64 * 4 * 8);
+  uint32_t* vhi_s = reinterpret_cast<uint32_t*>(smem + 2 * 3 * 64 * 4 * 8 + 3 * GQT * 64 * 2 * 8);
+  uint32_t* vlo_s = vhi_s + merge::kARow;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int nh = a.hist_len[b];
@@ -296,6 +301,8 @@ __device__ __forceinline__ void append_token(unsigned char* __restrict__ smem, i
     }
     return;
   }
+  uint4 rb[8 / NW][4];
+  if constexpr (kUnrot) merge::load_rv<NW>(a.rot_v, kv, rb);
   const int j = nh - 1;
   const int page = a.block_table[static_cast<size_t>(b) * a.max_pages + j / kPageTokens];
   const int slot = j % kPageTokens;
@@ -396,6 +403,8 @@ __device__ __forceinline__ void append_token(unsigned char* __restrict__ smem, i
             put(a.hist.l + o, 1.f);
           }
         }
+      } else if constexpr (kUnrot) {
+        merge::split2(static_cast<float>(h0), static_cast<float>(h1), vhi_s[lane], vlo_s[lane]);
       } else {
 #pragma unroll
         for (int g = 0; g < GQT; ++g) {
@@ -406,6 +415,15 @@ __device__ __forceinline__ void append_token(unsigned char* __restrict__ smem, i
       }
     }
     if (NW == 4 && pass == 0) __syncthreads();  // the V pass reuses the LDS
+  }
+  if constexpr (kUnrot) {
+    // the V row's A operand is in LDS: every wave un-rotates its output tiles, for all
+    // the KV head's query heads (the same vector)
+    __syncthreads();
+    merge::unrotate_tiles<NW>(vhi_s, vlo_s, 1, rb, [&](int, int d, float v) {
+#pragma unroll
+      for (int g = 0; g < GQT; ++g) put(a.hist.acc + ((hrow + g) * pstride + col) * kHeadDim + d, v);
+    });
   }
 }
 

@@ -130,6 +130,19 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// fp32 sum over the whole wave without LDS traffic: row butterflies, then the four rows
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = row16_sum(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+// two bf16 values in one dword (low half first), the operand type of the bf16 pair dot product
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const long long b = __double_as_longlong(v);

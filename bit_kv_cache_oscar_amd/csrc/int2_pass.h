@@ -55,6 +55,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "merge_pass.h"
 #include "launch.h"
 
 namespace oscar {
@@ -302,13 +303,16 @@ struct InlineQuery {
 // One workgroup (NW waves) of the INT2 pass: history split `split` of request b for the
 // query heads gy*GQ .. gy*GQ+GQ-1 (KV head gy / n_groups). `smem` holds
 // int2_smem_bytes<GQ, NW>(). With CB, `codebook` holds the codebook words [n_kv][K, V].
-template <int GQ, bool kCoherent = false, int NW = kWaves, bool CB = false>
+// With kUnrot the split's value sum is un-rotated (times R_V^T, rot_v [n_kv][128][128])
+// before it is written, so its partial is in the basis of the BF16 window's; otherwise it
+// stays in the rotated basis of R_V.
+template <int GQ, bool kCoherent = false, int NW = kWaves, bool CB = false, bool kUnrot = false>
 __device__ __forceinline__ void int2_split(
     unsigned char* __restrict__ smem, int split, int gy, int b, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ hist_len, int n_q, int n_kv, int n_groups, int n_splits,
     const char* __restrict__ qlimb, const QueryScal* __restrict__ qscal, float* __restrict__ out_m,
     float* __restrict__ out_l, float* __restrict__ out_acc, const uint32_t* __restrict__ codebook = nullptr,
-    const InlineQuery& iq = InlineQuery()) {
+    const InlineQuery& iq = InlineQuery(), const uint16_t* __restrict__ rot_v = nullptr) {
   constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
   constexpr int kPBytes = NW * MT * 16 * kPRow;
   constexpr int kFBytes = NW * MT * kFlushed * 64 * 4;
@@ -429,6 +433,51 @@ __device__ __forceinline__ void int2_split(
     }
     return head_base + static_cast<size_t>(__builtin_amdgcn_readlane(blk_lane, j & 63)) * page_stride;
   };
+  // Inline query preparation: q_rot = q R_K for the workgroup's heads, each wave over its
+  // RW rows with bf16 pair dot products (exact products, fp32 sums), joined through LDS;
+  // then per head (one wave each) the 22-bit fixed point, its limbs into the LDS rows of
+  // the page loop, and the head's scalars, as the separate query preparation computes
+  // them. The join uses the page loop's LDS; a head's scalars go to the spare bytes past
+  // the 128 dims of its first limb row, which nothing writes afterwards. The dot products come
+  // before the first page loads are issued: issuing those of all waves takes the compute
+  // unit's vector-memory path several hundred nanoseconds, which the query would wait out.
+  static_assert(NW * GQ * 64 * 8 + NW * GQ * RW * 2 <= kLoopBytes + kWaccBytes, "the query join fits the loop's LDS");
+  static_assert(kQRow - kHeadDim >= 16, "a head's scalars fit its row's spare bytes");
+  float2(*qpart)[GQ][64] = reinterpret_cast<float2(*)[GQ][64]>(scratch_s);
+  if (inline_q) {
+    // wave-private staging of the wave's query values: [GQ][RW] bf16 (the wave's own LDS
+    // accesses run in order, so no barrier is needed before reading them back)
+    uint32_t* qst = reinterpret_cast<uint32_t*>(scratch_s + NW * GQ * 64 * 8) + wave * (GQ * RW / 2);
+    if (lane < kQLanes) *reinterpret_cast<uint4*>(qst + 4 * lane) = qchunk;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // R_K pairs along the rows: (R[r][c], R[r + 1][c]) for this lane's columns c = 2 lane
+    // (low halves) and 2 lane + 1 (high halves)
+    uint32_t rc0[RW / 2], rc1[RW / 2];
+#pragma unroll
+    for (int j = 0; j < RW / 2; ++j) {
+      rc0[j] = __builtin_amdgcn_perm(rk[2 * j + 1], rk[2 * j], 0x05040100u);
+      rc1[j] = __builtin_amdgcn_perm(rk[2 * j + 1], rk[2 * j], 0x07060302u);
+    }
+#pragma unroll
+    for (int g = 0; g < GQ; ++g) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < RW / 2; ++j) {
+        const uint32_t qq = qst[g * (RW / 2) + j];  // (q[r], q[r + 1]), wave-uniform
+        a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq), __builtin_bit_cast(bf16x2_t, rc0[j]), a0, false);
+        a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qq), __builtin_bit_cast(bf16x2_t, rc1[j]), a1, false);
+      }
+      qpart[wave][g][lane] = make_float2(a0, a1);
+    }
+    // padding rows (heads past GQ, and every head's zero row 3) of the limb block
+    for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 64 * NW) {
+      const int row = i >> 3;
+      if ((row >> 2) >= GQ || (row & 3) == 3) *reinterpret_cast<uint4*>(q_s + row * kQRow + 16 * (i & 7)) = uint4{0, 0, 0, 0};
+    }
+  }
+  // keep the page loads below the dot products
+  __builtin_amdgcn_sched_barrier(0);
+
   // three page buffers: pages i + 1 and i + 2 load while page i is processed. A wave
   // without pages issues the same loads against an empty buffer, so every path carries
   // the same loads into the loop.
@@ -437,66 +486,31 @@ __device__ __forceinline__ void int2_split(
   load_page(buf[0], page_of(0), lane32, meta16, rec);
   load_page(buf[1], page_of(n_mine > 1 ? 1 : 0), lane32, meta16, rec);
   if (inline_q) {
-    // while the first pages load: q_rot = q R_K for the workgroup's heads in fp64 (bf16
-    // products are exact), each wave over its RW rows, joined through LDS; then per head
-    // (one wave each) the 22-bit fixed point, its limbs into the LDS rows of the page loop,
-    // and the head's scalars, as the separate query preparation computes them
-    // the join uses the page loop's LDS; the heads' scalars the epilogue's (wm_s, wl_s),
-    // which the page loop's set-up below does not touch
-    static_assert(NW * GQ * 64 * 16 <= kLoopBytes + kWaccBytes, "the query join fits the loop's LDS");
-    static_assert(GQ * static_cast<int>(sizeof(QueryScal)) <= 2 * NW * GQ * 4, "the heads' scalars fit");
-    static_assert(NW * GQ * 64 * 16 + NW * GQ * RW * 2 <= kLoopBytes + kWaccBytes, "the staged query fits too");
-    double(*qpart)[GQ][64][2] = reinterpret_cast<double(*)[GQ][64][2]>(scratch_s);
-    // wave-private staging of the wave's query values: [GQ][RW] bf16 (the wave's own LDS
-    // accesses run in order, so no barrier is needed before reading them back)
-    uint32_t* qst = reinterpret_cast<uint32_t*>(scratch_s + NW * GQ * 64 * 16) + wave * (GQ * RW / 2);
-    if (lane < kQLanes) *reinterpret_cast<uint4*>(qst + 4 * lane) = qchunk;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-#pragma unroll
-    for (int g = 0; g < GQ; ++g) {
-      double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-      for (int r = 0; r < RW; r += 2) {
-        const uint32_t qq = qst[g * (RW / 2) + r / 2];  // wave-uniform
-        const double q0 = static_cast<double>(__uint_as_float(qq << 16));
-        const double q1 = static_cast<double>(__uint_as_float(qq & 0xFFFF0000u));
-        a0 = fma(q0, static_cast<double>(__uint_as_float(rk[r] << 16)), a0);
-        a1 = fma(q0, static_cast<double>(__uint_as_float(rk[r] & 0xFFFF0000u)), a1);
-        a0 = fma(q1, static_cast<double>(__uint_as_float(rk[r + 1] << 16)), a0);
-        a1 = fma(q1, static_cast<double>(__uint_as_float(rk[r + 1] & 0xFFFF0000u)), a1);
-      }
-      qpart[wave][g][lane][0] = a0;
-      qpart[wave][g][lane][1] = a1;
-    }
-    // padding rows (heads past GQ, and every head's zero row 3) of the limb block
-    for (int i = tid; i < 4 * MT * 4 * (kHeadDim / 16); i += 64 * NW) {
-      const int row = i >> 3;
-      if ((row >> 2) >= GQ || (row & 3) == 3) *reinterpret_cast<uint4*>(q_s + row * kQRow + 16 * (i & 7)) = uint4{0, 0, 0, 0};
-    }
     __syncthreads();
     uint32_t klv = 0u;
     if constexpr (CB) klv = codebook[2 * kv];
-    QueryScal* qs_s = reinterpret_cast<QueryScal*>(wm_s);
     for (int g = wave; g < GQ; g += NW) {
-      double x0 = 0.0, x1 = 0.0;
+      float x0 = 0.f, x1 = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) {
-        x0 += qpart[w2][g][lane][0];
-        x1 += qpart[w2][g][lane][1];
+        const float2 v = qpart[w2][g][lane];
+        x0 += v.x;
+        x1 += v.y;
       }
-      const float amax = wave_max_f32(static_cast<float>(fmax(fabs(x0), fabs(x1))));
-      const double sm = wave_sum_f64(x0 + x1);
+      const float amax = wave_max_f32(fmaxf(fabsf(x0), fabsf(x1)));
+      const float sm = wave_sum_f32(x0 + x1);
       int k = 0;
       if (amax > 0.f) frexpf(amax, &k);  // amax < 2^k
       int sh = 21 - k;
       if (klv != 0u) {
-        const double l1 = wave_sum_f64(fabs(x0) + fabs(x1));
+        const float l1 = wave_sum_f32(fabsf(x0) + fabsf(x1));
         int kl = 0;
-        if (l1 > 0.0) frexp(l1, &kl);
+        if (l1 > 0.f) frexpf(l1, &kl);
         sh = min(sh, 26 - kl);
       }
-      const int Q0 = static_cast<int>(rint(x0 * pow2d(sh)));
-      const int Q1 = static_cast<int>(rint(x1 * pow2d(sh)));
+      // x 2^sh is exact (a power of two); |Q| <= 2^21
+      const int Q0 = static_cast<int>(rintf(x0 * pow2f(sh)));
+      const int Q1 = static_cast<int>(rintf(x1 * pow2f(sh)));
       auto limbs = [](int Q, int& l0, int& l1, int& l2) {
         l0 = static_cast<signed char>(Q & 0xFF);
         const int r1 = (Q - l0) >> 8;
@@ -510,7 +524,7 @@ __device__ __forceinline__ void int2_split(
       for (int r = 0; r < 3; ++r)
         *reinterpret_cast<uint16_t*>(q_s + (4 * g + r) * kQRow + 2 * lane) =
             static_cast<uint16_t>((la[r] & 0xFF) | ((lc[r] & 0xFF) << 8));
-      // exact integer sum of Q over the 128 dims (|Q| < 2^21): row butterflies, then the rows
+      // exact integer sum of Q over the 128 dims (|Q| <= 2^21): row butterflies, then the rows
       int sq = Q0 + Q1;
       sq += __builtin_amdgcn_update_dpp(0, sq, kDppQuadXor1, 0xF, 0xF, false);
       sq += __builtin_amdgcn_update_dpp(0, sq, kDppQuadXor2, 0xF, 0xF, false);
@@ -519,11 +533,13 @@ __device__ __forceinline__ void int2_split(
       sq = (__builtin_amdgcn_readlane(sq, 0) + __builtin_amdgcn_readlane(sq, 16)) +
            (__builtin_amdgcn_readlane(sq, 32) + __builtin_amdgcn_readlane(sq, 48));
       if (lane == 0) {
-        QueryScal o;
-        o.qsc = static_cast<float>(pow2d(-sh) * iq.scale_log2 * (klv != 0u ? 0.0625 : 1.0));
-        o.sig = static_cast<float>(sm * iq.scale_log2);
-        o.kcent = klv != 0u ? 0 : -2 * sq;
-        qs_s[g] = o;
+        // (qsc, sig, kcent) as the separate query preparation's QueryScal holds them
+        uint4 o;
+        o.x = __float_as_uint(static_cast<float>(pow2d(-sh) * iq.scale_log2 * (klv != 0u ? 0.0625 : 1.0)));
+        o.y = __float_as_uint(static_cast<float>(static_cast<double>(sm) * iq.scale_log2));
+        o.z = static_cast<uint32_t>(klv != 0u ? 0 : -2 * sq);
+        o.w = 0u;
+        *reinterpret_cast<uint4*>(q_s + 4 * g * kQRow + kHeadDim) = o;
       }
     }
     __syncthreads();
@@ -531,10 +547,10 @@ __device__ __forceinline__ void int2_split(
     for (int mt = 0; mt < MT; ++mt) {
       const int g = 4 * mt + G;
       if (head_ok[mt]) {
-        const QueryScal o = qs_s[g];
-        kcent[mt] = o.kcent;
-        qsc[mt] = o.qsc;
-        sig[mt] = o.sig;
+        const uint4 o = *reinterpret_cast<const uint4*>(q_s + 4 * g * kQRow + kHeadDim);
+        qsc[mt] = __uint_as_float(o.x);
+        sig[mt] = __uint_as_float(o.y);
+        kcent[mt] = static_cast<int>(o.z);
       }
     }
   }
@@ -742,7 +758,9 @@ __device__ __forceinline__ void int2_split(
   // an L2 hit), so no path without it joins between the loads and the use of a page.
   auto ntok_of = [&](int j) { return min(kPageTokens, nh - (p0 + NW * j) * kPageTokens); };
   auto next_of = [&](int j) { return page_of(j < n_mine ? j : n_mine - 1); };
-  __syncthreads();  // query limbs in LDS
+  // query limbs in LDS (the inline preparation's last barrier already covers them; the
+  // page loop's set-up above writes only wave-private LDS)
+  if (!inline_q) __syncthreads();
   // Whole triples of pages in a loop with one exit, then the last one or two: with a
   // single back edge the compiler's wait for a page covers only that page, and the
   // next one keeps loading.
@@ -759,6 +777,11 @@ __device__ __forceinline__ void int2_split(
     process(buf[0], ntok_of(i));
     if (i + 1 < n_mine) process(buf[1], ntok_of(i + 1));
   }
+
+  // R_V fragments of the un-rotation, requested now: they arrive while the waves' partials
+  // are joined
+  uint4 rb[8 / NW][4];
+  if constexpr (kUnrot) merge::load_rv<NW>(rot_v, kv, rb);
 
   // ---- wave partials: lane (G, n) holds head 4mt + G, dims 16dt + n
   float accf[MT][8], lf[MT], zf[MT];
@@ -786,6 +809,43 @@ __device__ __forceinline__ void int2_split(
   }
   __syncthreads();
 
+  if constexpr (kUnrot) {
+    // join the waves per (head, dim pair) into packed bf16 high / low A rows (the page
+    // loop's LDS is free now), then un-rotate on the matrix cores and write
+    static_assert(2 * 16 * merge::kARow * 4 <= kLoopBytes, "the A rows fit the loop's LDS");
+    uint32_t* ahi_s = reinterpret_cast<uint32_t*>(scratch_s);
+    uint32_t* alo_s = ahi_s + 16 * merge::kARow;
+    for (int idx = tid; idx < GQ * (kHeadDim / 2); idx += 64 * NW) {
+      const int g = idx / (kHeadDim / 2);
+      const int dd = 2 * (idx % (kHeadDim / 2));
+      float big = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) big = fmaxf(big, wm_s[w][g]);
+      float l = 0.f, a0 = 0.f, a1 = 0.f;
+      if (big != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float sc = wm_s[w][g] == -INFINITY ? 0.f : exp2f(wm_s[w][g] - big);
+          l = fmaf(sc, wl_s[w][g], l);
+          const float2 v = *reinterpret_cast<const float2*>(&wacc_s[w][g][dd]);
+          a0 = fmaf(sc, v.x, a0);
+          a1 = fmaf(sc, v.y, a1);
+        }
+      }
+      merge::split2(a0, a1, ahi_s[g * merge::kARow + dd / 2], alo_s[g * merge::kARow + dd / 2]);
+      if (dd == 0) {
+        const size_t o = (static_cast<size_t>(b) * n_q + h0 + g) * pstride + split;
+        store_partial<kCoherent>(out_m + o, big);
+        store_partial<kCoherent>(out_l + o, l);
+      }
+    }
+    __syncthreads();
+    merge::unrotate_tiles<NW>(ahi_s, alo_s, GQ, rb, [&](int g, int d, float v) {
+      const size_t o = (static_cast<size_t>(b) * n_q + h0 + g) * pstride + split;
+      store_partial<kCoherent>(out_acc + o * kHeadDim + d, v);
+    });
+    return;
+  }
   for (int idx = tid; idx < GQ * kHeadDim; idx += 64 * NW) {
     const int g = idx >> 7;
     const int dd = idx & 127;

@@ -117,11 +117,10 @@ hipError_t launch_attend(StepArgs a, hipStream_t stream);
 
 // The decode step in one launch: window items, appended-token items (each request's
 // appended token demoted, its term written as INT2 partial column n_splits), then INT2
-// splits with the query prepared inline; the last arrival per (request, KV head) merges. `hist` views n_splits + append columns; the counters must be zero at the start
-// and are left at zero.
+// splits with the query prepared inline; the last arrival per (request, KV head) merges.
+// `hist` views n_splits + append columns; the counters must be zero at the start and are
+// left at zero. hipErrorInvalidValue if the grid does not fit step_append_one_launch.
 hipError_t launch_step_append(StepArgs a, hipStream_t stream);
-// waves per workgroup of launch_step_append's grid
-int step_append_waves(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits);
 // whether the one-launch grid runs in a single dispatch round of 8-wave workgroups (else the
 // step is better run as prepare + attend)
 bool step_append_one_launch(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits);

@@ -133,12 +133,56 @@ __device__ __forceinline__ void load_rv(const uint16_t* __restrict__ rot_v, int 
                                                    8 * (lane >> 4));
 }
 
+// Un-rotation on the matrix cores of up to 16 vectors x (rotated basis, 128 dims each),
+// held in LDS as packed bf16 pairs: x = hi + lo (split2), rows of kARow words; rows at or
+// past `rows` are not read (zero). Gives x R_V^T for this wave's output tiles: put(row,
+// dim, value) for every row < rows and the 16 NTW dims of the wave's tiles. [16 rows] x
+// [128] x [16 dims] per tile in bf16 with fp32 accumulation (two products); R_V itself is
+// bf16 and exact. rb from load_rv<NW>.
+template <int NW, typename Put>
+__device__ __forceinline__ void unrotate_tiles(const uint32_t* ahi_s, const uint32_t* alo_s, int rows,
+                                               const uint4 (&rb)[8 / NW][4], Put put) {
+  constexpr int NTW = 8 / NW;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // A fragment: row = lane % 16, k = 32 ks + 8 (lane / 16) .. + 7
+  uint4 ahi[4], alo[4];
+  {
+    const int g = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int w0 = g * kARow + 16 * ks + 4 * (lane >> 4);
+      ahi[ks] = g < rows ? *reinterpret_cast<const uint4*>(ahi_s + w0) : make_uint4(0, 0, 0, 0);
+      alo[ks] = g < rows ? *reinterpret_cast<const uint4*>(alo_s + w0) : make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 bk = __builtin_bit_cast(bf16x8, rb[nt][ks]);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi[ks]), bk, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo[ks]), bk, c, 0, 0, 0);
+    }
+    // C fragment: rows 4 (lane / 16) + j, column dim 16 tile + lane % 16
+    const int d = 16 * (NTW * wave + nt) + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = 4 * (lane >> 4) + j;
+      if (g < rows) put(g, d, c[j]);
+    }
+  }
+}
+
 // Merge of the GQT query heads of KV head kv of request b: `ns` INT2 partials per head
 // (rotated V basis, written by this launch with agent-scope stores) and `nw` window
 // partials per head into out[b][h][128]. 64 NW threads; 1 <= ns <= kMaxSplits,
 // nw <= kMaxWin; rb from load_rv<NW>. kWinAgent: the window partials were written by this
 // launch with agent-scope stores (else by an earlier launch) and are read at agent scope.
-template <int GQT, int NW, bool kWinAgent = false>
+// kRot: the INT2 partials are in the rotated basis of R_V (else they were un-rotated when
+// written, and the merge is a weighted sum in one basis; rb is then not read).
+template <int GQT, int NW, bool kWinAgent = false, bool kRot = true>
 __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, int b, int kv, int n_q,
                                             const PartialsView& hist, int ns, const PartialsView& win, int nw,
                                             const uint4 (&rb)[8 / NW][4], float* __restrict__ out, int nqt = 1) {
@@ -290,42 +334,24 @@ __device__ __forceinline__ void merge_group(unsigned char* __restrict__ smem, in
         y.x += ys.x;
         y.y += ys.y;
       }
-      split2(x.x, x.y, ahi_s[g * kARow + d / 2], alo_s[g * kARow + d / 2]);
-      if (SL > 1) *reinterpret_cast<float2*>(accw_s + g * SL * kRow + d) = y;
+      if constexpr (kRot) {
+        split2(x.x, x.y, ahi_s[g * kARow + d / 2], alo_s[g * kARow + d / 2]);
+        if (SL > 1) *reinterpret_cast<float2*>(accw_s + g * SL * kRow + d) = y;
+      } else {
+        float* o = out + query_row(b, kv * GQT + p0 + g, n_q, GQT, nqt) * kHeadDim + d;
+        o[0] = (x.x + y.x) * inv_s[g];
+        o[1] = (x.y + y.y) * inv_s[g];
+      }
+    }
+    if constexpr (!kRot) {
+      if (p0 + HP < GQT) __syncthreads();  // the next pass reuses the LDS
+      continue;
     }
     __syncthreads();
 
-    // un-rotation on the matrix cores. A fragment: row = head lane % 16 (rows >= HP are
-    // zero), k = 32 ks + 8 (lane / 16) .. + 7
-    uint4 ahi[4], alo[4];
-    {
-      const int g = lane & 15;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int w0 = g * kARow + 16 * ks + 4 * (lane >> 4);
-        ahi[ks] = g < HP ? *reinterpret_cast<const uint4*>(ahi_s + w0) : make_uint4(0, 0, 0, 0);
-        alo[ks] = g < HP ? *reinterpret_cast<const uint4*>(alo_s + w0) : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 bk = __builtin_bit_cast(bf16x8, rb[nt][ks]);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ahi[ks]), bk, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, alo[ks]), bk, c, 0, 0, 0);
-      }
-      // C fragment: rows (heads) 4 (lane / 16) + j, column dim 16 tile + lane % 16
-      const int d = 16 * (NTW * wave + nt) + (lane & 15);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int g = 4 * (lane >> 4) + j;
-        if (g < HP)
-          out[query_row(b, kv * GQT + p0 + g, n_q, GQT, nqt) * kHeadDim + d] =
-              (c[j] + accw_s[g * SL * kRow + d]) * inv_s[g];
-      }
-    }
+    unrotate_tiles<NW>(ahi_s, alo_s, HP, rb, [&](int g, int d, float c) {
+      out[query_row(b, kv * GQT + p0 + g, n_q, GQT, nqt) * kHeadDim + d] = (c + accw_s[g * SL * kRow + d]) * inv_s[g];
+    });
     if (p0 + HP < GQT) __syncthreads();  // the next pass reuses the LDS
   }
 }

@@ -13,10 +13,12 @@
 //   per-KV-head arrival counters.
 // Launch 2 (main), grid (history split, KV head x head group, request): the INT2 pass of
 // the split, then a ticket: every workgroup writes its partial with agent-scope stores,
-// waits for them to complete and adds one to its (request, KV head) counter; the workgroup that draws the last ticket merges
-// all INT2 and window partials of that KV head's query heads, un-rotates and writes the
-// output, after re-arming the counter (so the main launch may be repeated on its own). No
-// workgroup ever waits for another.
+// waits for them to complete and adds one to its (request, KV head) counter; the workgroup
+// that draws the last ticket merges all INT2 and window partials of that KV head's query
+// heads and writes the output, after re-arming the counter (so the main launch may be
+// repeated on its own). The INT2 value sums are un-rotated (times R_V^T) by each split
+// before it writes them when the grid has one 8-wave workgroup per compute unit at most,
+// else by the merge. No workgroup ever waits for another.
 
 #include "demote_pass.h"
 #include "int2_pass.h"
@@ -82,9 +84,14 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // the INT2 pass and the merge use the same LDS one after the other
   __shared__ __align__(16) unsigned char smem[cmax(int2::int2_smem_bytes<GQ, NW>(), merge::smem_bytes<GQT, NW>())];
   __shared__ int ticket_s;
-  int2::int2_split<GQ, true, NW, CB>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table, a.max_pages,
-                                     a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits, a.hist.qlimb, a.hist.qscal,
-                                     a.hist.m, a.hist.l, a.hist.acc, a.codebook);
+  // 8-wave workgroups (a grid of at most one per compute unit) un-rotate their own value
+  // sums, so the merge after the last ticket is a weighted sum; 4-wave ones, several to a
+  // compute unit, leave that to the merge and keep the R_V fragments out of the page loop
+  constexpr bool kUnrot = NW == 8;
+  int2::int2_split<GQ, true, NW, CB, kUnrot>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table,
+                                             a.max_pages, a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits,
+                                             a.hist.qlimb, a.hist.qscal, a.hist.m, a.hist.l, a.hist.acc, a.codebook,
+                                             int2::InlineQuery(), a.rot_v);
   const int kv = blockIdx.y / a.n_groups;
   const int b = blockIdx.z;
   // the partials went out as agent-scope stores: once each thread's stores have completed
@@ -98,11 +105,12 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // last arrival for (b, kv): every workgroup of the group has drawn its ticket, so re-arm the
   // counter for the next launch; the group's partials are read with agent-scope loads
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // R_V fragments of the un-rotation: requested first, they travel with the partials' loads
-  // (one round trip), and only the merging workgroup reads R_V
+  // R_V fragments of the un-rotation (when the splits left it to the merge): requested
+  // first, they travel with the partials' loads (one round trip)
   uint4 rb[8 / NW][4];
-  merge::load_rv<NW>(a.rot_v, kv, rb);
-  merge::merge_group<GQT, NW>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, rb, a.out, a.nqt);
+  if constexpr (!kUnrot) merge::load_rv<NW>(a.rot_v, kv, rb);
+  merge::merge_group<GQT, NW, false, !kUnrot>(smem, b, kv, a.n_q, a.hist, a.n_splits, a.win, a.n_wsplits, rb, a.out,
+                                               a.nqt);
 }
 
 // A small window pass (fewer than 256 workgroups) spreads each KV head's query heads over up
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
     id -= n_win;
     kv = id % a.n_kv;
     b = id / a.n_kv;
-    demote::append_token<NW, GQT>(smem, b, kv, a, a.n_splits, pstride);
+    demote::append_token<NW, GQT, true>(smem, b, kv, a, a.n_splits, pstride);
   } else {
     id -= n_win + n_app;
     const int split = id % a.n_splits;
@@ -177,9 +185,9 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
     iq.scale_log2 = a.scale_log2;
     iq.n_excl = a.append;
     iq.pstride = pstride;
-    int2::int2_split<GQ, true, NW, CB>(smem, split, gy, b, a.pool, a.block_table, a.max_pages, a.hist_len, a.n_q,
-                                       a.n_kv, a.n_groups, a.n_splits, nullptr, nullptr, a.hist.m, a.hist.l,
-                                       a.hist.acc, a.codebook, iq);
+    int2::int2_split<GQ, true, NW, CB, true>(smem, split, gy, b, a.pool, a.block_table, a.max_pages, a.hist_len,
+                                             a.n_q, a.n_kv, a.n_groups, a.n_splits, nullptr, nullptr, a.hist.m,
+                                             a.hist.l, a.hist.acc, a.codebook, iq, a.rot_v);
   }
   // the partials went out as agent-scope stores: once each thread's stores have completed
   // and the barrier has passed, the ticket below is drawn after all of them
@@ -190,14 +198,13 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
   __syncthreads();
   if (ticket_s != a.n_splits * a.n_groups + a.n_wsplits + a.append - 1) return;
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every partial is in the window's basis (the INT2 splits and the appended token
+  // un-rotated theirs): the merge is a weighted sum
   uint4 rb[8 / NW][4];
-  merge::load_rv<NW>(a.rot_v, kv, rb);
-  merge::merge_group<GQT, NW, true>(smem, b, kv, a.n_q, a.hist, pstride, a.win, a.n_wsplits, rb, a.out, 1);
+  merge::merge_group<GQT, NW, true, false>(smem, b, kv, a.n_q, a.hist, pstride, a.win, a.n_wsplits, rb, a.out, 1);
 }
 
 constexpr int kStepSlots8 = 256;  // 8-wave workgroups resident at once (one per compute unit)
-
-int append_waves(long long items) { return items <= kStepSlots8 ? 8 : 4; }
 
 }  // namespace
 
@@ -208,14 +215,14 @@ bool step_append_one_launch(int batch, int n_kv, int n_groups, int n_splits, int
 
 namespace {
 
+// one 8-wave workgroup per item; the grid must fit one dispatch round (the caller checks
+// step_append_one_launch)
 template <int GQ, int GQT, bool CB>
 hipError_t launch_append_cb(const StepArgs& a, hipStream_t stream) {
   const long long items = static_cast<long long>(a.n_wsplits + a.append) * a.n_kv * a.batch +
                           static_cast<long long>(a.n_splits) * a.n_kv * a.n_groups * a.batch;
-  if (append_waves(items) == 8)
-    hipLaunchKernelGGL((append_kernel<GQ, GQT, 8, CB>), dim3(static_cast<unsigned>(items)), dim3(512), 0, stream, a);
-  else
-    hipLaunchKernelGGL((append_kernel<GQ, GQT, 4, CB>), dim3(static_cast<unsigned>(items)), dim3(256), 0, stream, a);
+  if (items > kStepSlots8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((append_kernel<GQ, GQT, 8, CB>), dim3(static_cast<unsigned>(items)), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -251,11 +258,6 @@ hipError_t launch_attend(StepArgs a, hipStream_t stream) {
 }  // namespace oscar
 
 namespace oscar {
-
-int step_append_waves(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits) {
-  return append_waves(static_cast<long long>(n_wsplits + 1) * n_kv * batch +
-                      static_cast<long long>(n_splits) * n_kv * n_groups * batch);
-}
 
 hipError_t launch_step_append(StepArgs a, hipStream_t stream) {
   switch (a.gq) {
