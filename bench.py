@@ -1,25 +1,26 @@
-"""Benchmark: one OSCAR decode step (demote the oldest recent token of each request into
-INT2 history, BF16 sink/recent pass, INT2 history pass, merge and un-rotation) on one
-MI355X, through oscar_decode_step (two launches: prepare, attend).
+"""Benchmark: the OSCAR decode step (each request's oldest recent token demoted into its INT2
+history, the BF16 sink/recent pass, the INT2 history pass, the merge and the un-rotation) on
+one MI355X, through oscar_decode_step_append: one launch when its workgroups fit the chip at
+once (batch 1 at 32K and 100K tokens), else prepare + attend.
 
-Workload (default): a Qwen3-8B-shaped attention layer, batch 1, 32,768 tokens of context
-(64 BF16 sink / 32,448 INT2 history / 256 BF16 recent), 32 query heads over 8 KV heads,
-head_dim 128, 64-token pages, seeded synthetic N(0,1) data with per-head outlier channels.
-Steps cycle over `--layers` distinct layer instances (separate pools, windows and
-rotations) so every step reads its KV pool from HBM, not from the 256 MB last-level cache,
-as a real model's per-layer decode does; like a model's layers, the instances share one
-block table and one set of history and window lengths.
+Workloads (rows, in this order by default): a Qwen3-8B-shaped layer at 32,768 tokens, batch
+1 (the headline: `value`); the same layer at 100,000 tokens over randomly permuted pages; a
+Qwen3-32B-shaped layer (64 query heads) at 131,072 tokens, batch 4; and batch 64 at 8K-16K
+tokens sharing a 4,096-token prefix. All: 64 BF16 sink tokens, 256 BF16 recent tokens,
+head_dim 128, 64-token pages, seeded synthetic N(0,1) data with per-head outlier channels,
+rotations built by the library from synthetic calibration data. Steps cycle over layer
+instances (separate pools, windows and rotations, sharing one block table) so every step
+reads its KV pool from HBM, not from the 256 MB last-level cache.
 
-Prints one JSON line. `value` is the whole step's algorithmic HBM bytes divided by its
-time (GB/s); `roofline` reports the dominant kernel (the attend launch: INT2 history pass
-and merge) against the 8 TB/s HBM peak, timed with events on its stream over back-to-back
-oscar_attend launches; `multi_query` times oscar_decode_multi (T query tokens per request
-over the same pools, as in speculative verification) the same way; `codebook` times the
-Lloyd-Max codebook variant (the same history demoted against per-head codebooks fitted on
-the calibration set, then oscar_decode_step_codebook and oscar_attend_codebook) the same
-way; `calibration` times the GPU calibration covariances; `bf16_baseline` times plain BF16
-decode over the same context held uncompressed; `cpu_baseline` is the CPU oracle timed on a
-bounded sample of the same workload.
+Prints one JSON line. `value` is the headline step's algorithmic HBM bytes divided by its
+time (GB/s). Each row (`rows`) has its step time and rate; `roofline` (the dominant kernel:
+the one-launch step's kernel, or the attend launch of a two-launch step) against the 8 TB/s
+HBM peak, timed with events on the launch stream, with `traffic` the HBM bytes per launch
+from the committed counter summary under profiles/ while the kernel sources are unchanged;
+and `cpu_baseline`, the CPU oracle timed on a bounded sample of the same workload. The
+headline row also carries `multi_query` (oscar_decode_multi), `codebook` (the Lloyd-Max
+codebook variant), `grouped` (groups of 64 and 32 dims), `calibration` and `bf16_baseline`
+(plain BF16 decode of the same context); the 128K row carries `bulk_demote`.
 """
 
 from __future__ import annotations
@@ -45,7 +46,10 @@ WIN_BYTES = 512          # per BF16 window token per KV head (K + V)
 ROT_BYTES = 128 * 128 * 2
 COPY_BYTES = 256 * 2 ** 20  # the plain copy whose counter readings calibrate FETCH_SIZE / WRITE_SIZE
 CSRC = os.path.join(ROOT, "bit_kv_cache_oscar_amd", "csrc")
-ATTEND_SOURCES = ("step.hip", "int2_pass.h", "merge_pass.h", "device_common.h", "launch.h")
+# the sources of the timed step kernels: a change to any of them retires the counter summaries
+STEP_SOURCES = ("step.hip", "int2_pass.h", "merge_pass.h", "window_pass.h", "demote_pass.h", "device_common.h",
+                "launch.h")
+CONFIGS = (2, 3, 5, 4)  # headline first
 
 
 def parse():
@@ -53,16 +57,30 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", type=int, default=2, help="workload config (2: 32K, 3: 100K, 4: B=64, 5: 128K B=4)")
+    p.add_argument("--configs", default=",".join(str(c) for c in CONFIGS),
+                   help="workload configs, headline first (2: 32K, 3: 100K, 5: 128K B=4, 4: B=64)")
+    p.add_argument("--config", type=int, default=0, help="one workload config only (overrides --configs)")
     p.add_argument("--layers", type=int, default=0, help="layer instances to cycle (0: enough for 512 MB)")
     p.add_argument("--splits", type=int, default=0, help="INT2 splits (0: library default)")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0 disables)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget per row (0 disables)")
+    p.add_argument("--extras", choices=("headline", "all", "none"), default="headline",
+                   help="rows beyond the step (multi-query, codebook, grouped, calibration, BF16 baseline)")
     return p.parse_args()
 
 
-def step_bytes(w):
-    """Algorithmic bytes of one step: what the method must move, nothing of our workspace."""
-    hist = int(sum(w.hist_lens)) * w.n_kv_heads * HIST_BYTES
+def hist_tokens(w, unique):
+    """History tokens the step reads: every request's own (logical), or with the shared
+    prefix pages counted once (unique: what HBM must deliver at the least)."""
+    n = int(sum(w.hist_lens))
+    if unique and w.shared_pages:
+        n -= (w.batch - 1) * w.shared_pages * 64
+    return n
+
+
+def step_bytes(w, unique=True):
+    """Algorithmic bytes of one step: what the method must move, nothing of our workspace.
+    Returns (step, attend launch) bytes."""
+    hist = hist_tokens(w, unique) * w.n_kv_heads * HIST_BYTES
     win = int(sum(w.win_lens)) * w.n_kv_heads * WIN_BYTES
     rot = 2 * w.n_kv_heads * ROT_BYTES
     qo = w.batch * w.n_q_heads * 128 * (2 + 4)
@@ -72,22 +90,22 @@ def step_bytes(w):
     return hist + win + rot + qo + demote, attend
 
 
-def attend_source_hash():
+def step_source_hash():
     import hashlib
 
     h = hashlib.sha256()
-    for f in ATTEND_SOURCES:
+    for f in STEP_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload, kernel="attend"):
-    """HBM bytes per launch of the attend kernel (kernel="attend_codebook": its codebook
-    variant) from the committed counter summary of this workload, or None when there is none
-    or the kernel source changed since it was taken. FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch) are each scaled by what the same counter reads for a plain copy of COPY_BYTES
-    bytes in the same run."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` ("step": the one-launch step kernel, "attend": the
+    attend launch, "attend_codebook": its codebook variant) from the committed counter summary
+    of this workload, or None when there is none or the kernel sources changed since it was
+    taken. FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same
+    counter reads for a plain copy of COPY_BYTES bytes in the same run."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -97,7 +115,7 @@ def measured_traffic(workload, kernel="attend"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        if kv.get("kernel_source_sha256") != attend_source_hash():
+        if kv.get("kernel_source_sha256") != step_source_hash():
             return None
         f = float(kv["fetch_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_fetch_kib"])
         wr = float(kv["write_kib_per_dispatch"]) * COPY_BYTES / float(kv["copy_write_kib"])
@@ -175,14 +193,20 @@ def cpu_baseline(w, budget_s):
             break
     per_rep_bytes = (w.hist_len(b) * HIST_BYTES + w.win_len(b) * WIN_BYTES + 2 * ROT_BYTES
                      + w.gq * 128 * 6 + 2 * 256 + HIST_BYTES)
+    rate = per_rep_bytes * reps / el
+    total, _ = step_bytes(w)
     return {
-        "value": round(per_rep_bytes * reps / el / 1e9, 6),
+        "value": round(rate / 1e9, 6),
         "unit": "GB/s",
         "cores": blas_threads(),
         "kind": "oracle",
         "sample": f"request 0, KV head 0 of {w.n_kv_heads} ({w.gq} query heads) over the full "
                   f"{w.ctx_lens[0]}-token context: demote one token + decode, {reps} repetitions in {el:.1f} s "
-                  f"(oracle pool built beforehand, untimed)",
+                  f"(oracle pool built beforehand, untimed); one repetition is "
+                  f"{per_rep_bytes / total:.4f} of the step's bytes, and the whole step at this rate is the "
+                  f"scaled figure",
+        "sample_fraction_of_step": round(per_rep_bytes / total, 6),
+        "us_per_step_scaled": round(total / rate * 1e6, 1),
     }
 
 
@@ -242,48 +266,46 @@ def bulk_demote(w, rk_bits, rv_bits, dev, stream, reps, codebook=None):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this path has no multi-GPU mode (the pool shards by KV head "
-              "or request with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
+
+class Setup:
+    """One workload on the device: layer instances with filled pools, the step's inputs."""
+
+
+def setup(cfg, args, dev, fill_rows_needed):
     import torch
 
     import synth
-    from bit_kv_cache_oscar_amd import (oscar_attend, oscar_decode_multi, oscar_decode_workspace_bytes,
-                                        oscar_default_splits)
+    from bit_kv_cache_oscar_amd import oscar_decode_step_append_splits, oscar_default_splits
     from bit_kv_cache_oscar_amd.layer import LayerCache
     from bit_kv_cache_oscar_amd.rotation import layer_rotations_from_calibration, layer_rotations_from_gram
 
-    assert torch.cuda.is_available(), "bench.py needs a HIP device"
-    dev = torch.device("cuda:0")
-    w = synth.workload(args.config)
+    S = Setup()
+    S.w = w = synth.workload(cfg)
     table, n_phys = synth.block_table(w)
-    total_bytes, attend_bytes = step_bytes(w)
-    layers = args.layers or max(2, -(-512 * 2 ** 20 // max(total_bytes, 1)))
-
+    S.total_bytes, S.attend_bytes = step_bytes(w)
+    S.logical_bytes, _ = step_bytes(w, unique=False)
+    S.layers = args.layers or max(2, -(-512 * 2 ** 20 // max(S.logical_bytes, 1)))
     # rotations: the library's host builder from the synthetic calibration data
     if w.calib == "gram":
-        rk_bits, rv_bits = layer_rotations_from_gram([synth.gram_matrix_source(w, kv) for kv in range(w.n_kv_heads)])
+        S.rk_bits, S.rv_bits = layer_rotations_from_gram([synth.gram_matrix_source(w, kv) for kv in range(w.n_kv_heads)])
     else:
-        rk_bits, rv_bits = layer_rotations_from_calibration(
+        S.rk_bits, S.rv_bits = layer_rotations_from_calibration(
             [synth.calibration_set(w, kv) for kv in range(w.n_kv_heads)], w.sm_scale)
-
     base = LayerCache(w.n_q_heads, w.n_kv_heads, w.batch, table.shape[1], n_phys, device=dev)
-    clip = np.full(w.n_kv_heads, w.clip_ratio, np.float32)
-    base.set_rotations(rk_bits, rv_bits, clip, clip)
+    S.clip = np.full(w.n_kv_heads, w.clip_ratio, np.float32)
+    base.set_rotations(S.rk_bits, S.rv_bits, S.clip, S.clip)
     base.set_block_table(table)
     base.set_hist_len(w.hist_lens)
     base.set_win_len(w.win_lens)
     # fill: every history token but the last goes in by bulk demotion; the last one is the
     # token each timed step demotes from the recent window
-    step_k = torch.zeros((w.batch, w.n_kv_heads, 128), dtype=torch.bfloat16, device=dev)
-    step_v = torch.zeros_like(step_k)
-    step_page = torch.zeros(w.batch, dtype=torch.int32, device=dev)
-    step_slot = torch.zeros(w.batch, dtype=torch.int32, device=dev)
-    fill_rows = []  # per request: the rows demoted by the fill, kept on the device for the codebook row
+    S.step_k = torch.zeros((w.batch, w.n_kv_heads, 128), dtype=torch.bfloat16, device=dev)
+    S.step_v = torch.zeros_like(S.step_k)
+    S.step_page = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    S.step_slot = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    S.fill_rows = []  # per request: the rows demoted by the fill (kept for the extra rows)
     for b in range(w.batch):
         n = w.hist_len(b)
         start = min(n, w.shared_pages * 64) if (w.shared_pages and b > 0) else 0
@@ -301,38 +323,159 @@ def main():
         sl = torch.from_numpy((j % 64).astype(np.int32)).to(dev)
         if n - start > 1:
             base.demote(kk[:-1], vv[:-1], pg[:-1], sl[:-1])
-            fill_rows.append((kk[:-1], vv[:-1], pg[:-1], sl[:-1]))
-        step_k[b], step_v[b] = kk[-1], vv[-1]
-        step_page[b], step_slot[b] = pg[-1], sl[-1]
-    q = torch.from_numpy(np.stack([synth.query(w, b) for b in range(w.batch)])).to(dev).to(torch.bfloat16)
-    splits = args.splits or oscar_default_splits(base.desc, w.batch, int(w.hist_lens.max()))
-    base.set_splits(splits)
-    insts = [base]
-    for _ in range(layers - 1):
+            if fill_rows_needed:
+                S.fill_rows.append((kk[:-1], vv[:-1], pg[:-1], sl[:-1]))
+        S.step_k[b], S.step_v[b] = kk[-1], vv[-1]
+        S.step_page[b], S.step_slot[b] = pg[-1], sl[-1]
+    S.q = torch.from_numpy(np.stack([synth.query(w, b) for b in range(w.batch)])).to(dev).to(torch.bfloat16)
+    # split counts: the two-launch default (attend launch), and the one-launch step's
+    S.splits = args.splits or oscar_default_splits(base.desc, w.batch, int(w.hist_lens.max()))
+    S.splits1 = args.splits or oscar_decode_step_append_splits(base.desc, w.batch, int(w.hist_lens.max()))
+    base.set_splits(S.splits)
+    S.insts = [base]
+    for _ in range(S.layers - 1):
         c = LayerCache(w.n_q_heads, w.n_kv_heads, w.batch, table.shape[1], n_phys, device=dev)
         for name in ("pool", "k_win", "v_win", "rot_k", "rot_v", "clip_k", "clip_v"):
             getattr(c, name).copy_(getattr(base, name))
         # one request's page table and lengths serve every layer of a model
         c.block_table, c.hist_len, c.win_len = base.block_table, base.hist_len, base.win_len
-        c.set_splits(splits)
-        insts.append(c)
+        c.set_splits(S.splits)
+        S.insts.append(c)
+    S.base = base
     torch.cuda.synchronize()
+    return S
 
-    # one plain copy of known size (untimed): its FETCH_SIZE / WRITE_SIZE readings calibrate
-    # the counters of the kernels in the same profiled run
-    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
 
-    stream = torch.cuda.current_stream()
+def make_timer(S, stream, torch):
+    def timed(fn, k):
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(k):
+            fn(S.insts[i % S.layers])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / k
 
-    def attend(c):
-        oscar_attend(c.desc, c.rot_v, c.pool, c.block_table, c.hist_len, c.n_splits, c.workspace, c.out, stream)
+    return timed
+
+
+def pct(v):
+    return [round(float(np.percentile(v, p)) * 1e3, 3) for p in (10, 50, 90)]
+
+
+def step_row(S, args, stream, torch):
+    """The step (oscar_decode_step_append) and its dominant kernel: times, rates, roofline."""
+    from bit_kv_cache_oscar_amd import oscar_attend, oscar_decode_step_append_launches
+
+    w = S.w
+    launches = oscar_decode_step_append_launches(S.base.desc, w.batch, S.splits1)
+    timed = make_timer(S, stream, torch)
 
     def step(c):
-        c.step(step_k, step_v, step_page, step_slot, q, w.sm_scale, stream)
+        c.n_splits = S.splits1
+        c.step_append(S.step_k, S.step_v, S.q, w.sm_scale, stream)
+
+    def step2(c):  # the two-launch step, whose workspace the attend launch reads
+        c.n_splits = S.splits
+        c.step(S.step_k, S.step_v, S.step_page, S.step_slot, S.q, w.sm_scale, stream)
+
+    def attend(c):
+        oscar_attend(c.desc, c.rot_v, c.pool, c.block_table, c.hist_len, S.splits, c.workspace, c.out, stream)
+
+    for c in S.insts:  # every instance's workspaces allocated and prepared before any timing
+        step2(c)
+        step(c)
+    for i in range(args.warmup):
+        step(S.insts[i % S.layers])
+    torch.cuda.synchronize()
+    # timed region 1: whole steps back to back over the layer instances, then five more
+    # regions for the spread (the reported figure stays the first region's)
+    ms = timed(step, args.steps)
+    rep_step = sorted([ms] + [timed(step, args.steps) for _ in range(5)])
+    S.step_ms = ms
+    row = {
+        "workload": w.name,
+        "entry": "oscar_decode_step_append (" + ("one launch" if launches == 1 else "prepare + attend") + ")",
+        "batch": w.batch,
+        "context_tokens": list(sorted(set(w.ctx_lens)))[:4] if len(set(w.ctx_lens)) <= 4 else
+        [int(min(w.ctx_lens)), int(max(w.ctx_lens))],
+        "q_heads": w.n_q_heads,
+        "kv_heads": w.n_kv_heads,
+        "int2_splits": S.splits1,
+        "launches": launches,
+        "layer_instances": S.layers,
+        "us_per_step": round(ms * 1e3, 3),
+        "us_per_step_p10_p50_p90": pct(rep_step),
+        "step_bytes": S.total_bytes,
+        "achieved_gbs": round(S.total_bytes / (ms * 1e-3) / 1e9, 2),
+        "pct_of_hbm_peak": round(100 * S.total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
+        "context_tokens_per_s": round(sum(w.ctx_lens) / (ms * 1e-3), 1),
+    }
+    if S.logical_bytes != S.total_bytes:
+        row["bytes_note"] = ("step_bytes counts the shared prefix pages once (what HBM must deliver); "
+                             "logical_step_bytes counts every request's own history")
+        row["logical_step_bytes"] = S.logical_bytes
+        row["logical_gbs"] = round(S.logical_bytes / (ms * 1e-3) / 1e9, 2)
+    if launches == 1:
+        # the one launch is the whole step: its kernel time is the step time measured above
+        S.dominant_ms = ms
+        roof = {
+            "kernel": "append_kernel (oscar_decode_step_append: window, appended token, INT2 history, merge)",
+            "bound": "hbm",
+            "achieved": round(S.total_bytes / (ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(S.total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name, "step"),
+            "us_per_launch": round(ms * 1e3, 3),
+            "bytes_per_launch": S.total_bytes,
+            "bytes_note": "the step's algorithmic bytes: history pages, window, R_K and R_V, query, output, "
+                          "the appended token's rows and codes",
+        }
+    else:
+        for i in range(max(2, args.warmup)):
+            step2(S.insts[i % S.layers])
+        attend_ms = timed(attend, args.steps)
+        rep_attend = sorted([attend_ms] + [timed(attend, args.steps) for _ in range(5)])
+        S.dominant_ms = attend_ms
+        roof = {
+            "kernel": "main_kernel (attend launch: INT2 history pass + merge)",
+            "bound": "hbm",
+            "achieved": round(S.attend_bytes / (attend_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(S.attend_bytes / (attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name, "attend"),
+            "us_per_launch": round(attend_ms * 1e3, 3),
+            "us_per_launch_p10_p50_p90": pct(rep_attend),
+            "bytes_per_launch": S.attend_bytes,
+            "bytes_note": "history pages (shared prefix once) + R_V + output",
+        }
+        if S.logical_bytes != S.total_bytes:
+            logical_attend = S.attend_bytes + (S.logical_bytes - S.total_bytes)
+            roof["logical_bytes_per_launch"] = logical_attend
+            roof["logical_gbs"] = round(logical_attend / (attend_ms * 1e-3) / 1e9, 2)
+    if roof["traffic"] is not None:
+        roof["traffic_gbs"] = round(roof["traffic"] / (roof["us_per_launch"] * 1e-6) / 1e9, 2)
+        roof["traffic_frac"] = round(roof["traffic_gbs"] / HBM_PEAK_GBS, 4)
+    row["roofline"] = roof
+    return row
+
+
+def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
+    """multi-query, grouped pages, codebook, calibration and BF16-baseline rows."""
+    import synth
+    from bit_kv_cache_oscar_amd import oscar_decode_multi, oscar_decode_workspace_bytes
+
+    w, base, splits, layers, q = S.w, S.base, S.splits, S.layers, S.q
+    step_k, step_v, step_page, step_slot = S.step_k, S.step_v, S.step_page, S.step_slot
+    total_bytes, attend_bytes, ms = S.total_bytes, S.attend_bytes, S.step_ms
+    rk_bits, rv_bits, clip, fill_rows = S.rk_bits, S.rv_bits, S.clip, S.fill_rows
+    insts = S.insts
+    out = {}
 
     def timed(fn, k):
         start = torch.cuda.Event(enable_timing=True)
@@ -345,43 +488,8 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / k
 
-    for c in insts:  # every instance's workspace allocated and prepared before any timing
-        step(c)
-    for i in range(args.warmup):
-        step(insts[i % layers])
-    torch.cuda.synchronize()
-    # timed region 1: whole steps back to back; timed region 2: the dominant kernel (attend)
-    # alone, launched back to back on the same stream over the same layer instances (each
-    # instance's workspace holds its prepared query and window partials from the warm-up)
-    ms = timed(step, args.steps)
-    attend_ms = timed(attend, args.steps)
-    # spread: five more timed regions of each, the same way (the reported figures stay the
-    # first region's)
-    rep_step = sorted([ms] + [timed(step, args.steps) for _ in range(5)])
-    rep_attend = sorted([attend_ms] + [timed(attend, args.steps) for _ in range(5)])
-
-    def pct(v):
-        return [round(float(np.percentile(v, p)) * 1e3, 3) for p in (10, 50, 90)]
-
-    # warm figures: the same launches repeated on one layer instance, whose pool then stays in
-    # the caches (the 256 MB last-level cache holds a 32K layer)
-    def timed_warm(fn, k):
-        fn(insts[0])
-        return timed_once(lambda: [fn(insts[0]) for _ in range(k)], stream, torch) / k
-
-    warm_step_ms = timed_warm(step, args.steps)
-    warm_attend_ms = timed_warm(attend, args.steps)
-
-    # measured stream ceiling of this box: the library's read probe over 1 GiB, best of five
-    from bit_kv_cache_oscar_amd import oscar_read_probe
-
-    probe = torch.ones(2 ** 28, dtype=torch.int32, device=dev)
-    probe_out = torch.zeros(4096, dtype=torch.int32, device=dev)
-    oscar_read_probe(probe, probe_out, stream)
-    ceil_ms = min(timed_once(lambda: oscar_read_probe(probe, probe_out, stream), stream, torch) for _ in range(5))
-    del probe, probe_out
-    ceiling_gbs = 2 ** 30 / (ceil_ms * 1e-3) / 1e9
-
+    for c in insts:
+        c.set_splits(splits)
     # timed region 3, the multi-query row: T query tokens per request over the same pools
     # (speculative verification reading the compressed prefix), oscar_decode_multi back to
     # back over the layer instances; T query heads' worth of rows per KV head, up to 16
@@ -564,20 +672,28 @@ def main():
         reps = 20
         cal_ms = timed_once(lambda: [calib() for _ in range(reps)], stream, torch) / reps
         rows = n_cal * w.n_q_heads
-        gram_flops = 2 * 2 * rows * 128 * 128             # the key and value Gram sums
-        attn_flops = 2 * 2 * w.n_q_heads * (n_cal * (n_cal + 1) // 2) * 128   # S_h V, causal
-        tflops = (gram_flops + attn_flops) / (cal_ms * 1e-3) / 1e12
+        causal = w.n_q_heads * (n_cal * (n_cal + 1) // 2)
+        # bf16 matrix-core work: the scores q k^T and the key Gram sum of q; fp32 matrix-core
+        # work: the weighted value sums S V and the value Gram sum of S V. Each is priced at
+        # its own peak: frac is the time a launch running both at peak would take, over the
+        # measured time.
+        bf16_flops = 2 * causal * 128 + 2 * rows * 128 * 128
+        fp32_flops = 2 * causal * 128 + 2 * rows * 128 * 128
+        ideal_s = bf16_flops / (BF16_PEAK_TFLOPS * 1e12) + fp32_flops / (FP32_PEAK_TFLOPS * 1e12)
         calib_row = {
             "entry": "oscar_calib_covariances (Sigma_K = sum Q^T Q, Sigma_V = sum (S V)^T (S V))",
             "tokens": n_cal,
             "us": round(cal_ms * 1e3, 3),
-            "bound": "mfma",  # bf16 scores and Gram of q, fp32 P V and Gram of S V: priced at the fp32 rate
-            "gram_flops": gram_flops,
-            "attn_flops": attn_flops,
-            "achieved": round(tflops, 3),
-            "peak": FP32_PEAK_TFLOPS,
+            "bound": "mfma",
+            "bf16_flops": bf16_flops,
+            "fp32_flops": fp32_flops,
+            "achieved_bf16_tflops": round(bf16_flops / (cal_ms * 1e-3) / 1e12, 3),
+            "achieved_fp32_tflops": round(fp32_flops / (cal_ms * 1e-3) / 1e12, 3),
+            "peak_bf16_tflops": BF16_PEAK_TFLOPS,
+            "peak_fp32_tflops": FP32_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(tflops / FP32_PEAK_TFLOPS, 4),
+            "frac": round(ideal_s / (cal_ms * 1e-3), 4),
+            "frac_note": "(bf16 flops / bf16 peak + fp32 flops / fp32 peak) / measured time",
         }
 
     # the uncompressed baseline: plain BF16 decode attention over the same context held dense
@@ -611,7 +727,7 @@ def main():
         "frac": round(dense_alg / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "bytes_per_call": dense_alg,
         "int2_step_speedup": round(dense_ms / ms, 3),
-        "int2_attend_speedup": round(dense_ms / attend_ms, 3),
+        "int2_dominant_kernel_speedup": round(dense_ms / S.dominant_ms, 3),
         # against any BF16 decode of this context on this machine: its bytes at the measured read
         # ceiling (a bound no BF16 kernel can beat)
         "bf16_at_ceiling_us": round(dense_alg / (ceiling_gbs * 1e9) * 1e6, 3),
@@ -620,56 +736,6 @@ def main():
     }
     del dense, ws_d, out_d
 
-    out = {
-        "metric": METRIC,
-        "value": round(total_bytes / (ms * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 6),
-        "us_per_step": round(ms * 1e3, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp32",
-        "data": "synthetic",
-        "config": {
-            "workload": w.name,
-            "batch": w.batch,
-            "context_tokens": list(sorted(set(w.ctx_lens)))[:4],
-            "hist_tokens": int(w.hist_lens.max()),
-            "q_heads": w.n_q_heads,
-            "kv_heads": w.n_kv_heads,
-            "head_dim": 128,
-            "page_tokens": 64,
-            "int2_splits": splits,
-            "layer_instances": layers,
-            "step": "oscar_decode_step: demote 1 token/request + BF16 pass + INT2 pass + merge",
-        },
-        "step_bytes": total_bytes,
-        "pct_of_hbm_peak": round(100 * total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(w.batch / (ms * 1e-3), 1),
-        "context_tokens_per_s": round(sum(w.ctx_lens) / (ms * 1e-3), 1),
-        "roofline": {
-            "kernel": "main_kernel (oscar_attend: INT2 history pass + merge)",
-            "bound": "hbm",
-            "achieved": round(attend_bytes / (attend_ms * 1e-3) / 1e9, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(attend_bytes / (attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name),
-            "us_per_launch": round(attend_ms * 1e3, 3),
-            "bytes_per_launch": attend_bytes,
-            "us_per_launch_p10_p50_p90": pct(rep_attend),
-            "us_per_launch_warm": round(warm_attend_ms * 1e3, 3),
-            "frac_of_measured_ceiling": round(attend_bytes / (attend_ms * 1e-3) / 1e9 / ceiling_gbs, 4),
-        },
-        "us_per_step_p10_p50_p90": pct(rep_step),
-        "us_per_step_warm": round(warm_step_ms * 1e3, 3),
-        "stream_ceiling": {"probe": "oscar_read_probe over 1 GiB (streaming 16-byte loads), best of 5",
-                           "gbs": round(ceiling_gbs, 1), "frac_of_peak": round(ceiling_gbs / HBM_PEAK_GBS, 4)},
-    }
     if multi is not None:
         out["multi_query"] = multi
     if cb_row is not None:
@@ -678,14 +744,101 @@ def main():
     if calib_row is not None:
         out["calibration"] = calib_row
     out["bf16_baseline"] = dense_row
-    if args.config == 5:
-        # the bulk-demotion row of this workload (after the decode timing: it allocates)
-        out["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5))
-        if cb_row is not None:
-            cb_row["bulk_demote"] = bulk_demote(w, rk_bits, rv_bits, dev, stream, max(5, args.steps // 5),
-                                                (klv, vlv))
-    if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (the pool shards by KV head "
+              "or request with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    configs = [args.config] if args.config else [int(c) for c in args.configs.split(",") if c.strip()]
+    stream = torch.cuda.current_stream()
+    t_start = time.perf_counter()
+
+    # one plain copy of known size (untimed): its FETCH_SIZE / WRITE_SIZE readings calibrate
+    # the counters of the kernels in the same profiled run
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    # measured stream ceiling of this box: the library's read probe over 1 GiB, best of five
+    from bit_kv_cache_oscar_amd import oscar_read_probe
+
+    probe = torch.ones(2 ** 28, dtype=torch.int32, device=dev)
+    probe_out = torch.zeros(4096, dtype=torch.int32, device=dev)
+    oscar_read_probe(probe, probe_out, stream)
+    ceil_ms = min(timed_once(lambda: oscar_read_probe(probe, probe_out, stream), stream, torch) for _ in range(5))
+    del probe, probe_out
+    ceiling_gbs = 2 ** 30 / (ceil_ms * 1e-3) / 1e9
+
+    rows = []
+    for i, cfg in enumerate(configs):
+        headline = i == 0
+        want_extras = args.extras == "all" or (args.extras == "headline" and headline)
+        S = setup(cfg, args, dev, fill_rows_needed=want_extras)
+        row = step_row(S, args, stream, torch)
+        row["roofline"]["frac_of_measured_ceiling"] = round(
+            row["roofline"]["achieved"] / ceiling_gbs, 4)
+        if want_extras:
+            row.update(extra_rows(S, args, stream, torch, dev, ceiling_gbs))
+        if cfg == 5:
+            # the bulk-demotion row of this workload (after the decode timing: it allocates)
+            row["bulk_demote"] = bulk_demote(S.w, S.rk_bits, S.rv_bits, dev, stream, max(5, args.steps // 5))
+        if args.cpu_seconds > 0:
+            row["cpu_baseline"] = cpu_baseline(S.w, args.cpu_seconds)
+        rows.append(row)
+        print(f"[bench] {S.w.name}: {row['us_per_step']} us/step, roofline frac {row['roofline']['frac']}, "
+              f"{time.perf_counter() - t_start:.0f} s elapsed", file=sys.stderr, flush=True)
+        del S
+        torch.cuda.empty_cache()
+
+    h = rows[0]
+    ms = h["us_per_step"] * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": h["achieved_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_step": h["us_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": h["workload"],
+            "batch": h["batch"],
+            "context_tokens": h["context_tokens"],
+            "q_heads": h["q_heads"],
+            "kv_heads": h["kv_heads"],
+            "head_dim": 128,
+            "page_tokens": 64,
+            "int2_splits": h["int2_splits"],
+            "layer_instances": h["layer_instances"],
+            "step": "oscar_decode_step_append: demote 1 token/request + BF16 pass + INT2 pass + merge",
+        },
+        "step_bytes": h["step_bytes"],
+        "pct_of_hbm_peak": h["pct_of_hbm_peak"],
+        "roofline": h["roofline"],
+        "stream_ceiling": {"probe": "oscar_read_probe over 1 GiB (streaming 16-byte loads), best of 5",
+                           "gbs": round(ceiling_gbs, 1), "frac_of_peak": round(ceiling_gbs / HBM_PEAK_GBS, 4)},
+        "rows": {r["workload"]: r for r in rows},
+        "wall_s": round(time.perf_counter() - t_start, 1),
+    }
+    if "cpu_baseline" in h:
+        out["cpu_baseline"] = h["cpu_baseline"]
     print(json.dumps(out), flush=True)
 
 

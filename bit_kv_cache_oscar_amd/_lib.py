@@ -73,6 +73,7 @@ _SIGNATURES = {
                                     c_void_p, c_void_p]),
     "oscar_decode_step_append_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32, c_int32]),
     "oscar_decode_step_append_splits": (c_int32, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_decode_step_append_launches": (c_int32, [POINTER(LayerDesc), c_int32, c_int32]),
     "oscar_decode_step_append": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
@@ -522,6 +523,12 @@ def oscar_decode_step_append_workspace_bytes(desc: LayerDesc, batch: int, n_spli
 
 def oscar_decode_step_append_splits(desc: LayerDesc, batch: int, max_hist_len: int) -> int:
     return int(lib().oscar_decode_step_append_splits(byref(desc), int(batch), int(max_hist_len)))
+
+
+def oscar_decode_step_append_launches(desc: LayerDesc, batch: int, n_splits: int) -> int:
+    """1 when oscar_decode_step_append runs in one launch for these sizes, 2 for prepare +
+    attend, 0 for invalid arguments."""
+    return int(lib().oscar_decode_step_append_launches(byref(desc), int(batch), int(n_splits)))
 
 
 def oscar_decode_step_append(desc: LayerDesc, k_src, v_src, clip_k, clip_v, q, rot_k, rot_v, pool, block_table,

@@ -631,6 +631,16 @@ size_t oscar_decode_step_append_workspace_bytes(const oscar_layer_desc* desc, in
   return oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits + 1, window_splits_of(desc));
 }
 
+constexpr long long kOneLaunchItems = 240;  // one-launch grid size the split count aims at
+
+int32_t oscar_decode_step_append_launches(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0 || n_splits <= 0) return 0;
+  const int gq = desc->n_q_heads / desc->n_kv_heads;
+  return oscar::step_append_one_launch(batch, desc->n_kv_heads, gq > 8 ? gq / 8 : 1, n_splits, window_splits_of(desc))
+             ? 1
+             : 2;
+}
+
 int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len) {
   if (check_desc_impl(desc) != OSCAR_OK || batch <= 0) return 1;
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
@@ -638,13 +648,12 @@ int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t ba
   const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1);
   // window items and appended-token items
   const long long n_win = static_cast<long long>(window_splits_of(desc) + 1) * batch * desc->n_kv_heads;
-  // one 8-wave workgroup per compute unit for window items and splits together while that
-  // keeps at least half the units on the history; otherwise two 4-wave workgroups per unit;
-  // past that (large batches) the two-launch default
   // one launch when its window and appended-token items and at least half the compute
   // units' worth of history splits fit one 8-wave workgroup per unit; otherwise the step
-  // runs as prepare + attend, with the two-launch default
-  long long s = (256 - n_win) / groups;
+  // runs as prepare + attend, with the two-launch default. The grid stays at 240 items:
+  // measured at 100K tokens, 248 and 256 items (every unit or nearly) cost about 2 us more
+  // per step than 232 to 240, with fewer pages per split.
+  long long s = (kOneLaunchItems - n_win) / groups;
   const long long by_pages = (pages + 7) / 8;
   if (s < 1 || s * groups < 128) {
     const int d = oscar_default_splits(desc, batch, max_hist_len);

@@ -257,12 +257,15 @@ int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const
  * a shared prefix page). k_src == NULL (with v_src, clip_k, clip_v NULL or
  * ignored) demotes nothing and decodes the pool as it is. A request with hist_len 0 while
  * appending is skipped (nothing is demoted for it).
- * One launch: window workgroups, and INT2 workgroups that rotate the query themselves; the
- * window workgroup of each (request, KV head)'s first split also demotes the appended token
- * and contributes that token's attention term; the workgroup that finishes last per
+ * One launch when its workgroups fit the chip at once (oscar_decode_step_append_launches):
+ * window workgroups; one workgroup per (request, KV head) that demotes the appended token
+ * and contributes that token's attention term; and INT2 workgroups that rotate the query
+ * themselves and leave the appended token out. The workgroup that finishes last per
  * (request, KV head) merges. No workgroup waits for another. While the appended token's V
  * codes are written, INT2 workgroups may read the 32-bit words that hold them; that slot has
  * weight zero in their pass, so whichever value such a read returns, the result is the same.
+ * Otherwise the step runs as two launches (prepare, attend), as oscar_decode_step does,
+ * with the appended token's page and slot taken from the block table on the device.
  * Arguments are those of oscar_decode_step, plus:
  *   n_splits   1..255, and ceil(max_pages / n_splits) <= 8192; oscar_decode_step_append_splits
  *              gives the count for which the launch's workgroups fit the chip at once
@@ -278,6 +281,10 @@ int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const
  */
 size_t oscar_decode_step_append_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits);
 int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len);
+/* Launches oscar_decode_step_append makes for (desc, batch, n_splits): 1 (one launch) or 2
+ * (prepare, attend); 0 for an invalid descriptor, batch or n_splits. Host only, no device
+ * work. */
+int32_t oscar_decode_step_append_launches(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits);
 int32_t oscar_decode_step_append(const oscar_layer_desc* desc, const void* k_src, const void* v_src,
                                  const float* clip_k, const float* clip_v, const void* q, const void* rot_k,
                                  const void* rot_v, void* pool, const int32_t* block_table, int32_t max_pages,

@@ -150,6 +150,28 @@ def test_default_splits_respect_the_pages_per_split_bound():
             assert 1 <= s <= 65535 and -(-pages // s) <= 8192, (batch, tokens, s)
 
 
+def test_one_launch_step_sizes():
+    """The one-launch step's split count keeps its grid (window items, one appended-token
+    item per (request, KV head), history splits) at 240 workgroups or fewer, and the launch
+    count follows from the grid fitting 256 workgroups."""
+    d = L.layer_desc(32, 8)  # 6 window splits of 64 tokens (64 sink + 256 recent)
+    ws = L.oscar_window_splits(d)
+    for hist in (32448, 99680):
+        s = L.oscar_decode_step_append_splits(d, 1, hist)
+        assert (ws + 1) * 8 + s * 8 <= 240 < (ws + 1) * 8 + (s + 1) * 8
+        assert L.oscar_decode_step_append_launches(d, 1, s) == 1
+    # 256 workgroups still run at once; one more does not
+    s_max = (256 - (ws + 1) * 8) // 8
+    assert L.oscar_decode_step_append_launches(d, 1, s_max) == 1
+    assert L.oscar_decode_step_append_launches(d, 1, s_max + 1) == 2
+    # batch 4 of a 64-query-head layer: too many window items for one launch
+    d5 = L.layer_desc(64, 8)
+    s5 = L.oscar_decode_step_append_splits(d5, 4, 130752)
+    assert L.oscar_decode_step_append_launches(d5, 4, s5) == 2
+    assert L.oscar_decode_step_append_launches(d, 0, 4) == 0
+    assert L.oscar_decode_step_append_launches(d, 1, 0) == 0
+
+
 def test_decode_bf16_and_merge_argument_checks(lib):
     desc = L.layer_desc(32, 8)
     d = ctypes.byref(desc)
