@@ -101,8 +101,9 @@ def step_source_hash():
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` ("step": the one-launch step kernel, "attend": the
-    attend launch, "attend_codebook": its codebook variant) from the committed counter summary
+    """HBM bytes per launch of `kernel` ("append_kernel": the one-launch step's kernel,
+    "main_kernel": the attend launch, "attend_codebook": the attend launch of the codebook
+    variant) from the committed counter summary
     of this workload, or None when there is none or the kernel sources changed since it was
     taken. FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same
     counter reads for a plain copy of COPY_BYTES bytes in the same run."""
@@ -429,7 +430,7 @@ def step_row(S, args, stream, torch):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(S.total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, "step"),
+            "traffic": measured_traffic(w.name, "append_kernel"),
             "us_per_launch": round(ms * 1e3, 3),
             "bytes_per_launch": S.total_bytes,
             "bytes_note": "the step's algorithmic bytes: history pages, window, R_K and R_V, query, output, "
@@ -448,7 +449,7 @@ def step_row(S, args, stream, torch):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(S.attend_bytes / (attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, "attend"),
+            "traffic": measured_traffic(w.name, "main_kernel"),
             "us_per_launch": round(attend_ms * 1e3, 3),
             "us_per_launch_p10_p50_p90": pct(rep_attend),
             "bytes_per_launch": S.attend_bytes,
