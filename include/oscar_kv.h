@@ -125,11 +125,14 @@ int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_
  *   s = fp16((hi - lo) / 3), z = fp16(lo)                    (round to nearest even)
  *   q_j = clamp(round_half_even((y_j - z) / s), 0, 3); all codes 0 when s == 0
  * and stores the codes, s and z at (dst_page[i], dst_slot[i]) of head h in the pool,
- * leaving every other slot's bits untouched. s and z are always exactly these. Below 64
- * tokens a per-row kernel decides every code exactly as well; from 64 tokens on a
- * matrix-core kernel takes the codes from fp32 values whose error stays below 1e-4 of the
- * code step, so a code whose (y_j - z) / s lies within 1e-4 of a rounding boundary may be
- * one level off (the same kernel falls back to exact sums for any token it cannot bound).
+ * leaving every other slot's bits untouched. s, z and the codes are always exactly these:
+ * below 64 tokens a per-row kernel sums in fp64 and re-sums with compensation any row its
+ * error bound cannot settle; from 64 tokens on a matrix-core kernel sums in fp32 under a
+ * proven any-order error bound and re-sums in fp64 (then with compensation) every extreme
+ * and every value whose bound straddles a rounding boundary, so ties round to even.
+ * Domain: the clipped extremes must stay within fp16 range (|c y| <= 65504). A row outside
+ * it gets the fp16 rounding of its scale and zero point (infinite) and all codes 0, and
+ * the other rows of the call are unaffected.
  *
  *   k_src, v_src   bf16 [n][n_kv_heads][128], the rows to demote (unrotated)
  *   dst_page       int32 [n], physical page of token i
