@@ -21,13 +21,14 @@
 // order (Higham, Accuracy and Stability of Numerical Algorithms, 2nd ed., section 4.2, with
 // unit 2^-23 per addition) bounds a chunk's error by gamma_32 sum |p| over its products,
 // gamma_32 < 32 2^-23 (1 + 2^-17); the three joins round to nearest (unit 2^-24), adding at
-// most 3 2^-24 (1 + 2^-15) sum |p|. With sum_i |x_i R_ij| <= |x| max_j |R_:,j|
-// (Cauchy-Schwarz),
-//   delta = 68 2^-24 (|x| max_j |R_:,j| (1 + 2^-10) + 2^-60) + 2^-116
-// bounds the error of every value of the token (the norms are fp32 sums of exact squares,
-// covered by the factor 1 + 2^-10; 2^-60 covers squares flushed to zero, 2^-116 the at most
-// 259 flushed products and partial sums of 2^-126 each). The matrix cores' own summation
-// order is thus never relied on, only this per-addition bound.
+// most 3 2^-24 (1 + 2^-15) sum |p|, so 68 2^-24 sum |p| (plus 2^-116 for at most 259
+// flushed products and partial sums of 2^-126 each) bounds a value's error. The sums
+// S_j = sum_i |x_i| |R_ij| come from the matrix cores too (|R^T| |x^T|, one 128-deep
+// accumulation): all their terms are >= 0, so in any order the fp32 result is within
+// gamma_127 < 2^-16 of S_j (flushed products: at most 2^-119). Hence
+//   delta = 68 2^-24 (1 + 2^-14) max_j S_j' + 2^-115
+// bounds the error of every value of the token. The matrix cores' own summation order is
+// thus never relied on, only this per-addition bound.
 //
 // Scales and zero points (bit for bit the quantiser's):
 //   - the exact extremes lie within delta of the fp32 ones and the quantiser's fp64 chain is
@@ -62,14 +63,13 @@ constexpr int kBWaves = 4;
 constexpr int kIters = 8;                              // 32-token iterations per wave
 constexpr int kRowsPerBlock = kBWaves * 32 * kIters;   // 1024
 constexpr int kRTRow = kHeadDim + 8;                   // bf16 per LDS row of R^T (16 bytes of bank spread)
-constexpr float kGamma = 68.f * 0x1p-24f;              // chunk bound plus the three joins, per sum |p|
+constexpr float kGammaS = 68.f * 0x1p-24f * (1.f + 0x1p-14f);  // per computed sum |p|: the chunks, the joins, S's own error
 constexpr float kFullT = 0x1p-7f;                      // bound on t above which a token is summed exactly
 
 struct BulkSmem {
   uint16_t rt[kHeadDim * kRTRow];             // R^T: row j holds column j of R
   uint16_t xs[kBWaves][2][16 * kHeadDim];     // per wave, the x rows of the iteration's two tiles (bf16 [16][128])
   unsigned char cs[kBWaves][16 * kHeadDim];   // per wave, the codes of the current tile
-  float colmax2[kBWaves];                     // per wave's share, max_j |R_:,j|^2
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -447,28 +447,6 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
     }
   }
   __syncthreads();
-  // largest squared column norm of R (threads 0..127: column tid)
-  if (tid < kHeadDim) {
-    float a = 0.f;
-    const uint4* row = reinterpret_cast<const uint4*>(sm.rt + tid * kRTRow);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint4 v = row[q];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = __uint_as_float(w4[k] << 16);
-        const float hi = __uint_as_float(w4[k] & 0xFFFF0000u);
-        a = fmaf(lo, lo, fmaf(hi, hi, a));
-      }
-    }
-    a = wave_max(a);
-    if (lane == 0) sm.colmax2[wave] = a;
-  }
-  __syncthreads();
-  // the fp32 sums of 128 exact squares: within 2^-16 relative, covered by the factor below
-  const float colmax2 = fmaxf(sm.colmax2[0], sm.colmax2[1]);
-
   unsigned char* cs = sm.cs[wave];
 
   for (int it = 0; it < kIters; ++it) {
@@ -495,25 +473,40 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         acc[mt][tt] = ((ch[0][tt] + ch[1][tt]) + ch[2][tt]) + ch[3][tt];
       }
     }
-    // this iteration's rows into LDS (for the exact paths) and their squared norms
-    float nxs[2];
+    // this iteration's rows into LDS (for the exact paths), then |x| in their registers
     int cpg[2], csl[2];
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      float nx = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         *reinterpret_cast<uint4*>(sm.xs[wave][tt] + n_ * kHeadDim + 32 * ks + 8 * G) = bx[tt][ks];
-        const uint32_t w4[4] = {bx[tt][ks].x, bx[tt][ks].y, bx[tt][ks].z, bx[tt][ks].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          nx = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[k]), __builtin_bit_cast(bf16x2, w4[k]), nx,
-                                               false);
+        bx[tt][ks] = make_uint4(bx[tt][ks].x & 0x7FFF7FFFu, bx[tt][ks].y & 0x7FFF7FFFu, bx[tt][ks].z & 0x7FFF7FFFu,
+                                bx[tt][ks].w & 0x7FFF7FFFu);
       }
-      nxs[tt] = nx;
       cpg[tt] = pg[tt];
       csl[tt] = sl[tt];
+    }
+    // The token's error bound. S = |R^T| |x^T| (the sum of |p| of every value) from one
+    // 128-deep accumulation: its terms are all >= 0, so the fp32 result is within
+    // gamma_127 < 2^-16 of S whatever the order (products below the fp32 range flushed: at
+    // most 2^-119 in all). dl = 68 2^-24 max S (1 + 2^-14) + 2^-115 then holds for every value
+    // of the token.
+    float smax[2] = {0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      f32x4 sb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 a = *reinterpret_cast<const uint4*>(sm.rt + (16 * mt + n_) * kRTRow + 32 * ks + 8 * G);
+        const uint4 aa = make_uint4(a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu, a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu);
+        const bf16x8 aav = __builtin_bit_cast(bf16x8, aa);
+        sb[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, bx[0][ks]), sb[0], 0, 0, 0);
+        sb[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, bx[1][ks]), sb[1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        smax[tt] = fmaxf(fmaxf(smax[tt], fmaxf(sb[tt][0], sb[tt][1])), fmaxf(sb[tt][2], sb[tt][3]));
     }
 
 
@@ -537,27 +530,24 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
       mn[tt] = b;
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      mx[tt] = fmaxf(mx[tt], __shfl_xor(mx[tt], 16, 64));
-      mn[tt] = fminf(mn[tt], __shfl_xor(mn[tt], 16, 64));
-      nxs[tt] += __shfl_xor(nxs[tt], 16, 64);
-    }
+    for (int o = 16; o <= 32; o <<= 1)
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      mx[tt] = fmaxf(mx[tt], __shfl_xor(mx[tt], 32, 64));
-      mn[tt] = fminf(mn[tt], __shfl_xor(mn[tt], 32, 64));
-      nxs[tt] += __shfl_xor(nxs[tt], 32, 64);
-    }
+      for (int tt = 0; tt < 2; ++tt) {
+        mx[tt] = fmaxf(mx[tt], __shfl_xor(mx[tt], o, 64));
+        mn[tt] = fminf(mn[tt], __shfl_xor(mn[tt], o, 64));
+        smax[tt] = fmaxf(smax[tt], __shfl_xor(smax[tt], o, 64));
+      }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
 #pragma clang fp contract(off)
-      // the bound of every fp32 value of this token
-      dl[tt] = kGamma * (sqrtf(nxs[tt] * colmax2) * (1.f + 0x1p-10f) + 0x1p-60f) + 0x1p-116f;
-      // The exact extremes lie in [mx - dl, mx + dl] and [mn - dl, mn + dl]; the chain below
-      // evaluates the quantiser's steps on those ends in fp32 and widens the results by more
-      // than every rounding of either evaluation (fp32 here, fp64 in the quantiser), so they
-      // bound the true scale and zero point. Rounding to fp16 is monotone: equal ends mean a
-      // determined value.
+      // the bound of every fp32 value of this token (fp32 rounding of the product and sum
+      // covered by the factor 1 + 2^-14 in kGammaS)
+      dl[tt] = fmaf(kGammaS, smax[tt], 0x1p-115f);
+      // The exact extremes lie within dl of mx and mn; the chain below evaluates the
+      // quantiser's steps on those ends in fp32 and widens the results by more than every
+      // rounding of either evaluation (fp32 here, fp64 in the quantiser), so they bound the
+      // true scale and zero point. Rounding to fp16 is monotone: equal ends mean a determined
+      // value.
       const float d = dl[tt];
       const float c32 = static_cast<float>(cr);
       s16[tt] = z16[tt] = 0;
