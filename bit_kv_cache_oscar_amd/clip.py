@@ -13,13 +13,16 @@ from __future__ import annotations
 
 import numpy as np
 
+from .extremes import rotate
+
 GRID = np.round(np.arange(50, 101) / 100.0, 2)
 
 
 def errors(rows, rot, grid=GRID) -> np.ndarray:
-    """Squared reconstruction error of rows [N, 128] under rotation rot for each clip ratio."""
-    y = np.asarray(rows, np.float64) @ np.asarray(rot, np.float64)
-    ymax, ymin = y.max(axis=1), y.min(axis=1)
+    """Squared reconstruction error of rows [N, 128] under rotation rot for each clip ratio
+    (the scale and zero point from the rows' exact extremes, as the demotion kernels take
+    them)."""
+    y, ymax, ymin = rotate(rows, rot)
     out = np.empty(len(grid))
     for i, c in enumerate(grid):
         c32 = float(np.float32(c))

@@ -22,17 +22,19 @@ from __future__ import annotations
 
 import numpy as np
 
+from .extremes import rotate
+
 UNIFORM = (0, 16, 32, 48)
 
 
 def normalized_samples(rows, rot, clip: float) -> np.ndarray:
     """t = (y - z16) / s16 for every value of calibration rows [N, 128] (bf16 values) rotated by
-    rot [128, 128]; rows whose fp16 scale is zero are dropped."""
-    x = np.asarray(rows, np.float64)
-    y = x @ np.asarray(rot, np.float64)
+    rot [128, 128]; rows whose fp16 scale is zero are dropped. The scale and zero point come
+    from the rows' exact extremes, as the demotion kernels take them."""
+    y, ymax, ymin = rotate(rows, rot)
     c = float(np.float32(clip))
-    hi = c * y.max(axis=1)
-    lo = c * y.min(axis=1)
+    hi = c * ymax
+    lo = c * ymin
     s = ((hi - lo) / 3.0).astype(np.float16).astype(np.float64)
     z = lo.astype(np.float16).astype(np.float64)
     keep = s > 0

@@ -222,8 +222,8 @@ def test_one_group_grouped_entries_match_the_one_group_path():
 def test_grouped_full_size_sampled(group):
     """The grouped path at the 32K workload's real size (32768-token context, 32 query heads,
     8 KV heads): every history token demoted on the GPU, then decoded at about four pages
-    per split (the split count the benchmark settles on); sampled KV heads compared with
-    the oracle (pool contents and the outputs of their query heads)."""
+    per split (the split count the benchmark settles on); every KV head compared with the
+    oracle (pool contents and the outputs of its query heads)."""
     from test_gpu_parity import _demote_all
 
     w = synth.workload(2)
@@ -244,7 +244,7 @@ def test_grouped_full_size_sampled(group):
     c.set_splits(s)
     got = c.decode(queries(w), w.sm_scale).cpu().numpy()
     pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, ogroups.head_block_bytes(group))
-    for b, kv in ((0, 0), (0, 5)):
+    for b, kv in [(0, kv) for kv in range(w.n_kv_heads)]:
         say("grouped full size sample", w.name, "group", group, "b", b, "kv", kv, "splits", s)
         ref_hist, km, vm = oracle_history_grouped(w, b, kv, rk, rv, group)
         gpu_hist = unpack_grouped(pool, table[b], kv, w.hist_len(b), group)
