@@ -469,7 +469,8 @@ def step_row(S, args, stream, torch):
 def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
     """multi-query, grouped pages, codebook, calibration and BF16-baseline rows."""
     import synth
-    from bit_kv_cache_oscar_amd import oscar_decode_multi, oscar_decode_workspace_bytes
+    from bit_kv_cache_oscar_amd import (oscar_decode_multi, oscar_decode_multi_splits, oscar_decode_workspace_bytes,
+                                        oscar_window_splits)
 
     w, base, splits, layers, q = S.w, S.base, S.splits, S.layers, S.q
     step_k, step_v, step_page, step_slot = S.step_k, S.step_v, S.step_page, S.step_slot
@@ -499,13 +500,17 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
     if n_tok >= 2:
         qm = torch.from_numpy(np.stack([synth.query_tokens(w, b, n_tok) for b in range(w.batch)])).to(dev)
         qm = qm.to(torch.bfloat16)
-        wsm = torch.zeros(oscar_decode_workspace_bytes(base.desc, w.batch * n_tok, splits), dtype=torch.uint8,
+        msplits = oscar_decode_multi_splits(base.desc, w.batch, n_tok, int(w.hist_lens.max()))
+        gqt = w.gq * n_tok
+        m_items = ((oscar_window_splits(base.desc) + 1) * w.n_kv_heads * w.batch +
+                   msplits * w.n_kv_heads * w.batch * (2 if gqt > 8 else 1))
+        wsm = torch.zeros(oscar_decode_workspace_bytes(base.desc, w.batch * n_tok, msplits), dtype=torch.uint8,
                           device=dev)
         outm = torch.empty((w.batch, n_tok, w.n_q_heads, 128), dtype=torch.float32, device=dev)
 
         def decode_multi(c):
             oscar_decode_multi(c.desc, qm, c.rot_k, c.rot_v, c.pool, c.block_table, c.hist_len, c.k_win, c.v_win,
-                               c.win_len, w.sm_scale, splits, wsm, outm, stream)
+                               c.win_len, w.sm_scale, msplits, wsm, outm, stream)
 
         for i in range(max(2, args.warmup)):
             decode_multi(insts[i % layers])
@@ -514,9 +519,12 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
         win = int(sum(w.win_lens)) * w.n_kv_heads * WIN_BYTES
         mbytes = hist + win + 2 * w.n_kv_heads * ROT_BYTES + w.batch * n_tok * w.n_q_heads * 128 * (2 + 4)
         multi = {
-            "entry": "oscar_decode_multi (prepare + attend, no demotion)",
+            "entry": "oscar_decode_multi (no demotion)",
+            "launches": 1 if m_items <= 256 else 2,
+            "n_splits": msplits,
             "query_tokens": n_tok,
             "us_per_call": round(multi_ms * 1e3, 3),
+            "vs_one_token_step": round(multi_ms / ms, 3),
             "bound": "hbm",
             "achieved": round(mbytes / (multi_ms * 1e-3) / 1e9, 2),
             "peak": HBM_PEAK_GBS,

@@ -74,6 +74,7 @@ _SIGNATURES = {
     "oscar_decode_step_append_workspace_bytes": (c_size_t, [POINTER(LayerDesc), c_int32, c_int32]),
     "oscar_decode_step_append_splits": (c_int32, [POINTER(LayerDesc), c_int32, c_int32]),
     "oscar_decode_step_append_launches": (c_int32, [POINTER(LayerDesc), c_int32, c_int32]),
+    "oscar_decode_multi_splits": (c_int32, [POINTER(LayerDesc), c_int32, c_int32, c_int32]),
     "oscar_decode_step_append": (c_int32, [POINTER(LayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                            c_void_p, c_void_p, c_int32, c_float, c_int32, c_void_p, c_size_t,
@@ -459,8 +460,9 @@ def oscar_decode_codebook(desc: LayerDesc, q, rot_k, rot_v, codebook, pool, bloc
 def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
                        sm_scale: float, n_splits: int, workspace, out, stream=None, codebook=None):
     """Decode attention for T query tokens per request (q [B, T, Hq, 128] bf16, out the same
-    shape in float32; token t sees the window up to its own position) in two launches;
-    workspace from oscar_decode_workspace_bytes(desc, B * T, n_splits)."""
+    shape in float32; token t sees the window up to its own position), in one launch when the grid fits the chip
+    at once (oscar_decode_multi_splits), else two; workspace from
+    oscar_decode_workspace_bytes(desc, B * T, n_splits), zero-filled once before first use."""
     _need(q.dim() == 4 and q.shape[2] == desc.n_q_heads and q.shape[3] == HEAD_DIM, "q must be [batch, T, n_q_heads, 128]")
     n_tok = int(q.shape[1])
     batch, nbytes = _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
@@ -523,6 +525,11 @@ def oscar_decode_step_append_workspace_bytes(desc: LayerDesc, batch: int, n_spli
 
 def oscar_decode_step_append_splits(desc: LayerDesc, batch: int, max_hist_len: int) -> int:
     return int(lib().oscar_decode_step_append_splits(byref(desc), int(batch), int(max_hist_len)))
+
+
+def oscar_decode_multi_splits(desc: LayerDesc, batch: int, n_tokens: int, max_hist_len: int) -> int:
+    """Split count for oscar_decode_multi: one launch when its grid fits the chip at once."""
+    return int(lib().oscar_decode_multi_splits(byref(desc), int(batch), int(n_tokens), int(max_hist_len)))
 
 
 def oscar_decode_step_append_launches(desc: LayerDesc, batch: int, n_splits: int) -> int:

@@ -298,6 +298,8 @@ struct InlineQuery {
   double scale_log2 = 0.0;
   int n_excl = 0;
   int pstride = 0;                  // 0: n_splits
+  int nqt = 1;                      // query tokens per request: q rows of virtual heads (query_row)
+  int gqv = 0;                      // virtual heads per KV head (with nqt > 1)
 };
 
 // One workgroup (NW waves) of the INT2 pass: history split `split` of request b for the
@@ -404,9 +406,11 @@ __device__ __forceinline__ void int2_split(
                                                            static_cast<size_t>(RW * wave) * kHeadDim) + lane;
 #pragma unroll
     for (int r = 0; r < RW; ++r) rk[r] = rp[r * (kHeadDim / 2)];
-    if (lane < kQLanes)
-      qchunk = *reinterpret_cast<const uint4*>(iq.q + (head0 + lane / (RW / 8)) * kHeadDim + RW * wave +
-                                               8 * (lane % (RW / 8)));
+    if (lane < kQLanes) {
+      const int g = lane / (RW / 8);
+      const size_t row = iq.nqt > 1 ? query_row(b, h0 + g, n_q, iq.gqv, iq.nqt) : head0 + g;
+      qchunk = *reinterpret_cast<const uint4*>(iq.q + row * kHeadDim + RW * wave + 8 * (lane % (RW / 8)));
+    }
   }
 
   // block ids of this wave's pages p0, p0 + NW, ...: lane i of blk_lane holds the id of the

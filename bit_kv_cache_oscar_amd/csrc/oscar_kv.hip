@@ -633,26 +633,17 @@ size_t oscar_decode_step_append_workspace_bytes(const oscar_layer_desc* desc, in
 
 constexpr long long kOneLaunchItems = 240;  // one-launch grid size the split count aims at
 
-int32_t oscar_decode_step_append_launches(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
-  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0 || n_splits <= 0) return 0;
-  const int gq = desc->n_q_heads / desc->n_kv_heads;
-  return oscar::step_append_one_launch(batch, desc->n_kv_heads, gq > 8 ? gq / 8 : 1, n_splits, window_splits_of(desc))
-             ? 1
-             : 2;
-}
-
-int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len) {
-  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0) return 1;
+// The split count of a one-launch grid (step or multi-query decode) with gqt query rows per
+// KV head: one launch when its window and appended-token items and at least half the
+// compute units' worth of history splits fit one 8-wave workgroup per unit; otherwise the
+// two-launch default. The grid stays at 240 items: measured at 100K tokens, 248 and 256
+// items (every unit or nearly) cost about 2 us more per step than 232 to 240, with fewer
+// pages per split.
+static int32_t one_launch_splits(const oscar_layer_desc* desc, int32_t batch, int gqt, int32_t max_hist_len) {
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
-  const int gq = desc->n_q_heads / desc->n_kv_heads;
-  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1);
+  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gqt > 8 ? gqt / 8 : 1);
   // window items and appended-token items
   const long long n_win = static_cast<long long>(window_splits_of(desc) + 1) * batch * desc->n_kv_heads;
-  // one launch when its window and appended-token items and at least half the compute
-  // units' worth of history splits fit one 8-wave workgroup per unit; otherwise the step
-  // runs as prepare + attend, with the two-launch default. The grid stays at 240 items:
-  // measured at 100K tokens, 248 and 256 items (every unit or nearly) cost about 2 us more
-  // per step than 232 to 240, with fewer pages per split.
   long long s = (kOneLaunchItems - n_win) / groups;
   const long long by_pages = (pages + 7) / 8;
   if (s < 1 || s * groups < 128) {
@@ -665,6 +656,26 @@ int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t ba
   if (s < 1) s = 1;
   if (s > 255) s = 255;
   return static_cast<int32_t>(s);
+}
+
+int32_t oscar_decode_step_append_launches(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0 || n_splits <= 0) return 0;
+  const int gq = desc->n_q_heads / desc->n_kv_heads;
+  return oscar::step_append_one_launch(batch, desc->n_kv_heads, gq > 8 ? gq / 8 : 1, n_splits, window_splits_of(desc))
+             ? 1
+             : 2;
+}
+
+int32_t oscar_decode_step_append_splits(const oscar_layer_desc* desc, int32_t batch, int32_t max_hist_len) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0) return 1;
+  return one_launch_splits(desc, batch, desc->n_q_heads / desc->n_kv_heads, max_hist_len);
+}
+
+int32_t oscar_decode_multi_splits(const oscar_layer_desc* desc, int32_t batch, int32_t n_tokens, int32_t max_hist_len) {
+  if (check_desc_impl(desc) != OSCAR_OK || batch <= 0 || n_tokens <= 0) return 1;
+  const long long gqt = static_cast<long long>(desc->n_q_heads / desc->n_kv_heads) * n_tokens;
+  if (gqt > 16) return oscar_default_splits(desc, batch, max_hist_len);
+  return one_launch_splits(desc, batch, static_cast<int>(gqt), max_hist_len);
 }
 
 int32_t oscar_decode_step_append(const oscar_layer_desc* desc, const void* k_src, const void* v_src,
@@ -798,6 +809,13 @@ int32_t multi_impl(const oscar_layer_desc* desc, const void* q, int32_t n_tokens
   a.out = out;
   a.codebook = codebook;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int gqt = gq * n_tokens;
+  if (oscar::step_append_one_launch(batch, desc->n_kv_heads, gqt > 8 ? gqt / 8 : 1, n_splits, window_splits_of(desc))) {
+    // one launch: window items and INT2 splits that rotate the query rows themselves; the
+    // arrival counters are zero from the workspace's fill or the previous call
+    a.append = 0;
+    return hip_status(oscar::launch_step_append(a, s), "one-launch multi-query decode");
+  }
   st = hip_status(oscar::launch_prepare(a, s), "prepare launch");
   if (st != OSCAR_OK) return st;
   return hip_status(oscar::launch_attend(a, s), "attend launch");

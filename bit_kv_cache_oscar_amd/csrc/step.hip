@@ -145,7 +145,8 @@ hipError_t launch_main(const StepArgs& a, hipStream_t stream) {
   return a.codebook ? launch_main_cb<GQ, GQT, true>(a, stream) : launch_main_cb<GQ, GQT, false>(a, stream);
 }
 
-// The one-launch step. Items 0 .. n_win - 1 are window splits (split c, KV head, request);
+// The one-launch step (and the one-launch multi-query decode: nqt query tokens per request
+// as virtual heads, no appended token). Items 0 .. n_win - 1 are window splits (split c, KV head, request);
 // when appending, the next B n_kv items each demote the appended token of one (request, KV
 // head) and write its own attention term; the rest are INT2 splits (split, KV head x head
 // group, request) with the query prepared inline and the appended token left out. Every
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
     kv = (id / a.n_wsplits) % a.n_kv;
     b = id / (a.n_wsplits * a.n_kv);
     window::window_split<GQT, NW, true>(smem, c, kv, kv * GQT, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q, a.n_kv,
-                                        a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc, GQT, 1);
+                                        a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc, GQT, a.nqt);
   } else if (id < n_win + n_app) {
     id -= n_win;
     kv = id % a.n_kv;
@@ -185,6 +186,8 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
     iq.scale_log2 = a.scale_log2;
     iq.n_excl = a.append;
     iq.pstride = pstride;
+    iq.nqt = a.nqt;
+    iq.gqv = GQT;
     int2::int2_split<GQ, true, NW, CB, true>(smem, split, gy, b, a.pool, a.block_table, a.max_pages, a.hist_len,
                                              a.n_q, a.n_kv, a.n_groups, a.n_splits, nullptr, nullptr, a.hist.m,
                                              a.hist.l, a.hist.acc, a.codebook, iq, a.rot_v);
@@ -201,7 +204,8 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
   // every partial is in the window's basis (the INT2 splits and the appended token
   // un-rotated theirs): the merge is a weighted sum
   uint4 rb[8 / NW][4];
-  merge::merge_group<GQT, NW, true, false>(smem, b, kv, a.n_q, a.hist, pstride, a.win, a.n_wsplits, rb, a.out, 1);
+  merge::merge_group<GQT, NW, true, false>(smem, b, kv, a.n_q, a.hist, pstride, a.win, a.n_wsplits, rb, a.out,
+                                           a.nqt);
 }
 
 constexpr int kStepSlots8 = 256;  // 8-wave workgroups resident at once (one per compute unit)

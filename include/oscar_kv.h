@@ -349,13 +349,22 @@ int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* ro
  * win_len[b] - n_tokens + t: it attends to the whole INT2 history and to window slots
  * [0, win_len[b] - (n_tokens - 1 - t)) (causal among the query tokens, whose K and V are
  * the last n_tokens window slots). With n_tokens == 1 this is oscar_decode.
+ * One launch when its workgroups fit the chip at once (the window workgroups and INT2
+ * workgroups that rotate their query rows themselves, as in oscar_decode_step_append
+ * without an appended token; oscar_decode_multi_splits gives a split count for which they
+ * do); otherwise two launches (prepare, attend).
  *   q          bf16 [batch][n_tokens][n_q_heads][128]
  *   out        float32 [batch][n_tokens][n_q_heads][128]
  *   n_tokens   a power of two with n_tokens * (n_q_heads / n_kv_heads) <= 16 (else
  *              OSCAR_ERR_UNSUPPORTED); batch * n_tokens <= 65535
- *   workspace  at least oscar_decode_workspace_bytes(desc, batch * n_tokens, n_splits) bytes
+ *   workspace  at least oscar_decode_workspace_bytes(desc, batch * n_tokens, n_splits)
+ *              bytes, whose arrival counters must be zero before the first call (zero-fill
+ *              it once after allocating it; every call leaves them at zero)
  * The other arguments are those of oscar_decode.
  */
+/* Split count for oscar_decode_multi at these sizes: the one-launch count when the grid can
+ * fit the chip at once, else oscar_default_splits. Host only; 1 for invalid arguments. */
+int32_t oscar_decode_multi_splits(const oscar_layer_desc* desc, int32_t batch, int32_t n_tokens, int32_t max_hist_len);
 int32_t oscar_decode_multi(const oscar_layer_desc* desc, const void* q, int32_t n_tokens, const void* rot_k,
                            const void* rot_v, const void* pool, const int32_t* block_table, int32_t max_pages,
                            const int32_t* hist_len, const void* k_win, const void* v_win, const int32_t* win_len,

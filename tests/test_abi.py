@@ -172,6 +172,24 @@ def test_one_launch_step_sizes():
     assert L.oscar_decode_step_append_launches(d, 1, 0) == 0
 
 
+def test_one_launch_multi_sizes():
+    """The multi-query decode's split count keeps its one-launch grid (window items and
+    history splits, T x query heads per KV head over one or two head groups) within 240
+    workgroups, falls back to the two-launch default when that grid cannot hold half the
+    chip's units of history splits, and answers 1 for invalid arguments."""
+    d = L.layer_desc(32, 8)
+    ws = L.oscar_window_splits(d)
+    for t, groups in ((1, 1), (2, 1), (4, 2)):
+        s = L.oscar_decode_multi_splits(d, 1, t, 32448)
+        assert s == L.oscar_decode_step_append_splits(d, 1, 32448) or t > 1
+        assert (ws + 1) * 8 + s * 8 * groups <= 240 < (ws + 1) * 8 + (s + 1) * 8 * groups
+    # batch 4 of a 64-query-head layer with two tokens: the two-launch default
+    d5 = L.layer_desc(64, 8)
+    assert L.oscar_decode_multi_splits(d5, 4, 2, 130752) == L.oscar_default_splits(d5, 4, 130752)
+    assert L.oscar_decode_multi_splits(d, 0, 2, 4096) == 1
+    assert L.oscar_decode_multi_splits(d, 1, 0, 4096) == 1
+
+
 def test_decode_bf16_and_merge_argument_checks(lib):
     desc = L.layer_desc(32, 8)
     d = ctypes.byref(desc)

@@ -17,7 +17,8 @@ from oracle import attention as oatt
 from oracle import codebook as ocb
 from oracle import pages as opages
 from oracle import quant as oquant
-from test_gpu_parity import DECODE_CASES, _demote_all, bf16, custom, make_cache, queries, say, wide_splits
+from test_gpu_parity import (DECODE_CASES, _demote_all, bf16, custom, make_cache, multi_split_counts, queries, say,
+                             wide_splits)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -305,7 +306,7 @@ def test_codebook_full_size_end_to_end_sampled(cfg):
 def test_codebook_multi_query_on_oracle_pages(case, n_tok, book):
     """oscar_decode_multi_codebook: T query tokens per request over a codebook pool built by
     the oracle, causal over the window, twice per split count."""
-    from bit_kv_cache_oscar_amd import oscar_decode_multi_codebook, oscar_decode_workspace_bytes, oscar_default_splits
+    from bit_kv_cache_oscar_amd import oscar_decode_multi_codebook, oscar_decode_workspace_bytes
 
     w = DECODE_CASES[case]()
     (rk_bits, rv_bits), (rk, rv) = rotations(w)
@@ -331,7 +332,7 @@ def test_codebook_multi_query_on_oracle_pages(case, n_tok, book):
     for b in range(w.batch):
         wk, wv = windows(w, b)
         refs.append(oatt.decode_multi(qn[b].astype(np.float64), rk, rv, wk, wv, hists[b], w.sm_scale, codebooks=books))
-    for s in sorted({oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())), 3}):
+    for s in sorted(multi_split_counts(c.desc, w, n_tok)):
         ws = torch.zeros(oscar_decode_workspace_bytes(c.desc, w.batch * n_tok, s), dtype=torch.uint8, device="cuda")
         out = torch.empty((w.batch, n_tok, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
         for rep in range(2):

@@ -125,6 +125,20 @@ MULTI_CASES = {
 }
 
 
+def multi_split_counts(desc, w, n_tok):
+    """Split counts a multi-query test runs: the two-launch default, the one-launch count,
+    3, and the smallest count whose grid no longer fits one launch (the two-launch path)."""
+    from bit_kv_cache_oscar_amd import oscar_decode_multi_splits, oscar_default_splits, oscar_window_splits
+
+    mh = int(w.hist_lens.max())
+    gqt = w.n_q_heads // w.n_kv_heads * n_tok
+    per_split = w.n_kv_heads * w.batch * (2 if gqt > 8 else 1)
+    fixed = (oscar_window_splits(desc) + 1) * w.n_kv_heads * w.batch
+    two = max(1, (256 - fixed) // per_split + 1)
+    return {oscar_default_splits(desc, w.batch, mh), oscar_decode_multi_splits(desc, w.batch, n_tok, mh), 3,
+            min(two, 255)}
+
+
 @pytest.mark.parametrize("name", list(MULTI_CASES))
 def test_decode_multi_on_oracle_pages(name):
     """T query tokens per request over one pool: token t sees the whole history and the window
@@ -144,7 +158,7 @@ def test_decode_multi_on_oracle_pages(name):
     for b in range(w.batch):
         wk, wv = windows(w, b)
         refs.append(oatt.decode_multi(qn[b].astype(np.float64), rk, rv, wk, wv, hists[b], w.sm_scale))
-    splits = {oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())), 3}
+    splits = multi_split_counts(c.desc, w, n_tok)
     for s in sorted(splits):
         ws = torch.zeros(oscar_decode_workspace_bytes(c.desc, w.batch * n_tok, s), dtype=torch.uint8, device="cuda")
         out = torch.empty((w.batch, n_tok, w.n_q_heads, 128), dtype=torch.float32, device="cuda")
