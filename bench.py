@@ -538,10 +538,24 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
     # same history demoted into grouped pools of every instance, then the three-launch decode
     # (oscar_decode_int2_grouped, oscar_decode_bf16, oscar_merge) and the grouped INT2 pass
     # alone, back to back over the instances
-    from bit_kv_cache_oscar_amd import oscar_decode_int2_grouped, oscar_default_splits
+    from bit_kv_cache_oscar_amd import oscar_attend, oscar_decode_int2_grouped, oscar_default_splits
     from bit_kv_cache_oscar_amd.layer import LayerCache
 
-    grouped_rows = {}
+    # the one-group baselines: the two-launch step and its attend launch alone, at the
+    # two-launch default split count
+    def one_step2(c):
+        c.n_splits = splits
+        c.step(step_k, step_v, step_page, step_slot, q, w.sm_scale, stream)
+
+    def one_attend(c):
+        oscar_attend(c.desc, c.rot_v, c.pool, c.block_table, c.hist_len, splits, c.workspace, c.out, stream)
+
+    for i in range(max(2, args.warmup)):
+        one_step2(insts[i % layers])
+    one_step2_ms = timed(one_step2, args.steps)
+    one_attend_ms = timed(one_attend, args.steps)
+    grouped_rows = {"one_group_step_us": round(one_step2_ms * 1e3, 3),
+                    "one_group_attend_us": round(one_attend_ms * 1e3, 3)}
     for group in (64, 32):
         ng = 128 // group
         gins = []
@@ -589,7 +603,12 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
         def g_step(c):
             c.step(step_k, step_v, step_page, step_slot, q, w.sm_scale, stream)
 
-        g_step(insts[0])
+        # the two-launch grouped step at the library's default split count
+        g_splits = oscar_default_splits(gins[0].desc, w.batch, int(max(w.hist_lens)))
+        for c in gins:
+            c.set_splits(g_splits)
+        for i in range(max(2, args.warmup)):
+            g_step(insts[i % layers])
         g_step_ms = timed(g_step, args.steps)
         insts = saved
         g_bytes = int(sum(w.hist_lens)) * w.n_kv_heads * (64 + 8 * ng) + w.n_kv_heads * ROT_BYTES + \
@@ -602,8 +621,12 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
             "int2_pass_us_by_splits": {str(k): round(v * 1e3, 3) for k, v in sorted(sweep.items())},
             "us_per_decode": round(g_ms * 1e3, 3),
             "us_per_step": round(g_step_ms * 1e3, 3),
-            "step_entry": "oscar_decode_step_grouped (demote one token per request, window pass, grouped pass, merge)",
+            "step_splits": g_splits,
+            "step_entry": "oscar_decode_step_grouped (prepare: demotion, window pass, query; attend: grouped "
+                          "matrix-core pass + merge)",
+            "step_vs_one_group_step": round(g_step_ms / one_step2_ms, 3),
             "int2_pass_us_per_launch": round(g_int2_ms * 1e3, 3),
+            "int2_pass_vs_one_group_attend": round(g_int2_ms / one_attend_ms, 3),
             "bound": "hbm",
             "achieved": round(g_bytes / (g_int2_ms * 1e-3) / 1e9, 2),
             "peak": HBM_PEAK_GBS,

@@ -13,6 +13,15 @@ constexpr int kKCodes = 0;
 constexpr int kVCodes = 2048;
 constexpr int kKMeta = 4096;
 constexpr int kVMeta = 4352;
+// Bytes of one page for one KV head with NG quantisation groups per vector (groups of
+// 128 / NG rotated dims): the K and V codes (4096 bytes), then the K (scale, zero) pairs,
+// NG per slot (slot t, group g at 4 (NG t + g)), then the V pairs the same way. NG = 1 is
+// the one-group layout above.
+template <int NG>
+constexpr int head_block_bytes() {
+  return kKMeta + 512 * NG;
+}
+static_assert(head_block_bytes<1>() == kHeadBlock && kVMeta - kKMeta == 256, "one-group layout");
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Byte offsets inside a head's page block of the word holding K slot t, dims 16w..16w+15

@@ -43,6 +43,15 @@
 // sum(q_rot). V takes the levels themselves (0..48, the same bound as the scaled codes),
 // every lane with the factor 16.
 //
+// Quantisation groups (QbitAI article on OSCAR, section on aiming the rotation at attention:
+// a scale and zero point per group of G = 128 / NG rotated dims, NG = 2 or 4): the K product
+// runs once per group against a copy of the query limbs that is zero outside the group's
+// dims, and group g's term s_g Q_g . (c - 2) + (z_g + 2 s_g) S_g joins the score, with
+// S_g = sum of Q over the group (from the same copy times a B of ones) standing in for the
+// exact sum of the rotated query; the V side takes one set of P' limbs per group (each dim
+// tile lies in one group) and one zero-point sum per group. Query heads come in tiles of
+// four there (the per-group metadata leaves no registers for two tiles).
+//
 // A workgroup serves one (history split, KV head x head group, request), 4 waves, at most 8
 // query heads (16 query heads per KV head run as two groups of 8). Wave w walks
 // pages split_begin + w, + 4, ... of its split with two page buffers in flight. In a page,
@@ -117,42 +126,47 @@ __device__ __forceinline__ float v_combo(const i32x4& c) {
   return fmaf(b2, 65536.f, fmaf(b1, 256.f, b0));
 }
 
+template <int NG = 1>
 struct PageRegs {
-  uint4 k[2];  // K words: slots 4n..4n+3 (two words each: dims 32G..32G+15, 32G+16..32G+31)
-  uint4 km;    // K (scale, zero) of slots 4n..4n+3
-  uint4 vm;    // V (scale, zero) of slots 4n..4n+3
-  uint4 v[2];  // V words of dims 16dt + n, dt = 0..7, slots 16G..16G+15
+  uint4 k[2];    // K words: slots 4n..4n+3 (two words each: dims 32G..32G+15, 32G+16..32G+31)
+  uint4 km[NG];  // K (scale, zero) of slots 4n..4n+3, NG groups each
+  uint4 vm[NG];  // V (scale, zero) of slots 4n..4n+3, NG groups each
+  uint4 v[2];    // V words of dims 16dt + n, dt = 0..7, slots 16G..16G+15
 
   __device__ __forceinline__ uint32_t kword(int nt, int h) const {
     const uint4& c = k[nt >> 1];
     return (nt & 1) ? (h ? c.w : c.z) : (h ? c.y : c.x);
   }
-  __device__ __forceinline__ uint32_t kmeta(int nt) const { return nt == 0 ? km.x : nt == 1 ? km.y : nt == 2 ? km.z : km.w; }
-  __device__ __forceinline__ uint32_t vmeta(int nt) const { return nt == 0 ? vm.x : nt == 1 ? vm.y : nt == 2 ? vm.z : vm.w; }
-  __device__ __forceinline__ uint32_t vword(int dt) const {
-    const uint4& c = v[dt >> 2];
-    const int i = dt & 3;
+  static __device__ __forceinline__ uint32_t pick(const uint4& c, int i) {
     return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w;
   }
+  // pair of slot 4n + nt, group g
+  __device__ __forceinline__ uint32_t kmeta(int nt, int g = 0) const { return pick(km[(NG * nt + g) >> 2], (NG * nt + g) & 3); }
+  __device__ __forceinline__ uint32_t vmeta(int nt, int g = 0) const { return pick(vm[(NG * nt + g) >> 2], (NG * nt + g) & 3); }
+  __device__ __forceinline__ uint32_t vword(int dt) const { return pick(v[dt >> 2], dt & 3); }
 };
 
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int imm) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + imm, 0, 0));
 }
 
-// Lane l = 16 G + n reads its page data as six 16-byte loads (the page layout keeps each
-// lane's K and V words contiguous) through a raw buffer descriptor of the page's 4608-byte
-// head block, built in scalar registers from the wave-uniform page address.
-// `bytes` is kHeadBlock, or 0 for a request that reads nothing (every load then returns 0
-// without touching memory).
-__device__ __forceinline__ void load_page(PageRegs& r, const uint8_t* page, uint32_t lane32, uint32_t meta16,
-                                          int bytes = kHeadBlock) {
+// Lane l = 16 G + n reads its page data as 4 + 2 NG 16-byte loads (the page layout keeps
+// each lane's K and V words, and the pairs of its four slots, contiguous) through a raw
+// buffer descriptor of the page's head block, built in scalar registers from the
+// wave-uniform page address. `meta16` is kKMeta + 16 NG n; `bytes` is the head block's
+// size, or 0 for a request that reads nothing (every load then returns 0 without touching
+// memory).
+template <int NG>
+__device__ __forceinline__ void load_page(PageRegs<NG>& r, const uint8_t* page, uint32_t lane32, uint32_t meta16,
+                                          int bytes = head_block_bytes<NG>()) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(page), 0, bytes, kRsrcWord3);
   r.k[0] = load16(rs, lane32, kKCodes);
   r.k[1] = load16(rs, lane32, kKCodes + 16);
-  r.km = load16(rs, meta16, 0);
-  r.vm = load16(rs, meta16, kVMeta - kKMeta);
+#pragma unroll
+  for (int i = 0; i < NG; ++i) r.km[i] = load16(rs, meta16, 16 * i);
+#pragma unroll
+  for (int i = 0; i < NG; ++i) r.vm[i] = load16(rs, meta16, 256 * NG + 16 * i);
   r.v[0] = load16(rs, lane32, kVCodes);
   r.v[1] = load16(rs, lane32, kVCodes + 16);
 }
@@ -255,27 +269,33 @@ __device__ __forceinline__ void qprep_head(unsigned char* smem, const uint16_t* 
 // "Pending" sums are in units of 2^E relative to the reference maximum m (the V sums in the
 // int32 MFMA accumulators, in units of 2^(E-1)). The "flushed" sums (true values relative
 // to m: sum p s^V c^V per dim, l and sum p z^V) live in LDS, touched only when flushing.
-template <int MT>
+template <int MT, int NG = 1>
 struct WaveState {
   float m[MT];        // reference maximum, log2 units; -inf before the first page
   float bias[MT];     // E - m (0 before the first page); -inf for padding heads
   float lq[MT];       // pending sum of p 2^E over this lane's slots
-  float zq[MT];       // pending sum of p 2^E z^V
+  float zq[MT][NG];   // pending sum of p 2^E z^V per quantisation group
   i32x4 acci[MT][8];  // pending fragments (rows: 3 XORed limbs + code sum), dims 16 dt + n
 };
 
-constexpr int kQRow = 144;   // bytes of one query-limb row in LDS: 128 dims + 16 of bank spread
-constexpr int kFlushed = 10;  // flushed values per lane and tile: 8 dim tiles, l, sum p z
+constexpr int kQRow = 144;  // bytes of one query-limb row in LDS: 128 dims + 16 of bank spread
+// flushed values per lane and tile: 8 dim tiles, l, sum p z per quantisation group
+template <int NG>
+constexpr int flushed_values() {
+  return 9 + NG;
+}
 
 // GQ is the number of query heads one workgroup serves (at most 8); a KV head whose group
 // is larger is served by n_groups = (query heads per KV head) / GQ workgroups along y.
-// NW is the number of waves of the workgroup.
-template <int GQ, int NW = kWaves>
+// NW is the number of waves of the workgroup; NG the quantisation groups per vector (the
+// query limbs are then held once per group, each copy zero outside the group's dims, and
+// the P' limbs once per group).
+template <int GQ, int NW = kWaves, int NG = 1>
 constexpr int int2_smem_bytes() {
   constexpr int MT = (GQ + 3) / 4;
-  constexpr int loop = NW * MT * 16 * kPRow + NW * MT * kFlushed * 64 * 4;
+  constexpr int loop = NW * MT * NG * 16 * kPRow + NW * MT * flushed_values<NG>() * 64 * 4;
   constexpr int wacc = NW * GQ * kHeadDim * 4;
-  return 4 * MT * 4 * kQRow + loop + wacc + 2 * NW * GQ * 4;
+  return NG * 4 * MT * 4 * kQRow + loop + wacc + 2 * NW * GQ * 4;
 }
 
 // Partial-result store: with kCoherent, an agent-scope store that is visible to every
@@ -308,7 +328,7 @@ struct InlineQuery {
 // With kUnrot the split's value sum is un-rotated (times R_V^T, rot_v [n_kv][128][128])
 // before it is written, so its partial is in the basis of the BF16 window's; otherwise it
 // stays in the rotated basis of R_V.
-template <int GQ, bool kCoherent = false, int NW = kWaves, bool CB = false, bool kUnrot = false>
+template <int GQ, bool kCoherent = false, int NW = kWaves, bool CB = false, bool kUnrot = false, int NG = 1>
 __device__ __forceinline__ void int2_split(
     unsigned char* __restrict__ smem, int split, int gy, int b, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ hist_len, int n_q, int n_kv, int n_groups, int n_splits,
@@ -316,15 +336,21 @@ __device__ __forceinline__ void int2_split(
     float* __restrict__ out_l, float* __restrict__ out_acc, const uint32_t* __restrict__ codebook = nullptr,
     const InlineQuery& iq = InlineQuery(), const uint16_t* __restrict__ rot_v = nullptr) {
   constexpr int MT = (GQ + 3) / 4;  // 16-row M tiles
-  constexpr int kPBytes = NW * MT * 16 * kPRow;
-  constexpr int kFBytes = NW * MT * kFlushed * 64 * 4;
+  static_assert(NG == 1 || NG == 2 || NG == 4, "one, two or four quantisation groups per vector");
+  static_assert(NG == 1 || !CB, "codebooks are defined for one group per vector");
+  constexpr int kFl = flushed_values<NG>();
+  constexpr int kPBytes = NW * MT * NG * 16 * kPRow;
+  constexpr int kFBytes = NW * MT * kFl * 64 * 4;
   constexpr int kLoopBytes = kPBytes + kFBytes;
   constexpr int kWaccBytes = NW * GQ * kHeadDim * 4;
+  constexpr int kQCopy = 4 * MT * 4 * kQRow;  // one copy of the query limb rows
+  constexpr int kBlock = head_block_bytes<NG>();
 
-  // page loop: query limbs; P' limbs and flushed sums of each wave. Epilogue: wave partials
-  // in a space of their own, so a wave writes its partial as soon as its pages are done.
+  // page loop: query limbs (one copy per quantisation group); P' limbs and flushed sums of
+  // each wave. Epilogue: wave partials in a space of their own, so a wave writes its partial
+  // as soon as its pages are done.
   unsigned char* q_s = smem;
-  unsigned char* scratch_s = smem + 4 * MT * 4 * kQRow;
+  unsigned char* scratch_s = smem + NG * kQCopy;
   float (*wacc_s)[GQ][kHeadDim] = reinterpret_cast<float (*)[GQ][kHeadDim]>(scratch_s + kLoopBytes);
   float(*wm_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kLoopBytes + kWaccBytes);
   float(*wl_s)[GQ] = reinterpret_cast<float(*)[GQ]>(scratch_s + kLoopBytes + kWaccBytes + NW * GQ * 4);
@@ -357,10 +383,10 @@ __device__ __forceinline__ void int2_split(
   const int p_begin = split * pps;
   const int p_end = min(n_pages, p_begin + pps);
   const int32_t* table = block_table + static_cast<size_t>(b) * max_pages;
-  const uint8_t* head_base = pool + static_cast<size_t>(kv) * kHeadBlock;
-  const size_t page_stride = static_cast<size_t>(n_kv) * kHeadBlock;
+  const uint8_t* head_base = pool + static_cast<size_t>(kv) * kBlock;
+  const size_t page_stride = static_cast<size_t>(n_kv) * kBlock;
   const uint32_t lane32 = 32u * lane;
-  const uint32_t meta16 = kKMeta + 16u * n;
+  const uint32_t meta16 = kKMeta + 16u * NG * n;
   const size_t head0 = static_cast<size_t>(b) * n_q + h0;
 
   // Prologue, in two memory round trips: the query operands (which do not depend on the
@@ -371,7 +397,7 @@ __device__ __forceinline__ void int2_split(
   static_assert(kQChunks <= 64 * NW, "one query-limb chunk per thread");
   const int qrow = tid >> 3;
   const int qc = tid & 7;
-  const bool inline_q = iq.q != nullptr;  // uniform
+  const bool inline_q = NG == 1 && iq.q != nullptr;  // uniform (groups take the prepared query)
   uint4 qv = {0u, 0u, 0u, 0u};
   if (!inline_q && tid < kQChunks && (qrow >> 2) < GQ)
     qv = *reinterpret_cast<const uint4*>(qlimb + (head0 + (qrow >> 2)) * 512 + (qrow & 3) * kHeadDim + 16 * qc);
@@ -425,7 +451,17 @@ __device__ __forceinline__ void int2_split(
   asm volatile("" ::"v"(qchunk.x), "v"(qchunk.y), "v"(qchunk.z), "v"(qchunk.w));
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(kcent[mt]), "v"(qsc[mt]), "v"(sig[mt]));
-  if (!inline_q && tid < kQChunks) *reinterpret_cast<uint4*>(q_s + qrow * kQRow + 16 * qc) = qv;
+  if (!inline_q && tid < kQChunks) {
+    if constexpr (NG == 1) {
+      *reinterpret_cast<uint4*>(q_s + qrow * kQRow + 16 * qc) = qv;
+    } else {
+      // copy g keeps the dims of group g (chunk qc holds dims 16 qc .. 16 qc + 15)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        *reinterpret_cast<uint4*>(q_s + g * kQCopy + qrow * kQRow + 16 * qc) =
+            (qc * NG) / 8 == g ? qv : uint4{0u, 0u, 0u, 0u};
+    }
+  }
   auto page_of = [&](int j) -> const uint8_t* {  // j wave-uniform, 0 <= j < n_mine
     if ((j >> 6) != chunk) {
       chunk = j >> 6;
@@ -482,11 +518,13 @@ __device__ __forceinline__ void int2_split(
   // keep the page loads below the dot products
   __builtin_amdgcn_sched_barrier(0);
 
-  // three page buffers: pages i + 1 and i + 2 load while page i is processed. A wave
-  // without pages issues the same loads against an empty buffer, so every path carries
-  // the same loads into the loop.
-  const int rec = n_mine > 0 ? kHeadBlock : 0;
-  PageRegs buf[3];
+  // three page buffers: pages i + 1 and i + 2 load while page i is processed (two with
+  // the larger per-group metadata of four groups, or of two groups over two head tiles:
+  // page i + 1 loads while page i is processed). A wave without pages issues the same
+  // loads against an empty buffer, so every path carries the same loads into the loop.
+  constexpr int NB = (NG == 1 || (NG == 2 && MT == 1)) ? 3 : 2;
+  const int rec = n_mine > 0 ? kBlock : 0;
+  PageRegs<NG> buf[NB];
   load_page(buf[0], page_of(0), lane32, meta16, rec);
   load_page(buf[1], page_of(n_mine > 1 ? 1 : 0), lane32, meta16, rec);
   if (inline_q) {
@@ -559,12 +597,14 @@ __device__ __forceinline__ void int2_split(
     }
   }
 
-  WaveState<MT> st;
+  WaveState<MT, NG> st;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     st.m[mt] = -INFINITY;
     st.bias[mt] = head_ok[mt] ? 0.f : -INFINITY;
-    st.lq[mt] = st.zq[mt] = 0.f;
+    st.lq[mt] = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) st.zq[mt][g] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.acci[mt][dt] = i32x4{0, 0, 0, 0};
   }
@@ -578,15 +618,28 @@ __device__ __forceinline__ void int2_split(
   float vcap_l = -1.f;  // V scales below vcap_l / vscale fit the current E
   bool fresh = true;    // no page processed yet
 
-  // wave-private P'-limb rows: row mt*16 + 4 g + l; rows with l == 3 hold constant ones
-  unsigned char* pl = scratch_s + wave * (MT * 16 * kPRow);
-  // wave-private flushed sums: [mt][k][lane], k < 8: dim tile k, 8: l, 9: sum p z
-  float* fl = reinterpret_cast<float*>(scratch_s + kPBytes) + wave * (MT * kFlushed * 64) + lane;
+  // wave-private P'-limb rows: row (mt NG + group) 16 + 4 g + l; rows with l == 3 hold
+  // constant ones
+  unsigned char* pl = scratch_s + wave * (MT * NG * 16 * kPRow);
+  // wave-private flushed sums: [mt][k][lane], k < 8: dim tile k, 8: l, 9 + group: sum p z
+  float* fl = reinterpret_cast<float*>(scratch_s + kPBytes) + wave * (MT * kFl * 64) + lane;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    *reinterpret_cast<uint32_t*>(pl + (mt * 16 + 4 * G + 3) * kPRow + 4 * n) = 0x01010101u;
 #pragma unroll
-    for (int k = 0; k < kFlushed; ++k) fl[(mt * kFlushed + k) * 64] = 0.f;
+    for (int g = 0; g < NG; ++g)
+      *reinterpret_cast<uint32_t*>(pl + ((mt * NG + g) * 16 + 4 * G + 3) * kPRow + 4 * n) = 0x01010101u;
+#pragma unroll
+    for (int k = 0; k < kFl; ++k) fl[(mt * kFl + k) * 64] = 0.f;
+  }
+
+  // the centring seed and the offset weight of each (tile, group): -2 sum Q and sig with
+  // one group; with groups, from the group sums S_g of the fixed-point query (below)
+  int kcg[MT][NG];
+  float sgg[MT][NG];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    kcg[mt][0] = kcent[mt];
+    sgg[mt][0] = sig[mt];
   }
 
   // fold tile mt's pending sums into the flushed ones, rescaled to the reference m_new
@@ -595,71 +648,125 @@ __device__ __forceinline__ void int2_split(
       const float alpha = st.m[mt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m[mt] - m_new);
       const float down = pow2f(-E);
       const float down_v = pow2f(1 - E);
-      float* f = fl + mt * kFlushed * 64;
+      float* f = fl + mt * kFl * 64;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) f[dt * 64] = fmaf(v_combo(st.acci[mt][dt]), down_v, f[dt * 64]) * alpha;
       f[8 * 64] = fmaf(st.lq[mt], down, f[8 * 64]) * alpha;
-      f[9 * 64] = fmaf(st.zq[mt], down, f[9 * 64]) * alpha;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) f[(9 + g) * 64] = fmaf(st.zq[mt][g], down, f[(9 + g) * 64]) * alpha;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.acci[mt][dt] = i32x4{0, 0, 0, 0};
-    st.lq[mt] = st.zq[mt] = 0.f;
+    st.lq[mt] = 0.f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) st.zq[mt][g] = 0.f;
     st.m[mt] = m_new;
   };
 
-  auto process = [&](const PageRegs& cur, int ntok) {
-    // K side: rows (head, limb) x 16 slots per tile
-    i8x16 aK[MT][2];
+  auto process = [&](const PageRegs<NG>& cur, int ntok) {
+    // K side: rows (head, limb) x 16 slots per tile. With groups, one product per group,
+    // from the query copy that is zero outside the group's dims, each folded into the
+    // scores as it completes.
+    float x[MT][4];  // scores relative to the frame: x = score_log2 - m + E
+    float sv[NG][4], zv[NG][4];
+    if constexpr (NG == 1) {
+      i8x16 aK[MT][2];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        aK[mt][ks] = *reinterpret_cast<const i8x16*>(q_s + (16 * mt + n) * kQRow + 32 * G + 16 * ks);
-    i32x4 d[MT][4];
+        for (int ks = 0; ks < 2; ++ks)
+          aK[mt][ks] = *reinterpret_cast<const i8x16*>(q_s + (16 * mt + n) * kQRow + 32 * G + 16 * ks);
+      i32x4 d[MT][4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      i8x16 b0, b1;
-      if constexpr (CB) {
-        b0 = unpack16_lut(cur.kword(nt, 0), klut);
-        b1 = unpack16_lut(cur.kword(nt, 1), klut);
-      } else {
-        b0 = unpack16(cur.kword(nt, 0));
-        b1 = unpack16(cur.kword(nt, 1));
+      for (int nt = 0; nt < 4; ++nt) {
+        i8x16 b0, b1;
+        if constexpr (CB) {
+          b0 = unpack16_lut(cur.kword(nt, 0), klut);
+          b1 = unpack16_lut(cur.kword(nt, 1), klut);
+        } else {
+          b0 = unpack16(cur.kword(nt, 0));
+          b1 = unpack16(cur.kword(nt, 1));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, i32x4{kcg[mt][0], 0, 0, 0}));
+      }
+      // slot metadata of this lane's slots 4n..4n+3
+      float sk[4], u[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t km = cur.kmeta(nt);
+        const uint32_t vm = cur.vmeta(nt);
+        sk[nt] = f16_to_f32(km);
+        u[nt] = fmaf(kmid, sk[nt], f16_to_f32(km >> 16));  // z + 2 s (codebook: z + s mid / 16)
+        sv[0][nt] = f16_to_f32(vm) * vscale;  // V scale over the factor of this lane's codes
+        zv[0][nt] = f16_to_f32(vm >> 16);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        d[mt][nt] = mfma16(aK[mt][1], b1, mfma16(aK[mt][0], b0, i32x4{kcent[mt], 0, 0, 0}));
-    }
-    // slot metadata of this lane's slots 4n..4n+3
-    float sk[4], u[4], sv[4], zv[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint32_t km = cur.kmeta(nt);
-      const uint32_t vm = cur.vmeta(nt);
-      sk[nt] = f16_to_f32(km);
-      u[nt] = fmaf(kmid, sk[nt], f16_to_f32(km >> 16));  // z + 2 s (codebook: z + s mid / 16)
-      sv[nt] = f16_to_f32(vm) * vscale;  // V scale over the factor of this lane's codes
-      zv[nt] = f16_to_f32(vm >> 16);
-    }
-    // scores relative to the frame: x = score_log2 - m + E
-    float x[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int nt = 0; nt < 4; ++nt) {
+          const i32x4 c = d[mt][nt];
+          // Q . (c - 2), exact (the partial terms may wrap; the sum fits)
+          const int D = static_cast<int>(static_cast<uint32_t>(c[0]) + (static_cast<uint32_t>(c[1]) << 8) +
+                                         (static_cast<uint32_t>(c[2]) << 16));
+          x[mt][nt] = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sgg[mt][0], st.bias[mt]));
+        }
+    } else {
+      i8x16 b0[4], b1[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const i32x4 c = d[mt][nt];
-        // Q . (c - 2), exact (the partial terms may wrap; the sum fits)
-        const int D = static_cast<int>(static_cast<uint32_t>(c[0]) + (static_cast<uint32_t>(c[1]) << 8) +
-                                       (static_cast<uint32_t>(c[2]) << 16));
-        x[mt][nt] = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sig[mt], st.bias[mt]));
+        b0[nt] = unpack16(cur.kword(nt, 0));
+        b1[nt] = unpack16(cur.kword(nt, 1));
       }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) x[mt][nt] = st.bias[mt];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float sk[4], u[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const uint32_t km = cur.kmeta(nt, g);
+          sk[nt] = f16_to_f32(km);
+          u[nt] = fmaf(2.f, sk[nt], f16_to_f32(km >> 16));  // z + 2 s
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const unsigned char* qa = q_s + g * kQCopy + (16 * mt + n) * kQRow + 32 * G;
+          const i8x16 a0 = *reinterpret_cast<const i8x16*>(qa);
+          const i8x16 a1 = *reinterpret_cast<const i8x16*>(qa + 16);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const i32x4 c = mfma16(a1, b1[nt], mfma16(a0, b0[nt], i32x4{kcg[mt][g], 0, 0, 0}));
+            // Q_g . (c - 2) over the group's dims, exact
+            const int D = static_cast<int>(static_cast<uint32_t>(c[0]) + (static_cast<uint32_t>(c[1]) << 8) +
+                                           (static_cast<uint32_t>(c[2]) << 16));
+            x[mt][nt] = fmaf(static_cast<float>(D) * sk[nt], qsc[mt], fmaf(u[nt], sgg[mt][g], x[mt][nt]));
+          }
+        }
+      }
+      // the V metadata once the K codes are done with
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const uint32_t vm = cur.vmeta(nt, g);
+          sv[g][nt] = f16_to_f32(vm) * vscale;
+          zv[g][nt] = f16_to_f32(vm >> 16);
+        }
+    }
     if (ntok < kPageTokens) {
       // slots past the history end may hold stale bits: no weight, no scale
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const bool valid = 4 * n + nt < ntok;
-        sv[nt] = valid ? sv[nt] : 0.f;
-        zv[nt] = valid ? zv[nt] : 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          sv[g][nt] = valid ? sv[g][nt] : 0.f;
+          zv[g][nt] = valid ? zv[g][nt] : 0.f;
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) x[mt][nt] = valid ? x[mt][nt] : -INFINITY;
       }
@@ -671,7 +778,9 @@ __device__ __forceinline__ void int2_split(
       xm[mt] = fmaxf(fmaxf(x[mt][0], x[mt][1]), fmaxf(x[mt][2], x[mt][3]));
       over = over || xm[mt] > thr;
     }
-    const float svm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    float svm = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+#pragma unroll
+    for (int g = 1; g < NG; ++g) svm = fmaxf(svm, fmaxf(fmaxf(sv[g][0], sv[g][1]), fmaxf(sv[g][2], sv[g][3])));
     const bool vover = svm > vcap_l;
     if (fresh || __any(over || vover)) {
       // a new exponent for the wave's V scales moves every tile's frame
@@ -700,51 +809,67 @@ __device__ __forceinline__ void int2_split(
       thr = static_cast<float>(E + kTau);
       fresh = false;
     }
-    // probabilities (units of 2^E), pending sums, P' limbs. A tile whose P' are all zero
-    // (every weight p s^V 2^E below one unit) adds exactly nothing to the V sums: its limb
-    // rows then hold -128 c per code and the constant row c, which cancel in v_combo, so its
-    // limbs and matrix products are skipped (wave-uniform).
-    bool vskip[MT];
+    // probabilities (units of 2^E), pending sums, P' limbs (per group: the V scales differ).
+    // A (tile, group) whose P' are all zero (every weight p s^V 2^E below one unit) adds
+    // exactly nothing to the V sums: its limb rows then hold -128 c per code and the
+    // constant row c, which cancel in v_combo, so its limbs and matrix products are skipped
+    // (wave-uniform).
+    bool vskip[MT][NG];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      uint32_t P[4];
+      float pe[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const float pe = __builtin_amdgcn_exp2f(x[mt][nt]);
-        st.lq[mt] += pe;
-        st.zq[mt] = fmaf(pe, zv[nt], st.zq[mt]);
-        // pe sv < 2^24: the float pe sv + 2^24 holds round(pe sv / 2) in its mantissa, and its
-        // exponent's low bit is bit 23
-        P[nt] = __float_as_uint(fmaf(pe, sv[nt], 16777216.f));
+        pe[nt] = __builtin_amdgcn_exp2f(x[mt][nt]);
+        st.lq[mt] += pe[nt];
       }
-      vskip[mt] = __all((P[0] | P[1] | P[2] | P[3]) == 0x4B800000u);  // 2^24: P' = 0
-      if (!vskip[mt]) {
-        // byte l of the four P' values into one dword per limb, in signed range
-        const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
-        const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
-        const uint32_t u01 = __builtin_amdgcn_perm(P[1], P[0], 0x0C0C0602u);
-        const uint32_t u23 = __builtin_amdgcn_perm(P[3], P[2], 0x0C0C0602u);
-        const uint32_t L0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
-        const uint32_t L1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
-        const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // bit 7 set by the exponent
-        unsigned char* row = pl + (mt * 16 + 4 * G) * kPRow + 4 * n;
-        *reinterpret_cast<uint32_t*>(row) = L0;
-        *reinterpret_cast<uint32_t*>(row + kPRow) = L1;
-        *reinterpret_cast<uint32_t*>(row + 2 * kPRow) = L2;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        uint32_t P[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          st.zq[mt][g] = fmaf(pe[nt], zv[g][nt], st.zq[mt][g]);
+          // pe sv < 2^24: the float pe sv + 2^24 holds round(pe sv / 2) in its mantissa, and
+          // its exponent's low bit is bit 23
+          P[nt] = __float_as_uint(fmaf(pe[nt], sv[g][nt], 16777216.f));
+        }
+        vskip[mt][g] = __all((P[0] | P[1] | P[2] | P[3]) == 0x4B800000u);  // 2^24: P' = 0
+        if (!vskip[mt][g]) {
+          // byte l of the four P' values into one dword per limb, in signed range
+          const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
+          const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
+          const uint32_t u01 = __builtin_amdgcn_perm(P[1], P[0], 0x0C0C0602u);
+          const uint32_t u23 = __builtin_amdgcn_perm(P[3], P[2], 0x0C0C0602u);
+          const uint32_t L0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
+          const uint32_t L1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
+          const uint32_t L2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);  // bit 7 set by the exponent
+          unsigned char* row = pl + ((mt * NG + g) * 16 + 4 * G) * kPRow + 4 * n;
+          *reinterpret_cast<uint32_t*>(row) = L0;
+          *reinterpret_cast<uint32_t*>(row + kPRow) = L1;
+          *reinterpret_cast<uint32_t*>(row + 2 * kPRow) = L2;
+        }
       }
     }
     bool vall = true;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) vall = vall && vskip[mt];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) vall = vall && vskip[mt][g];
     if (!vall) {
       // the wave's LDS operations run in order: the reads below see the writes above
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      i8x16 aP[MT];
+      i8x16 aP[MT][NG];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) aP[mt] = *reinterpret_cast<const i8x16*>(pl + (mt * 16 + n) * kPRow + 16 * G);
-      // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          aP[mt][g] = *reinterpret_cast<const i8x16*>(pl + ((mt * NG + g) * 16 + n) * kPRow + 16 * G);
+      // V side: rows (head, limb) x 64 slots x 16 dims per dim tile, accumulated in int32;
+      // dim tile dt lies in group dt NG / 8
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
+        constexpr int kTilesPerGroup = 8 / NG;
+        const int g = dt / kTilesPerGroup;
         i8x16 bv;
         if constexpr (CB)
           bv = unpack16_lut(cur.vword(dt), vlut);
@@ -752,7 +877,7 @@ __device__ __forceinline__ void int2_split(
           bv = unpack16_scaled(cur.vword(dt));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          if (MT == 1 || !vskip[mt]) st.acci[mt][dt] = mfma16(aP[mt], bv, st.acci[mt][dt]);
+          if ((MT == 1 && NG == 1) || !vskip[mt][g]) st.acci[mt][dt] = mfma16(aP[mt][g], bv, st.acci[mt][dt]);
       }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -765,21 +890,51 @@ __device__ __forceinline__ void int2_split(
   // query limbs in LDS (the inline preparation's last barrier already covers them; the
   // page loop's set-up above writes only wave-private LDS)
   if (!inline_q) __syncthreads();
-  // Whole triples of pages in a loop with one exit, then the last one or two: with a
-  // single back edge the compiler's wait for a page covers only that page, and the
-  // next one keeps loading.
-  int i = 0;
-  for (; i + 3 <= n_mine; i += 3) {
-    load_page(buf[2], next_of(i + 2), lane32, meta16);
-    process(buf[0], ntok_of(i));
-    load_page(buf[0], next_of(i + 3), lane32, meta16);
-    process(buf[1], ntok_of(i + 1));
-    load_page(buf[1], next_of(i + 4), lane32, meta16);
-    process(buf[2], ntok_of(i + 2));
+  if constexpr (NG > 1) {
+    // S_g = sum of Q over group g's dims, exact in int32 (|S_g| <= 64 2^21), as the group's
+    // query copy times a B of ones on the matrix cores. The group's centring seed is -2 S_g
+    // and its offset weight qsc S_g: the fold then takes the fixed-point query for both of
+    // its terms, so the group's score term is qsc Q_g . (s c + z), the dequantised key's dot
+    // with the query as the K product sees it.
+    const i8x16 ones = __builtin_bit_cast(i8x16, uint4{0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u});
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const unsigned char* qa = q_s + g * kQCopy + (16 * mt + n) * kQRow + 32 * G;
+        const i32x4 c = mfma16(*reinterpret_cast<const i8x16*>(qa + 16), ones,
+                               mfma16(*reinterpret_cast<const i8x16*>(qa), ones, i32x4{0, 0, 0, 0}));
+        const int S = static_cast<int>(static_cast<uint32_t>(c[0]) + (static_cast<uint32_t>(c[1]) << 8) +
+                                       (static_cast<uint32_t>(c[2]) << 16));
+        kcg[mt][g] = -2 * S;
+        sgg[mt][g] = qsc[mt] * static_cast<float>(S);
+      }
   }
-  if (i < n_mine) {
-    process(buf[0], ntok_of(i));
-    if (i + 1 < n_mine) process(buf[1], ntok_of(i + 1));
+  // Whole triples (pairs) of pages in a loop with one exit, then the last one or two: with
+  // a single back edge the compiler's wait for a page covers only that page, and the next
+  // one keeps loading.
+  int i = 0;
+  if constexpr (NB == 3) {
+    for (; i + 3 <= n_mine; i += 3) {
+      load_page(buf[2], next_of(i + 2), lane32, meta16);
+      process(buf[0], ntok_of(i));
+      load_page(buf[0], next_of(i + 3), lane32, meta16);
+      process(buf[1], ntok_of(i + 1));
+      load_page(buf[1], next_of(i + 4), lane32, meta16);
+      process(buf[2], ntok_of(i + 2));
+    }
+    if (i < n_mine) {
+      process(buf[0], ntok_of(i));
+      if (i + 1 < n_mine) process(buf[1], ntok_of(i + 1));
+    }
+  } else {
+    for (; i + 2 <= n_mine; i += 2) {
+      process(buf[0], ntok_of(i));
+      load_page(buf[0], next_of(i + 2), lane32, meta16);
+      process(buf[1], ntok_of(i + 1));
+      load_page(buf[1], next_of(i + 3), lane32, meta16);
+    }
+    if (i < n_mine) process(buf[0], ntok_of(i));
   }
 
   // R_V fragments of the un-rotation, requested now: they arrive while the waves' partials
@@ -788,27 +943,30 @@ __device__ __forceinline__ void int2_split(
   if constexpr (kUnrot) merge::load_rv<NW>(rot_v, kv, rb);
 
   // ---- wave partials: lane (G, n) holds head 4mt + G, dims 16dt + n
-  float accf[MT][8], lf[MT], zf[MT];
+  float accf[MT][8], lf[MT], zf[MT][NG];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     if (!fresh) flush_tile(mt, st.m[mt]);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) accf[mt][dt] = fl[(mt * kFlushed + dt) * 64];
-    lf[mt] = fl[(mt * kFlushed + 8) * 64];
-    zf[mt] = fl[(mt * kFlushed + 9) * 64];
+    for (int dt = 0; dt < 8; ++dt) accf[mt][dt] = fl[(mt * kFl + dt) * 64];
+    lf[mt] = fl[(mt * kFl + 8) * 64];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) zf[mt][q] = fl[(mt * kFl + 9 + q) * 64];
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int g = 4 * mt + G;
     const float l = row16_sum(lf[mt]);
-    const float zs = row16_sum(zf[mt]);
+    float zs[NG];
+#pragma unroll
+    for (int q = 0; q < NG; ++q) zs[q] = row16_sum(zf[mt][q]);
     if (g < GQ) {
       if (n == 0) {
         wm_s[wave][g] = st.m[mt];
         wl_s[wave][g] = l;
       }
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) wacc_s[wave][g][16 * dt + n] = accf[mt][dt] + zs;
+      for (int dt = 0; dt < 8; ++dt) wacc_s[wave][g][16 * dt + n] = accf[mt][dt] + zs[dt / (8 / NG)];
     }
   }
   __syncthreads();

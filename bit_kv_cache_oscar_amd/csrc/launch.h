@@ -64,10 +64,11 @@ hipError_t launch_demote_bulk(const LayerShape& L, const void* k_src, const void
                               const void* rot_v, const float* clip_k, const float* clip_v, void* pool,
                               hipStream_t stream, const uint32_t* codebook = nullptr);
 
+// `group`: rotated dims per quantisation group (128, or 64 and 32 for grouped pages)
 hipError_t launch_decode_int2(const LayerShape& L, const void* q, const void* rot_k, const void* pool,
                               const int32_t* block_table, int max_pages, const int32_t* hist_len,
                               int batch, float sm_scale, int n_splits, const PartialsView& out,
-                              hipStream_t stream);
+                              hipStream_t stream, int group = 128);
 
 hipError_t launch_decode_bf16(const LayerShape& L, const void* q, const void* k_win, const void* v_win,
                               const int32_t* win_len, int batch, float sm_scale, int n_win_splits,
@@ -97,6 +98,7 @@ struct StepArgs {
   int batch, n_q, n_kv, gq, window, n_splits, n_wsplits, n_groups;
   int win_groups;  // workgroups per (window split, KV head, request), each for gq / win_groups heads
   int nqt;         // query tokens per request; n_q and gq count virtual heads (token, head)
+  int n_qgroups = 1;  // quantisation groups per vector of the pool's pages: 1, 2 or 4
   double scale_log2;
   PartialsView hist;  // INT2 partials and the query tail
   PartialsView win;   // window partials

@@ -140,15 +140,6 @@ hipError_t launch_decode_grouped(const LayerShape& L, int group, const void* q, 
                                  float sm_scale, int n_splits, const PartialsView& out, hipStream_t stream);
 }  // namespace oscar
 
-namespace {
-// Workspace of oscar_decode_step_grouped: the INT2 partials, then (from the next multiple of
-// 256 bytes) the window partials.
-size_t grouped_step_workspace(const oscar_layer_desc* d, int batch, int n_splits) {
-  const size_t a = oscar::partials_bytes(batch, d->n_q_heads, n_splits);
-  return (a + 255) / 256 * 256 + oscar::partials_bytes(batch, d->n_q_heads, window_splits_of(d));
-}
-}  // namespace
-
 extern "C" {
 
 int32_t oscar_version(void) { return 100; }
@@ -195,7 +186,9 @@ int32_t oscar_default_splits(const oscar_layer_desc* desc, int32_t batch, int32_
   if (check_desc_grouped(desc) != OSCAR_OK || batch <= 0) return 1;
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
   const int gq = desc->n_q_heads / desc->n_kv_heads;
-  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > 8 ? gq / 8 : 1);
+  // query heads per INT2 workgroup: 8, or 4 over grouped pages
+  const int tile = desc->group_size == 128 ? 8 : 4;
+  const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gq > tile ? gq / tile : 1);
   // small grids: one 8-wave workgroup per compute unit (at most 256 workgroups, which the
   // fused decode runs with 8 waves); larger ones: about two 4-wave workgroups per unit
   long long s, by_pages;
@@ -340,7 +333,6 @@ int32_t oscar_decode_dense_bf16(const oscar_layer_desc* desc, const void* q, con
 
 size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits) {
   if (check_desc_grouped(desc) != OSCAR_OK || batch < 0 || n_splits < 0) return 0;
-  if (desc->group_size != 128) return grouped_step_workspace(desc, batch, n_splits);
   return oscar::step_workspace_bytes(batch, desc->n_q_heads, desc->n_kv_heads, n_splits, window_splits_of(desc));
 }
 
@@ -351,8 +343,8 @@ namespace {
 // Checks shared by the two halves of the decode step; fills the workspace views. With nqt
 // query tokens per request the heads are virtual (token, head) pairs: nqt n_q of them.
 int32_t check_step_common(const oscar_layer_desc* desc, int32_t batch, int32_t n_splits, void* workspace,
-                          size_t workspace_bytes, oscar::StepArgs& a, int nqt = 1) {
-  int32_t st = check_desc_impl(desc);
+                          size_t workspace_bytes, oscar::StepArgs& a, int nqt = 1, bool grouped = false) {
+  int32_t st = grouped ? check_desc_grouped(desc) : check_desc_impl(desc);
   if (st != OSCAR_OK) return st;
   if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
@@ -377,6 +369,7 @@ int32_t check_step_common(const oscar_layer_desc* desc, int32_t batch, int32_t n
   a.n_splits = n_splits;
   a.n_wsplits = ws;
   a.n_groups = 1;
+  a.n_qgroups = 128 / desc->group_size;
   a.hist = oscar::partials_view(base, batch, n_qv, n_splits);
   a.win = oscar::partials_view(base + hist_bytes, batch, n_qv, ws);
   a.counters = reinterpret_cast<int*>(base + hist_bytes + win_bytes);
@@ -387,9 +380,9 @@ int32_t prepare_impl(const oscar_layer_desc* desc, const void* k_src, const void
                      const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k, const float* clip_v,
                      const void* q, const void* rot_k, const void* rot_v, const uint32_t* codebook, void* pool,
                      const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale,
-                     int32_t n_splits, void* workspace, size_t workspace_bytes, void* stream) {
+                     int32_t n_splits, void* workspace, size_t workspace_bytes, void* stream, bool grouped = false) {
   oscar::StepArgs a;
-  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
+  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a, 1, grouped);
   if (st != OSCAR_OK) return st;
   if (n < 0) return fail(OSCAR_ERR_INVALID_ARG, "n %d < 0", n);
   if (n > 0 && (!k_src || !v_src || !dst_page || !dst_slot || !clip_k || !clip_v || !rot_v || !pool))
@@ -421,9 +414,10 @@ int32_t prepare_impl(const oscar_layer_desc* desc, const void* k_src, const void
 
 int32_t attend_impl(const oscar_layer_desc* desc, const void* rot_v, const uint32_t* codebook, const void* pool,
                     const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, int32_t batch,
-                    int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+                    int32_t n_splits, void* workspace, size_t workspace_bytes, float* out, void* stream,
+                    bool grouped = false) {
   oscar::StepArgs a;
-  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
+  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a, 1, grouped);
   if (st != OSCAR_OK) return st;
   if (int32_t e = check_pages(max_pages, n_splits)) return e;
   if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
@@ -442,18 +436,18 @@ int32_t step_impl(const oscar_layer_desc* desc, const void* k_src, const void* v
                   const void* q, const void* rot_k, const void* rot_v, const uint32_t* codebook, void* pool,
                   const int32_t* block_table, int32_t max_pages, const int32_t* hist_len, const void* k_win,
                   const void* v_win, const int32_t* win_len, int32_t batch, float sm_scale, int32_t n_splits,
-                  void* workspace, size_t workspace_bytes, float* out, void* stream) {
+                  void* workspace, size_t workspace_bytes, float* out, void* stream, bool grouped = false) {
   // the attend half's arguments are checked before anything is enqueued
   oscar::StepArgs a;
-  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a);
+  int32_t st = check_step_common(desc, batch, n_splits, workspace, workspace_bytes, a, 1, grouped);
   if (st != OSCAR_OK) return st;
   if (int32_t e = check_pages(max_pages, n_splits)) return e;
   if (!rot_v || !pool || !block_table || !hist_len || !out) return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
   st = prepare_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, codebook, pool, k_win,
-                    v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, stream);
+                    v_win, win_len, batch, sm_scale, n_splits, workspace, workspace_bytes, stream, grouped);
   if (st != OSCAR_OK) return st;
   return attend_impl(desc, rot_v, codebook, pool, block_table, max_pages, hist_len, batch, n_splits, workspace,
-                     workspace_bytes, out, stream);
+                     workspace_bytes, out, stream, grouped);
 }
 
 }  // namespace
@@ -585,6 +579,7 @@ int32_t step_append_impl(const oscar_layer_desc* desc, const void* k_src, const 
   a.n_kv = L.n_kv;
   a.gq = L.gq;
   a.nqt = 1;
+  a.n_qgroups = 1;
   a.window = L.window;
   a.n_splits = n_splits;
   a.n_wsplits = ws;
@@ -936,6 +931,7 @@ int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, c
   if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
   if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(rot_k) % 16 != 0)
     return fail(OSCAR_ERR_INVALID_ARG, "q and rot_k must be 16-byte aligned");
+  if (int32_t e = check_pages(max_pages, n_splits)) return e;
   const size_t need = oscar::partials_bytes(batch, desc->n_q_heads, n_splits);
   if (partials_bytes < need)
     return fail(OSCAR_ERR_WORKSPACE, "partials workspace %zu < %zu bytes", partials_bytes, need);
@@ -954,44 +950,9 @@ int32_t oscar_decode_step_grouped(const oscar_layer_desc* desc, const void* k_sr
                                   const void* k_win, const void* v_win, const int32_t* win_len, int32_t batch,
                                   float sm_scale, int32_t n_splits, void* workspace, size_t workspace_bytes, float* out,
                                   void* stream) {
-  int32_t st = check_desc_grouped(desc);
-  if (st != OSCAR_OK) return st;
-  if (batch <= 0) return fail(OSCAR_ERR_INVALID_ARG, "batch %d <= 0", batch);
-  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch %d > 65535", batch);
-  if (n_splits <= 0 || n_splits > 65535) return fail(OSCAR_ERR_INVALID_ARG, "n_splits %d out of [1, 65535]", n_splits);
-  if (max_pages <= 0) return fail(OSCAR_ERR_INVALID_ARG, "max_pages %d <= 0", max_pages);
-  if (n < 0) return fail(OSCAR_ERR_INVALID_ARG, "n %d < 0", n);
-  if (n > 0 && (!k_src || !v_src || !dst_page || !dst_slot || !clip_k || !clip_v))
-    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
-  if (!q || !rot_k || !rot_v || !pool || !block_table || !hist_len || !k_win || !v_win || !win_len || !workspace || !out)
-    return fail(OSCAR_ERR_INVALID_ARG, "null pointer argument");
-  if (2LL * n * desc->n_kv_heads > 0x7FFFFFFFLL)
-    return fail(OSCAR_ERR_UNSUPPORTED, "2 * n * n_kv_heads exceeds the grid limit");
-  if (!(sm_scale > 0.0f) || sm_scale == INFINITY) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
-  if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(rot_k) % 16 != 0)
-    return fail(OSCAR_ERR_INVALID_ARG, "q and rot_k must be 16-byte aligned");
-  const size_t need = grouped_step_workspace(desc, batch, n_splits);
-  if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-  const oscar::LayerShape L = shape_of(desc);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int ws = window_splits_of(desc);
-  char* base = static_cast<char*>(workspace);
-  const size_t win_off = (oscar::partials_bytes(batch, desc->n_q_heads, n_splits) + 255) / 256 * 256;
-  const oscar::PartialsView h = oscar::partials_view(base, batch, desc->n_q_heads, n_splits);
-  const oscar::PartialsView w = oscar::partials_view(base + win_off, batch, desc->n_q_heads, ws);
-  if (n > 0) {
-    st = hip_status(oscar::launch_demote_grouped(desc->n_kv_heads, desc->group_size, k_src, v_src, n, dst_page,
-                                                 dst_slot, rot_k, rot_v, clip_k, clip_v, pool, s),
-                    "grouped demote launch");
-    if (st != OSCAR_OK) return st;
-  }
-  st = hip_status(oscar::launch_decode_bf16(L, q, k_win, v_win, win_len, batch, sm_scale, ws, w, s), "window pass launch");
-  if (st != OSCAR_OK) return st;
-  st = hip_status(oscar::launch_decode_grouped(L, desc->group_size, q, rot_k, pool, block_table, max_pages, hist_len,
-                                               batch, sm_scale, n_splits, h, s),
-                  "grouped decode launch");
-  if (st != OSCAR_OK) return st;
-  return hip_status(oscar::launch_merge(L, h, n_splits, w, ws, rot_v, out, batch, s), "merge launch");
+  return step_impl(desc, k_src, v_src, n, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, nullptr, pool,
+                   block_table, max_pages, hist_len, k_win, v_win, win_len, batch, sm_scale, n_splits, workspace,
+                   workspace_bytes, out, stream, true);
 }
 
 }  // extern "C"

@@ -21,6 +21,7 @@
 // else by the merge. No workgroup ever waits for another.
 
 #include "demote_pass.h"
+#include "grouped_pass.h"
 #include "int2_pass.h"
 #include "merge_pass.h"
 #include "window_pass.h"
@@ -30,14 +31,20 @@ namespace {
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int GQW>
+// NG: quantisation groups per vector of the pool's pages (the demotion rows' format)
+template <int GQW, int NG>
 __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
-  __shared__ __align__(16) unsigned char smem[cmax(cmax(demote::kSmemBytes, window::window_smem_bytes<GQW>()),
+  __shared__ __align__(16) unsigned char smem[cmax(cmax(cmax(demote::kSmemBytes, demote::kGroupedSmemBytes),
+                                                        window::window_smem_bytes<GQW>()),
                                                    int2::kQprepSmem)];
   int id = blockIdx.x;
   if (id < a.n_dem_items) {
-    demote::demote_row(smem, id, a.k_src, a.v_src, a.n_kv, a.append ? nullptr : a.dst_page, a.dst_slot, a.rot_k,
-                       a.rot_v, a.clip_k, a.clip_v, a.pool, a.codebook, a.block_table, a.max_pages, a.hist_len);
+    if constexpr (NG == 1)
+      demote::demote_row(smem, id, a.k_src, a.v_src, a.n_kv, a.append ? nullptr : a.dst_page, a.dst_slot, a.rot_k,
+                         a.rot_v, a.clip_k, a.clip_v, a.pool, a.codebook, a.block_table, a.max_pages, a.hist_len);
+    else
+      demote::demote_grouped_row<NG>(smem, id, a.k_src, a.v_src, a.n_kv, a.dst_page, a.dst_slot, a.rot_k, a.rot_v,
+                                     a.clip_k, a.clip_v, a.pool);
     return;
   }
   id -= a.n_dem_items;
@@ -78,20 +85,20 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
 }
 
 // GQ query heads per workgroup, GQT per KV head (GQT = GQ n_groups), NW waves; CB: the
-// codebook variant
-template <int GQ, int GQT, int NW, bool CB>
+// codebook variant; NG quantisation groups per vector
+template <int GQ, int GQT, int NW, bool CB, int NG = 1>
 __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // the INT2 pass and the merge use the same LDS one after the other
-  __shared__ __align__(16) unsigned char smem[cmax(int2::int2_smem_bytes<GQ, NW>(), merge::smem_bytes<GQT, NW>())];
+  __shared__ __align__(16) unsigned char smem[cmax(int2::int2_smem_bytes<GQ, NW, NG>(), merge::smem_bytes<GQT, NW>())];
   __shared__ int ticket_s;
   // 8-wave workgroups (a grid of at most one per compute unit) un-rotate their own value
   // sums, so the merge after the last ticket is a weighted sum; 4-wave ones, several to a
   // compute unit, leave that to the merge and keep the R_V fragments out of the page loop
   constexpr bool kUnrot = NW == 8;
-  int2::int2_split<GQ, true, NW, CB, kUnrot>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table,
-                                             a.max_pages, a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits,
-                                             a.hist.qlimb, a.hist.qscal, a.hist.m, a.hist.l, a.hist.acc, a.codebook,
-                                             int2::InlineQuery(), a.rot_v);
+  int2::int2_split<GQ, true, NW, CB, kUnrot, NG>(smem, blockIdx.x, blockIdx.y, blockIdx.z, a.pool, a.block_table,
+                                                 a.max_pages, a.hist_len, a.n_q, a.n_kv, a.n_groups, a.n_splits,
+                                                 a.hist.qlimb, a.hist.qscal, a.hist.m, a.hist.l, a.hist.acc,
+                                                 a.codebook, int2::InlineQuery(), a.rot_v);
   const int kv = blockIdx.y / a.n_groups;
   const int b = blockIdx.z;
   // the partials went out as agent-scope stores: once each thread's stores have completed
@@ -117,32 +124,57 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
 // to four workgroups: each then has a fraction of the value sums and stores, and the batch-1
 // window pass, the longest item of the launch, ends sooner. The K and V rows it reads again
 // come from L2.
-template <int GQT>
+template <int GQT, int NG>
 hipError_t launch_prep(StepArgs a, hipStream_t stream) {
   const long long base = static_cast<long long>(a.n_wsplits) * a.n_kv * a.batch;
   a.win_groups = 1;
   while (a.win_groups < 4 && GQT % (2 * a.win_groups) == 0 && base * 2 * a.win_groups <= 256) a.win_groups *= 2;
   const unsigned n_prep =
       static_cast<unsigned>(a.n_dem_items + base * a.win_groups + static_cast<long long>(a.n_q) * a.batch);
-  hipLaunchKernelGGL(prep_kernel<GQT>, dim3(n_prep), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prep_kernel<GQT, NG>), dim3(n_prep), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 // Up to 256 workgroups (one per CU) run with 8 waves each, so few splits still give
 // every SIMD two waves; larger grids use 4 waves per workgroup.
-template <int GQ, int GQT, bool CB>
+template <int GQ, int GQT, bool CB, int NG = 1>
 hipError_t launch_main_cb(const StepArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_splits, a.n_kv * a.n_groups, a.batch);
   if (static_cast<long long>(grid.x) * grid.y * grid.z <= 256)
-    hipLaunchKernelGGL((main_kernel<GQ, GQT, 8, CB>), grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((main_kernel<GQ, GQT, 8, CB, NG>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL((main_kernel<GQ, GQT, 4, CB>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((main_kernel<GQ, GQT, 4, CB, NG>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int GQ, int GQT>
 hipError_t launch_main(const StepArgs& a, hipStream_t stream) {
   return a.codebook ? launch_main_cb<GQ, GQT, true>(a, stream) : launch_main_cb<GQ, GQT, false>(a, stream);
+}
+
+// grouped pages: head tiles of four (the per-group metadata leaves no registers for two)
+template <int NG>
+hipError_t launch_main_grouped(StepArgs a, hipStream_t stream) {
+  switch (a.gq) {
+    case 1: a.n_groups = 1; return launch_main_cb<1, 1, false, NG>(a, stream);
+    case 2: a.n_groups = 1; return launch_main_cb<2, 2, false, NG>(a, stream);
+    case 4: a.n_groups = 1; return launch_main_cb<4, 4, false, NG>(a, stream);
+    case 8: a.n_groups = 2; return launch_main_cb<4, 8, false, NG>(a, stream);
+    case 16: a.n_groups = 4; return launch_main_cb<4, 16, false, NG>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int NG>
+hipError_t launch_prep_ng(const StepArgs& a, hipStream_t stream) {
+  switch (a.gq) {
+    case 1: return launch_prep<1, NG>(a, stream);
+    case 2: return launch_prep<2, NG>(a, stream);
+    case 4: return launch_prep<4, NG>(a, stream);
+    case 8: return launch_prep<8, NG>(a, stream);
+    case 16: return launch_prep<16, NG>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // The one-launch step (and the one-launch multi-query decode: nqt query tokens per request
@@ -238,17 +270,18 @@ hipError_t launch_append(const StepArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prepare(StepArgs a, hipStream_t stream) {
-  switch (a.gq) {
-    case 1: return launch_prep<1>(a, stream);
-    case 2: return launch_prep<2>(a, stream);
-    case 4: return launch_prep<4>(a, stream);
-    case 8: return launch_prep<8>(a, stream);
-    case 16: return launch_prep<16>(a, stream);
+  switch (a.n_qgroups) {
+    case 1: return launch_prep_ng<1>(a, stream);
+    case 2: return launch_prep_ng<2>(a, stream);
+    case 4: return launch_prep_ng<4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_attend(StepArgs a, hipStream_t stream) {
+  if (a.n_qgroups == 2) return a.codebook ? hipErrorInvalidValue : launch_main_grouped<2>(a, stream);
+  if (a.n_qgroups == 4) return a.codebook ? hipErrorInvalidValue : launch_main_grouped<4>(a, stream);
+  if (a.n_qgroups != 1) return hipErrorInvalidValue;
   switch (a.gq) {
     case 1: a.n_groups = 1; return launch_main<1, 1>(a, stream);
     case 2: a.n_groups = 1; return launch_main<2, 2>(a, stream);

@@ -534,21 +534,28 @@ int32_t oscar_demote_grouped(const oscar_layer_desc* desc, const void* k_src, co
 
 /* INT2 history pass over grouped pages: each code dequantises with its own group's scale
  * and zero point. Arguments as oscar_decode_int2, with partials in the same format (so
- * oscar_decode_bf16 and oscar_merge complete the decode); there is no per-split page
- * limit; q and rot_k must be 16-byte aligned (else OSCAR_ERR_INVALID_ARG). Runs on the
- * vector ALU in fp32; about four pages per split suit it. */
+ * oscar_decode_bf16 and oscar_merge complete the decode), the same per-split page limit
+ * (ceil(max_pages / n_splits) <= 8192, else OSCAR_ERR_UNSUPPORTED); q and rot_k must be
+ * 16-byte aligned (else OSCAR_ERR_INVALID_ARG). The matrix-core pass of oscar_decode_int2
+ * with one K product per group (the query's limbs masked to the group's dims), the
+ * per-group V scales folded into per-group softmax weights and per-group zero-point sums;
+ * query heads in tiles of four. Its scores take the 22-bit fixed-point query in both terms
+ * of the fold (qsc Q . (s c + z) per group), where the one-group pass takes the exact
+ * sum of the rotated query for the zero-point term. */
 int32_t oscar_decode_int2_grouped(const oscar_layer_desc* desc, const void* q, const void* rot_k, const void* pool,
                                   const int32_t* block_table, int32_t max_pages, const int32_t* hist_len,
                                   int32_t batch, float sm_scale, int32_t n_splits, void* partials,
                                   size_t partials_bytes, void* stream);
 
-/* One decode step over grouped pages: oscar_demote_grouped of the n tokens, then
- * oscar_decode_bf16, oscar_decode_int2_grouped and oscar_merge, in four launches on `stream`
- * (the same result as those calls in that order). Arguments as oscar_decode_step, with
- * n_splits in 1..65535 and no per-split page limit; workspace of at least
- * oscar_decode_workspace_bytes(desc, batch, n_splits) bytes (for a grouped desc: the INT2
- * partials, then from the next multiple of 256 bytes the window partials), owned by the
- * caller, no initialisation needed. q and rot_k 16-byte aligned. */
+/* One decode step over grouped pages in two launches on `stream`, as oscar_decode_step:
+ * prepare (oscar_demote_grouped's rows for the n tokens, the BF16 window pass, the query
+ * preparation), then attend (the grouped INT2 pass of oscar_decode_int2_grouped, each
+ * split writing its partial, the last arrival per (request, KV head) merging). The result
+ * is that of oscar_demote_grouped, oscar_decode_bf16, oscar_decode_int2_grouped and
+ * oscar_merge in that order. Arguments, limits (n_splits 1..256, ceil(max_pages /
+ * n_splits) <= 8192), errors and workspace (oscar_decode_workspace_bytes(desc, batch,
+ * n_splits) bytes, the same size as for a one-group desc, no initialisation needed) as
+ * oscar_decode_step. */
 int32_t oscar_decode_step_grouped(const oscar_layer_desc* desc, const void* k_src, const void* v_src, int32_t n,
                                   const int32_t* dst_page, const int32_t* dst_slot, const float* clip_k,
                                   const float* clip_v, const void* q, const void* rot_k, const void* rot_v, void* pool,

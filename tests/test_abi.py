@@ -106,9 +106,9 @@ def test_grouped_descriptors(lib, group):
     st = lib.oscar_decode_step_grouped
     args = [FAKE, FAKE, 0, None, None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, 1, 0.08,
             4, FAKE]
+    # the grouped step runs the one-group step's two launches: the same workspace
     wneed = L.oscar_decode_workspace_bytes(d, 1, 4)
-    a256 = -(-L.oscar_partials_bytes(d, 1, 4) // 256) * 256
-    assert wneed == a256 + L.oscar_partials_bytes(d, 1, L.oscar_window_splits(d))
+    assert wneed == L.oscar_decode_workspace_bytes(one, 1, 4)
     assert st(r, *args, wneed - 1, FAKE, None) == L.OSCAR_ERR_WORKSPACE
     assert st(r, FAKE, FAKE, 2, None, FAKE, FAKE, FAKE, *args[7:], wneed, FAKE, None) == L.OSCAR_ERR_INVALID_ARG
     assert st(r, *args[:7], None, *args[8:], wneed, FAKE, None) == L.OSCAR_ERR_INVALID_ARG

@@ -221,9 +221,10 @@ def test_one_group_grouped_entries_match_the_one_group_path():
 @pytest.mark.parametrize("group", [32, 64])
 def test_grouped_full_size_sampled(group):
     """The grouped path at the 32K workload's real size (32768-token context, 32 query heads,
-    8 KV heads): every history token demoted on the GPU, then decoded at about four pages
-    per split (the split count the benchmark settles on); every KV head compared with the
-    oracle (pool contents and the outputs of its query heads)."""
+    8 KV heads): every history token demoted on the GPU, then decoded in three launches at
+    about four pages per split and by the two-launch grouped step at the default split count
+    (the benchmark's); every KV head compared with the oracle (pool contents and the outputs
+    of its query heads)."""
     from test_gpu_parity import _demote_all
 
     w = synth.workload(2)
@@ -240,9 +241,15 @@ def test_grouped_full_size_sampled(group):
         j = np.arange(n)
         say("grouped full size", w.name, "group", group, "b", b, "tokens", n)
         _demote_all(c, w, b, table[b, j // 64], j % 64, np.stack(ks, 1), np.stack(vs, 1))
+    from bit_kv_cache_oscar_amd import oscar_default_splits
+
     s = -(-(-(-int(w.hist_lens.max()) // 64)) // 4)
     c.set_splits(s)
     got = c.decode(queries(w), w.sm_scale).cpu().numpy()
+    # the two-launch grouped step (nothing demoted) at the default split count
+    c.set_splits(oscar_default_splits(c.desc, w.batch, int(w.hist_lens.max())))
+    say("grouped full size step", w.name, "group", group, "splits", c.n_splits)
+    got_step = c.step(None, None, None, None, queries(w), w.sm_scale).cpu().numpy()
     pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, ogroups.head_block_bytes(group))
     for b, kv in [(0, kv) for kv in range(w.n_kv_heads)]:
         say("grouped full size sample", w.name, "group", group, "b", b, "kv", kv, "splits", s)
@@ -254,6 +261,7 @@ def test_grouped_full_size_sampled(group):
         for h in range(kv * w.gq, (kv + 1) * w.gq):
             ref = oatt.decode_head(q[h], rk[kv], rv[kv], wk[kv], wv[kv], ref_hist, w.sm_scale)
             assert_close(got[b, h], ref, f"{w.name} g{group} b{b} h{h}")
+            assert_close(got_step[b, h], ref, f"{w.name} g{group} step b{b} h{h}")
 
 
 @pytest.mark.parametrize("case,group", [("c2-4k", 32), ("c5-gq8", 64), ("gq16", 32)])
