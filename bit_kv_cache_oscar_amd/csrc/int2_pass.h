@@ -621,16 +621,26 @@ __device__ __forceinline__ void int2_split(
   // wave-private P'-limb rows: row (mt NG + group) 16 + 4 g + l; rows with l == 3 hold
   // constant ones
   unsigned char* pl = scratch_s + wave * (MT * NG * 16 * kPRow);
-  // wave-private flushed sums: [mt][k][lane], k < 8: dim tile k, 8: l, 9 + group: sum p z
+  // flushed sums per lane and tile: k < 8: dim tile k, 8: l, 9 + group: sum p z. One tile of
+  // one or two groups keeps them in registers; otherwise they live in wave-private LDS,
+  // [mt][k][lane]
+  constexpr bool kFlReg = MT == 1 && NG <= 2;
+  float flr[kFlReg ? kFl : 1];
   float* fl = reinterpret_cast<float*>(scratch_s + kPBytes) + wave * (MT * kFl * 64) + lane;
+#pragma unroll
+  for (int k = 0; k < (kFlReg ? kFl : 1); ++k) flr[k] = 0.f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
       *reinterpret_cast<uint32_t*>(pl + ((mt * NG + g) * 16 + 4 * G + 3) * kPRow + 4 * n) = 0x01010101u;
+    if constexpr (!kFlReg) {
 #pragma unroll
-    for (int k = 0; k < kFl; ++k) fl[(mt * kFl + k) * 64] = 0.f;
+      for (int k = 0; k < kFl; ++k) fl[(mt * kFl + k) * 64] = 0.f;
+    }
   }
+  // flushed value k of tile mt
+  auto flv = [&](int mt, int k) -> float& { return kFlReg ? flr[k] : fl[(mt * kFl + k) * 64]; };
 
   // the centring seed and the offset weight of each (tile, group): -2 sum Q and sig with
   // one group; with groups, from the group sums S_g of the fixed-point query (below)
@@ -648,12 +658,11 @@ __device__ __forceinline__ void int2_split(
       const float alpha = st.m[mt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m[mt] - m_new);
       const float down = pow2f(-E);
       const float down_v = pow2f(1 - E);
-      float* f = fl + mt * kFl * 64;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) f[dt * 64] = fmaf(v_combo(st.acci[mt][dt]), down_v, f[dt * 64]) * alpha;
-      f[8 * 64] = fmaf(st.lq[mt], down, f[8 * 64]) * alpha;
+      for (int dt = 0; dt < 8; ++dt) flv(mt, dt) = fmaf(v_combo(st.acci[mt][dt]), down_v, flv(mt, dt)) * alpha;
+      flv(mt, 8) = fmaf(st.lq[mt], down, flv(mt, 8)) * alpha;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) f[(9 + g) * 64] = fmaf(st.zq[mt][g], down, f[(9 + g) * 64]) * alpha;
+      for (int g = 0; g < NG; ++g) flv(mt, 9 + g) = fmaf(st.zq[mt][g], down, flv(mt, 9 + g)) * alpha;
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.acci[mt][dt] = i32x4{0, 0, 0, 0};
@@ -948,10 +957,10 @@ __device__ __forceinline__ void int2_split(
   for (int mt = 0; mt < MT; ++mt) {
     if (!fresh) flush_tile(mt, st.m[mt]);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) accf[mt][dt] = fl[(mt * kFl + dt) * 64];
-    lf[mt] = fl[(mt * kFl + 8) * 64];
+    for (int dt = 0; dt < 8; ++dt) accf[mt][dt] = flv(mt, dt);
+    lf[mt] = flv(mt, 8);
 #pragma unroll
-    for (int q = 0; q < NG; ++q) zf[mt][q] = fl[(mt * kFl + 9 + q) * 64];
+    for (int q = 0; q < NG; ++q) zf[mt][q] = flv(mt, 9 + q);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
