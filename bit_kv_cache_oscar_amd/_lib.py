@@ -6,6 +6,7 @@ There is no fallback: if the library is missing, every call fails loudly."""
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from ctypes import POINTER, byref, c_float, c_int32, c_size_t, c_void_p
 
@@ -154,6 +155,15 @@ def _check(status: int):
         raise OscarError(status, lib().oscar_last_error().decode())
 
 
+def _run(prepare: bool, fn, *args):
+    """fn(*args), its status checked. With `prepare`, that call is returned as a zero-argument
+    callable instead: the arguments are validated and marshalled once, and each call of the
+    callable is the C-ABI call alone (the tensors must stay alive and in place)."""
+    if prepare:
+        return functools.partial(_run, False, fn, *args)
+    _check(fn(*args))
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -290,7 +300,7 @@ def oscar_demote_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot
 
 
 def oscar_decode_int2(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm_scale: float, n_splits: int,
-                      partials, stream=None):
+                      partials, stream=None, prepare=False):
     """INT2 history pass; q [B, Hq, 128] bf16, block_table [B, max_pages] int32,
     hist_len [B] int32; partials from oscar_partials_bytes(desc, B, n_splits). A desc with
     group_size 64 or 32 reads grouped pages (oscar_decode_int2_grouped)."""
@@ -306,12 +316,13 @@ def oscar_decode_int2(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm
     _need(partials.is_cuda and partials.is_contiguous(), "partials must be a contiguous device tensor")
     nbytes = partials.numel() * partials.element_size()
     fn = lib().oscar_decode_int2 if desc.group_size == 128 else lib().oscar_decode_int2_grouped
-    _check(fn(byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool), _ptr(block_table),
-                                   int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale),
-                                   int(n_splits), _ptr(partials), nbytes, _stream(stream)))
+    return _run(prepare, fn, byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool), _ptr(block_table),
+                int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale), int(n_splits), _ptr(partials),
+                nbytes, _stream(stream))
 
 
-def oscar_decode_bf16(desc: LayerDesc, q, k_win, v_win, win_len, sm_scale: float, win_partials, stream=None):
+def oscar_decode_bf16(desc: LayerDesc, q, k_win, v_win, win_len, sm_scale: float, win_partials, stream=None,
+                      prepare=False):
     """BF16 window pass; k_win/v_win [B, Hkv, 320, 128] bf16, win_len [B] int32."""
     batch = int(q.shape[0])
     _device16(q, "q")
@@ -323,8 +334,8 @@ def oscar_decode_bf16(desc: LayerDesc, q, k_win, v_win, win_len, sm_scale: float
     _device_i32(win_len, "win_len", batch)
     _need(win_partials.is_cuda and win_partials.is_contiguous(), "win_partials must be a contiguous device tensor")
     nbytes = win_partials.numel() * win_partials.element_size()
-    _check(lib().oscar_decode_bf16(byref(desc), _ptr(q), _ptr(k_win), _ptr(v_win), _ptr(win_len), batch,
-                                   float(sm_scale), _ptr(win_partials), nbytes, _stream(stream)))
+    return _run(prepare, lib().oscar_decode_bf16, byref(desc), _ptr(q), _ptr(k_win), _ptr(v_win), _ptr(win_len),
+                batch, float(sm_scale), _ptr(win_partials), nbytes, _stream(stream))
 
 
 def oscar_dense_workspace_bytes(desc: LayerDesc, batch: int, capacity: int) -> int:
@@ -391,7 +402,7 @@ def oscar_read_probe(buf, out, stream=None):
     _check(lib().oscar_read_probe(_ptr(buf), nbytes, _ptr(out), _stream(stream)))
 
 
-def oscar_merge(desc: LayerDesc, partials, n_splits: int, win_partials, rot_v, out, stream=None):
+def oscar_merge(desc: LayerDesc, partials, n_splits: int, win_partials, rot_v, out, stream=None, prepare=False):
     """Join both segments into out [B, Hq, 128] float32."""
     import torch
 
@@ -404,8 +415,8 @@ def oscar_merge(desc: LayerDesc, partials, n_splits: int, win_partials, rot_v, o
     _need(partials.numel() * partials.element_size() >= need, "partials smaller than oscar_partials_bytes")
     wneed = oscar_partials_bytes(desc, batch, oscar_window_splits(desc))
     _need(win_partials.numel() * win_partials.element_size() >= wneed, "win_partials too small")
-    _check(lib().oscar_merge(byref(desc), _ptr(partials), int(n_splits), _ptr(win_partials), _ptr(rot_v),
-                             _ptr(out), batch, _stream(stream)))
+    return _run(prepare, lib().oscar_merge, byref(desc), _ptr(partials), int(n_splits), _ptr(win_partials),
+                _ptr(rot_v), _ptr(out), batch, _stream(stream))
 
 
 def _check_decode_args(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
@@ -458,7 +469,7 @@ def oscar_decode_codebook(desc: LayerDesc, q, rot_k, rot_v, codebook, pool, bloc
 
 
 def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len,
-                       sm_scale: float, n_splits: int, workspace, out, stream=None, codebook=None):
+                       sm_scale: float, n_splits: int, workspace, out, stream=None, codebook=None, prepare=False):
     """Decode attention for T query tokens per request (q [B, T, Hq, 128] bf16, out the same
     shape in float32; token t sees the window up to its own position), in one launch when the grid fits the chip
     at once (oscar_decode_multi_splits), else two; workspace from
@@ -470,11 +481,10 @@ def oscar_decode_multi(desc: LayerDesc, q, rot_k, rot_v, pool, block_table, hist
     rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win),
             _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
     if codebook is None:
-        _check(lib().oscar_decode_multi(byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v), *rest))
-    else:
-        _check_codebook(desc, codebook)
-        _check(lib().oscar_decode_multi_codebook(byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v),
-                                                 _ptr(codebook), *rest))
+        return _run(prepare, lib().oscar_decode_multi, byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v), *rest)
+    _check_codebook(desc, codebook)
+    return _run(prepare, lib().oscar_decode_multi_codebook, byref(desc), _ptr(q), n_tok, _ptr(rot_k), _ptr(rot_v),
+                _ptr(codebook), *rest)
 
 
 def oscar_decode_multi_codebook(desc: LayerDesc, q, rot_k, rot_v, codebook, pool, block_table, hist_len, k_win, v_win,
@@ -486,7 +496,7 @@ def oscar_decode_multi_codebook(desc: LayerDesc, q, rot_k, rot_v, codebook, pool
 
 def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool,
                       block_table, hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace, out,
-                      stream=None, codebook=None):
+                      stream=None, codebook=None, prepare=False):
     """Demote n tokens (k_src/v_src [n, Hkv, 128] bf16, n may be 0) and decode, in two launches.
     With `codebook` this is oscar_decode_step_codebook; with a desc of group_size 64 or 32,
     oscar_decode_step_grouped (four launches)."""
@@ -511,12 +521,11 @@ def oscar_decode_step(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k,
             _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
     if desc.group_size != 128:
         _need(codebook is None, "codebooks are defined for one group per vector")
-        _check(lib().oscar_decode_step_grouped(byref(desc), *head, *rest))
-    elif codebook is None:
-        _check(lib().oscar_decode_step(byref(desc), *head, *rest))
-    else:
-        _check_codebook(desc, codebook)
-        _check(lib().oscar_decode_step_codebook(byref(desc), *head, _ptr(codebook), *rest))
+        return _run(prepare, lib().oscar_decode_step_grouped, byref(desc), *head, *rest)
+    if codebook is None:
+        return _run(prepare, lib().oscar_decode_step, byref(desc), *head, *rest)
+    _check_codebook(desc, codebook)
+    return _run(prepare, lib().oscar_decode_step_codebook, byref(desc), *head, _ptr(codebook), *rest)
 
 
 def oscar_decode_step_append_workspace_bytes(desc: LayerDesc, batch: int, n_splits: int) -> int:
@@ -540,10 +549,11 @@ def oscar_decode_step_append_launches(desc: LayerDesc, batch: int, n_splits: int
 
 def oscar_decode_step_append(desc: LayerDesc, k_src, v_src, clip_k, clip_v, q, rot_k, rot_v, pool, block_table,
                              hist_len, k_win, v_win, win_len, sm_scale: float, n_splits: int, workspace, out,
-                             stream=None, codebook=None):
+                             stream=None, codebook=None, prepare=False):
     """One decode step in one launch: token b of k_src/v_src [batch, n_kv_heads, 128] bf16
     (None: nothing) becomes history token hist_len[b] - 1 of request b, then decode. The
-    workspace's arrival counters must be zero before the first call (zero-fill it once)."""
+    workspace's arrival counters must be zero before the first call (zero-fill it once).
+    With `prepare`, returns the call as a callable (see _run)."""
     _need(desc.group_size == 128, "the one-launch step reads one-group pages")
     batch = int(q.shape[0])
     _check_decode_args(desc, q, rot_k, rot_v, pool, block_table, hist_len, k_win, v_win, win_len, n_splits,
@@ -566,10 +576,9 @@ def oscar_decode_step_append(desc: LayerDesc, k_src, v_src, clip_k, clip_v, q, r
     rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), _ptr(k_win), _ptr(v_win),
             _ptr(win_len), batch, float(sm_scale), int(n_splits), _ptr(workspace), nbytes, _ptr(out), _stream(stream))
     if codebook is None:
-        _check(lib().oscar_decode_step_append(byref(desc), *head, *rest))
-    else:
-        _check_codebook(desc, codebook)
-        _check(lib().oscar_decode_step_append_codebook(byref(desc), *head, _ptr(codebook), *rest))
+        return _run(prepare, lib().oscar_decode_step_append, byref(desc), *head, *rest)
+    _check_codebook(desc, codebook)
+    return _run(prepare, lib().oscar_decode_step_append_codebook, byref(desc), *head, _ptr(codebook), *rest)
 
 
 def oscar_decode_step_noalloc_max_bytes() -> int:
@@ -610,7 +619,7 @@ def oscar_decode_step_codebook(desc: LayerDesc, k_src, v_src, dst_page, dst_slot
 
 
 def oscar_attend(desc: LayerDesc, rot_v, pool, block_table, hist_len, n_splits: int, workspace, out, stream=None,
-                 codebook=None):
+                 codebook=None, prepare=False):
     """The second launch of oscar_decode_step alone (INT2 pass + merge into out). With
     `codebook` this is oscar_attend_codebook."""
     import torch
@@ -628,16 +637,16 @@ def oscar_attend(desc: LayerDesc, rot_v, pool, block_table, hist_len, n_splits: 
     rest = (_ptr(pool), _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), batch, int(n_splits),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
     if codebook is None:
-        _check(lib().oscar_attend(byref(desc), _ptr(rot_v), *rest))
-    else:
-        _check_codebook(desc, codebook)
-        _check(lib().oscar_attend_codebook(byref(desc), _ptr(rot_v), _ptr(codebook), *rest))
+        return _run(prepare, lib().oscar_attend, byref(desc), _ptr(rot_v), *rest)
+    _check_codebook(desc, codebook)
+    return _run(prepare, lib().oscar_attend_codebook, byref(desc), _ptr(rot_v), _ptr(codebook), *rest)
 
 
 def oscar_attend_codebook(desc: LayerDesc, rot_v, codebook, pool, block_table, hist_len, n_splits: int, workspace,
-                          out, stream=None):
+                          out, stream=None, prepare=False):
     """oscar_attend for a workspace that oscar_prepare_codebook prepared with the same codebook."""
-    oscar_attend(desc, rot_v, pool, block_table, hist_len, n_splits, workspace, out, stream, codebook)
+    return oscar_attend(desc, rot_v, pool, block_table, hist_len, n_splits, workspace, out, stream, codebook,
+                        prepare=prepare)
 
 
 def oscar_prepare(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool, k_win,
@@ -706,7 +715,7 @@ def oscar_demote_grouped(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, rot_
 
 
 def oscar_decode_int2_grouped(desc: LayerDesc, q, rot_k, pool, block_table, hist_len, sm_scale: float,
-                              n_splits: int, partials, stream=None):
+                              n_splits: int, partials, stream=None, prepare=False):
     """INT2 history pass over grouped pages (desc.group_size 128, 64 or 32); arguments as
     oscar_decode_int2."""
     batch = int(q.shape[0])
@@ -716,10 +725,9 @@ def oscar_decode_int2_grouped(desc: LayerDesc, q, rot_k, pool, block_table, hist
     _device_i32(block_table, "block_table")
     _device_i32(hist_len, "hist_len", batch)
     _need(pool.is_cuda and partials.is_cuda and partials.is_contiguous(), "pool/partials must be device tensors")
-    _check(lib().oscar_decode_int2_grouped(byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool), _ptr(block_table),
-                                           int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale),
-                                           int(n_splits), _ptr(partials), partials.numel() * partials.element_size(),
-                                           _stream(stream)))
+    return _run(prepare, lib().oscar_decode_int2_grouped, byref(desc), _ptr(q), _ptr(rot_k), _ptr(pool),
+                _ptr(block_table), int(block_table.shape[1]), _ptr(hist_len), batch, float(sm_scale), int(n_splits),
+                _ptr(partials), partials.numel() * partials.element_size(), _stream(stream))
 
 
 def oscar_decode_step_grouped(desc: LayerDesc, k_src, v_src, dst_page, dst_slot, clip_k, clip_v, q, rot_k, rot_v, pool,

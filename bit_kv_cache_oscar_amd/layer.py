@@ -129,15 +129,23 @@ class LayerCache:
         L.oscar_demote(self.desc, k_rows, v_rows, pages, slots, self.rot_k, self.rot_v, self.clip_k,
                        self.clip_v, self.pool, stream, self.codebook)
 
-    def decode(self, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
-        """Attention output [B, Hq, 128] float32 for queries q [B, Hq, 128] bf16."""
+    def decode(self, q: torch.Tensor, sm_scale: float, stream=None, prepare=False):
+        """Attention output [B, Hq, 128] float32 for queries q [B, Hq, 128] bf16, in three
+        launches (INT2 pass, window pass, merge). With `prepare`, returns the three calls as one
+        zero-argument callable (validated once)."""
         if self.codebook is not None:
             raise ValueError("the separate entry points read uniform INT2 levels; use decode_fused() or step()")
-        L.oscar_decode_int2(self.desc, q, self.rot_k, self.pool, self.block_table, self.hist_len, sm_scale,
-                            self.n_splits, self.partials, stream)
-        L.oscar_decode_bf16(self.desc, q, self.k_win, self.v_win, self.win_len, sm_scale, self.win_partials,
-                            stream)
-        L.oscar_merge(self.desc, self.partials, self.n_splits, self.win_partials, self.rot_v, self.out, stream)
+        calls = (L.oscar_decode_int2(self.desc, q, self.rot_k, self.pool, self.block_table, self.hist_len, sm_scale,
+                                     self.n_splits, self.partials, stream, prepare=prepare),
+                 L.oscar_decode_bf16(self.desc, q, self.k_win, self.v_win, self.win_len, sm_scale, self.win_partials,
+                                     stream, prepare=prepare),
+                 L.oscar_merge(self.desc, self.partials, self.n_splits, self.win_partials, self.rot_v, self.out,
+                               stream, prepare=prepare))
+        if prepare:
+            def run():
+                for c in calls:
+                    c()
+            return run
         return self.out
 
     def decode_fused(self, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
@@ -147,18 +155,22 @@ class LayerCache:
                        stream, self.codebook)
         return self.out
 
-    def step(self, k_rows, v_rows, pages, slots, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
+    def step(self, k_rows, v_rows, pages, slots, q: torch.Tensor, sm_scale: float, stream=None, prepare=False):
         """Demote k_rows/v_rows [n, Hkv, 128] into (pages, slots), then decode q: one decode step in
-        two launches (oscar_decode_step). hist_len must already count the demoted tokens."""
-        L.oscar_decode_step(self.desc, k_rows, v_rows, pages, slots, self.clip_k, self.clip_v, q, self.rot_k,
-                            self.rot_v, self.pool, self.block_table, self.hist_len, self.k_win, self.v_win,
-                            self.win_len, sm_scale, self.n_splits, self.workspace, self.out, stream, self.codebook)
-        return self.out
+        two launches (oscar_decode_step). hist_len must already count the demoted tokens. Returns
+        out, or with `prepare` the call as a zero-argument callable (validated once)."""
+        call = L.oscar_decode_step(self.desc, k_rows, v_rows, pages, slots, self.clip_k, self.clip_v, q, self.rot_k,
+                                   self.rot_v, self.pool, self.block_table, self.hist_len, self.k_win, self.v_win,
+                                   self.win_len, sm_scale, self.n_splits, self.workspace, self.out, stream,
+                                   self.codebook, prepare=prepare)
+        return call if prepare else self.out
 
-    def step_append(self, k_rows, v_rows, q: torch.Tensor, sm_scale: float, stream=None) -> torch.Tensor:
+    def step_append(self, k_rows, v_rows, q: torch.Tensor, sm_scale: float, stream=None, prepare=False):
         """One decode step in one launch (oscar_decode_step_append): k_rows/v_rows [B, Hkv, 128]
-        (or None) become history token hist_len[b] - 1 of each request b, then decode q."""
-        L.oscar_decode_step_append(self.desc, k_rows, v_rows, self.clip_k, self.clip_v, q, self.rot_k, self.rot_v,
-                                   self.pool, self.block_table, self.hist_len, self.k_win, self.v_win, self.win_len,
-                                   sm_scale, self.n_splits, self.append_workspace, self.out, stream, self.codebook)
-        return self.out
+        (or None) become history token hist_len[b] - 1 of each request b, then decode q. Returns
+        out, or with `prepare` the call as a zero-argument callable (validated once)."""
+        call = L.oscar_decode_step_append(self.desc, k_rows, v_rows, self.clip_k, self.clip_v, q, self.rot_k,
+                                          self.rot_v, self.pool, self.block_table, self.hist_len, self.k_win,
+                                          self.v_win, self.win_len, sm_scale, self.n_splits, self.append_workspace,
+                                          self.out, stream, self.codebook, prepare=prepare)
+        return call if prepare else self.out

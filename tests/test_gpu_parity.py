@@ -859,3 +859,16 @@ def test_decode_step_append_one_launch(case):
             got = c.step_append(None, None, q, w.sm_scale).cpu().numpy()
             for b in range(w.batch):
                 assert_close(got[b], refs[b], f"{case} one-launch decode b{b} splits {splits} call {rep}")
+        # the same calls prepared once (prepare=True) and issued twice: the same bits
+        kk, vv = bf16(lk), bf16(lv)  # a prepared call keeps pointers only: the tensors stay alive here
+        want = c.step_append(kk, vv, q, w.sm_scale).clone()
+        call = c.step_append(kk, vv, q, w.sm_scale, prepare=True)
+        for rep in range(2):
+            c.out.fill_(np.nan)
+            call()
+            assert torch.equal(c.out, want), f"{case} prepared one-launch step splits {splits} call {rep}"
+        want = c.decode_fused(q, w.sm_scale).clone()
+        call = c.decode(q, w.sm_scale, prepare=True)
+        c.out.fill_(np.nan)
+        call()
+        assert_close(c.out.cpu().numpy()[0], want.cpu().numpy()[0], f"{case} prepared three-launch decode")
