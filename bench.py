@@ -47,8 +47,8 @@ ROT_BYTES = 128 * 128 * 2
 COPY_BYTES = 256 * 2 ** 20  # the plain copy whose counter readings calibrate FETCH_SIZE / WRITE_SIZE
 CSRC = os.path.join(ROOT, "bit_kv_cache_oscar_amd", "csrc")
 # the sources of the timed step kernels: a change to any of them retires the counter summaries
-STEP_SOURCES = ("step.hip", "int2_pass.h", "merge_pass.h", "window_pass.h", "demote_pass.h", "device_common.h",
-                "launch.h")
+STEP_SOURCES = ("step.hip", "int2_pass.h", "merge_pass.h", "window_pass.h", "demote_pass.h", "grouped_pass.h",
+                "device_common.h", "launch.h", "decode_int2.hip")
 CONFIGS = (2, 3, 5, 4)  # headline first
 
 
@@ -103,7 +103,9 @@ def step_source_hash():
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` ("append_kernel": the one-launch step's kernel,
     "main_kernel": the attend launch, "attend_codebook": the attend launch of the codebook
-    variant) from the committed counter summary
+    variant, "multi_query": the one-launch multi-query decode, "grouped_pass_g64" / "_g32":
+    the grouped INT2 pass alone, "grouped_attend_g64" / "_g32": the grouped step's attend
+    launch) from the committed counter summary
     of this workload, or None when there is none or the kernel sources changed since it was
     taken. FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same
     counter reads for a plain copy of COPY_BYTES bytes in the same run."""
@@ -534,12 +536,13 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
         for i in range(max(2, args.warmup)):
             decode_multi(insts[i % layers])
         multi_ms = timed(decode_multi, args.steps)
+        launches_m = 1 if m_items <= 256 else 2
         hist = int(sum(w.hist_lens)) * w.n_kv_heads * HIST_BYTES
         win = int(sum(w.win_lens)) * w.n_kv_heads * WIN_BYTES
         mbytes = hist + win + 2 * w.n_kv_heads * ROT_BYTES + w.batch * n_tok * w.n_q_heads * 128 * (2 + 4)
         multi = {
             "entry": "oscar_decode_multi (no demotion)",
-            "launches": 1 if m_items <= 256 else 2,
+            "launches": launches_m,
             "n_splits": msplits,
             "query_tokens": n_tok,
             "us_per_call": round(multi_ms * 1e3, 3),
@@ -550,6 +553,7 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
             "unit": "GB/s",
             "frac": round(mbytes / (multi_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_call": mbytes,
+            "traffic": measured_traffic(w.name, "multi_query") if launches_m == 1 else None,
             "query_tokens_per_s": round(w.batch * n_tok / (multi_ms * 1e-3), 1),
         }
 
@@ -653,6 +657,8 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(g_bytes / (g_int2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(w.name, f"grouped_pass_g{group}"),
+            "attend_traffic": measured_traffic(w.name, f"grouped_attend_g{group}"),
         }
         del gins
         torch.cuda.empty_cache()

@@ -179,9 +179,10 @@ hipError_t launch_prep_ng(const StepArgs& a, hipStream_t stream) {
 
 // The one-launch step (and the one-launch multi-query decode: nqt query tokens per request
 // as virtual heads, no appended token). Items 0 .. n_win - 1 are window splits (split c, KV head, request);
-// when appending, the next B n_kv items each demote the appended token of one (request, KV
-// head) and write its own attention term; the rest are INT2 splits (split, KV head x head
-// group, request) with the query prepared inline and the appended token left out. Every
+// when appending, the next B n_kv items each demote the appended token of one (KV head,
+// request) and write its own attention term; the rest are INT2 splits (KV head, head group,
+// split, request, the first fastest) with the query prepared inline and the appended token
+// left out. Every
 // item starts at once, writes its partials with agent-scope stores and draws a ticket; the
 // last of a (request, KV head) merges.
 template <int GQ, int GQT, int NW, bool CB>
@@ -207,11 +208,15 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
     b = id / a.n_kv;
     demote::append_token<NW, GQT, true>(smem, b, kv, a, a.n_splits, pstride);
   } else {
+    // the KV head varies fastest: workgroups go to the 8 XCDs in turn, so with 8 KV heads
+    // every INT2 item of a KV head (its splits and head groups) runs on one XCD, whose L2
+    // then fetches the head's R_K and R_V once, and a page that two head groups read once
     id -= n_win + n_app;
-    const int split = id % a.n_splits;
-    const int gy = (id / a.n_splits) % (a.n_kv * a.n_groups);
-    b = id / (a.n_splits * a.n_kv * a.n_groups);
-    kv = gy / a.n_groups;
+    kv = id % a.n_kv;
+    const int rest = id / a.n_kv;
+    const int gy = kv * a.n_groups + rest % a.n_groups;
+    const int split = (rest / a.n_groups) % a.n_splits;
+    b = rest / (a.n_groups * a.n_splits);
     int2::InlineQuery iq;
     iq.q = a.q;
     iq.rot_k = a.rot_k;
