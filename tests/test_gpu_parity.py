@@ -484,9 +484,10 @@ def test_full_size_benchmarked_path(cfg):
     demotes the last token of each request and decodes in two launches (prepare; attend =
     INT2 pass with the in-launch ticket merge). Then the attend launch alone, twice, on the
     workspace the step prepared (what the benchmark's roofline row times), oscar_decode
-    (the two launches without demotion) and the four separate entry points. Pool bytes and
-    the outputs of every query head of the listed (request, KV head) pairs are compared
-    with the oracle; every path must meet the decode tolerance."""
+    (the two launches without demotion), the three separate passes, the one-launch step
+    and the multi-query decode at the benchmark's T and split count. Pool bytes and the
+    outputs of every query head (and query token) of the listed (request, KV head) pairs
+    are compared with the oracle; every path must meet the decode tolerance."""
     from bit_kv_cache_oscar_amd import oscar_attend, oscar_default_splits
 
     w = synth.workload(cfg)
@@ -544,6 +545,20 @@ def test_full_size_benchmarked_path(cfg):
                                                  w.sm_scale).cpu().numpy()
     c.out.fill_(np.nan)
     outs["one-launch decode"] = c.step_append(None, None, q, w.sm_scale).cpu().numpy()
+    # the multi-query decode as the benchmark times it: T query tokens per request (T query
+    # heads' worth of rows per KV head, 16 at most) at its own split count (one launch at
+    # batch 1, prepare + attend at batch 4 and 64)
+    from bit_kv_cache_oscar_amd import oscar_decode_multi, oscar_decode_multi_splits, oscar_decode_workspace_bytes
+
+    n_tok = min(4, 16 // w.gq)
+    qn = np.stack([synth.query_tokens(w, b, n_tok) for b in range(w.batch)])
+    ms = oscar_decode_multi_splits(c.desc, w.batch, n_tok, int(w.hist_lens.max()))
+    wsm = torch.zeros(oscar_decode_workspace_bytes(c.desc, w.batch * n_tok, ms), dtype=torch.uint8, device=dev)
+    outm = torch.full((w.batch, n_tok, w.n_q_heads, 128), np.nan, dtype=torch.float32, device=dev)
+    say("full size multi-query decode", w.name, "T", n_tok, "splits", ms)
+    oscar_decode_multi(c.desc, bf16(qn), c.rot_k, c.rot_v, c.pool, c.block_table, c.hist_len, c.k_win, c.v_win,
+                       c.win_len, w.sm_scale, ms, wsm, outm)
+    got_m = outm.cpu().numpy()
     torch.cuda.synchronize()
     pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, opages.HEAD_BLOCK)
     for b, kv in FULL_PAIRS[cfg]:
@@ -556,6 +571,13 @@ def test_full_size_benchmarked_path(cfg):
         for name, got in outs.items():
             for h in heads:
                 assert_close(got[b, h], ref[h], f"{w.name} {name} b{b} h{h}")
+        wk, wv = windows(w, b)
+        sl_h = slice(kv * w.gq, (kv + 1) * w.gq)
+        ref_m = oatt.decode_multi(qn[b][:, sl_h].astype(np.float64), rk[kv:kv + 1], rv[kv:kv + 1], wk[kv:kv + 1],
+                                  wv[kv:kv + 1], [ref_hist], w.sm_scale)
+        for t in range(n_tok):
+            for i, h in enumerate(heads):
+                assert_close(got_m[b, t, h], ref_m[t, i], f"{w.name} multi-query b{b} t{t} h{h}")
 
 
 STEP_CASES = ["c1", "c2-4k", "c4-shared-ragged", "c5-gq8", "gq16", "edges"]
