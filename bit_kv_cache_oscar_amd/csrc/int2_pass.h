@@ -821,7 +821,7 @@ __device__ __forceinline__ void int2_split(
     // probabilities (units of 2^E), pending sums, P' limbs (per group: the V scales differ).
     // A (tile, group) whose P' are all zero (every weight p s^V 2^E below one unit) adds
     // exactly nothing to the V sums: its limb rows then hold -128 c per code and the
-    // constant row c, which cancel in v_combo, so its limbs and matrix products are skipped
+    // constant row c, which cancel in v_combo. When every pair is so, the V side is skipped
     // (wave-uniform).
     bool vskip[MT][NG];
 #pragma unroll
@@ -843,7 +843,11 @@ __device__ __forceinline__ void int2_split(
           P[nt] = __float_as_uint(fmaf(pe[nt], sv[g][nt], 16777216.f));
         }
         vskip[mt][g] = __all((P[0] | P[1] | P[2] | P[3]) == 0x4B800000u);  // 2^24: P' = 0
-        if (!vskip[mt][g]) {
+        // with several head tiles the limbs are written whatever vskip says: a tile whose P'
+        // are all zero then gets rows encoding P' = 0 (each dword 0x80808080), which add
+        // exactly nothing, and the V products below run for every tile in straight-line
+        // code (per-tile branches there cost more than the products they skip)
+        if (MT > 1 || !vskip[mt][g]) {
           // byte l of the four P' values into one dword per limb, in signed range
           const uint32_t t01 = __builtin_amdgcn_perm(P[1], P[0], 0x05010400u);
           const uint32_t t23 = __builtin_amdgcn_perm(P[3], P[2], 0x05010400u);
@@ -886,7 +890,7 @@ __device__ __forceinline__ void int2_split(
           bv = unpack16_scaled(cur.vword(dt));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          if ((MT == 1 && NG == 1) || !vskip[mt][g]) st.acci[mt][dt] = mfma16(aP[mt][g], bv, st.acci[mt][dt]);
+          if (MT > 1 || NG == 1 || !vskip[mt][g]) st.acci[mt][dt] = mfma16(aP[mt][g], bv, st.acci[mt][dt]);
       }
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
