@@ -56,7 +56,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--configs", default=",".join(str(c) for c in CONFIGS),
                    help="workload configs, headline first (2: 32K, 3: 100K, 5: 128K B=4, 4: B=64)")
     p.add_argument("--config", type=int, default=0, help="one workload config only (overrides --configs)")
