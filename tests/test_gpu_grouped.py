@@ -307,3 +307,53 @@ def test_grouped_step_demotes_then_decodes(case, group):
             ref, km, vm = oracle_history_grouped(w, b, kv, rk, rv, group)
             got_h = unpack_grouped(pool, table[b], kv, w.hist_len(b), group)
             compare_history(got_h, ref, km, vm, f"{case} g{group} step pool b{b} kv{kv}")
+
+
+@pytest.mark.parametrize("kind", ["hadamard", "identity"])
+@pytest.mark.parametrize("group", [64, 32])
+def test_grouped_plain_rotations(kind, group):
+    """Grouped pages with R = H P (Hadamard and bit reversal, no eigenbasis: the QuaRot-style
+    baseline) and R = I (naive INT2), the comparisons the pages draw for the bit-reversal's
+    group balancing: the history of the 4K workload demoted on the GPU (the last token of
+    each request through the grouped step), then decoded by the step and by the three
+    separate passes; every token of the pool and every output against the oracle."""
+    from test_gpu_parity import plain_rotations
+
+    w = DECODE_CASES["c2-4k"]()
+    rk_bits, rk = plain_rotations(kind, w.n_kv_heads)
+    table, n_phys = synth.block_table(w)
+    c = grouped_cache(w, rk_bits, rk_bits, table, n_phys, group)
+    last_k, last_v, last_p, last_s = [], [], [], []
+    hists = [[None] * w.n_kv_heads for _ in range(w.batch)]
+    for b in range(w.batch):
+        rows = [synth.history_rows(w, b, kv) for kv in range(w.n_kv_heads)]
+        n = len(rows[0][0])
+        hk = np.stack([r[0] for r in rows], 1)
+        hv = np.stack([r[1] for r in rows], 1)
+        j = np.arange(n - 1)
+        c.demote(bf16(hk[:-1]), bf16(hv[:-1]), torch.from_numpy(table[b, j // 64].astype(np.int32)).cuda(),
+                 torch.from_numpy((j % 64).astype(np.int32)).cuda())
+        last_k.append(hk[-1])
+        last_v.append(hv[-1])
+        last_p.append(table[b, (n - 1) // 64])
+        last_s.append((n - 1) % 64)
+        for kv in range(w.n_kv_heads):
+            hists[b][kv], _, _ = oracle_history_grouped(w, b, kv, rk, rk, group)
+    refs = decode_refs(w, rk, rk, hists)
+    pages = torch.tensor(np.array(last_p, np.int32)).cuda()
+    slots = torch.tensor(np.array(last_s, np.int32)).cuda()
+    c.set_splits(5)
+    q = queries(w)
+    say("grouped", kind, "group", group, "step")
+    outs = {"step": c.step(bf16(np.stack(last_k)), bf16(np.stack(last_v)), pages, slots, q, w.sm_scale)
+            .cpu().numpy()}
+    c.out.fill_(np.nan)
+    outs["decode"] = c.decode(q, w.sm_scale).cpu().numpy()
+    pool = c.pool.cpu().numpy().reshape(n_phys, w.n_kv_heads, ogroups.head_block_bytes(group))
+    for b in range(w.batch):
+        for kv in range(w.n_kv_heads):
+            ref, km, vm = oracle_history_grouped(w, b, kv, rk, rk, group)
+            got_h = unpack_grouped(pool, table[b], kv, w.hist_len(b), group)
+            compare_history(got_h, ref, km, vm, f"{kind} g{group} pool b{b} kv{kv}")
+        for name, got in outs.items():
+            assert_close(got[b], refs[b], f"{kind} g{group} {name} b{b}")
