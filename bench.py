@@ -523,7 +523,7 @@ def extra_rows(S, args, stream, torch, dev, ceiling_gbs):
         qm = qm.to(torch.bfloat16)
         msplits = oscar_decode_multi_splits(base.desc, w.batch, n_tok, int(w.hist_lens.max()))
         gqt = w.gq * n_tok
-        m_items = ((oscar_window_splits(base.desc) + 1) * w.n_kv_heads * w.batch +
+        m_items = (((oscar_window_splits(base.desc) + 1) // 2 + 1) * w.n_kv_heads * w.batch +
                    msplits * w.n_kv_heads * w.batch * (2 if gqt > 8 else 1))
         wsm = torch.zeros(oscar_decode_workspace_bytes(base.desc, w.batch * n_tok, msplits), dtype=torch.uint8,
                           device=dev)

@@ -123,6 +123,9 @@ hipError_t launch_attend(StepArgs a, hipStream_t stream);
 // `hist` views n_splits + append columns; the counters must be zero at the start and are
 // left at zero. hipErrorInvalidValue if the grid does not fit step_append_one_launch.
 hipError_t launch_step_append(StepArgs a, hipStream_t stream);
+// Window workgroups of the one-launch grid per (request, KV head): each runs two of the
+// window's 64-slot splits, one per half of its 8 waves.
+__host__ __device__ inline int window_items(int n_wsplits) { return (n_wsplits + 1) / 2; }
 // whether the one-launch grid runs in a single dispatch round of 8-wave workgroups (else the
 // step is better run as prepare + attend)
 bool step_append_one_launch(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits);

@@ -637,8 +637,8 @@ constexpr long long kOneLaunchItems = 240;  // one-launch grid size the split co
 static int32_t one_launch_splits(const oscar_layer_desc* desc, int32_t batch, int gqt, int32_t max_hist_len) {
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
   const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gqt > 8 ? gqt / 8 : 1);
-  // window items and appended-token items
-  const long long n_win = static_cast<long long>(window_splits_of(desc) + 1) * batch * desc->n_kv_heads;
+  // window items (two splits each) and appended-token items
+  const long long n_win = static_cast<long long>(oscar::window_items(window_splits_of(desc)) + 1) * batch * desc->n_kv_heads;
   long long s = (kOneLaunchItems - n_win) / groups;
   const long long by_pages = (pages + 7) / 8;
   if (s < 1 || s * groups < 128) {

@@ -188,20 +188,23 @@ hipError_t launch_prep_ng(const StepArgs& a, hipStream_t stream) {
 template <int GQ, int GQT, int NW, bool CB>
 __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
   constexpr int kSmem = cmax(cmax(int2::int2_smem_bytes<GQ, NW>(), merge::smem_bytes<GQT, NW>()),
-                             cmax(window::window_smem_bytes<GQT>(), demote::append_smem_bytes<GQT>()));
+                             cmax(2 * window::window_smem_bytes<GQT>(), demote::append_smem_bytes<GQT>()));
   __shared__ __align__(16) unsigned char smem[kSmem];
   __shared__ int ticket_s;
-  const int n_win = a.n_wsplits * a.n_kv * a.batch;
+  // each window item runs two 64-slot splits, one per half of its waves
+  const int n_witems = window_items(a.n_wsplits);
+  const int n_win = n_witems * a.n_kv * a.batch;
   const int pstride = a.n_splits + a.append;
   int id = blockIdx.x;
   int kv, b;
   const int n_app = a.append ? a.n_kv * a.batch : 0;
   if (id < n_win) {
-    const int c = id % a.n_wsplits;
-    kv = (id / a.n_wsplits) % a.n_kv;
-    b = id / (a.n_wsplits * a.n_kv);
-    window::window_split<GQT, NW, true>(smem, c, kv, kv * GQT, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q, a.n_kv,
-                                        a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l, a.win.acc, GQT, a.nqt);
+    const int c = 2 * (id % n_witems);
+    kv = (id / n_witems) % a.n_kv;
+    b = id / (n_witems * a.n_kv);
+    window::window_split<GQT, NW, true, NW == 8>(smem, c, kv, kv * GQT, b, a.q, a.k_win, a.v_win, a.win_len, a.n_q,
+                                                 a.n_kv, a.window, a.n_wsplits, a.scale_log2, a.win.m, a.win.l,
+                                                 a.win.acc, GQT, a.nqt);
   } else if (id < n_win + n_app) {
     id -= n_win;
     kv = id % a.n_kv;
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
   int* counter = a.counters + b * a.n_kv + kv;
   if (threadIdx.x == 0) ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (ticket_s != a.n_splits * a.n_groups + a.n_wsplits + a.append - 1) return;
+  if (ticket_s != a.n_splits * a.n_groups + n_witems + a.append - 1) return;
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // every partial is in the window's basis (the INT2 splits and the appended token
   // un-rotated theirs): the merge is a weighted sum
@@ -250,7 +253,8 @@ constexpr int kStepSlots8 = 256;  // 8-wave workgroups resident at once (one per
 }  // namespace
 
 bool step_append_one_launch(int batch, int n_kv, int n_groups, int n_splits, int n_wsplits) {
-  return static_cast<long long>(n_wsplits + 1) * n_kv * batch + static_cast<long long>(n_splits) * n_kv * n_groups * batch <=
+  return static_cast<long long>(window_items(n_wsplits) + 1) * n_kv * batch +
+             static_cast<long long>(n_splits) * n_kv * n_groups * batch <=
          kStepSlots8;
 }
 
@@ -260,7 +264,7 @@ namespace {
 // step_append_one_launch)
 template <int GQ, int GQT, bool CB>
 hipError_t launch_append_cb(const StepArgs& a, hipStream_t stream) {
-  const long long items = static_cast<long long>(a.n_wsplits + a.append) * a.n_kv * a.batch +
+  const long long items = static_cast<long long>(window_items(a.n_wsplits) + a.append) * a.n_kv * a.batch +
                           static_cast<long long>(a.n_splits) * a.n_kv * a.n_groups * a.batch;
   if (items > kStepSlots8) return hipErrorInvalidValue;
   hipLaunchKernelGGL((append_kernel<GQ, GQT, 8, CB>), dim3(static_cast<unsigned>(items)), dim3(512), 0, stream, a);

@@ -34,23 +34,30 @@ constexpr int window_smem_bytes() {
 // for its query heads h0 .. h0 + GQ - 1 (GQ <= 16; the KV head's heads, or a group of them
 // when several workgroups share a KV head). `smem` holds window_smem_bytes<GQ>(). The pass
 // uses four waves; a workgroup of NWB waves (4 or 8) lets the others pass its barriers
-// idle. kCoherent: the partial goes out with agent-scope stores (for a merge inside the
-// same launch).
-template <int GQ, int NWB = 4, bool kCoherent = false>
+// idle, or with kDual (8 waves) runs split c + 1 on them (smem then holds twice as much; a
+// half past the last split does nothing). kCoherent: the partial goes out with agent-scope
+// stores (for a merge inside the same launch).
+template <int GQ, int NWB = 4, bool kCoherent = false, bool kDual = false>
 __device__ __forceinline__ void window_split(
     unsigned char* __restrict__ smem, int c, int kv, int h0, int b, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_win, const uint16_t* __restrict__ v_win,
     const int32_t* __restrict__ win_len, int n_q, int n_kv, int window, int n_wsplits, double scale_log2,
     float* __restrict__ out_m, float* __restrict__ out_l, float* __restrict__ out_acc, int gqv = GQ, int nqt = 1) {
   static_assert(GQ >= 1 && GQ <= 16, "one 16-column score tile holds the KV head's query heads");
+  static_assert(!kDual || NWB == 8, "two splits need eight waves");
+  // with kDual, waves 4..7 run split c + 1 as a pass of their own
+  const int half = kDual ? static_cast<int>(threadIdx.x >> 8) : 0;
+  c += half;
+  smem += half * window_smem_bytes<GQ>();
   float(*mx_s)[16] = reinterpret_cast<float(*)[16]>(smem);
   float(*l_s)[16] = reinterpret_cast<float(*)[16]>(smem + 4 * 64);
   float(*p_s)[kPageTokens] = reinterpret_cast<float(*)[kPageTokens]>(smem + 4 * 128);
   float(*acc_s)[GQ][kHeadDim] = reinterpret_cast<float(*)[GQ][kHeadDim]>(smem + 4 * 128 + 4 * GQ * kPageTokens);
   static_assert(NWB == 4 || NWB == 8, "4 or 8 waves");
-  const int tid = threadIdx.x;
+  const int tid = kDual ? static_cast<int>(threadIdx.x & 255) : static_cast<int>(threadIdx.x);  // within the pass
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool act = NWB == 4 || wave < 4;  // wave-uniform: the waves that do the pass
+  // wave-uniform: the waves that do a pass (with kDual, both halves while their split exists)
+  const bool act = (NWB == 4 || kDual || wave < 4) && c < n_wsplits;
   const int t0 = c * kPageTokens;
   const size_t base = ((static_cast<size_t>(b) * n_kv + kv) * window + t0) * kHeadDim;
   // the window length first: the score mask needs it as soon as K and q have arrived
@@ -149,7 +156,8 @@ __device__ __forceinline__ void window_split(
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < GQ * kHeadDim; idx += 64 * NWB) {
+  // (without kDual every thread stores: idle waves hold no data of their own but take part)
+  for (int idx = tid; (!kDual || act) && idx < GQ * kHeadDim; idx += 64 * (kDual ? 4 : NWB)) {
     const int h = idx >> 7;
     const int d = idx & 127;
     const size_t o = (static_cast<size_t>(b) * n_q + h0 + h) * n_wsplits + c;

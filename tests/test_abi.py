@@ -154,14 +154,15 @@ def test_one_launch_step_sizes():
     """The one-launch step's split count keeps its grid (window items, one appended-token
     item per (request, KV head), history splits) at 240 workgroups or fewer, and the launch
     count follows from the grid fitting 256 workgroups."""
-    d = L.layer_desc(32, 8)  # 6 window splits of 64 tokens (64 sink + 256 recent)
-    ws = L.oscar_window_splits(d)
+    d = L.layer_desc(32, 8)  # 5 window splits of 64 tokens (64 sink + 256 recent)
+    # window items (two splits each) and the appended-token item, per KV head
+    fixed = (L.oscar_window_splits(d) + 1) // 2 + 1
     for hist in (32448, 99680):
         s = L.oscar_decode_step_append_splits(d, 1, hist)
-        assert (ws + 1) * 8 + s * 8 <= 240 < (ws + 1) * 8 + (s + 1) * 8
+        assert fixed * 8 + s * 8 <= 240 < fixed * 8 + (s + 1) * 8
         assert L.oscar_decode_step_append_launches(d, 1, s) == 1
     # 256 workgroups still run at once; one more does not
-    s_max = (256 - (ws + 1) * 8) // 8
+    s_max = (256 - fixed * 8) // 8
     assert L.oscar_decode_step_append_launches(d, 1, s_max) == 1
     assert L.oscar_decode_step_append_launches(d, 1, s_max + 1) == 2
     # batch 4 of a 64-query-head layer: too many window items for one launch
@@ -178,11 +179,11 @@ def test_one_launch_multi_sizes():
     workgroups, falls back to the two-launch default when that grid cannot hold half the
     chip's units of history splits, and answers 1 for invalid arguments."""
     d = L.layer_desc(32, 8)
-    ws = L.oscar_window_splits(d)
+    fixed = (L.oscar_window_splits(d) + 1) // 2 + 1
     for t, groups in ((1, 1), (2, 1), (4, 2)):
         s = L.oscar_decode_multi_splits(d, 1, t, 32448)
         assert s == L.oscar_decode_step_append_splits(d, 1, 32448) or t > 1
-        assert (ws + 1) * 8 + s * 8 * groups <= 240 < (ws + 1) * 8 + (s + 1) * 8 * groups
+        assert fixed * 8 + s * 8 * groups <= 240 < fixed * 8 + (s + 1) * 8 * groups
     # batch 4 of a 64-query-head layer with two tokens: the two-launch default
     d5 = L.layer_desc(64, 8)
     assert L.oscar_decode_multi_splits(d5, 4, 2, 130752) == L.oscar_default_splits(d5, 4, 130752)

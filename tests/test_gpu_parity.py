@@ -133,7 +133,7 @@ def multi_split_counts(desc, w, n_tok):
     mh = int(w.hist_lens.max())
     gqt = w.n_q_heads // w.n_kv_heads * n_tok
     per_split = w.n_kv_heads * w.batch * (2 if gqt > 8 else 1)
-    fixed = (oscar_window_splits(desc) + 1) * w.n_kv_heads * w.batch
+    fixed = ((oscar_window_splits(desc) + 1) // 2 + 1) * w.n_kv_heads * w.batch
     two = max(1, (256 - fixed) // per_split + 1)
     return {oscar_default_splits(desc, w.batch, mh), oscar_decode_multi_splits(desc, w.batch, n_tok, mh), 3,
             min(two, 255)}
