@@ -223,64 +223,100 @@ __device__ __forceinline__ int dim_of(int b, int G) { return 16 * (b >> 2) + 4 *
 // Extremes of the undecided tokens of an iteration's two tiles from their candidates:
 // bits 32 tt + 4 mt + e of cmax / cmin are this lane's candidates in tile tt (its token n,
 // its lane group's dims); xs2 holds the x rows of both tiles (tile tt, token n at row
-// 16 tt + n). Up to four candidates per pass, one per 16-lane group, fp64 sums
-// (group_dot). Returns, in every lane of a token, the max of the token's cmax values and the
-// min of its cmin values per tile. Out of line: its registers stay out of the kernel's main
-// loop.
+// 16 tt + n). The candidates go into a wave-private list in `stage` (kCandCap entries at a
+// time, each lane's at its rank among the wave's candidates), then each 16-lane group sums
+// one listed value per pass in fp64 (group_dot) and each lane folds its own values back.
+// Returns, in every lane of a token, the max of the token's cmax values and the min of its
+// cmin values per tile. Out of line: its registers stay out of the kernel's main loop.
+constexpr int kCandCap = 128;  // list entries per round: 4 B each, then an 8-byte sum each
 struct Extremes {
   double emax[2], emin[2];
 };
 __device__ __attribute__((noinline)) Extremes candidate_extremes(const uint16_t* xs2, const uint16_t* rt,
-                                                                 uint64_t cmax, uint64_t cmin) {
+                                                                 uint64_t cmax, uint64_t cmin,
+                                                                 unsigned char* stage) {
   const int lane = threadIdx.x & 63;
-  Extremes e = {{-INFINITY, -INFINITY}, {INFINITY, INFINITY}};
-  uint64_t cand = cmax | cmin;
-  uint64_t lanes = __ballot(cand != 0ull);
-  while (lanes) {
-    int js[4], rows[4], owner[4], kind[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      owner[r] = -1;
-      js[r] = 0;
-      rows[r] = 0;
-      kind[r] = 0;
-      if (lanes) {
-        const int ls = __builtin_ctzll(lanes);
-        const uint64_t cm = lane_u64(cand, ls);
-        const int b = __builtin_ctzll(cm);
-        const uint64_t xm = lane_u64(cmax, ls);
-        const uint64_t nm = lane_u64(cmin, ls);
-        kind[r] = static_cast<int>((xm >> b) & 1ull) | (static_cast<int>((nm >> b) & 1ull) << 1) | ((b >> 5) << 2);
-        if (lane == ls) cand &= cand - 1ull;
-        lanes = __ballot(cand != 0ull);
-        owner[r] = ls;
-        rows[r] = 16 * (b >> 5) + (ls & 15);
-        js[r] = dim_of(b & 31, ls >> 4);
-      }
-    }
-    const int g = lane >> 4;
-    const int jg = g == 0 ? js[0] : (g == 1 ? js[1] : (g == 2 ? js[2] : js[3]));
-    const int rg = g == 0 ? rows[0] : (g == 1 ? rows[1] : (g == 2 ? rows[2] : rows[3]));
-    const double y = group_dot(xs2 + rg * kHeadDim, rt + jg * kRTRow, lane & 15);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (owner[r] < 0) continue;
-      const double yr = lane_f64(y, 16 * r);
-      if ((lane & 15) == (owner[r] & 15)) {
-        const int tt = kind[r] >> 2;
-        if (kind[r] & 1) {
-          if (tt) e.emax[1] = fmax(e.emax[1], yr);
-          else e.emax[0] = fmax(e.emax[0], yr);
-        }
-        if (kind[r] & 2) {
-          if (tt) e.emin[1] = fmin(e.emin[1], yr);
-          else e.emin[0] = fmin(e.emin[0], yr);
-        }
-      }
-    }
+  uint32_t* list = reinterpret_cast<uint32_t*>(stage);
+  double* sums = reinterpret_cast<double*>(stage + 4 * kCandCap);
+  double emax0 = -INFINITY, emax1 = -INFINITY, emin0 = INFINITY, emin1 = INFINITY;
+  const uint64_t cand = cmax | cmin;
+  // rank of this lane's first candidate: the candidates of the lanes below it
+  const int cnt = __builtin_popcountll(cand);
+  int rank = 0, total = 0;
+  for (int k = 1;; ++k) {
+    const uint64_t m = __ballot(cnt >= k);
+    if (m == 0ull) break;
+    rank = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), rank)));
+    total += __builtin_popcountll(m);
   }
-  return e;
+  for (int r0 = 0; r0 < total; r0 += kCandCap) {
+    const int nr = min(kCandCap, total - r0);
+    // this lane's entries of the round: candidate bit b | lane << 6
+    {
+      uint64_t bits = cand;
+      int idx = rank - r0;
+      while (__any(bits != 0ull)) {
+        if (bits != 0ull) {
+          const int b = __builtin_ctzll(bits);
+          bits &= bits - 1ull;
+          if (idx >= 0 && idx < nr) list[idx] = static_cast<uint32_t>(b | (lane << 6));
+          ++idx;
+        }
+      }
+    }
+    // (the wave's LDS operations run in order: the reads below see the writes above)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // group g of pass p sums entry p + g: token row 16 tt + n of the owner, dim of bit b
+    for (int p = 0; p < nr; p += 4) {
+      const int ent = p + (lane >> 4);
+      if (ent < nr) {
+        const uint32_t v = list[ent];
+        const int b = static_cast<int>(v & 63u);
+        const int ls = static_cast<int>(v >> 6);
+        const double y = group_dot(xs2 + (16 * (b >> 5) + (ls & 15)) * kHeadDim, rt + dim_of(b & 31, ls >> 4) * kRTRow,
+                                   lane & 15);
+        if ((lane & 15) == 0) sums[ent] = y;
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // each lane folds its own sums, in the same order as it listed them
+    {
+      uint64_t bits = cand;
+      int idx = rank - r0;
+      while (__any(bits != 0ull)) {
+        if (bits != 0ull) {
+          const int b = __builtin_ctzll(bits);
+          bits &= bits - 1ull;
+          if (idx >= 0 && idx < nr) {
+            const double y = sums[idx];
+            const bool hi = (cmax >> b) & 1ull;
+            const bool lo = (cmin >> b) & 1ull;
+            if (b >= 32) {
+              if (hi) emax1 = fmax(emax1, y);
+              if (lo) emin1 = fmin(emin1, y);
+            } else {
+              if (hi) emax0 = fmax(emax0, y);
+              if (lo) emin0 = fmin(emin0, y);
+            }
+          }
+          ++idx;
+        }
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+  // the token's four lanes (lane groups) join theirs
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    emax0 = fmax(emax0, __shfl_xor(emax0, o, 64));
+    emax1 = fmax(emax1, __shfl_xor(emax1, o, 64));
+    emin0 = fmin(emin0, __shfl_xor(emin0, o, 64));
+    emin1 = fmin(emin1, __shfl_xor(emin1, o, 64));
+  }
+  return Extremes{{emax0, emax1}, {emin0, emin1}};
 }
+static_assert(kCandCap * (4 + 8) <= 16 * kHeadDim, "the candidate list and its sums fit a wave's code stage");
 
 // Codes of the flagged values of a tile (flags: this lane's bits (mt, e)), decided from
 // fp64 sums on an interval, and from compensated sums where that interval holds the
@@ -451,8 +487,8 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
 
   for (int it = 0; it < kIters; ++it) {
     const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * 32;  // first token of the iteration
-    if (tb >= n) break;  // wave-uniform
-    if (it > 0) load_iter(it);  // (iteration 0's rows were requested before R^T was staged)
+    if (tb >= n) break;  // wave-uniform (this iteration's rows were requested before R^T was
+                         // staged, or by the iteration before)
     // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n; four chunks from zero,
     // joined in a fixed order with rounding to nearest
     f32x4 acc[8][2];
@@ -508,7 +544,6 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
       for (int tt = 0; tt < 2; ++tt)
         smax[tt] = fmaxf(fmaxf(smax[tt], fmaxf(sb[tt][0], sb[tt][1])), fmaxf(sb[tt][2], sb[tt][3]));
     }
-
 
     // ---- both tiles at once: extremes, norms, error bounds and the fp32 interval test of
     // the scale and zero point
@@ -585,13 +620,15 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         const float thi = und ? mx[tt] - 3.f * dl[tt] : INFINITY;
         const float tlo = und ? mn[tt] + 3.f * dl[tt] : -INFINITY;
         uint32_t a = 0u, b = 0u;
+        if (__any(und)) {  // (a tile with no undecided token has no candidates)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+          for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a |= acc[mt][tt][e] >= thi ? (1u << (4 * mt + e)) : 0u;
-            b |= acc[mt][tt][e] <= tlo ? (1u << (4 * mt + e)) : 0u;
-          }
+            for (int e = 0; e < 4; ++e) {
+              a |= acc[mt][tt][e] >= thi ? (1u << (4 * mt + e)) : 0u;
+              b |= acc[mt][tt][e] <= tlo ? (1u << (4 * mt + e)) : 0u;
+            }
+        }
         // a token with more than two candidates on one side in one lane (a range comparable
         // to its bound) takes the full path instead
         const uint64_t many = __ballot(und && (__builtin_popcount(a) > 2 || __builtin_popcount(b) > 2));
@@ -604,7 +641,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         cmin |= static_cast<uint64_t>(b) << (32 * tt);
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const Extremes ce = candidate_extremes(sm.xs[wave][0], sm.rt, cmax, cmin);
+      const Extremes ce = candidate_extremes(sm.xs[wave][0], sm.rt, cmax, cmin, cs);
       bool settled[2] = {true, true};
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -659,6 +696,9 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         }
       }
     }
+
+    // the next iteration's rows: they load while this iteration's codes are made and stored
+    if (it + 1 < kIters && tb + kBWaves * 32 < n) load_iter(it + 1);
 
     // ---- per tile: codes, the exact decisions near boundaries, packing and stores
 #pragma unroll
