@@ -5,10 +5,11 @@
 // history, with a scale and zero point per group. The quantiser is the one demote_pass.h
 // implements per row; this kernel reaches the same scales and codes for many rows at once.
 //
-// A workgroup (4 waves) takes up to 1024 consecutive rows (tokens) of one (KV head, K or V)
-// with R^T staged in LDS; a wave does 32 tokens per iteration as two 16-token tiles, the
-// two tiles' extremes, interval tests and exact sums taken together (their dependency
-// chains interleave, and one exact pass serves both):
+// A workgroup (16 waves, one per CU) takes up to 2048 consecutive rows (tokens) of one
+// (KV head, K or V) with R^T staged in LDS; a wave does one 16-token tile per iteration
+// (kNT = 2 would give two tiles whose extremes, interval tests and exact sums are taken
+// together, but at twice the registers: four waves per SIMD with one tile hide more
+// latency than two waves with two):
 //   y^T = R^T x^T as four 32-deep chunks on v_mfma_f32_16x16x32_bf16, each from a zero
 //   accumulator, joined on the vector ALU as ((c0 + c1) + c2) + c3; lane (G, n) of a tile
 //   holds dims 16 mt + 4 G + e (mt < 8, e < 4) of token n.
@@ -59,17 +60,22 @@
 namespace oscar {
 namespace {
 
-constexpr int kBWaves = 4;
-constexpr int kIters = 8;                              // 32-token iterations per wave
-constexpr int kRowsPerBlock = kBWaves * 32 * kIters;   // 1024
+constexpr int kNT = 1;                                   // 16-token tiles per wave and iteration
+constexpr int kTokIter = 16 * kNT;                       // tokens per wave and iteration
+constexpr int kBWaves = 16;                              // waves per workgroup
+constexpr int kIters = 8;                                // iterations per wave
+constexpr int kRowsPerBlock = kBWaves * kTokIter * kIters;
+static_assert(kNT == 1 || kNT == 2, "tile bits of the candidate masks: two tiles at most");
 constexpr int kRTRow = kHeadDim + 8;                   // bf16 per LDS row of R^T (16 bytes of bank spread)
+constexpr int kXRow = kHeadDim + 8;                    // bf16 per LDS row of x (the same spread)
+constexpr int kKRow = kHeadDim + 16;                   // bytes per token of the K code stage (bank spread)
 constexpr float kGammaS = 68.f * 0x1p-24f * (1.f + 0x1p-14f);  // per computed sum |p|: the chunks, the joins, S's own error
 constexpr float kFullT = 0x1p-7f;                      // bound on t above which a token is summed exactly
 
 struct BulkSmem {
   uint16_t rt[kHeadDim * kRTRow];             // R^T: row j holds column j of R
-  uint16_t xs[kBWaves][2][16 * kHeadDim];     // per wave, the x rows of the iteration's two tiles (bf16 [16][128])
-  unsigned char cs[kBWaves][16 * kHeadDim];   // per wave, the codes of the current tile
+  uint16_t xs[kBWaves][kNT][16 * kXRow];     // per wave, the x rows of the iteration's tiles (bf16 [16][kXRow] each)
+  unsigned char cs[kBWaves][16 * kKRow];     // per wave, the codes of the current tile
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -215,7 +221,7 @@ __device__ __forceinline__ T boundary_gap(T t, uint32_t lv) {
 }
 
 // Byte offset of token n, dim j in a tile's code stage: K codes token-major, V dim-major.
-__device__ __forceinline__ int code_pos(bool is_v, int n, int j) { return is_v ? j * 16 + n : n * kHeadDim + j; }
+__device__ __forceinline__ int code_pos(bool is_v, int n, int j) { return is_v ? j * 16 + n : n * kKRow + j; }
 
 // Dim of candidate bit b (= 4 mt + e) of a lane in lane group G.
 __device__ __forceinline__ int dim_of(int b, int G) { return 16 * (b >> 2) + 4 * G + (b & 3); }
@@ -274,7 +280,7 @@ __device__ __attribute__((noinline)) Extremes candidate_extremes(const uint16_t*
         const uint32_t v = list[ent];
         const int b = static_cast<int>(v & 63u);
         const int ls = static_cast<int>(v >> 6);
-        const double y = group_dot(xs2 + (16 * (b >> 5) + (ls & 15)) * kHeadDim, rt + dim_of(b & 31, ls >> 4) * kRTRow,
+        const double y = group_dot(xs2 + (16 * (b >> 5) + (ls & 15)) * kXRow, rt + dim_of(b & 31, ls >> 4) * kRTRow,
                                    lane & 15);
         if ((lane & 15) == 0) sums[ent] = y;
       }
@@ -316,7 +322,7 @@ __device__ __attribute__((noinline)) Extremes candidate_extremes(const uint16_t*
   }
   return Extremes{{emax0, emax1}, {emin0, emin1}};
 }
-static_assert(kCandCap * (4 + 8) <= 16 * kHeadDim, "the candidate list and its sums fit a wave's code stage");
+static_assert(kCandCap * (4 + 8) <= 16 * kKRow, "the candidate list and its sums fit a wave's code stage");
 
 // Codes of the flagged values of a tile (flags: this lane's bits (mt, e)), decided from
 // fp64 sums on an interval, and from compensated sums where that interval holds the
@@ -348,7 +354,7 @@ __device__ __attribute__((noinline)) void fix_codes(const uint16_t* xs, const ui
     const int g = lane >> 4;
     const int jg = g == 0 ? js[0] : (g == 1 ? js[1] : (g == 2 ? js[2] : js[3]));
     const int ng = g == 0 ? ns[0] : (g == 1 ? ns[1] : (g == 2 ? ns[2] : ns[3]));
-    const double y = group_dot(xs + ng * kHeadDim, rt + jg * kRTRow, lane & 15);
+    const double y = group_dot(xs + ng * kXRow, rt + jg * kRTRow, lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (owner[r] < 0) continue;
@@ -373,7 +379,7 @@ __device__ __attribute__((noinline)) void fix_codes(const uint16_t* xs, const ui
           q = static_cast<uint32_t>(codebook_code(t, lv));
         }
       } else {
-        const double ye = coop_dot(xs + ns[r] * kHeadDim, rt + js[r] * kRTRow, lane);
+        const double ye = coop_dot(xs + ns[r] * kXRow, rt + js[r] * kRTRow, lane);
         q = exact_code(ye, s16, z16, lv);
       }
       if (lane == 0) cs[code_pos(is_v, ns[r], js[r])] = static_cast<unsigned char>(q);
@@ -388,7 +394,7 @@ __device__ __attribute__((noinline)) uint32_t full_token(const uint16_t* xs, con
                                                          int nf, double cr, bool is_v, uint32_t lv) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
-  const uint16_t* xrow = xs + nf * kHeadDim;
+  const uint16_t* xrow = xs + nf * kXRow;
   double yv[2];
   double ymx = -INFINITY, ymn = INFINITY;
 #pragma unroll
@@ -425,7 +431,7 @@ __device__ __attribute__((noinline)) uint32_t full_token(const uint16_t* xs, con
 
 // CB: the Lloyd-Max codebook variant (codebook words [n_kv][K, V])
 template <bool CB>
-__global__ __launch_bounds__(256) void demote_bulk_kernel(
+__global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, int n, int n_kv,
     const int32_t* __restrict__ dst_page, const int32_t* __restrict__ dst_slot,
     const uint16_t* __restrict__ rot_k, const uint16_t* __restrict__ rot_v, const float* __restrict__ clip_k,
@@ -448,12 +454,12 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
   // x fragments (B operand) of one iteration: lane (G, n) holds token tb + 16 tt + n,
   // elements 32 ks + 8 G .. + 7 (tokens past the end read the last row; nothing of theirs is
   // stored), with the tokens' destination page and slot
-  uint4 bx[2][4];
-  int pg[2], sl[2];
+  uint4 bx[kNT][4];
+  int pg[kNT], sl[kNT];
   auto load_iter = [&](int it) {
-    const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * 32;
+    const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * kTokIter;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < kNT; ++tt) {
       const int t = min(tb + 16 * tt + n_, n - 1);
       const uint16_t* xr = src + static_cast<size_t>(t) * head_stride + static_cast<size_t>(head) * kHeadDim;
 #pragma unroll
@@ -462,11 +468,11 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
       sl[tt] = dst_slot[t];
     }
   };
-  const int tb0 = blockIdx.x * kRowsPerBlock + wave * 32;
+  const int tb0 = blockIdx.x * kRowsPerBlock + wave * kTokIter;
   if (tb0 < n) load_iter(0);  // in flight while R^T is staged
 
-  // R^T into LDS: thread (i, half) copies row i, columns 64 half .. + 63
-  {
+  // R^T into LDS: thread (i, half) of the first 256 copies row i, columns 64 half .. + 63
+  if (tid < 256) {
     const int i = tid >> 1;
     const int c0 = 64 * (tid & 1);
     const uint4* rrow = reinterpret_cast<const uint4*>(rot + i * kHeadDim + c0);
@@ -486,37 +492,38 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
   unsigned char* cs = sm.cs[wave];
 
   for (int it = 0; it < kIters; ++it) {
-    const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * 32;  // first token of the iteration
+    const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * kTokIter;  // first token of the iteration
     if (tb >= n) break;  // wave-uniform (this iteration's rows were requested before R^T was
                          // staged, or by the iteration before)
     // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n; four chunks from zero,
     // joined in a fixed order with rounding to nearest
-    f32x4 acc[8][2];
+    f32x4 acc[8][kNT];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      f32x4 ch[4][2];
+      f32x4 ch[4][kNT];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 a = *reinterpret_cast<const uint4*>(sm.rt + (16 * mt + n_) * kRTRow + 32 * ks + 8 * G);
         const bf16x8 av = __builtin_bit_cast(bf16x8, a);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        ch[ks][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[0][ks]), z, 0, 0, 0);
-        ch[ks][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[1][ks]), z, 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < kNT; ++tt)
+          ch[ks][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[tt][ks]), z, 0, 0, 0);
       }
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < kNT; ++tt) {
 #pragma clang fp contract(off)
         acc[mt][tt] = ((ch[0][tt] + ch[1][tt]) + ch[2][tt]) + ch[3][tt];
       }
     }
     // this iteration's rows into LDS (for the exact paths), then |x| in their registers
-    int cpg[2], csl[2];
+    int cpg[kNT], csl[kNT];
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < kNT; ++tt) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        *reinterpret_cast<uint4*>(sm.xs[wave][tt] + n_ * kHeadDim + 32 * ks + 8 * G) = bx[tt][ks];
+        *reinterpret_cast<uint4*>(sm.xs[wave][tt] + n_ * kXRow + 32 * ks + 8 * G) = bx[tt][ks];
         bx[tt][ks] = make_uint4(bx[tt][ks].x & 0x7FFF7FFFu, bx[tt][ks].y & 0x7FFF7FFFu, bx[tt][ks].z & 0x7FFF7FFFu,
                                 bx[tt][ks].w & 0x7FFF7FFFu);
       }
@@ -528,30 +535,35 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
     // gamma_127 < 2^-16 of S whatever the order (products below the fp32 range flushed: at
     // most 2^-119 in all). dl = 68 2^-24 max S (1 + 2^-14) + 2^-115 then holds for every value
     // of the token.
-    float smax[2] = {0.f, 0.f};
+    float smax[kNT];
+#pragma unroll
+    for (int tt = 0; tt < kNT; ++tt) smax[tt] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      f32x4 sb[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      f32x4 sb[kNT];
+#pragma unroll
+      for (int tt = 0; tt < kNT; ++tt) sb[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 a = *reinterpret_cast<const uint4*>(sm.rt + (16 * mt + n_) * kRTRow + 32 * ks + 8 * G);
         const uint4 aa = make_uint4(a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu, a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu);
         const bf16x8 aav = __builtin_bit_cast(bf16x8, aa);
-        sb[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, bx[0][ks]), sb[0], 0, 0, 0);
-        sb[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, bx[1][ks]), sb[1], 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < kNT; ++tt)
+          sb[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, bx[tt][ks]), sb[tt], 0, 0, 0);
       }
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < kNT; ++tt)
         smax[tt] = fmaxf(fmaxf(smax[tt], fmaxf(sb[tt][0], sb[tt][1])), fmaxf(sb[tt][2], sb[tt][3]));
     }
 
     // ---- both tiles at once: extremes, norms, error bounds and the fp32 interval test of
     // the scale and zero point
-    float mx[2], mn[2], dl[2];
-    bool valid[2], known[2], full[2];
-    uint16_t s16[2], z16[2];
+    float mx[kNT], mn[kNT], dl[kNT];
+    bool valid[kNT], known[kNT], full[kNT];
+    uint16_t s16[kNT], z16[kNT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < kNT; ++tt) {
       valid[tt] = tb + 16 * tt + n_ < n;
       float a = -INFINITY, b = INFINITY;
 #pragma unroll
@@ -567,13 +579,13 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < kNT; ++tt) {
         mx[tt] = fmaxf(mx[tt], __shfl_xor(mx[tt], o, 64));
         mn[tt] = fminf(mn[tt], __shfl_xor(mn[tt], o, 64));
         smax[tt] = fmaxf(smax[tt], __shfl_xor(smax[tt], o, 64));
       }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < kNT; ++tt) {
 #pragma clang fp contract(off)
       // the bound of every fp32 value of this token (fp32 rounding of the product and sum
       // covered by the factor 1 + 2^-14 in kGammaS)
@@ -608,19 +620,23 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
 
     // ---- the undecided tokens of both tiles: their candidates' fp64 sums, then the same
     // test in fp64; compensated sums when even that leaves the fp16 values open
-    const bool und0 = !known[0] && !full[0];
-    const bool und1 = !known[1] && !full[1];
-    if (__any(und0 || und1)) {
+    bool und[kNT];
+    bool any_und = false;
+#pragma unroll
+    for (int tt = 0; tt < kNT; ++tt) {
+      und[tt] = !known[tt] && !full[tt];
+      any_und = any_und || und[tt];
+    }
+    if (__any(any_und)) {
       uint64_t cmax = 0ull, cmin = 0ull;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const bool und = tt ? und1 : und0;
+      for (int tt = 0; tt < kNT; ++tt) {
         // candidates: values within 3 dl of an fp32 extreme (the thresholds' own rounding is
         // below dl / 256, so this holds every value within 2 dl of the exact extreme)
-        const float thi = und ? mx[tt] - 3.f * dl[tt] : INFINITY;
-        const float tlo = und ? mn[tt] + 3.f * dl[tt] : -INFINITY;
+        const float thi = und[tt] ? mx[tt] - 3.f * dl[tt] : INFINITY;
+        const float tlo = und[tt] ? mn[tt] + 3.f * dl[tt] : -INFINITY;
         uint32_t a = 0u, b = 0u;
-        if (__any(und)) {  // (a tile with no undecided token has no candidates)
+        if (__any(und[tt])) {  // (a tile with no undecided token has no candidates)
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -631,7 +647,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         }
         // a token with more than two candidates on one side in one lane (a range comparable
         // to its bound) takes the full path instead
-        const uint64_t many = __ballot(und && (__builtin_popcount(a) > 2 || __builtin_popcount(b) > 2));
+        const uint64_t many = __ballot(und[tt] && (__builtin_popcount(a) > 2 || __builtin_popcount(b) > 2));
         const uint32_t toks = static_cast<uint32_t>((many | (many >> 16) | (many >> 32) | (many >> 48)) & 0xFFFFull);
         if ((toks >> n_) & 1u) {
           full[tt] = true;
@@ -642,9 +658,11 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       const Extremes ce = candidate_extremes(sm.xs[wave][0], sm.rt, cmax, cmin, cs);
-      bool settled[2] = {true, true};
+      bool settled[kNT];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < kNT; ++tt) settled[tt] = true;
+#pragma unroll
+      for (int tt = 0; tt < kNT; ++tt) {
 #pragma clang fp contract(off)
         if (!known[tt] && !full[tt]) {
           // the sums are within 11 2^-53 sum|p| < 2^-31 dl of the exact extremes; then room
@@ -663,7 +681,9 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         }
       }
       // the vanishing remainder: compensated sums of the candidates, token by token
-      uint64_t rest = __ballot(!settled[0] && G == 0) | (__ballot(!settled[1] && G == 0) << 16);
+      uint64_t rest = 0ull;
+#pragma unroll
+      for (int tt = 0; tt < kNT; ++tt) rest |= __ballot(!settled[tt] && G == 0) << (16 * tt);
       while (rest) {
         const int m = __builtin_ctzll(rest);  // token 16 tt + n of the iteration
         rest &= rest - 1;
@@ -678,31 +698,28 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
           while (cm) {
             const int b = __builtin_ctz(cm);
             cm &= cm - 1u;
-            const double y = coop_dot(sm.xs[wave][tt] + nf * kHeadDim, sm.rt + dim_of(b, g) * kRTRow, lane);
+            const double y = coop_dot(sm.xs[wave][tt] + nf * kXRow, sm.rt + dim_of(b, g) * kRTRow, lane);
             if ((cxm >> b) & 1u) ex = fmax(ex, y);
             if ((cnm >> b) & 1u) en = fmin(en, y);
           }
         }
         uint16_t a16, b16;
         scale_zero(cr, ex, en, a16, b16);
-        if (n_ == nf) {
-          if (tt) {
-            s16[1] = a16;
-            z16[1] = b16;
-          } else {
-            s16[0] = a16;
-            z16[0] = b16;
+#pragma unroll
+        for (int t2 = 0; t2 < kNT; ++t2)
+          if (n_ == nf && t2 == tt) {
+            s16[t2] = a16;
+            z16[t2] = b16;
           }
-        }
       }
     }
 
     // the next iteration's rows: they load while this iteration's codes are made and stored
-    if (it + 1 < kIters && tb + kBWaves * 32 < n) load_iter(it + 1);
+    if (it + 1 < kIters && tb + kBWaves * kTokIter < n) load_iter(it + 1);
 
     // ---- per tile: codes, the exact decisions near boundaries, packing and stores
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < kNT; ++tt) {
       const int t0 = tb + 16 * tt;  // first token of the tile
       if (t0 >= n) break;           // wave-uniform
       const uint16_t* xs = sm.xs[wave][tt];
@@ -743,7 +760,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
         }
         if (!usable) w = 0u;
         if (!is_v) {
-          *reinterpret_cast<uint32_t*>(cs + n_ * kHeadDim + 16 * mt + 4 * G) = w;
+          *reinterpret_cast<uint32_t*>(cs + n_ * kKRow + 16 * mt + 4 * G) = w;
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) cs[(16 * mt + 4 * G + e) * 16 + n_] = static_cast<unsigned char>(w >> (8 * e));
@@ -801,7 +818,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(
           const int pgw = __shfl(page, tk, 64);
           const int slw = __shfl(slot, tk, 64);
           if (t0 + tk < n) {
-            const uint4 b = *reinterpret_cast<const uint4*>(cs + tk * kHeadDim + 16 * w);
+            const uint4 b = *reinterpret_cast<const uint4*>(cs + tk * kKRow + 16 * w);
             const uint32_t word = b.x | (b.y << 2) | (b.z << 4) | (b.w << 6);
             uint8_t* blk = pool + (static_cast<size_t>(pgw) * n_kv + head) * kHeadBlock;
             *reinterpret_cast<uint32_t*>(blk + k_word_offset(slw, w)) = word;
@@ -852,12 +869,12 @@ hipError_t launch_demote_bulk(const LayerShape& L, const void* k_src, const void
   if (n <= 0) return hipSuccess;
   const unsigned blocks = static_cast<unsigned>((n + kRowsPerBlock - 1) / kRowsPerBlock);
   if (codebook)
-    hipLaunchKernelGGL(demote_bulk_kernel<true>, dim3(blocks, L.n_kv, 2), dim3(256), 0, stream,
+    hipLaunchKernelGGL(demote_bulk_kernel<true>, dim3(blocks, L.n_kv, 2), dim3(64 * kBWaves), 0, stream,
                        static_cast<const uint16_t*>(k_src), static_cast<const uint16_t*>(v_src), n, L.n_kv, dst_page,
                        dst_slot, static_cast<const uint16_t*>(rot_k), static_cast<const uint16_t*>(rot_v), clip_k,
                        clip_v, static_cast<uint8_t*>(pool), codebook);
   else
-    hipLaunchKernelGGL(demote_bulk_kernel<false>, dim3(blocks, L.n_kv, 2), dim3(256), 0, stream,
+    hipLaunchKernelGGL(demote_bulk_kernel<false>, dim3(blocks, L.n_kv, 2), dim3(64 * kBWaves), 0, stream,
                        static_cast<const uint16_t*>(k_src), static_cast<const uint16_t*>(v_src), n, L.n_kv, dst_page,
                        dst_slot, static_cast<const uint16_t*>(rot_k), static_cast<const uint16_t*>(rot_v), clip_k,
                        clip_v, static_cast<uint8_t*>(pool), nullptr);
