@@ -806,11 +806,15 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
         uint8_t* blk = pool + (static_cast<size_t>(page) * n_kv + head) * kHeadBlock;
         *reinterpret_cast<uint32_t*>(blk + meta_off + 4 * slot) = sz;
       }
+      // the lane's store offsets are formed here from an opaque copy of the lane index:
+      // offsets made once ahead of the loop would each hold a register through it (and spill)
+      int lane_s = lane;
+      asm volatile("" : "+v"(lane_s));
       if (!is_v) {
         // K words: word q = lane + 64 r is (token q / 8 of the tile, dims 16 (q % 8) ..)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          const int q = lane + 64 * r;
+          const int q = lane_s + 64 * r;
           const int tk = q >> 3;
           const int w = q & 7;
           // page and slot of the word's token from lane tk, which loaded them (every lane
@@ -834,7 +838,7 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
           uint8_t* blk = pool + (static_cast<size_t>(page0) * n_kv + head) * kHeadBlock;
 #pragma unroll
           for (int r = 0; r < 2; ++r) {
-            const int d = lane + 64 * r;
+            const int d = lane_s + 64 * r;
             const uint4 b = *reinterpret_cast<const uint4*>(cs + d * 16);
             const uint32_t word = b.x | (b.y << 2) | (b.z << 4) | (b.w << 6);
             *reinterpret_cast<uint32_t*>(blk + v_word_offset(d, slot0 >> 4)) = word;
