@@ -770,6 +770,65 @@ def test_bulk_demotion_adversarial_rows_exact():
         assert compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"adversarial head {kv}") == 0
 
 
+def _tie_rows(g, n):
+    """Rows under R = I whose scale (max - min) / 3 is exactly halfway between two fp16
+    values, with two values at the maximum and two at the minimum in each lane group's
+    dims (d % 16) // 4 of the bulk kernel's layout, the rest strictly between."""
+    def bf16_range(lo_e, hi_e):
+        return np.concatenate([(1.0 + np.arange(128) / 128.0) * 2.0 ** e for e in range(lo_e, hi_e)])
+    hi_vals, lo_vals = bf16_range(-1, 2), -bf16_range(-8, 2)
+    s = (hi_vals[:, None] - lo_vals[None, :]) / 3.0
+    ulp = 2.0 ** (np.floor(np.log2(s)) - 10)
+    ties = np.argwhere(s == (np.floor(s / ulp) + 0.5) * ulp)
+    pick = ties[g.choice(len(ties), n, replace=False)]
+    d = np.arange(128)
+    grp = (d % 16) // 4
+    rows = np.empty((n, 128))
+    for r, (i, j) in enumerate(pick):
+        hi, lo = hi_vals[i], lo_vals[j]
+        rows[r] = synth.to_bf16_values(g.uniform(lo + 0.25 * (hi - lo), hi - 0.25 * (hi - lo), 128).astype(np.float32))
+        for gg in range(4):
+            dims = d[grp == gg]
+            rows[r, dims[:2]] = hi
+            rows[r, dims[2:4]] = lo
+    return rows
+
+
+def test_bulk_demotion_many_open_tokens_exact():
+    """Tiles whose every token leaves its fp16 scale open (exact ties under R = I, clip 1)
+    and puts four extreme candidates in each of its lanes: 256 candidates per wave and
+    iteration, more than one pass of the kernel's candidate list, then the compensated sums
+    that settle ties (to even); with random rows after them. Scales, zero points and codes
+    equal to the oracle's."""
+    w = custom("open tokens", 4, 2, [64 * 2 + 320], cfg=2)
+    (rk_bits, rv_bits), _ = rotations(w)
+    table = np.array([[0, 1]], np.int32)
+    c = make_cache(w, rk_bits, rv_bits, table, 2, with_windows=False)
+    eye_bits = np.zeros((2, 128, 128), np.uint16)
+    eye_bits[:, np.arange(128), np.arange(128)] = 0x3F80
+    one = np.ones(2, np.float32)
+    c.set_rotations(eye_bits, eye_bits, one, one)
+    g = np.random.default_rng(77)
+    n_tie, n = 64, 96
+    rows = np.empty((n, 2, 128), np.float32)
+    for kv in range(2):
+        rows[:n_tie, kv] = _tie_rows(g, n_tie)
+        rows[n_tie:, kv] = synth.to_bf16_values(g.standard_normal((n - n_tie, 128)).astype(np.float32))
+    j = np.arange(n)
+    say("bulk demotion, open tokens", n)
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, rows, rows[::-1].copy())
+    torch.cuda.synchronize()
+    pool = c.pool.cpu().numpy().reshape(2, 2, opages.HEAD_BLOCK)
+    from oracle import quant as oquant
+    for kv in range(2):
+        kc, ks, kz, km = oquant.quantize_rows(rows[:, kv].astype(np.float64), np.eye(128), 1.0)
+        vc, vs, vz, vm = oquant.quantize_rows(rows[::-1][:, kv].astype(np.float64), np.eye(128), 1.0)
+        got = opages.unpack_history(pool, table[0], kv, n)
+        compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"open tokens head {kv}")
+        for a, b in zip(got, (kc, ks, kz, vc, vs, vz)):
+            assert np.array_equal(np.asarray(a), np.asarray(b)), "open-token demotion differs from the oracle"
+
+
 @pytest.mark.parametrize("n", [40, 128])
 def test_demotion_fp16_overflow_contract(n):
     """A row whose clipped range exceeds fp16 is outside the quantiser's domain (the oracle
