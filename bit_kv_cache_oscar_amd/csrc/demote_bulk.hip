@@ -226,9 +226,9 @@ __device__ __forceinline__ int code_pos(bool is_v, int n, int j) { return is_v ?
 // Dim of candidate bit b (= 4 mt + e) of a lane in lane group G.
 __device__ __forceinline__ int dim_of(int b, int G) { return 16 * (b >> 2) + 4 * G + (b & 3); }
 
-// Extremes of the undecided tokens of an iteration's two tiles from their candidates:
+// Extremes of the undecided tokens of an iteration's tiles from their candidates:
 // bits 32 tt + 4 mt + e of cmax / cmin are this lane's candidates in tile tt (its token n,
-// its lane group's dims); xs2 holds the x rows of both tiles (tile tt, token n at row
+// its lane group's dims); xs2 holds the x rows of the tiles (tile tt, token n at row
 // 16 tt + n). The candidates go into a wave-private list in `stage` (kCandCap entries at a
 // time, each lane's at its rank among the wave's candidates), then each 16-lane group sums
 // one listed value per pass in fp64 (group_dot) and each lane folds its own values back.
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
         smax[tt] = fmaxf(fmaxf(smax[tt], fmaxf(sb[tt][0], sb[tt][1])), fmaxf(sb[tt][2], sb[tt][3]));
     }
 
-    // ---- both tiles at once: extremes, norms, error bounds and the fp32 interval test of
+    // ---- the iteration's tiles: extremes, norms, error bounds and the fp32 interval test of
     // the scale and zero point
     float mx[kNT], mn[kNT], dl[kNT];
     bool valid[kNT], known[kNT], full[kNT];
@@ -618,7 +618,7 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
       }
     }
 
-    // ---- the undecided tokens of both tiles: their candidates' fp64 sums, then the same
+    // ---- the undecided tokens of the tiles: their candidates' fp64 sums, then the same
     // test in fp64; compensated sums when even that leaves the fp16 values open
     bool und[kNT];
     bool any_und = false;
