@@ -52,6 +52,11 @@ struct PartialsView {
 
 size_t partials_bytes(int batch, int n_q, int n_splits);
 PartialsView partials_view(void* base, int batch, int n_q, int n_splits);
+// Ints between two arrival counters: each (request, KV head) counter has a 256-byte line of
+// its own. Packed, the counters share one line that every workgroup of the launch updates
+// with an agent-scope atomic: measured at 32K tokens, batch 1, 8 KV heads, the one-launch
+// step took 14.36 us per step with packed counters and 13.09 us with a line each.
+constexpr int kCounterStride = 64;
 size_t step_workspace_bytes(int batch, int n_q, int n_kv, int n_splits, int n_wsplits);
 
 // `codebook`: null for the uniform levels, else the codebook words [n_kv][K, V]
@@ -102,7 +107,7 @@ struct StepArgs {
   double scale_log2;
   PartialsView hist;  // INT2 partials and the query tail
   PartialsView win;   // window partials
-  int* counters;      // [batch][n_kv] arrival counters
+  int* counters;      // [batch][n_kv] arrival counters, kCounterStride ints apart
   float* out;
   // Lloyd-Max codebook variant: words [n_kv][K, V], byte c = level c in sixteenths of the
   // scale; null for the uniform INT2 levels

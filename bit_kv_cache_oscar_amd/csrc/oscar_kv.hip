@@ -108,7 +108,7 @@ size_t partials_bytes(int batch, int n_q, int n_splits) {
 // [INT2 partials + query tail | window partials | arrival counters]
 size_t step_workspace_bytes(int batch, int n_q, int n_kv, int n_splits, int n_wsplits) {
   return align256(partials_bytes(batch, n_q, n_splits)) + align256(partials_bytes(batch, n_q, n_wsplits)) +
-         align256(static_cast<size_t>(batch) * n_kv * 4);
+         align256(static_cast<size_t>(batch) * n_kv * 4 * kCounterStride);
 }
 
 PartialsView partials_view(void* base, int batch, int n_q, int n_splits) {
@@ -353,7 +353,9 @@ int32_t check_step_common(const oscar_layer_desc* desc, int32_t batch, int32_t n
   if (!workspace) return fail(OSCAR_ERR_INVALID_ARG, "null workspace");
   const int ws = window_splits_of(desc);
   const int n_qv = desc->n_q_heads * nqt;
-  const size_t need = oscar::step_workspace_bytes(batch, n_qv, desc->n_kv_heads, n_splits, ws);
+  // the documented size: oscar_decode_workspace_bytes of batch x nqt requests (the same
+  // partials as batch requests of nqt x n_q virtual heads, and more counter lines)
+  const size_t need = oscar::step_workspace_bytes(batch * nqt, desc->n_q_heads, desc->n_kv_heads, n_splits, ws);
   if (workspace_bytes < need) return fail(OSCAR_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   const oscar::LayerShape L = shape_of(desc);
   char* base = static_cast<char*>(workspace);

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void prep_kernel(StepArgs a) {
   id -= n_win;
   const int h = id % a.n_q;
   const int b = id / a.n_q;
-  if (threadIdx.x == 0 && h % a.gq == 0) a.counters[b * a.n_kv + h / a.gq] = 0;
+  if (threadIdx.x == 0 && h % a.gq == 0) a.counters[(b * a.n_kv + h / a.gq) * kCounterStride] = 0;
   int2::qprep_head(smem, a.q, a.rot_k, a.n_q, a.gq, a.scale_log2, a.hist.qlimb, a.hist.qscal, h, b, a.nqt,
                    a.codebook);
 }
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * NW) void main_kernel(StepArgs a) {
   // and the barrier has passed, the ticket below is drawn after all of them
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int* counter = a.counters + b * a.n_kv + kv;
+  int* counter = a.counters + (b * a.n_kv + kv) * kCounterStride;
   if (threadIdx.x == 0) ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (ticket_s != a.n_splits * a.n_groups - 1) return;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void append_kernel(StepArgs a) {
   // and the barrier has passed, the ticket below is drawn after all of them
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int* counter = a.counters + b * a.n_kv + kv;
+  int* counter = a.counters + (b * a.n_kv + kv) * kCounterStride;
   if (threadIdx.x == 0) ticket_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (ticket_s != a.n_splits * a.n_groups + n_witems + a.append - 1) return;

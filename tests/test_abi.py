@@ -216,7 +216,8 @@ def test_demote_argument_checks(lib):
 def test_decode_workspace_size():
     d = L.layer_desc(32, 8)
     a256 = lambda x: -(-x // 256) * 256
-    want = a256(L.oscar_partials_bytes(d, 3, 7)) + a256(L.oscar_partials_bytes(d, 3, 5)) + a256(3 * 8 * 4)
+    # INT2 partials, window partials, then one 256-byte line per (request, KV head) arrival counter
+    want = a256(L.oscar_partials_bytes(d, 3, 7)) + a256(L.oscar_partials_bytes(d, 3, 5)) + 3 * 8 * 256
     assert L.oscar_decode_workspace_bytes(d, 3, 7) == want
     bad = L.layer_desc(32, 8)
     bad.head_dim = 64
