@@ -552,7 +552,8 @@ def oscar_decode_step_append(desc: LayerDesc, k_src, v_src, clip_k, clip_v, q, r
                              stream=None, codebook=None, prepare=False):
     """One decode step in one launch: token b of k_src/v_src [batch, n_kv_heads, 128] bf16
     (None: nothing) becomes history token hist_len[b] - 1 of request b, then decode. The
-    workspace's arrival counters must be zero before the first call (zero-fill it once).
+    workspace's arrival counters must be zero before the first call (zero-fill it, and again
+    when the batch or split count changes).
     With `prepare`, returns the call as a callable (see _run)."""
     _need(desc.group_size == 128, "the one-launch step reads one-group pages")
     batch = int(q.shape[0])

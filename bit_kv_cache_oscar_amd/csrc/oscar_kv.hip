@@ -633,9 +633,9 @@ constexpr long long kOneLaunchItems = 240;  // one-launch grid size the split co
 // The split count of a one-launch grid (step or multi-query decode) with gqt query rows per
 // KV head: one launch when its window and appended-token items and at least half the
 // compute units' worth of history splits fit one 8-wave workgroup per unit; otherwise the
-// two-launch default. The grid stays at 240 items: measured at 100K tokens, 248 and 256
-// items (every unit or nearly) cost about 2 us more per step than 232 to 240, with fewer
-// pages per split.
+// two-launch default. The grid stays at 240 items: measured at batch 1 with 8 KV heads,
+// 24, 26, 27 and 28 splits (224 to 256 items) took 13.70, 13.08, 13.06 and 13.08 us per
+// step at 32K tokens and 20.19, 19.88, 20.07 and 20.05 us at 100K.
 static int32_t one_launch_splits(const oscar_layer_desc* desc, int32_t batch, int gqt, int32_t max_hist_len) {
   const long long pages = (static_cast<long long>(max_hist_len > 0 ? max_hist_len : 0) + 63) / 64;
   const long long groups = static_cast<long long>(batch) * desc->n_kv_heads * (gqt > 8 ? gqt / 8 : 1);

@@ -52,6 +52,7 @@ class LayerCache:
         self.codebook = None  # Lloyd-Max variant: uint8 [Hkv, 2, 4] levels (None: uniform INT2)
         self._partials = None
         self._workspace = None
+        self._append_ws_splits = None  # the split count the step workspace was zeroed for
         self._append_ws = None
         self.win_partials = torch.zeros(L.oscar_partials_bytes(self.desc, batch, L.oscar_window_splits(self.desc)),
                                         dtype=torch.uint8, device=self.device)
@@ -109,11 +110,17 @@ class LayerCache:
 
     @property
     def append_workspace(self) -> torch.Tensor:
-        """Workspace of the one-launch step, zero-filled when allocated (its arrival counters
-        must start at zero; every call leaves them there)."""
+        """Workspace of the one-launch step, zero-filled when allocated and again when the
+        split count changes: its arrival counters must start at zero (every call leaves them
+        there), and they sit after the partials, whose size depends on the split count."""
         need = L.oscar_decode_step_append_workspace_bytes(self.desc, self.batch, self.n_splits)
         if self._append_ws is None or self._append_ws.numel() < need:
             self._append_ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self._append_ws_splits = self.n_splits
+        elif self._append_ws_splits != self.n_splits:
+            self._append_ws.zero_()
+            torch.cuda.current_stream(self.device).synchronize()  # before a launch on any stream
+            self._append_ws_splits = self.n_splits
         return self._append_ws
 
     @property

@@ -274,10 +274,11 @@ int32_t oscar_decode_step(const oscar_layer_desc* desc, const void* k_src, const
  *              gives the count for which the launch's workgroups fit the chip at once
  *   workspace  at least oscar_decode_step_append_workspace_bytes(desc, batch, n_splits)
  *              bytes of device memory, owned by the caller, whose arrival counters must be
- *              zero before the first call: zero-fill it once after allocating it; every
- *              call leaves them at zero (oscar_decode_step and oscar_decode leave them at
- *              zero too, so a workspace can serve both). Calls that share a workspace must
- *              not overlap in time.
+ *              zero before the first call: zero-fill it after allocating it and again
+ *              when batch or n_splits change (the counters follow the partials, whose
+ *              size depends on both); every call leaves them at zero (oscar_decode_step
+ *              and oscar_decode leave them at zero too, so a workspace can serve both).
+ *              Calls that share a workspace must not overlap in time.
  * Errors: OSCAR_ERR_INVALID_ARG (null pointers, batch or n_splits <= 0, bad sm_scale),
  * OSCAR_ERR_UNSUPPORTED (sizes past the limits above), OSCAR_ERR_WORKSPACE (too small),
  * OSCAR_ERR_HIP (launch failure).
@@ -359,7 +360,8 @@ int32_t oscar_decode(const oscar_layer_desc* desc, const void* q, const void* ro
  *              OSCAR_ERR_UNSUPPORTED); batch * n_tokens <= 65535
  *   workspace  at least oscar_decode_workspace_bytes(desc, batch * n_tokens, n_splits)
  *              bytes, whose arrival counters must be zero before the first call (zero-fill
- *              it once after allocating it; every call leaves them at zero)
+ *              it after allocating it and again when batch, n_tokens or n_splits change;
+ *              every call leaves them at zero)
  * The other arguments are those of oscar_decode.
  */
 /* Split count for oscar_decode_multi at these sizes: the one-launch count when the grid can
