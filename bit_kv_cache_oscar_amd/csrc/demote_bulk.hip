@@ -495,51 +495,35 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
     const int tb = blockIdx.x * kRowsPerBlock + (it * kBWaves + wave) * kTokIter;  // first token of the iteration
     if (tb >= n) break;  // wave-uniform (this iteration's rows were requested before R^T was
                          // staged, or by the iteration before)
-    // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n; four chunks from zero,
-    // joined in a fixed order with rounding to nearest
-    f32x4 acc[8][kNT];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      f32x4 ch[4][kNT];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 a = *reinterpret_cast<const uint4*>(sm.rt + (16 * mt + n_) * kRTRow + 32 * ks + 8 * G);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int tt = 0; tt < kNT; ++tt)
-          ch[ks][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, bx[tt][ks]), z, 0, 0, 0);
-      }
-#pragma unroll
-      for (int tt = 0; tt < kNT; ++tt) {
-#pragma clang fp contract(off)
-        acc[mt][tt] = ((ch[0][tt] + ch[1][tt]) + ch[2][tt]) + ch[3][tt];
-      }
-    }
-    // this iteration's rows into LDS (for the exact paths), then |x| in their registers
+    // this iteration's rows into LDS (for the exact paths), and |x| beside them
     int cpg[kNT], csl[kNT];
+    uint4 bxa[kNT][4];
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
     for (int tt = 0; tt < kNT; ++tt) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         *reinterpret_cast<uint4*>(sm.xs[wave][tt] + n_ * kXRow + 32 * ks + 8 * G) = bx[tt][ks];
-        bx[tt][ks] = make_uint4(bx[tt][ks].x & 0x7FFF7FFFu, bx[tt][ks].y & 0x7FFF7FFFu, bx[tt][ks].z & 0x7FFF7FFFu,
-                                bx[tt][ks].w & 0x7FFF7FFFu);
+        bxa[tt][ks] = make_uint4(bx[tt][ks].x & 0x7FFF7FFFu, bx[tt][ks].y & 0x7FFF7FFFu, bx[tt][ks].z & 0x7FFF7FFFu,
+                                 bx[tt][ks].w & 0x7FFF7FFFu);
       }
       cpg[tt] = pg[tt];
       csl[tt] = sl[tt];
     }
-    // The token's error bound. S = |R^T| |x^T| (the sum of |p| of every value) from one
-    // 128-deep accumulation: its terms are all >= 0, so the fp32 result is within
-    // gamma_127 < 2^-16 of S whatever the order (products below the fp32 range flushed: at
-    // most 2^-119 in all). dl = 68 2^-24 max S (1 + 2^-14) + 2^-115 then holds for every value
-    // of the token.
+    // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n; four chunks from zero,
+    // joined in a fixed order with rounding to nearest. Beside it, from the same R^T
+    // fragments with the sign bits cleared, the token's error bound: S = |R^T| |x^T| (the sum
+    // of |p| of every value) from one 128-deep accumulation, whose terms are all >= 0, so the
+    // fp32 result is within gamma_127 < 2^-16 of S whatever the order (products below the fp32
+    // range flushed: at most 2^-119 in all). dl = 68 2^-24 max S (1 + 2^-14) + 2^-115 then
+    // holds for every value of the token.
+    f32x4 acc[8][kNT];
     float smax[kNT];
 #pragma unroll
     for (int tt = 0; tt < kNT; ++tt) smax[tt] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
+      f32x4 ch[4][kNT];
       f32x4 sb[kNT];
 #pragma unroll
       for (int tt = 0; tt < kNT; ++tt) sb[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -547,14 +531,21 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 a = *reinterpret_cast<const uint4*>(sm.rt + (16 * mt + n_) * kRTRow + 32 * ks + 8 * G);
         const uint4 aa = make_uint4(a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu, a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu);
-        const bf16x8 aav = __builtin_bit_cast(bf16x8, aa);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int tt = 0; tt < kNT; ++tt)
-          sb[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aav, __builtin_bit_cast(bf16x8, bx[tt][ks]), sb[tt], 0, 0, 0);
+        for (int tt = 0; tt < kNT; ++tt) {
+          ch[ks][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, bx[tt][ks]), z, 0, 0, 0);
+          sb[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
+                                                          __builtin_bit_cast(bf16x8, bxa[tt][ks]), sb[tt], 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int tt = 0; tt < kNT; ++tt)
+      for (int tt = 0; tt < kNT; ++tt) {
+#pragma clang fp contract(off)
+        acc[mt][tt] = ((ch[0][tt] + ch[1][tt]) + ch[2][tt]) + ch[3][tt];
         smax[tt] = fmaxf(fmaxf(smax[tt], fmaxf(sb[tt][0], sb[tt][1])), fmaxf(sb[tt][2], sb[tt][3]));
+      }
     }
 
     // ---- the iteration's tiles: extremes, norms, error bounds and the fp32 interval test of
