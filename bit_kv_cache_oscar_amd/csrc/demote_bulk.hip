@@ -24,12 +24,17 @@
 // gamma_32 < 32 2^-23 (1 + 2^-17); the three joins round to nearest (unit 2^-24), adding at
 // most 3 2^-24 (1 + 2^-15) sum |p|, so 68 2^-24 sum |p| (plus 2^-116 for at most 259
 // flushed products and partial sums of 2^-126 each) bounds a value's error. The sums
-// S_j = sum_i |x_i| |R_ij| come from the matrix cores too (|R^T| |x^T|, one 128-deep
-// accumulation): all their terms are >= 0, so in any order the fp32 result is within
-// gamma_127 < 2^-16 of S_j (flushed products: at most 2^-119). Hence
-//   delta = 68 2^-24 (1 + 2^-14) max_j S_j' + 2^-115
+// S_j = sum_i |x_i| |R_ij| are bounded per group of 8 consecutive dims j: with
+// M_gi = max over j in group g of |R_ij| (a bf16, exact), S_j <= T_g = sum_i |x_i| M_gi for
+// every j of group g. The 16 T_g of a token come from the matrix cores (M |x^T|, one
+// 128-deep accumulation, one 16-row tile): all their terms are >= 0, so in any order the
+// fp32 result is within gamma_127 < 2^-16 of T_g (flushed products: at most 2^-119). Hence
+//   delta = 68 2^-24 (1 + 2^-14) max_g T_g' + 2^-115
 // bounds the error of every value of the token. The matrix cores' own summation order is
-// thus never relied on, only this per-addition bound.
+// thus never relied on, only this per-addition bound. (The group maxima make delta about
+// 1.6 times the largest S_j on the workloads' rows, and more tokens take the fp64 path, but
+// they cost 4 matrix products per tile where the S_j themselves cost 32 and the masking of
+// every R^T fragment.)
 //
 // Scales and zero points (bit for bit the quantiser's):
 //   - the exact extremes lie within delta of the fp32 ones and the quantiser's fp64 chain is
@@ -76,6 +81,7 @@ struct BulkSmem {
   uint16_t rt[kHeadDim * kRTRow];             // R^T: row j holds column j of R
   uint16_t xs[kBWaves][kNT][16 * kXRow];     // per wave, the x rows of the iteration's tiles (bf16 [16][kXRow] each)
   unsigned char cs[kBWaves][16 * kKRow];     // per wave, the codes of the current tile
+  uint16_t gt[16 * kRTRow];                  // M: row g, column i holds max_{j in 8g..8g+7} |R_ij| (bf16)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -489,6 +495,19 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
     }
   }
   __syncthreads();
+  // the group maxima of |R^T| (magnitude order of bf16 is the integer order of its bits
+  // with the sign cleared)
+  for (int e = tid; e < 16 * kHeadDim; e += 64 * kBWaves) {
+    const int g = e / kHeadDim, i = e % kHeadDim;
+    uint16_t m = 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint16_t v = sm.rt[(8 * g + r) * kRTRow + i] & 0x7FFFu;
+      m = v > m ? v : m;
+    }
+    sm.gt[g * kRTRow + i] = m;
+  }
+  __syncthreads();
   unsigned char* cs = sm.cs[wave];
 
   for (int it = 0; it < kIters; ++it) {
@@ -510,44 +529,50 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
       cpg[tt] = pg[tt];
       csl[tt] = sl[tt];
     }
-    // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n; four chunks from zero,
-    // joined in a fixed order with rounding to nearest. Beside it, from the same R^T
-    // fragments with the sign bits cleared, the token's error bound: S = |R^T| |x^T| (the sum
-    // of |p| of every value) from one 128-deep accumulation, whose terms are all >= 0, so the
-    // fp32 result is within gamma_127 < 2^-16 of S whatever the order (products below the fp32
-    // range flushed: at most 2^-119 in all). dl = 68 2^-24 max S (1 + 2^-14) + 2^-115 then
-    // holds for every value of the token.
-    f32x4 acc[8][kNT];
     float smax[kNT];
-#pragma unroll
-    for (int tt = 0; tt < kNT; ++tt) smax[tt] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      f32x4 ch[4][kNT];
+    // The token's error bound: T = M |x^T| (row g: the sum of |x_i| times the group maxima
+    // of |R_ij|, at least S_j for every dim j of group g) from one 128-deep accumulation, whose
+    // terms are all >= 0, so the fp32 result is within gamma_127 < 2^-16 of T whatever the
+    // order (products below the fp32 range flushed: at most 2^-119 in all).
+    // dl = 68 2^-24 max T (1 + 2^-14) + 2^-115 then holds for every value of the token.
+    {
       f32x4 sb[kNT];
 #pragma unroll
       for (int tt = 0; tt < kNT; ++tt) sb[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        const uint4 ga = *reinterpret_cast<const uint4*>(sm.gt + n_ * kRTRow + 32 * ks + 8 * G);
+#pragma unroll
+        for (int tt = 0; tt < kNT; ++tt)
+          sb[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ga),
+                                                          __builtin_bit_cast(bf16x8, bxa[tt][ks]), sb[tt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < kNT; ++tt)
+        smax[tt] = fmaxf(fmaxf(sb[tt][0], sb[tt][1]), fmaxf(sb[tt][2], sb[tt][3]));
+    }
+    // y^T = R^T x^T: rows dims 16 mt + 4 G + e, column token n; four chunks from zero,
+    // joined in a fixed order with rounding to nearest.
+    f32x4 acc[8][kNT];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      f32x4 ch[4][kNT];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
         const uint4 a = *reinterpret_cast<const uint4*>(sm.rt + (16 * mt + n_) * kRTRow + 32 * ks + 8 * G);
-        const uint4 aa = make_uint4(a.x & 0x7FFF7FFFu, a.y & 0x7FFF7FFFu, a.z & 0x7FFF7FFFu, a.w & 0x7FFF7FFFu);
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int tt = 0; tt < kNT; ++tt) {
           ch[ks][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                               __builtin_bit_cast(bf16x8, bx[tt][ks]), z, 0, 0, 0);
-          sb[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aa),
-                                                          __builtin_bit_cast(bf16x8, bxa[tt][ks]), sb[tt], 0, 0, 0);
         }
       }
 #pragma unroll
       for (int tt = 0; tt < kNT; ++tt) {
 #pragma clang fp contract(off)
         acc[mt][tt] = ((ch[0][tt] + ch[1][tt]) + ch[2][tt]) + ch[3][tt];
-        smax[tt] = fmaxf(fmaxf(smax[tt], fmaxf(sb[tt][0], sb[tt][1])), fmaxf(sb[tt][2], sb[tt][3]));
       }
     }
-
     // ---- the iteration's tiles: extremes, norms, error bounds and the fp32 interval test of
     // the scale and zero point
     float mx[kNT], mn[kNT], dl[kNT];
