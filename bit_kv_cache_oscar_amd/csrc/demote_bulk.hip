@@ -742,21 +742,24 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
       const int page = cpg[tt];
       const int slot = csl[tt];
 
-      // codes of this lane's 32 values: v = (y - z16) / s16 + 1/2 as one fused step
-      // (|v - (t + 1/2)| <= dt + (8 + 4.1 |z16 / s16|) 2^-24 near a boundary), the code
-      // floor(v) on [0, 3.5]; values with v within bt of an integer may lie on the other
-      // side of it than the exact value and take the exact path (the integers 0 and 4 are no
-      // boundaries: flagging them only costs an exact sum)
+      // codes of this lane's 32 values: v = (y - z16) / s16 as one fused step (|v - t| <=
+      // dt + (8 + 4.1 |z16 / s16|) 2^-24 near a boundary), the code v on [0, 3] rounded to
+      // nearest by the packing conversion (v_cvt_pk_u8_f32 rounds to nearest: a GPU test
+      // pins it on every bf16 value of t from 1/4 to 3); values with v within bt of a
+      // half-integer may lie on the other side of it than the exact value and take the exact
+      // path, which also rounds exact ties to even (-1/2 and 7/2 are no boundaries: flagging
+      // them only costs an exact sum)
       const float sf = f16_to_f32(s16[tt]);
       const float zf = f16_to_f32(z16[tt]);
       const bool usable = sf != 0.f && f16_finite(s16[tt]) && f16_finite(z16[tt]);
       const float inv_s = usable ? 1.f / sf : 0.f;
       const float zs = zf * inv_s;
-      const float cb = CB ? -zs : 0.5f - zs;
+      const float cb = -zs;
       const float dt = dl[tt] * inv_s * (1.f + 0x1p-20f);
       bool fullt = full[tt] || (valid[tt] && usable && dt > kFullT);
       const float bt = (valid[tt] && usable && !fullt) ? dt + (1.f + 0.6f * fabsf(zs)) * 0x1p-21f : -1.f;
-      float gmax = 0.f;  // largest closeness to a boundary of this lane's values
+      float gmax = 0.f;  // codebook: largest closeness to a boundary of this lane's values
+      float gmin = 1.f;  // uniform levels: smallest distance to a half-integer
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
@@ -764,15 +767,13 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v = fmaf(acc[mt][tt][e], inv_s, cb);
-          uint32_t q;
           if constexpr (CB) {
-            q = static_cast<uint32_t>(codebook_code(v, lv));
+            w |= static_cast<uint32_t>(codebook_code(v, lv)) << (8 * e);
             gmax = fmaxf(gmax, 1.f - boundary_gap(v, lv));
           } else {
-            q = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(v, 0.f, 3.5f));
-            gmax = fmaxf(gmax, fabsf(__builtin_amdgcn_fractf(v) - 0.5f));
+            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(v, 0.f, 3.f), e, w);
+            gmin = fminf(gmin, fabsf(__builtin_amdgcn_fractf(v) - 0.5f));
           }
-          w |= q << (8 * e);
         }
         if (!usable) w = 0u;
         if (!is_v) {
@@ -782,9 +783,10 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
           for (int e = 0; e < 4; ++e) cs[(16 * mt + 4 * G + e) * 16 + n_] = static_cast<unsigned char>(w >> (8 * e));
         }
       }
-      // uniform levels: |fract(v) - 1/2| >= 1/2 - bt means v within bt of an integer; the
-      // codebook's 1 - gap >= 1 - bt means t within bt of a level midpoint
-      const bool flagged = CB ? (gmax >= 1.f - bt) : (gmax >= 0.5f - bt);
+      // uniform levels: |fract(v) - 1/2| <= bt means v within bt of a half-integer (exact for
+      // fract(v) >= 1/4, and at least 1/4 otherwise); the codebook's 1 - gap >= 1 - bt means
+      // v within bt of a level midpoint
+      const bool flagged = CB ? (gmax >= 1.f - bt) : (gmin <= bt);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       uint32_t sz = static_cast<uint32_t>(s16[tt]) | (static_cast<uint32_t>(z16[tt]) << 16);
       if (__any(flagged && bt >= 0.f)) {
@@ -800,8 +802,7 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
               if constexpr (CB) {
                 near = boundary_gap(v, lv) <= bt;
               } else {
-                const float f = __builtin_amdgcn_fractf(v);
-                near = fminf(f, 1.f - f) <= bt;
+                near = fabsf(__builtin_amdgcn_fractf(v) - 0.5f) <= bt;
               }
               if (near) flags |= 1u << (4 * mt + e);
             }

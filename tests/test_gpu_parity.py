@@ -829,6 +829,49 @@ def test_bulk_demotion_many_open_tokens_exact():
             assert np.array_equal(np.asarray(a), np.asarray(b)), "open-token demotion differs from the oracle"
 
 
+def test_bulk_demotion_codes_on_every_bf16_t():
+    """Rows under R = I with clip 1 holding 0 and 3 (so s16 = 1 and z16 = 0 exactly, and
+    t = y) and, between them, every bf16 value from 1/4 to 3: the matrix-core kernel takes
+    each code from the hardware's float-to-byte packing conversion unless the value lies
+    within its error bound of a half-integer, so this pins that conversion's rounding to
+    nearest at every representable t next to each code boundary (0.498 and 0.502 beside
+    1/2, and so on), and the exact ties 1/2, 3/2 and 5/2 to even."""
+    w = custom("every t", 4, 2, [64 * 2 + 320], cfg=2)
+    (rk_bits, rv_bits), _ = rotations(w)
+    table = np.array([[0, 1]], np.int32)
+    c = make_cache(w, rk_bits, rv_bits, table, 2, with_windows=False)
+    eye_bits = np.zeros((2, 128, 128), np.uint16)
+    eye_bits[:, np.arange(128), np.arange(128)] = 0x3F80
+    one = np.ones(2, np.float32)
+    c.set_rotations(eye_bits, eye_bits, one, one)
+    ts = np.concatenate([(1.0 + np.arange(128) / 128.0) * 2.0 ** e for e in (-2, -1, 0, 1)])
+    ts = ts[ts <= 3.0]
+    assert 0.5 in ts and 1.5 in ts and 2.5 in ts and len(ts) == 449
+    g = np.random.default_rng(5)
+    n = 128
+    rows = np.empty((n, 2, 128), np.float32)
+    for r in range(n):
+        for kv in range(2):
+            vals = np.resize(np.roll(ts, -126 * r - 61 * kv), 126)
+            row = np.concatenate([[0.0, 3.0], vals])
+            rows[r, kv] = row[g.permutation(128)]
+    assert np.array_equal(synth.to_bf16_values(rows), rows)
+    j = np.arange(n)
+    say("bulk demotion, every bf16 t", n)
+    _demote_all(c, w, 0, table[0, j // 64], j % 64, rows, rows[::-1].copy())
+    torch.cuda.synchronize()
+    pool = c.pool.cpu().numpy().reshape(2, 2, opages.HEAD_BLOCK)
+    from oracle import quant as oquant
+    for kv in range(2):
+        kc, ks, kz, km = oquant.quantize_rows(rows[:, kv].astype(np.float64), np.eye(128), 1.0)
+        vc, vs, vz, vm = oquant.quantize_rows(rows[::-1][:, kv].astype(np.float64), np.eye(128), 1.0)
+        assert np.all(ks == 1.0) and np.all(kz == 0.0)
+        got = opages.unpack_history(pool, table[0], kv, n)
+        compare_history(got, (kc, ks, kz, vc, vs, vz), km, vm, f"every t head {kv}")
+        for a, b in zip(got, (kc, ks, kz, vc, vs, vz)):
+            assert np.array_equal(np.asarray(a), np.asarray(b)), "codes differ from the oracle"
+
+
 @pytest.mark.parametrize("n", [40, 128])
 def test_demotion_fp16_overflow_contract(n):
     """A row whose clipped range exceeds fp16 is outside the quantiser's domain (the oracle
