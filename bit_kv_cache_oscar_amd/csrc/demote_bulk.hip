@@ -88,6 +88,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// LDS-qualified types for the out-of-line helpers: through plain pointers their LDS accesses
+// would compile to flat memory operations
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t ld1(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ uint32_t ld1(const lds_u16* p) { return *(const __attribute__((address_space(3))) uint32_t*)(p); }
+__device__ __forceinline__ uint4 ld4(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 ld4(const lds_u16* p) {
+  const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ double bf16lo(uint32_t w) { return static_cast<double>(__uint_as_float(w << 16)); }
 __device__ __forceinline__ double bf16hi(uint32_t w) { return static_cast<double>(__uint_as_float(w & 0xFFFF0000u)); }
 
@@ -108,10 +121,11 @@ __device__ __forceinline__ void scale_zero(double cr, double ymax, double ymin, 
 // sum_i x_i R_ij in fp64 from the exact products, by the whole wave: lane L takes i = 2L, 2L+1
 // and the 64 (sum, compensation) pairs are joined by two-sum steps; every lane gets the
 // result (within 2^-52 of it plus 2^-100 sum |p| of the exact sum)
-__device__ __forceinline__ double coop_dot(const uint16_t* xrow, const uint16_t* rtrow, int lane) {
+template <typename P>
+__device__ __forceinline__ double coop_dot(P xrow, P rtrow, int lane) {
 #pragma clang fp contract(off)
-  const uint32_t xv = *reinterpret_cast<const uint32_t*>(xrow + 2 * lane);
-  const uint32_t rv = *reinterpret_cast<const uint32_t*>(rtrow + 2 * lane);
+  const uint32_t xv = ld1(xrow + 2 * lane);
+  const uint32_t rv = ld1(rtrow + 2 * lane);
   double s = bf16lo(xv) * bf16lo(rv);
   double c = 0.0;
   demote::two_sum_add(s, c, bf16hi(xv) * bf16hi(rv));
@@ -139,10 +153,11 @@ __device__ __forceinline__ double dpp_f64(double v) {
 // i = 8q .. 8q + 7, the exact products are summed in fp64 in the lane and over the group by
 // DPP (eleven rounded additions, |error| <= 11 2^-53 sum_i |x_i R_ij|); every lane of the
 // group gets the sum
-__device__ __forceinline__ double group_dot(const uint16_t* xrow, const uint16_t* rtrow, int q) {
+template <typename P>
+__device__ __forceinline__ double group_dot(P xrow, P rtrow, int q) {
 #pragma clang fp contract(off)
-  const uint4 xv = *reinterpret_cast<const uint4*>(xrow + 8 * q);
-  const uint4 rv = *reinterpret_cast<const uint4*>(rtrow + 8 * q);
+  const uint4 xv = ld4(xrow + 8 * q);
+  const uint4 rv = ld4(rtrow + 8 * q);
   const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
   const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
   // fma: each product is exact in fp64, so the fused step rounds exactly as a sum does
@@ -235,106 +250,100 @@ __device__ __forceinline__ int dim_of(int b, int G) { return 16 * (b >> 2) + 4 *
 // Extremes of the undecided tokens of an iteration's tiles from their candidates:
 // bits 32 tt + 4 mt + e of cmax / cmin are this lane's candidates in tile tt (its token n,
 // its lane group's dims); xs2 holds the x rows of the tiles (tile tt, token n at row
-// 16 tt + n). The candidates go into a wave-private list in `stage` (kCandCap entries at a
-// time, each lane's at its rank among the wave's candidates), then each 16-lane group sums
-// one listed value per pass in fp64 (group_dot) and each lane folds its own values back.
-// Returns, in every lane of a token, the max of the token's cmax values and the min of its
-// cmin values per tile. Out of line: its registers stay out of the kernel's main loop.
-constexpr int kCandCap = 128;  // list entries per round: 4 B each, then an 8-byte sum each
+// 16 tt + n). Every lane's masks go into `stage`; 16-lane groups 2k and 2k + 1 then take the
+// token with candidates of rank 2r + k among the iteration's in round r, group 2k its cmax
+// side and group 2k + 1 its cmin side: the group reads the token's four masks of its side and
+// sums those candidates one at a time in fp64 (group_dot), keeping the largest (smallest);
+// the token's lanes read both back from `stage`. (An open token has one candidate per side
+// as a rule, so a round costs one sum per group.) Returns them per tile in every lane of a
+// token. Out of line: its registers stay out of the kernel's main loop.
 struct Extremes {
   double emax[2], emin[2];
 };
-__device__ __attribute__((noinline)) Extremes candidate_extremes(const uint16_t* xs2, const uint16_t* rt,
-                                                                 uint64_t cmax, uint64_t cmin,
-                                                                 unsigned char* stage) {
+constexpr int kStageMasks = 64 * 16;  // bytes: each lane's (cmax, cmin)
+constexpr int kStageExt = 32 * 16;    // bytes: each token's (max, min)
+static_assert(kStageMasks + kStageExt <= 16 * kKRow, "the candidate masks and extremes fit a wave's code stage");
+__device__ __attribute__((noinline)) Extremes candidate_extremes(const lds_u16* xs2, const lds_u16* rt,
+                                                                 uint64_t cmax, uint64_t cmin, lds_u8* stage) {
+#pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
-  uint32_t* list = reinterpret_cast<uint32_t*>(stage);
-  double* sums = reinterpret_cast<double*>(stage + 4 * kCandCap);
-  double emax0 = -INFINITY, emax1 = -INFINITY, emin0 = INFINITY, emin1 = INFINITY;
-  const uint64_t cand = cmax | cmin;
-  // rank of this lane's first candidate: the candidates of the lanes below it
-  const int cnt = __builtin_popcountll(cand);
-  int rank = 0, total = 0;
-  for (int k = 1;; ++k) {
-    const uint64_t m = __ballot(cnt >= k);
-    if (m == 0ull) break;
-    rank = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), rank)));
-    total += __builtin_popcountll(m);
-  }
-  for (int r0 = 0; r0 < total; r0 += kCandCap) {
-    const int nr = min(kCandCap, total - r0);
-    // this lane's entries of the round: candidate bit b | lane << 6
-    {
-      uint64_t bits = cand;
-      int idx = rank - r0;
-      while (__any(bits != 0ull)) {
-        if (bits != 0ull) {
-          const int b = __builtin_ctzll(bits);
-          bits &= bits - 1ull;
-          if (idx >= 0 && idx < nr) list[idx] = static_cast<uint32_t>(b | (lane << 6));
-          ++idx;
-        }
-      }
-    }
-    // (the wave's LDS operations run in order: the reads below see the writes above)
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    // group g of pass p sums entry p + g: token row 16 tt + n of the owner, dim of bit b
-    for (int p = 0; p < nr; p += 4) {
-      const int ent = p + (lane >> 4);
-      if (ent < nr) {
-        const uint32_t v = list[ent];
-        const int b = static_cast<int>(v & 63u);
-        const int ls = static_cast<int>(v >> 6);
-        const double y = group_dot(xs2 + (16 * (b >> 5) + (ls & 15)) * kXRow, rt + dim_of(b & 31, ls >> 4) * kRTRow,
-                                   lane & 15);
-        if ((lane & 15) == 0) sums[ent] = y;
-      }
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    // each lane folds its own sums, in the same order as it listed them
-    {
-      uint64_t bits = cand;
-      int idx = rank - r0;
-      while (__any(bits != 0ull)) {
-        if (bits != 0ull) {
-          const int b = __builtin_ctzll(bits);
-          bits &= bits - 1ull;
-          if (idx >= 0 && idx < nr) {
-            const double y = sums[idx];
-            const bool hi = (cmax >> b) & 1ull;
-            const bool lo = (cmin >> b) & 1ull;
-            if (b >= 32) {
-              if (hi) emax1 = fmax(emax1, y);
-              if (lo) emin1 = fmin(emin1, y);
-            } else {
-              if (hi) emax0 = fmax(emax0, y);
-              if (lo) emin0 = fmin(emin0, y);
-            }
-          }
-          ++idx;
-        }
-      }
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  }
-  // the token's four lanes (lane groups) join theirs
+  const int g = lane >> 4;
+  __attribute__((address_space(3))) uint64_t* masks = (__attribute__((address_space(3))) uint64_t*)(stage);
+  __attribute__((address_space(3))) double* ext = (__attribute__((address_space(3))) double*)(stage + kStageMasks);
+  masks[2 * lane] = cmax;
+  masks[2 * lane + 1] = cmin;
+  // the tokens with candidates: bit 16 tt + n (wave-uniform)
+  uint32_t toks = 0u;
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    emax0 = fmax(emax0, __shfl_xor(emax0, o, 64));
-    emax1 = fmax(emax1, __shfl_xor(emax1, o, 64));
-    emin0 = fmin(emin0, __shfl_xor(emin0, o, 64));
-    emin1 = fmin(emin1, __shfl_xor(emin1, o, 64));
+  for (int tt = 0; tt < kNT; ++tt) {
+    const uint64_t m = __ballot(static_cast<uint32_t>((cmax | cmin) >> (32 * tt)) != 0u);
+    toks |= static_cast<uint32_t>((m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFull) << (16 * tt);
   }
-  return Extremes{{emax0, emax1}, {emin0, emin1}};
+  // (the wave's LDS operations run in order: the reads below see the writes above)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const int side = g & 1;  // 0: the cmax candidates, 1: the cmin candidates
+  while (toks) {
+    // this round's two tokens, one per pair of lane groups (wave-uniform picks)
+    const int p0 = __builtin_ctz(toks);
+    toks &= toks - 1u;
+    const int p1 = toks ? __builtin_ctz(toks) : -1;
+    if (toks) toks &= toks - 1u;
+    const int m = g < 2 ? p0 : p1;
+    uint32_t c[4] = {0u, 0u, 0u, 0u};
+    if (m >= 0) {
+      const int tt = m >> 4, n = m & 15;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) c[G] = static_cast<uint32_t>(masks[2 * (16 * G + n) + side] >> (32 * tt));
+    }
+    double e = side ? INFINITY : -INFINITY;
+    const int xoff = (m < 0 ? 0 : m) * kXRow;
+    for (;;) {
+      // the group's next candidate: lane group G of the token, value bit b
+      int G = -1;
+      uint32_t u = 0u;
+#pragma unroll
+      for (int k = 3; k >= 0; --k)
+        if (c[k]) {
+          G = k;
+          u = c[k];
+        }
+      if (!__any(G >= 0)) break;
+      if (G >= 0) {
+        const int b = __builtin_ctz(u);
+        // (an opaque row offset: the row's loads and conversions hoisted out of the loop
+        // would hold registers that the caller then saves around every call)
+        int xo = xoff;
+        asm volatile("" : "+v"(xo));
+        const double y = group_dot(xs2 + xo, rt + dim_of(b, G) * kRTRow, lane & 15);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (k == G) c[k] &= c[k] - 1u;
+        e = side ? fmin(e, y) : fmax(e, y);
+      }
+    }
+    if (m >= 0 && (lane & 15) == 0) ext[2 * m + side] = e;
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  Extremes r;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    r.emax[tt] = -INFINITY;
+    r.emin[tt] = INFINITY;
+  }
+#pragma unroll
+  for (int tt = 0; tt < kNT; ++tt) {
+    const int m = 16 * tt + (lane & 15);
+    r.emax[tt] = ext[2 * m];
+    r.emin[tt] = ext[2 * m + 1];
+  }
+  return r;
 }
-static_assert(kCandCap * (4 + 8) <= 16 * kKRow, "the candidate list and its sums fit a wave's code stage");
 
 // Codes of the flagged values of a tile (flags: this lane's bits (mt, e)), decided from
 // fp64 sums on an interval, and from compensated sums where that interval holds the
 // boundary; written into the tile's code stage. sz: this lane's packed (s16, z16); dl: its
 // token's error bound.
-__device__ __attribute__((noinline)) void fix_codes(const uint16_t* xs, const uint16_t* rt, unsigned char* cs,
+__device__ __attribute__((noinline)) void fix_codes(const lds_u16* xs, const lds_u16* rt, lds_u8* cs,
                                                     uint32_t flags, uint32_t sz, float dl, bool is_v, uint32_t lv) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
@@ -396,21 +405,21 @@ __device__ __attribute__((noinline)) void fix_codes(const uint16_t* xs, const ui
 // Every value of the tile's token nf summed with compensation (lane L: dims L and L + 64);
 // its extremes give the scale and zero point and each value its code, written into the
 // code stage. Returns the packed (s16, z16) (wave-uniform).
-__device__ __attribute__((noinline)) uint32_t full_token(const uint16_t* xs, const uint16_t* rt, unsigned char* cs,
+__device__ __attribute__((noinline)) uint32_t full_token(const lds_u16* xs, const lds_u16* rt, lds_u8* cs,
                                                          int nf, double cr, bool is_v, uint32_t lv) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
-  const uint16_t* xrow = xs + nf * kXRow;
+  const lds_u16* xrow = xs + nf * kXRow;
   double yv[2];
   double ymx = -INFINITY, ymn = INFINITY;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int j = lane + 64 * h;
-    const uint16_t* rr = rt + j * kRTRow;
+    const lds_u16* rr = rt + j * kRTRow;
     double s = 0.0, c = 0.0;
     for (int i = 0; i < kHeadDim; i += 8) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xrow + i);
-      const uint4 rv = *reinterpret_cast<const uint4*>(rr + i);
+      const uint4 xv = ld4(xrow + i);
+      const uint4 rv = ld4(rr + i);
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
       const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
@@ -673,7 +682,8 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
         cmin |= static_cast<uint64_t>(b) << (32 * tt);
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const Extremes ce = candidate_extremes(sm.xs[wave][0], sm.rt, cmax, cmin, cs);
+      const Extremes ce = candidate_extremes((const lds_u16*)sm.xs[wave][0], (const lds_u16*)sm.rt, cmax, cmin,
+                                             (lds_u8*)cs);
       bool settled[kNT];
 #pragma unroll
       for (int tt = 0; tt < kNT; ++tt) settled[tt] = true;
@@ -807,13 +817,13 @@ __global__ __launch_bounds__(64 * kBWaves) void demote_bulk_kernel(
               if (near) flags |= 1u << (4 * mt + e);
             }
         }
-        fix_codes(xs, sm.rt, cs, flags, sz, dl[tt], is_v, lv);
+        fix_codes((const lds_u16*)xs, (const lds_u16*)sm.rt, (lds_u8*)cs, flags, sz, dl[tt], is_v, lv);
       }
       uint64_t fulls = __ballot(fullt && G == 0);
       while (fulls) {
         const int nf = __builtin_ctzll(fulls);
         fulls &= fulls - 1;
-        const uint32_t r = full_token(xs, sm.rt, cs, nf, cr, is_v, lv);
+        const uint32_t r = full_token((const lds_u16*)xs, (const lds_u16*)sm.rt, (lds_u8*)cs, nf, cr, is_v, lv);
         if (n_ == nf) sz = r;
       }
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
