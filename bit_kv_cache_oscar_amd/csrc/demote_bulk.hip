@@ -41,8 +41,8 @@
 //     monotone in both: when both ends of those intervals round to the same fp16 scale and
 //     zero point (evaluated in fp32 with outward margins), those are the values;
 //   - otherwise the candidates (values within 3 delta of an fp32 extreme) are summed again
-//     in fp64 from the exact products, 16 lanes per sum, four sums at a time, for every
-//     undecided token of the tile together (|error| <= 11 2^-53 sum |p| < 2^-31 delta), and the
+//     in fp64 from the exact products, 16 lanes per sum, one 16-lane group per (undecided
+//     token, side), two tokens at a time (|error| <= 11 2^-53 sum |p| < 2^-31 delta), and the
 //     same test runs in fp64;
 //   - when even that interval holds an fp16 rounding boundary, compensated (two-sum) sums
 //     over the wave give the extremes and the chain runs on them.

@@ -796,8 +796,9 @@ def _tie_rows(g, n):
 
 def test_bulk_demotion_many_open_tokens_exact():
     """Tiles whose every token leaves its fp16 scale open (exact ties under R = I, clip 1)
-    and puts four extreme candidates in each of its lanes: 256 candidates per wave and
-    iteration, more than one pass of the kernel's candidate list, then the compensated sums
+    and puts four extreme candidates in each of its lanes: eight candidates per side and
+    token, so each of the kernel's 16-lane groups sums many in turn, over eight rounds of two
+    tokens per wave and iteration, then the compensated sums
     that settle ties (to even); with random rows after them. Scales, zero points and codes
     equal to the oracle's."""
     w = custom("open tokens", 4, 2, [64 * 2 + 320], cfg=2)
